@@ -1,0 +1,365 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against a closed form, a value printed on the pages, a
+library routine, an invariant of the mathematics, or a brute-force computation built a
+different way, chosen so that a plausible slip (dropped term, wrong sign or index,
+transposed operand, wrong head grouping, wrong slot) fails at least one of them.
+"""
+
+import json
+import math
+import os
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from oracle import layer as ol
+from synth import workloads as sw
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_values.json")))
+
+
+def _cfg(**kw):
+    base = dict(hidden=32, n_q=4, n_kv=2, head_dim=16, ffn=48, block_size=16, rms_eps=1e-5,
+                rope_base=10000.0)
+    base.update(kw)
+    return SimpleNamespace(**base)
+
+
+def _bf16_exact(rng, shape, scale=1.0):
+    """float64 values that are exactly representable in bf16."""
+    return ol.bf16_to_f64(sw.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * scale))
+
+
+# ----------------------------------------------------------------------------- bf16
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    vals = (rng.standard_normal(200000) * 10).astype(np.float32)
+    # exact ties between two bf16 neighbours (low 16 bits = 0x8000) with both parities
+    ties = (np.arange(1, 2000, dtype=np.uint32) << np.uint32(16)) | np.uint32(0x8000)
+    vals = np.concatenate([vals, ties.view(np.float32), np.float32([0.0, -0.0, 1e-30, -3e30])])
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = ol.f64_to_bf16(vals.astype(np.float64))
+    assert np.array_equal(got, ref)
+    assert np.array_equal(ol.bf16_to_f64(ref), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy())
+
+
+# ----------------------------------------------------------------------------- FLOPs
+
+
+def test_flop_counter_reproduces_table2_ug():
+    g = GOLDEN["table2_ug_gflop"]
+    cfg = _cfg(hidden=g["shape"]["hidden"], ffn=g["shape"]["ffn"], n_q=64, n_kv=8, head_dim=128)
+    ug = ol.op_flops(cfg, g["shape"]["dense_batch"])["ug"] * g["shape"]["n_layers"]
+    assert ug == 153_931_627_888_640
+    assert round(ug / 1e9, 1) == g["value"]
+
+
+def test_layer_flops_equals_two_params_per_token_plus_attention():
+    # closed form: 2 T P_layer + sum over (query head, visible key) of 4 d
+    cfg = _cfg()
+    b = sw.batch_from_lengths([5, 0, 17], [4, 9], [0, 3], seed=1)
+    P = cfg.hidden * (cfg.n_q + 2 * cfg.n_kv) * cfg.head_dim + cfg.n_q * cfg.head_dim * cfg.hidden \
+        + 3 * cfg.hidden * cfg.ffn
+    T = b.n_tokens
+    att = 4 * cfg.head_dim * cfg.n_q * ((5 + 1) + (0 + 1) + (17 + 1) + 4 * 5 // 2 + (4 + 5 + 6 + 7 + 8 + 9 + 10 + 11 + 12))
+    assert ol.layer_flops(cfg, b) == 2 * T * P + att
+
+
+# ----------------------------------------------------------------------------- norm / rope / swiglu / linear
+
+
+def test_rmsnorm_constant_row_closed_form():
+    c = 3.25
+    g = np.linspace(0.5, 2.0, 64)
+    out = ol.rmsnorm(np.full((1, 64), c), g, 1e-5)
+    assert np.allclose(out[0], g * c / math.sqrt(c * c + 1e-5), rtol=1e-15, atol=0)
+
+
+def test_rmsnorm_scale_invariance_and_unit_rms():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((7, 128))
+    a = ol.rmsnorm(x, np.ones(128), 0.0)
+    b = ol.rmsnorm(13.0 * x, np.ones(128), 0.0)
+    assert np.allclose(a, b, rtol=1e-13)
+    assert np.allclose(np.sqrt(np.mean(a * a, axis=1)), 1.0, rtol=1e-13)
+
+
+def test_rope_position_zero_is_identity():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((3, 2, 16))
+    assert np.array_equal(ol.rope(x, np.zeros(3, np.int64), 10000.0), x)
+
+
+def test_rope_matches_complex_rotation():
+    # rotate-half pairs (i, i + d/2) rotate like complex numbers x_i + j x_{i+d/2} by pos*theta_i
+    rng = np.random.default_rng(4)
+    d = 16
+    x = rng.standard_normal((5, 3, d))
+    pos = np.array([0, 1, 7, 100, 4095])
+    out = ol.rope(x, pos, 10000.0)
+    z = x[..., : d // 2] + 1j * x[..., d // 2 :]
+    theta = pos[:, None] * np.power(10000.0, -np.arange(0, d, 2) / d)[None, :]
+    zr = z * np.exp(1j * theta)[:, None, :]
+    assert np.allclose(out[..., : d // 2], zr.real, atol=1e-12)
+    assert np.allclose(out[..., d // 2 :], zr.imag, atol=1e-12)
+
+
+def test_rope_relative_position_property():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 1, 32))
+    k = rng.standard_normal((1, 1, 32))
+    dots = []
+    for m, n in [(10, 3), (107, 100), (2007, 2000)]:
+        dots.append(float(np.sum(ol.rope(q, [m], 10000.0) * ol.rope(k, [n], 10000.0))))
+    assert np.allclose(dots, dots[0], rtol=1e-9)
+    norm = np.linalg.norm(ol.rope(q, [123], 10000.0)[0, 0].reshape(2, 16), axis=0)
+    assert np.allclose(norm, np.linalg.norm(q[0, 0].reshape(2, 16), axis=0))
+
+
+def test_silu_and_swiglu():
+    z = np.linspace(-30, 30, 601)
+    assert np.allclose(ol.silu(z), z * scipy.special.expit(z), rtol=1e-14, atol=1e-300)
+    assert ol.silu(np.array([0.0]))[0] == 0.0
+    assert abs(ol.silu(np.array([40.0]))[0] - 40.0) < 1e-12
+    assert abs(ol.silu(np.array([-40.0]))[0]) < 1e-15
+    gate = np.array([[1.0, -2.0, 0.0]])
+    up = np.array([[3.0, 5.0, 7.0]])
+    got = ol.swiglu(np.concatenate([gate, up], axis=1), 3)
+    assert np.allclose(got, scipy.special.expit(gate) * gate * up)
+
+
+def test_linear_uses_out_in_layout():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((4, 9))
+    perm = np.array([8, 0, 3, 3, 5])  # output j picks input perm[j]
+    w = np.zeros((5, 9))
+    w[np.arange(5), perm] = 1.0
+    assert np.array_equal(ol.linear(x, w), x[:, perm])
+
+
+# ----------------------------------------------------------------------------- slots
+
+
+def test_new_token_slots_match_block_expansion():
+    b = sw.batch_from_lengths([0, 15, 16, 33], [17, 40], [0, 5], seed=7)
+    # expand each request's table into a per-position list of (block, offset) pairs
+    expected = []
+    for r, (cached, qlen) in enumerate(zip(b.cached_lens(), b.q_lens())):
+        per_pos = [(int(blk), off) for blk in b.block_table[r] if blk >= 0 for off in range(16)]
+        expected += per_pos[cached : cached + qlen]
+    assert ol.new_token_slots(b, 16) == expected
+
+
+def test_write_kv_touches_exactly_the_new_slots():
+    cfg = _cfg()
+    b = sw.batch_from_lengths([3, 20, 31], [19], [2], seed=8)
+    canary = np.uint16(0x7FC1)  # a NaN pattern that rounding of finite values never yields
+    kp = np.full((b.num_blocks, cfg.n_kv, 16, cfg.head_dim), canary, np.uint16)
+    vp = np.full((b.num_blocks, cfg.n_kv, cfg.head_dim, 16), canary, np.uint16)
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal((b.n_tokens, cfg.n_kv, cfg.head_dim))
+    v = rng.standard_normal((b.n_tokens, cfg.n_kv, cfg.head_dim))
+    k2, v2 = ol.write_kv(kp, vp, b, 16, k, v)
+    changed_k = {(int(i), int(o)) for i, _, o, _ in zip(*np.nonzero(k2 != canary))}
+    changed_v = {(int(i), int(o)) for i, _, _, o in zip(*np.nonzero(v2 != canary))}
+    want = set(ol.new_token_slots(b, 16))
+    assert changed_k == want and changed_v == want
+    # every written entry of each token holds that token's rounded vector
+    for t, (blk, off) in enumerate(ol.new_token_slots(b, 16)):
+        assert np.array_equal(k2[blk, :, off, :], ol.f64_to_bf16(k[t]))
+        assert np.array_equal(v2[blk, :, :, off], ol.f64_to_bf16(v[t]))
+
+
+def test_slot_rejects_bad_tables():
+    b = sw.batch_from_lengths([20], [], seed=0)
+    bad = sw.Batch(b.decode_ctx, b.prefill_len, b.prefill_prefix, b.block_table.copy(), b.num_blocks)
+    bad.block_table[0, 1] = b.num_blocks
+    with pytest.raises(IndexError):
+        ol.new_token_slots(bad, 16)
+    short = sw.Batch(b.decode_ctx, b.prefill_len, b.prefill_prefix, b.block_table[:, :1].copy(), b.num_blocks)
+    with pytest.raises(IndexError):
+        ol.new_token_slots(short, 16)
+
+
+# ----------------------------------------------------------------------------- attention
+
+
+def _paged_pool_from_sequences(b, seqs_k, seqs_v, n_kv, d):
+    """Place each request's contiguous K/V sequence into its blocks, block by block."""
+    kp = np.zeros((b.num_blocks, n_kv, 16, d), np.uint16)
+    vp = np.zeros((b.num_blocks, n_kv, d, 16), np.uint16)
+    for r, (sk, sv) in enumerate(zip(seqs_k, seqs_v)):
+        n = sk.shape[0]
+        nblk = (n + 15) // 16
+        pad = nblk * 16 - n
+        sk = np.concatenate([sk, np.zeros((pad,) + sk.shape[1:])])
+        sv = np.concatenate([sv, np.zeros((pad,) + sv.shape[1:])])
+        for lb in range(nblk):
+            blk = b.block_table[r, lb]
+            kp[blk] = ol.f64_to_bf16(sk[lb * 16 : (lb + 1) * 16].transpose(1, 0, 2))
+            vp[blk] = ol.f64_to_bf16(sv[lb * 16 : (lb + 1) * 16].transpose(1, 2, 0))
+    return kp, vp
+
+
+@pytest.mark.parametrize("n_q,n_kv", [(4, 2), (4, 1), (2, 2), (3, 3)])
+def test_attention_matches_brute_force(n_q, n_kv):
+    rng = np.random.default_rng(10 + n_q * 7 + n_kv)
+    d = 16
+    cfg = _cfg(n_q=n_q, n_kv=n_kv, head_dim=d)
+    dec = [0, 1, 15, 16, 23]
+    pre, pre_prefix = [1, 7, 17], [0, 0, 20]
+    b = sw.batch_from_lengths(dec, pre, pre_prefix, seed=11)
+    totals = list(b.cached_lens() + b.q_lens())
+    seqs_k = [_bf16_exact(rng, (n, n_kv, d)) for n in totals]
+    seqs_v = [_bf16_exact(rng, (n, n_kv, d)) for n in totals]
+    kp, vp = _paged_pool_from_sequences(b, seqs_k, seqs_v, n_kv, d)
+    q = rng.standard_normal((b.n_tokens, n_q, d))
+    got = ol.attention_all(cfg, b, q, kp, vp)
+
+    # brute force: whole score matrix of the dense batch over the concatenated sequences,
+    # masked to same-request keys at or before the query position, softmax from scipy
+    owner_k = np.concatenate([np.full(n, r) for r, n in enumerate(totals)])
+    pos_k = np.concatenate([np.arange(n) for n in totals])
+    K = np.concatenate(seqs_k)
+    V = np.concatenate(seqs_v)
+    owner_q = np.concatenate([np.full(int(ql), r) for r, ql in enumerate(b.q_lens())])
+    pos_q = np.concatenate([np.arange(int(c), int(c) + int(ql)) for c, ql in zip(b.cached_lens(), b.q_lens())])
+    mask = (owner_q[:, None] == owner_k[None, :]) & (pos_k[None, :] <= pos_q[:, None])
+    want = np.zeros_like(got)
+    for h in range(n_q):
+        g = (h * n_kv) // n_q
+        s = np.einsum("td,kd->tk", q[:, h], K[:, g]) / math.sqrt(d)
+        s = np.where(mask, s, -np.inf)
+        want[:, h] = scipy.special.softmax(s, axis=1) @ V[:, g]
+    assert np.allclose(got, want, rtol=1e-10, atol=1e-12)
+
+
+def test_attention_special_cases():
+    d = 8
+    rng = np.random.default_rng(12)
+    # one key: output equals the value
+    v = rng.standard_normal((1, 1, d))
+    o = ol.attend(rng.standard_normal((1, 2, d)), rng.standard_normal((1, 1, d)), v, [0], 2, 1)
+    assert np.allclose(o[0, 0], v[0, 0]) and np.allclose(o[0, 1], v[0, 0])
+    # identical keys: uniform weights, output equals the mean of visible values
+    keys = np.repeat(rng.standard_normal((1, 1, d)), 9, axis=0)
+    vals = rng.standard_normal((9, 1, d))
+    o = ol.attend(rng.standard_normal((2, 1, d)), keys, vals, [4, 8], 1, 1)
+    assert np.allclose(o[0, 0], vals[:5, 0].mean(axis=0)) and np.allclose(o[1, 0], vals[:, 0].mean(axis=0))
+    # GQA with replicated KV heads equals MHA
+    q = rng.standard_normal((3, 4, d))
+    k2 = rng.standard_normal((6, 2, d))
+    v2 = rng.standard_normal((6, 2, d))
+    gqa = ol.attend(q, k2, v2, [3, 4, 5], 4, 2)
+    mha = ol.attend(q, np.repeat(k2, 2, axis=1), np.repeat(v2, 2, axis=1), [3, 4, 5], 4, 4)
+    assert np.allclose(gqa, mha, rtol=1e-14)
+
+
+# ----------------------------------------------------------------------------- whole layer
+
+
+def _tiny_inputs(seed=0, gain_jitter=0.1):
+    wl = sw.WORKLOADS["tiny"]
+    b = sw.make_batch("tiny", seed)
+    w = sw.make_weights(wl.shape, seed, gain_jitter=gain_jitter)
+    x = sw.make_x(wl.shape, b.n_tokens, seed)
+    kp, vp = sw.make_kv_pool(wl.shape, b.num_blocks, seed)
+    return wl.shape, b, w, x, kp, vp
+
+
+def test_layer_paged_equals_contiguous():
+    shape, b, w, x, kp, vp = _tiny_inputs(1)
+    ident = sw.make_batch("tiny", 1, shuffle=False)
+    assert np.array_equal(ident.decode_ctx, b.decode_ctx)
+    kp2 = np.zeros_like(kp)
+    vp2 = np.zeros_like(vp)
+    for r in range(b.n_requests):
+        for lb in range(b.max_blocks):
+            if b.block_table[r, lb] >= 0:
+                kp2[ident.block_table[r, lb]] = kp[b.block_table[r, lb]]
+                vp2[ident.block_table[r, lb]] = vp[b.block_table[r, lb]]
+    a = ol.layer_forward(shape, w, x, b, kp, vp)
+    c = ol.layer_forward(shape, w, x, ident, kp2, vp2)
+    assert np.array_equal(a["y"], c["y"])
+    for r in range(b.n_requests):
+        for lb in range(b.max_blocks):
+            if b.block_table[r, lb] >= 0:
+                assert np.array_equal(a["k_pool"][b.block_table[r, lb]], c["k_pool"][ident.block_table[r, lb]])
+                assert np.array_equal(a["v_pool"][b.block_table[r, lb]], c["v_pool"][ident.block_table[r, lb]])
+
+
+def test_layer_request_subset_invariance():
+    shape, b, w, x, kp, vp = _tiny_inputs(2)
+    full = ol.layer_forward(shape, w, x, b, kp, vp)
+    ranges = ol.request_ranges(b)
+    for subset in ([0, 5, 14], [3, 15], [1, 2, 4, 6, 8, 10, 12]):
+        sub = b.select(subset)
+        rows = np.concatenate([np.arange(ranges[r][0], ranges[r][1]) for r in sorted(subset)])
+        part = ol.layer_forward(shape, w, x[rows], sub, kp, vp)
+        assert np.allclose(part["y"], full["y"][rows], rtol=1e-12, atol=1e-12)
+        assert np.allclose(part["attn"], full["attn"][rows], rtol=1e-12, atol=1e-13)
+
+
+def test_layer_decode_equals_last_prefill_row():
+    # prefilling L tokens == prefilling L-1 tokens, then decoding the last one at ctx L-1
+    shape = sw.WORKLOADS["tiny"].shape
+    L = 21
+    w = sw.make_weights(shape, 3, gain_jitter=0.1)
+    x = sw.make_x(shape, L, 3)
+    one = sw.batch_from_lengths([], [L], seed=3, spare_blocks=0)
+    kp = np.zeros((one.num_blocks, shape.n_kv, 16, shape.head_dim), np.uint16)
+    vp = np.zeros((one.num_blocks, shape.n_kv, shape.head_dim, 16), np.uint16)
+    full = ol.layer_forward(shape, w, x, one, kp, vp)
+    first = sw.Batch(np.zeros(0, np.int32), np.array([L - 1], np.int32), np.zeros(1, np.int32),
+                     one.block_table, one.num_blocks)
+    part = ol.layer_forward(shape, w, x[: L - 1], first, kp, vp)
+    dec = sw.Batch(np.array([L - 1], np.int32), np.zeros(0, np.int32), np.zeros(0, np.int32),
+                   one.block_table, one.num_blocks)
+    last = ol.layer_forward(shape, w, x[L - 1 :], dec, part["k_pool"], part["v_pool"])
+    assert np.allclose(last["y"][0], full["y"][L - 1], rtol=1e-12, atol=1e-12)
+    assert np.array_equal(last["k_pool"], full["k_pool"])
+    assert np.array_equal(last["v_pool"], full["v_pool"])
+
+
+def test_layer_zero_projections_pass_residual_through():
+    shape, b, w, x, kp, vp = _tiny_inputs(4)
+    w0 = dict(w)
+    w0["w_o"] = np.zeros_like(w["w_o"])
+    w0["w_down"] = np.zeros_like(w["w_down"])
+    out = ol.layer_forward(shape, w0, x, b, kp, vp)
+    assert np.array_equal(out["y"], ol.bf16_to_f64(x))
+    w1 = dict(w)
+    w1["w_down"] = np.zeros_like(w["w_down"])
+    out1 = ol.layer_forward(shape, w1, x, b, kp, vp)
+    assert np.array_equal(out1["y"], out1["x1"])
+
+
+def test_layer_value_head_routes_to_attention_output():
+    # With W_q = 0 every score is 0, so each query averages the visible values; with the V
+    # rows of W_qkv selecting hidden features, attention output is a causal running mean.
+    shape, b, w, x, kp, vp = _tiny_inputs(5, gain_jitter=0.0)
+    H, d, nq, nkv = shape.hidden, shape.head_dim, shape.n_q, shape.n_kv
+    wq = ol.bf16_to_f64(w["w_qkv"]).copy()
+    wq[: nq * d] = 0.0
+    wq[(nq + nkv) * d :] = 0.0
+    for j in range(nkv * d):
+        wq[(nq + nkv) * d + j, j] = 1.0
+    w2 = dict(w)
+    w2["w_qkv"] = ol.f64_to_bf16(wq)
+    out = ol.layer_forward(shape, w2, x, b, kp, vp)
+    hv = ol.bf16_to_f64(ol.f64_to_bf16(out["h"][:, : nkv * d])).reshape(-1, nkv, d)
+    for r, (s, e, cached, qlen) in enumerate(ol.request_ranges(b)):
+        keys, vals = ol.gather_kv(kp, vp, b, 16, r, cached)
+        hist = vals  # cached values from the pool
+        seq = np.concatenate([hist, hv[s:e]])  # this iteration's values, as stored
+        for i in range(qlen):
+            want = seq[: cached + i + 1].mean(axis=0)  # [n_kv, d]
+            got = out["attn"][s + i].reshape(nq, d)
+            for h in range(nq):
+                assert np.allclose(got[h], want[h // (nq // nkv)], rtol=1e-12, atol=1e-12)
