@@ -30,6 +30,9 @@ Readings where the pages are silent (stated again in the design notes):
   pool after this iteration's writes, i.e. as stored (bfloat16).
 * SwiGLU: silu(gate) * up with gate = the first F rows of the gate/up weight.
 * bfloat16 rounding is round-to-nearest-even of the exact value.
+* Numeric model "bf16 storage, fp32 accumulation": tensors passed between operations are
+  stored in bfloat16; arithmetic inside an operation is exact here (float64, which bounds
+  any fp32 accumulation). ``storage="exact"`` drops the between-op rounding.
 
 Pool layout (the library's boundary layout): K [num_blocks, n_kv, BS, d] (token-major in a
 block), V [num_blocks, n_kv, d, BS] (dim-major in a block). Both hold bfloat16 bit patterns.
@@ -236,7 +239,12 @@ def attention_all(cfg, batch, q, k_pool, v_pool):
     return out
 
 
-def layer_forward(cfg, weights, x_bits, batch, k_pool, v_pool):
+def store_bf16(a):
+    """A tensor stored between operations in bfloat16: round to nearest even, as float64."""
+    return bf16_to_f64(f64_to_bf16(a))
+
+
+def layer_forward(cfg, weights, x_bits, batch, k_pool, v_pool, storage: str = "bf16"):
     """One decoder-layer iteration.
 
     cfg     object with hidden, n_q, n_kv, head_dim, ffn, block_size, rms_eps, rope_base
@@ -245,10 +253,18 @@ def layer_forward(cfg, weights, x_bits, batch, k_pool, v_pool):
     x_bits  bf16 bits [T, H]
     batch   object with decode_ctx, prefill_len, prefill_prefix, block_table, num_blocks
     k_pool  bf16 bits [num_blocks, n_kv, BS, d]; v_pool bf16 bits [num_blocks, n_kv, d, BS]
+    storage "bf16": the numeric model of a bf16-storage layer — every tensor handed from one
+            operation to the next (h, qkv, rotated q, attention output, x1, h2, a, y; K/V in
+            the pool) is stored in bfloat16 (round to nearest even) and everything inside an
+            operation is exact (float64). "exact": no rounding except the KV pool, which is
+            bfloat16 storage by definition.
 
     Returns a dict: y (float64 [T, H]), k_pool / v_pool (updated copies), the intermediates
     h, q, k, v (after rotary), attn [T, n_q d], x1, h2, a, and flops (int).
     """
+    if storage not in ("bf16", "exact"):
+        raise ValueError("storage must be 'bf16' or 'exact'")
+    st = store_bf16 if storage == "bf16" else (lambda a: a)
     H, nq, nkv, d, F = cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.ffn
     x = bf16_to_f64(x_bits)
     T = x.shape[0]
@@ -257,19 +273,19 @@ def layer_forward(cfg, weights, x_bits, batch, k_pool, v_pool):
     if pos.shape[0] != T:
         raise ValueError(f"batch holds {pos.shape[0]} tokens but x has {T} rows")
 
-    h = rmsnorm(x, W["g_attn"], cfg.rms_eps)
-    qkv = linear(h, W["w_qkv"])
+    h = st(rmsnorm(x, W["g_attn"], cfg.rms_eps))
+    qkv = st(linear(h, W["w_qkv"]))
     q = qkv[:, : nq * d].reshape(T, nq, d)
     k = qkv[:, nq * d : (nq + nkv) * d].reshape(T, nkv, d)
     v = qkv[:, (nq + nkv) * d :].reshape(T, nkv, d)
-    q = rope(q, pos, cfg.rope_base)
+    q = st(rope(q, pos, cfg.rope_base))
     k = rope(k, pos, cfg.rope_base)
     k_new, v_new = write_kv(k_pool, v_pool, batch, cfg.block_size, k, v)
-    attn = attention_all(cfg, batch, q, k_new, v_new).reshape(T, nq * d)
-    x1 = x + linear(attn, W["w_o"])
-    h2 = rmsnorm(x1, W["g_ffn"], cfg.rms_eps)
-    a = swiglu(linear(h2, W["w_gate_up"]), F)
-    y = x1 + linear(a, W["w_down"])
+    attn = st(attention_all(cfg, batch, q, k_new, v_new).reshape(T, nq * d))
+    x1 = st(x + linear(attn, W["w_o"]))
+    h2 = st(rmsnorm(x1, W["g_ffn"], cfg.rms_eps))
+    a = st(swiglu(linear(h2, W["w_gate_up"]), F))
+    y = st(x1 + linear(a, W["w_down"]))
     return {
         "y": y, "k_pool": k_new, "v_pool": v_new, "h": h, "q": q, "k": k, "v": v,
         "attn": attn, "x1": x1, "h2": h2, "a": a, "flops": layer_flops(cfg, batch),
