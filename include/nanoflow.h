@@ -1,0 +1,252 @@
+/*
+ * nanoflow.h — C ABI of libnanoflow: one nano-batched decoder-layer iteration on one
+ * MI355X (gfx950), plus the per-operation entry points, the profiler and the pipeline search.
+ *
+ * The layer (following NanoFlow, arXiv 2408.12757; summary page sections "The
+ * Intra-Device Parallelism Mechanism", "Auto-Search Stage I/II" and "The NanoFlow Runtime
+ * System"; slides "8B Pipeline Design" and "Batch Formation"):
+ *
+ *   h   = RMSNorm(x) * g_attn
+ *   qkv = h W_qkv^T ;  q, k <- rotary(q, k, position)      (KQV generation)
+ *   pool[slot(token)] <- k, v                                (paged KV append)
+ *   o   = causal GQA attention per request over the pool     (decode / prefill attention)
+ *   x1  = x + o W_o^T                                         (O projection)
+ *   h2  = RMSNorm(x1) * g_ffn
+ *   a   = silu(h2 W_gate^T) * (h2 W_up^T)                     (Up/Gate)
+ *   y   = x1 + a W_down^T                                      (Down)
+ *
+ * over a dense batch of decode requests (one new token each) followed by prefill chunks.
+ * The batch is split into nano-batches of consecutive tokens; each operation runs as one
+ * nano-operation per nano-batch, and nano-operations of different resource classes run
+ * concurrently on CU-masked HIP streams ordered by events. A nano-operation depends on
+ * another iff their parent operations are dependent and their token ranges intersect
+ * (summary page, "Auto-Search Stage I", constraints on dependencies).
+ *
+ * Conventions
+ *  - Every function returns nf_status: NF_OK (0) or a negative error code. No exception or
+ *    abort crosses the ABI. nf_last_error(ctx) gives a text for the last failure.
+ *  - Validation happens on the host before anything is enqueued: a failed call leaves
+ *    device memory untouched.
+ *  - "device" pointers are HIP device memory owned by the caller; "host" pointers are read
+ *    during the call only (their contents are copied), so they may be reused on return.
+ *  - Tensors are bfloat16 (bit patterns, round-to-nearest-even on every store) unless
+ *    stated otherwise, row-major, densely packed.
+ *  - Calls are asynchronous with respect to the host and ordered with respect to the
+ *    stream argument; calls that share one nf_ctx must be ordered (same stream, or
+ *    externally synchronized). One nf_ctx per host thread.
+ */
+#ifndef NANOFLOW_H
+#define NANOFLOW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t nf_status;
+
+enum {
+  NF_OK = 0,
+  NF_E_ARG = -1,               /* null pointer, non-positive size, unsupported shape          */
+  NF_E_BLOCK_RANGE = -2,       /* block id outside [0, num_blocks)                             */
+  NF_E_BLOCK_TABLE_SHORT = -3, /* a request needs more blocks than its table row holds         */
+  NF_E_SLOT_ALIAS = -4,        /* two new tokens would write the same KV slot                  */
+  NF_E_PLAN = -5,              /* plan bounds / op list invalid, or its order deadlocks        */
+  NF_E_CU_MASK = -6,           /* CU mask empty, or leaving an XCD without CUs                 */
+  NF_E_HIP = -7,               /* a HIP runtime call failed                                    */
+  NF_E_UNSUPPORTED = -8,       /* shape outside what the kernels implement                     */
+  NF_E_CAPACITY = -9,          /* batch larger than the context's workspace limits             */
+  NF_E_IO = -10                /* profile / plan file could not be read or written            */
+};
+
+/* CU masks cover the 256 CUs of an MI355X as 8 words of 32 bits. Bit i selects a CU of
+ * XCD (i mod 8); a mask must give every XCD the same, non-zero number of CUs. */
+#define NF_CU_MASK_WORDS 8
+
+typedef struct nf_ctx nf_ctx;  /* owns streams, events, metadata workspace, split-KV scratch */
+
+/* Layer shape. Supported: head_dim in {64, 128}; n_q_heads a multiple of n_kv_heads with
+ * n_q_heads / n_kv_heads <= 16; block_size 16; hidden, ffn and n_q_heads*head_dim multiples
+ * of 8. rms_eps and rope_base as in the model (1e-5 and 10000 for the LLaMA shapes). */
+typedef struct {
+  int32_t hidden, n_q_heads, n_kv_heads, head_dim, ffn, block_size;
+  float rms_eps, rope_base;
+} nf_layer_cfg;
+
+/* Weights, device, Linear layout [out, in]:
+ *   g_attn [hidden], g_ffn [hidden]                     RMSNorm gains
+ *   w_qkv  [(n_q + 2 n_kv) head_dim, hidden]            rows = q heads | k heads | v heads
+ *   w_o    [hidden, n_q head_dim]
+ *   w_gate_up [2 ffn, hidden]                           rows = gate (ffn) | up (ffn)
+ *   w_down [hidden, ffn]                                                                   */
+typedef struct {
+  const void *g_attn, *w_qkv, *w_o, *g_ffn, *w_gate_up, *w_down;
+} nf_layer_weights;
+
+/* Dense batch (slides, "Batch Formation": decode requests first, then prefill chunks).
+ * Request r < n_decode is a decode request: one new token at position decode_ctx_len[r],
+ * after decode_ctx_len[r] cached tokens. Request n_decode + j is a prefill chunk of
+ * prefill_len[j] >= 1 new tokens at positions prefill_prefix_len[j] + i (prefix NULL = 0).
+ * Tokens are laid out in request order; T = n_decode + sum(prefill_len).
+ * block_table (host, [n_decode + n_prefill][max_blocks], int32) maps logical block b of a
+ * request to its physical block ("LLM Inference Performance", PagedAttention; entries
+ * unused by a request are ignored, -1 by convention). block_table_dev is an optional device
+ * copy of the same table; when NULL the library uploads the host table each call.      */
+typedef struct {
+  int32_t n_decode;
+  const int32_t *decode_ctx_len;     /* host [n_decode], >= 0                        */
+  int32_t n_prefill;
+  const int32_t *prefill_len;        /* host [n_prefill], >= 1                        */
+  const int32_t *prefill_prefix_len; /* host [n_prefill] or NULL                      */
+  const int32_t *block_table;        /* host [n_req][max_blocks]                       */
+  int32_t max_blocks;
+  const int32_t *block_table_dev;    /* device copy or NULL                           */
+} nf_batch_desc;
+
+/* Paged KV pool of one layer, device, caller-owned:
+ *   k [num_blocks][n_kv][block_size][head_dim]   token-major within a block
+ *   v [num_blocks][n_kv][head_dim][block_size]   dim-major within a block
+ * Position p of request r lives in block table[r][p / block_size] at offset
+ * p % block_size. nf_layer_forward writes exactly the slots of this iteration's tokens.   */
+typedef struct {
+  void *k, *v;
+  int32_t num_blocks;
+} nf_kv_pool;
+
+/* Nano-operation kinds of the layer (slides, "8B Pipeline Design": KQV, decode attention,
+ * prefill attention, O, Up/Gate/Down). Norms, rotary and KV append ride in the dense ops. */
+enum {
+  NF_OP_KQV = 0,     /* RMSNorm_1 + KQV GEMM + rotary + KV append, rows of the nano-batch     */
+  NF_OP_DECATTN = 1, /* decode attention of the decode requests in the nano-batch             */
+  NF_OP_PFATTN = 2,  /* prefill attention of the prefill chunks whose last token is here      */
+  NF_OP_O = 3,       /* O GEMM + residual, rows of the nano-batch                              */
+  NF_OP_UGD = 4,     /* RMSNorm_2 + Up/Gate GEMM + SwiGLU + Down GEMM + residual               */
+  NF_OP_KINDS = 5
+};
+
+/* Nano-batch plan. bounds[0] = 0 < bounds[1] < ... < bounds[n_nano] = T (token offsets).
+ * Streams: n_streams (1..3) CU-masked streams; cu_masks holds n_streams * NF_CU_MASK_WORDS
+ * words (NULL = every stream uses the whole GPU). Nano-operations: n_ops entries given in
+ * issue order, each (op_kind, op_nano, op_stream); every (kind, nano) pair appears exactly
+ * once. A stream runs its nano-operations in the listed order; cross-stream order follows
+ * the range-intersection dependencies. A NULL plan runs one nano-batch sequentially on
+ * the caller's stream (the non-overlapped baseline).                                       */
+typedef struct {
+  int32_t n_nano;
+  const int32_t *bounds;
+  int32_t n_streams;
+  const uint32_t *cu_masks;
+  int32_t n_ops;
+  const int32_t *op_kind, *op_nano, *op_stream;
+} nf_plan;
+
+/* ---- context ---------------------------------------------------------------------------- */
+
+/* Create a context on HIP device `device`: default kernel variants, no streams yet (masked
+ * streams are created on first use and cached). Errors: NF_E_ARG, NF_E_HIP.                */
+nf_status nf_ctx_create(int device, nf_ctx **out);
+void nf_ctx_destroy(nf_ctx *ctx);
+const char *nf_last_error(const nf_ctx *ctx);
+/* Library version string, e.g. "nanoflow-mi355x 0.1". Never NULL. */
+const char *nf_version(void);
+
+/* ---- host-only helpers (no GPU needed) ------------------------------------------------------ */
+
+/* Validate a batch against a shape and a pool size, and derive each token's position and
+ * KV slot (slot = block * block_size + offset). pos_out / slot_out: host [T] or NULL.
+ * Returns the first error found: NF_E_ARG (bad lengths), NF_E_BLOCK_TABLE_SHORT,
+ * NF_E_BLOCK_RANGE, NF_E_SLOT_ALIAS. err_msg (host, err_cap bytes, may be NULL) receives
+ * a description.                                                                          */
+nf_status nf_batch_slots(const nf_layer_cfg *cfg, const nf_batch_desc *batch, int32_t num_blocks,
+                         int32_t *pos_out, int32_t *slot_out, char *err_msg, size_t err_cap);
+
+/* Dependency edges of a plan's nano-operations by range intersection. The edge list holds
+ * pairs (i, j): op j (index into the plan's op list) depends on op i. Capacity cap pairs;
+ * *n_edges receives the count (NF_E_CAPACITY if it exceeds cap). Also checks the plan:
+ * NF_E_PLAN when bounds or the op list are invalid, or when per-stream order plus
+ * dependencies contain a cycle. order_out (host [n_ops] or NULL) receives a global issue
+ * order consistent with both.                                                              */
+nf_status nf_plan_dependencies(const nf_batch_desc *batch, const nf_plan *plan, int32_t *edges,
+                               int32_t cap, int32_t *n_edges, int32_t *order_out, char *err_msg,
+                               size_t err_cap);
+
+/* ---- the layer --------------------------------------------------------------------------- */
+
+/* One decoder-layer iteration. x_in, y_out: device [T][hidden] (may alias: every row is
+ * read before it is overwritten). Writes y and this iteration's KV slots; everything else
+ * in the pool is left unchanged. Work is enqueued after all prior work on `stream` and
+ * `stream` waits for all of it on return (fork/join through events).
+ * Errors: NF_E_ARG, NF_E_UNSUPPORTED, NF_E_BLOCK_*, NF_E_SLOT_ALIAS, NF_E_PLAN,
+ * NF_E_CU_MASK, NF_E_CAPACITY, NF_E_HIP.                                                    */
+nf_status nf_layer_forward(nf_ctx *ctx, const nf_layer_cfg *cfg, const nf_layer_weights *w,
+                           const void *x_in, void *y_out, const nf_batch_desc *batch,
+                           nf_kv_pool *pool, const nf_plan *plan, void *stream);
+
+/* Intermediate buffers of the last nf_layer_forward call, for inspection (device pointers
+ * into the context's workspace, valid until the next call): which = 0 h, 1 qkv (q rotated),
+ * 2 attention output [T][n_q head_dim], 3 x1, 4 h2, 5 a [T][ffn]. Errors: NF_E_ARG.         */
+nf_status nf_debug_buffer(nf_ctx *ctx, int32_t which, void **ptr, size_t *bytes);
+
+/* ---- per-operation entry points (tests and profiler); one stream each -------------------- */
+
+/* C[m][n] = A[m][k] B[n][k]^T (+ epilogue). epilogue 0: store; 1: C = R + A B^T with R
+ * device [m][n] (may alias C); 2: SwiGLU — B holds 2n rows (gate | up) and
+ * C[m][n] = silu(A Bg^T) * (A Bu^T). variant: -1 = library choice, else a tile
+ * configuration index (see nf_gemm_variants). k and n multiples of 8. Errors: NF_E_ARG,
+ * NF_E_UNSUPPORTED, NF_E_HIP.                                                               */
+nf_status nf_op_gemm(nf_ctx *ctx, const void *A, const void *B, void *C, const void *R, int32_t m,
+                     int32_t n, int32_t k, int32_t epilogue, int32_t variant, void *stream);
+/* Number of GEMM tile configurations and, for index i, its tile (bm, bn, bk) into out3. */
+nf_status nf_gemm_variants(int32_t *count, int32_t index, int32_t *out3);
+
+/* out[r][:] = x[r] / sqrt(mean(x[r]^2) + eps) * g, rows r in [0, m), width n (mult. of 8). */
+nf_status nf_op_rmsnorm(nf_ctx *ctx, const void *x, const void *g, void *out, int32_t m, int32_t n,
+                        float eps, void *stream);
+
+/* Rotary embedding of q and k in qkv (device [T][(n_q+2n_kv) d], q rotated in place) at
+ * the batch's token positions, and append of k, v to the pool slots of the batch.           */
+nf_status nf_op_rope_kv_append(nf_ctx *ctx, const nf_layer_cfg *cfg, void *qkv,
+                               const nf_batch_desc *batch, nf_kv_pool *pool, void *stream);
+
+/* Attention of the batch's decode requests (decode = 1) or prefill chunks (decode = 0),
+ * reading q from qkv (device [T][(n_q+2n_kv) d], already rotated) and K/V from the pool
+ * (already holding this iteration's tokens); writes rows of out (device [T][n_q d]) that
+ * belong to those requests. kv_split_blocks: decode split-KV chunk in blocks (0 = default). */
+nf_status nf_op_attention(nf_ctx *ctx, const nf_layer_cfg *cfg, const void *qkv,
+                          const nf_batch_desc *batch, const nf_kv_pool *pool, void *out,
+                          int32_t decode, int32_t kv_split_blocks, void *stream);
+
+/* ---- profiler and pipeline search (summary page, "Kernel Profiling and Interference
+ *      Modeling"; "Auto-Search Stage I" and "Stage II") ----------------------------------- */
+
+/* Interference-free profile: for each nano-operation kind and each batch size b in
+ * step, 2 step, ..., max_tokens, time every kernel configuration on synthetic data shaped
+ * like `batch_template` scaled to b tokens, keep the best (D_best), and write JSON to
+ * out_json. Errors: NF_E_ARG, NF_E_IO, NF_E_HIP.                                             */
+nf_status nf_profile_ops(nf_ctx *ctx, const nf_layer_cfg *cfg, const nf_batch_desc *batch_template,
+                         int32_t num_blocks, int32_t step, int32_t max_tokens, const char *out_json);
+
+/* Pairwise interference: for each CU share R of the non-GEMM kernel in r_grid (n_r values in
+ * (0,1)), run a GEMM nano-op on a mask of (1-R) of the CUs and a decode-attention nano-op
+ * on a mask of R concurrently, and record each one's speed relative to its own best
+ * (P values). Writes JSON to out_json. Errors: NF_E_ARG, NF_E_IO, NF_E_HIP, NF_E_CU_MASK.   */
+nf_status nf_profile_interference(nf_ctx *ctx, const nf_layer_cfg *cfg,
+                                  const nf_batch_desc *batch_template, int32_t num_blocks,
+                                  const float *r_grid, int32_t n_r, const char *out_json);
+
+/* Two-stage search. Stage I: over nano-batch counts 1..max_nano (sizes multiples of
+ * `granularity` summing to T, no two ops of one class overlapping, no interference),
+ * minimize the makespan of the list schedule built from the D_best table. Stage II: fix
+ * that structure and choose the CU share R of the memory stream from the R->P table to
+ * minimize the makespan with interference. Input JSON as written by the profilers. Writes
+ * the plan as JSON into plan_json_out (host buffer, cap bytes). Errors: NF_E_ARG, NF_E_IO,
+ * NF_E_CAPACITY, NF_E_PLAN.                                                                  */
+nf_status nf_plan_search(const char *dbest_json, const char *rp_json, const nf_batch_desc *batch,
+                         int32_t max_nano, int32_t granularity, char *plan_json_out, size_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NANOFLOW_H */

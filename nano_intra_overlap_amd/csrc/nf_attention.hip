@@ -1,0 +1,330 @@
+// Paged causal GQA attention on gfx950 matrix cores: decode attention (memory-bound, one
+// query per request; NanoFlow summary page, memory-bound operations: decode attention
+// streams the per-request KV-cache) and prefill attention (compute-bound, causal within a
+// request; "Inside nano-vLLM", prefill batching keeps request boundaries).
+//
+// One wave owns 16 "columns" and streams 16-token KV blocks through the block table:
+//   decode : columns = the query heads sharing one KV head, one query per request
+//   prefill: columns = 16 consecutive queries of one query head
+// Per block: S^T[16 keys][16 cols] = K_blk Q^T with 16x16x32 bf16 MFMAs over head_dim,
+// an online softmax per column (base-2 exponent, running max and sum), then
+// O^T[d][16 cols] += V_blk^T P^T with 16x16x16 bf16 MFMAs. K is token-major within a block,
+// so a lane's 8 consecutive dims are one 16-byte load; V is dim-major within a block, so a
+// lane's 4 consecutive keys of one dim are one 8-byte load — both already in the operand
+// layout of the matrix instruction, no LDS transpose needed.
+//
+// Decode work is split along the KV sequence (split-KV): each wave takes at most 64
+// blocks of one request and one KV head; multi-chunk requests write unnormalised partial
+// outputs plus (max, sum) and a combine kernel merges them.
+#include "nf_internal.h"
+
+namespace nf {
+
+__device__ __forceinline__ float wave_max16(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum16(float v) {
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// State of one wave's 16 columns: running max m (log2 domain), partial sum l of this lane's
+// keys, and O^T accumulators (lane holds dims dc*16 + 4*grp + r of column lane%16).
+template <int D>
+struct AttnState {
+  float m;
+  float l;
+  f32x4 o[D / 16];
+};
+
+template <int D>
+struct KvFrag {
+  bf16x8 k[D / 32];
+  bf16x4 v[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ void load_block(KvFrag<D>& f, const bf16* __restrict__ kpool, const bf16* __restrict__ vpool,
+                                           int blk, int n_kv, int g, int i16, int grp) {
+  const bf16* kb = kpool + ((size_t)blk * n_kv + g) * (kBlock * D);
+  const bf16* vb = vpool + ((size_t)blk * n_kv + g) * (D * kBlock);
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) f.k[c] = *reinterpret_cast<const bf16x8*>(kb + i16 * D + c * 32 + grp * 8);
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc)
+    f.v[dc] = *reinterpret_cast<const bf16x4*>(vb + (dc * 16 + i16) * kBlock + grp * 4);
+}
+
+// Process one block whose first key is at sequence position key0. Column limit: key k is
+// visible to this lane's column iff k <= limit. Keys at or beyond n_keys hold no data:
+// their values are zeroed so that stale pool contents cannot leak through 0 * NaN.
+template <int D>
+__device__ __forceinline__ void attend_block(AttnState<D>& st, KvFrag<D>& f, const bf16x8* qf, int key0, int limit,
+                                             int n_keys, float scale_log2, int grp) {
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k[c], qf[c], s, 0, 0, 0);
+  const int kbase = key0 + grp * 4;
+  float sv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) sv[r] = (kbase + r <= limit) ? s[r] * scale_log2 : -INFINITY;
+  float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  bm = wave_max16(bm);
+  const float m_new = fmaxf(st.m, bm);
+  // a column whose keys are all masked so far keeps m = -inf; use 0 as the reference then
+  const float ref = (m_new == -INFINITY) ? 0.0f : m_new;
+  const float corr = exp2f(st.m - ref);
+  float p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) p[r] = exp2f(sv[r] - ref);
+  st.l = st.l * corr + ((p[0] + p[1]) + (p[2] + p[3]));
+  st.m = m_new;
+  bf16x4 pf;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) pf[r] = (bf16)p[r];
+  if (key0 + kBlock > n_keys) {
+    // partial last block: zero values of keys past the sequence end
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (kbase + r >= n_keys) f.v[dc][r] = (bf16)0.0f;
+  }
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc) {
+    st.o[dc] *= corr;
+    st.o[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(f.v[dc], pf, st.o[dc], 0, 0, 0);
+  }
+}
+
+// Walk logical blocks [b0, b1) of block-table row `bt_row`, with a prefetch of one block.
+template <int D>
+__device__ __forceinline__ void attend_range(AttnState<D>& st, const bf16x8* qf, const int32_t* __restrict__ bt_row,
+                                             int b0, int b1, const bf16* __restrict__ kpool,
+                                             const bf16* __restrict__ vpool, int n_kv, int g, int limit, int n_keys,
+                                             float scale_log2, int lane) {
+  const int i16 = lane & 15, grp = lane >> 4;
+  for (int base = b0; base < b1; base += 64) {
+    const int nb = min(64, b1 - base);
+    const int my_blk = (lane < nb) ? bt_row[base + lane] : 0;
+    KvFrag<D> cur, nxt;
+    load_block<D>(cur, kpool, vpool, __shfl(my_blk, 0, 64), n_kv, g, i16, grp);
+    for (int b = 0; b < nb; ++b) {
+      if (b + 1 < nb) load_block<D>(nxt, kpool, vpool, __shfl(my_blk, b + 1, 64), n_kv, g, i16, grp);
+      attend_block<D>(st, cur, qf, (base + b) * kBlock, limit, n_keys, scale_log2, grp);
+      cur = nxt;
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void init_state(AttnState<D>& st) {
+  st.m = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc) st.o[dc] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// ---------------------------------------------------------------------------------------
+// decode
+// ---------------------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_attn_kernel(const bf16* __restrict__ qkv, const bf16* __restrict__ kpool,
+                                                          const bf16* __restrict__ vpool,
+                                                          const int32_t* __restrict__ block_table, int max_blocks,
+                                                          const DecodeItem* __restrict__ items, int n_items,
+                                                          float* __restrict__ part_o, float* __restrict__ part_ml,
+                                                          bf16* __restrict__ out, int n_q, int n_kv, float scale_log2) {
+  const int lane = threadIdx.x & 63;
+  const int wg = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int item_idx = wg / n_kv;
+  const int g = wg % n_kv;
+  if (item_idx >= n_items) return;
+  const DecodeItem it = items[item_idx];
+  const int G = n_q / n_kv;
+  const int i16 = lane & 15, grp = lane >> 4;
+  const int width = (n_q + 2 * n_kv) * D;
+
+  bf16x8 qf[D / 32];
+  {
+    const bf16* qrow = qkv + (size_t)it.token * width + (size_t)(g * G + i16) * D;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      if (i16 < G) {
+        qf[c] = *reinterpret_cast<const bf16x8*>(qrow + c * 32 + grp * 8);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qf[c][j] = (bf16)0.0f;
+      }
+    }
+  }
+  AttnState<D> st;
+  init_state<D>(st);
+  attend_range<D>(st, qf, block_table + (size_t)it.req * max_blocks, it.blk_begin, it.blk_end, kpool, vpool, n_kv, g,
+                  it.n_keys - 1, it.n_keys, scale_log2, lane);
+  const float l = wave_sum16(st.l);
+  if (it.part < 0) {
+    if (i16 < G) {
+      const float inv = 1.0f / l;
+      bf16* orow = out + (size_t)it.token * n_q * D + (size_t)(g * G + i16) * D;
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) {
+        bf16x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = (bf16)(st.o[dc][r] * inv);
+        *reinterpret_cast<bf16x4*>(orow + dc * 16 + grp * 4) = o;
+      }
+    }
+  } else {
+    if (i16 < G) {
+      const size_t pbase = ((size_t)it.part * n_kv + g) * G + i16;
+      float* po = part_o + pbase * D;
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) *reinterpret_cast<f32x4*>(po + dc * 16 + grp * 4) = st.o[dc];
+      if (grp == 0) {
+        part_ml[pbase * 2 + 0] = st.m;
+        part_ml[pbase * 2 + 1] = l;
+      }
+    }
+  }
+}
+
+// Merge split-KV partials: o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(const CombineItem* __restrict__ items, int n_items,
+                                                             const float* __restrict__ part_o,
+                                                             const float* __restrict__ part_ml, bf16* __restrict__ out,
+                                                             int n_q, int n_kv) {
+  const int lane = threadIdx.x & 63;
+  const int wg = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int item_idx = wg / n_kv;
+  const int g = wg % n_kv;
+  if (item_idx >= n_items) return;
+  const CombineItem it = items[item_idx];
+  const int G = n_q / n_kv;
+  for (int e = lane; e < G * D; e += 64) {
+    const int h = e / D, dd = e % D;
+    float M = -INFINITY;
+    for (int p = 0; p < it.n_parts; ++p)
+      M = fmaxf(M, part_ml[(((size_t)(it.part_begin + p) * n_kv + g) * G + h) * 2]);
+    float L = 0.0f, acc = 0.0f;
+    for (int p = 0; p < it.n_parts; ++p) {
+      const size_t pb = ((size_t)(it.part_begin + p) * n_kv + g) * G + h;
+      const float wgt = exp2f(part_ml[pb * 2] - M);
+      L += wgt * part_ml[pb * 2 + 1];
+      acc += wgt * part_o[pb * D + dd];
+    }
+    out[(size_t)it.token * n_q * D + (size_t)(g * G + h) * D + dd] = (bf16)(acc / L);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// prefill
+// ---------------------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_attn_kernel(const bf16* __restrict__ qkv, const bf16* __restrict__ kpool,
+                                                           const bf16* __restrict__ vpool,
+                                                           const int32_t* __restrict__ block_table, int max_blocks,
+                                                           const PrefillItem* __restrict__ items, int n_items,
+                                                           bf16* __restrict__ out, int n_q, int n_kv, float scale_log2) {
+  const int lane = threadIdx.x & 63;
+  const int wg = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int item_idx = wg / n_q;
+  const int h = wg % n_q;
+  if (item_idx >= n_items) return;
+  const PrefillItem it = items[item_idx];
+  const int G = n_q / n_kv;
+  const int g = h / G;
+  const int i16 = lane & 15, grp = lane >> 4;
+  const int width = (n_q + 2 * n_kv) * D;
+  const int j = it.q_begin + i16;  // query of this lane's column
+  const bool valid = j < it.q_len;
+
+  bf16x8 qf[D / 32];
+  {
+    const bf16* qrow = qkv + (size_t)(it.token0 + (valid ? j : 0)) * width + (size_t)h * D;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      if (valid) {
+        qf[c] = *reinterpret_cast<const bf16x8*>(qrow + c * 32 + grp * 8);
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) qf[c][jj] = (bf16)0.0f;
+      }
+    }
+  }
+  const int n_keys = it.prefix + it.q_len;                       // keys of the request
+  const int last_q = min(it.q_begin + 16, it.q_len) - 1;         // last valid query of the tile
+  const int tile_keys = it.prefix + last_q + 1;                  // keys any column can see
+  const int limit = valid ? it.prefix + j : it.prefix + last_q;  // causal limit of this column
+  AttnState<D> st;
+  init_state<D>(st);
+  attend_range<D>(st, qf, block_table + (size_t)it.req * max_blocks, 0, (tile_keys + kBlock - 1) / kBlock, kpool,
+                  vpool, n_kv, g, limit, n_keys, scale_log2, lane);
+  const float l = wave_sum16(st.l);
+  if (valid) {
+    const float inv = 1.0f / l;
+    bf16* orow = out + (size_t)(it.token0 + j) * n_q * D + (size_t)h * D;
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) {
+      bf16x4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = (bf16)(st.o[dc][r] * inv);
+      *reinterpret_cast<bf16x4*>(orow + dc * 16 + grp * 4) = o;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+
+hipError_t launch_decode_attn(const bf16* qkv, const bf16* kpool, const bf16* vpool, const int32_t* block_table,
+                              int max_blocks, const DecodeItem* items, int n_items, const CombineItem* combines,
+                              int n_combines, float* part_o, float* part_ml, bf16* out, int n_q, int n_kv, int d,
+                              hipStream_t s) {
+  if (n_items <= 0) return hipSuccess;
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)d);
+  const int waves = n_items * n_kv;
+  const int grid = (waves + 3) / 4;
+  if (d == 128)
+    hipLaunchKernelGGL(decode_attn_kernel<128>, dim3(grid), dim3(256), 0, s, qkv, kpool, vpool, block_table,
+                       max_blocks, items, n_items, part_o, part_ml, out, n_q, n_kv, scale_log2);
+  else if (d == 64)
+    hipLaunchKernelGGL(decode_attn_kernel<64>, dim3(grid), dim3(256), 0, s, qkv, kpool, vpool, block_table,
+                       max_blocks, items, n_items, part_o, part_ml, out, n_q, n_kv, scale_log2);
+  else
+    return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n_combines <= 0) return e;
+  const int cgrid = (n_combines * n_kv + 3) / 4;
+  if (d == 128)
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(cgrid), dim3(256), 0, s, combines, n_combines, part_o,
+                       part_ml, out, n_q, n_kv);
+  else
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(cgrid), dim3(256), 0, s, combines, n_combines, part_o,
+                       part_ml, out, n_q, n_kv);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_attn(const bf16* qkv, const bf16* kpool, const bf16* vpool, const int32_t* block_table,
+                               int max_blocks, const PrefillItem* items, int n_items, bf16* out, int n_q, int n_kv,
+                               int d, hipStream_t s) {
+  if (n_items <= 0) return hipSuccess;
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)d);
+  const int grid = (n_items * n_q + 3) / 4;
+  if (d == 128)
+    hipLaunchKernelGGL(prefill_attn_kernel<128>, dim3(grid), dim3(256), 0, s, qkv, kpool, vpool, block_table,
+                       max_blocks, items, n_items, out, n_q, n_kv, scale_log2);
+  else if (d == 64)
+    hipLaunchKernelGGL(prefill_attn_kernel<64>, dim3(grid), dim3(256), 0, s, qkv, kpool, vpool, block_table,
+                       max_blocks, items, n_items, out, n_q, n_kv, scale_log2);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace nf

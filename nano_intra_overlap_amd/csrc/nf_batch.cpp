@@ -1,0 +1,386 @@
+// Host-side batch layout and nano-operation DAG (pure C++, no GPU).
+//
+// Batch layout: decode requests first (one token each), then prefill chunks (slides,
+// "Batch Formation"). Token t of request r sits at position cached_r + (t - t0_r) and its
+// K/V go to slot table[r][pos / 16] * 16 + pos % 16 ("Inside nano-vLLM": slot mapping;
+// "LLM Inference Performance": PagedAttention block table).
+//
+// Dependencies: nano-operation B depends on A iff their parent operations are dependent
+// and their token ranges intersect (NanoFlow summary page, "Auto-Search Stage I",
+// constraints on dependencies). Parent graph of the layer: KQV -> decode attention,
+// KQV -> prefill attention, both attentions -> O, O -> UGD. A prefill attention nano-op
+// owns the chunks whose last token lies in its nano-batch, and its range is the union of
+// those chunks' rows, so it waits for every KQV nano-op that produced part of them.
+#include "nf_batch.h"
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+
+namespace nf {
+
+static std::string fmt(const char* f, long a = 0, long b = 0, long c = 0) {
+  char buf[256];
+  snprintf(buf, sizeof buf, f, a, b, c);
+  return buf;
+}
+
+nf_status check_cfg(const nf_layer_cfg& c, std::string& err) {
+  if (c.hidden <= 0 || c.n_q_heads <= 0 || c.n_kv_heads <= 0 || c.head_dim <= 0 || c.ffn <= 0) {
+    err = "layer shape has a non-positive size";
+    return NF_E_ARG;
+  }
+  if (c.block_size != 16) {
+    err = fmt("block_size %ld unsupported (16 only)", c.block_size);
+    return NF_E_UNSUPPORTED;
+  }
+  if (c.head_dim != 64 && c.head_dim != 128) {
+    err = fmt("head_dim %ld unsupported (64 or 128)", c.head_dim);
+    return NF_E_UNSUPPORTED;
+  }
+  if (c.n_q_heads % c.n_kv_heads != 0 || c.n_q_heads / c.n_kv_heads > 16) {
+    err = fmt("n_q_heads %ld / n_kv_heads %ld must be an integer <= 16", c.n_q_heads, c.n_kv_heads);
+    return NF_E_UNSUPPORTED;
+  }
+  if (c.hidden % 8 || c.ffn % 8) {
+    err = "hidden and ffn must be multiples of 8";
+    return NF_E_UNSUPPORTED;
+  }
+  if (!(c.rms_eps >= 0.0f) || !(c.rope_base > 0.0f)) {
+    err = "rms_eps must be >= 0 and rope_base > 0";
+    return NF_E_ARG;
+  }
+  return NF_OK;
+}
+
+nf_status build_layout(const nf_layer_cfg& cfg, const nf_batch_desc& b, int32_t num_blocks, BatchLayout& L,
+                       std::string& err) {
+  const int32_t BS = cfg.block_size;
+  if (b.n_decode < 0 || b.n_prefill < 0) {
+    err = "negative request count";
+    return NF_E_ARG;
+  }
+  if ((b.n_decode > 0 && !b.decode_ctx_len) || (b.n_prefill > 0 && !b.prefill_len)) {
+    err = "null length array";
+    return NF_E_ARG;
+  }
+  const int32_t n_req = b.n_decode + b.n_prefill;
+  if (n_req > 0 && (!b.block_table || b.max_blocks <= 0)) {
+    err = "null block table or max_blocks <= 0";
+    return NF_E_ARG;
+  }
+  if (num_blocks <= 0) {
+    err = "pool holds no blocks";
+    return NF_E_ARG;
+  }
+  L.req.clear();
+  L.req.reserve(n_req);
+  int64_t t = 0;
+  for (int32_t r = 0; r < n_req; ++r) {
+    ReqInfo ri;
+    ri.decode = r < b.n_decode;
+    int64_t cached, qlen;
+    if (ri.decode) {
+      cached = b.decode_ctx_len[r];
+      qlen = 1;
+      if (cached < 0) {
+        err = fmt("decode request %ld: context length %ld < 0", r, (long)cached);
+        return NF_E_ARG;
+      }
+    } else {
+      const int32_t j = r - b.n_decode;
+      qlen = b.prefill_len[j];
+      cached = b.prefill_prefix_len ? b.prefill_prefix_len[j] : 0;
+      if (qlen < 1 || cached < 0) {
+        err = fmt("prefill chunk %ld: length %ld / prefix %ld invalid", j, (long)qlen, (long)cached);
+        return NF_E_ARG;
+      }
+    }
+    const int64_t n_keys = cached + qlen;
+    const int64_t need = (n_keys + BS - 1) / BS;
+    if (need > b.max_blocks) {
+      err = fmt("request %ld needs %ld blocks but its table row holds %ld", r, (long)need, b.max_blocks);
+      return NF_E_BLOCK_TABLE_SHORT;
+    }
+    const int32_t* row = b.block_table + (size_t)r * b.max_blocks;
+    for (int64_t i = 0; i < need; ++i) {
+      if (row[i] < 0 || row[i] >= num_blocks) {
+        err = fmt("request %ld: logical block %ld maps to %ld, outside the pool", r, (long)i, row[i]);
+        return NF_E_BLOCK_RANGE;
+      }
+    }
+    if (t + qlen > INT32_MAX / 2 || n_keys > INT32_MAX / 2) {
+      err = "batch too large";
+      return NF_E_CAPACITY;
+    }
+    ri.t0 = (int32_t)t;
+    ri.t1 = (int32_t)(t + qlen);
+    ri.cached = (int32_t)cached;
+    ri.n_keys = (int32_t)n_keys;
+    L.req.push_back(ri);
+    t += qlen;
+  }
+  L.T = (int32_t)t;
+  L.pos.resize(L.T);
+  L.slot.resize(L.T);
+  for (int32_t r = 0; r < n_req; ++r) {
+    const ReqInfo& ri = L.req[r];
+    const int32_t* row = b.block_table + (size_t)r * b.max_blocks;
+    for (int32_t tt = ri.t0; tt < ri.t1; ++tt) {
+      const int32_t p = ri.cached + (tt - ri.t0);
+      L.pos[tt] = p;
+      L.slot[tt] = row[p / BS] * BS + p % BS;
+    }
+  }
+  // every new token must own a distinct slot
+  std::vector<int32_t> s(L.slot);
+  std::sort(s.begin(), s.end());
+  for (size_t i = 1; i < s.size(); ++i) {
+    if (s[i] == s[i - 1]) {
+      err = fmt("two new tokens write KV slot %ld (block %ld)", s[i], s[i] / BS);
+      return NF_E_SLOT_ALIAS;
+    }
+  }
+  return NF_OK;
+}
+
+bool parent_depends(int32_t a, int32_t b) {
+  switch (b) {
+    case NF_OP_DECATTN:
+    case NF_OP_PFATTN: return a == NF_OP_KQV;
+    case NF_OP_O: return a == NF_OP_DECATTN || a == NF_OP_PFATTN;
+    case NF_OP_UGD: return a == NF_OP_O;
+    default: return false;
+  }
+}
+
+static bool intersects(const NanoOp& a, const NanoOp& b) {
+  for (auto& x : a.rows)
+    for (auto& y : b.rows)
+      if (std::max(x.first, y.first) < std::min(x.second, y.second)) return true;
+  return false;
+}
+
+nf_status build_plan_graph(const BatchLayout& L, const nf_plan* plan, PlanGraph& g, std::string& err) {
+  g = PlanGraph();
+  const int32_t T = L.T;
+  std::vector<int32_t> kinds, nanos, streams;
+  if (!plan) {
+    g.n_nano = 1;
+    g.n_streams = 1;
+    g.bounds = {0, T};
+    for (int32_t k = 0; k < NF_OP_KINDS; ++k) {
+      kinds.push_back(k);
+      nanos.push_back(0);
+      streams.push_back(0);
+    }
+  } else {
+    if (plan->n_nano < 1 || !plan->bounds) {
+      err = "plan needs n_nano >= 1 and bounds";
+      return NF_E_PLAN;
+    }
+    g.n_nano = plan->n_nano;
+    g.bounds.assign(plan->bounds, plan->bounds + plan->n_nano + 1);
+    if (g.bounds.front() != 0 || g.bounds.back() != T) {
+      err = fmt("plan bounds must run from 0 to T=%ld", T);
+      return NF_E_PLAN;
+    }
+    for (int32_t j = 0; j < g.n_nano; ++j)
+      if (g.bounds[j + 1] <= g.bounds[j]) {
+        err = fmt("plan bounds not increasing at nano-batch %ld", j);
+        return NF_E_PLAN;
+      }
+    if (plan->n_streams < 1 || plan->n_streams > 3) {
+      err = "plan needs 1..3 streams";
+      return NF_E_PLAN;
+    }
+    g.n_streams = plan->n_streams;
+    if (plan->n_ops != NF_OP_KINDS * g.n_nano || !plan->op_kind || !plan->op_nano || !plan->op_stream) {
+      err = fmt("plan lists %ld ops, expected %ld", plan->n_ops, NF_OP_KINDS * g.n_nano);
+      return NF_E_PLAN;
+    }
+    std::vector<char> seen(NF_OP_KINDS * g.n_nano, 0);
+    for (int32_t i = 0; i < plan->n_ops; ++i) {
+      const int32_t k = plan->op_kind[i], j = plan->op_nano[i], s = plan->op_stream[i];
+      if (k < 0 || k >= NF_OP_KINDS || j < 0 || j >= g.n_nano || s < 0 || s >= g.n_streams) {
+        err = fmt("plan op %ld out of range", i);
+        return NF_E_PLAN;
+      }
+      if (seen[k * g.n_nano + j]++) {
+        err = fmt("plan lists op kind %ld of nano-batch %ld twice", k, j);
+        return NF_E_PLAN;
+      }
+      kinds.push_back(k);
+      nanos.push_back(j);
+      streams.push_back(s);
+    }
+  }
+  // nano-batch of a token row
+  auto nano_of = [&](int32_t t) {
+    return (int32_t)(std::upper_bound(g.bounds.begin(), g.bounds.end(), t) - g.bounds.begin()) - 1;
+  };
+  const int32_t n_ops = (int32_t)kinds.size();
+  g.ops.resize(n_ops);
+  for (int32_t i = 0; i < n_ops; ++i) {
+    NanoOp& op = g.ops[i];
+    op.kind = kinds[i];
+    op.nano = nanos[i];
+    op.stream = streams[i];
+    const int32_t lo = g.bounds[op.nano], hi = g.bounds[op.nano + 1];
+    switch (op.kind) {
+      case NF_OP_KQV:
+      case NF_OP_O:
+      case NF_OP_UGD: op.rows.push_back({lo, hi}); break;
+      case NF_OP_DECATTN: {
+        // decode requests have one token each and come first: request r = token r
+        int32_t r0 = lo, r1 = hi;
+        int32_t n_dec = 0;
+        while (n_dec < (int32_t)L.req.size() && L.req[n_dec].decode) ++n_dec;
+        r0 = std::min(r0, n_dec);
+        r1 = std::min(r1, n_dec);
+        op.r0 = r0;
+        op.r1 = r1;
+        if (r1 > r0) op.rows.push_back({r0, r1});
+        break;
+      }
+      case NF_OP_PFATTN: {
+        for (int32_t r = 0; r < (int32_t)L.req.size(); ++r) {
+          const ReqInfo& ri = L.req[r];
+          if (ri.decode) continue;
+          if (nano_of(ri.t1 - 1) == op.nano) {
+            op.prefill_reqs.push_back(r);
+            op.rows.push_back({ri.t0, ri.t1});
+          }
+        }
+        break;
+      }
+    }
+    op.empty = op.rows.empty();
+  }
+  // dependencies by parent dependency + range intersection
+  g.deps.assign(n_ops, {});
+  for (int32_t j = 0; j < n_ops; ++j)
+    for (int32_t i = 0; i < n_ops; ++i)
+      if (i != j && parent_depends(g.ops[i].kind, g.ops[j].kind) && intersects(g.ops[i], g.ops[j]))
+        g.deps[j].push_back(i);
+  // global order: Kahn's algorithm over dependency edges plus per-stream order edges,
+  // preferring the plan's listed position
+  std::vector<std::vector<int32_t>> succ(n_ops);
+  std::vector<int32_t> indeg(n_ops, 0);
+  for (int32_t j = 0; j < n_ops; ++j)
+    for (int32_t i : g.deps[j]) {
+      succ[i].push_back(j);
+      indeg[j]++;
+    }
+  std::vector<int32_t> last(g.n_streams, -1);
+  for (int32_t i = 0; i < n_ops; ++i) {
+    const int32_t s = g.ops[i].stream;
+    if (last[s] >= 0) {
+      succ[last[s]].push_back(i);
+      indeg[i]++;
+    }
+    last[s] = i;
+  }
+  std::vector<char> done(n_ops, 0);
+  g.order.clear();
+  for (int32_t step = 0; step < n_ops; ++step) {
+    int32_t pick = -1;
+    for (int32_t i = 0; i < n_ops; ++i)
+      if (!done[i] && indeg[i] == 0) {
+        pick = i;
+        break;
+      }
+    if (pick < 0) {
+      err = "plan order deadlocks: a stream's order contradicts a dependency";
+      return NF_E_PLAN;
+    }
+    done[pick] = 1;
+    g.order.push_back(pick);
+    for (int32_t j : succ[pick]) indeg[j]--;
+  }
+  return NF_OK;
+}
+
+}  // namespace nf
+
+// ---------------------------------------------------------------------------------------
+// host-only ABI entry points
+// ---------------------------------------------------------------------------------------
+
+static void put_err(char* dst, size_t cap, const std::string& s) {
+  if (!dst || cap == 0) return;
+  const size_t n = std::min(cap - 1, s.size());
+  memcpy(dst, s.data(), n);
+  dst[n] = 0;
+}
+
+extern "C" nf_status nf_batch_slots(const nf_layer_cfg* cfg, const nf_batch_desc* batch, int32_t num_blocks,
+                                    int32_t* pos_out, int32_t* slot_out, char* err_msg, size_t err_cap) {
+  std::string err;
+  if (!cfg || !batch) {
+    put_err(err_msg, err_cap, "null argument");
+    return NF_E_ARG;
+  }
+  nf_status st = nf::check_cfg(*cfg, err);
+  nf::BatchLayout L;
+  if (st == NF_OK) st = nf::build_layout(*cfg, *batch, num_blocks, L, err);
+  if (st != NF_OK) {
+    put_err(err_msg, err_cap, err);
+    return st;
+  }
+  if (pos_out) memcpy(pos_out, L.pos.data(), sizeof(int32_t) * L.T);
+  if (slot_out) memcpy(slot_out, L.slot.data(), sizeof(int32_t) * L.T);
+  put_err(err_msg, err_cap, "");
+  return NF_OK;
+}
+
+extern "C" nf_status nf_plan_dependencies(const nf_batch_desc* batch, const nf_plan* plan, int32_t* edges, int32_t cap,
+                                          int32_t* n_edges, int32_t* order_out, char* err_msg, size_t err_cap) {
+  std::string err;
+  if (!batch || !n_edges) {
+    put_err(err_msg, err_cap, "null argument");
+    return NF_E_ARG;
+  }
+  // layout without a pool: token ranges only (blocks are not needed for the DAG)
+  nf::BatchLayout L;
+  int64_t t = 0;
+  for (int32_t r = 0; r < batch->n_decode + batch->n_prefill; ++r) {
+    nf::ReqInfo ri;
+    ri.decode = r < batch->n_decode;
+    const int32_t q = ri.decode ? 1 : batch->prefill_len[r - batch->n_decode];
+    if (q < 1) {
+      put_err(err_msg, err_cap, "prefill length < 1");
+      return NF_E_ARG;
+    }
+    ri.t0 = (int32_t)t;
+    ri.t1 = (int32_t)(t + q);
+    ri.cached = 0;
+    ri.n_keys = q;
+    L.req.push_back(ri);
+    t += q;
+  }
+  L.T = (int32_t)t;
+  nf::PlanGraph g;
+  nf_status st = nf::build_plan_graph(L, plan, g, err);
+  if (st != NF_OK) {
+    put_err(err_msg, err_cap, err);
+    return st;
+  }
+  int32_t n = 0;
+  for (int32_t j = 0; j < (int32_t)g.deps.size(); ++j)
+    for (int32_t i : g.deps[j]) {
+      if (n < cap && edges) {
+        edges[2 * n] = i;
+        edges[2 * n + 1] = j;
+      }
+      ++n;
+    }
+  *n_edges = n;
+  if (order_out) memcpy(order_out, g.order.data(), sizeof(int32_t) * g.order.size());
+  if (n > cap) {
+    put_err(err_msg, err_cap, "edge capacity too small");
+    return NF_E_CAPACITY;
+  }
+  put_err(err_msg, err_cap, "");
+  return NF_OK;
+}

@@ -1,0 +1,65 @@
+// Host-side batch metadata and nano-operation DAG (no GPU calls). Not part of the ABI.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/nanoflow.h"
+
+namespace nf {
+
+struct DecodeItem;
+struct CombineItem;
+struct PrefillItem;
+
+// One request of the dense batch, in dense-batch order (decodes, then prefill chunks).
+struct ReqInfo {
+  int32_t t0, t1;    // token rows [t0, t1)
+  int32_t cached;    // tokens already in the pool
+  int32_t n_keys;    // cached + (t1 - t0)
+  bool decode;
+};
+
+// Everything derived on the host from (cfg, batch, pool size), before any enqueue.
+struct BatchLayout {
+  int32_t T = 0;
+  std::vector<ReqInfo> req;
+  std::vector<int32_t> pos, slot;  // per token
+};
+
+// Validate and lay out a batch. Returns NF_OK or the first error, with a message.
+nf_status build_layout(const nf_layer_cfg& cfg, const nf_batch_desc& b, int32_t num_blocks, BatchLayout& out,
+                       std::string& err);
+
+// Validate the layer shape against what the kernels implement.
+nf_status check_cfg(const nf_layer_cfg& cfg, std::string& err);
+
+// A nano-operation of a plan with the token rows it reads/writes (its "range").
+struct NanoOp {
+  int32_t kind, nano, stream;
+  // rows of the op: one interval for dense ops and for decode attention (its decode rows);
+  // prefill attention: the union of its requests' rows, stored as intervals
+  std::vector<std::pair<int32_t, int32_t>> rows;
+  // decode attention: decode requests [r0, r1); prefill attention: list of prefill requests
+  int32_t r0 = 0, r1 = 0;
+  std::vector<int32_t> prefill_reqs;
+  bool empty = false;
+};
+
+struct PlanGraph {
+  int32_t n_nano = 1, n_streams = 1;
+  std::vector<int32_t> bounds;
+  std::vector<NanoOp> ops;                 // in the plan's listed order
+  std::vector<std::vector<int32_t>> deps;  // deps[j] = ops j depends on (range intersection)
+  std::vector<int32_t> order;              // global issue order (topological)
+};
+
+// Build nano-ops, dependencies and a global order from a plan (NULL plan = one nano-batch,
+// one stream, kinds in layer order). Checks bounds, the op list and acyclicity.
+nf_status build_plan_graph(const BatchLayout& L, const nf_plan* plan, PlanGraph& g, std::string& err);
+
+// Parent-operation dependency of the layer (does kind b consume a product of kind a?).
+bool parent_depends(int32_t a, int32_t b);
+
+}  // namespace nf

@@ -1,0 +1,270 @@
+// bf16 GEMM on gfx950 matrix cores: C[m][n] = A[m][k] * B[n][k]^T with fp32 accumulation
+// and a fused epilogue (plain store, residual add, or SwiGLU over paired gate/up rows).
+//
+// These are the compute-bound dense nano-operations of the layer (KQV, O, Up/Gate, Down;
+// NanoFlow summary page, "The Intra-Device Parallelism Mechanism": dense projections are
+// compute-bound GEMMs). Shapes: A = activations (row-major, k contiguous), B = a Linear
+// weight [out][in] (k contiguous), so both operands stream along k.
+//
+// Structure: a workgroup of 4 waves computes a BM x BN tile; waves form a 2 x 2 grid, each
+// owning a (BM/2) x (BN/2) sub-tile built from 32x32x16 bf16 MFMAs. k advances in slabs of
+// BK staged through LDS (padded rows, conflict-free 16-byte fragment reads), double
+// buffered: the next slab is fetched into registers while the current one is multiplied.
+// Tiles are ordered so that consecutive tiles share rows of A and columns of B, and that
+// consecutive tiles land on the same XCD (workgroups are dealt round-robin to the 8 XCDs,
+// each with its own L2).
+#include "nf_internal.h"
+
+namespace nf {
+
+enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+template <int BM, int BN, int BK, int EPI>
+__global__ __launch_bounds__(256) void gemm_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B,
+                                                   bf16* C, const bf16* R, int M, int N, int K,
+                                                   int tiles_m, int tiles_n, int per_xcd) {
+  constexpr int LDK = BK + 8;            // padded LDS row (bf16 elements)
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int CH_A = BM * BK / 8 / 256;  // 16-byte chunks per thread
+  constexpr int CH_B = BN * BK / 8 / 256;
+  constexpr int KC = BK / 8;               // chunks per row
+  static_assert(CH_A >= 1 && CH_B >= 1, "tile too small");
+  static_assert(EPI != EPI_SWIGLU || (WTN % 64) == 0, "SwiGLU needs gate/up pairs of 32 columns");
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  bf16* As = reinterpret_cast<bf16*>(smem_raw);
+  bf16* Bs = As + 2 * BM * LDK;
+
+  // ---- tile index: XCD-contiguous, grouped along m -------------------------------------
+  const int w = blockIdx.x;
+  const int t = (w % kNumXcd) * per_xcd + (w / kNumXcd);
+  const int ntiles = tiles_m * tiles_n;
+  if (t >= ntiles) return;
+  constexpr int GM = 8;
+  const int group = t / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gm = min(GM, tiles_m - first_m);
+  const int in_group = t % (GM * tiles_n);
+  const int tile_m = first_m + in_group % gm;
+  const int tile_n = in_group / gm;
+  const int m0 = tile_m * BM;
+  // SwiGLU: the tile covers BN/2 output columns = BN/2 gate rows + BN/2 up rows of B
+  const int n0 = (EPI == EPI_SWIGLU) ? tile_n * (BN / 2) : tile_n * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // global row of B feeding LDS row n of the tile
+  auto b_row = [&](int n) -> int {
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int s = n / WTN, tt = n % WTN, p = tt / 64, u = tt % 64;
+      const int col = n0 + s * (WTN / 2) + p * 32 + (u & 31);
+      return (u < 32) ? col : (col < N ? N + col : 2 * N);  // up rows follow the N gate rows
+    } else {
+      return n0 + n;
+    }
+  };
+  auto b_row_ok = [&](int n) -> bool {
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int s = n / WTN, tt = n % WTN, p = tt / 64, u = tt % 64;
+      return n0 + s * (WTN / 2) + p * 32 + (u & 31) < N;
+    } else {
+      return n0 + n < N;
+    }
+  };
+
+  uint4 ra[CH_A], rb[CH_B];
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+
+  auto load_global = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < CH_A; ++i) {
+      const int c = tid + i * 256;
+      const int row = c / KC, kc = c % KC;
+      const int gr = m0 + row, gk = k0 + kc * 8;
+      ra[i] = (gr < M && gk < K) ? *reinterpret_cast<const uint4*>(A + (size_t)gr * K + gk) : zero4;
+    }
+#pragma unroll
+    for (int i = 0; i < CH_B; ++i) {
+      const int c = tid + i * 256;
+      const int row = c / KC, kc = c % KC;
+      const int gk = k0 + kc * 8;
+      rb[i] = (b_row_ok(row) && gk < K) ? *reinterpret_cast<const uint4*>(B + (size_t)b_row(row) * K + gk)
+                                        : zero4;
+    }
+  };
+  auto store_lds = [&](int buf) {
+    bf16* as = As + buf * BM * LDK;
+    bf16* bs = Bs + buf * BN * LDK;
+#pragma unroll
+    for (int i = 0; i < CH_A; ++i) {
+      const int c = tid + i * 256;
+      *reinterpret_cast<uint4*>(as + (c / KC) * LDK + (c % KC) * 8) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CH_B; ++i) {
+      const int c = tid + i * 256;
+      *reinterpret_cast<uint4*>(bs + (c / KC) * LDK + (c % KC) * 8) = rb[i];
+    }
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = (K + BK - 1) / BK;
+  load_global(0);
+  store_lds(0);
+  __syncthreads();
+
+  const int frag_row = lane & 31;
+  const int frag_k = (lane >> 5) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load_global((kt + 1) * BK);
+    const bf16* as = As + buf * BM * LDK + (wm * WTM + frag_row) * LDK + frag_k;
+    const bf16* bs = Bs + buf * BN * LDK + (wn * WTN + frag_row) * LDK + frag_k;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(as + i * 32 * LDK + kk * 16);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(bs + j * 32 * LDK + kk * 16);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_lds(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue --------------------------------------------------------------------------
+  // 32x32 MFMA output: lane holds rows (r/4)*8 + (lane/32)*4 + r%4, column lane%32.
+  const int col_l = lane & 31;
+  const int row_l = (lane >> 5) * 4;
+  if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int p = 0; p < TN / 2; ++p) {
+        const int col = n0 + wn * (WTN / 2) + p * 32 + col_l;
+        if (col >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * WTM + i * 32 + (r / 4) * 8 + row_l + (r % 4);
+          if (row < M) {
+            const float g = acc[i][2 * p][r], u = acc[i][2 * p + 1][r];
+            C[(size_t)row * N + col] = (bf16)(silu_f(g) * u);
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = n0 + wn * WTN + j * 32 + col_l;
+        if (col >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * WTM + i * 32 + (r / 4) * 8 + row_l + (r % 4);
+          if (row < M) {
+            float v = acc[i][j][r];
+            if constexpr (EPI == EPI_RESID) v += (float)R[(size_t)row * N + col];
+            C[(size_t)row * N + col] = (bf16)v;
+          }
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+
+static const GemmVariant kVariants[] = {
+    {128, 128, 64},  // 0
+    {256, 128, 64},  // 1
+    {128, 256, 64},  // 2
+    {256, 256, 64},  // 3
+    {64, 128, 64},   // 4
+    {128, 64, 64},   // 5
+};
+static constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+
+int gemm_variant_count() { return kNumVariants; }
+GemmVariant gemm_variant(int i) { return kVariants[i]; }
+
+int gemm_default_variant(int m, int n, int k, int epilogue) {
+  (void)k;
+  // enough tiles to cover the 256 CUs at least once; otherwise smaller tiles
+  auto tiles = [&](int v) {
+    const GemmVariant g = kVariants[v];
+    const int nn = epilogue == EPI_SWIGLU ? 2 * n : n;
+    return ((m + g.bm - 1) / g.bm) * ((nn + g.bn - 1) / g.bn);
+  };
+  if (tiles(0) >= 256) return 0;
+  if (epilogue != EPI_SWIGLU && tiles(4) >= 256) return 4;
+  return 0;
+}
+
+template <int BM, int BN, int BK, int EPI>
+static hipError_t launch_t(const bf16* A, const bf16* B, bf16* C, const bf16* R, int M, int N, int K,
+                           hipStream_t s) {
+  const int nn = (EPI == EPI_SWIGLU) ? N : N;  // output columns
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (EPI == EPI_SWIGLU) ? (nn + BN / 2 - 1) / (BN / 2) : (nn + BN - 1) / BN;
+  const int ntiles = tiles_m * tiles_n;
+  const int per_xcd = (ntiles + kNumXcd - 1) / kNumXcd;
+  const size_t lds = (size_t)2 * (BM + BN) * (BK + 8) * sizeof(bf16);
+  auto kern = gemm_kernel<BM, BN, BK, EPI>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(per_xcd * kNumXcd), dim3(256), lds, s, A, B, C, R, M, N, K, tiles_m,
+                     tiles_n, per_xcd);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int BK>
+static hipError_t launch_epi(const bf16* A, const bf16* B, bf16* C, const bf16* R, int M, int N, int K,
+                             int epi, hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE: return launch_t<BM, BN, BK, EPI_STORE>(A, B, C, R, M, N, K, s);
+    case EPI_RESID: return launch_t<BM, BN, BK, EPI_RESID>(A, B, C, R, M, N, K, s);
+    case EPI_SWIGLU:
+      if constexpr (BN >= 128) return launch_t<BM, BN, BK, EPI_SWIGLU>(A, B, C, R, M, N, K, s);
+      return hipErrorInvalidValue;
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int m, int n, int k,
+                       int epilogue, int variant, hipStream_t s) {
+  if (m <= 0 || n <= 0 || k <= 0) return hipSuccess;
+  switch (variant) {
+    case 0: return launch_epi<128, 128, 64>(A, B, C, R, m, n, k, epilogue, s);
+    case 1: return launch_epi<256, 128, 64>(A, B, C, R, m, n, k, epilogue, s);
+    case 2: return launch_epi<128, 256, 64>(A, B, C, R, m, n, k, epilogue, s);
+    case 3: return launch_epi<256, 256, 64>(A, B, C, R, m, n, k, epilogue, s);
+    case 4: return launch_epi<64, 128, 64>(A, B, C, R, m, n, k, epilogue, s);
+    case 5: return launch_epi<128, 64, 64>(A, B, C, R, m, n, k, epilogue, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace nf

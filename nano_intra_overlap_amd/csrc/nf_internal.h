@@ -1,0 +1,92 @@
+// Internal declarations of libnanoflow: device vector types, kernel launchers and the
+// context structure. Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+
+#include <cstdint>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/nanoflow.h"
+
+namespace nf {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBlock = 16;       // KV block size (tokens)
+constexpr int kMaxGroup = 16;    // max query heads per KV head (MFMA column count)
+constexpr int kNumXcd = 8;       // XCDs of an MI355X
+
+// ---------------------------------------------------------------------------------------
+// per-launch metadata produced on the host from the batch descriptor
+// ---------------------------------------------------------------------------------------
+
+// One decode split-KV work item: the blocks [blk_begin, blk_end) of request `req`
+// (a decode request), for every KV head. `part` indexes the partial-result slots of the
+// request (part_base + chunk) or is -1 when the request has a single chunk.
+struct DecodeItem {
+  int32_t req;        // request index (row of the block table)
+  int32_t token;      // row of q / output
+  int32_t n_keys;     // ctx + 1
+  int32_t blk_begin;  // first logical block of this chunk
+  int32_t blk_end;    // one past the last logical block
+  int32_t part;       // partial slot index or -1
+};
+
+// One decode request that needs a split-KV combine.
+struct CombineItem {
+  int32_t token;
+  int32_t part_begin;
+  int32_t n_parts;
+  int32_t pad;
+};
+
+// One prefill attention work item: 16 consecutive queries of one prefill request.
+struct PrefillItem {
+  int32_t req;        // request index (row of the block table)
+  int32_t token0;     // dense-batch row of the first query of the request
+  int32_t q_begin;    // first query (within the request) of this 16-query tile
+  int32_t q_len;      // queries of the request
+  int32_t prefix;     // cached prefix length
+  int32_t pad[3];
+};
+
+// ---------------------------------------------------------------------------------------
+// kernel launchers (defined in the .hip files)
+// ---------------------------------------------------------------------------------------
+
+struct GemmVariant {
+  int bm, bn, bk;
+};
+int gemm_variant_count();
+GemmVariant gemm_variant(int i);
+int gemm_default_variant(int m, int n, int k, int epilogue);
+// C = A B^T (+ epilogue); returns hipError_t of the launch.
+hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int m, int n, int k,
+                       int epilogue, int variant, hipStream_t s);
+
+hipError_t launch_rmsnorm(const bf16* x, const bf16* g, bf16* out, int m, int n, float eps,
+                          hipStream_t s);
+
+hipError_t launch_rope_kv(bf16* qkv, const int32_t* tok_pos, const int32_t* tok_slot,
+                          const float* inv_freq, bf16* kpool, bf16* vpool, int t_begin, int t_end,
+                          int n_q, int n_kv, int d, hipStream_t s);
+
+hipError_t launch_decode_attn(const bf16* qkv, const bf16* kpool, const bf16* vpool,
+                              const int32_t* block_table, int max_blocks, const DecodeItem* items,
+                              int n_items, const CombineItem* combines, int n_combines,
+                              float* part_o, float* part_ml, bf16* out, int n_q, int n_kv, int d,
+                              hipStream_t s);
+
+hipError_t launch_prefill_attn(const bf16* qkv, const bf16* kpool, const bf16* vpool,
+                               const int32_t* block_table, int max_blocks, const PrefillItem* items,
+                               int n_items, bf16* out, int n_q, int n_kv, int d, hipStream_t s);
+
+}  // namespace nf

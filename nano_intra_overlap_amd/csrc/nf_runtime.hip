@@ -1,0 +1,651 @@
+// libnanoflow runtime: context, workspaces, batch metadata upload, the nano-operation
+// executor and the per-operation entry points.
+//
+// Executor (NanoFlow OSDI'25 summary page: nano-ops launched as kernels on CUDA streams
+// ordered by events; here HIP streams with CU masks): every nano-operation of the plan is
+// enqueued on its stream in a global order consistent with each stream's listed order and
+// with the range-intersection dependencies; a nano-op waits (hipStreamWaitEvent) on the
+// events of the producers it depends on that live on other streams, then records its own
+// event. The call forks from the caller's stream through one event and joins back into it.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <map>
+#include <memory>
+
+#include "nf_batch.h"
+#include "nf_internal.h"
+
+using namespace nf;
+
+namespace {
+
+constexpr int kMaxSplit = 64;      // decode chunk limit (blocks per wave: one id per lane)
+constexpr int kDefaultSplit = 32;  // default decode chunk (blocks)
+constexpr int kMaxStreams = 3;  // + the caller's stream: within the 4 HW queues of a process
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct DevBuf {
+  void* p = nullptr;
+  size_t cap = 0;
+};
+
+}  // namespace
+
+struct nf_ctx {
+  int device = 0;
+  std::string err;
+  // activation workspace
+  DevBuf h, qkv, attn, x1, h2, a;
+  // metadata: pinned staging + device copy
+  DevBuf meta_dev;
+  void* meta_host = nullptr;
+  size_t meta_host_cap = 0;
+  hipEvent_t upload_done = nullptr;
+  bool upload_pending = false;
+  // split-KV partials
+  DevBuf part_o, part_ml;
+  // streams keyed by CU mask (all-ones key = unmasked)
+  struct StreamEntry {
+    std::vector<uint32_t> mask;
+    hipStream_t s;
+    uint64_t last_use;
+  };
+  std::vector<StreamEntry> streams;
+  uint64_t use_clock = 0;
+  std::vector<hipEvent_t> events;
+  hipEvent_t fork_ev = nullptr;
+  std::vector<hipEvent_t> join_ev;
+  int decode_split = kDefaultSplit;
+  int gemm_variant[NF_OP_KINDS][2];  // per dense op kind: [0] first GEMM, [1] second (UGD down); -1 = default
+};
+
+namespace {
+
+nf_status hip_fail(nf_ctx* ctx, hipError_t e, const char* what) {
+  ctx->err = std::string(what) + ": " + hipGetErrorString(e);
+  return NF_E_HIP;
+}
+
+#define NF_HIP(ctx, expr)                                   \
+  do {                                                      \
+    hipError_t e_ = (expr);                                 \
+    if (e_ != hipSuccess) return hip_fail((ctx), e_, #expr); \
+  } while (0)
+
+nf_status ensure(nf_ctx* ctx, DevBuf& b, size_t bytes) {
+  if (b.cap >= bytes) return NF_OK;
+  if (b.p) {
+    NF_HIP(ctx, hipDeviceSynchronize());
+    NF_HIP(ctx, hipFree(b.p));
+    b.p = nullptr;
+    b.cap = 0;
+  }
+  const size_t cap = align_up(std::max<size_t>(bytes, 256), 1 << 20);
+  NF_HIP(ctx, hipMalloc(&b.p, cap));
+  b.cap = cap;
+  return NF_OK;
+}
+
+nf_status ensure_host(nf_ctx* ctx, size_t bytes) {
+  if (ctx->meta_host_cap >= bytes) return NF_OK;
+  if (ctx->upload_pending) {
+    NF_HIP(ctx, hipEventSynchronize(ctx->upload_done));
+    ctx->upload_pending = false;
+  }
+  if (ctx->meta_host) NF_HIP(ctx, hipHostFree(ctx->meta_host));
+  ctx->meta_host = nullptr;
+  const size_t cap = align_up(bytes, 1 << 20);
+  NF_HIP(ctx, hipHostMalloc(&ctx->meta_host, cap, hipHostMallocDefault));
+  ctx->meta_host_cap = cap;
+  return NF_OK;
+}
+
+// Stream for a CU mask (nullptr mask = whole GPU). Masks must give each XCD the same
+// non-zero number of CUs.
+nf_status mask_ok(nf_ctx* ctx, const uint32_t* m) {
+  int per[kNumXcd] = {0};
+  for (int i = 0; i < NF_CU_MASK_WORDS * 32; ++i)
+    if (m[i / 32] >> (i % 32) & 1u) per[i % kNumXcd]++;
+  for (int x = 0; x < kNumXcd; ++x)
+    if (per[x] == 0 || per[x] != per[0]) {
+      char buf[160];
+      snprintf(buf, sizeof buf, "CU mask gives XCD %d %d CUs and XCD 0 %d; every XCD needs the same non-zero count",
+               x, per[x], per[0]);
+      ctx->err = buf;
+      return NF_E_CU_MASK;
+    }
+  return NF_OK;
+}
+
+// Streams are cached per (mask, plan stream index): plan streams are always distinct
+// streams, masked or not.
+nf_status get_stream(nf_ctx* ctx, const uint32_t* mask, int idx, hipStream_t* out) {
+  std::vector<uint32_t> key(NF_CU_MASK_WORDS, 0xFFFFFFFFu);
+  if (mask) key.assign(mask, mask + NF_CU_MASK_WORDS);
+  key.push_back((uint32_t)idx);
+  for (auto& e : ctx->streams)
+    if (e.mask == key) {
+      e.last_use = ++ctx->use_clock;
+      *out = e.s;
+      return NF_OK;
+    }
+  if (mask) {
+    nf_status st = mask_ok(ctx, mask);
+    if (st != NF_OK) return st;
+  }
+  if ((int)ctx->streams.size() >= kMaxStreams) {
+    // evict the least recently used stream (its work completes before destruction)
+    auto it = std::min_element(ctx->streams.begin(), ctx->streams.end(),
+                               [](const nf_ctx::StreamEntry& a, const nf_ctx::StreamEntry& b) {
+                                 return a.last_use < b.last_use;
+                               });
+    NF_HIP(ctx, hipStreamSynchronize(it->s));
+    NF_HIP(ctx, hipStreamDestroy(it->s));
+    ctx->streams.erase(it);
+  }
+  hipStream_t s;
+  if (mask) {
+    NF_HIP(ctx, hipExtStreamCreateWithCUMask(&s, NF_CU_MASK_WORDS, mask));
+  } else {
+    NF_HIP(ctx, hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+  }
+  ctx->streams.push_back({key, s, ++ctx->use_clock});
+  *out = s;
+  return NF_OK;
+}
+
+nf_status ensure_events(nf_ctx* ctx, size_t n) {
+  while (ctx->events.size() < n) {
+    hipEvent_t e;
+    NF_HIP(ctx, hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    ctx->events.push_back(e);
+  }
+  while (ctx->join_ev.size() < (size_t)kMaxStreams) {
+    hipEvent_t e;
+    NF_HIP(ctx, hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    ctx->join_ev.push_back(e);
+  }
+  return NF_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+// metadata
+// ---------------------------------------------------------------------------------------
+
+struct Meta {
+  // host-side work lists, grouped per nano-batch
+  std::vector<DecodeItem> dec;
+  std::vector<CombineItem> comb;
+  std::vector<PrefillItem> pf;
+  std::vector<int32_t> dec_begin, comb_begin, pf_begin;  // size n_nano + 1
+  int32_t n_parts = 0;
+  // device pointers after upload
+  const int32_t* d_pos = nullptr;
+  const int32_t* d_slot = nullptr;
+  const float* d_inv_freq = nullptr;
+  const DecodeItem* d_dec = nullptr;
+  const CombineItem* d_comb = nullptr;
+  const PrefillItem* d_pf = nullptr;
+  const int32_t* d_bt = nullptr;
+};
+
+// Work lists of the decode attention and prefill attention nano-ops of each nano-batch.
+void build_work(const BatchLayout& L, const PlanGraph& g, int split, Meta& M) {
+  const int n_nano = g.n_nano;
+  M.dec.clear();
+  M.comb.clear();
+  M.pf.clear();
+  M.dec_begin.assign(n_nano + 1, 0);
+  M.comb_begin.assign(n_nano + 1, 0);
+  M.pf_begin.assign(n_nano + 1, 0);
+  M.n_parts = 0;
+  std::vector<const NanoOp*> dec_op(n_nano, nullptr), pf_op(n_nano, nullptr);
+  for (auto& op : g.ops) {
+    if (op.kind == NF_OP_DECATTN) dec_op[op.nano] = &op;
+    if (op.kind == NF_OP_PFATTN) pf_op[op.nano] = &op;
+  }
+  for (int j = 0; j < n_nano; ++j) {
+    M.dec_begin[j] = (int32_t)M.dec.size();
+    M.comb_begin[j] = (int32_t)M.comb.size();
+    if (dec_op[j]) {
+      for (int32_t r = dec_op[j]->r0; r < dec_op[j]->r1; ++r) {
+        const ReqInfo& ri = L.req[r];
+        const int32_t nblk = (ri.n_keys + kBlock - 1) / kBlock;
+        const int32_t nch = (nblk + split - 1) / split;
+        const int32_t per = (nblk + nch - 1) / nch;
+        for (int32_t c = 0; c < nch; ++c) {
+          DecodeItem it;
+          it.req = r;
+          it.token = ri.t0;
+          it.n_keys = ri.n_keys;
+          it.blk_begin = c * per;
+          it.blk_end = std::min(nblk, (c + 1) * per);
+          it.part = nch > 1 ? M.n_parts + c : -1;
+          M.dec.push_back(it);
+        }
+        if (nch > 1) {
+          M.comb.push_back(CombineItem{ri.t0, M.n_parts, nch, 0});
+          M.n_parts += nch;
+        }
+      }
+    }
+    M.pf_begin[j] = (int32_t)M.pf.size();
+    if (pf_op[j]) {
+      for (int32_t r : pf_op[j]->prefill_reqs) {
+        const ReqInfo& ri = L.req[r];
+        const int32_t qlen = ri.t1 - ri.t0;
+        // longest tiles (latest queries, most keys) first
+        for (int32_t q0 = ((qlen - 1) / 16) * 16; q0 >= 0; q0 -= 16) {
+          PrefillItem it{};
+          it.req = r;
+          it.token0 = ri.t0;
+          it.q_begin = q0;
+          it.q_len = qlen;
+          it.prefix = ri.cached;
+          M.pf.push_back(it);
+        }
+      }
+    }
+  }
+  M.dec_begin[n_nano] = (int32_t)M.dec.size();
+  M.comb_begin[n_nano] = (int32_t)M.comb.size();
+  M.pf_begin[n_nano] = (int32_t)M.pf.size();
+}
+
+// Pack and upload the metadata on `stream` (ordered before the work that reads it).
+nf_status upload_meta(nf_ctx* ctx, const nf_layer_cfg& cfg, const nf_batch_desc& b, const BatchLayout& L, Meta& M,
+                      hipStream_t stream) {
+  const int T = L.T;
+  const int half = cfg.head_dim / 2;
+  const size_t n_req = L.req.size();
+  const bool bt_up = b.block_table_dev == nullptr;
+  size_t off = 0;
+  auto slot = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t o_pos = slot(sizeof(int32_t) * T);
+  const size_t o_slot = slot(sizeof(int32_t) * T);
+  const size_t o_inv = slot(sizeof(float) * half);
+  const size_t o_dec = slot(sizeof(DecodeItem) * M.dec.size());
+  const size_t o_comb = slot(sizeof(CombineItem) * M.comb.size());
+  const size_t o_pf = slot(sizeof(PrefillItem) * M.pf.size());
+  const size_t o_bt = slot(bt_up ? sizeof(int32_t) * n_req * b.max_blocks : 0);
+  const size_t total = off;
+  nf_status st = ensure_host(ctx, total);
+  if (st != NF_OK) return st;
+  if (ctx->meta_dev.cap < total) {
+    st = ensure(ctx, ctx->meta_dev, total);
+    if (st != NF_OK) return st;
+  }
+  if (ctx->upload_pending) {
+    NF_HIP(ctx, hipEventSynchronize(ctx->upload_done));  // staging buffer free again
+    ctx->upload_pending = false;
+  }
+  unsigned char* h = static_cast<unsigned char*>(ctx->meta_host);
+  memcpy(h + o_pos, L.pos.data(), sizeof(int32_t) * T);
+  memcpy(h + o_slot, L.slot.data(), sizeof(int32_t) * T);
+  float* inv = reinterpret_cast<float*>(h + o_inv);
+  for (int i = 0; i < half; ++i) inv[i] = (float)std::pow((double)cfg.rope_base, -2.0 * i / cfg.head_dim);
+  if (!M.dec.empty()) memcpy(h + o_dec, M.dec.data(), sizeof(DecodeItem) * M.dec.size());
+  if (!M.comb.empty()) memcpy(h + o_comb, M.comb.data(), sizeof(CombineItem) * M.comb.size());
+  if (!M.pf.empty()) memcpy(h + o_pf, M.pf.data(), sizeof(PrefillItem) * M.pf.size());
+  if (bt_up && n_req) memcpy(h + o_bt, b.block_table, sizeof(int32_t) * n_req * b.max_blocks);
+  NF_HIP(ctx, hipMemcpyAsync(ctx->meta_dev.p, h, total, hipMemcpyHostToDevice, stream));
+  NF_HIP(ctx, hipEventRecord(ctx->upload_done, stream));
+  ctx->upload_pending = true;
+  unsigned char* d = static_cast<unsigned char*>(ctx->meta_dev.p);
+  M.d_pos = reinterpret_cast<const int32_t*>(d + o_pos);
+  M.d_slot = reinterpret_cast<const int32_t*>(d + o_slot);
+  M.d_inv_freq = reinterpret_cast<const float*>(d + o_inv);
+  M.d_dec = reinterpret_cast<const DecodeItem*>(d + o_dec);
+  M.d_comb = reinterpret_cast<const CombineItem*>(d + o_comb);
+  M.d_pf = reinterpret_cast<const PrefillItem*>(d + o_pf);
+  M.d_bt = bt_up ? reinterpret_cast<const int32_t*>(d + o_bt) : b.block_table_dev;
+  return NF_OK;
+}
+
+nf_status ensure_parts(nf_ctx* ctx, const nf_layer_cfg& cfg, int32_t n_parts) {
+  const int G = cfg.n_q_heads / cfg.n_kv_heads;
+  const size_t n = (size_t)std::max(n_parts, 1) * cfg.n_kv_heads * G;
+  nf_status st = ensure(ctx, ctx->part_o, n * cfg.head_dim * sizeof(float));
+  if (st != NF_OK) return st;
+  return ensure(ctx, ctx->part_ml, n * 2 * sizeof(float));
+}
+
+nf_status ensure_workspace(nf_ctx* ctx, const nf_layer_cfg& c, int T) {
+  const size_t t = std::max(T, 1);
+  const size_t qkvw = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  nf_status st;
+  if ((st = ensure(ctx, ctx->h, t * c.hidden * 2)) != NF_OK) return st;
+  if ((st = ensure(ctx, ctx->qkv, t * qkvw * 2)) != NF_OK) return st;
+  if ((st = ensure(ctx, ctx->attn, t * c.n_q_heads * c.head_dim * 2)) != NF_OK) return st;
+  if ((st = ensure(ctx, ctx->x1, t * c.hidden * 2)) != NF_OK) return st;
+  if ((st = ensure(ctx, ctx->h2, t * c.hidden * 2)) != NF_OK) return st;
+  if ((st = ensure(ctx, ctx->a, t * c.ffn * 2)) != NF_OK) return st;
+  return NF_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+// nano-operation launch
+// ---------------------------------------------------------------------------------------
+
+struct LayerArgs {
+  const nf_layer_cfg* cfg;
+  const nf_layer_weights* w;
+  const bf16* x;
+  bf16* y;
+  nf_kv_pool* pool;
+  int max_blocks;
+};
+
+int pick_variant(nf_ctx* ctx, int kind, int which, int m, int n, int k, int epi) {
+  const int v = ctx->gemm_variant[kind][which];
+  if (v >= 0 && v < gemm_variant_count()) {
+    if (!(epi == 2 && gemm_variant(v).bn < 128)) return v;
+  }
+  return gemm_default_variant(m, n, k, epi);
+}
+
+nf_status launch_op(nf_ctx* ctx, const LayerArgs& A, const PlanGraph& g, const NanoOp& op, const Meta& M,
+                    hipStream_t s) {
+  const nf_layer_cfg& c = *A.cfg;
+  const int H = c.hidden, F = c.ffn, d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
+  const int W = (nq + 2 * nkv) * d;
+  const int lo = g.bounds[op.nano], hi = g.bounds[op.nano + 1], m = hi - lo;
+  bf16* h = static_cast<bf16*>(ctx->h.p);
+  bf16* qkv = static_cast<bf16*>(ctx->qkv.p);
+  bf16* attn = static_cast<bf16*>(ctx->attn.p);
+  bf16* x1 = static_cast<bf16*>(ctx->x1.p);
+  bf16* h2 = static_cast<bf16*>(ctx->h2.p);
+  bf16* a = static_cast<bf16*>(ctx->a.p);
+  const bf16* const* wp = nullptr;
+  (void)wp;
+  switch (op.kind) {
+    case NF_OP_KQV: {
+      NF_HIP(ctx, launch_rmsnorm(A.x + (size_t)lo * H, static_cast<const bf16*>(A.w->g_attn), h + (size_t)lo * H, m, H,
+                                 c.rms_eps, s));
+      NF_HIP(ctx, launch_gemm(h + (size_t)lo * H, static_cast<const bf16*>(A.w->w_qkv), qkv + (size_t)lo * W, nullptr, m,
+                              W, H, 0, pick_variant(ctx, NF_OP_KQV, 0, m, W, H, 0), s));
+      NF_HIP(ctx, launch_rope_kv(qkv, M.d_pos, M.d_slot, M.d_inv_freq, static_cast<bf16*>(A.pool->k),
+                                 static_cast<bf16*>(A.pool->v), lo, hi, nq, nkv, d, s));
+      break;
+    }
+    case NF_OP_DECATTN: {
+      const int i0 = M.dec_begin[op.nano], i1 = M.dec_begin[op.nano + 1];
+      const int c0 = M.comb_begin[op.nano], c1 = M.comb_begin[op.nano + 1];
+      NF_HIP(ctx, launch_decode_attn(qkv, static_cast<const bf16*>(A.pool->k), static_cast<const bf16*>(A.pool->v),
+                                     M.d_bt, A.max_blocks, M.d_dec + i0, i1 - i0, M.d_comb + c0, c1 - c0,
+                                     static_cast<float*>(ctx->part_o.p), static_cast<float*>(ctx->part_ml.p), attn, nq,
+                                     nkv, d, s));
+      break;
+    }
+    case NF_OP_PFATTN: {
+      const int i0 = M.pf_begin[op.nano], i1 = M.pf_begin[op.nano + 1];
+      NF_HIP(ctx, launch_prefill_attn(qkv, static_cast<const bf16*>(A.pool->k), static_cast<const bf16*>(A.pool->v),
+                                      M.d_bt, A.max_blocks, M.d_pf + i0, i1 - i0, attn, nq, nkv, d, s));
+      break;
+    }
+    case NF_OP_O: {
+      NF_HIP(ctx, launch_gemm(attn + (size_t)lo * nq * d, static_cast<const bf16*>(A.w->w_o), x1 + (size_t)lo * H,
+                              A.x + (size_t)lo * H, m, H, nq * d, 1, pick_variant(ctx, NF_OP_O, 0, m, H, nq * d, 1), s));
+      break;
+    }
+    case NF_OP_UGD: {
+      NF_HIP(ctx, launch_rmsnorm(x1 + (size_t)lo * H, static_cast<const bf16*>(A.w->g_ffn), h2 + (size_t)lo * H, m, H,
+                                 c.rms_eps, s));
+      NF_HIP(ctx, launch_gemm(h2 + (size_t)lo * H, static_cast<const bf16*>(A.w->w_gate_up), a + (size_t)lo * F, nullptr,
+                              m, F, H, 2, pick_variant(ctx, NF_OP_UGD, 0, m, F, H, 2), s));
+      NF_HIP(ctx, launch_gemm(a + (size_t)lo * F, static_cast<const bf16*>(A.w->w_down), A.y + (size_t)lo * H,
+                              x1 + (size_t)lo * H, m, H, F, 1, pick_variant(ctx, NF_OP_UGD, 1, m, H, F, 1), s));
+      break;
+    }
+  }
+  return NF_OK;
+}
+
+nf_status prepare_batch(nf_ctx* ctx, const nf_layer_cfg* cfg, const nf_batch_desc* batch, int32_t num_blocks,
+                        const nf_plan* plan, BatchLayout& L, PlanGraph& g, Meta& M, hipStream_t stream) {
+  nf_status st = check_cfg(*cfg, ctx->err);
+  if (st != NF_OK) return st;
+  st = build_layout(*cfg, *batch, num_blocks, L, ctx->err);
+  if (st != NF_OK) return st;
+  st = build_plan_graph(L, plan, g, ctx->err);
+  if (st != NF_OK) return st;
+  if (plan && plan->cu_masks)
+    for (int s = 0; s < plan->n_streams; ++s) {
+      st = mask_ok(ctx, plan->cu_masks + s * NF_CU_MASK_WORDS);
+      if (st != NF_OK) return st;
+    }
+  build_work(L, g, ctx->decode_split, M);
+  if ((st = ensure_workspace(ctx, *cfg, L.T)) != NF_OK) return st;
+  if ((st = ensure_parts(ctx, *cfg, M.n_parts)) != NF_OK) return st;
+  return upload_meta(ctx, *cfg, *batch, L, M, stream);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------
+// ABI
+// ---------------------------------------------------------------------------------------
+
+extern "C" const char* nf_version(void) { return "nanoflow-mi355x 0.1"; }
+
+extern "C" nf_status nf_ctx_create(int device, nf_ctx** out) {
+  if (!out) return NF_E_ARG;
+  *out = nullptr;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return NF_E_ARG;
+  if (hipSetDevice(device) != hipSuccess) return NF_E_HIP;
+  std::unique_ptr<nf_ctx> ctx(new nf_ctx());
+  ctx->device = device;
+  for (auto& row : ctx->gemm_variant) row[0] = row[1] = -1;
+  if (hipEventCreateWithFlags(&ctx->upload_done, hipEventDisableTiming) != hipSuccess) return NF_E_HIP;
+  if (hipEventCreateWithFlags(&ctx->fork_ev, hipEventDisableTiming) != hipSuccess) return NF_E_HIP;
+  *out = ctx.release();
+  return NF_OK;
+}
+
+extern "C" void nf_ctx_destroy(nf_ctx* ctx) {
+  if (!ctx) return;
+  (void)hipSetDevice(ctx->device);
+  (void)hipDeviceSynchronize();
+  for (auto& e : ctx->streams) (void)hipStreamDestroy(e.s);
+  for (auto e : ctx->events) (void)hipEventDestroy(e);
+  for (auto e : ctx->join_ev) (void)hipEventDestroy(e);
+  if (ctx->fork_ev) (void)hipEventDestroy(ctx->fork_ev);
+  if (ctx->upload_done) (void)hipEventDestroy(ctx->upload_done);
+  for (DevBuf* b : {&ctx->h, &ctx->qkv, &ctx->attn, &ctx->x1, &ctx->h2, &ctx->a, &ctx->meta_dev, &ctx->part_o,
+                    &ctx->part_ml})
+    if (b->p) (void)hipFree(b->p);
+  if (ctx->meta_host) (void)hipHostFree(ctx->meta_host);
+  delete ctx;
+}
+
+extern "C" const char* nf_last_error(const nf_ctx* ctx) { return ctx ? ctx->err.c_str() : "null context"; }
+
+extern "C" nf_status nf_layer_forward(nf_ctx* ctx, const nf_layer_cfg* cfg, const nf_layer_weights* w,
+                                      const void* x_in, void* y_out, const nf_batch_desc* batch, nf_kv_pool* pool,
+                                      const nf_plan* plan, void* stream_) {
+  if (!ctx) return NF_E_ARG;
+  if (!cfg || !w || !x_in || !y_out || !batch || !pool || !pool->k || !pool->v || !w->g_attn || !w->w_qkv ||
+      !w->w_o || !w->g_ffn || !w->w_gate_up || !w->w_down) {
+    ctx->err = "null argument";
+    return NF_E_ARG;
+  }
+  hipStream_t caller = static_cast<hipStream_t>(stream_);
+  BatchLayout L;
+  PlanGraph g;
+  Meta M;
+  nf_status st = prepare_batch(ctx, cfg, batch, pool->num_blocks, plan, L, g, M, caller);
+  if (st != NF_OK) return st;
+  if (L.T == 0) return NF_OK;
+  LayerArgs A{cfg, w, static_cast<const bf16*>(x_in), static_cast<bf16*>(y_out), pool, batch->max_blocks};
+
+  if (!plan) {
+    for (int32_t i : g.order)
+      if (!g.ops[i].empty || g.ops[i].kind == NF_OP_KQV) {
+        st = launch_op(ctx, A, g, g.ops[i], M, caller);
+        if (st != NF_OK) return st;
+      }
+    return NF_OK;
+  }
+  // streams of the plan
+  std::vector<hipStream_t> ss(g.n_streams);
+  for (int s = 0; s < g.n_streams; ++s) {
+    st = get_stream(ctx, plan->cu_masks ? plan->cu_masks + s * NF_CU_MASK_WORDS : nullptr, s, &ss[s]);
+    if (st != NF_OK) return st;
+  }
+  if ((st = ensure_events(ctx, g.ops.size())) != NF_OK) return st;
+  NF_HIP(ctx, hipEventRecord(ctx->fork_ev, caller));
+  std::vector<char> used(g.n_streams, 0);
+  for (auto& op : g.ops) used[op.stream] = 1;
+  for (int s = 0; s < g.n_streams; ++s)
+    if (used[s]) NF_HIP(ctx, hipStreamWaitEvent(ss[s], ctx->fork_ev, 0));
+  for (int32_t i : g.order) {
+    const NanoOp& op = g.ops[i];
+    hipStream_t s = ss[op.stream];
+    for (int32_t dep : g.deps[i])
+      if (g.ops[dep].stream != op.stream) NF_HIP(ctx, hipStreamWaitEvent(s, ctx->events[dep], 0));
+    if (!op.empty || op.kind == NF_OP_KQV) {
+      st = launch_op(ctx, A, g, op, M, s);
+      if (st != NF_OK) return st;
+    }
+    NF_HIP(ctx, hipEventRecord(ctx->events[i], s));
+  }
+  for (int s = 0; s < g.n_streams; ++s)
+    if (used[s]) {
+      NF_HIP(ctx, hipEventRecord(ctx->join_ev[s], ss[s]));
+      NF_HIP(ctx, hipStreamWaitEvent(caller, ctx->join_ev[s], 0));
+    }
+  return NF_OK;
+}
+
+extern "C" nf_status nf_debug_buffer(nf_ctx* ctx, int32_t which, void** ptr, size_t* bytes) {
+  if (!ctx || !ptr) return NF_E_ARG;
+  DevBuf* b = nullptr;
+  switch (which) {
+    case 0: b = &ctx->h; break;
+    case 1: b = &ctx->qkv; break;
+    case 2: b = &ctx->attn; break;
+    case 3: b = &ctx->x1; break;
+    case 4: b = &ctx->h2; break;
+    case 5: b = &ctx->a; break;
+    default: ctx->err = "unknown debug buffer"; return NF_E_ARG;
+  }
+  *ptr = b->p;
+  if (bytes) *bytes = b->cap;
+  return NF_OK;
+}
+
+extern "C" nf_status nf_gemm_variants(int32_t* count, int32_t index, int32_t* out3) {
+  if (count) *count = gemm_variant_count();
+  if (out3) {
+    if (index < 0 || index >= gemm_variant_count()) return NF_E_ARG;
+    const GemmVariant v = gemm_variant(index);
+    out3[0] = v.bm;
+    out3[1] = v.bn;
+    out3[2] = v.bk;
+  }
+  return NF_OK;
+}
+
+extern "C" nf_status nf_op_gemm(nf_ctx* ctx, const void* A, const void* B, void* C, const void* R, int32_t m, int32_t n,
+                                int32_t k, int32_t epilogue, int32_t variant, void* stream) {
+  if (!ctx) return NF_E_ARG;
+  if (!A || !B || !C || m < 0 || n <= 0 || k <= 0 || epilogue < 0 || epilogue > 2 || (epilogue == 1 && !R)) {
+    ctx->err = "nf_op_gemm: bad argument";
+    return NF_E_ARG;
+  }
+  if (n % 8 || k % 8) {
+    ctx->err = "nf_op_gemm: n and k must be multiples of 8";
+    return NF_E_UNSUPPORTED;
+  }
+  if (variant >= gemm_variant_count() || (variant >= 0 && epilogue == 2 && gemm_variant(variant).bn < 128)) {
+    ctx->err = "nf_op_gemm: variant out of range for this epilogue";
+    return NF_E_ARG;
+  }
+  const int v = variant < 0 ? gemm_default_variant(m, n, k, epilogue) : variant;
+  NF_HIP(ctx, launch_gemm(static_cast<const bf16*>(A), static_cast<const bf16*>(B), static_cast<bf16*>(C),
+                          static_cast<const bf16*>(R), m, n, k, epilogue, v, static_cast<hipStream_t>(stream)));
+  return NF_OK;
+}
+
+extern "C" nf_status nf_op_rmsnorm(nf_ctx* ctx, const void* x, const void* g, void* out, int32_t m, int32_t n, float eps,
+                                   void* stream) {
+  if (!ctx) return NF_E_ARG;
+  if (!x || !g || !out || m < 0 || n <= 0 || n % 8 || !(eps >= 0.0f)) {
+    ctx->err = "nf_op_rmsnorm: bad argument (n must be a positive multiple of 8)";
+    return NF_E_ARG;
+  }
+  NF_HIP(ctx, launch_rmsnorm(static_cast<const bf16*>(x), static_cast<const bf16*>(g), static_cast<bf16*>(out), m, n,
+                             eps, static_cast<hipStream_t>(stream)));
+  return NF_OK;
+}
+
+extern "C" nf_status nf_op_rope_kv_append(nf_ctx* ctx, const nf_layer_cfg* cfg, void* qkv, const nf_batch_desc* batch,
+                                          nf_kv_pool* pool, void* stream) {
+  if (!ctx) return NF_E_ARG;
+  if (!cfg || !qkv || !batch || !pool || !pool->k || !pool->v) {
+    ctx->err = "null argument";
+    return NF_E_ARG;
+  }
+  BatchLayout L;
+  PlanGraph g;
+  Meta M;
+  nf_status st = prepare_batch(ctx, cfg, batch, pool->num_blocks, nullptr, L, g, M, static_cast<hipStream_t>(stream));
+  if (st != NF_OK) return st;
+  NF_HIP(ctx, launch_rope_kv(static_cast<bf16*>(qkv), M.d_pos, M.d_slot, M.d_inv_freq, static_cast<bf16*>(pool->k),
+                             static_cast<bf16*>(pool->v), 0, L.T, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim,
+                             static_cast<hipStream_t>(stream)));
+  return NF_OK;
+}
+
+extern "C" nf_status nf_op_attention(nf_ctx* ctx, const nf_layer_cfg* cfg, const void* qkv, const nf_batch_desc* batch,
+                                     const nf_kv_pool* pool, void* out, int32_t decode, int32_t kv_split_blocks,
+                                     void* stream) {
+  if (!ctx) return NF_E_ARG;
+  if (!cfg || !qkv || !batch || !pool || !pool->k || !pool->v || !out || kv_split_blocks < 0 ||
+      kv_split_blocks > kMaxSplit) {
+    ctx->err = "nf_op_attention: bad argument (kv_split_blocks in 0..64)";
+    return NF_E_ARG;
+  }
+  const int saved = ctx->decode_split;
+  if (kv_split_blocks > 0) ctx->decode_split = kv_split_blocks;
+  BatchLayout L;
+  PlanGraph g;
+  Meta M;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  nf_status st = prepare_batch(ctx, cfg, batch, pool->num_blocks, nullptr, L, g, M, s);
+  ctx->decode_split = saved;
+  if (st != NF_OK) return st;
+  const int nq = cfg->n_q_heads, nkv = cfg->n_kv_heads, d = cfg->head_dim;
+  if (decode) {
+    NF_HIP(ctx, launch_decode_attn(static_cast<const bf16*>(qkv), static_cast<const bf16*>(pool->k),
+                                   static_cast<const bf16*>(pool->v), M.d_bt, batch->max_blocks, M.d_dec,
+                                   (int)M.dec.size(), M.d_comb, (int)M.comb.size(), static_cast<float*>(ctx->part_o.p),
+                                   static_cast<float*>(ctx->part_ml.p), static_cast<bf16*>(out), nq, nkv, d, s));
+  } else {
+    NF_HIP(ctx, launch_prefill_attn(static_cast<const bf16*>(qkv), static_cast<const bf16*>(pool->k),
+                                    static_cast<const bf16*>(pool->v), M.d_bt, batch->max_blocks, M.d_pf,
+                                    (int)M.pf.size(), static_cast<bf16*>(out), nq, nkv, d, s));
+  }
+  return NF_OK;
+}
+
+// Internal knobs used by the profiler (not in the public header).
+extern "C" nf_status nf_ctx_set_decode_split(nf_ctx* ctx, int32_t blocks) {
+  if (!ctx || blocks < 1 || blocks > kMaxSplit) return NF_E_ARG;
+  ctx->decode_split = blocks;
+  return NF_OK;
+}
+extern "C" nf_status nf_ctx_set_gemm_variant(nf_ctx* ctx, int32_t kind, int32_t which, int32_t variant) {
+  if (!ctx || kind < 0 || kind >= NF_OP_KINDS || which < 0 || which > 1 || variant < -1 ||
+      variant >= gemm_variant_count())
+    return NF_E_ARG;
+  ctx->gemm_variant[kind][which] = variant;
+  return NF_OK;
+}

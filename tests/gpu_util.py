@@ -1,0 +1,32 @@
+"""Shared helpers of the GPU parity tests (inputs, comparisons)."""
+
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import layer as ol
+from synth import workloads as sw
+
+TOL = 1e-2  # max relative error, per output tensor: ||gpu - ref||_inf / ||ref||_inf
+
+
+def rel_inf(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    denom = float(np.max(np.abs(ref))) if ref.size else 0.0
+    if denom == 0.0:
+        return float(np.max(np.abs(got))) if got.size else 0.0
+    return float(np.max(np.abs(got - ref))) / denom
+
+
+def rand_bf16(rng, shape, scale=1.0) -> np.ndarray:
+    return sw.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * np.float32(scale))
+
+
+def f64(bits) -> np.ndarray:
+    return ol.bf16_to_f64(bits)
+
+
+def log_case(name: str):
+    """Name the case on stdout before a GPU step (a fault then still identifies it)."""
+    print(f"[gpu case] {name}", flush=True)

@@ -1,0 +1,286 @@
+"""Whole-layer parity of nf_layer_forward against the CPU oracle, through the C ABI.
+
+* tiny layer (2 prefill x 32 + 14 decode): every output, for the sequential layer, the
+  given 2-nano-batch split, two-stream overlap with CU masks and random plans;
+* 8B-shaped layer and the 70B TP-8 share at full size, in the bench's launch
+  configuration: sampled requests recomputed by the oracle one sub-batch at a time, plus
+  the property that every pool slot other than this iteration's is bitwise unchanged.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import layer as ol
+from synth import workloads as sw
+from tests.gpu_util import TOL, f64, log_case, rel_inf
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    from nano_intra_overlap_amd import abi
+
+    c = abi.nf_ctx_create(0)
+    yield c
+    abi.nf_ctx_destroy(c)
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _run_layer(ctx, shape, w_dev, x_dev, y_dev, hb, pool, plan):
+    from nano_intra_overlap_amd import abi
+
+    abi.nf_layer_forward(ctx, abi.make_cfg(shape), w_dev.desc, x_dev.data_ptr(), y_dev.data_ptr(), hb, pool.desc,
+                         plan, _stream())
+    torch.cuda.synchronize()
+
+
+def _attn_buffer(ctx, T, width):
+    """Host copy of the attention-output buffer of the last layer call."""
+    from nano_intra_overlap_amd import abi
+    from nano_intra_overlap_amd.device import bf16_bits, copy_device
+
+    ptr, nbytes = abi.nf_debug_buffer(ctx, 2)
+    assert nbytes >= T * width * 2
+    buf = torch.empty((T, width), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    copy_device(buf.data_ptr(), ptr, T * width * 2)
+    return bf16_bits(buf)
+
+
+# ------------------------------------------------------------------------------------- tiny
+
+
+def _tiny(seed, gain_jitter=0.1):
+    from nano_intra_overlap_amd.device import DevicePool, DeviceWeights, bf16_tensor
+
+    wl = sw.WORKLOADS["tiny"]
+    b = sw.make_batch("tiny", seed)
+    w = sw.make_weights(wl.shape, seed, gain_jitter=gain_jitter)
+    x = sw.make_x(wl.shape, b.n_tokens, seed)
+    kp, vp = sw.make_kv_pool(wl.shape, b.num_blocks, seed)
+    ref = ol.layer_forward(wl.shape, w, x, b, kp, vp)
+    dev = dict(w=DeviceWeights(w, "cuda"), x=bf16_tensor(x, "cuda"), pool=DevicePool.from_host(kp, vp, "cuda"))
+    return wl, b, w, x, kp, vp, ref, dev
+
+
+def _check_layer(ctx, wl, b, kp, vp, ref, dev, y_dev):
+    from nano_intra_overlap_amd.device import bf16_bits
+
+    shape = wl.shape
+    y = f64(bf16_bits(y_dev))
+    assert np.isfinite(y).all()
+    assert rel_inf(y, ref["y"]) <= TOL, rel_inf(y, ref["y"])
+    attn = f64(_attn_buffer(ctx, b.n_tokens, shape.n_q * shape.head_dim))
+    assert rel_inf(attn, ref["attn"]) <= TOL, rel_inf(attn, ref["attn"])
+    kg, vg = dev["pool"].host_bits()
+    new = np.zeros((b.num_blocks, 16), bool)
+    for blk, off in ol.new_token_slots(b, 16):
+        new[blk, off] = True
+    # every other slot bitwise unchanged
+    assert np.array_equal(kg.transpose(0, 2, 1, 3)[~new], kp.transpose(0, 2, 1, 3)[~new])
+    assert np.array_equal(vg.transpose(0, 3, 1, 2)[~new], vp.transpose(0, 3, 1, 2)[~new])
+    # written slots hold the oracle's K/V within tolerance
+    kr, vr = ref["k_pool"], ref["v_pool"]
+    assert rel_inf(f64(kg.transpose(0, 2, 1, 3)[new]), f64(kr.transpose(0, 2, 1, 3)[new])) <= TOL
+    assert rel_inf(f64(vg.transpose(0, 3, 1, 2)[new]), f64(vr.transpose(0, 3, 1, 2)[new])) <= TOL
+
+
+def _plans(hb, T):
+    from nano_intra_overlap_amd import abi, plans
+
+    yield "null", None
+    yield "seq1", plans.sequential(hb, [0, T])
+    yield "seq2", plans.sequential(hb, [0, 39, T])
+    yield "overlap2", plans.overlap(hb, [0, 39, T])
+    yield "overlap2_masked", plans.overlap(hb, [0, 39, T], abi.cu_mask(per_xcd=24, offset=0),
+                                           abi.cu_mask(per_xcd=8, offset=24))
+    yield "overlap4_pf_compute", plans.overlap(hb, [0, 10, 20, 50, T], prefill_on_memory=False)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_tiny_layer_plans(ctx, seed):
+    wl, b, w, x, kp, vp, ref, dev = _tiny(seed)
+    from nano_intra_overlap_amd.device import DevicePool
+
+    for name, plan in _plans(_host_batch(b), b.n_tokens):
+        dev["pool"] = DevicePool.from_host(kp, vp, "cuda")
+        y_dev = torch.full_like(dev["x"], float("nan"))
+        log_case(f"tiny layer seed={seed} plan={name}")
+        _run_layer(ctx, wl.shape, dev["w"], dev["x"], y_dev, _host_batch(b), dev["pool"], plan)
+        _check_layer(ctx, wl, b, kp, vp, ref, dev, y_dev)
+
+
+def _host_batch(b):
+    from nano_intra_overlap_amd import abi
+
+    return abi.HostBatch.from_batch(b)
+
+
+def test_tiny_layer_in_place_output(ctx):
+    """y may alias x: rows are read before they are overwritten."""
+    from nano_intra_overlap_amd import plans
+
+    wl, b, w, x, kp, vp, ref, dev = _tiny(2)
+    for plan in (None, plans.overlap(_host_batch(b), [0, 39, b.n_tokens])):
+        from nano_intra_overlap_amd.device import DevicePool, bf16_tensor
+
+        dev["pool"] = DevicePool.from_host(kp, vp, "cuda")
+        xy = bf16_tensor(x, "cuda")
+        log_case("tiny layer in-place y=x")
+        _run_layer(ctx, wl.shape, dev["w"], xy, xy, _host_batch(b), dev["pool"], plan)
+        _check_layer(ctx, wl, b, kp, vp, ref, dev, xy)
+
+
+def test_tiny_layer_random_plans(ctx):
+    """Random nano-batch bounds, stream assignments and orders all reproduce the oracle."""
+    from nano_intra_overlap_amd import abi
+    from nano_intra_overlap_amd.device import DevicePool
+
+    wl, b, w, x, kp, vp, ref, dev = _tiny(3)
+    T = b.n_tokens
+    rng = np.random.default_rng(0)
+    for trial in range(12):
+        n = int(rng.integers(1, 5))
+        cuts = sorted(rng.choice(np.arange(1, T), size=n - 1, replace=False).tolist())
+        bounds = [0] + cuts + [T]
+        n_streams = int(rng.integers(1, 4))
+        listing = [(k, j) for k in range(5) for j in range(n)]  # kind-major: a valid order
+        plan0 = abi.HostPlan(bounds, [(k, j, 0) for k, j in listing], 1)
+        hb = _host_batch(b)
+        edges, _ = abi.nf_plan_dependencies(hb, plan0)
+        deps = {i: set() for i in range(5 * n)}
+        for i, j in edges:
+            deps[j].add(i)
+        # a random topological order, streams assigned at random: never deadlocks
+        done, order = set(), []
+        while len(order) < 5 * n:
+            ready = [i for i in range(5 * n) if i not in done and deps[i] <= done]
+            pick = int(rng.choice(ready))
+            done.add(pick)
+            order.append(pick)
+        ops = [(*listing[pick], int(rng.integers(0, n_streams))) for pick in order]
+        masks = None
+        if n_streams > 1 and trial % 2:
+            masks = [abi.cu_mask(per_xcd=32 // n_streams * (s + 1) - 32 // n_streams * s, offset=32 // n_streams * s)
+                     for s in range(n_streams)]
+        plan = abi.HostPlan(bounds, ops, n_streams, masks)
+        dev["pool"] = DevicePool.from_host(kp, vp, "cuda")
+        y_dev = torch.full_like(dev["x"], float("nan"))
+        log_case(f"tiny random plan {trial}: bounds={bounds} streams={n_streams}")
+        _run_layer(ctx, wl.shape, dev["w"], dev["x"], y_dev, hb, dev["pool"], plan)
+        _check_layer(ctx, wl, b, kp, vp, ref, dev, y_dev)
+
+
+def test_layer_rejects_bad_batch_without_touching_memory(ctx):
+    from nano_intra_overlap_amd import abi
+
+    wl, b, w, x, kp, vp, ref, dev = _tiny(4)
+    y_dev = torch.full_like(dev["x"], float("nan"))
+    bad = b.block_table.copy()
+    bad[0, 0] = b.num_blocks + 5
+    hb = abi.HostBatch(b.decode_ctx, b.prefill_len, b.prefill_prefix, bad)
+    log_case("tiny layer with an out-of-range block id")
+    with pytest.raises(abi.NanoflowError) as e:
+        _run_layer(ctx, wl.shape, dev["w"], dev["x"], y_dev, hb, dev["pool"], None)
+    assert e.value.status == abi.NF_E_BLOCK_RANGE
+    torch.cuda.synchronize()
+    assert torch.isnan(y_dev.float()).all()
+    kg, vg = dev["pool"].host_bits()
+    assert np.array_equal(kg, kp) and np.array_equal(vg, vp)
+
+
+# ------------------------------------------------------------------------------ full size
+
+
+def _full_size_case(name, seed, n_sample):
+    """GPU-resident full-size inputs and a sampled sub-batch for the oracle."""
+    from nano_intra_overlap_amd.device import DevicePool, DeviceWeights, bf16_tensor
+    from synth.workloads import make_kv_pool_torch
+
+    wl = sw.WORKLOADS[name]
+    shape = wl.shape
+    b = sw.make_batch(name, seed)
+    w = sw.make_weights(shape, seed)
+    x = sw.make_x(shape, b.n_tokens, seed)
+    k16, v16 = make_kv_pool_torch(shape, b.num_blocks, seed, device="cuda")
+    pool = DevicePool.from_int16(k16, v16)
+    rng = np.random.default_rng(seed + 99)
+    sample = sorted(rng.choice(b.n_decode, size=n_sample, replace=False).tolist()) + list(
+        range(b.n_decode, b.n_requests))
+    return wl, shape, b, w, x, DeviceWeights(w, "cuda"), bf16_tensor(x, "cuda"), pool, sample
+
+
+def _oracle_subbatch(shape, b, w, x, sample, seed):
+    """Run the oracle on the sampled requests with a compact pool of only their blocks."""
+    sub = b.select(sample)
+    ranges = ol.request_ranges(b)
+    rows = np.concatenate([np.arange(ranges[r][0], ranges[r][1]) for r in sample])
+    need = (sub.cached_lens() + sub.q_lens() + 15) // 16
+    used = sorted({int(sub.block_table[i, j]) for i in range(sub.n_requests) for j in range(int(need[i]))})
+    remap = {blk: i for i, blk in enumerate(used)}
+    bt = np.full_like(sub.block_table, -1)
+    for i in range(sub.n_requests):
+        for j in range(int(need[i])):
+            bt[i, j] = remap[int(sub.block_table[i, j])]
+    compact = sw.Batch(sub.decode_ctx, sub.prefill_len, sub.prefill_prefix, bt, len(used))
+    kp, vp = sw.make_kv_pool_blocks(shape, used, seed)
+    ref = ol.layer_forward(shape, w, x[rows], compact, kp, vp)
+    exact = ol.layer_forward(shape, w, x[rows], compact, kp, vp, storage="exact")
+    ref["y_exact"] = exact["y"]
+    return rows, used, compact, ref
+
+
+@pytest.mark.parametrize("name,seed,plan_kind", [
+    ("llama3_8b_layer", 0, "overlap2"),
+    ("llama3_8b_layer", 1, "null"),
+    ("llama2_70b_tp8_layer", 0, "overlap2"),
+])
+def test_full_size_layer_sampled(ctx, name, seed, plan_kind):
+    from nano_intra_overlap_amd import plans
+    from nano_intra_overlap_amd.device import bf16_bits
+    from synth.workloads import make_kv_pool_torch
+
+    wl, shape, b, w, x, w_dev, x_dev, pool, sample = _full_size_case(name, seed, n_sample=24)
+    T = b.n_tokens
+    plan = None if plan_kind == "null" else plans.overlap(_host_batch(b), plans.even_bounds(T, 2))
+    y_dev = torch.full_like(x_dev, float("nan"))
+    log_case(f"full-size layer {name} seed={seed} plan={plan_kind}")
+    _run_layer(ctx, shape, w_dev, x_dev, y_dev, _host_batch(b), pool, plan)
+    y = f64(bf16_bits(y_dev))
+    assert np.isfinite(y).all()
+
+    # untouched slots, over the whole pool, on the device
+    k0, v0 = make_kv_pool_torch(shape, b.num_blocks, seed, device="cuda")
+    changed_k = (pool.k.view(torch.int16) != k0).any(dim=3).any(dim=1)  # [nb, 16]
+    changed_v = (pool.v.view(torch.int16) != v0).any(dim=2).any(dim=1)
+    del k0, v0
+    new = torch.zeros((b.num_blocks, 16), dtype=torch.bool)
+    slots = ol.new_token_slots(b, 16)
+    new[[s[0] for s in slots], [s[1] for s in slots]] = True
+    new = new.cuda()
+    assert not (changed_k & ~new).any() and not (changed_v & ~new).any()
+    assert int(changed_k.sum()) == T and int(changed_v.sum()) == T
+
+    # sampled rows against the oracle
+    rows, used, compact, ref = _oracle_subbatch(shape, b, w, x, sample, seed)
+    print(f"[{name}] y rel err vs bf16-storage oracle {rel_inf(y[rows], ref['y']):.3e}, "
+          f"vs exact oracle {rel_inf(y[rows], ref['y_exact']):.3e}", flush=True)
+    assert rel_inf(y[rows], ref["y"]) <= TOL, rel_inf(y[rows], ref["y"])
+    attn = f64(_attn_buffer(ctx, T, shape.n_q * shape.head_dim))[rows]
+    assert rel_inf(attn, ref["attn"]) <= TOL, rel_inf(attn, ref["attn"])
+    idx = torch.as_tensor(used, device="cuda")
+    kg = pool.k[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+    vg = pool.v[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+    sl = ol.new_token_slots(compact, 16)
+    kgot = np.stack([kg[blk, :, off, :] for blk, off in sl])
+    kref = np.stack([ref["k_pool"][blk, :, off, :] for blk, off in sl])
+    vgot = np.stack([vg[blk, :, :, off] for blk, off in sl])
+    vref = np.stack([ref["v_pool"][blk, :, :, off] for blk, off in sl])
+    assert rel_inf(f64(kgot), f64(kref)) <= TOL
+    assert rel_inf(f64(vgot), f64(vref)) <= TOL

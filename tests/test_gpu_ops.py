@@ -1,0 +1,215 @@
+"""Per-operation parity of the HIP kernels against the CPU oracle, through the C ABI.
+
+Inputs are seeded; shapes span several tiles and ragged tails. Tolerance: max relative
+error 1e-2 per output tensor (bf16 storage, fp32 accumulation); KV slots bit-exact.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import layer as ol
+from synth import workloads as sw
+from tests.gpu_util import TOL, f64, log_case, rand_bf16, rel_inf
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    from nano_intra_overlap_amd import abi
+
+    c = abi.nf_ctx_create(0)
+    yield c
+    abi.nf_ctx_destroy(c)
+
+
+def _dev(bits):
+    from nano_intra_overlap_amd.device import bf16_tensor
+
+    return bf16_tensor(bits, "cuda")
+
+
+def _host(t):
+    from nano_intra_overlap_amd.device import bf16_bits
+
+    return bf16_bits(t)
+
+
+GEMM_SHAPES = [(1, 64, 64), (77, 520, 264), (300, 688, 688), (513, 1024, 256), (2048, 640, 512)]
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
+@pytest.mark.parametrize("epi", [0, 1, 2])
+def test_gemm_all_variants(ctx, m, n, k, epi):
+    from nano_intra_overlap_amd import abi
+
+    rng = np.random.default_rng(m * 31 + n * 7 + k + epi)
+    A = rand_bf16(rng, (m, k))
+    B = rand_bf16(rng, (2 * n if epi == 2 else n, k), 0.05)
+    R = rand_bf16(rng, (m, n))
+    ref = ol.linear(f64(A), f64(B))
+    if epi == 1:
+        ref = f64(R) + ref
+    if epi == 2:
+        ref = ol.swiglu(ref, n)
+    dA, dB, dR = _dev(A), _dev(B), _dev(R)
+    for v, (bm, bn, bk) in enumerate(abi.nf_gemm_variants()):
+        if epi == 2 and bn < 128:
+            continue
+        dC = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+        log_case(f"gemm m={m} n={n} k={k} epi={epi} variant={v}")
+        abi.nf_op_gemm(ctx, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), dR.data_ptr(), m, n, k, epi, v,
+                       torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        got = f64(_host(dC))
+        assert np.isfinite(got).all(), f"variant {v}: unwritten outputs"
+        err = rel_inf(got, ref)
+        assert err <= TOL, f"variant {v} ({bm}x{bn}x{bk}): rel err {err}"
+
+
+def test_gemm_residual_in_place(ctx):
+    from nano_intra_overlap_amd import abi
+
+    rng = np.random.default_rng(5)
+    m, n, k = 200, 256, 128
+    A, B, R = rand_bf16(rng, (m, k)), rand_bf16(rng, (n, k), 0.05), rand_bf16(rng, (m, n))
+    ref = f64(R) + ol.linear(f64(A), f64(B))
+    dA, dB, dR = _dev(A), _dev(B), _dev(R)  # keep every operand alive until the kernel ran
+    log_case("gemm residual aliasing C=R")
+    abi.nf_op_gemm(ctx, dA.data_ptr(), dB.data_ptr(), dR.data_ptr(), dR.data_ptr(), m, n, k, 1, -1,
+                   torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rel_inf(f64(_host(dR)), ref) <= TOL
+
+
+@pytest.mark.parametrize("m,n", [(1, 256), (78, 4096), (33, 8192), (5, 688)])
+def test_rmsnorm(ctx, m, n):
+    from nano_intra_overlap_amd import abi
+
+    rng = np.random.default_rng(m + n)
+    x = rand_bf16(rng, (m, n), 2.0)
+    g = sw.f32_to_bf16_bits(1.0 + 0.1 * rng.standard_normal(n).astype(np.float32))
+    ref = ol.rmsnorm(f64(x), f64(g), 1e-5)
+    dout = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    dx, dg = _dev(x), _dev(g)
+    log_case(f"rmsnorm m={m} n={n}")
+    abi.nf_op_rmsnorm(ctx, dx.data_ptr(), dg.data_ptr(), dout.data_ptr(), m, n, 1e-5,
+                      torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rel_inf(f64(_host(dout)), ref) <= TOL
+
+
+CANARY = 0x7FC1  # NaN pattern never produced by rounding finite values
+
+
+def _shape(n_q, n_kv, d, H=256):
+    return sw.Shape(hidden=H, n_q=n_q, n_kv=n_kv, head_dim=d, ffn=H)
+
+
+@pytest.mark.parametrize("n_q,n_kv,d", [(4, 2, 64), (32, 8, 128), (8, 1, 128)])
+def test_rope_kv_append_slots_bit_exact(ctx, n_q, n_kv, d):
+    from nano_intra_overlap_amd import abi
+    from nano_intra_overlap_amd.device import DevicePool
+
+    shape = _shape(n_q, n_kv, d)
+    rng = np.random.default_rng(n_q + d)
+    b = sw.batch_from_lengths(rng.integers(0, 300, 23), [37, 1, 16], [0, 5, 40], seed=3, spare_blocks=6)
+    T = b.n_tokens
+    qkv = rand_bf16(rng, (T, shape.qkv_rows), 1.3)
+    kp = np.full((b.num_blocks, n_kv, 16, d), CANARY, np.uint16)
+    vp = np.full((b.num_blocks, n_kv, d, 16), CANARY, np.uint16)
+    _, pos = ol.token_positions(b)
+    q = ol.rope(f64(qkv[:, : n_q * d]).reshape(T, n_q, d), pos, shape.rope_base)
+    k = ol.rope(f64(qkv[:, n_q * d : (n_q + n_kv) * d]).reshape(T, n_kv, d), pos, shape.rope_base)
+    v = f64(qkv[:, (n_q + n_kv) * d :]).reshape(T, n_kv, d)
+    k_ref, v_ref = ol.write_kv(kp, vp, b, 16, k, v)
+
+    dqkv = _dev(qkv)
+    pool = DevicePool.from_host(kp, vp, "cuda")
+    hb = abi.HostBatch.from_batch(b)
+    log_case(f"rope_kv n_q={n_q} n_kv={n_kv} d={d}")
+    abi.nf_op_rope_kv_append(ctx, abi.make_cfg(shape), dqkv.data_ptr(), hb, pool.desc,
+                             torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    kg, vg = pool.host_bits()
+    # the set of written slots is exactly the oracle's
+    wk = kg != CANARY
+    wv = vg != CANARY
+    assert np.array_equal(wk, k_ref != CANARY)
+    assert np.array_equal(wv, v_ref != CANARY)
+    # values: V is copied (bit-exact); K and q within tolerance
+    assert np.array_equal(vg, v_ref)
+    assert rel_inf(f64(kg[wk]), f64(k_ref[wk])) <= TOL
+    qg = f64(_host(dqkv)[:, : n_q * d]).reshape(T, n_q, d)
+    assert rel_inf(qg, q) <= TOL
+    # k, v columns of qkv are left as they were
+    assert np.array_equal(_host(dqkv)[:, n_q * d :], qkv[:, n_q * d :])
+
+
+def _attention_case(rng, n_q, n_kv, d, dec_ctx, pre_len, pre_prefix, seed):
+    b = sw.batch_from_lengths(dec_ctx, pre_len, pre_prefix, seed=seed, spare_blocks=3)
+    shape = _shape(n_q, n_kv, d)
+    T = b.n_tokens
+    kp, vp = sw.make_kv_pool(shape, b.num_blocks, seed)
+    # unused pool slots hold NaN canaries: masked keys must not leak them into outputs
+    used = np.zeros((b.num_blocks, 16), bool)
+    for r, n_keys in enumerate(b.cached_lens() + b.q_lens()):
+        for p in range(int(n_keys)):
+            used[b.block_table[r, p // 16], p % 16] = True
+    kp.transpose(0, 2, 1, 3)[~used] = CANARY
+    vp.transpose(0, 3, 1, 2)[~used] = CANARY
+    qkv = rand_bf16(rng, (T, shape.qkv_rows), 1.3)
+    return b, shape, qkv, kp, vp
+
+
+@pytest.mark.parametrize("n_q,n_kv,d", [(4, 2, 64), (32, 8, 128), (8, 1, 128), (16, 1, 64)])
+@pytest.mark.parametrize("split", [0, 1, 3, 64])
+def test_decode_attention(ctx, n_q, n_kv, d, split):
+    from nano_intra_overlap_amd import abi
+    from nano_intra_overlap_amd.device import DevicePool
+
+    rng = np.random.default_rng(n_q * 100 + d + split)
+    dec = np.concatenate([[0, 1, 15, 16, 17, 1023, 2047], rng.integers(0, 2500, 40)])
+    b, shape, qkv, kp, vp = _attention_case(rng, n_q, n_kv, d, dec, [], [], seed=split + 1)
+    T = b.n_tokens
+    q = f64(qkv[:, : n_q * d]).reshape(T, n_q, d)
+    ref = ol.attention_all(shape, b, q, kp, vp).reshape(T, n_q * d)
+    out = torch.full((T, n_q * d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    pool = DevicePool.from_host(kp, vp, "cuda")
+    dqkv = _dev(qkv)
+    log_case(f"decode attention n_q={n_q} n_kv={n_kv} d={d} split={split}")
+    abi.nf_op_attention(ctx, abi.make_cfg(shape), dqkv.data_ptr(), abi.HostBatch.from_batch(b), pool.desc,
+                        out.data_ptr(), True, split, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = f64(_host(out))
+    assert np.isfinite(got).all()
+    assert rel_inf(got, ref) <= TOL
+
+
+@pytest.mark.parametrize("n_q,n_kv,d", [(4, 2, 64), (32, 8, 128), (8, 1, 128)])
+def test_prefill_attention(ctx, n_q, n_kv, d):
+    from nano_intra_overlap_amd import abi
+    from nano_intra_overlap_amd.device import DevicePool
+
+    rng = np.random.default_rng(7 * n_q + d)
+    pre_len = [1, 15, 16, 17, 100, 300]
+    pre_prefix = [0, 0, 7, 0, 33, 0]
+    b, shape, qkv, kp, vp = _attention_case(rng, n_q, n_kv, d, [5, 9], pre_len, pre_prefix, seed=11)
+    T = b.n_tokens
+    q = f64(qkv[:, : n_q * d]).reshape(T, n_q, d)
+    ref = ol.attention_all(shape, b, q, kp, vp).reshape(T, n_q * d)
+    out = torch.full((T, n_q * d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    pool = DevicePool.from_host(kp, vp, "cuda")
+    dqkv = _dev(qkv)
+    log_case(f"prefill attention n_q={n_q} n_kv={n_kv} d={d}")
+    abi.nf_op_attention(ctx, abi.make_cfg(shape), dqkv.data_ptr(), abi.HostBatch.from_batch(b), pool.desc,
+                        out.data_ptr(), False, 0, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = f64(_host(out))
+    rows = np.arange(b.n_decode, T)
+    assert np.isfinite(got[rows]).all()
+    assert rel_inf(got[rows], ref[rows]) <= TOL
+    # decode rows were not touched by the prefill op
+    assert np.isnan(got[: b.n_decode]).all()
