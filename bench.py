@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of one nano-batched decoder-layer iteration on one MI355X.
+
+A step is one nf_layer_forward call over the dense batch (host batch layout and slot
+derivation, metadata upload, then every nano-operation: RMSNorm, KQV GEMM, rotary + KV
+append, decode and prefill attention, O GEMM + residual, RMSNorm, Up/Gate GEMM + SwiGLU,
+Down GEMM + residual), with weights, activations, KV pool and block table resident in HBM
+before the timed region starts.
+
+Prints one JSON line: tokens/s, the dominant kernel's roofline (live HIP-event timing on
+the stream it runs on), the fraction of the bf16 MFMA peak the layer reaches, the
+sequential single-stream baseline, and the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "tokens/s/GPU at 2048-token dense batch; % of bf16 MFMA roofline"
+PEAK_BF16 = 2.5e15  # dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12  # HBM3E, B/s
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="llama3_8b_layer")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--plan", default="overlap", choices=["overlap", "sequential", "null", "searched"])
+    p.add_argument("--n-nano", type=int, default=2)
+    p.add_argument("--mem-cus", type=int, default=0, help="CUs per XCD for the memory stream (0 = unmasked)")
+    p.add_argument("--plan-json", default="", help="plan written by nf_plan_search (with --plan searched)")
+    p.add_argument("--no-baseline", action="store_true", help="skip the sequential-schedule comparison")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-decode-sample", type=int, default=96)
+    return p.parse_args()
+
+
+def algorithmic(shape, b, n_nano):
+    """Algorithmic FLOPs and bytes of one layer iteration (per-unit figures x units)."""
+    H, nq, nkv, d, F = shape.hidden, shape.n_q, shape.n_kv, shape.head_dim, shape.ffn
+    T = b.n_tokens
+    p_layer = H * (nq + 2 * nkv) * d + nq * d * H + 3 * H * F  # weight elements of the GEMMs
+    gemm_flops = 2 * T * p_layer
+    ctx = b.decode_ctx.astype(np.int64)
+    kv_unit = 2 * nkv * d * 2  # bytes of K and V per key (all KV heads)
+    decode_keys = int((ctx + 1).sum())
+    decode_bytes = decode_keys * kv_unit + b.n_decode * (nq * d * 2) * 2  # KV stream + q in + o out
+    pre = b.prefill_len.astype(np.int64)
+    attn_flops = 4 * d * nq * (decode_keys + int((pre * (pre + 1) // 2).sum()))
+    weight_bytes = 2 * p_layer
+    act_bytes = T * H * 2 * 2 + T * 2 * nkv * d * 2  # x in, y out, new K/V written
+    return {
+        "gemm_flops": gemm_flops,
+        "attn_flops": attn_flops,
+        "decode_bytes": decode_bytes,
+        "decode_keys": decode_keys,
+        "kv_unit_bytes": kv_unit,
+        "layer_bytes": decode_bytes + int(pre.sum()) * kv_unit + n_nano * weight_bytes + act_bytes,
+        "p_layer": p_layer,
+    }
+
+
+def cpu_baseline(shape, b, w, x, seed, n_dec):
+    """The oracle as it stands, on the sampled decode requests plus the prefill chunks."""
+    from oracle import layer as ol
+    from synth import workloads as sw
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    rng = np.random.default_rng(seed + 7)
+    n_dec = min(n_dec, b.n_decode)
+    sample = sorted(rng.choice(b.n_decode, size=n_dec, replace=False).tolist()) + list(range(b.n_decode, b.n_requests))
+    sub = b.select(sample)
+    ranges = ol.request_ranges(b)
+    rows = np.concatenate([np.arange(ranges[r][0], ranges[r][1]) for r in sample])
+    need = (sub.cached_lens() + sub.q_lens() + 15) // 16
+    used = sorted({int(sub.block_table[i, j]) for i in range(sub.n_requests) for j in range(int(need[i]))})
+    remap = {blk: i for i, blk in enumerate(used)}
+    bt = np.full_like(sub.block_table, -1)
+    for i in range(sub.n_requests):
+        for j in range(int(need[i])):
+            bt[i, j] = remap[int(sub.block_table[i, j])]
+    compact = sw.Batch(sub.decode_ctx, sub.prefill_len, sub.prefill_prefix, bt, len(used))
+    kp, vp = sw.make_kv_pool_blocks(shape, used, seed)
+    xs = x[rows]
+    t0 = time.perf_counter()
+    ol.layer_forward(shape, w, xs, compact, kp, vp)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(len(rows) / dt, 2),
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{n_dec} of {b.n_decode} decode requests (sampled, seed {seed + 7}) + all "
+                  f"{b.n_prefill} prefill chunk(s) ({int(b.prefill_len.sum())} tokens) = {len(rows)} tokens, "
+                  f"one float64 layer pass in {dt:.2f} s on {os.cpu_count()} host CPUs",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from nano_intra_overlap_amd import abi, plans
+    from nano_intra_overlap_amd.device import DevicePool, DeviceWeights, bf16_tensor
+    from synth import workloads as sw
+    from synth.workloads import make_kv_pool_torch
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    wl = sw.WORKLOADS[args.workload]
+    shape = wl.shape
+    b = sw.make_batch(args.workload, args.seed)
+    T = b.n_tokens
+    log(f"workload {wl.name}: T={T}, decode={b.n_decode}, prefill={b.prefill_len.tolist()}, blocks={b.num_blocks}")
+    t0 = time.time()
+    w = sw.make_weights(shape, args.seed)
+    x = sw.make_x(shape, T, args.seed)
+    wd = DeviceWeights(w, "cuda")
+    xd = bf16_tensor(x, "cuda")
+    yd = torch.empty_like(xd)
+    k16, v16 = make_kv_pool_torch(shape, b.num_blocks, args.seed, device="cuda")
+    pool = DevicePool.from_int16(k16, v16)
+    bt_dev = torch.from_numpy(np.ascontiguousarray(b.block_table)).cuda()
+    hb = abi.HostBatch.from_batch(b, block_table_dev_ptr=bt_dev.data_ptr())
+    cfg = abi.make_cfg(shape)
+    torch.cuda.synchronize()
+    log(f"inputs resident in {time.time() - t0:.1f} s")
+
+    ctx = abi.nf_ctx_create(0)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def make_plan(kind):
+        if kind == "null":
+            return None, "sequential, one nano-batch, caller stream"
+        if kind == "sequential":
+            bounds = plans.even_bounds(T, args.n_nano)
+            return plans.sequential(hb, bounds), f"sequential, {len(bounds) - 1} nano-batches"
+        if kind == "searched":
+            text = open(args.plan_json).read()
+            plan, rec = plans.from_json(text)
+            return plan, f"searched: {rec.get('summary', '')}"
+        bounds = plans.even_bounds(T, args.n_nano)
+        masks = (None, None)
+        if args.mem_cus:
+            masks = (abi.cu_mask(per_xcd=32 - args.mem_cus, offset=0), abi.cu_mask(per_xcd=args.mem_cus,
+                                                                                     offset=32 - args.mem_cus))
+        desc = f"overlap, {len(bounds) - 1} nano-batches, bounds {bounds}, memory stream " + (
+            f"{args.mem_cus}/32 CUs per XCD" if args.mem_cus else "unmasked")
+        return plans.overlap(hb, bounds, *masks), desc
+
+    def run(plan, steps, warmup, timing_mask=0):
+        for _ in range(warmup):
+            abi.nf_layer_forward(ctx, cfg, wd.desc, xd.data_ptr(), yd.data_ptr(), hb, pool.desc, plan, stream)
+        torch.cuda.synchronize()
+        abi.nf_ctx_set_timing(ctx, timing_mask)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            abi.nf_layer_forward(ctx, cfg, wd.desc, xd.data_ptr(), yd.data_ptr(), hb, pool.desc, plan, stream)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        kernels = {}
+        for cls in range(abi.NF_K_CLASSES):
+            if timing_mask >> cls & 1:
+                n, tot, mn, mx = abi.nf_timing_summary(ctx, cls)
+                kernels[abi.KERNEL_CLASS_NAMES[cls]] = {"launches": n, "total_ms": tot, "min_ms": mn, "max_ms": mx}
+        abi.nf_ctx_set_timing(ctx, 0)
+        return ms, kernels
+
+    plan, plan_desc = make_plan(args.plan)
+    alg = algorithmic(shape, b, 1 if plan is None else len(plan.bounds) - 1)
+
+    # timed region: the whole step, with the dominant kernel (decode attention) bracketed
+    # by HIP events on its own stream
+    ms, kern = run(plan, args.steps, args.warmup, 1 << abi.NF_K_DECODE_ATTN)
+    dk = kern["decode_attn"]
+    launches_per_step = dk["launches"] / args.steps
+    dec_avg_ms = dk["total_ms"] / dk["launches"]
+    bytes_per_launch = alg["decode_bytes"] / launches_per_step
+    achieved = bytes_per_launch / (dec_avg_ms * 1e-3)
+    log(f"plan: {plan_desc}: {ms:.3f} ms/step; decode attention {dec_avg_ms:.3f} ms/launch "
+        f"x {launches_per_step:g} -> {achieved / 1e9:.0f} GB/s")
+
+    # per-kernel breakdown (separate instrumented pass; informational)
+    all_mask = (1 << abi.NF_K_CLASSES) - 1
+    _, breakdown = run(plan, 5, 1, all_mask)
+    for k, v in breakdown.items():
+        v["avg_ms"] = v["total_ms"] / max(v["launches"], 1)
+    flops_by = {
+        "gemm_kqv": 2 * T * shape.hidden * shape.qkv_rows,
+        "gemm_o": 2 * T * shape.q_width * shape.hidden,
+        "gemm_ug_swiglu": 2 * T * shape.hidden * 2 * shape.ffn,
+        "gemm_down": 2 * T * shape.ffn * shape.hidden,
+    }
+    for k, f in flops_by.items():
+        if k in breakdown and breakdown[k]["launches"]:
+            per_step_ms = breakdown[k]["total_ms"] / 5
+            breakdown[k]["tflops"] = round(f / (per_step_ms * 1e-3) / 1e12, 1)
+            breakdown[k]["mfma_frac"] = round(f / (per_step_ms * 1e-3) / PEAK_BF16, 4)
+
+    seq_ms = None
+    if not args.no_baseline and plan is not None:
+        seq_ms, _ = run(None, args.steps, args.warmup)
+        log(f"sequential single-stream baseline: {seq_ms:.3f} ms/step")
+
+    tokens_per_s = T / (ms * 1e-3)
+    layer_flops = alg["gemm_flops"] + alg["attn_flops"]
+    mfma_frac = alg["gemm_flops"] / (ms * 1e-3) / PEAK_BF16
+    t_lb = max(alg["gemm_flops"] / PEAK_BF16, alg["layer_bytes"] / PEAK_HBM)
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(shape, b, w, x, args.seed, args.cpu_decode_sample)
+        log(f"cpu oracle: {cpu['value']} tokens/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "dense_batch": T,
+            "n_decode": b.n_decode,
+            "prefill_len": b.prefill_len.tolist(),
+            "decode_ctx_range": list(wl.decode_ctx_range),
+            "seed": args.seed,
+            "plan": plan_desc,
+        },
+        "mfma_frac_of_bf16_peak": round(mfma_frac, 4),
+        "layer_gemm_tflops": round(alg["gemm_flops"] / (ms * 1e-3) / 1e12, 1),
+        "layer_roofline_frac": round(t_lb / (ms * 1e-3), 4),
+        "sequential_ms_per_step": None if seq_ms is None else round(seq_ms, 4),
+        "speedup_vs_sequential": None if seq_ms is None else round(seq_ms / ms, 4),
+        "roofline": {
+            "kernel": "decode_attn_kernel<128> (paged GQA decode attention, split-KV)",
+            "bound": "hbm",
+            "achieved": round(achieved / 1e9, 1),
+            "peak": PEAK_HBM / 1e9,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM, 4),
+            "traffic": None,
+            "bytes_per_launch": int(bytes_per_launch),
+            "avg_launch_ms": round(dec_avg_ms, 4),
+            "launches_per_step": launches_per_step,
+        },
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in breakdown.items()},
+        "cpu_baseline": cpu,
+    }
+    abi.nf_ctx_destroy(ctx)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

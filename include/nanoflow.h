@@ -218,6 +218,33 @@ nf_status nf_op_attention(nf_ctx *ctx, const nf_layer_cfg *cfg, const void *qkv,
                           const nf_batch_desc *batch, const nf_kv_pool *pool, void *out,
                           int32_t decode, int32_t kv_split_blocks, void *stream);
 
+/* ---- kernel timing ------------------------------------------------------------------------ */
+
+/* Kernel classes that can be timed. */
+enum {
+  NF_K_DECODE_ATTN = 0,    /* split-KV decode attention kernel              */
+  NF_K_DECODE_COMBINE = 1, /* split-KV merge kernel                          */
+  NF_K_PREFILL_ATTN = 2,   /* prefill attention kernel                       */
+  NF_K_GEMM_KQV = 3,
+  NF_K_GEMM_O = 4,
+  NF_K_GEMM_UG = 5,        /* Up/Gate GEMM with the SwiGLU epilogue           */
+  NF_K_GEMM_DOWN = 6,
+  NF_K_RMSNORM = 7,
+  NF_K_ROPE_KV = 8,
+  NF_K_CLASSES = 9
+};
+
+/* Start collecting kernel timings for the classes whose bit is set in class_mask (0 stops):
+ * every later launch of such a kernel by nf_layer_forward is bracketed by HIP timing events
+ * recorded on the stream the kernel runs on. Clears earlier records. Errors: NF_E_ARG.      */
+nf_status nf_ctx_set_timing(nf_ctx *ctx, uint32_t class_mask);
+
+/* Launch count and total / min / max duration (ms) of the recorded launches of class `cls`
+ * since the last nf_ctx_set_timing. Waits for those launches to finish. min_ms / max_ms may
+ * be NULL. Errors: NF_E_ARG, NF_E_HIP.                                                        */
+nf_status nf_timing_summary(nf_ctx *ctx, int32_t cls, int32_t *count, double *total_ms, double *min_ms,
+                            double *max_ms);
+
 /* ---- profiler and pipeline search (summary page, "Kernel Profiling and Interference
  *      Modeling"; "Auto-Search Stage I" and "Stage II") ----------------------------------- */
 

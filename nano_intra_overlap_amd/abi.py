@@ -31,6 +31,10 @@ STATUS_NAMES = {v: k for k, v in dict(globals()).items() if k.startswith("NF_E_"
 NF_CU_MASK_WORDS = 8
 NF_OP_KQV, NF_OP_DECATTN, NF_OP_PFATTN, NF_OP_O, NF_OP_UGD, NF_OP_KINDS = range(6)
 OP_NAMES = ["KQV", "DECATTN", "PFATTN", "O", "UGD"]
+(NF_K_DECODE_ATTN, NF_K_DECODE_COMBINE, NF_K_PREFILL_ATTN, NF_K_GEMM_KQV, NF_K_GEMM_O, NF_K_GEMM_UG, NF_K_GEMM_DOWN,
+ NF_K_RMSNORM, NF_K_ROPE_KV, NF_K_CLASSES) = range(10)
+KERNEL_CLASS_NAMES = ["decode_attn", "decode_combine", "prefill_attn", "gemm_kqv", "gemm_o", "gemm_ug_swiglu",
+                      "gemm_down", "rmsnorm", "rope_kv_append"]
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _u32p = ctypes.POINTER(ctypes.c_uint32)
@@ -106,6 +110,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                         ctypes.POINTER(ctypes.c_float), I, ctypes.c_char_p]),
         "nf_plan_search": (I, [ctypes.c_char_p, ctypes.c_char_p, ctypes.POINTER(nf_batch_desc), I, I,
                                ctypes.c_char_p, S]),
+        "nf_ctx_set_timing": (I, [V, ctypes.c_uint32]),
+        "nf_timing_summary": (I, [V, I, _i32p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                  ctypes.POINTER(ctypes.c_double)]),
         "nf_ctx_set_decode_split": (I, [V, I]),
         "nf_ctx_set_gemm_variant": (I, [V, I, I, I]),
     }
@@ -335,6 +342,19 @@ def nf_plan_search(dbest_json: str, rp_json: str, batch: HostBatch, max_nano: in
     if st != NF_OK:
         raise NanoflowError(st, buf.value.decode())
     return buf.value.decode()
+
+
+def nf_ctx_set_timing(ctx, class_mask: int) -> None:
+    _check(load().nf_ctx_set_timing(ctx, class_mask), ctx)
+
+
+def nf_timing_summary(ctx, cls: int):
+    """(count, total_ms, min_ms, max_ms) of the timed launches of a kernel class."""
+    n = ctypes.c_int32()
+    tot, mn, mx = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(load().nf_timing_summary(ctx, cls, ctypes.byref(n), ctypes.byref(tot), ctypes.byref(mn), ctypes.byref(mx)),
+           ctx)
+    return n.value, tot.value, mn.value, mx.value
 
 
 def nf_ctx_set_decode_split(ctx, blocks: int) -> None:

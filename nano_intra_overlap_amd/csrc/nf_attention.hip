@@ -283,9 +283,8 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(const bf16* __restric
 // ---------------------------------------------------------------------------------------
 
 hipError_t launch_decode_attn(const bf16* qkv, const bf16* kpool, const bf16* vpool, const int32_t* block_table,
-                              int max_blocks, const DecodeItem* items, int n_items, const CombineItem* combines,
-                              int n_combines, float* part_o, float* part_ml, bf16* out, int n_q, int n_kv, int d,
-                              hipStream_t s) {
+                              int max_blocks, const DecodeItem* items, int n_items, float* part_o, float* part_ml,
+                              bf16* out, int n_q, int n_kv, int d, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)d);
   const int waves = n_items * n_kv;
@@ -298,15 +297,21 @@ hipError_t launch_decode_attn(const bf16* qkv, const bf16* kpool, const bf16* vp
                        max_blocks, items, n_items, part_o, part_ml, out, n_q, n_kv, scale_log2);
   else
     return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || n_combines <= 0) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_combine(const CombineItem* combines, int n_combines, const float* part_o,
+                                 const float* part_ml, bf16* out, int n_q, int n_kv, int d, hipStream_t s) {
+  if (n_combines <= 0) return hipSuccess;
   const int cgrid = (n_combines * n_kv + 3) / 4;
   if (d == 128)
     hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(cgrid), dim3(256), 0, s, combines, n_combines, part_o,
                        part_ml, out, n_q, n_kv);
-  else
+  else if (d == 64)
     hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(cgrid), dim3(256), 0, s, combines, n_combines, part_o,
                        part_ml, out, n_q, n_kv);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

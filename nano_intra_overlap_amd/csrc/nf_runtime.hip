@@ -59,6 +59,15 @@ struct nf_ctx {
   std::vector<hipEvent_t> join_ev;
   int decode_split = kDefaultSplit;
   int gemm_variant[NF_OP_KINDS][2];  // per dense op kind: [0] first GEMM, [1] second (UGD down); -1 = default
+  // kernel timing: events recorded around instrumented kernel classes on their own stream
+  uint32_t timing_mask = 0;
+  struct TimedLaunch {
+    int32_t cls;
+    hipEvent_t start, stop;
+  };
+  std::vector<TimedLaunch> timed;
+  std::vector<hipEvent_t> timing_pool;  // timing-enabled events, reused
+  size_t timing_pool_used = 0;
 };
 
 namespace {
@@ -350,6 +359,35 @@ int pick_variant(nf_ctx* ctx, int kind, int which, int m, int n, int k, int epi)
   return gemm_default_variant(m, n, k, epi);
 }
 
+nf_status timing_event(nf_ctx* ctx, hipEvent_t* e) {
+  if (ctx->timing_pool_used == ctx->timing_pool.size()) {
+    hipEvent_t ev;
+    NF_HIP(ctx, hipEventCreate(&ev));
+    ctx->timing_pool.push_back(ev);
+  }
+  *e = ctx->timing_pool[ctx->timing_pool_used++];
+  return NF_OK;
+}
+
+// Launch `fn` on stream s, bracketed by timing events when its class is instrumented.
+template <class F>
+nf_status timed(nf_ctx* ctx, int cls, hipStream_t s, F fn) {
+  const bool on = (ctx->timing_mask >> cls) & 1u;
+  hipEvent_t a = nullptr, b = nullptr;
+  if (on) {
+    nf_status st = timing_event(ctx, &a);
+    if (st == NF_OK) st = timing_event(ctx, &b);
+    if (st != NF_OK) return st;
+    NF_HIP(ctx, hipEventRecord(a, s));
+  }
+  NF_HIP(ctx, fn());
+  if (on) {
+    NF_HIP(ctx, hipEventRecord(b, s));
+    ctx->timed.push_back({cls, a, b});
+  }
+  return NF_OK;
+}
+
 nf_status launch_op(nf_ctx* ctx, const LayerArgs& A, const PlanGraph& g, const NanoOp& op, const Meta& M,
                     hipStream_t s) {
   const nf_layer_cfg& c = *A.cfg;
@@ -364,46 +402,74 @@ nf_status launch_op(nf_ctx* ctx, const LayerArgs& A, const PlanGraph& g, const N
   bf16* a = static_cast<bf16*>(ctx->a.p);
   const bf16* const* wp = nullptr;
   (void)wp;
+  nf_status st = NF_OK;
+#define NF_TRY(expr)              \
+  do {                            \
+    if ((st = (expr)) != NF_OK) return st; \
+  } while (0)
   switch (op.kind) {
     case NF_OP_KQV: {
-      NF_HIP(ctx, launch_rmsnorm(A.x + (size_t)lo * H, static_cast<const bf16*>(A.w->g_attn), h + (size_t)lo * H, m, H,
-                                 c.rms_eps, s));
-      NF_HIP(ctx, launch_gemm(h + (size_t)lo * H, static_cast<const bf16*>(A.w->w_qkv), qkv + (size_t)lo * W, nullptr, m,
-                              W, H, 0, pick_variant(ctx, NF_OP_KQV, 0, m, W, H, 0), s));
-      NF_HIP(ctx, launch_rope_kv(qkv, M.d_pos, M.d_slot, M.d_inv_freq, static_cast<bf16*>(A.pool->k),
-                                 static_cast<bf16*>(A.pool->v), lo, hi, nq, nkv, d, s));
+      NF_TRY(timed(ctx, NF_K_RMSNORM, s, [&] {
+        return launch_rmsnorm(A.x + (size_t)lo * H, static_cast<const bf16*>(A.w->g_attn), h + (size_t)lo * H, m, H,
+                              c.rms_eps, s);
+      }));
+      NF_TRY(timed(ctx, NF_K_GEMM_KQV, s, [&] {
+        return launch_gemm(h + (size_t)lo * H, static_cast<const bf16*>(A.w->w_qkv), qkv + (size_t)lo * W, nullptr, m,
+                           W, H, 0, pick_variant(ctx, NF_OP_KQV, 0, m, W, H, 0), s);
+      }));
+      NF_TRY(timed(ctx, NF_K_ROPE_KV, s, [&] {
+        return launch_rope_kv(qkv, M.d_pos, M.d_slot, M.d_inv_freq, static_cast<bf16*>(A.pool->k),
+                              static_cast<bf16*>(A.pool->v), lo, hi, nq, nkv, d, s);
+      }));
       break;
     }
     case NF_OP_DECATTN: {
       const int i0 = M.dec_begin[op.nano], i1 = M.dec_begin[op.nano + 1];
       const int c0 = M.comb_begin[op.nano], c1 = M.comb_begin[op.nano + 1];
-      NF_HIP(ctx, launch_decode_attn(qkv, static_cast<const bf16*>(A.pool->k), static_cast<const bf16*>(A.pool->v),
-                                     M.d_bt, A.max_blocks, M.d_dec + i0, i1 - i0, M.d_comb + c0, c1 - c0,
-                                     static_cast<float*>(ctx->part_o.p), static_cast<float*>(ctx->part_ml.p), attn, nq,
-                                     nkv, d, s));
+      NF_TRY(timed(ctx, NF_K_DECODE_ATTN, s, [&] {
+        return launch_decode_attn(qkv, static_cast<const bf16*>(A.pool->k), static_cast<const bf16*>(A.pool->v),
+                                  M.d_bt, A.max_blocks, M.d_dec + i0, i1 - i0, static_cast<float*>(ctx->part_o.p),
+                                  static_cast<float*>(ctx->part_ml.p), attn, nq, nkv, d, s);
+      }));
+      if (c1 > c0)
+        NF_TRY(timed(ctx, NF_K_DECODE_COMBINE, s, [&] {
+          return launch_decode_combine(M.d_comb + c0, c1 - c0, static_cast<const float*>(ctx->part_o.p),
+                                       static_cast<const float*>(ctx->part_ml.p), attn, nq, nkv, d, s);
+        }));
       break;
     }
     case NF_OP_PFATTN: {
       const int i0 = M.pf_begin[op.nano], i1 = M.pf_begin[op.nano + 1];
-      NF_HIP(ctx, launch_prefill_attn(qkv, static_cast<const bf16*>(A.pool->k), static_cast<const bf16*>(A.pool->v),
-                                      M.d_bt, A.max_blocks, M.d_pf + i0, i1 - i0, attn, nq, nkv, d, s));
+      NF_TRY(timed(ctx, NF_K_PREFILL_ATTN, s, [&] {
+        return launch_prefill_attn(qkv, static_cast<const bf16*>(A.pool->k), static_cast<const bf16*>(A.pool->v),
+                                   M.d_bt, A.max_blocks, M.d_pf + i0, i1 - i0, attn, nq, nkv, d, s);
+      }));
       break;
     }
     case NF_OP_O: {
-      NF_HIP(ctx, launch_gemm(attn + (size_t)lo * nq * d, static_cast<const bf16*>(A.w->w_o), x1 + (size_t)lo * H,
-                              A.x + (size_t)lo * H, m, H, nq * d, 1, pick_variant(ctx, NF_OP_O, 0, m, H, nq * d, 1), s));
+      NF_TRY(timed(ctx, NF_K_GEMM_O, s, [&] {
+        return launch_gemm(attn + (size_t)lo * nq * d, static_cast<const bf16*>(A.w->w_o), x1 + (size_t)lo * H,
+                           A.x + (size_t)lo * H, m, H, nq * d, 1, pick_variant(ctx, NF_OP_O, 0, m, H, nq * d, 1), s);
+      }));
       break;
     }
     case NF_OP_UGD: {
-      NF_HIP(ctx, launch_rmsnorm(x1 + (size_t)lo * H, static_cast<const bf16*>(A.w->g_ffn), h2 + (size_t)lo * H, m, H,
-                                 c.rms_eps, s));
-      NF_HIP(ctx, launch_gemm(h2 + (size_t)lo * H, static_cast<const bf16*>(A.w->w_gate_up), a + (size_t)lo * F, nullptr,
-                              m, F, H, 2, pick_variant(ctx, NF_OP_UGD, 0, m, F, H, 2), s));
-      NF_HIP(ctx, launch_gemm(a + (size_t)lo * F, static_cast<const bf16*>(A.w->w_down), A.y + (size_t)lo * H,
-                              x1 + (size_t)lo * H, m, H, F, 1, pick_variant(ctx, NF_OP_UGD, 1, m, H, F, 1), s));
+      NF_TRY(timed(ctx, NF_K_RMSNORM, s, [&] {
+        return launch_rmsnorm(x1 + (size_t)lo * H, static_cast<const bf16*>(A.w->g_ffn), h2 + (size_t)lo * H, m, H,
+                              c.rms_eps, s);
+      }));
+      NF_TRY(timed(ctx, NF_K_GEMM_UG, s, [&] {
+        return launch_gemm(h2 + (size_t)lo * H, static_cast<const bf16*>(A.w->w_gate_up), a + (size_t)lo * F, nullptr,
+                           m, F, H, 2, pick_variant(ctx, NF_OP_UGD, 0, m, F, H, 2), s);
+      }));
+      NF_TRY(timed(ctx, NF_K_GEMM_DOWN, s, [&] {
+        return launch_gemm(a + (size_t)lo * F, static_cast<const bf16*>(A.w->w_down), A.y + (size_t)lo * H,
+                           x1 + (size_t)lo * H, m, H, F, 1, pick_variant(ctx, NF_OP_UGD, 1, m, H, F, 1), s);
+      }));
       break;
     }
   }
+#undef NF_TRY
   return NF_OK;
 }
 
@@ -455,6 +521,7 @@ extern "C" void nf_ctx_destroy(nf_ctx* ctx) {
   (void)hipDeviceSynchronize();
   for (auto& e : ctx->streams) (void)hipStreamDestroy(e.s);
   for (auto e : ctx->events) (void)hipEventDestroy(e);
+  for (auto e : ctx->timing_pool) (void)hipEventDestroy(e);
   for (auto e : ctx->join_ev) (void)hipEventDestroy(e);
   if (ctx->fork_ev) (void)hipEventDestroy(ctx->fork_ev);
   if (ctx->upload_done) (void)hipEventDestroy(ctx->upload_done);
@@ -626,13 +693,46 @@ extern "C" nf_status nf_op_attention(nf_ctx* ctx, const nf_layer_cfg* cfg, const
   if (decode) {
     NF_HIP(ctx, launch_decode_attn(static_cast<const bf16*>(qkv), static_cast<const bf16*>(pool->k),
                                    static_cast<const bf16*>(pool->v), M.d_bt, batch->max_blocks, M.d_dec,
-                                   (int)M.dec.size(), M.d_comb, (int)M.comb.size(), static_cast<float*>(ctx->part_o.p),
+                                   (int)M.dec.size(), static_cast<float*>(ctx->part_o.p),
                                    static_cast<float*>(ctx->part_ml.p), static_cast<bf16*>(out), nq, nkv, d, s));
+    NF_HIP(ctx, launch_decode_combine(M.d_comb, (int)M.comb.size(), static_cast<const float*>(ctx->part_o.p),
+                                      static_cast<const float*>(ctx->part_ml.p), static_cast<bf16*>(out), nq, nkv, d,
+                                      s));
   } else {
     NF_HIP(ctx, launch_prefill_attn(static_cast<const bf16*>(qkv), static_cast<const bf16*>(pool->k),
                                     static_cast<const bf16*>(pool->v), M.d_bt, batch->max_blocks, M.d_pf,
                                     (int)M.pf.size(), static_cast<bf16*>(out), nq, nkv, d, s));
   }
+  return NF_OK;
+}
+
+extern "C" nf_status nf_ctx_set_timing(nf_ctx* ctx, uint32_t class_mask) {
+  if (!ctx) return NF_E_ARG;
+  ctx->timing_mask = class_mask;
+  ctx->timed.clear();
+  ctx->timing_pool_used = 0;
+  return NF_OK;
+}
+
+extern "C" nf_status nf_timing_summary(nf_ctx* ctx, int32_t cls, int32_t* count, double* total_ms, double* min_ms,
+                                       double* max_ms) {
+  if (!ctx || cls < 0 || cls >= NF_K_CLASSES || !count || !total_ms) return NF_E_ARG;
+  int32_t n = 0;
+  double tot = 0.0, mn = 1e300, mx = 0.0;
+  for (auto& t : ctx->timed) {
+    if (t.cls != cls) continue;
+    NF_HIP(ctx, hipEventSynchronize(t.stop));
+    float ms = 0.0f;
+    NF_HIP(ctx, hipEventElapsedTime(&ms, t.start, t.stop));
+    ++n;
+    tot += ms;
+    mn = std::min(mn, (double)ms);
+    mx = std::max(mx, (double)ms);
+  }
+  *count = n;
+  *total_ms = tot;
+  if (min_ms) *min_ms = n ? mn : 0.0;
+  if (max_ms) *max_ms = n ? mx : 0.0;
   return NF_OK;
 }
 
