@@ -7,9 +7,10 @@
 // weight [out][in] (k contiguous), so both operands stream along k.
 //
 // Structure: a workgroup of 4 waves computes a BM x BN tile; waves form a 2 x 2 grid, each
-// owning a (BM/2) x (BN/2) sub-tile built from 32x32x16 bf16 MFMAs. k advances in slabs of
-// BK staged through LDS (padded rows, conflict-free 16-byte fragment reads), double
-// buffered: the next slab is fetched into registers while the current one is multiplied.
+// owning a (BM/2) x (BN/2) sub-tile built from 32x32x16 bf16 MFMAs. Two pipelines:
+//  - gemm_pipe_kernel (K a multiple of 32, the layer's shapes): the load unit writes a ring
+//    of 4 LDS slabs directly (no register staging), 3 slabs ahead of the MFMAs;
+//  - gemm_kernel (any K multiple of 8): register-staged, padded LDS, double buffered.
 // Tiles are ordered so that consecutive tiles share rows of A and columns of B, and that
 // consecutive tiles land on the same XCD (workgroups are dealt round-robin to the 8 XCDs,
 // each with its own L2).
@@ -191,6 +192,191 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16* __restrict__ A, c
 }
 
 // ---------------------------------------------------------------------------------------
+// Pipelined variant: global -> LDS with the load unit writing LDS directly
+// (global_load_lds_dwordx4: lane l lands at LDS base + 16 l), a ring of STAGES slabs of
+// BK = 32, loads issued STAGES-1 slabs ahead of the MFMAs. Rows of a slab hold 4 chunks
+// of 16 bytes; chunk slot s of row r holds k-chunk s ^ f(r), f(r) = ((r >> 2) & 3) ^ (r & 2),
+// which makes the fragment reads (32 rows, one k-chunk) hit distinct banks for both 8- and
+// 16-lane LDS read phases. Rows past M / N are clamped to the last valid row (their results
+// are never stored); K must be a multiple of 32.
+// ---------------------------------------------------------------------------------------
+
+__device__ __forceinline__ int swz(int row) { return ((row >> 2) & 3) ^ (row & 2); }
+
+// s_waitcnt vmcnt(n) with expcnt / lgkmcnt left free (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int BM, int BN, int STAGES, int EPI>
+__global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, bf16* C,
+                                                        const bf16* R, int M, int N, int K, int tiles_m, int tiles_n,
+                                                        int per_xcd) {
+  constexpr int BK = 32;
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int A_CH = BM * 4, B_CH = BN * 4;       // 16-byte chunks per slab
+  constexpr int STAGE_BYTES = (A_CH + B_CH) * 16;
+  constexpr int A_LOADS = A_CH / 256, B_LOADS = B_CH / 256;  // per thread (= per wave instruction count)
+  constexpr int NL = A_LOADS + B_LOADS;
+  static_assert(EPI != EPI_SWIGLU || (WTN % 64) == 0, "SwiGLU needs gate/up pairs of 32 columns");
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+
+  const int w = blockIdx.x;
+  const int t = (w % kNumXcd) * per_xcd + (w / kNumXcd);
+  const int ntiles = tiles_m * tiles_n;
+  if (t >= ntiles) return;
+  constexpr int GM = 8;
+  const int group = t / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gm = min(GM, tiles_m - first_m);
+  const int in_group = t % (GM * tiles_n);
+  const int tile_m = first_m + in_group % gm;
+  const int tile_n = in_group / gm;
+  const int m0 = tile_m * BM;
+  const int n0 = (EPI == EPI_SWIGLU) ? tile_n * (BN / 2) : tile_n * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // per-thread source rows of the direct loads (fixed across k): chunk c = (i*4 + wave)*64 + lane
+  const bf16* a_src[A_LOADS];
+  const bf16* b_src[B_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int c = (i * 4 + wave) * 64 + lane;
+    const int row = c >> 2, kc = (c & 3) ^ swz(row);
+    const int gr = min(m0 + row, M - 1);
+    a_src[i] = A + (size_t)gr * K + kc * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) {
+    const int c = (i * 4 + wave) * 64 + lane;
+    const int row = c >> 2, kc = (c & 3) ^ swz(row);
+    int gr;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int sl = row / WTN, tt = row % WTN, p = tt / 64, u = tt % 64;
+      const int col = min(n0 + sl * (WTN / 2) + p * 32 + (u & 31), N - 1);
+      gr = (u < 32) ? col : N + col;
+    } else {
+      gr = min(n0 + row, N - 1);
+    }
+    b_src[i] = B + (size_t)gr * K + kc * 8;
+  }
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto issue = [&](int kt) {
+    lds_void* base = (lds_void*)(smem_raw + (kt % STAGES) * STAGE_BYTES);
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + k0),
+                                       (lds_void*)((unsigned char __attribute__((address_space(3)))*)base +
+                                                   ((i * 4 + wave) * 64) * 16),
+                                       16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + k0),
+                                       (lds_void*)((unsigned char __attribute__((address_space(3)))*)base + A_CH * 16 +
+                                                   ((i * 4 + wave) * 64) * 16),
+                                       16, 0, 0);
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = K / BK;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s);
+
+  // fragment read offsets (bytes within a slab): row (l % 32) of each 32-row tile, k-chunk 2 kk + l / 32
+  const int fr = lane & 31, fk = lane >> 5;
+  int a_off[TM][2], b_off[TN][2];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int row = wm * WTM + i * 32 + fr;
+      a_off[i][kk] = row * 64 + (((2 * kk + fk) ^ swz(row)) * 16);
+    }
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int row = wn * WTN + j * 32 + fr;
+      b_off[j][kk] = A_CH * 16 + row * 64 + (((2 * kk + fk) ^ swz(row)) * 16);
+    }
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // slab kt landed for this wave once at most the loads of the newer in-flight slabs remain
+    const int newer = min(STAGES - 2, nk - 1 - kt);
+    if (newer >= STAGES - 2) wait_vmcnt<NL * (STAGES - 2)>();
+    else if (newer == 1) wait_vmcnt<NL>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+    const unsigned char* slab = smem_raw + (kt % STAGES) * STAGE_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(slab + a_off[i][kk]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(slab + b_off[j][kk]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  const int col_l = lane & 31;
+  const int row_l = (lane >> 5) * 4;
+  if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int p = 0; p < TN / 2; ++p) {
+        const int col = n0 + wn * (WTN / 2) + p * 32 + col_l;
+        if (col >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * WTM + i * 32 + (r / 4) * 8 + row_l + (r % 4);
+          if (row < M) C[(size_t)row * N + col] = (bf16)(silu_f(acc[i][2 * p][r]) * acc[i][2 * p + 1][r]);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = n0 + wn * WTN + j * 32 + col_l;
+        if (col >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * WTM + i * 32 + (r / 4) * 8 + row_l + (r % 4);
+          if (row < M) {
+            float v = acc[i][j][r];
+            if constexpr (EPI == EPI_RESID) v += (float)R[(size_t)row * N + col];
+            C[(size_t)row * N + col] = (bf16)v;
+          }
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 
 static const GemmVariant kVariants[] = {
     {128, 128, 64},  // 0
@@ -199,14 +385,35 @@ static const GemmVariant kVariants[] = {
     {256, 256, 64},  // 3
     {64, 128, 64},   // 4
     {128, 64, 64},   // 5
+    // pipelined (direct-to-LDS, 4 slabs of 32), K % 32 == 0
+    {256, 256, 32},  // 6
+    {256, 128, 32},  // 7
+    {128, 256, 32},  // 8
+    {128, 128, 32},  // 9
 };
 static constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 int gemm_variant_count() { return kNumVariants; }
 GemmVariant gemm_variant(int i) { return kVariants[i]; }
 
+bool gemm_variant_supported(int v, int m, int n, int k, int epilogue) {
+  if (v < 0 || v >= kNumVariants) return false;
+  if (epilogue == EPI_SWIGLU && kVariants[v].bn < 128) return false;
+  if (v >= 6 && (k % 32 != 0)) return false;
+  (void)m;
+  (void)n;
+  return true;
+}
+
 int gemm_default_variant(int m, int n, int k, int epilogue) {
-  (void)k;
+  if (k % 32 == 0 && m >= 64) {
+    // pipelined tiles (measured on MI355X at the layer's shapes): 256x256 once there are
+    // enough tiles to cover most of the 256 CUs, else 128x128
+    const int nn = epilogue == EPI_SWIGLU ? 2 * n : n;
+    auto tiles = [&](int bm, int bn) { return ((m + bm - 1) / bm) * ((nn + bn - 1) / bn); };
+    if (tiles(256, 256) >= (epilogue == EPI_SWIGLU ? 128 : 192)) return 6;
+    return 9;
+  }
   // enough tiles to cover the 256 CUs at least once; otherwise smaller tiles
   auto tiles = [&](int v) {
     const GemmVariant g = kVariants[v];
@@ -240,6 +447,38 @@ static hipError_t launch_t(const bf16* A, const bf16* B, bf16* C, const bf16* R,
   return hipGetLastError();
 }
 
+template <int BM, int BN, int STAGES, int EPI>
+static hipError_t launch_pipe_t(const bf16* A, const bf16* B, bf16* C, const bf16* R, int M, int N, int K,
+                                hipStream_t s) {
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (EPI == EPI_SWIGLU) ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
+  const int ntiles = tiles_m * tiles_n;
+  const int per_xcd = (ntiles + kNumXcd - 1) / kNumXcd;
+  const size_t lds = (size_t)STAGES * (BM + BN) * 64;
+  auto kern = gemm_pipe_kernel<BM, BN, STAGES, EPI>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(per_xcd * kNumXcd), dim3(256), lds, s, A, B, C, R, M, N, K, tiles_m, tiles_n,
+                     per_xcd);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int STAGES>
+static hipError_t launch_pipe(const bf16* A, const bf16* B, bf16* C, const bf16* R, int M, int N, int K, int epi,
+                              hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE: return launch_pipe_t<BM, BN, STAGES, EPI_STORE>(A, B, C, R, M, N, K, s);
+    case EPI_RESID: return launch_pipe_t<BM, BN, STAGES, EPI_RESID>(A, B, C, R, M, N, K, s);
+    case EPI_SWIGLU: return launch_pipe_t<BM, BN, STAGES, EPI_SWIGLU>(A, B, C, R, M, N, K, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int BM, int BN, int BK>
 static hipError_t launch_epi(const bf16* A, const bf16* B, bf16* C, const bf16* R, int M, int N, int K,
                              int epi, hipStream_t s) {
@@ -263,6 +502,10 @@ hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int
     case 3: return launch_epi<256, 256, 64>(A, B, C, R, m, n, k, epilogue, s);
     case 4: return launch_epi<64, 128, 64>(A, B, C, R, m, n, k, epilogue, s);
     case 5: return launch_epi<128, 64, 64>(A, B, C, R, m, n, k, epilogue, s);
+    case 6: return launch_pipe<256, 256, 4>(A, B, C, R, m, n, k, epilogue, s);
+    case 7: return launch_pipe<256, 128, 4>(A, B, C, R, m, n, k, epilogue, s);
+    case 8: return launch_pipe<128, 256, 4>(A, B, C, R, m, n, k, epilogue, s);
+    case 9: return launch_pipe<128, 128, 4>(A, B, C, R, m, n, k, epilogue, s);
   }
   return hipErrorInvalidValue;
 }

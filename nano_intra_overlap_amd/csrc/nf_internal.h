@@ -68,6 +68,7 @@ struct GemmVariant {
 int gemm_variant_count();
 GemmVariant gemm_variant(int i);
 int gemm_default_variant(int m, int n, int k, int epilogue);
+bool gemm_variant_supported(int v, int m, int n, int k, int epilogue);
 // C = A B^T (+ epilogue); returns hipError_t of the launch.
 hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int m, int n, int k,
                        int epilogue, int variant, hipStream_t s);

@@ -353,9 +353,7 @@ struct LayerArgs {
 
 int pick_variant(nf_ctx* ctx, int kind, int which, int m, int n, int k, int epi) {
   const int v = ctx->gemm_variant[kind][which];
-  if (v >= 0 && v < gemm_variant_count()) {
-    if (!(epi == 2 && gemm_variant(v).bn < 128)) return v;
-  }
+  if (gemm_variant_supported(v, m, n, k, epi)) return v;
   return gemm_default_variant(m, n, k, epi);
 }
 
@@ -631,8 +629,8 @@ extern "C" nf_status nf_op_gemm(nf_ctx* ctx, const void* A, const void* B, void*
     ctx->err = "nf_op_gemm: n and k must be multiples of 8";
     return NF_E_UNSUPPORTED;
   }
-  if (variant >= gemm_variant_count() || (variant >= 0 && epilogue == 2 && gemm_variant(variant).bn < 128)) {
-    ctx->err = "nf_op_gemm: variant out of range for this epilogue";
+  if (variant >= 0 && !gemm_variant_supported(variant, m, n, k, epilogue)) {
+    ctx->err = "nf_op_gemm: variant not available for this epilogue / k";
     return NF_E_ARG;
   }
   const int v = variant < 0 ? gemm_default_variant(m, n, k, epilogue) : variant;

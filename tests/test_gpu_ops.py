@@ -37,7 +37,15 @@ def _host(t):
     return bf16_bits(t)
 
 
-GEMM_SHAPES = [(1, 64, 64), (77, 520, 264), (300, 688, 688), (513, 1024, 256), (2048, 640, 512)]
+GEMM_SHAPES = [(1, 64, 64), (77, 520, 264), (300, 688, 688), (513, 1024, 256), (2048, 640, 512), (77, 520, 256),
+               (300, 688, 672), (1, 256, 96)]
+# the layer's shapes (K, N of each projection at the 8B and 70B-share sizes), checked on sampled rows
+LAYER_GEMMS = [(1024, 6144, 4096, 0), (2048, 4096, 4096, 1), (1536, 14336, 4096, 2), (1024, 4096, 14336, 1),
+               (2048, 10240, 8192, 0), (512, 3584, 8192, 2), (2048, 8192, 3584, 1)]
+
+
+def _supported(v, k, epi, bn):
+    return not (epi == 2 and bn < 128) and not (v >= 6 and k % 32)
 
 
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
@@ -56,7 +64,7 @@ def test_gemm_all_variants(ctx, m, n, k, epi):
         ref = ol.swiglu(ref, n)
     dA, dB, dR = _dev(A), _dev(B), _dev(R)
     for v, (bm, bn, bk) in enumerate(abi.nf_gemm_variants()):
-        if epi == 2 and bn < 128:
+        if not _supported(v, k, epi, bn):
             continue
         dC = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
         log_case(f"gemm m={m} n={n} k={k} epi={epi} variant={v}")
@@ -67,6 +75,35 @@ def test_gemm_all_variants(ctx, m, n, k, epi):
         assert np.isfinite(got).all(), f"variant {v}: unwritten outputs"
         err = rel_inf(got, ref)
         assert err <= TOL, f"variant {v} ({bm}x{bn}x{bk}): rel err {err}"
+
+
+@pytest.mark.parametrize("m,n,k,epi", LAYER_GEMMS)
+def test_gemm_layer_shapes_sampled_rows(ctx, m, n, k, epi):
+    from nano_intra_overlap_amd import abi
+
+    rng = np.random.default_rng(m + n + k + epi)
+    A = rand_bf16(rng, (m, k))
+    B = rand_bf16(rng, (2 * n if epi == 2 else n, k), 0.02)
+    R = rand_bf16(rng, (m, n))
+    rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, 40, replace=False)]))
+    ref = ol.linear(f64(A[rows]), f64(B))
+    if epi == 1:
+        ref = f64(R[rows]) + ref
+    if epi == 2:
+        ref = ol.swiglu(ref, n)
+    dA, dB, dR = _dev(A), _dev(B), _dev(R)
+    for v, (bm, bn, bk) in [(-1, (0, 0, 0))] + list(enumerate(abi.nf_gemm_variants())):
+        if v >= 0 and (not _supported(v, k, epi, bn) or v < 6):
+            continue
+        dC = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+        log_case(f"gemm layer shape m={m} n={n} k={k} epi={epi} variant={v}")
+        abi.nf_op_gemm(ctx, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), dR.data_ptr(), m, n, k, epi, v,
+                       torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        full = _host(dC)
+        assert not np.isnan(f64(full)).any(), f"variant {v}: unwritten outputs"
+        err = rel_inf(f64(full[rows]), ref)
+        assert err <= TOL, f"variant {v}: rel err {err}"
 
 
 def test_gemm_residual_in_place(ctx):
