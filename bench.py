@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--no-baseline", action="store_true", help="skip the sequential-schedule comparison")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-decode-sample", type=int, default=96)
+    p.add_argument("--decode-grid", type=int, default=0, help="max decode-attention workgroups (0 = one wave per unit)")
+    p.add_argument("--decode-nbuf", type=int, default=2, choices=[1, 2, 4], help="KV blocks per softmax step")
+    p.add_argument("--gemm-variant", type=int, default=-1, help="force one GEMM tile variant for every GEMM")
     return p.parse_args()
 
 
@@ -153,6 +156,11 @@ def main():
 
     ctx = abi.nf_ctx_create(0)
     stream = torch.cuda.current_stream().cuda_stream
+    abi.nf_ctx_set_decode_launch(ctx, args.decode_grid, args.decode_nbuf)
+    if args.gemm_variant >= 0:
+        for kind in (abi.NF_OP_KQV, abi.NF_OP_O, abi.NF_OP_UGD):
+            for which in (0, 1):
+                abi.nf_ctx_set_gemm_variant(ctx, kind, which, args.gemm_variant)
 
     def make_plan(kind):
         if kind == "null":
@@ -262,6 +270,9 @@ def main():
             "decode_ctx_range": list(wl.decode_ctx_range),
             "seed": args.seed,
             "plan": plan_desc,
+            "decode_grid": args.decode_grid,
+            "decode_nbuf": args.decode_nbuf,
+            "gemm_variant": args.gemm_variant,
         },
         "mfma_frac_of_bf16_peak": round(mfma_frac, 4),
         "layer_gemm_tflops": round(alg["gemm_flops"] / (ms * 1e-3) / 1e12, 1),

@@ -115,6 +115,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                   ctypes.POINTER(ctypes.c_double)]),
         "nf_ctx_set_decode_split": (I, [V, I]),
         "nf_ctx_set_gemm_variant": (I, [V, I, I, I]),
+        "nf_ctx_set_decode_launch": (I, [V, I, I]),
     }
     missing = []
     for name, (res, args) in sig.items():
@@ -359,6 +360,10 @@ def nf_timing_summary(ctx, cls: int):
 
 def nf_ctx_set_decode_split(ctx, blocks: int) -> None:
     _check(load().nf_ctx_set_decode_split(ctx, blocks), ctx)
+
+
+def nf_ctx_set_decode_launch(ctx, max_workgroups: int, nbuf: int = 2) -> None:
+    _check(load().nf_ctx_set_decode_launch(ctx, max_workgroups, nbuf), ctx)
 
 
 def nf_ctx_set_gemm_variant(ctx, kind: int, which: int, variant: int) -> None:

@@ -46,77 +46,112 @@ struct KvFrag {
   bf16x4 v[D / 16];
 };
 
+// K/V are streamed once per iteration: nontemporal loads keep them from displacing the
+// GEMMs' weight tiles in L2 and the last-level cache while both run.
 template <int D>
 __device__ __forceinline__ void load_block(KvFrag<D>& f, const bf16* __restrict__ kpool, const bf16* __restrict__ vpool,
                                            int blk, int n_kv, int g, int i16, int grp) {
   const bf16* kb = kpool + ((size_t)blk * n_kv + g) * (kBlock * D);
   const bf16* vb = vpool + ((size_t)blk * n_kv + g) * (D * kBlock);
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c) f.k[c] = *reinterpret_cast<const bf16x8*>(kb + i16 * D + c * 32 + grp * 8);
+  for (int c = 0; c < D / 32; ++c)
+    f.k[c] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(kb + i16 * D + c * 32 + grp * 8));
 #pragma unroll
   for (int dc = 0; dc < D / 16; ++dc)
-    f.v[dc] = *reinterpret_cast<const bf16x4*>(vb + (dc * 16 + i16) * kBlock + grp * 4);
+    f.v[dc] = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(vb + (dc * 16 + i16) * kBlock + grp * 4));
 }
 
-// Process one block whose first key is at sequence position key0. Column limit: key k is
-// visible to this lane's column iff k <= limit. Keys at or beyond n_keys hold no data:
-// their values are zeroed so that stale pool contents cannot leak through 0 * NaN.
-template <int D>
-__device__ __forceinline__ void attend_block(AttnState<D>& st, KvFrag<D>& f, const bf16x8* qf, int key0, int limit,
-                                             int n_keys, float scale_log2, int grp) {
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+// Process NB consecutive blocks (16*NB keys starting at sequence position key0) in one
+// online-softmax step: the NB score tiles are independent MFMAs, then one running-max /
+// rescale update for all of them, then the NB value products. Column limit: key k is
+// visible to this lane's column iff k <= limit.
+template <int D, int NB>
+__device__ __forceinline__ void attend_group(AttnState<D>& st, const KvFrag<D> (&f)[NB], const bf16x8* qf, int key0,
+                                             int limit, float scale_log2, int grp) {
+  float sv[NB][4];
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k[c], qf[c], s, 0, 0, 0);
-  const int kbase = key0 + grp * 4;
-  float sv[4];
+  for (int j = 0; j < NB; ++j) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int r = 0; r < 4; ++r) sv[r] = (kbase + r <= limit) ? s[r] * scale_log2 : -INFINITY;
-  float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    for (int c = 0; c < D / 32; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f[j].k[c], qf[c], s, 0, 0, 0);
+    const int kbase = key0 + j * kBlock + grp * 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[j][r] = (kbase + r <= limit) ? s[r] * scale_log2 : -INFINITY;
+  }
+  float bm = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) bm = fmaxf(bm, fmaxf(fmaxf(sv[j][0], sv[j][1]), fmaxf(sv[j][2], sv[j][3])));
   bm = wave_max16(bm);
   const float m_new = fmaxf(st.m, bm);
   // a column whose keys are all masked so far keeps m = -inf; use 0 as the reference then
   const float ref = (m_new == -INFINITY) ? 0.0f : m_new;
   const float corr = exp2f(st.m - ref);
-  float p[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) p[r] = exp2f(sv[r] - ref);
-  st.l = st.l * corr + ((p[0] + p[1]) + (p[2] + p[3]));
   st.m = m_new;
-  bf16x4 pf;
+  bf16x4 pf[NB];
+  float lsum = 0.0f;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) pf[r] = (bf16)p[r];
-  if (key0 + kBlock > n_keys) {
-    // partial last block: zero values of keys past the sequence end
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = exp2f(sv[j][r] - ref);
+      lsum += p;
+      pf[j][r] = (bf16)p;
+    }
+  st.l = st.l * corr + lsum;
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc) st.o[dc] *= corr;
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (kbase + r >= n_keys) f.v[dc][r] = (bf16)0.0f;
-  }
-#pragma unroll
-  for (int dc = 0; dc < D / 16; ++dc) {
-    st.o[dc] *= corr;
-    st.o[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(f.v[dc], pf, st.o[dc], 0, 0, 0);
-  }
+      st.o[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(f[j].v[dc], pf[j], st.o[dc], 0, 0, 0);
 }
 
-// Walk logical blocks [b0, b1) of block-table row `bt_row`, with a prefetch of one block.
-template <int D>
+template <int D, int NB>
+__device__ __forceinline__ void load_group(KvFrag<D> (&f)[NB], const bf16* __restrict__ kpool,
+                                           const bf16* __restrict__ vpool, int my_blk, int b, int nb, int n_kv, int g,
+                                           int i16, int grp) {
+#pragma unroll
+  for (int j = 0; j < NB; ++j) load_block<D>(f[j], kpool, vpool, __shfl(my_blk, min(b + j, nb - 1), 64), n_kv, g, i16, grp);
+}
+
+// Walk logical blocks [b0, b1) of block-table row `bt_row` (a request with n_keys keys).
+// Full blocks stream in groups of NB through two register buffers (the next group is in
+// flight while the current one is multiplied). The loop body has no branches, which keeps
+// the compiler's memory wait counts exact: loads past the range repeat its last block (a
+// cache hit) and those phantom blocks are masked out. A partial last block is handled
+// after the loop, with the values of keys past the sequence end zeroed so that stale pool
+// contents cannot leak through 0 * NaN.
+template <int D, int NB>
 __device__ __forceinline__ void attend_range(AttnState<D>& st, const bf16x8* qf, const int32_t* __restrict__ bt_row,
                                              int b0, int b1, const bf16* __restrict__ kpool,
                                              const bf16* __restrict__ vpool, int n_kv, int g, int limit, int n_keys,
                                              float scale_log2, int lane) {
   const int i16 = lane & 15, grp = lane >> 4;
-  for (int base = b0; base < b1; base += 64) {
-    const int nb = min(64, b1 - base);
-    const int my_blk = (lane < nb) ? bt_row[base + lane] : 0;
-    KvFrag<D> cur, nxt;
-    load_block<D>(cur, kpool, vpool, __shfl(my_blk, 0, 64), n_kv, g, i16, grp);
-    for (int b = 0; b < nb; ++b) {
-      if (b + 1 < nb) load_block<D>(nxt, kpool, vpool, __shfl(my_blk, b + 1, 64), n_kv, g, i16, grp);
-      attend_block<D>(st, cur, qf, (base + b) * kBlock, limit, n_keys, scale_log2, grp);
-      cur = nxt;
+  const int e = min(b1, n_keys / kBlock);  // full blocks: [b0, e)
+  const int ring_limit = min(limit, e * kBlock - 1);
+  for (int base = b0; base < e; base += 64) {
+    const int nb = min(64, e - base);
+    const int my_blk = bt_row[base + min(lane, nb - 1)];
+    KvFrag<D> f0[NB], f1[NB];
+    load_group<D, NB>(f0, kpool, vpool, my_blk, 0, nb, n_kv, g, i16, grp);
+    for (int b = 0; b < nb; b += 2 * NB) {
+      load_group<D, NB>(f1, kpool, vpool, my_blk, b + NB, nb, n_kv, g, i16, grp);
+      attend_group<D, NB>(st, f0, qf, (base + b) * kBlock, ring_limit, scale_log2, grp);
+      load_group<D, NB>(f0, kpool, vpool, my_blk, b + 2 * NB, nb, n_kv, g, i16, grp);
+      attend_group<D, NB>(st, f1, qf, (base + b + NB) * kBlock, ring_limit, scale_log2, grp);
     }
+  }
+  if (b1 > e) {
+    KvFrag<D> f[1];
+    load_block<D>(f[0], kpool, vpool, bt_row[e], n_kv, g, i16, grp);
+    const int kbase = e * kBlock + grp * 4;
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (kbase + r >= n_keys) f[0].v[dc][r] = (bf16)0.0f;
+    attend_group<D, 1>(st, f, qf, e * kBlock, limit, scale_log2, grp);
   }
 }
 
@@ -132,7 +167,10 @@ __device__ __forceinline__ void init_state(AttnState<D>& st) {
 // decode
 // ---------------------------------------------------------------------------------------
 
-template <int D>
+// Waves take work units (item, KV head) in strides of the grid's wave count, so a grid
+// smaller than the work keeps a bounded footprint (the memory nano-op's resource share)
+// while each wave streams many blocks.
+template <int D, int NB>
 __global__ __launch_bounds__(256) void decode_attn_kernel(const bf16* __restrict__ qkv, const bf16* __restrict__ kpool,
                                                           const bf16* __restrict__ vpool,
                                                           const int32_t* __restrict__ block_table, int max_blocks,
@@ -140,54 +178,52 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const bf16* __restrict
                                                           float* __restrict__ part_o, float* __restrict__ part_ml,
                                                           bf16* __restrict__ out, int n_q, int n_kv, float scale_log2) {
   const int lane = threadIdx.x & 63;
-  const int wg = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int item_idx = wg / n_kv;
-  const int g = wg % n_kv;
-  if (item_idx >= n_items) return;
-  const DecodeItem it = items[item_idx];
+  const int n_waves = gridDim.x * 4;
   const int G = n_q / n_kv;
   const int i16 = lane & 15, grp = lane >> 4;
   const int width = (n_q + 2 * n_kv) * D;
-
-  bf16x8 qf[D / 32];
-  {
-    const bf16* qrow = qkv + (size_t)it.token * width + (size_t)(g * G + i16) * D;
+  for (int wg = blockIdx.x * 4 + (threadIdx.x >> 6); wg < n_items * n_kv; wg += n_waves) {
+    const int item_idx = wg / n_kv;
+    const int g = wg % n_kv;
+    const DecodeItem it = items[item_idx];
+    bf16x8 qf[D / 32];
+    {
+      const bf16* qrow = qkv + (size_t)it.token * width + (size_t)(g * G + i16) * D;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      if (i16 < G) {
-        qf[c] = *reinterpret_cast<const bf16x8*>(qrow + c * 32 + grp * 8);
+      for (int c = 0; c < D / 32; ++c) {
+        if (i16 < G) {
+          qf[c] = *reinterpret_cast<const bf16x8*>(qrow + c * 32 + grp * 8);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) qf[c][j] = (bf16)0.0f;
+        }
+      }
+    }
+    AttnState<D> st;
+    init_state<D>(st);
+    attend_range<D, NB>(st, qf, block_table + (size_t)it.req * max_blocks, it.blk_begin, it.blk_end, kpool, vpool,
+                          n_kv, g, it.n_keys - 1, it.n_keys, scale_log2, lane);
+    const float l = wave_sum16(st.l);
+    if (i16 < G) {
+      if (it.part < 0) {
+        const float inv = 1.0f / l;
+        bf16* orow = out + (size_t)it.token * n_q * D + (size_t)(g * G + i16) * D;
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc) {
+          bf16x4 o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = (bf16)(st.o[dc][r] * inv);
+          *reinterpret_cast<bf16x4*>(orow + dc * 16 + grp * 4) = o;
+        }
       } else {
+        const size_t pbase = ((size_t)it.part * n_kv + g) * G + i16;
+        float* po = part_o + pbase * D;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) qf[c][j] = (bf16)0.0f;
-      }
-    }
-  }
-  AttnState<D> st;
-  init_state<D>(st);
-  attend_range<D>(st, qf, block_table + (size_t)it.req * max_blocks, it.blk_begin, it.blk_end, kpool, vpool, n_kv, g,
-                  it.n_keys - 1, it.n_keys, scale_log2, lane);
-  const float l = wave_sum16(st.l);
-  if (it.part < 0) {
-    if (i16 < G) {
-      const float inv = 1.0f / l;
-      bf16* orow = out + (size_t)it.token * n_q * D + (size_t)(g * G + i16) * D;
-#pragma unroll
-      for (int dc = 0; dc < D / 16; ++dc) {
-        bf16x4 o;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = (bf16)(st.o[dc][r] * inv);
-        *reinterpret_cast<bf16x4*>(orow + dc * 16 + grp * 4) = o;
-      }
-    }
-  } else {
-    if (i16 < G) {
-      const size_t pbase = ((size_t)it.part * n_kv + g) * G + i16;
-      float* po = part_o + pbase * D;
-#pragma unroll
-      for (int dc = 0; dc < D / 16; ++dc) *reinterpret_cast<f32x4*>(po + dc * 16 + grp * 4) = st.o[dc];
-      if (grp == 0) {
-        part_ml[pbase * 2 + 0] = st.m;
-        part_ml[pbase * 2 + 1] = l;
+        for (int dc = 0; dc < D / 16; ++dc) *reinterpret_cast<f32x4*>(po + dc * 16 + grp * 4) = st.o[dc];
+        if (grp == 0) {
+          part_ml[pbase * 2 + 0] = st.m;
+          part_ml[pbase * 2 + 1] = l;
+        }
       }
     }
   }
@@ -264,8 +300,8 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(const bf16* __restric
   const int limit = valid ? it.prefix + j : it.prefix + last_q;  // causal limit of this column
   AttnState<D> st;
   init_state<D>(st);
-  attend_range<D>(st, qf, block_table + (size_t)it.req * max_blocks, 0, (tile_keys + kBlock - 1) / kBlock, kpool,
-                  vpool, n_kv, g, limit, n_keys, scale_log2, lane);
+  attend_range<D, 2>(st, qf, block_table + (size_t)it.req * max_blocks, 0, (tile_keys + kBlock - 1) / kBlock, kpool,
+                     vpool, n_kv, g, limit, n_keys, scale_log2, lane);
   const float l = wave_sum16(st.l);
   if (valid) {
     const float inv = 1.0f / l;
@@ -282,22 +318,53 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(const bf16* __restric
 
 // ---------------------------------------------------------------------------------------
 
+template <int D, int NB>
+static void launch_decode_t(int grid, hipStream_t s, const bf16* qkv, const bf16* kpool, const bf16* vpool,
+                            const int32_t* block_table, int max_blocks, const DecodeItem* items, int n_items,
+                            float* part_o, float* part_ml, bf16* out, int n_q, int n_kv, float scale_log2) {
+  hipLaunchKernelGGL((decode_attn_kernel<D, NB>), dim3(grid), dim3(256), 0, s, qkv, kpool, vpool, block_table,
+                     max_blocks, items, n_items, part_o, part_ml, out, n_q, n_kv, scale_log2);
+}
+
+template <int D>
+static hipError_t launch_decode_d(int nb, int grid, hipStream_t s, const bf16* qkv, const bf16* kpool,
+                                  const bf16* vpool, const int32_t* block_table, int max_blocks,
+                                  const DecodeItem* items, int n_items, float* part_o, float* part_ml, bf16* out,
+                                  int n_q, int n_kv, float scale_log2) {
+  switch (nb) {
+    case 1:
+      launch_decode_t<D, 1>(grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o, part_ml, out,
+                            n_q, n_kv, scale_log2);
+      break;
+    case 2:
+      launch_decode_t<D, 2>(grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o, part_ml, out,
+                            n_q, n_kv, scale_log2);
+      break;
+    case 4:
+      launch_decode_t<D, 4>(grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o, part_ml, out,
+                            n_q, n_kv, scale_log2);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// nb: KV blocks per softmax step (1, 2 or 4); max_grid: workgroup cap (0 = one wave per unit)
 hipError_t launch_decode_attn(const bf16* qkv, const bf16* kpool, const bf16* vpool, const int32_t* block_table,
                               int max_blocks, const DecodeItem* items, int n_items, float* part_o, float* part_ml,
-                              bf16* out, int n_q, int n_kv, int d, hipStream_t s) {
+                              bf16* out, int n_q, int n_kv, int d, int max_grid, int nb, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)d);
   const int waves = n_items * n_kv;
-  const int grid = (waves + 3) / 4;
+  int grid = (waves + 3) / 4;
+  if (max_grid > 0 && grid > max_grid) grid = max_grid;
   if (d == 128)
-    hipLaunchKernelGGL(decode_attn_kernel<128>, dim3(grid), dim3(256), 0, s, qkv, kpool, vpool, block_table,
-                       max_blocks, items, n_items, part_o, part_ml, out, n_q, n_kv, scale_log2);
-  else if (d == 64)
-    hipLaunchKernelGGL(decode_attn_kernel<64>, dim3(grid), dim3(256), 0, s, qkv, kpool, vpool, block_table,
-                       max_blocks, items, n_items, part_o, part_ml, out, n_q, n_kv, scale_log2);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+    return launch_decode_d<128>(nb, grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o,
+                                part_ml, out, n_q, n_kv, scale_log2);
+  if (d == 64)
+    return launch_decode_d<64>(nb, grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o,
+                               part_ml, out, n_q, n_kv, scale_log2);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_combine(const CombineItem* combines, int n_combines, const float* part_o,

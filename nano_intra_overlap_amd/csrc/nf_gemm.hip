@@ -210,6 +210,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Workgroup barrier ordering LDS only. __syncthreads() (a workgroup fence) also waits for
+// every outstanding global load, vmcnt(0), which would drain the slabs still in flight.
+// Here: this wave's LDS reads complete (lgkmcnt(0)), then s_barrier; the empty asm
+// statements keep the compiler from moving memory accesses across the barrier. Slab data
+// written by the load unit is covered by the explicit vmcnt wait before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int BM, int BN, int STAGES, int EPI>
 __global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, bf16* C,
                                                         const bf16* R, int M, int N, int K, int tiles_m, int tiles_n,
@@ -323,7 +335,7 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__
     if (newer >= STAGES - 2) wait_vmcnt<NL * (STAGES - 2)>();
     else if (newer == 1) wait_vmcnt<NL>();
     else wait_vmcnt<0>();
-    __syncthreads();
+    lds_barrier();
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
     const unsigned char* slab = smem_raw + (kt % STAGES) * STAGE_BYTES;
 #pragma unroll

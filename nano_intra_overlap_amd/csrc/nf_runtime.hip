@@ -58,6 +58,8 @@ struct nf_ctx {
   hipEvent_t fork_ev = nullptr;
   std::vector<hipEvent_t> join_ev;
   int decode_split = kDefaultSplit;
+  int decode_grid = 0;  // max workgroups of the decode attention kernel (0 = one wave per work unit)
+  int decode_nbuf = 2;  // KV blocks per online-softmax step (1, 2, 4); one more group in flight
   int gemm_variant[NF_OP_KINDS][2];  // per dense op kind: [0] first GEMM, [1] second (UGD down); -1 = default
   // kernel timing: events recorded around instrumented kernel classes on their own stream
   uint32_t timing_mask = 0;
@@ -427,7 +429,8 @@ nf_status launch_op(nf_ctx* ctx, const LayerArgs& A, const PlanGraph& g, const N
       NF_TRY(timed(ctx, NF_K_DECODE_ATTN, s, [&] {
         return launch_decode_attn(qkv, static_cast<const bf16*>(A.pool->k), static_cast<const bf16*>(A.pool->v),
                                   M.d_bt, A.max_blocks, M.d_dec + i0, i1 - i0, static_cast<float*>(ctx->part_o.p),
-                                  static_cast<float*>(ctx->part_ml.p), attn, nq, nkv, d, s);
+                                  static_cast<float*>(ctx->part_ml.p), attn, nq, nkv, d, ctx->decode_grid,
+                                  ctx->decode_nbuf, s);
       }));
       if (c1 > c0)
         NF_TRY(timed(ctx, NF_K_DECODE_COMBINE, s, [&] {
@@ -692,7 +695,8 @@ extern "C" nf_status nf_op_attention(nf_ctx* ctx, const nf_layer_cfg* cfg, const
     NF_HIP(ctx, launch_decode_attn(static_cast<const bf16*>(qkv), static_cast<const bf16*>(pool->k),
                                    static_cast<const bf16*>(pool->v), M.d_bt, batch->max_blocks, M.d_dec,
                                    (int)M.dec.size(), static_cast<float*>(ctx->part_o.p),
-                                   static_cast<float*>(ctx->part_ml.p), static_cast<bf16*>(out), nq, nkv, d, s));
+                                   static_cast<float*>(ctx->part_ml.p), static_cast<bf16*>(out), nq, nkv, d,
+                                   ctx->decode_grid, ctx->decode_nbuf, s));
     NF_HIP(ctx, launch_decode_combine(M.d_comb, (int)M.comb.size(), static_cast<const float*>(ctx->part_o.p),
                                       static_cast<const float*>(ctx->part_ml.p), static_cast<bf16*>(out), nq, nkv, d,
                                       s));
@@ -738,6 +742,12 @@ extern "C" nf_status nf_timing_summary(nf_ctx* ctx, int32_t cls, int32_t* count,
 extern "C" nf_status nf_ctx_set_decode_split(nf_ctx* ctx, int32_t blocks) {
   if (!ctx || blocks < 1 || blocks > kMaxSplit) return NF_E_ARG;
   ctx->decode_split = blocks;
+  return NF_OK;
+}
+extern "C" nf_status nf_ctx_set_decode_launch(nf_ctx* ctx, int32_t max_workgroups, int32_t nbuf) {
+  if (!ctx || max_workgroups < 0 || (nbuf != 1 && nbuf != 2 && nbuf != 4)) return NF_E_ARG;
+  ctx->decode_grid = max_workgroups;
+  ctx->decode_nbuf = nbuf;
   return NF_OK;
 }
 extern "C" nf_status nf_ctx_set_gemm_variant(nf_ctx* ctx, int32_t kind, int32_t which, int32_t variant) {

@@ -59,3 +59,163 @@ def dependencies(batch, bounds) -> set:
             if ka in PARENTS.get(kb, ()) and ra & rb:
                 deps.add(((ka, ja), (kb, jb)))
     return deps
+
+
+# --------------------------------------------------------------------------------------
+# durations, list-schedule simulation, brute-force two-stage search
+# --------------------------------------------------------------------------------------
+#
+# Follows "Auto-Search Stage I" (structure under no interference: number of nano-batches,
+# sizes in multiples of the granularity summing to the dense batch, ordering; nano-ops of
+# one class never overlap; each nano-op takes its profiled best time) and "Auto-Search
+# Stage II" (structure fixed; an op's time is its best time divided by its normalised
+# performance P under the chosen resource split). Readings (no MILP is given on the pages):
+# one in-order stream per class (compute: KQV, O, UGD; memory: decode attention; prefill
+# attention on either), orders drawn from a KQV-lookahead family, profiled times
+# interpolated linearly in the nano-batch size, and P depending only on whether an op of
+# the other class is running. A configuration gives (P_gemm_both, P_mem_both,
+# P_gemm_alone, P_mem_alone).
+
+def interp(points, x):
+    """Piecewise-linear through (size, ms) points; through the origin below the first,
+    extended along the last segment above the last."""
+    if x <= 0 or not points:
+        return 0.0
+    pts = sorted(points)
+    if x <= pts[0][0]:
+        return pts[0][1] * x / pts[0][0]
+    for (x0, y0), (x1, y1) in zip(pts, pts[1:]):
+        if x <= x1:
+            return y0 + (y1 - y0) * (x - x0) / (x1 - x0)
+    if len(pts) == 1:
+        return pts[0][1] * x / pts[0][0]
+    (x0, y0), (x1, y1) = pts[-2], pts[-1]
+    return y1 + (y1 - y0) * (x - x1) / (x1 - x0)
+
+
+def durations(batch, bounds, table):
+    """Best time of every nano-op (kind, nano) from a D_best table {kind: [(size, ms)]}."""
+    n = len(bounds) - 1
+    reqs = _requests(batch)
+    out = {}
+    for j in range(n):
+        lo, hi = bounds[j], bounds[j + 1]
+        out[(KQV, j)] = interp(table["KQV"], hi - lo)
+        out[(O, j)] = interp(table["O"], hi - lo)
+        out[(UGD, j)] = interp(table["UGD"], hi - lo)
+        n_dec = sum(1 for s, e, dec in reqs if dec and lo <= s < hi)
+        out[(DECATTN, j)] = interp(table.get("DECATTN", []), n_dec)
+        out[(PFATTN, j)] = sum(interp(table.get("PFATTN", []), e - s) for s, e, dec in reqs
+                               if not dec and lo <= e - 1 < hi)
+    return out
+
+
+def simulate(streams, deps, dur, speeds=None):
+    """Makespan of in-order streams (lists of (kind, nano)) with dependency waits.
+
+    speeds: None (every op at full speed) or a dict with p_gemm_both, p_mem_both,
+    p_gemm_alone, p_mem_alone; stream 0 is the compute stream. Returns None on deadlock.
+    Time advances from one completion to the next; a running op progresses at its speed.
+    """
+    pos = [0] * len(streams)
+    cur = [None] * len(streams)
+    left = [0.0] * len(streams)
+    end = {}
+    t = 0.0
+    total = sum(len(s) for s in streams)
+    while len(end) < total:
+        progress = True
+        while progress:  # zero-length ops may unblock another stream's head: repeat
+            progress = False
+            for s, ops in enumerate(streams):
+                while cur[s] is None and pos[s] < len(ops):
+                    op = ops[pos[s]]
+                    if not all(d in end and end[d] <= t for d in deps.get(op, ())):
+                        break
+                    pos[s] += 1
+                    progress = True
+                    if dur[op] <= 0:
+                        end[op] = t
+                        continue
+                    cur[s], left[s] = op, dur[op]
+        running = [s for s in range(len(streams)) if cur[s] is not None]
+        if not running:
+            if len(end) == total:
+                break
+            return None  # deadlock: a stream head waits on an op that can never run
+        rate = {}
+        for s in running:
+            if speeds is None or len(streams) == 1:
+                rate[s] = 1.0
+            else:
+                both = len(running) > 1
+                key = ("p_gemm_" if s == 0 else "p_mem_") + ("both" if both else "alone")
+                rate[s] = speeds[key]
+        dt = min(left[s] / rate[s] for s in running)
+        t += dt
+        for s in running:
+            left[s] -= dt * rate[s]
+            if left[s] <= 1e-12 * max(1.0, dur[cur[s]]):
+                end[cur[s]] = t
+                cur[s] = None
+    return max(end.values()) if end else 0.0
+
+
+def structure(n, lookahead, pf_on_memory):
+    """Per-stream orders: compute = KQV_0..KQV_{a-1}, then per nano-batch j: (prefill
+    attention,) O_j, UGD_j, KQV_{j+a}; memory = decode attention (and prefill) per j."""
+    comp = [(KQV, j) for j in range(min(lookahead, n))]
+    mem = []
+    for j in range(n):
+        if not pf_on_memory:
+            comp.append((PFATTN, j))
+        comp += [(O, j), (UGD, j)]
+        if j + lookahead < n:
+            comp.append((KQV, j + lookahead))
+        mem.append((DECATTN, j))
+        if pf_on_memory:
+            mem.append((PFATTN, j))
+    return [comp, mem]
+
+
+def all_bounds(T, n, gran):
+    """Every split of [0, T) into n nano-batches cut at multiples of gran."""
+    import itertools
+
+    cuts = list(range(gran, T, gran))
+    for c in itertools.combinations(cuts, n - 1):
+        yield [0, *c, T]
+
+
+def search(batch, table, configs=None, max_nano=4, gran=128, top_k=8):
+    """Brute force over the same space as the library: Stage I by exhaustive enumeration,
+    Stage II over the interference configurations for the K best structures and the
+    sequential single-stream plan. Returns (best makespan, stage-I best makespan)."""
+    T = sum(e - s for s, e, _ in _requests(batch))
+    cands = []
+    for n in range(1, max_nano + 1):
+        for bounds in all_bounds(T, n, gran):
+            deps = {}
+            for a, b in dependencies(batch, bounds):
+                deps.setdefault(b, set()).add(a)
+            dur = durations(batch, bounds, table)
+            for look in range(1, n + 1):
+                for pfm in (False, True):
+                    st = structure(n, look, pfm)
+                    ms = simulate(st, deps, dur)
+                    if ms is not None:
+                        cands.append((ms, n, bounds, st, deps, dur))
+    cands.sort(key=lambda c: (c[0], c[1]))
+    stage1 = cands[0][0]
+    seq_bounds = [0, T]
+    seq_deps = {}
+    for a, b in dependencies(batch, seq_bounds):
+        seq_deps.setdefault(b, set()).add(a)
+    seq_dur = durations(batch, seq_bounds, table)
+    best = simulate([[(k, 0) for k in range(5)]], seq_deps, seq_dur)
+    for ms, n, bounds, st, deps, dur in cands[:top_k]:
+        for c in (configs or [None]):
+            r = simulate(st, deps, dur, c)
+            if r is not None and r < best:
+                best = r
+    return best, stage1

@@ -1,0 +1,152 @@
+"""Two-stage pipeline search: the library's nf_plan_search against hand-computed schedules,
+the pages' Stage I rules, and a brute-force Python search over the same space."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import schedule as osch
+from synth import workloads as sw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_values.json")))
+
+
+@pytest.fixture(scope="module")
+def abi():
+    from nano_intra_overlap_amd import abi as a
+
+    a.load()
+    return a
+
+
+def _write(tmp_path, name, obj):
+    p = tmp_path / name
+    p.write_text(json.dumps(obj))
+    return str(p)
+
+
+def _table(rng, scale=1.0):
+    """A synthetic D_best table: dense ops ~linear in tokens with a fixed cost (weight
+    loads), decode attention linear in decode tokens, prefill quadratic-ish."""
+    sizes = list(range(128, 2049, 128))
+    a, b = rng.uniform(0.02, 0.08), rng.uniform(1e-4, 5e-4)
+    return {
+        "KQV": [[s, scale * (a + b * s)] for s in sizes],
+        "O": [[s, scale * (0.6 * a + 0.7 * b * s)] for s in sizes],
+        "UGD": [[s, scale * (3 * a + 4 * b * s)] for s in sizes],
+        "DECATTN": [[s, scale * rng.uniform(5e-4, 1.2e-3) * s] for s in sizes],
+        "PFATTN": [[s, scale * 2e-8 * s * s + 0.01] for s in sizes],
+    }
+
+
+# ------------------------------------------------------------------------ simulator pins
+
+
+def test_simulator_hand_computed_two_nano_schedule():
+    # 2 decode-only nano-batches; compute: KQV0 KQV1 O0 U0 O1 U1; memory: D0 D1
+    b = sw.batch_from_lengths(np.full(4, 10), [], seed=0)
+    bounds = [0, 2, 4]
+    deps = {}
+    for x, y in osch.dependencies(b, bounds):
+        deps.setdefault(y, set()).add(x)
+    K, D, P, O, U = osch.KQV, osch.DECATTN, osch.PFATTN, osch.O, osch.UGD
+    dur = {(K, 0): 1, (K, 1): 1, (D, 0): 5, (D, 1): 5, (P, 0): 0, (P, 1): 0, (O, 0): 1, (O, 1): 1,
+           (U, 0): 2, (U, 1): 2}
+    st = osch.structure(2, 2, True)
+    # KQV0 [0,1] KQV1 [1,2]; D0 [1,6]; D1 [6,11]; O0 [6,7] U0 [7,9]; O1 [11,12] U1 [12,14]
+    assert osch.simulate(st, deps, dur) == 14
+    # Stage II: with both streams at half speed while overlapping, T = D_best / P
+    speeds = dict(p_gemm_both=0.5, p_mem_both=0.5, p_gemm_alone=1.0, p_mem_alone=1.0)
+    only_two = {k: 0 for k in dur}
+    only_two[(K, 0)] = 0
+    only_two[(D, 0)] = 4
+    only_two[(O, 0)] = 0
+    only_two[(U, 0)] = 0
+    only_two[(K, 1)] = 4
+    # D0 and KQV1 both run from t=0 at half speed: each takes 4 / 0.5 = 8
+    assert osch.simulate(st, deps, only_two, speeds) == pytest.approx(8.0)
+
+
+def test_stage1_rules_from_the_pages():
+    rules = GOLDEN["stage1_rules"]
+    for n in (2, 3, 4):
+        for bounds in osch.all_bounds(2048, n, rules["granularity"]):
+            sizes = np.diff(bounds)
+            assert (sizes % rules["granularity"] == 0).all() and (sizes >= rules["min_batch"]).all()
+            assert sum(sizes) == 2048
+    # the page's example splits are among the enumerated ones
+    ex = GOLDEN["nano_batch_examples"]
+    two = [0, ex["up_two"][0][1], 2048]
+    four = [0] + [r[1] for r in ex["kqv_four"]]
+    assert two in list(osch.all_bounds(2048, 2, 128))
+    assert four in list(osch.all_bounds(2048, 4, 128))
+
+
+# ------------------------------------------------------------------------ library vs oracle
+
+
+def _batch(rng, T=1024):
+    p = int(rng.integers(100, 400))
+    return sw.batch_from_lengths(rng.integers(200, 2000, T - p), [p], seed=1)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_search_matches_brute_force(abi, tmp_path, seed):
+    rng = np.random.default_rng(seed)
+    b = _batch(rng)
+    table = _table(rng)
+    configs = [
+        {"name": "shared", "p_gemm_both": 0.7, "p_mem_both": 0.8},
+        {"name": "mem25", "r_mem": 0.25, "p_gemm_both": 0.85, "p_mem_both": 0.5, "p_gemm_alone": 0.75,
+         "p_mem_alone": 0.55},
+    ]
+    dpath = _write(tmp_path, "dbest.json", {"ops": table})
+    rpath = _write(tmp_path, "rp.json", {"configs": configs})
+    hb = abi.HostBatch.from_batch(b)
+    plan = json.loads(abi.nf_plan_search(dpath, rpath, hb, max_nano=4, granularity=128))
+    speeds = [{k: c.get(k, 1.0) for k in ("p_gemm_both", "p_mem_both", "p_gemm_alone", "p_mem_alone")}
+              for c in configs]
+    best, stage1 = osch.search(b, table, speeds, max_nano=4, gran=128, top_k=8)
+    assert plan["stage1"]["best_ms"] == pytest.approx(stage1, rel=1e-9)
+    assert plan["predicted_ms"] == pytest.approx(best, rel=1e-6)
+    # the plan is valid for the executor
+    from nano_intra_overlap_amd import plans
+
+    hp, rec = plans.from_json(json.dumps(plan))
+    abi.nf_plan_dependencies(hb, hp)
+
+
+def test_search_prefers_sequential_when_interference_is_ruinous(abi, tmp_path):
+    rng = np.random.default_rng(9)
+    b = _batch(rng)
+    table = _table(rng)
+    dpath = _write(tmp_path, "dbest.json", {"ops": table})
+    rpath = _write(tmp_path, "rp.json", {"configs": [{"name": "bad", "p_gemm_both": 0.2, "p_mem_both": 0.2}]})
+    plan = json.loads(abi.nf_plan_search(dpath, rpath, abi.HostBatch.from_batch(b), max_nano=4, granularity=128))
+    assert plan["n_streams"] == 1 and plan["bounds"] == [0, b.n_tokens]
+    assert plan["predicted_ms"] == pytest.approx(plan["sequential_ms"])
+
+
+def test_search_without_interference_table_overlaps(abi, tmp_path):
+    rng = np.random.default_rng(3)
+    b = _batch(rng)
+    dpath = _write(tmp_path, "dbest.json", {"ops": _table(rng)})
+    plan = json.loads(abi.nf_plan_search(dpath, "", abi.HostBatch.from_batch(b), max_nano=4, granularity=128))
+    assert plan["n_streams"] == 2 and len(plan["bounds"]) >= 3
+    assert plan["predicted_ms"] < plan["sequential_ms"]
+
+
+def test_search_rejects_bad_inputs(abi, tmp_path):
+    b = _batch(np.random.default_rng(0))
+    hb = abi.HostBatch.from_batch(b)
+    with pytest.raises(abi.NanoflowError) as e:
+        abi.nf_plan_search(str(tmp_path / "missing.json"), "", hb)
+    assert e.value.status == abi.NF_E_IO
+    bad = _write(tmp_path, "bad.json", {"ops": {"KQV": [[128, 0.1]]}})
+    with pytest.raises(abi.NanoflowError):
+        abi.nf_plan_search(bad, "", hb)
+    with pytest.raises(abi.NanoflowError):
+        abi.nf_plan_search(_write(tmp_path, "d.json", {"ops": _table(np.random.default_rng(1))}), "", hb, max_nano=0)
