@@ -169,7 +169,9 @@ def main():
             bounds = plans.even_bounds(T, args.n_nano)
             return plans.sequential(hb, bounds), f"sequential, {len(bounds) - 1} nano-batches"
         if kind == "searched":
-            text = open(args.plan_json).read()
+            from nano_intra_overlap_amd import autosearch
+
+            text = open(args.plan_json).read() if args.plan_json else autosearch.search_plan(args.workload, args.seed)
             plan, rec = plans.from_json(text)
             return plan, f"searched: {rec.get('summary', '')}"
         bounds = plans.even_bounds(T, args.n_nano)

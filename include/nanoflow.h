@@ -132,7 +132,9 @@ enum {
  * issue order, each (op_kind, op_nano, op_stream); every (kind, nano) pair appears exactly
  * once. A stream runs its nano-operations in the listed order; cross-stream order follows
  * the range-intersection dependencies. A NULL plan runs one nano-batch sequentially on
- * the caller's stream (the non-overlapped baseline).                                       */
+ * the caller's stream (the non-overlapped baseline). decode_max_workgroups bounds the
+ * decode-attention grid (its waves then stride over the work), i.e. the memory nano-op's
+ * share of the CUs' wave slots when it shares them with the GEMMs.                        */
 typedef struct {
   int32_t n_nano;
   const int32_t *bounds;
@@ -140,6 +142,7 @@ typedef struct {
   const uint32_t *cu_masks;
   int32_t n_ops;
   const int32_t *op_kind, *op_nano, *op_stream;
+  int32_t decode_max_workgroups; /* cap on decode-attention workgroups, 0 = context default */
 } nf_plan;
 
 /* ---- context ---------------------------------------------------------------------------- */

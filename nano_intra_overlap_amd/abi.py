@@ -62,7 +62,8 @@ class nf_kv_pool(ctypes.Structure):
 
 class nf_plan(ctypes.Structure):
     _fields_ = [("n_nano", ctypes.c_int32), ("bounds", _i32p), ("n_streams", ctypes.c_int32), ("cu_masks", _u32p),
-                ("n_ops", ctypes.c_int32), ("op_kind", _i32p), ("op_nano", _i32p), ("op_stream", _i32p)]
+                ("n_ops", ctypes.c_int32), ("op_kind", _i32p), ("op_nano", _i32p), ("op_stream", _i32p),
+                ("decode_max_workgroups", ctypes.c_int32)]
 
 
 class NanoflowError(RuntimeError):
@@ -192,7 +193,7 @@ class HostPlan:
     NF_CU_MASK_WORDS words, or None for unmasked streams.
     """
 
-    def __init__(self, bounds, ops, n_streams: int, cu_masks=None):
+    def __init__(self, bounds, ops, n_streams: int, cu_masks=None, decode_max_workgroups: int = 0):
         self.bounds = _i32(bounds)
         ops = np.asarray(ops, dtype=np.int32).reshape(-1, 3)
         self.kind = np.ascontiguousarray(ops[:, 0])
@@ -204,7 +205,7 @@ class HostPlan:
         self.n_streams = n_streams
         self.desc = nf_plan(self.bounds.shape[0] - 1, _ptr(self.bounds), n_streams,
                             None if self.masks is None else self.masks.ctypes.data_as(_u32p), ops.shape[0],
-                            _ptr(self.kind), _ptr(self.nano), _ptr(self.stream))
+                            _ptr(self.kind), _ptr(self.nano), _ptr(self.stream), int(decode_max_workgroups))
 
     @property
     def ops(self):

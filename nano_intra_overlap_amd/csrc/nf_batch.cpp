@@ -301,6 +301,70 @@ nf_status build_plan_graph(const BatchLayout& L, const nf_plan* plan, PlanGraph&
   return NF_OK;
 }
 
+// Work lists of the decode attention and prefill attention nano-ops of each nano-batch.
+void build_work(const BatchLayout& L, const PlanGraph& g, int split, Meta& M) {
+  const int n_nano = g.n_nano;
+  M.dec.clear();
+  M.comb.clear();
+  M.pf.clear();
+  M.dec_begin.assign(n_nano + 1, 0);
+  M.comb_begin.assign(n_nano + 1, 0);
+  M.pf_begin.assign(n_nano + 1, 0);
+  M.n_parts = 0;
+  std::vector<const NanoOp*> dec_op(n_nano, nullptr), pf_op(n_nano, nullptr);
+  for (auto& op : g.ops) {
+    if (op.kind == NF_OP_DECATTN) dec_op[op.nano] = &op;
+    if (op.kind == NF_OP_PFATTN) pf_op[op.nano] = &op;
+  }
+  for (int j = 0; j < n_nano; ++j) {
+    M.dec_begin[j] = (int32_t)M.dec.size();
+    M.comb_begin[j] = (int32_t)M.comb.size();
+    if (dec_op[j]) {
+      for (int32_t r = dec_op[j]->r0; r < dec_op[j]->r1; ++r) {
+        const ReqInfo& ri = L.req[r];
+        const int32_t nblk = (ri.n_keys + 15) / 16;  // KV blocks of 16 tokens
+        const int32_t nch = (nblk + split - 1) / split;
+        const int32_t per = (nblk + nch - 1) / nch;
+        for (int32_t c = 0; c < nch; ++c) {
+          DecodeItem it;
+          it.req = r;
+          it.token = ri.t0;
+          it.n_keys = ri.n_keys;
+          it.blk_begin = c * per;
+          it.blk_end = std::min(nblk, (c + 1) * per);
+          it.part = nch > 1 ? M.n_parts + c : -1;
+          M.dec.push_back(it);
+        }
+        if (nch > 1) {
+          M.comb.push_back(CombineItem{ri.t0, M.n_parts, nch, 0});
+          M.n_parts += nch;
+        }
+      }
+    }
+    M.pf_begin[j] = (int32_t)M.pf.size();
+    if (pf_op[j]) {
+      for (int32_t r : pf_op[j]->prefill_reqs) {
+        const ReqInfo& ri = L.req[r];
+        const int32_t qlen = ri.t1 - ri.t0;
+        // longest tiles (latest queries, most keys) first
+        for (int32_t q0 = ((qlen - 1) / 16) * 16; q0 >= 0; q0 -= 16) {
+          PrefillItem it{};
+          it.req = r;
+          it.token0 = ri.t0;
+          it.q_begin = q0;
+          it.q_len = qlen;
+          it.prefix = ri.cached;
+          M.pf.push_back(it);
+        }
+      }
+    }
+  }
+  M.dec_begin[n_nano] = (int32_t)M.dec.size();
+  M.comb_begin[n_nano] = (int32_t)M.comb.size();
+  M.pf_begin[n_nano] = (int32_t)M.pf.size();
+}
+
+
 }  // namespace nf
 
 // ---------------------------------------------------------------------------------------

@@ -9,9 +9,35 @@
 
 namespace nf {
 
-struct DecodeItem;
-struct CombineItem;
-struct PrefillItem;
+// One decode split-KV work item: the blocks [blk_begin, blk_end) of request `req`
+// (a decode request), for every KV head. `part` indexes the partial-result slots of the
+// request (part_base + chunk) or is -1 when the request has a single chunk.
+struct DecodeItem {
+  int32_t req;        // request index (row of the block table)
+  int32_t token;      // row of q / output
+  int32_t n_keys;     // ctx + 1
+  int32_t blk_begin;  // first logical block of this chunk
+  int32_t blk_end;    // one past the last logical block
+  int32_t part;       // partial slot index or -1
+};
+
+// One decode request that needs a split-KV combine.
+struct CombineItem {
+  int32_t token;
+  int32_t part_begin;
+  int32_t n_parts;
+  int32_t pad;
+};
+
+// One prefill attention work item: 16 consecutive queries of one prefill request.
+struct PrefillItem {
+  int32_t req;        // request index (row of the block table)
+  int32_t token0;     // dense-batch row of the first query of the request
+  int32_t q_begin;    // first query (within the request) of this 16-query tile
+  int32_t q_len;      // queries of the request
+  int32_t prefix;     // cached prefix length
+  int32_t pad[3];
+};
 
 // One request of the dense batch, in dense-batch order (decodes, then prefill chunks).
 struct ReqInfo {
@@ -61,5 +87,25 @@ nf_status build_plan_graph(const BatchLayout& L, const nf_plan* plan, PlanGraph&
 
 // Parent-operation dependency of the layer (does kind b consume a product of kind a?).
 bool parent_depends(int32_t a, int32_t b);
+
+// Attention work lists of every nano-batch (host side) and, after upload, device pointers.
+struct Meta {
+  std::vector<DecodeItem> dec;
+  std::vector<CombineItem> comb;
+  std::vector<PrefillItem> pf;
+  std::vector<int32_t> dec_begin, comb_begin, pf_begin;  // size n_nano + 1
+  int32_t n_parts = 0;
+  const int32_t* d_pos = nullptr;
+  const int32_t* d_slot = nullptr;
+  const float* d_inv_freq = nullptr;
+  const DecodeItem* d_dec = nullptr;
+  const CombineItem* d_comb = nullptr;
+  const PrefillItem* d_pf = nullptr;
+  const int32_t* d_bt = nullptr;
+};
+
+// Decode split-KV chunks of at most `split` blocks (multi-chunk requests get partial slots
+// and a combine entry) and 16-query prefill tiles (longest first), per nano-batch.
+void build_work(const BatchLayout& L, const PlanGraph& g, int split, Meta& M);
 
 }  // namespace nf

@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "../../include/nanoflow.h"
+#include "nf_batch.h"
 
 namespace nf {
 
@@ -23,40 +24,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kBlock = 16;       // KV block size (tokens)
 constexpr int kMaxGroup = 16;    // max query heads per KV head (MFMA column count)
 constexpr int kNumXcd = 8;       // XCDs of an MI355X
-
-// ---------------------------------------------------------------------------------------
-// per-launch metadata produced on the host from the batch descriptor
-// ---------------------------------------------------------------------------------------
-
-// One decode split-KV work item: the blocks [blk_begin, blk_end) of request `req`
-// (a decode request), for every KV head. `part` indexes the partial-result slots of the
-// request (part_base + chunk) or is -1 when the request has a single chunk.
-struct DecodeItem {
-  int32_t req;        // request index (row of the block table)
-  int32_t token;      // row of q / output
-  int32_t n_keys;     // ctx + 1
-  int32_t blk_begin;  // first logical block of this chunk
-  int32_t blk_end;    // one past the last logical block
-  int32_t part;       // partial slot index or -1
-};
-
-// One decode request that needs a split-KV combine.
-struct CombineItem {
-  int32_t token;
-  int32_t part_begin;
-  int32_t n_parts;
-  int32_t pad;
-};
-
-// One prefill attention work item: 16 consecutive queries of one prefill request.
-struct PrefillItem {
-  int32_t req;        // request index (row of the block table)
-  int32_t token0;     // dense-batch row of the first query of the request
-  int32_t q_begin;    // first query (within the request) of this 16-query tile
-  int32_t q_len;      // queries of the request
-  int32_t prefix;     // cached prefix length
-  int32_t pad[3];
-};
 
 // ---------------------------------------------------------------------------------------
 // kernel launchers (defined in the .hip files)

@@ -185,86 +185,6 @@ nf_status ensure_events(nf_ctx* ctx, size_t n) {
 // metadata
 // ---------------------------------------------------------------------------------------
 
-struct Meta {
-  // host-side work lists, grouped per nano-batch
-  std::vector<DecodeItem> dec;
-  std::vector<CombineItem> comb;
-  std::vector<PrefillItem> pf;
-  std::vector<int32_t> dec_begin, comb_begin, pf_begin;  // size n_nano + 1
-  int32_t n_parts = 0;
-  // device pointers after upload
-  const int32_t* d_pos = nullptr;
-  const int32_t* d_slot = nullptr;
-  const float* d_inv_freq = nullptr;
-  const DecodeItem* d_dec = nullptr;
-  const CombineItem* d_comb = nullptr;
-  const PrefillItem* d_pf = nullptr;
-  const int32_t* d_bt = nullptr;
-};
-
-// Work lists of the decode attention and prefill attention nano-ops of each nano-batch.
-void build_work(const BatchLayout& L, const PlanGraph& g, int split, Meta& M) {
-  const int n_nano = g.n_nano;
-  M.dec.clear();
-  M.comb.clear();
-  M.pf.clear();
-  M.dec_begin.assign(n_nano + 1, 0);
-  M.comb_begin.assign(n_nano + 1, 0);
-  M.pf_begin.assign(n_nano + 1, 0);
-  M.n_parts = 0;
-  std::vector<const NanoOp*> dec_op(n_nano, nullptr), pf_op(n_nano, nullptr);
-  for (auto& op : g.ops) {
-    if (op.kind == NF_OP_DECATTN) dec_op[op.nano] = &op;
-    if (op.kind == NF_OP_PFATTN) pf_op[op.nano] = &op;
-  }
-  for (int j = 0; j < n_nano; ++j) {
-    M.dec_begin[j] = (int32_t)M.dec.size();
-    M.comb_begin[j] = (int32_t)M.comb.size();
-    if (dec_op[j]) {
-      for (int32_t r = dec_op[j]->r0; r < dec_op[j]->r1; ++r) {
-        const ReqInfo& ri = L.req[r];
-        const int32_t nblk = (ri.n_keys + kBlock - 1) / kBlock;
-        const int32_t nch = (nblk + split - 1) / split;
-        const int32_t per = (nblk + nch - 1) / nch;
-        for (int32_t c = 0; c < nch; ++c) {
-          DecodeItem it;
-          it.req = r;
-          it.token = ri.t0;
-          it.n_keys = ri.n_keys;
-          it.blk_begin = c * per;
-          it.blk_end = std::min(nblk, (c + 1) * per);
-          it.part = nch > 1 ? M.n_parts + c : -1;
-          M.dec.push_back(it);
-        }
-        if (nch > 1) {
-          M.comb.push_back(CombineItem{ri.t0, M.n_parts, nch, 0});
-          M.n_parts += nch;
-        }
-      }
-    }
-    M.pf_begin[j] = (int32_t)M.pf.size();
-    if (pf_op[j]) {
-      for (int32_t r : pf_op[j]->prefill_reqs) {
-        const ReqInfo& ri = L.req[r];
-        const int32_t qlen = ri.t1 - ri.t0;
-        // longest tiles (latest queries, most keys) first
-        for (int32_t q0 = ((qlen - 1) / 16) * 16; q0 >= 0; q0 -= 16) {
-          PrefillItem it{};
-          it.req = r;
-          it.token0 = ri.t0;
-          it.q_begin = q0;
-          it.q_len = qlen;
-          it.prefix = ri.cached;
-          M.pf.push_back(it);
-        }
-      }
-    }
-  }
-  M.dec_begin[n_nano] = (int32_t)M.dec.size();
-  M.comb_begin[n_nano] = (int32_t)M.comb.size();
-  M.pf_begin[n_nano] = (int32_t)M.pf.size();
-}
-
 // Pack and upload the metadata on `stream` (ordered before the work that reads it).
 nf_status upload_meta(nf_ctx* ctx, const nf_layer_cfg& cfg, const nf_batch_desc& b, const BatchLayout& L, Meta& M,
                       hipStream_t stream) {
@@ -351,6 +271,7 @@ struct LayerArgs {
   bf16* y;
   nf_kv_pool* pool;
   int max_blocks;
+  int decode_grid;
 };
 
 int pick_variant(nf_ctx* ctx, int kind, int which, int m, int n, int k, int epi) {
@@ -429,7 +350,7 @@ nf_status launch_op(nf_ctx* ctx, const LayerArgs& A, const PlanGraph& g, const N
       NF_TRY(timed(ctx, NF_K_DECODE_ATTN, s, [&] {
         return launch_decode_attn(qkv, static_cast<const bf16*>(A.pool->k), static_cast<const bf16*>(A.pool->v),
                                   M.d_bt, A.max_blocks, M.d_dec + i0, i1 - i0, static_cast<float*>(ctx->part_o.p),
-                                  static_cast<float*>(ctx->part_ml.p), attn, nq, nkv, d, ctx->decode_grid,
+                                  static_cast<float*>(ctx->part_ml.p), attn, nq, nkv, d, A.decode_grid,
                                   ctx->decode_nbuf, s);
       }));
       if (c1 > c0)
@@ -551,7 +472,8 @@ extern "C" nf_status nf_layer_forward(nf_ctx* ctx, const nf_layer_cfg* cfg, cons
   nf_status st = prepare_batch(ctx, cfg, batch, pool->num_blocks, plan, L, g, M, caller);
   if (st != NF_OK) return st;
   if (L.T == 0) return NF_OK;
-  LayerArgs A{cfg, w, static_cast<const bf16*>(x_in), static_cast<bf16*>(y_out), pool, batch->max_blocks};
+  LayerArgs A{cfg,  w, static_cast<const bf16*>(x_in), static_cast<bf16*>(y_out), pool, batch->max_blocks,
+              (plan && plan->decode_max_workgroups > 0) ? plan->decode_max_workgroups : ctx->decode_grid};
 
   if (!plan) {
     for (int32_t i : g.order)

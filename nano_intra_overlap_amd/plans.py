@@ -96,4 +96,4 @@ def from_json(text: str) -> tuple[HostPlan, dict]:
     rec = json.loads(text)
     ops = [(o["kind"], o["nano"], o["stream"]) for o in rec["ops"]]
     masks = rec.get("cu_masks")
-    return HostPlan(rec["bounds"], ops, rec["n_streams"], masks), rec
+    return HostPlan(rec["bounds"], ops, rec["n_streams"], masks, rec.get("decode_grid", 0)), rec
