@@ -41,17 +41,49 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="llama3_8b_layer")
     p.add_argument("--seed", type=int, default=0)
-    p.add_argument("--plan", default="overlap", choices=["overlap", "sequential", "null", "searched"])
+    p.add_argument("--plan", default="searched", choices=["overlap", "sequential", "null", "searched"],
+                   help="searched: the two-stage search's plan for this batch (from the profiled tables)")
     p.add_argument("--n-nano", type=int, default=2)
     p.add_argument("--mem-cus", type=int, default=0, help="CUs per XCD for the memory stream (0 = unmasked)")
     p.add_argument("--plan-json", default="", help="plan written by nf_plan_search (with --plan searched)")
-    p.add_argument("--no-baseline", action="store_true", help="skip the sequential-schedule comparison")
+    p.add_argument("--no-baseline", action="store_true",
+                   help="skip the comparison schedules (sequential, nano-batching only, overlap template)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--cpu-decode-sample", type=int, default=96)
+    p.add_argument("--cpu-decode-sample", type=int, default=-1,
+                   help="decode requests in the CPU oracle's sample (-1 = all: the whole dense batch)")
     p.add_argument("--decode-grid", type=int, default=0, help="max decode-attention workgroups (0 = one wave per unit)")
-    p.add_argument("--decode-nbuf", type=int, default=2, choices=[1, 2, 4], help="KV blocks per softmax step")
+    p.add_argument("--decode-nbuf", type=int, default=1, choices=[1, 2, 4], help="KV blocks per softmax step")
     p.add_argument("--gemm-variant", type=int, default=-1, help="force one GEMM tile variant for every GEMM")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="run one plain device copy of this many MiB first (a known-size reference for "
+                        "hardware traffic counters)")
     return p.parse_args()
+
+
+def kernel_source_hash(files) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counted_traffic(workload: str, seed: int, launches_per_step: float):
+    """HBM bytes per decode-attention launch from the committed hardware-counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a known-size copy),
+    or None when there is none for this workload and launch count, or when the kernel's
+    source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"decode_attn_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if (rec.get("seed") != seed or rec.get("decode_launches_per_step") != launches_per_step
+            or rec.get("source_sha256") != kernel_source_hash(rec["source_files"])):
+        return None
+    return int(rec["traffic_bytes_per_launch"])
 
 
 def algorithmic(shape, b, n_nano):
@@ -79,8 +111,10 @@ def algorithmic(shape, b, n_nano):
     }
 
 
-def cpu_baseline(shape, b, w, x, seed, n_dec):
-    """The oracle as it stands, on the sampled decode requests plus the prefill chunks."""
+def cpu_baseline(shape, b, w, x, seed, n_dec, fetch_blocks):
+    """The oracle as it stands, timed on a sample of the workload: n_dec decode requests
+    (all of them when n_dec < 0) plus every prefill chunk, over a compact copy of the KV
+    blocks they use (fetch_blocks(ids) -> (k, v) bf16 bit arrays of those pool blocks)."""
     from oracle import layer as ol
     from synth import workloads as sw
 
@@ -90,33 +124,37 @@ def cpu_baseline(shape, b, w, x, seed, n_dec):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    rng = np.random.default_rng(seed + 7)
-    n_dec = min(n_dec, b.n_decode)
-    sample = sorted(rng.choice(b.n_decode, size=n_dec, replace=False).tolist()) + list(range(b.n_decode, b.n_requests))
+    if n_dec < 0 or n_dec >= b.n_decode:
+        n_dec = b.n_decode
+        sample = list(range(b.n_requests))
+    else:
+        rng = np.random.default_rng(seed + 7)
+        sample = sorted(rng.choice(b.n_decode, size=n_dec, replace=False).tolist()) + list(
+            range(b.n_decode, b.n_requests))
     sub = b.select(sample)
     ranges = ol.request_ranges(b)
     rows = np.concatenate([np.arange(ranges[r][0], ranges[r][1]) for r in sample])
     need = (sub.cached_lens() + sub.q_lens() + 15) // 16
-    used = sorted({int(sub.block_table[i, j]) for i in range(sub.n_requests) for j in range(int(need[i]))})
-    remap = {blk: i for i, blk in enumerate(used)}
+    mask = np.arange(sub.block_table.shape[1])[None, :] < need[:, None]
+    used = np.unique(sub.block_table[mask])
     bt = np.full_like(sub.block_table, -1)
-    for i in range(sub.n_requests):
-        for j in range(int(need[i])):
-            bt[i, j] = remap[int(sub.block_table[i, j])]
+    bt[mask] = np.searchsorted(used, sub.block_table[mask])
     compact = sw.Batch(sub.decode_ctx, sub.prefill_len, sub.prefill_prefix, bt, len(used))
-    kp, vp = sw.make_kv_pool_blocks(shape, used, seed)
+    kp, vp = fetch_blocks(used)
     xs = x[rows]
     t0 = time.perf_counter()
     ol.layer_forward(shape, w, xs, compact, kp, vp)
     dt = time.perf_counter() - t0
+    what = ("the whole dense batch" if n_dec == b.n_decode else
+            f"{n_dec} of {b.n_decode} decode requests (sampled, seed {seed + 7}) + all prefill chunks")
     return {
         "value": round(len(rows) / dt, 2),
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{n_dec} of {b.n_decode} decode requests (sampled, seed {seed + 7}) + all "
-                  f"{b.n_prefill} prefill chunk(s) ({int(b.prefill_len.sum())} tokens) = {len(rows)} tokens, "
-                  f"one float64 layer pass in {dt:.2f} s on {os.cpu_count()} host CPUs",
+        "sample": f"{what}: {len(rows)} tokens ({b.n_prefill} prefill chunk(s), {int(b.prefill_len.sum())} "
+                  f"tokens), {len(used)} KV blocks; one float64 layer pass in {dt:.2f} s "
+                  f"({os.cpu_count()} host CPUs, {threads} BLAS threads)",
     }
 
 
@@ -153,6 +191,17 @@ def main():
     cfg = abi.make_cfg(shape)
     torch.cuda.synchronize()
     log(f"inputs resident in {time.time() - t0:.1f} s")
+
+    if args.copy_probe_mib:
+        nbytes = args.copy_probe_mib << 20
+        src = torch.ones(nbytes // 2, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        abi.nf_copy_reference(dst.data_ptr(), src.data_ptr(), nbytes, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert bool((dst == 1).all()), "reference copy mismatch"
+        log(f"reference copy: {nbytes} bytes read + {nbytes} bytes written (copy_ref_kernel)")
+        del src, dst
 
     ctx = abi.nf_ctx_create(0)
     stream = torch.cuda.current_stream().cuda_stream
@@ -235,11 +284,20 @@ def main():
             breakdown[k]["tflops"] = round(f / (per_step_ms * 1e-3) / 1e12, 1)
             breakdown[k]["mfma_frac"] = round(f / (per_step_ms * 1e-3) / PEAK_BF16, 4)
 
+    # comparison schedules on the same batch: the plain sequential layer (one nano-batch,
+    # caller stream), nano-batching without overlap, and the two-stream overlap template
+    schedules = {"timed": round(ms, 4)}
     seq_ms = None
-    if not args.no_baseline and plan is not None:
+    if not args.no_baseline:
         seq_ms, _ = run(None, args.steps, args.warmup)
-        log(f"sequential single-stream baseline: {seq_ms:.3f} ms/step")
+        schedules["sequential"] = round(seq_ms, 4)
+        for n in (2, 4):
+            bnd = plans.even_bounds(T, n)
+            schedules[f"nanobatch_only_{n}"] = round(run(plans.sequential(hb, bnd), args.steps, args.warmup)[0], 4)
+            schedules[f"overlap_{n}"] = round(run(plans.overlap(hb, bnd), args.steps, args.warmup)[0], 4)
+        log("schedules (ms/step): " + ", ".join(f"{k} {v:.3f}" for k, v in schedules.items()))
 
+    traffic = counted_traffic(wl.name, args.seed, launches_per_step)
     tokens_per_s = T / (ms * 1e-3)
     layer_flops = alg["gemm_flops"] + alg["attn_flops"]
     mfma_frac = alg["gemm_flops"] / (ms * 1e-3) / PEAK_BF16
@@ -248,7 +306,13 @@ def main():
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
-        cpu = cpu_baseline(shape, b, w, x, args.seed, args.cpu_decode_sample)
+        def fetch_blocks(ids):
+            idx = torch.from_numpy(np.asarray(ids, dtype=np.int64)).cuda()
+            kp = k16.index_select(0, idx).cpu().numpy().view(np.uint16)
+            vp = v16.index_select(0, idx).cpu().numpy().view(np.uint16)
+            return kp, vp
+
+        cpu = cpu_baseline(shape, b, w, x, args.seed, args.cpu_decode_sample, fetch_blocks)
         log(f"cpu oracle: {cpu['value']} tokens/s on {cpu['cores']} threads")
 
     out = {
@@ -281,6 +345,7 @@ def main():
         "layer_roofline_frac": round(t_lb / (ms * 1e-3), 4),
         "sequential_ms_per_step": None if seq_ms is None else round(seq_ms, 4),
         "speedup_vs_sequential": None if seq_ms is None else round(seq_ms / ms, 4),
+        "schedules_ms_per_step": schedules,
         "roofline": {
             "kernel": "decode_attn_kernel<128> (paged GQA decode attention, split-KV)",
             "bound": "hbm",
@@ -288,7 +353,9 @@ def main():
             "peak": PEAK_HBM / 1e9,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_unit": "bytes/launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a known-size copy)",
+            "traffic_vs_algorithmic": None if traffic is None else round(traffic / bytes_per_launch, 4),
             "bytes_per_launch": int(bytes_per_launch),
             "avg_launch_ms": round(dec_avg_ms, 4),
             "launches_per_step": launches_per_step,

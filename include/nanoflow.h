@@ -248,6 +248,13 @@ nf_status nf_ctx_set_timing(nf_ctx *ctx, uint32_t class_mask);
 nf_status nf_timing_summary(nf_ctx *ctx, int32_t cls, int32_t *count, double *total_ms, double *min_ms,
                             double *max_ms);
 
+/* Plain device-to-device copy of `bytes` bytes (a multiple of 16; both pointers 16-byte
+ * aligned; the ranges must not overlap), enqueued on `stream`: every lane moves 16 bytes per
+ * load and store, loads nontemporal like the KV stream of decode attention. It reads and
+ * writes exactly `bytes` bytes once, which makes it the known-size reference that scales
+ * hardware traffic counters (bytes per counted unit). Errors: NF_E_ARG, NF_E_HIP.         */
+nf_status nf_copy_reference(void *dst, const void *src, size_t bytes, void *stream);
+
 /* ---- profiler and pipeline search (summary page, "Kernel Profiling and Interference
  *      Modeling"; "Auto-Search Stage I" and "Stage II") ----------------------------------- */
 

@@ -117,6 +117,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "nf_ctx_set_decode_split": (I, [V, I]),
         "nf_ctx_set_gemm_variant": (I, [V, I, I, I]),
         "nf_ctx_set_decode_launch": (I, [V, I, I]),
+        "nf_copy_reference": (I, [V, V, S, V]),
     }
     missing = []
     for name, (res, args) in sig.items():
@@ -344,6 +345,13 @@ def nf_plan_search(dbest_json: str, rp_json: str, batch: HostBatch, max_nano: in
     if st != NF_OK:
         raise NanoflowError(st, buf.value.decode())
     return buf.value.decode()
+
+
+def nf_copy_reference(dst: int, src: int, nbytes: int, stream: int = 0) -> None:
+    """Known-size device copy (reference for hardware traffic counters)."""
+    st = load().nf_copy_reference(dst, src, nbytes, stream)
+    if st != NF_OK:
+        raise NanoflowError(st, "nf_copy_reference failed")
 
 
 def nf_ctx_set_timing(ctx, class_mask: int) -> None:

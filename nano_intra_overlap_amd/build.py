@@ -25,6 +25,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-Wno-u
           "-Wno-unused-but-set-variable", f"-I{os.path.join(ROOT, 'include')}"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-munsafe-fp-atomics"]
+# attention: MFMA accumulators in ordinary VGPRs (fewer registers, no AGPR copies around the
+# online-softmax rescale), which leaves room for GEMM waves on the same SIMD
+PER_FILE_FLAGS = {"nf_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():
@@ -34,7 +37,7 @@ def sources():
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     if src.endswith(".hip"):
-        cmd = [HIPCC, *HIP_FLAGS, *COMMON, "-c", src, "-o", obj]
+        cmd = [HIPCC, *HIP_FLAGS, *PER_FILE_FLAGS.get(os.path.basename(src), []), *COMMON, "-c", src, "-o", obj]
     else:
         cmd = [HIPCC, *COMMON, "-D__HIP_PLATFORM_AMD__", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

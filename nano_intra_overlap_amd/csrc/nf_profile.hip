@@ -75,6 +75,13 @@ bool fill(Err& E, Buf& b, size_t n, uint32_t seed, float scale, hipStream_t s) {
   return true;
 }
 
+// Known-size copy: 16 bytes per lane, grid-stride, nontemporal loads.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__global__ void copy_ref_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src, size_t n16) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = __builtin_nontemporal_load(src + i);
+}
+
 // Average time (ms) of fn over reps runs on stream s, after one warm-up run.
 bool time_ms(Err& E, hipStream_t s, int reps, const std::function<hipError_t()>& fn, double& out) {
   hipEvent_t a, b;
@@ -569,4 +576,18 @@ extern "C" nf_status nf_profile_interference(nf_ctx* ctx, const nf_layer_cfg* cf
   Err W;
   if (!write_file(W, out_json, o.str())) return W.st;
   return NF_OK;
+}
+
+extern "C" nf_status nf_copy_reference(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src || bytes % 16 || reinterpret_cast<uintptr_t>(dst) % 16 || reinterpret_cast<uintptr_t>(src) % 16)
+    return NF_E_ARG;
+  const char* d = static_cast<const char*>(dst);
+  const char* s = static_cast<const char*>(src);
+  if (d < s + bytes && s < d + bytes) return NF_E_ARG;
+  if (bytes == 0) return NF_OK;
+  const size_t n16 = bytes / 16;
+  const unsigned grid = (unsigned)std::min<size_t>((n16 + 255) / 256, 8192);
+  hipLaunchKernelGGL(copy_ref_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), static_cast<u32x4*>(dst),
+                     static_cast<const u32x4*>(src), n16);
+  return hipGetLastError() == hipSuccess ? NF_OK : NF_E_HIP;
 }

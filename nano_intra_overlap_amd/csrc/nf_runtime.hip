@@ -475,7 +475,10 @@ extern "C" nf_status nf_layer_forward(nf_ctx* ctx, const nf_layer_cfg* cfg, cons
   LayerArgs A{cfg,  w, static_cast<const bf16*>(x_in), static_cast<bf16*>(y_out), pool, batch->max_blocks,
               (plan && plan->decode_max_workgroups > 0) ? plan->decode_max_workgroups : ctx->decode_grid};
 
-  if (!plan) {
+  // one nano-batch on one unmasked stream: nothing to order across streams, so the
+  // caller's stream runs it directly (no fork/join)
+  const bool single = plan && g.n_streams == 1 && !plan->cu_masks;
+  if (!plan || single) {
     for (int32_t i : g.order)
       if (!g.ops[i].empty || g.ops[i].kind == NF_OP_KQV) {
         st = launch_op(ctx, A, g, g.ops[i], M, caller);
@@ -490,6 +493,11 @@ extern "C" nf_status nf_layer_forward(nf_ctx* ctx, const nf_layer_cfg* cfg, cons
     if (st != NF_OK) return st;
   }
   if ((st = ensure_events(ctx, g.ops.size())) != NF_OK) return st;
+  // an op's completion event is recorded only when an op on another stream waits for it
+  std::vector<char> waited(g.ops.size(), 0);
+  for (size_t i = 0; i < g.ops.size(); ++i)
+    for (int32_t dep : g.deps[i])
+      if (g.ops[dep].stream != g.ops[i].stream) waited[dep] = 1;
   NF_HIP(ctx, hipEventRecord(ctx->fork_ev, caller));
   std::vector<char> used(g.n_streams, 0);
   for (auto& op : g.ops) used[op.stream] = 1;
@@ -504,7 +512,7 @@ extern "C" nf_status nf_layer_forward(nf_ctx* ctx, const nf_layer_cfg* cfg, cons
       st = launch_op(ctx, A, g, op, M, s);
       if (st != NF_OK) return st;
     }
-    NF_HIP(ctx, hipEventRecord(ctx->events[i], s));
+    if (waited[i]) NF_HIP(ctx, hipEventRecord(ctx->events[i], s));
   }
   for (int s = 0; s < g.n_streams; ++s)
     if (used[s]) {
