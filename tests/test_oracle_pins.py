@@ -381,3 +381,51 @@ def test_bf16_storage_model_rounds_every_handoff():
         assert not np.array_equal(e[name], r[name]), name
     rel = np.max(np.abs(r["y"] - e["y"])) / np.max(np.abs(e["y"]))
     assert 0 < rel < 2e-2
+
+
+# ---- analytical cost model -----------------------------------------------------------
+
+from oracle import costmodel as cm  # noqa: E402
+
+
+def test_eq5_reproduces_the_pages_70b_example():
+    g = GOLDEN["eq5_example"]
+    v = cm.optimal_throughput(g["compute_flops"], g["params"])
+    assert abs(v - g["approx_tokens_per_s"]) / g["approx_tokens_per_s"] < 0.01
+    # the quoted 1857 corresponds to a profiled peak of about 260 TFLOP/s, below 280
+    assert cm.optimal_throughput(260e12, g["params"]) == pytest.approx(g["quoted"], rel=0.001)
+
+
+def test_kv_bytes_per_token_matches_the_pages():
+    for g in GOLDEN["kv_bytes_per_token"]:
+        assert cm.kv_bytes_per_token(g["n_layers"], g["n_kv"], g["head_dim"], g["dtype_bytes"]) == g["value"], g
+
+
+def test_effective_decode_intensity_matches_the_roofline_lesson():
+    for g in GOLDEN["effective_decode_intensity"]:
+        v = cm.decode_effective_intensity(g["params"], g["batch"], g["live_tokens"], g["kv_bytes_per_token"],
+                                          g["weight_bytes_per_param"])
+        assert round(v) == g["approx"], (g, v)
+    # with no KV the intensity is the batch size (the lesson's "decode intensity ~ B")
+    assert cm.decode_effective_intensity(8e9, 64, 0, 131072) == pytest.approx(64.0)
+
+
+def test_eq4_factored_form_equals_time_ratio():
+    # Equation 4 is T_mem / T_compute rearranged; check on unrelated numbers
+    compute, bw, size, params, b = 2.5e15, 8e12, 288e9, 8.03e9, 2048
+    tr = cm.tr_ratio(compute, bw, size, params, b)
+    assert tr == pytest.approx(cm.t_mem(size, bw) / cm.t_compute(b, params, compute), rel=1e-12)
+    assert 2.6 < tr < 2.8  # an 8B model on one 288 GB / 8 TB/s / 2.5 PF device is memory-bound
+    # more tokens per batch lowers TR proportionally
+    assert cm.tr_ratio(compute, bw, size, params, 2 * b) == pytest.approx(tr / 2)
+
+
+def test_net_to_compute_ratio_is_the_ratio_of_the_two_times():
+    # "Compute" and "NetBW" are aggregates over the tensor-parallel group in both forms
+    d, layers, n_gpu, s = 8192, 80, 8, 2
+    params = 12 * d * d * layers  # the page's P ~ 12 D^2 L
+    compute, net_bw, b = 8 * 312e12, 8 * 300e9, 2048
+    r = cm.net_to_compute(d, layers, params, n_gpu, compute, net_bw, s)
+    ratio = cm.t_net(n_gpu, b, d, s, layers, net_bw) / cm.t_compute(b, params, compute)
+    assert ratio == pytest.approx(r, rel=1e-12)
+    assert 2 * d * layers / params == pytest.approx(1 / (6 * d))
