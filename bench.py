@@ -52,7 +52,9 @@ def parse():
     p.add_argument("--cpu-decode-sample", type=int, default=-1,
                    help="decode requests in the CPU oracle's sample (-1 = all: the whole dense batch)")
     p.add_argument("--decode-grid", type=int, default=0, help="max decode-attention workgroups (0 = one wave per unit)")
-    p.add_argument("--decode-nbuf", type=int, default=1, choices=[1, 2, 4], help="KV blocks per softmax step")
+    p.add_argument("--decode-nbuf", type=int, default=1, choices=[1, 2], help="KV blocks per softmax step")
+    p.add_argument("--decode-ring", type=int, default=2, choices=[2, 3, 4],
+                   help="decode attention register ring depth (ring - 1 groups of KV blocks in flight)")
     p.add_argument("--gemm-variant", type=int, default=-1, help="force one GEMM tile variant for every GEMM")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="run one plain device copy of this many MiB first (a known-size reference for "
@@ -205,7 +207,7 @@ def main():
 
     ctx = abi.nf_ctx_create(0)
     stream = torch.cuda.current_stream().cuda_stream
-    abi.nf_ctx_set_decode_launch(ctx, args.decode_grid, args.decode_nbuf)
+    abi.nf_ctx_set_decode_launch(ctx, args.decode_grid, args.decode_nbuf, args.decode_ring)
     if args.gemm_variant >= 0:
         for kind in (abi.NF_OP_KQV, abi.NF_OP_O, abi.NF_OP_UGD):
             for which in (0, 1):
@@ -338,6 +340,7 @@ def main():
             "plan": plan_desc,
             "decode_grid": args.decode_grid,
             "decode_nbuf": args.decode_nbuf,
+            "decode_ring": args.decode_ring,
             "gemm_variant": args.gemm_variant,
         },
         "mfma_frac_of_bf16_peak": round(mfma_frac, 4),

@@ -216,7 +216,8 @@ nf_status nf_op_rope_kv_append(nf_ctx *ctx, const nf_layer_cfg *cfg, void *qkv,
 /* Attention of the batch's decode requests (decode = 1) or prefill chunks (decode = 0),
  * reading q from qkv (device [T][(n_q+2n_kv) d], already rotated) and K/V from the pool
  * (already holding this iteration's tokens); writes rows of out (device [T][n_q d]) that
- * belong to those requests. kv_split_blocks: decode split-KV chunk in blocks (0 = default). */
+ * belong to those requests. kv_split_blocks: decode split-KV chunk in blocks, 0..4096
+ * (0 = the context's default). */
 nf_status nf_op_attention(nf_ctx *ctx, const nf_layer_cfg *cfg, const void *qkv,
                           const nf_batch_desc *batch, const nf_kv_pool *pool, void *out,
                           int32_t decode, int32_t kv_split_blocks, void *stream);

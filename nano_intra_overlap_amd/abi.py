@@ -116,7 +116,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                   ctypes.POINTER(ctypes.c_double)]),
         "nf_ctx_set_decode_split": (I, [V, I]),
         "nf_ctx_set_gemm_variant": (I, [V, I, I, I]),
-        "nf_ctx_set_decode_launch": (I, [V, I, I]),
+        "nf_ctx_set_decode_launch": (I, [V, I, I, I]),
         "nf_copy_reference": (I, [V, V, S, V]),
     }
     missing = []
@@ -371,8 +371,10 @@ def nf_ctx_set_decode_split(ctx, blocks: int) -> None:
     _check(load().nf_ctx_set_decode_split(ctx, blocks), ctx)
 
 
-def nf_ctx_set_decode_launch(ctx, max_workgroups: int, nbuf: int = 2) -> None:
-    _check(load().nf_ctx_set_decode_launch(ctx, max_workgroups, nbuf), ctx)
+def nf_ctx_set_decode_launch(ctx, max_workgroups: int, nbuf: int = 1, ring: int = 2) -> None:
+    """Decode attention launch: workgroup cap (0 = one wave per unit), KV blocks per softmax
+    step, and ring depth (register buffers of nbuf blocks; ring - 1 groups in flight)."""
+    _check(load().nf_ctx_set_decode_launch(ctx, max_workgroups, nbuf, ring), ctx)
 
 
 def nf_ctx_set_gemm_variant(ctx, kind: int, which: int, variant: int) -> None:

@@ -13,7 +13,7 @@
 // lane's 4 consecutive keys of one dim are one 8-byte load — both already in the operand
 // layout of the matrix instruction, no LDS transpose needed.
 //
-// Decode work is split along the KV sequence (split-KV): each wave takes at most 64
+// Decode work is split along the KV sequence (split-KV): each wave takes a bounded run of
 // blocks of one request and one KV head; multi-chunk requests write unnormalised partial
 // outputs plus (max, sum) and a combine kernel merges them.
 #include "nf_internal.h"
@@ -115,31 +115,45 @@ __device__ __forceinline__ void load_group(KvFrag<D> (&f)[NB], const bf16* __res
   for (int j = 0; j < NB; ++j) load_block<D>(f[j], kpool, vpool, __shfl(my_blk, min(b + j, nb - 1), 64), n_kv, g, i16, grp);
 }
 
+// Keeps the compiler from moving the loads issued before it past the math after it, and
+// the math of a later group above it (the scheduler would otherwise pull the next group's
+// MFMAs forward, which waits for the loads just issued and empties the pipe every trip).
+__device__ __forceinline__ void issue_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Walk logical blocks [b0, b1) of block-table row `bt_row` (a request with n_keys keys).
-// Full blocks stream in groups of NB through two register buffers (the next group is in
-// flight while the current one is multiplied). The loop body has no branches, which keeps
-// the compiler's memory wait counts exact: loads past the range repeat its last block (a
-// cache hit) and those phantom blocks are masked out. A partial last block is handled
+// Full blocks stream in groups of NB through a ring of R register buffers: while one group
+// is multiplied, the next R-1 groups are in flight. The loop body has no branches, which
+// keeps the compiler's memory wait counts exact: loads past the range repeat its last block
+// (a cache hit) and those phantom blocks are masked out. A partial last block is handled
 // after the loop, with the values of keys past the sequence end zeroed so that stale pool
 // contents cannot leak through 0 * NaN.
-template <int D, int NB>
+template <int D, int NB, int R>
 __device__ __forceinline__ void attend_range(AttnState<D>& st, const bf16x8* qf, const int32_t* __restrict__ bt_row,
                                              int b0, int b1, const bf16* __restrict__ kpool,
                                              const bf16* __restrict__ vpool, int n_kv, int g, int limit, int n_keys,
                                              float scale_log2, int lane) {
+  static_assert(R >= 2, "ring of at least two buffers");
   const int i16 = lane & 15, grp = lane >> 4;
   const int e = min(b1, n_keys / kBlock);  // full blocks: [b0, e)
-  const int ring_limit = min(limit, e * kBlock - 1);
   for (int base = b0; base < e; base += 64) {
     const int nb = min(64, e - base);
     const int my_blk = bt_row[base + min(lane, nb - 1)];
-    KvFrag<D> f0[NB], f1[NB];
-    load_group<D, NB>(f0, kpool, vpool, my_blk, 0, nb, n_kv, g, i16, grp);
-    for (int b = 0; b < nb; b += 2 * NB) {
-      load_group<D, NB>(f1, kpool, vpool, my_blk, b + NB, nb, n_kv, g, i16, grp);
-      attend_group<D, NB>(st, f0, qf, (base + b) * kBlock, ring_limit, scale_log2, grp);
-      load_group<D, NB>(f0, kpool, vpool, my_blk, b + 2 * NB, nb, n_kv, g, i16, grp);
-      attend_group<D, NB>(st, f1, qf, (base + b + NB) * kBlock, ring_limit, scale_log2, grp);
+    // phantom blocks past this batch of (at most 64) blocks are masked out here, also when
+    // the range continues in the next batch
+    const int ring_limit = min(limit, (base + nb) * kBlock - 1);
+    KvFrag<D> f[R][NB];
+#pragma unroll
+    for (int i = 0; i < R - 1; ++i) load_group<D, NB>(f[i], kpool, vpool, my_blk, i * NB, nb, n_kv, g, i16, grp);
+    for (int b = 0; b < nb; b += R * NB) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        load_group<D, NB>(f[(i + R - 1) % R], kpool, vpool, my_blk, b + (i + R - 1) * NB, nb, n_kv, g, i16, grp);
+        issue_fence();
+        attend_group<D, NB>(st, f[i], qf, (base + b + i * NB) * kBlock, ring_limit, scale_log2, grp);
+      }
     }
   }
   if (b1 > e) {
@@ -170,7 +184,7 @@ __device__ __forceinline__ void init_state(AttnState<D>& st) {
 // Waves take work units (item, KV head) in strides of the grid's wave count, so a grid
 // smaller than the work keeps a bounded footprint (the memory nano-op's resource share)
 // while each wave streams many blocks.
-template <int D, int NB>
+template <int D, int NB, int R>
 __global__ __launch_bounds__(256) void decode_attn_kernel(const bf16* __restrict__ qkv, const bf16* __restrict__ kpool,
                                                           const bf16* __restrict__ vpool,
                                                           const int32_t* __restrict__ block_table, int max_blocks,
@@ -201,7 +215,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const bf16* __restrict
     }
     AttnState<D> st;
     init_state<D>(st);
-    attend_range<D, NB>(st, qf, block_table + (size_t)it.req * max_blocks, it.blk_begin, it.blk_end, kpool, vpool,
+    attend_range<D, NB, R>(st, qf, block_table + (size_t)it.req * max_blocks, it.blk_begin, it.blk_end, kpool, vpool,
                           n_kv, g, it.n_keys - 1, it.n_keys, scale_log2, lane);
     const float l = wave_sum16(st.l);
     if (i16 < G) {
@@ -300,7 +314,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(const bf16* __restric
   const int limit = valid ? it.prefix + j : it.prefix + last_q;  // causal limit of this column
   AttnState<D> st;
   init_state<D>(st);
-  attend_range<D, 2>(st, qf, block_table + (size_t)it.req * max_blocks, 0, (tile_keys + kBlock - 1) / kBlock, kpool,
+  attend_range<D, 2, 2>(st, qf, block_table + (size_t)it.req * max_blocks, 0, (tile_keys + kBlock - 1) / kBlock, kpool,
                      vpool, n_kv, g, limit, n_keys, scale_log2, lane);
   const float l = wave_sum16(st.l);
   if (valid) {
@@ -318,51 +332,54 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(const bf16* __restric
 
 // ---------------------------------------------------------------------------------------
 
-template <int D, int NB>
+template <int D, int NB, int R>
 static void launch_decode_t(int grid, hipStream_t s, const bf16* qkv, const bf16* kpool, const bf16* vpool,
                             const int32_t* block_table, int max_blocks, const DecodeItem* items, int n_items,
                             float* part_o, float* part_ml, bf16* out, int n_q, int n_kv, float scale_log2) {
-  hipLaunchKernelGGL((decode_attn_kernel<D, NB>), dim3(grid), dim3(256), 0, s, qkv, kpool, vpool, block_table,
+  hipLaunchKernelGGL((decode_attn_kernel<D, NB, R>), dim3(grid), dim3(256), 0, s, qkv, kpool, vpool, block_table,
                      max_blocks, items, n_items, part_o, part_ml, out, n_q, n_kv, scale_log2);
 }
 
+// Supported (blocks per softmax step, ring depth) pairs.
 template <int D>
-static hipError_t launch_decode_d(int nb, int grid, hipStream_t s, const bf16* qkv, const bf16* kpool,
+static hipError_t launch_decode_d(int nb, int ring, int grid, hipStream_t s, const bf16* qkv, const bf16* kpool,
                                   const bf16* vpool, const int32_t* block_table, int max_blocks,
                                   const DecodeItem* items, int n_items, float* part_o, float* part_ml, bf16* out,
                                   int n_q, int n_kv, float scale_log2) {
-  switch (nb) {
-    case 1:
-      launch_decode_t<D, 1>(grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o, part_ml, out,
-                            n_q, n_kv, scale_log2);
-      break;
-    case 2:
-      launch_decode_t<D, 2>(grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o, part_ml, out,
-                            n_q, n_kv, scale_log2);
-      break;
-    case 4:
-      launch_decode_t<D, 4>(grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o, part_ml, out,
-                            n_q, n_kv, scale_log2);
-      break;
-    default: return hipErrorInvalidValue;
+#define NF_DECODE_CASE(NB_, R_)                                                                                 \
+  if (nb == NB_ && ring == R_) {                                                                                \
+    launch_decode_t<D, NB_, R_>(grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o,    \
+                                part_ml, out, n_q, n_kv, scale_log2);                                           \
+    return hipGetLastError();                                                                                   \
   }
-  return hipGetLastError();
+  NF_DECODE_CASE(1, 2)
+  NF_DECODE_CASE(1, 3)
+  NF_DECODE_CASE(1, 4)
+  NF_DECODE_CASE(2, 2)
+  NF_DECODE_CASE(2, 3)
+#undef NF_DECODE_CASE
+  return hipErrorInvalidValue;
 }
 
-// nb: KV blocks per softmax step (1, 2 or 4); max_grid: workgroup cap (0 = one wave per unit)
+bool decode_config_supported(int nb, int ring) {
+  return (nb == 1 && ring >= 2 && ring <= 4) || (nb == 2 && (ring == 2 || ring == 3));
+}
+
+// nb: KV blocks per softmax step; ring: register buffers of nb blocks (ring - 1 groups in
+// flight); max_grid: workgroup cap (0 = one wave per unit)
 hipError_t launch_decode_attn(const bf16* qkv, const bf16* kpool, const bf16* vpool, const int32_t* block_table,
                               int max_blocks, const DecodeItem* items, int n_items, float* part_o, float* part_ml,
-                              bf16* out, int n_q, int n_kv, int d, int max_grid, int nb, hipStream_t s) {
+                              bf16* out, int n_q, int n_kv, int d, int max_grid, int nb, int ring, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)d);
   const int waves = n_items * n_kv;
   int grid = (waves + 3) / 4;
   if (max_grid > 0 && grid > max_grid) grid = max_grid;
   if (d == 128)
-    return launch_decode_d<128>(nb, grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o,
+    return launch_decode_d<128>(nb, ring, grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o,
                                 part_ml, out, n_q, n_kv, scale_log2);
   if (d == 64)
-    return launch_decode_d<64>(nb, grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o,
+    return launch_decode_d<64>(nb, ring, grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o,
                                part_ml, out, n_q, n_kv, scale_log2);
   return hipErrorInvalidValue;
 }

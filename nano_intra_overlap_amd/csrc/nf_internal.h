@@ -50,7 +50,8 @@ hipError_t launch_rope_kv(bf16* qkv, const int32_t* tok_pos, const int32_t* tok_
 hipError_t launch_decode_attn(const bf16* qkv, const bf16* kpool, const bf16* vpool,
                               const int32_t* block_table, int max_blocks, const DecodeItem* items,
                               int n_items, float* part_o, float* part_ml, bf16* out, int n_q,
-                              int n_kv, int d, int max_grid, int nbuf, hipStream_t s);
+                              int n_kv, int d, int max_grid, int nb, int ring, hipStream_t s);
+bool decode_config_supported(int nb, int ring);
 hipError_t launch_decode_combine(const CombineItem* combines, int n_combines, const float* part_o,
                                  const float* part_ml, bf16* out, int n_q, int n_kv, int d,
                                  hipStream_t s);

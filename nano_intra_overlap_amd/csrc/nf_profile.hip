@@ -250,14 +250,14 @@ bool write_file(Err& E, const char* path, const std::string& text) {
 // Decode attention timing for one launch configuration. bt / bt_stride: the device block
 // table the items index (request r's row starts at r * bt_stride).
 bool time_decode(Err& E, hipStream_t s, const nf_layer_cfg& c, DecodeSet& D, const bf16* qkv, const bf16* kp,
-                 const bf16* vp, const int32_t* bt, int bt_stride, bf16* out, int grid, int nb, int reps,
+                 const bf16* vp, const int32_t* bt, int bt_stride, bf16* out, int grid, int nb, int ring, int reps,
                  double& ms) {
   return time_ms(E, s, reps,
                  [&] {
                    hipError_t e = launch_decode_attn(qkv, kp, vp, bt, bt_stride, D.d_items.as<DecodeItem>(),
                                                      (int)D.M.dec.size(), D.d_part_o.as<float>(),
                                                      D.d_part_ml.as<float>(), out, c.n_q_heads, c.n_kv_heads,
-                                                     c.head_dim, grid, nb, s);
+                                                     c.head_dim, grid, nb, ring, s);
                    if (e != hipSuccess) return e;
                    return launch_decode_combine(D.d_comb.as<CombineItem>(), (int)D.M.comb.size(),
                                                 D.d_part_o.as<float>(), D.d_part_ml.as<float>(), out, c.n_q_heads,
@@ -337,23 +337,25 @@ extern "C" nf_status nf_profile_ops(nf_ctx* ctx, const nf_layer_cfg* cfg, const 
       bool first = true;
       for (int n = step; n <= n_max; n += step) {
         double best = 1e30;
-        int bsplit = 0, bnb = 0;
-        for (int split : {16, 32, 64})
-          for (int nb : {1, 2}) {
+        int bsplit = 0, bnb = 0, bring = 0;
+        for (int split : {32, 64, 128, 256})
+          for (auto cf : {std::pair<int, int>{1, 2}, {1, 3}, {2, 2}}) {
             DecodeSet D;
             if (!build_decode_set(E, c, *tmpl, n, split, D, false)) return false;
             double ms;
             // requests 0..n-1 of D have the contexts of big's first n rows: use big's table
             if (!time_decode(E, s, c, D, S.qkv.as<bf16>(), kp.as<bf16>(), vp.as<bf16>(), big.d_bt.as<int32_t>(),
-                             big.max_blocks, out.as<bf16>(), 0, nb, 3, ms))
+                             big.max_blocks, out.as<bf16>(), 0, cf.first, cf.second, 3, ms))
               return false;
             if (ms < best) {
               best = ms;
               bsplit = split;
-              bnb = nb;
+              bnb = cf.first;
+              bring = cf.second;
             }
           }
-        dec << (first ? "" : ", ") << "[" << n << ", " << json::num(best) << ", " << bsplit << ", " << bnb << "]";
+        dec << (first ? "" : ", ") << "[" << n << ", " << json::num(best) << ", " << bsplit << ", " << bnb << ", "
+            << bring << "]";
         first = false;
       }
     }
@@ -462,7 +464,7 @@ extern "C" nf_status nf_profile_interference(nf_ctx* ctx, const nf_layer_cfg* cf
       hipError_t e = launch_decode_attn(S.qkv.as<bf16>(), kp.as<bf16>(), vp.as<bf16>(), D.d_bt.as<int32_t>(),
                                         D.max_blocks, D.d_items.as<DecodeItem>(), (int)D.M.dec.size(),
                                         D.d_part_o.as<float>(), D.d_part_ml.as<float>(), out.as<bf16>(),
-                                        c.n_q_heads, c.n_kv_heads, d, grid, 1, s);
+                                        c.n_q_heads, c.n_kv_heads, d, grid, 1, 2, s);
       if (e != hipSuccess) return e;
       return launch_decode_combine(D.d_comb.as<CombineItem>(), (int)D.M.comb.size(), D.d_part_o.as<float>(),
                                    D.d_part_ml.as<float>(), out.as<bf16>(), c.n_q_heads, c.n_kv_heads, d, s);

@@ -20,8 +20,8 @@ using namespace nf;
 
 namespace {
 
-constexpr int kMaxSplit = 64;      // decode chunk limit (blocks per wave: one id per lane)
-constexpr int kDefaultSplit = 32;  // default decode chunk (blocks)
+constexpr int kMaxSplit = 4096;    // decode chunk limit (blocks per work item)
+constexpr int kDefaultSplit = 128;  // default decode chunk (blocks)
 constexpr int kMaxStreams = 3;  // + the caller's stream: within the 4 HW queues of a process
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -59,7 +59,8 @@ struct nf_ctx {
   std::vector<hipEvent_t> join_ev;
   int decode_split = kDefaultSplit;
   int decode_grid = 0;  // max workgroups of the decode attention kernel (0 = one wave per work unit)
-  int decode_nbuf = 2;  // KV blocks per online-softmax step (1, 2, 4); one more group in flight
+  int decode_nbuf = 1;  // KV blocks per online-softmax step
+  int decode_ring = 2;  // register buffers of decode_nbuf blocks; decode_ring - 1 groups in flight
   int gemm_variant[NF_OP_KINDS][2];  // per dense op kind: [0] first GEMM, [1] second (UGD down); -1 = default
   // kernel timing: events recorded around instrumented kernel classes on their own stream
   uint32_t timing_mask = 0;
@@ -351,7 +352,7 @@ nf_status launch_op(nf_ctx* ctx, const LayerArgs& A, const PlanGraph& g, const N
         return launch_decode_attn(qkv, static_cast<const bf16*>(A.pool->k), static_cast<const bf16*>(A.pool->v),
                                   M.d_bt, A.max_blocks, M.d_dec + i0, i1 - i0, static_cast<float*>(ctx->part_o.p),
                                   static_cast<float*>(ctx->part_ml.p), attn, nq, nkv, d, A.decode_grid,
-                                  ctx->decode_nbuf, s);
+                                  ctx->decode_nbuf, ctx->decode_ring, s);
       }));
       if (c1 > c0)
         NF_TRY(timed(ctx, NF_K_DECODE_COMBINE, s, [&] {
@@ -608,7 +609,7 @@ extern "C" nf_status nf_op_attention(nf_ctx* ctx, const nf_layer_cfg* cfg, const
   if (!ctx) return NF_E_ARG;
   if (!cfg || !qkv || !batch || !pool || !pool->k || !pool->v || !out || kv_split_blocks < 0 ||
       kv_split_blocks > kMaxSplit) {
-    ctx->err = "nf_op_attention: bad argument (kv_split_blocks in 0..64)";
+    ctx->err = "nf_op_attention: bad argument (kv_split_blocks in 0..4096)";
     return NF_E_ARG;
   }
   const int saved = ctx->decode_split;
@@ -626,7 +627,7 @@ extern "C" nf_status nf_op_attention(nf_ctx* ctx, const nf_layer_cfg* cfg, const
                                    static_cast<const bf16*>(pool->v), M.d_bt, batch->max_blocks, M.d_dec,
                                    (int)M.dec.size(), static_cast<float*>(ctx->part_o.p),
                                    static_cast<float*>(ctx->part_ml.p), static_cast<bf16*>(out), nq, nkv, d,
-                                   ctx->decode_grid, ctx->decode_nbuf, s));
+                                   ctx->decode_grid, ctx->decode_nbuf, ctx->decode_ring, s));
     NF_HIP(ctx, launch_decode_combine(M.d_comb, (int)M.comb.size(), static_cast<const float*>(ctx->part_o.p),
                                       static_cast<const float*>(ctx->part_ml.p), static_cast<bf16*>(out), nq, nkv, d,
                                       s));
@@ -674,10 +675,11 @@ extern "C" nf_status nf_ctx_set_decode_split(nf_ctx* ctx, int32_t blocks) {
   ctx->decode_split = blocks;
   return NF_OK;
 }
-extern "C" nf_status nf_ctx_set_decode_launch(nf_ctx* ctx, int32_t max_workgroups, int32_t nbuf) {
-  if (!ctx || max_workgroups < 0 || (nbuf != 1 && nbuf != 2 && nbuf != 4)) return NF_E_ARG;
+extern "C" nf_status nf_ctx_set_decode_launch(nf_ctx* ctx, int32_t max_workgroups, int32_t nbuf, int32_t ring) {
+  if (!ctx || max_workgroups < 0 || !decode_config_supported(nbuf, ring)) return NF_E_ARG;
   ctx->decode_grid = max_workgroups;
   ctx->decode_nbuf = nbuf;
+  ctx->decode_ring = ring;
   return NF_OK;
 }
 extern "C" nf_status nf_ctx_set_gemm_variant(nf_ctx* ctx, int32_t kind, int32_t which, int32_t variant) {

@@ -202,7 +202,7 @@ def _attention_case(rng, n_q, n_kv, d, dec_ctx, pre_len, pre_prefix, seed):
 
 
 @pytest.mark.parametrize("n_q,n_kv,d", [(4, 2, 64), (32, 8, 128), (8, 1, 128), (16, 1, 64)])
-@pytest.mark.parametrize("split", [0, 1, 3, 64])
+@pytest.mark.parametrize("split", [0, 1, 3, 64, 200])
 def test_decode_attention(ctx, n_q, n_kv, d, split):
     from nano_intra_overlap_amd import abi
     from nano_intra_overlap_amd.device import DevicePool
@@ -223,6 +223,63 @@ def test_decode_attention(ctx, n_q, n_kv, d, split):
     got = f64(_host(out))
     assert np.isfinite(got).all()
     assert rel_inf(got, ref) <= TOL
+
+
+@pytest.mark.parametrize("nb,ring,grid", [(1, 2, 0), (1, 3, 0), (1, 4, 0), (2, 2, 0), (2, 3, 0), (1, 2, 64), (2, 2, 37)])
+@pytest.mark.parametrize("n_q,n_kv,d", [(32, 8, 128), (16, 1, 64)])
+def test_decode_attention_launch_configs(ctx, n_q, n_kv, d, nb, ring, grid):
+    """Every supported (blocks per softmax step, ring depth) pair and bounded persistent
+    grids give the oracle's result, for chunks shorter and longer than 64 blocks."""
+    from nano_intra_overlap_amd import abi
+    from nano_intra_overlap_amd.device import DevicePool
+
+    rng = np.random.default_rng(nb * 10 + ring + grid)
+    dec = np.concatenate([[0, 15, 16, 17, 1023, 1024, 2047, 2600], rng.integers(0, 2700, 30)])
+    b, shape, qkv, kp, vp = _attention_case(rng, n_q, n_kv, d, dec, [], [], seed=nb + ring)
+    T = b.n_tokens
+    q = f64(qkv[:, : n_q * d]).reshape(T, n_q, d)
+    ref = ol.attention_all(shape, b, q, kp, vp).reshape(T, n_q * d)
+    pool = DevicePool.from_host(kp, vp, "cuda")
+    dqkv = _dev(qkv)
+    try:
+        abi.nf_ctx_set_decode_launch(ctx, grid, nb, ring)
+        for split in (0, 48, 300):
+            out = torch.full((T, n_q * d), float("nan"), dtype=torch.bfloat16, device="cuda")
+            log_case(f"decode attention nb={nb} ring={ring} grid={grid} split={split} n_q={n_q} d={d}")
+            abi.nf_op_attention(ctx, abi.make_cfg(shape), dqkv.data_ptr(), abi.HostBatch.from_batch(b), pool.desc,
+                                out.data_ptr(), True, split, torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            got = f64(_host(out))
+            assert np.isfinite(got).all()
+            assert rel_inf(got, ref) <= TOL, (split, rel_inf(got, ref))
+        # q = 0: every key gets weight exactly 1, so the output is the plain mean of the
+        # request's values up to bf16 output rounding and fp32 summation; a key block
+        # counted twice or skipped shifts that mean far more than the bound
+        qkv0 = qkv.copy()
+        qkv0[:, : n_q * d] = 0
+        ref0 = ol.attention_all(shape, b, np.zeros((T, n_q, d)), kp, vp).reshape(T, n_q * d)
+        vmax = np.abs(f64(vp[np.isfinite(f64(vp))])).max()
+        dq0 = _dev(qkv0)
+        for split in (0, 48, 300):
+            out = torch.full((T, n_q * d), float("nan"), dtype=torch.bfloat16, device="cuda")
+            log_case(f"uniform decode attention nb={nb} ring={ring} grid={grid} split={split} n_q={n_q} d={d}")
+            abi.nf_op_attention(ctx, abi.make_cfg(shape), dq0.data_ptr(), abi.HostBatch.from_batch(b), pool.desc,
+                                out.data_ptr(), True, split, torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            got = f64(_host(out))
+            bound = 2.0**-8 * np.abs(ref0) + 4e-4 * vmax
+            bad = np.abs(got - ref0) > bound
+            assert not bad.any(), (split, int(bad.sum()), np.argwhere(bad)[:4].tolist())
+    finally:
+        abi.nf_ctx_set_decode_launch(ctx, 0)
+
+
+def test_decode_launch_rejects_unsupported_configs(ctx):
+    from nano_intra_overlap_amd import abi
+
+    for nb, ring in ((1, 1), (1, 5), (2, 4), (3, 2), (4, 2)):
+        with pytest.raises(abi.NanoflowError):
+            abi.nf_ctx_set_decode_launch(ctx, 0, nb, ring)
 
 
 @pytest.mark.parametrize("n_q,n_kv,d", [(4, 2, 64), (32, 8, 128), (8, 1, 128)])
