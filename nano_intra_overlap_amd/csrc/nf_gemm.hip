@@ -222,6 +222,20 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Scheduling request for the region before the next sched_barrier: one MFMA, one LDS read,
+// repeated, then the remaining MFMAs (or reads).
+template <int NR, int NM>
+__device__ __forceinline__ void interleave_reads() {
+  constexpr int P = NR < NM ? NR : NM;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
+  if constexpr (NM > P) __builtin_amdgcn_sched_group_barrier(0x008, NM - P, 0);
+  if constexpr (NR > P) __builtin_amdgcn_sched_group_barrier(0x100, NR - P, 0);
+}
+
 template <int BM, int BN, int STAGES, int EPI>
 __global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, bf16* C,
                                                         const bf16* R, int M, int N, int K, int tiles_m, int tiles_n,
@@ -307,8 +321,10 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int nk = K / BK;
+  // all STAGES slabs in flight from the start; slab kt + STAGES is issued into slab kt's
+  // buffer once every wave has read slab kt
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
+  for (int s = 0; s < STAGES; ++s)
     if (s < nk) issue(s);
 
   // fragment read offsets (bytes within a slab): row (l % 32) of each 32-row tile, k-chunk 2 kk + l / 32
@@ -329,29 +345,68 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__
       b_off[j][kk] = A_CH * 16 + row * 64 + (((2 * kk + fk) ^ swz(row)) * 16);
     }
 
-  for (int kt = 0; kt < nk; ++kt) {
-    // slab kt landed for this wave once at most the loads of the newer in-flight slabs remain
-    const int newer = min(STAGES - 2, nk - 1 - kt);
-    if (newer >= STAGES - 2) wait_vmcnt<NL * (STAGES - 2)>();
-    else if (newer == 1) wait_vmcnt<NL>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+  // Fragments of the two 16-wide k halves of a slab live in separate registers, so the LDS
+  // reads of one half are in flight while the MFMAs of the other run. Per slab kt:
+  //   read half 1 of kt | MFMAs half 0 | wait slab kt+1, barrier, issue slab kt+STAGES,
+  //   read half 0 of kt+1 | MFMAs half 1.
+  // The scheduling barriers keep the compiler from regrouping reads next to their MFMAs.
+  bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+  auto read_frags = [&](int kt, int kk, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
     const unsigned char* slab = smem_raw + (kt % STAGES) * STAGE_BYTES;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 af[TM], bfr[TN];
+    for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(slab + a_off[i][kk]);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(slab + a_off[i][kk]);
+    for (int j = 0; j < TN; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(slab + b_off[j][kk]);
+  };
+  auto mfmas = [&](const bf16x8 (&fa)[TM], const bf16x8 (&fb)[TN]) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(slab + b_off[j][kk]);
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-  }
+      for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  // wait until at most `newer` slabs issued after the awaited one are still in flight
+  auto wait_slab = [&](int newer) {
+    if (newer >= 3) wait_vmcnt<NL * 3>();
+    else if (newer == 2) wait_vmcnt<NL * 2>();
+    else if (newer == 1) wait_vmcnt<NL>();
+    else wait_vmcnt<0>();
+  };
+  static_assert(STAGES == 4, "wait_slab covers up to three newer slabs");
+
+  wait_slab(min(STAGES - 1, nk - 1));
+  lds_barrier();
+  read_frags(0, 0, fa0, fb0);
+  // one trip: MFMAs of slab kt's first half with the reads of its second half slotted
+  // between them, then the barrier that frees slab kt's buffer and its refill, then the
+  // MFMAs of the second half with the reads of slab kt+1's first half slotted between them.
+  // Each MFMA phase starts with no newer LDS read in flight, so its wait covers only reads
+  // issued a whole phase earlier.
+  auto trip = [&](int kt, auto wait_next, bool refill) {
+    read_frags(kt, 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    interleave_reads<TM + TN, TM * TN>();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_next();
+    lds_barrier();  // every wave has read slab kt
+    if (refill) issue(kt + STAGES);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(kt + 1, 0, fa0, fb0);
+    mfmas(fa1, fb1);
+    interleave_reads<TM + TN, TM * TN>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // steady state: slabs kt+1 .. kt+STAGES-1 in flight, slab kt+1 is awaited with the two
+  // newest still outstanding; the body is straight-line so the compiler's LDS wait counts
+  // stay exact
+  int kt = 0;
+  for (; kt + STAGES < nk; ++kt) trip(kt, [] { wait_vmcnt<NL * 2>(); }, true);
+  // drain: no refills; at most min(2, nk - 2 - kt) newer slabs remain
+  for (; kt + 1 < nk; ++kt) trip(kt, [&] { wait_slab(min(STAGES - 2, nk - 2 - kt)); }, false);
+  read_frags(nk - 1, 1, fa1, fb1);
+  mfmas(fa0, fb0);
+  interleave_reads<TM + TN, TM * TN>();
+  __builtin_amdgcn_sched_barrier(0);
+  mfmas(fa1, fb1);
 
   const int col_l = lane & 31;
   const int row_l = (lane >> 5) * 4;
@@ -419,11 +474,12 @@ bool gemm_variant_supported(int v, int m, int n, int k, int epilogue) {
 
 int gemm_default_variant(int m, int n, int k, int epilogue) {
   if (k % 32 == 0 && m >= 64) {
-    // pipelined tiles (measured on MI355X at the layer's shapes): 256x256 once there are
-    // enough tiles to cover most of the 256 CUs, else 128x128
+    // pipelined tiles (measured on MI355X at the layer's shapes): the largest tile that
+    // still gives at least 192 tiles (three quarters of the 256 CUs in one round)
     const int nn = epilogue == EPI_SWIGLU ? 2 * n : n;
     auto tiles = [&](int bm, int bn) { return ((m + bm - 1) / bm) * ((nn + bn - 1) / bn); };
-    if (tiles(256, 256) >= (epilogue == EPI_SWIGLU ? 128 : 192)) return 6;
+    if (tiles(256, 256) >= 192) return 6;
+    if (tiles(256, 128) >= 192) return 7;
     return 9;
   }
   // enough tiles to cover the 256 CUs at least once; otherwise smaller tiles
