@@ -304,7 +304,7 @@ def nf_gemm_variants():
     _check(lib.nf_gemm_variants(ctypes.byref(cnt), 0, None))
     out = []
     for i in range(cnt.value):
-        t = (ctypes.c_int32 * 3)()
+        t = (ctypes.c_int32 * 4)()
         _check(lib.nf_gemm_variants(None, i, t))
         out.append(tuple(t))
     return out

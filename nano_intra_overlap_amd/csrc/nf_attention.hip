@@ -244,32 +244,53 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const bf16* __restrict
 }
 
 // Merge split-KV partials: o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// One wave per (request, query head): lane p holds part p's (m, l) (64 parts per round),
+// then the weighted sum over parts streams each part's D-vector as one coalesced row.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const CombineItem* __restrict__ items, int n_items,
                                                              const float* __restrict__ part_o,
                                                              const float* __restrict__ part_ml, bf16* __restrict__ out,
                                                              int n_q, int n_kv) {
+  constexpr int PER = D / 64;  // outputs per lane
   const int lane = threadIdx.x & 63;
-  const int wg = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int item_idx = wg / n_kv;
-  const int g = wg % n_kv;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int item_idx = wid / n_q;
+  const int hq = wid % n_q;  // query head
   if (item_idx >= n_items) return;
   const CombineItem it = items[item_idx];
   const int G = n_q / n_kv;
-  for (int e = lane; e < G * D; e += 64) {
-    const int h = e / D, dd = e % D;
-    float M = -INFINITY;
-    for (int p = 0; p < it.n_parts; ++p)
-      M = fmaxf(M, part_ml[(((size_t)(it.part_begin + p) * n_kv + g) * G + h) * 2]);
-    float L = 0.0f, acc = 0.0f;
-    for (int p = 0; p < it.n_parts; ++p) {
-      const size_t pb = ((size_t)(it.part_begin + p) * n_kv + g) * G + h;
-      const float wgt = exp2f(part_ml[pb * 2] - M);
-      L += wgt * part_ml[pb * 2 + 1];
-      acc += wgt * part_o[pb * D + dd];
+  const int g = hq / G, h = hq % G;
+  auto slot = [&](int p) { return ((size_t)(it.part_begin + p) * n_kv + g) * G + h; };
+  float M = -INFINITY;
+  for (int p0 = 0; p0 < it.n_parts; p0 += 64)
+    if (p0 + lane < it.n_parts) M = fmaxf(M, part_ml[slot(p0 + lane) * 2]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  float L = 0.0f, acc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc[j] = 0.0f;
+  for (int p0 = 0; p0 < it.n_parts; p0 += 64) {
+    const int np = min(64, it.n_parts - p0);
+    float wgt = 0.0f;
+    if (lane < np) {
+      const size_t sl = slot(p0 + lane);
+      wgt = exp2f(part_ml[sl * 2] - M);
+      L += wgt * part_ml[sl * 2 + 1];
     }
-    out[(size_t)it.token * n_q * D + (size_t)(g * G + h) * D + dd] = (bf16)(acc / L);
+#pragma unroll 4
+    for (int q = 0; q < np; ++q) {
+      const float w = __shfl(wgt, q, 64);
+      const float* po = part_o + slot(p0 + q) * D + lane * PER;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) acc[j] += w * po[j];
+    }
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
+  const float inv = 1.0f / L;
+  bf16* orow = out + (size_t)it.token * n_q * D + (size_t)hq * D + lane * PER;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) orow[j] = (bf16)(acc[j] * inv);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -387,7 +408,7 @@ hipError_t launch_decode_attn(const bf16* qkv, const bf16* kpool, const bf16* vp
 hipError_t launch_decode_combine(const CombineItem* combines, int n_combines, const float* part_o,
                                  const float* part_ml, bf16* out, int n_q, int n_kv, int d, hipStream_t s) {
   if (n_combines <= 0) return hipSuccess;
-  const int cgrid = (n_combines * n_kv + 3) / 4;
+  const int cgrid = (n_combines * n_q + 3) / 4;
   if (d == 128)
     hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(cgrid), dim3(256), 0, s, combines, n_combines, part_o,
                        part_ml, out, n_q, n_kv);

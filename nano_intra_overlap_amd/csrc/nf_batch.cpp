@@ -301,8 +301,23 @@ nf_status build_plan_graph(const BatchLayout& L, const nf_plan* plan, PlanGraph&
   return NF_OK;
 }
 
+// Chunk size (blocks) for the decode requests [r0, r1): the longest of 128, 64, 32, 16
+// blocks that still yields at least kMinUnits (request chunk, KV head) work units, so that
+// the waves fill the GPU several times over; long chunks have fewer start-ups and combines.
+static int32_t auto_split(const BatchLayout& L, int32_t r0, int32_t r1, int32_t n_kv) {
+  constexpr int64_t kMinUnits = 8192;
+  int32_t sp = 128;
+  for (; sp > 16; sp /= 2) {
+    int64_t units = 0;
+    for (int32_t r = r0; r < r1; ++r) units += ((L.req[r].n_keys + 15) / 16 + sp - 1) / sp;
+    if (units * n_kv >= kMinUnits) break;
+  }
+  return sp;
+}
+
 // Work lists of the decode attention and prefill attention nano-ops of each nano-batch.
-void build_work(const BatchLayout& L, const PlanGraph& g, int split, Meta& M) {
+// split: decode chunk in blocks, 0 = auto_split per nano-op.
+void build_work(const BatchLayout& L, const PlanGraph& g, int split, int n_kv, Meta& M) {
   const int n_nano = g.n_nano;
   M.dec.clear();
   M.comb.clear();
@@ -320,10 +335,11 @@ void build_work(const BatchLayout& L, const PlanGraph& g, int split, Meta& M) {
     M.dec_begin[j] = (int32_t)M.dec.size();
     M.comb_begin[j] = (int32_t)M.comb.size();
     if (dec_op[j]) {
+      const int32_t sp = split > 0 ? split : auto_split(L, dec_op[j]->r0, dec_op[j]->r1, n_kv);
       for (int32_t r = dec_op[j]->r0; r < dec_op[j]->r1; ++r) {
         const ReqInfo& ri = L.req[r];
         const int32_t nblk = (ri.n_keys + 15) / 16;  // KV blocks of 16 tokens
-        const int32_t nch = (nblk + split - 1) / split;
+        const int32_t nch = (nblk + sp - 1) / sp;
         const int32_t per = (nblk + nch - 1) / nch;
         for (int32_t c = 0; c < nch; ++c) {
           DecodeItem it;

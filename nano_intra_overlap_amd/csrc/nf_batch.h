@@ -102,10 +102,13 @@ struct Meta {
   const CombineItem* d_comb = nullptr;
   const PrefillItem* d_pf = nullptr;
   const int32_t* d_bt = nullptr;
+  // dense ops: byte offset of each GEMM's split-K workspace (2 per op: first, second GEMM)
+  std::vector<size_t> gemm_ws_off;
 };
 
-// Decode split-KV chunks of at most `split` blocks (multi-chunk requests get partial slots
+// Decode split-KV chunks of at most `split` blocks (0 = chosen per nano-op so that its
+// (chunk, KV head) units fill the GPU several times; multi-chunk requests get partial slots
 // and a combine entry) and 16-query prefill tiles (longest first), per nano-batch.
-void build_work(const BatchLayout& L, const PlanGraph& g, int split, Meta& M);
+void build_work(const BatchLayout& L, const PlanGraph& g, int split, int n_kv, Meta& M);
 
 }  // namespace nf

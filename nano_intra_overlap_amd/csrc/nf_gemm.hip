@@ -14,11 +14,14 @@
 // Tiles are ordered so that consecutive tiles share rows of A and columns of B, and that
 // consecutive tiles land on the same XCD (workgroups are dealt round-robin to the 8 XCDs,
 // each with its own L2).
+#include <algorithm>
+#include <type_traits>
+
 #include "nf_internal.h"
 
 namespace nf {
 
-enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_PARTIAL = 3 };
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
@@ -239,7 +242,7 @@ __device__ __forceinline__ void interleave_reads() {
 template <int BM, int BN, int STAGES, int EPI>
 __global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, bf16* C,
                                                         const bf16* R, int M, int N, int K, int tiles_m, int tiles_n,
-                                                        int per_xcd) {
+                                                        int per_xcd, float* __restrict__ part) {
   constexpr int BK = 32;
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -270,6 +273,9 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
+  // split-K: slice blockIdx.y of gridDim.y equal slices of K (EPI_PARTIAL only)
+  const int Ks = K / (int)gridDim.y;
+  const int k_begin = (int)blockIdx.y * Ks;
   // per-thread source rows of the direct loads (fixed across k): chunk c = (i*4 + wave)*64 + lane
   const bf16* a_src[A_LOADS];
   const bf16* b_src[B_LOADS];
@@ -278,7 +284,7 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__
     const int c = (i * 4 + wave) * 64 + lane;
     const int row = c >> 2, kc = (c & 3) ^ swz(row);
     const int gr = min(m0 + row, M - 1);
-    a_src[i] = A + (size_t)gr * K + kc * 8;
+    a_src[i] = A + (size_t)gr * K + k_begin + kc * 8;
   }
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
@@ -292,7 +298,7 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__
     } else {
       gr = min(n0 + row, N - 1);
     }
-    b_src[i] = B + (size_t)gr * K + kc * 8;
+    b_src[i] = B + (size_t)gr * K + k_begin + kc * 8;
   }
   typedef __attribute__((address_space(3))) void lds_void;
   auto issue = [&](int kt) {
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = K / BK;
+  const int nk = Ks / BK;
   // all STAGES slabs in flight from the start; slab kt + STAGES is issued into slab kt's
   // buffer once every wave has read slab kt
 #pragma unroll
@@ -408,55 +414,96 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__
   __builtin_amdgcn_sched_barrier(0);
   mfmas(fa1, fb1);
 
+  // Epilogue through LDS: waves park their results row-major in the (now idle) slab ring,
+  // then every thread moves whole 16-byte rows pieces: residual loads and output stores are
+  // 16 bytes per lane instead of the MFMA layout's 2 bytes. The residual sum is taken in
+  // fp32 (one rounding), so that epilogue parks fp32 values, in two passes of row halves
+  // when the tile does not fit.
+  using T = typename std::conditional<EPI == EPI_RESID || EPI == EPI_PARTIAL, float, bf16>::type;
+  constexpr int OC = (EPI == EPI_SWIGLU) ? BN / 2 : BN;  // output columns of the tile
+  constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  constexpr int PASSES = (BM * OC * (int)sizeof(T) <= LDS_BYTES) ? 1 : 2;
+  static_assert(PASSES == 1 || WTM * OC * (int)sizeof(T) <= LDS_BYTES, "epilogue tile half must fit");
+  constexpr int RP = PASSES == 1 ? BM : WTM;  // rows per pass
+  T* park = reinterpret_cast<T*>(smem_raw);
   const int col_l = lane & 31;
   const int row_l = (lane >> 5) * 4;
-  if constexpr (EPI == EPI_SWIGLU) {
+  lds_barrier();  // every wave is done with the slab ring
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int pass = 0; pass < PASSES; ++pass) {
+    if (PASSES == 1 || wm == pass) {
+      const int rbase = PASSES == 1 ? wm * WTM : 0;
 #pragma unroll
-      for (int p = 0; p < TN / 2; ++p) {
-        const int col = n0 + wn * (WTN / 2) + p * 32 + col_l;
-        if (col >= N) continue;
+      for (int i = 0; i < TM; ++i) {
+        if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * WTM + i * 32 + (r / 4) * 8 + row_l + (r % 4);
-          if (row < M) C[(size_t)row * N + col] = (bf16)(silu_f(acc[i][2 * p][r]) * acc[i][2 * p + 1][r]);
+          for (int p = 0; p < TN / 2; ++p)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int lr = rbase + i * 32 + (r / 4) * 8 + row_l + (r % 4);
+              park[lr * OC + wn * (WTN / 2) + p * 32 + col_l] = (bf16)(silu_f(acc[i][2 * p][r]) * acc[i][2 * p + 1][r]);
+            }
+        } else {
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int lr = rbase + i * 32 + (r / 4) * 8 + row_l + (r % 4);
+              park[lr * OC + wn * WTN + j * 32 + col_l] = (T)acc[i][j][r];
+            }
         }
       }
-  } else {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = n0 + wn * WTN + j * 32 + col_l;
-        if (col >= N) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * WTM + i * 32 + (r / 4) * 8 + row_l + (r % 4);
-          if (row < M) {
-            float v = acc[i][j][r];
-            if constexpr (EPI == EPI_RESID) v += (float)R[(size_t)row * N + col];
-            C[(size_t)row * N + col] = (bf16)v;
-          }
-        }
+    }
+    lds_barrier();
+    const int grow0 = m0 + (PASSES == 1 ? 0 : pass * WTM);
+    constexpr int CPR = OC / 8;  // 16-byte output pieces per row
+    for (int c = tid; c < RP * CPR; c += 256) {
+      const int lr = c / CPR, lc = (c % CPR) * 8;
+      const int grow = grow0 + lr, gcol = n0 + lc;
+      if (grow >= M || gcol >= N) continue;
+      if constexpr (EPI == EPI_PARTIAL) {
+        float* dst = part + ((size_t)blockIdx.y * M + grow) * N + gcol;
+        *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(park + lr * OC + lc);
+        *reinterpret_cast<f32x4*>(dst + 4) = *reinterpret_cast<const f32x4*>(park + lr * OC + lc + 4);
+        continue;
       }
+      bf16x8 o;
+      if constexpr (EPI == EPI_RESID) {
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(park + lr * OC + lc);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(park + lr * OC + lc + 4);
+        const bf16x8 rr = *reinterpret_cast<const bf16x8*>(R + (size_t)grow * N + gcol);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] = (bf16)(v0[e] + (float)rr[e]);
+          o[4 + e] = (bf16)(v1[e] + (float)rr[4 + e]);
+        }
+      } else {
+        o = *reinterpret_cast<const bf16x8*>(park + lr * OC + lc);
+      }
+      *reinterpret_cast<bf16x8*>(C + (size_t)grow * N + gcol) = o;
+    }
+    if (PASSES > 1 && pass + 1 < PASSES) lds_barrier();
   }
 }
 
 // ---------------------------------------------------------------------------------------
 
 static const GemmVariant kVariants[] = {
-    {128, 128, 64},  // 0
-    {256, 128, 64},  // 1
-    {128, 256, 64},  // 2
-    {256, 256, 64},  // 3
-    {64, 128, 64},   // 4
-    {128, 64, 64},   // 5
+    {128, 128, 64, 1},  // 0
+    {256, 128, 64, 1},  // 1
+    {128, 256, 64, 1},  // 2
+    {256, 256, 64, 1},  // 3
+    {64, 128, 64, 1},   // 4
+    {128, 64, 64, 1},   // 5
     // pipelined (direct-to-LDS, 4 slabs of 32), K % 32 == 0
-    {256, 256, 32},  // 6
-    {256, 128, 32},  // 7
-    {128, 256, 32},  // 8
-    {128, 128, 32},  // 9
+    {256, 256, 32, 1},  // 6
+    {256, 128, 32, 1},  // 7
+    {128, 256, 32, 1},  // 8
+    {128, 128, 32, 1},  // 9
+    // pipelined 128x128 with K split in 2 or 4 slices (fp32 partials + reduce), for
+    // products with too few output tiles to fill the GPU; not with SwiGLU
+    {128, 128, 32, 2},  // 10
+    {128, 128, 32, 4},  // 11
 };
 static constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -465,11 +512,18 @@ GemmVariant gemm_variant(int i) { return kVariants[i]; }
 
 bool gemm_variant_supported(int v, int m, int n, int k, int epilogue) {
   if (v < 0 || v >= kNumVariants) return false;
-  if (epilogue == EPI_SWIGLU && kVariants[v].bn < 128) return false;
+  const GemmVariant& g = kVariants[v];
+  if (epilogue == EPI_SWIGLU && g.bn < 128) return false;
   if (v >= 6 && (k % 32 != 0)) return false;
+  if (g.ks > 1 && (epilogue == EPI_SWIGLU || k % (32 * g.ks) != 0)) return false;
   (void)m;
   (void)n;
   return true;
+}
+
+size_t gemm_workspace_bytes(int v, int m, int n) {
+  if (v < 0 || v >= kNumVariants || kVariants[v].ks <= 1) return 0;
+  return (size_t)kVariants[v].ks * m * n * sizeof(float);
 }
 
 int gemm_default_variant(int m, int n, int k, int epilogue) {
@@ -480,6 +534,14 @@ int gemm_default_variant(int m, int n, int k, int epilogue) {
     auto tiles = [&](int bm, int bn) { return ((m + bm - 1) / bm) * ((nn + bn - 1) / bn); };
     if (tiles(256, 256) >= 192) return 6;
     if (tiles(256, 128) >= 192) return 7;
+    const int t = tiles(128, 128);
+    if (t < 128 && epilogue != EPI_SWIGLU) {
+      // half the CUs or fewer busy: K slices of at least 1024 (measured: 2 slices pay off
+      // from here, the partial round trip eats the gain above it)
+      if (k % 64 == 0 && k / 2 >= 1024 && 2 * t >= 128) return 10;
+      if (k % 128 == 0 && k / 4 >= 1024) return 11;
+      if (k % 64 == 0 && k / 2 >= 1024) return 10;
+    }
     return 9;
   }
   // enough tiles to cover the 256 CUs at least once; otherwise smaller tiles
@@ -515,9 +577,40 @@ static hipError_t launch_t(const bf16* A, const bf16* B, bf16* C, const bf16* R,
   return hipGetLastError();
 }
 
+// C = sum of the ks fp32 partial products part[s] (+ R), 8 outputs per thread.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int ks, bf16* C,
+                                                            const bf16* R, int M, int N) {
+  const size_t n8 = (size_t)M * N / 8;
+  const size_t plane = (size_t)M * N;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n8; i += (size_t)gridDim.x * blockDim.x) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(part + i * 8);
+    f32x4 b = *reinterpret_cast<const f32x4*>(part + i * 8 + 4);
+    for (int sl = 1; sl < ks; ++sl) {
+      a += *reinterpret_cast<const f32x4*>(part + sl * plane + i * 8);
+      b += *reinterpret_cast<const f32x4*>(part + sl * plane + i * 8 + 4);
+    }
+    bf16x8 o;
+    if (R) {
+      const bf16x8 rr = *reinterpret_cast<const bf16x8*>(R + i * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = (bf16)(a[e] + (float)rr[e]);
+        o[4 + e] = (bf16)(b[e] + (float)rr[4 + e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = (bf16)a[e];
+        o[4 + e] = (bf16)b[e];
+      }
+    }
+    *reinterpret_cast<bf16x8*>(C + i * 8) = o;
+  }
+}
+
 template <int BM, int BN, int STAGES, int EPI>
-static hipError_t launch_pipe_t(const bf16* A, const bf16* B, bf16* C, const bf16* R, int M, int N, int K,
-                                hipStream_t s) {
+static hipError_t launch_pipe_t(const bf16* A, const bf16* B, bf16* C, const bf16* R, int M, int N, int K, int ks,
+                                float* part, hipStream_t s) {
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (EPI == EPI_SWIGLU) ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
   const int ntiles = tiles_m * tiles_n;
@@ -531,18 +624,28 @@ static hipError_t launch_pipe_t(const bf16* A, const bf16* B, bf16* C, const bf1
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(per_xcd * kNumXcd), dim3(256), lds, s, A, B, C, R, M, N, K, tiles_m, tiles_n,
-                     per_xcd);
+  hipLaunchKernelGGL(kern, dim3(per_xcd * kNumXcd, ks), dim3(256), lds, s, A, B, C, R, M, N, K, tiles_m, tiles_n,
+                     per_xcd, part);
   return hipGetLastError();
 }
 
 template <int BM, int BN, int STAGES>
 static hipError_t launch_pipe(const bf16* A, const bf16* B, bf16* C, const bf16* R, int M, int N, int K, int epi,
-                              hipStream_t s) {
+                              int ks, float* ws, hipStream_t s) {
+  if (ks > 1) {
+    // fp32 partials of the ks K-slices, then one pass that sums them with the epilogue
+    hipError_t e = launch_pipe_t<BM, BN, STAGES, EPI_PARTIAL>(A, B, C, R, M, N, K, ks, ws, s);
+    if (e != hipSuccess) return e;
+    const size_t n8 = (size_t)M * N / 8;
+    const int grid = (int)std::min<size_t>((n8 + 255) / 256, 4096);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, s, ws, ks, C, epi == EPI_RESID ? R : nullptr,
+                       M, N);
+    return hipGetLastError();
+  }
   switch (epi) {
-    case EPI_STORE: return launch_pipe_t<BM, BN, STAGES, EPI_STORE>(A, B, C, R, M, N, K, s);
-    case EPI_RESID: return launch_pipe_t<BM, BN, STAGES, EPI_RESID>(A, B, C, R, M, N, K, s);
-    case EPI_SWIGLU: return launch_pipe_t<BM, BN, STAGES, EPI_SWIGLU>(A, B, C, R, M, N, K, s);
+    case EPI_STORE: return launch_pipe_t<BM, BN, STAGES, EPI_STORE>(A, B, C, R, M, N, K, 1, nullptr, s);
+    case EPI_RESID: return launch_pipe_t<BM, BN, STAGES, EPI_RESID>(A, B, C, R, M, N, K, 1, nullptr, s);
+    case EPI_SWIGLU: return launch_pipe_t<BM, BN, STAGES, EPI_SWIGLU>(A, B, C, R, M, N, K, 1, nullptr, s);
   }
   return hipErrorInvalidValue;
 }
@@ -561,8 +664,10 @@ static hipError_t launch_epi(const bf16* A, const bf16* B, bf16* C, const bf16* 
 }
 
 hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int m, int n, int k,
-                       int epilogue, int variant, hipStream_t s) {
+                       int epilogue, int variant, hipStream_t s, float* ws, size_t ws_bytes) {
   if (m <= 0 || n <= 0 || k <= 0) return hipSuccess;
+  if (gemm_workspace_bytes(variant, m, n) > ws_bytes || (gemm_workspace_bytes(variant, m, n) && !ws))
+    return hipErrorInvalidValue;
   switch (variant) {
     case 0: return launch_epi<128, 128, 64>(A, B, C, R, m, n, k, epilogue, s);
     case 1: return launch_epi<256, 128, 64>(A, B, C, R, m, n, k, epilogue, s);
@@ -570,10 +675,12 @@ hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int
     case 3: return launch_epi<256, 256, 64>(A, B, C, R, m, n, k, epilogue, s);
     case 4: return launch_epi<64, 128, 64>(A, B, C, R, m, n, k, epilogue, s);
     case 5: return launch_epi<128, 64, 64>(A, B, C, R, m, n, k, epilogue, s);
-    case 6: return launch_pipe<256, 256, 4>(A, B, C, R, m, n, k, epilogue, s);
-    case 7: return launch_pipe<256, 128, 4>(A, B, C, R, m, n, k, epilogue, s);
-    case 8: return launch_pipe<128, 256, 4>(A, B, C, R, m, n, k, epilogue, s);
-    case 9: return launch_pipe<128, 128, 4>(A, B, C, R, m, n, k, epilogue, s);
+    case 6: return launch_pipe<256, 256, 4>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 7: return launch_pipe<256, 128, 4>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 8: return launch_pipe<128, 256, 4>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 9: return launch_pipe<128, 128, 4>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 10: return launch_pipe<128, 128, 4>(A, B, C, R, m, n, k, epilogue, 2, ws, s);
+    case 11: return launch_pipe<128, 128, 4>(A, B, C, R, m, n, k, epilogue, 4, ws, s);
   }
   return hipErrorInvalidValue;
 }

@@ -30,15 +30,18 @@ constexpr int kNumXcd = 8;       // XCDs of an MI355X
 // ---------------------------------------------------------------------------------------
 
 struct GemmVariant {
-  int bm, bn, bk;
+  int bm, bn, bk, ks;  // tile, k step, K slices (split-K; 1 = none)
 };
 int gemm_variant_count();
 GemmVariant gemm_variant(int i);
 int gemm_default_variant(int m, int n, int k, int epilogue);
 bool gemm_variant_supported(int v, int m, int n, int k, int epilogue);
-// C = A B^T (+ epilogue); returns hipError_t of the launch.
+// fp32 workspace a variant needs for an m x n product (split-K partials; 0 for most)
+size_t gemm_workspace_bytes(int variant, int m, int n);
+// C = A B^T (+ epilogue); returns hipError_t of the launch. ws: workspace of at least
+// gemm_workspace_bytes(variant, m, n) bytes (may be null when that is 0).
 hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int m, int n, int k,
-                       int epilogue, int variant, hipStream_t s);
+                       int epilogue, int variant, hipStream_t s, float* ws = nullptr, size_t ws_bytes = 0);
 
 hipError_t launch_rmsnorm(const bf16* x, const bf16* g, bf16* out, int m, int n, float eps,
                           hipStream_t s);

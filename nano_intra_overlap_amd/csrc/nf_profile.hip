@@ -153,7 +153,7 @@ bool build_decode_set(Err& E, const nf_layer_cfg& c, const nf_batch_desc& tmpl, 
     E.msg = err;
     return false;
   }
-  build_work(D.L, D.g, split, D.M);
+  build_work(D.L, D.g, split, c.n_kv_heads, D.M);
   const int G = c.n_q_heads / c.n_kv_heads;
   if (upload_table) {
     PF_HIP(D.d_bt.alloc(D.bt.size() * 4));
@@ -216,10 +216,16 @@ bool best_gemm(Err& E, hipStream_t s, const bf16* A, const bf16* B, bf16* C, con
                int epi, int reps, double& best_ms, int& best_v) {
   best_ms = 1e30;
   best_v = -1;
+  size_t wsb = 0;
+  for (int v = 0; v < gemm_variant_count(); ++v)
+    if (gemm_variant_supported(v, m, n, k, epi)) wsb = std::max(wsb, gemm_workspace_bytes(v, m, n));
+  Buf ws;
+  if (wsb) PF_HIP(ws.alloc(wsb));
   for (int v = 0; v < gemm_variant_count(); ++v) {
     if (!gemm_variant_supported(v, m, n, k, epi)) continue;
     double ms;
-    if (!time_ms(E, s, reps, [&] { return launch_gemm(A, B, C, R, m, n, k, epi, v, s); }, ms)) return false;
+    if (!time_ms(E, s, reps, [&] { return launch_gemm(A, B, C, R, m, n, k, epi, v, s, ws.as<float>(), wsb); }, ms))
+      return false;
     if (ms < best_ms) {
       best_ms = ms;
       best_v = v;
@@ -338,7 +344,7 @@ extern "C" nf_status nf_profile_ops(nf_ctx* ctx, const nf_layer_cfg* cfg, const 
       for (int n = step; n <= n_max; n += step) {
         double best = 1e30;
         int bsplit = 0, bnb = 0, bring = 0;
-        for (int split : {32, 64, 128, 256})
+        for (int split : {0, 16, 32, 64, 128})
           for (auto cf : {std::pair<int, int>{1, 2}, {1, 3}, {2, 2}}) {
             DecodeSet D;
             if (!build_decode_set(E, c, *tmpl, n, split, D, false)) return false;
@@ -453,11 +459,16 @@ extern "C" nf_status nf_profile_interference(nf_ctx* ctx, const nf_layer_cfg* cf
     if (!fill(E, vp, (size_t)D.num_blocks * per_block, 92, 1.3f, s0)) return false;
     PF_HIP(hipStreamSynchronize(s0));
     const int vug = gemm_default_variant(m, F, H, 2), vdn = gemm_default_variant(m, H, F, 1);
+    const size_t wsb = std::max(gemm_workspace_bytes(vug, m, F), gemm_workspace_bytes(vdn, m, H));
+    Buf gws;
+    if (wsb) PF_HIP(gws.alloc(wsb));
     // compute op: one Up/Gate/Down nano-op; memory op: one decode attention nano-op
     auto gemm_op = [&](hipStream_t s) -> hipError_t {
-      hipError_t e = launch_gemm(S.h2.as<bf16>(), S.wgu.as<bf16>(), S.a.as<bf16>(), nullptr, m, F, H, 2, vug, s);
+      hipError_t e = launch_gemm(S.h2.as<bf16>(), S.wgu.as<bf16>(), S.a.as<bf16>(), nullptr, m, F, H, 2, vug, s,
+                                 gws.as<float>(), wsb);
       if (e != hipSuccess) return e;
-      return launch_gemm(S.a.as<bf16>(), S.wd.as<bf16>(), S.y.as<bf16>(), S.x1.as<bf16>(), m, H, F, 1, vdn, s);
+      return launch_gemm(S.a.as<bf16>(), S.wd.as<bf16>(), S.y.as<bf16>(), S.x1.as<bf16>(), m, H, F, 1, vdn, s,
+                         gws.as<float>(), wsb);
     };
     int grid = 0;
     auto mem_op = [&](hipStream_t s) -> hipError_t {

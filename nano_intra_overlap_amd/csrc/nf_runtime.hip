@@ -21,7 +21,7 @@ using namespace nf;
 namespace {
 
 constexpr int kMaxSplit = 4096;    // decode chunk limit (blocks per work item)
-constexpr int kDefaultSplit = 128;  // default decode chunk (blocks)
+constexpr int kDefaultSplit = 0;  // default decode chunk: 0 = chosen per nano-op from its work
 constexpr int kMaxStreams = 3;  // + the caller's stream: within the 4 HW queues of a process
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -46,6 +46,7 @@ struct nf_ctx {
   bool upload_pending = false;
   // split-KV partials
   DevBuf part_o, part_ml;
+  DevBuf gemm_ws;  // split-K fp32 partials, one region per GEMM of a plan
   // streams keyed by CU mask (all-ones key = unmasked)
   struct StreamEntry {
     std::vector<uint32_t> mask;
@@ -281,6 +282,32 @@ int pick_variant(nf_ctx* ctx, int kind, int which, int m, int n, int k, int epi)
   return gemm_default_variant(m, n, k, epi);
 }
 
+// Split-K workspace of every GEMM of the plan, each in a region of its own (GEMMs of one
+// plan may run concurrently on different streams).
+nf_status plan_gemm_ws(nf_ctx* ctx, const nf_layer_cfg& c, const PlanGraph& g, Meta& M) {
+  const int H = c.hidden, F = c.ffn, Q = c.n_q_heads * c.head_dim;
+  const int W = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  M.gemm_ws_off.assign(2 * g.ops.size(), 0);
+  size_t total = 0;
+  auto take = [&](size_t i, size_t bytes) {
+    if (!bytes) return;
+    M.gemm_ws_off[i] = total;
+    total += (bytes + 255) / 256 * 256;
+  };
+  for (size_t i = 0; i < g.ops.size(); ++i) {
+    const NanoOp& op = g.ops[i];
+    const int m = g.bounds[op.nano + 1] - g.bounds[op.nano];
+    if (m <= 0) continue;
+    if (op.kind == NF_OP_KQV) take(2 * i, gemm_workspace_bytes(pick_variant(ctx, NF_OP_KQV, 0, m, W, H, 0), m, W));
+    if (op.kind == NF_OP_O) take(2 * i, gemm_workspace_bytes(pick_variant(ctx, NF_OP_O, 0, m, H, Q, 1), m, H));
+    if (op.kind == NF_OP_UGD) {
+      take(2 * i, gemm_workspace_bytes(pick_variant(ctx, NF_OP_UGD, 0, m, F, H, 2), m, F));
+      take(2 * i + 1, gemm_workspace_bytes(pick_variant(ctx, NF_OP_UGD, 1, m, H, F, 1), m, H));
+    }
+  }
+  return total ? ensure(ctx, ctx->gemm_ws, total) : NF_OK;
+}
+
 nf_status timing_event(nf_ctx* ctx, hipEvent_t* e) {
   if (ctx->timing_pool_used == ctx->timing_pool.size()) {
     hipEvent_t ev;
@@ -316,6 +343,11 @@ nf_status launch_op(nf_ctx* ctx, const LayerArgs& A, const PlanGraph& g, const N
   const int H = c.hidden, F = c.ffn, d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
   const int W = (nq + 2 * nkv) * d;
   const int lo = g.bounds[op.nano], hi = g.bounds[op.nano + 1], m = hi - lo;
+  const size_t op_i = &op - g.ops.data();
+  auto ws = [&](int which) {
+    return reinterpret_cast<float*>(static_cast<char*>(ctx->gemm_ws.p) + M.gemm_ws_off[2 * op_i + which]);
+  };
+  const size_t ws_cap = ctx->gemm_ws.cap;
   bf16* h = static_cast<bf16*>(ctx->h.p);
   bf16* qkv = static_cast<bf16*>(ctx->qkv.p);
   bf16* attn = static_cast<bf16*>(ctx->attn.p);
@@ -337,7 +369,7 @@ nf_status launch_op(nf_ctx* ctx, const LayerArgs& A, const PlanGraph& g, const N
       }));
       NF_TRY(timed(ctx, NF_K_GEMM_KQV, s, [&] {
         return launch_gemm(h + (size_t)lo * H, static_cast<const bf16*>(A.w->w_qkv), qkv + (size_t)lo * W, nullptr, m,
-                           W, H, 0, pick_variant(ctx, NF_OP_KQV, 0, m, W, H, 0), s);
+                           W, H, 0, pick_variant(ctx, NF_OP_KQV, 0, m, W, H, 0), s, ws(0), ws_cap - M.gemm_ws_off[2 * op_i]);
       }));
       NF_TRY(timed(ctx, NF_K_ROPE_KV, s, [&] {
         return launch_rope_kv(qkv, M.d_pos, M.d_slot, M.d_inv_freq, static_cast<bf16*>(A.pool->k),
@@ -372,7 +404,8 @@ nf_status launch_op(nf_ctx* ctx, const LayerArgs& A, const PlanGraph& g, const N
     case NF_OP_O: {
       NF_TRY(timed(ctx, NF_K_GEMM_O, s, [&] {
         return launch_gemm(attn + (size_t)lo * nq * d, static_cast<const bf16*>(A.w->w_o), x1 + (size_t)lo * H,
-                           A.x + (size_t)lo * H, m, H, nq * d, 1, pick_variant(ctx, NF_OP_O, 0, m, H, nq * d, 1), s);
+                           A.x + (size_t)lo * H, m, H, nq * d, 1, pick_variant(ctx, NF_OP_O, 0, m, H, nq * d, 1), s,
+                           ws(0), ws_cap - M.gemm_ws_off[2 * op_i]);
       }));
       break;
     }
@@ -383,11 +416,13 @@ nf_status launch_op(nf_ctx* ctx, const LayerArgs& A, const PlanGraph& g, const N
       }));
       NF_TRY(timed(ctx, NF_K_GEMM_UG, s, [&] {
         return launch_gemm(h2 + (size_t)lo * H, static_cast<const bf16*>(A.w->w_gate_up), a + (size_t)lo * F, nullptr,
-                           m, F, H, 2, pick_variant(ctx, NF_OP_UGD, 0, m, F, H, 2), s);
+                           m, F, H, 2, pick_variant(ctx, NF_OP_UGD, 0, m, F, H, 2), s, ws(0),
+                           ws_cap - M.gemm_ws_off[2 * op_i]);
       }));
       NF_TRY(timed(ctx, NF_K_GEMM_DOWN, s, [&] {
         return launch_gemm(a + (size_t)lo * F, static_cast<const bf16*>(A.w->w_down), A.y + (size_t)lo * H,
-                           x1 + (size_t)lo * H, m, H, F, 1, pick_variant(ctx, NF_OP_UGD, 1, m, H, F, 1), s);
+                           x1 + (size_t)lo * H, m, H, F, 1, pick_variant(ctx, NF_OP_UGD, 1, m, H, F, 1), s, ws(1),
+                           ws_cap - M.gemm_ws_off[2 * op_i + 1]);
       }));
       break;
     }
@@ -409,9 +444,10 @@ nf_status prepare_batch(nf_ctx* ctx, const nf_layer_cfg* cfg, const nf_batch_des
       st = mask_ok(ctx, plan->cu_masks + s * NF_CU_MASK_WORDS);
       if (st != NF_OK) return st;
     }
-  build_work(L, g, ctx->decode_split, M);
+  build_work(L, g, ctx->decode_split, cfg->n_kv_heads, M);
   if ((st = ensure_workspace(ctx, *cfg, L.T)) != NF_OK) return st;
   if ((st = ensure_parts(ctx, *cfg, M.n_parts)) != NF_OK) return st;
+  if ((st = plan_gemm_ws(ctx, *cfg, g, M)) != NF_OK) return st;
   return upload_meta(ctx, *cfg, *batch, L, M, stream);
 }
 
@@ -449,7 +485,7 @@ extern "C" void nf_ctx_destroy(nf_ctx* ctx) {
   if (ctx->fork_ev) (void)hipEventDestroy(ctx->fork_ev);
   if (ctx->upload_done) (void)hipEventDestroy(ctx->upload_done);
   for (DevBuf* b : {&ctx->h, &ctx->qkv, &ctx->attn, &ctx->x1, &ctx->h2, &ctx->a, &ctx->meta_dev, &ctx->part_o,
-                    &ctx->part_ml})
+                    &ctx->part_ml, &ctx->gemm_ws})
     if (b->p) (void)hipFree(b->p);
   if (ctx->meta_host) (void)hipHostFree(ctx->meta_host);
   delete ctx;
@@ -540,14 +576,15 @@ extern "C" nf_status nf_debug_buffer(nf_ctx* ctx, int32_t which, void** ptr, siz
   return NF_OK;
 }
 
-extern "C" nf_status nf_gemm_variants(int32_t* count, int32_t index, int32_t* out3) {
+extern "C" nf_status nf_gemm_variants(int32_t* count, int32_t index, int32_t* out4) {
   if (count) *count = gemm_variant_count();
-  if (out3) {
+  if (out4) {
     if (index < 0 || index >= gemm_variant_count()) return NF_E_ARG;
     const GemmVariant v = gemm_variant(index);
-    out3[0] = v.bm;
-    out3[1] = v.bn;
-    out3[2] = v.bk;
+    out4[0] = v.bm;
+    out4[1] = v.bn;
+    out4[2] = v.bk;
+    out4[3] = v.ks;
   }
   return NF_OK;
 }
@@ -568,8 +605,14 @@ extern "C" nf_status nf_op_gemm(nf_ctx* ctx, const void* A, const void* B, void*
     return NF_E_ARG;
   }
   const int v = variant < 0 ? gemm_default_variant(m, n, k, epilogue) : variant;
+  const size_t wsb = gemm_workspace_bytes(v, m, n);
+  if (wsb) {
+    nf_status st = ensure(ctx, ctx->gemm_ws, wsb);
+    if (st != NF_OK) return st;
+  }
   NF_HIP(ctx, launch_gemm(static_cast<const bf16*>(A), static_cast<const bf16*>(B), static_cast<bf16*>(C),
-                          static_cast<const bf16*>(R), m, n, k, epilogue, v, static_cast<hipStream_t>(stream)));
+                          static_cast<const bf16*>(R), m, n, k, epilogue, v, static_cast<hipStream_t>(stream),
+                          static_cast<float*>(ctx->gemm_ws.p), ctx->gemm_ws.cap));
   return NF_OK;
 }
 
@@ -671,7 +714,7 @@ extern "C" nf_status nf_timing_summary(nf_ctx* ctx, int32_t cls, int32_t* count,
 
 // Internal knobs used by the profiler (not in the public header).
 extern "C" nf_status nf_ctx_set_decode_split(nf_ctx* ctx, int32_t blocks) {
-  if (!ctx || blocks < 1 || blocks > kMaxSplit) return NF_E_ARG;
+  if (!ctx || blocks < 0 || blocks > kMaxSplit) return NF_E_ARG;
   ctx->decode_split = blocks;
   return NF_OK;
 }

@@ -41,11 +41,13 @@ GEMM_SHAPES = [(1, 64, 64), (77, 520, 264), (300, 688, 688), (513, 1024, 256), (
                (300, 688, 672), (1, 256, 96)]
 # the layer's shapes (K, N of each projection at the 8B and 70B-share sizes), checked on sampled rows
 LAYER_GEMMS = [(1024, 6144, 4096, 0), (2048, 4096, 4096, 1), (1536, 14336, 4096, 2), (1024, 4096, 14336, 1),
-               (2048, 10240, 8192, 0), (512, 3584, 8192, 2), (2048, 8192, 3584, 1)]
+               (2048, 1280, 8192, 0), (1024, 1280, 8192, 0), (512, 3584, 8192, 2), (2048, 8192, 3584, 1),
+               (1024, 8192, 1024, 1)]
 
 
-def _supported(v, k, epi, bn):
-    return not (epi == 2 and bn < 128) and not (v >= 6 and k % 32)
+def _supported(v, k, epi, bn, ks=1):
+    return (not (epi == 2 and bn < 128) and not (v >= 6 and k % 32)
+            and not (ks > 1 and (epi == 2 or k % (32 * ks))))
 
 
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
@@ -63,8 +65,8 @@ def test_gemm_all_variants(ctx, m, n, k, epi):
     if epi == 2:
         ref = ol.swiglu(ref, n)
     dA, dB, dR = _dev(A), _dev(B), _dev(R)
-    for v, (bm, bn, bk) in enumerate(abi.nf_gemm_variants()):
-        if not _supported(v, k, epi, bn):
+    for v, (bm, bn, bk, ks) in enumerate(abi.nf_gemm_variants()):
+        if not _supported(v, k, epi, bn, ks):
             continue
         dC = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
         log_case(f"gemm m={m} n={n} k={k} epi={epi} variant={v}")
@@ -74,7 +76,7 @@ def test_gemm_all_variants(ctx, m, n, k, epi):
         got = f64(_host(dC))
         assert np.isfinite(got).all(), f"variant {v}: unwritten outputs"
         err = rel_inf(got, ref)
-        assert err <= TOL, f"variant {v} ({bm}x{bn}x{bk}): rel err {err}"
+        assert err <= TOL, f"variant {v} ({bm}x{bn}x{bk}, {ks} K slices): rel err {err}"
 
 
 @pytest.mark.parametrize("m,n,k,epi", LAYER_GEMMS)
@@ -92,8 +94,8 @@ def test_gemm_layer_shapes_sampled_rows(ctx, m, n, k, epi):
     if epi == 2:
         ref = ol.swiglu(ref, n)
     dA, dB, dR = _dev(A), _dev(B), _dev(R)
-    for v, (bm, bn, bk) in [(-1, (0, 0, 0))] + list(enumerate(abi.nf_gemm_variants())):
-        if v >= 0 and (not _supported(v, k, epi, bn) or v < 6):
+    for v, (bm, bn, bk, ks) in [(-1, (0, 0, 0, 1))] + list(enumerate(abi.nf_gemm_variants())):
+        if v >= 0 and (not _supported(v, k, epi, bn, ks) or v < 6):
             continue
         dC = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
         log_case(f"gemm layer shape m={m} n={n} k={k} epi={epi} variant={v}")
@@ -106,16 +108,17 @@ def test_gemm_layer_shapes_sampled_rows(ctx, m, n, k, epi):
         assert err <= TOL, f"variant {v}: rel err {err}"
 
 
-def test_gemm_residual_in_place(ctx):
+@pytest.mark.parametrize("variant", [-1, 6, 7, 9, 10, 11])
+def test_gemm_residual_in_place(ctx, variant):
     from nano_intra_overlap_amd import abi
 
-    rng = np.random.default_rng(5)
-    m, n, k = 200, 256, 128
+    rng = np.random.default_rng(5 + variant)
+    m, n, k = 200, 256, 256
     A, B, R = rand_bf16(rng, (m, k)), rand_bf16(rng, (n, k), 0.05), rand_bf16(rng, (m, n))
     ref = f64(R) + ol.linear(f64(A), f64(B))
     dA, dB, dR = _dev(A), _dev(B), _dev(R)  # keep every operand alive until the kernel ran
-    log_case("gemm residual aliasing C=R")
-    abi.nf_op_gemm(ctx, dA.data_ptr(), dB.data_ptr(), dR.data_ptr(), dR.data_ptr(), m, n, k, 1, -1,
+    log_case(f"gemm residual aliasing C=R variant={variant}")
+    abi.nf_op_gemm(ctx, dA.data_ptr(), dB.data_ptr(), dR.data_ptr(), dR.data_ptr(), m, n, k, 1, variant,
                    torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert rel_inf(f64(_host(dR)), ref) <= TOL
