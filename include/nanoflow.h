@@ -106,10 +106,14 @@ typedef struct {
 } nf_batch_desc;
 
 /* Paged KV pool of one layer, device, caller-owned:
- *   k [num_blocks][n_kv][block_size][head_dim]   token-major within a block
- *   v [num_blocks][n_kv][head_dim][block_size]   dim-major within a block
+ *   k [num_blocks][n_kv][head_dim / 32][block_size][32]   within a block, the key dims in
+ *                                                      column chunks of 32, each chunk
+ *                                                      token-major (dim = chunk * 32 + j)
+ *   v [num_blocks][n_kv][head_dim][block_size]         dim-major within a block
  * Position p of request r lives in block table[r][p / block_size] at offset
- * p % block_size. nf_layer_forward writes exactly the slots of this iteration's tokens.   */
+ * p % block_size. nf_layer_forward writes exactly the slots of this iteration's tokens.
+ * (The chunked key layout makes one load instruction of the attention kernels cover whole
+ * 128-byte lines: 16 tokens x 64 bytes of one chunk are contiguous.)                       */
 typedef struct {
   void *k, *v;
   int32_t num_blocks;

@@ -8,10 +8,11 @@
 //   prefill: columns = 16 consecutive queries of one query head
 // Per block: S^T[16 keys][16 cols] = K_blk Q^T with 16x16x32 bf16 MFMAs over head_dim,
 // an online softmax per column (base-2 exponent, running max and sum), then
-// O^T[d][16 cols] += V_blk^T P^T with 16x16x16 bf16 MFMAs. K is token-major within a block,
-// so a lane's 8 consecutive dims are one 16-byte load; V is dim-major within a block, so a
-// lane's 4 consecutive keys of one dim are one 8-byte load — both already in the operand
-// layout of the matrix instruction, no LDS transpose needed.
+// O^T[d][16 cols] += V_blk^T P^T with 16x16x16 bf16 MFMAs. K is stored in 32-dim column
+// chunks, each token-major, so a lane's 8 consecutive dims are one 16-byte load and one
+// wave instruction reads 16 tokens x 64 bytes = 1 KB of whole lines; V is dim-major within
+// a block, so a lane's 4 consecutive keys of one dim are one 8-byte load — both already in
+// the operand layout of the matrix instruction, no LDS transpose needed.
 //
 // Decode work is split along the KV sequence (split-KV): each wave takes a bounded run of
 // blocks of one request and one KV head; multi-chunk requests write unnormalised partial
@@ -55,7 +56,7 @@ __device__ __forceinline__ void load_block(KvFrag<D>& f, const bf16* __restrict_
   const bf16* vb = vpool + ((size_t)blk * n_kv + g) * (D * kBlock);
 #pragma unroll
   for (int c = 0; c < D / 32; ++c)
-    f.k[c] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(kb + i16 * D + c * 32 + grp * 8));
+    f.k[c] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(kb + c * (kBlock * 32) + i16 * 32 + grp * 8));
 #pragma unroll
   for (int dc = 0; dc < D / 16; ++dc)
     f.v[dc] = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(vb + (dc * 16 + i16) * kBlock + grp * 4));

@@ -5,8 +5,9 @@
 // Rotary: rotate-half pairs (i, i + d/2) of every q and k head by angle pos * inv_freq[i];
 // the rotated k and the value v of each token are stored at the token's paged-KV slot
 // ("Inside nano-vLLM", paged KV: the slot mapping locates new KV stores; "LLM Inference
-// Performance", PagedAttention block tables). K is stored token-major within a block,
-// V dim-major within a block (the layout the attention kernels read with matrix cores).
+// Performance", PagedAttention block tables). Within a block, K is stored in 32-dim column
+// chunks, each token-major, and V dim-major (the layouts the attention kernels read with
+// matrix cores).
 #include "nf_internal.h"
 
 namespace nf {
@@ -79,10 +80,11 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(bf16* __restrict__ qkv, co
       hp[j] = o1;
       hp[j + half] = o2;
     } else {
+      // key block layout [d/32][16][32]: dim i of this token at (i / 32, off, i % 32)
       const int g = head - n_q;
-      bf16* kp = kpool + (((size_t)blk * n_kv + g) * kBlock + off) * d;
-      kp[j] = o1;
-      kp[j + half] = o2;
+      bf16* kb = kpool + ((size_t)blk * n_kv + g) * (kBlock * d) + off * 32;
+      kb[(j >> 5) * (kBlock * 32) + (j & 31)] = o1;
+      kb[((j + half) >> 5) * (kBlock * 32) + ((j + half) & 31)] = o2;
     }
   }
   const bf16* vrow = row + (n_q + n_kv) * d;

@@ -34,7 +34,8 @@ class DeviceWeights:
 
 
 class DevicePool:
-    """Paged KV pool of one layer on the device (K token-major, V dim-major in a block)."""
+    """Paged KV pool of one layer on the device (K in 32-dim column chunks, each token-major,
+    and V dim-major within a block)."""
 
     def __init__(self, k: torch.Tensor, v: torch.Tensor):
         assert k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16

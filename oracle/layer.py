@@ -34,8 +34,10 @@ Readings where the pages are silent (stated again in the design notes):
   stored in bfloat16; arithmetic inside an operation is exact here (float64, which bounds
   any fp32 accumulation). ``storage="exact"`` drops the between-op rounding.
 
-Pool layout (the library's boundary layout): K [num_blocks, n_kv, BS, d] (token-major in a
-block), V [num_blocks, n_kv, d, BS] (dim-major in a block). Both hold bfloat16 bit patterns.
+Pool layout (the library's boundary layout): K [num_blocks, n_kv, d/32, BS, 32] (in a block,
+the keys' dims in column chunks of 32, each chunk token-major; a head dim that is not a
+multiple of 32 is a single chunk), V [num_blocks, n_kv, d, BS] (dim-major in a block). Both
+hold bfloat16 bit patterns.
 
 Parity pins: every function here is pinned by the not-gpu tests (brute-force attention on
 tiny inputs, paged/contiguous invariance, request-subset invariance, decode/prefill
@@ -181,7 +183,8 @@ def gather_kv(k_pool, v_pool, batch, block_size: int, r: int, n_keys: int):
     if np.any(blk < 0) or np.any(blk >= batch.num_blocks):
         raise IndexError(f"request {r}: block id out of range")
     off = p % block_size
-    keys = k_pool[blk, :, off, :]  # [n, n_kv, d]
+    keys = k_pool[blk, :, :, off, :]  # advanced indices first: [n, n_kv, d/32, 32]
+    keys = keys.reshape(keys.shape[0], keys.shape[1], keys.shape[2] * keys.shape[3])  # dim = chunk * c + j
     values = v_pool[blk, :, :, off]  # advanced indices first: [n, n_kv, d]
     return bf16_to_f64(keys), bf16_to_f64(values)
 
@@ -217,9 +220,28 @@ def write_kv(k_pool, v_pool, batch, block_size: int, k, v):
     kb = f64_to_bf16(k)
     vb = f64_to_bf16(v)
     for t, (blk, off) in enumerate(new_token_slots(batch, block_size)):
-        k_new[blk, :, off, :] = kb[t]
+        k_new[blk, :, :, off, :] = kb[t].reshape(kb.shape[1], k_pool.shape[2], k_pool.shape[4])
         v_new[blk, :, :, off] = vb[t]
     return k_new, v_new
+
+
+def k_tokens(k_pool):
+    """Token-major view [num_blocks, n_kv, BS, d] of a key pool in the boundary layout."""
+    nb, g, nc, bs, ch = k_pool.shape
+    return k_pool.transpose(0, 1, 3, 2, 4).reshape(nb, g, bs, nc * ch)
+
+
+def k_chunk(d: int) -> int:
+    """Dims per key column chunk: 32 (the library's head dims are multiples of 32); a head dim
+    that is not a multiple of 32 is one chunk (plain token-major)."""
+    return 32 if d % 32 == 0 else d
+
+
+def k_pool_from_tokens(k_tok):
+    """Boundary layout [num_blocks, n_kv, d/c, BS, c] of token-major keys [.., BS, d]."""
+    nb, g, bs, d = k_tok.shape
+    c = k_chunk(d)
+    return np.ascontiguousarray(k_tok.reshape(nb, g, bs, d // c, c).transpose(0, 1, 3, 2, 4))
 
 
 # --------------------------------------------------------------------------------------
@@ -252,7 +274,7 @@ def layer_forward(cfg, weights, x_bits, batch, k_pool, v_pool, storage: str = "b
             g_ffn [H], w_gate_up [2F, H], w_down [H, F]
     x_bits  bf16 bits [T, H]
     batch   object with decode_ctx, prefill_len, prefill_prefix, block_table, num_blocks
-    k_pool  bf16 bits [num_blocks, n_kv, BS, d]; v_pool bf16 bits [num_blocks, n_kv, d, BS]
+    k_pool  bf16 bits [num_blocks, n_kv, d/32, BS, 32]; v_pool bf16 bits [num_blocks, n_kv, d, BS]
     storage "bf16": the numeric model of a bf16-storage layer — every tensor handed from one
             operation to the next (h, qkv, rotated q, attention output, x1, h2, a, y; K/V in
             the pool) is stored in bfloat16 (round to nearest even) and everything inside an

@@ -18,6 +18,11 @@ from dataclasses import dataclass, field
 import numpy as np
 
 BLOCK_SIZE = 16
+K_CHUNK = 32  # keys are stored in column chunks of this many dims (see make_kv_pool_blocks)
+
+
+def _k_chunk(d: int) -> int:
+    return K_CHUNK if d % K_CHUNK == 0 else d
 
 # --------------------------------------------------------------------------------------
 # bf16 storage helpers (input generation only)
@@ -391,9 +396,9 @@ def _kv_scale(shape: Shape) -> np.float32:
 def make_kv_pool_blocks(shape: Shape, blocks, seed: int, layer: int = 0):
     """History contents of the given physical blocks (host, numpy).
 
-    Returns (K, V) as uint16 bf16 bits with shapes K [n, n_kv, BS, d] and V [n, n_kv, d, BS]
-    (token-major keys, dim-major values within a block). Element (block b, head g, token t,
-    dim i) is the same value in K and V's logical index space whichever layout holds it.
+    Returns (K, V) as uint16 bf16 bits with shapes K [n, n_kv, d/32, BS, 32] (keys in
+    32-dim column chunks, each chunk token-major) and V [n, n_kv, d, BS] (dim-major values).
+    Element (block b, head g, token t, dim i) has the same value whichever layout holds it.
     """
     blocks = np.asarray(blocks, dtype=np.int64).reshape(-1)
     G, BS, D = shape.n_kv, shape.block_size, shape.head_dim
@@ -410,6 +415,8 @@ def make_kv_pool_blocks(shape: Shape, blocks, seed: int, layer: int = 0):
         bits = f32_to_bf16_bits(vals).reshape(blocks.shape[0], G, BS, D)
         out.append(bits)
     k_bits, v_bits = out
+    ch = _k_chunk(D)
+    k_bits = k_bits.reshape(blocks.shape[0], G, BS, D // ch, ch).transpose(0, 1, 3, 2, 4)
     return np.ascontiguousarray(k_bits), np.ascontiguousarray(v_bits.transpose(0, 1, 3, 2))
 
 
@@ -422,7 +429,7 @@ def make_kv_pool_torch(shape: Shape, num_blocks: int, seed: int, layer: int = 0,
                        chunk_blocks: int = 4096):
     """Whole pool as torch int16 tensors on ``device`` (bit-identical to make_kv_pool).
 
-    K is [num_blocks, n_kv, BS, d], V is [num_blocks, n_kv, d, BS].
+    K is [num_blocks, n_kv, d/32, BS, 32], V is [num_blocks, n_kv, d, BS].
     """
     import torch
 
@@ -430,7 +437,8 @@ def make_kv_pool_torch(shape: Shape, num_blocks: int, seed: int, layer: int = 0,
     per_block = G * BS * D
     if num_blocks * per_block > 2**32:
         raise ValueError("KV pool too large for the 32-bit element counter")
-    K = torch.empty((num_blocks, G, BS, D), dtype=torch.int16, device=device)
+    ch = _k_chunk(D)
+    K = torch.empty((num_blocks, G, D // ch, BS, ch), dtype=torch.int16, device=device)
     V = torch.empty((num_blocks, G, D, BS), dtype=torch.int16, device=device)
     scale = float(_kv_scale(shape))
     for kind, dst in ((0, K), (1, V)):
@@ -442,7 +450,7 @@ def make_kv_pool_torch(shape: Shape, num_blocks: int, seed: int, layer: int = 0,
                                         torch, lambda s: s.to(torch.float32))
             bits = vals.to(torch.bfloat16).view(torch.int16).view(b1 - b0, G, BS, D)
             if kind == 0:
-                dst[b0:b1].copy_(bits)
+                dst[b0:b1].copy_(bits.view(b1 - b0, G, BS, D // ch, ch).permute(0, 1, 3, 2, 4))
             else:
                 dst[b0:b1].copy_(bits.transpose(2, 3))
             del idx, vals, bits

@@ -83,11 +83,11 @@ def _check_layer(ctx, wl, b, kp, vp, ref, dev, y_dev):
     for blk, off in ol.new_token_slots(b, 16):
         new[blk, off] = True
     # every other slot bitwise unchanged
-    assert np.array_equal(kg.transpose(0, 2, 1, 3)[~new], kp.transpose(0, 2, 1, 3)[~new])
+    assert np.array_equal(kg.transpose(0, 3, 1, 2, 4)[~new], kp.transpose(0, 3, 1, 2, 4)[~new])
     assert np.array_equal(vg.transpose(0, 3, 1, 2)[~new], vp.transpose(0, 3, 1, 2)[~new])
     # written slots hold the oracle's K/V within tolerance
     kr, vr = ref["k_pool"], ref["v_pool"]
-    assert rel_inf(f64(kg.transpose(0, 2, 1, 3)[new]), f64(kr.transpose(0, 2, 1, 3)[new])) <= TOL
+    assert rel_inf(f64(kg.transpose(0, 3, 1, 2, 4)[new]), f64(kr.transpose(0, 3, 1, 2, 4)[new])) <= TOL
     assert rel_inf(f64(vg.transpose(0, 3, 1, 2)[new]), f64(vr.transpose(0, 3, 1, 2)[new])) <= TOL
 
 
@@ -257,7 +257,7 @@ def test_full_size_layer_sampled(ctx, name, seed, plan_kind):
 
     # untouched slots, over the whole pool, on the device
     k0, v0 = make_kv_pool_torch(shape, b.num_blocks, seed, device="cuda")
-    changed_k = (pool.k.view(torch.int16) != k0).any(dim=3).any(dim=1)  # [nb, 16]
+    changed_k = (pool.k.view(torch.int16) != k0).any(dim=4).any(dim=2).any(dim=1)  # [nb, 16]
     changed_v = (pool.v.view(torch.int16) != v0).any(dim=2).any(dim=1)
     del k0, v0
     new = torch.zeros((b.num_blocks, 16), dtype=torch.bool)
@@ -278,8 +278,8 @@ def test_full_size_layer_sampled(ctx, name, seed, plan_kind):
     kg = pool.k[idx].view(torch.int16).cpu().numpy().view(np.uint16)
     vg = pool.v[idx].view(torch.int16).cpu().numpy().view(np.uint16)
     sl = ol.new_token_slots(compact, 16)
-    kgot = np.stack([kg[blk, :, off, :] for blk, off in sl])
-    kref = np.stack([ref["k_pool"][blk, :, off, :] for blk, off in sl])
+    kgot = np.stack([kg[blk, :, :, off, :] for blk, off in sl])
+    kref = np.stack([ref["k_pool"][blk, :, :, off, :] for blk, off in sl])
     vgot = np.stack([vg[blk, :, :, off] for blk, off in sl])
     vref = np.stack([ref["v_pool"][blk, :, :, off] for blk, off in sl])
     assert rel_inf(f64(kgot), f64(kref)) <= TOL

@@ -158,7 +158,7 @@ def test_rope_kv_append_slots_bit_exact(ctx, n_q, n_kv, d):
     b = sw.batch_from_lengths(rng.integers(0, 300, 23), [37, 1, 16], [0, 5, 40], seed=3, spare_blocks=6)
     T = b.n_tokens
     qkv = rand_bf16(rng, (T, shape.qkv_rows), 1.3)
-    kp = np.full((b.num_blocks, n_kv, 16, d), CANARY, np.uint16)
+    kp = np.full((b.num_blocks, n_kv, d // 32, 16, 32), CANARY, np.uint16)
     vp = np.full((b.num_blocks, n_kv, d, 16), CANARY, np.uint16)
     _, pos = ol.token_positions(b)
     q = ol.rope(f64(qkv[:, : n_q * d]).reshape(T, n_q, d), pos, shape.rope_base)
@@ -198,7 +198,7 @@ def _attention_case(rng, n_q, n_kv, d, dec_ctx, pre_len, pre_prefix, seed):
     for r, n_keys in enumerate(b.cached_lens() + b.q_lens()):
         for p in range(int(n_keys)):
             used[b.block_table[r, p // 16], p % 16] = True
-    kp.transpose(0, 2, 1, 3)[~used] = CANARY
+    kp.transpose(0, 3, 1, 2, 4)[~used] = CANARY
     vp.transpose(0, 3, 1, 2)[~used] = CANARY
     qkv = rand_bf16(rng, (T, shape.qkv_rows), 1.3)
     return b, shape, qkv, kp, vp

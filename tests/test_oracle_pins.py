@@ -160,20 +160,35 @@ def test_write_kv_touches_exactly_the_new_slots():
     cfg = _cfg()
     b = sw.batch_from_lengths([3, 20, 31], [19], [2], seed=8)
     canary = np.uint16(0x7FC1)  # a NaN pattern that rounding of finite values never yields
-    kp = np.full((b.num_blocks, cfg.n_kv, 16, cfg.head_dim), canary, np.uint16)
+    kp = ol.k_pool_from_tokens(np.full((b.num_blocks, cfg.n_kv, 16, cfg.head_dim), canary, np.uint16))
     vp = np.full((b.num_blocks, cfg.n_kv, cfg.head_dim, 16), canary, np.uint16)
     rng = np.random.default_rng(9)
     k = rng.standard_normal((b.n_tokens, cfg.n_kv, cfg.head_dim))
     v = rng.standard_normal((b.n_tokens, cfg.n_kv, cfg.head_dim))
     k2, v2 = ol.write_kv(kp, vp, b, 16, k, v)
-    changed_k = {(int(i), int(o)) for i, _, o, _ in zip(*np.nonzero(k2 != canary))}
+    changed_k = {(int(i), int(o)) for i, _, _, o, _ in zip(*np.nonzero(k2 != canary))}
     changed_v = {(int(i), int(o)) for i, _, _, o in zip(*np.nonzero(v2 != canary))}
     want = set(ol.new_token_slots(b, 16))
     assert changed_k == want and changed_v == want
     # every written entry of each token holds that token's rounded vector
     for t, (blk, off) in enumerate(ol.new_token_slots(b, 16)):
-        assert np.array_equal(k2[blk, :, off, :], ol.f64_to_bf16(k[t]))
+        assert np.array_equal(ol.k_tokens(k2)[blk, :, off, :], ol.f64_to_bf16(k[t]))
         assert np.array_equal(v2[blk, :, :, off], ol.f64_to_bf16(v[t]))
+
+
+def test_key_pool_layout_is_column_chunks_of_32():
+    # written by hand: dim i of token `off` of KV head g in block blk sits at [blk, g, i // 32, off, i % 32]
+    b = sw.batch_from_lengths([5], [], seed=1, spare_blocks=0)
+    d, n_kv = 64, 2
+    kp = np.zeros((b.num_blocks, n_kv, 2, 16, 32), np.uint16)
+    vp = np.zeros((b.num_blocks, n_kv, d, 16), np.uint16)
+    k = np.arange(n_kv * d, dtype=np.float64).reshape(1, n_kv, d)
+    k2, _ = ol.write_kv(kp, vp, b, 16, k, np.zeros_like(k))
+    blk, off = ol.new_token_slots(b, 16)[0]
+    assert off == 5
+    for g in range(n_kv):
+        for i in (0, 31, 32, 35, 63):
+            assert ol.bf16_to_f64(k2[blk, g, i // 32, off, i % 32]) == g * d + i
 
 
 def test_slot_rejects_bad_tables():
@@ -192,7 +207,7 @@ def test_slot_rejects_bad_tables():
 
 def _paged_pool_from_sequences(b, seqs_k, seqs_v, n_kv, d):
     """Place each request's contiguous K/V sequence into its blocks, block by block."""
-    kp = np.zeros((b.num_blocks, n_kv, 16, d), np.uint16)
+    kp = np.zeros((b.num_blocks, n_kv, 16, d), np.uint16)  # token-major, converted at the end
     vp = np.zeros((b.num_blocks, n_kv, d, 16), np.uint16)
     for r, (sk, sv) in enumerate(zip(seqs_k, seqs_v)):
         n = sk.shape[0]
@@ -204,7 +219,7 @@ def _paged_pool_from_sequences(b, seqs_k, seqs_v, n_kv, d):
             blk = b.block_table[r, lb]
             kp[blk] = ol.f64_to_bf16(sk[lb * 16 : (lb + 1) * 16].transpose(1, 0, 2))
             vp[blk] = ol.f64_to_bf16(sv[lb * 16 : (lb + 1) * 16].transpose(1, 2, 0))
-    return kp, vp
+    return ol.k_pool_from_tokens(kp), vp
 
 
 @pytest.mark.parametrize("n_q,n_kv", [(4, 2), (4, 1), (2, 2), (3, 3)])
@@ -317,7 +332,7 @@ def test_layer_decode_equals_last_prefill_row():
     w = sw.make_weights(shape, 3, gain_jitter=0.1)
     x = sw.make_x(shape, L, 3)
     one = sw.batch_from_lengths([], [L], seed=3, spare_blocks=0)
-    kp = np.zeros((one.num_blocks, shape.n_kv, 16, shape.head_dim), np.uint16)
+    kp = np.zeros((one.num_blocks, shape.n_kv, shape.head_dim // 32, 16, 32), np.uint16)
     vp = np.zeros((one.num_blocks, shape.n_kv, shape.head_dim, 16), np.uint16)
     full = ol.layer_forward(shape, w, x, one, kp, vp, storage="exact")
     first = sw.Batch(np.zeros(0, np.int32), np.array([L - 1], np.int32), np.zeros(1, np.int32),
