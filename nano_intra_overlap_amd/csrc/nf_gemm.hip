@@ -239,6 +239,28 @@ __device__ __forceinline__ void interleave_reads() {
   if constexpr (NR > P) __builtin_amdgcn_sched_group_barrier(0x100, NR - P, 0);
 }
 
+// As interleave_reads, with NL global (direct-to-LDS) loads first: MFMA, load, ..., then
+// MFMA, LDS read, ..., then whatever is left (MFMAs, or reads when the tile has fewer MFMAs
+// than memory instructions).
+template <int NL, int NR, int NM>
+__device__ __forceinline__ void interleave_loads_reads() {
+  constexpr int PL = NL < NM ? NL : NM;            // MFMA + load pairs
+  constexpr int PR = NR < NM - PL ? NR : NM - PL;  // MFMA + read pairs
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+  }
+#pragma unroll
+  for (int i = 0; i < PR; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
+  if constexpr (NM > PL + PR) __builtin_amdgcn_sched_group_barrier(0x008, NM - PL - PR, 0);
+  if constexpr (NL > PL) __builtin_amdgcn_sched_group_barrier(0x020, NL - PL, 0);
+  if constexpr (NR > PR) __builtin_amdgcn_sched_group_barrier(0x100, NR - PR, 0);
+}
+
 template <int BM, int BN, int STAGES, int EPI>
 __global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, bf16* C,
                                                         const bf16* R, int M, int N, int K, int tiles_m, int tiles_n,
@@ -377,7 +399,7 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__
     else if (newer == 1) wait_vmcnt<NL>();
     else wait_vmcnt<0>();
   };
-  static_assert(STAGES == 4, "wait_slab covers up to three newer slabs");
+  static_assert(STAGES >= 3 && STAGES <= 4, "wait_slab covers up to three newer slabs");
 
   wait_slab(min(STAGES - 1, nk - 1));
   lds_barrier();
@@ -394,18 +416,23 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__
     __builtin_amdgcn_sched_barrier(0);
     wait_next();
     lds_barrier();  // every wave has read slab kt
-    if (refill) issue(kt + STAGES);
     __builtin_amdgcn_sched_barrier(0);
+    // the refill's loads go between this phase's MFMAs too: a load held back by the memory
+    // pipeline then delays one MFMA issue, not the whole phase
+    if (refill) issue(kt + STAGES);
     read_frags(kt + 1, 0, fa0, fb0);
     mfmas(fa1, fb1);
-    interleave_reads<TM + TN, TM * TN>();
+    if (refill)
+      interleave_loads_reads<NL, TM + TN, TM * TN>();
+    else
+      interleave_reads<TM + TN, TM * TN>();
     __builtin_amdgcn_sched_barrier(0);
   };
   // steady state: slabs kt+1 .. kt+STAGES-1 in flight, slab kt+1 is awaited with the two
   // newest still outstanding; the body is straight-line so the compiler's LDS wait counts
   // stay exact
   int kt = 0;
-  for (; kt + STAGES < nk; ++kt) trip(kt, [] { wait_vmcnt<NL * 2>(); }, true);
+  for (; kt + STAGES < nk; ++kt) trip(kt, [] { wait_vmcnt<NL * (STAGES - 2)>(); }, true);
   // drain: no refills; at most min(2, nk - 2 - kt) newer slabs remain
   for (; kt + 1 < nk; ++kt) trip(kt, [&] { wait_slab(min(STAGES - 2, nk - 2 - kt)); }, false);
   read_frags(nk - 1, 1, fa1, fb1);
@@ -681,6 +708,7 @@ hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int
     case 9: return launch_pipe<128, 128, 4>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
     case 10: return launch_pipe<128, 128, 4>(A, B, C, R, m, n, k, epilogue, 2, ws, s);
     case 11: return launch_pipe<128, 128, 4>(A, B, C, R, m, n, k, epilogue, 4, ws, s);
+
   }
   return hipErrorInvalidValue;
 }

@@ -31,6 +31,7 @@ constexpr int kNumXcd = 8;       // XCDs of an MI355X
 
 struct GemmVariant {
   int bm, bn, bk, ks;  // tile, k step, K slices (split-K; 1 = none)
+  int stages = 4;      // LDS slabs of the pipelined kernels
 };
 int gemm_variant_count();
 GemmVariant gemm_variant(int i);
