@@ -305,7 +305,7 @@ nf_status build_plan_graph(const BatchLayout& L, const nf_plan* plan, PlanGraph&
 // blocks that still yields at least kMinUnits (request chunk, KV head) work units, so that
 // the waves fill the GPU several times over; long chunks have fewer start-ups and combines.
 static int32_t auto_split(const BatchLayout& L, int32_t r0, int32_t r1, int32_t n_kv) {
-  constexpr int64_t kMinUnits = 8192;
+  constexpr int64_t kMinUnits = 4096;
   int32_t sp = 128;
   for (; sp > 16; sp /= 2) {
     int64_t units = 0;
