@@ -5,7 +5,9 @@ A step is one nf_layer_forward call over the dense batch (host batch layout and 
 derivation, metadata upload, then every nano-operation: RMSNorm, KQV GEMM, rotary + KV
 append, decode and prefill attention, O GEMM + residual, RMSNorm, Up/Gate GEMM + SwiGLU,
 Down GEMM + residual), with weights, activations, KV pool and block table resident in HBM
-before the timed region starts.
+before the timed region starts. For a layer-stack workload (the 32-layer 8B stack) a step
+is one nf_stack_forward call: every layer end to end over the batch, each layer with its
+own weights and KV pool.
 
 Prints one JSON line: tokens/s, the dominant kernel's roofline (live HIP-event timing on
 the stream it runs on), the fraction of the bf16 MFMA peak the layer reaches, the
@@ -56,6 +58,10 @@ def parse():
     p.add_argument("--decode-ring", type=int, default=2, choices=[2, 3, 4],
                    help="decode attention register ring depth (ring - 1 groups of KV blocks in flight)")
     p.add_argument("--gemm-variant", type=int, default=-1, help="force one GEMM tile variant for every GEMM")
+    p.add_argument("--no-pipeline", action="store_true",
+                   help="layer stacks: issue layer by layer instead of cross-layer pipelining")
+    p.add_argument("--cpu-layers", type=int, default=2,
+                   help="layer stacks: layers the CPU oracle runs on its sample (its time is scaled to all layers)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="run one plain device copy of this many MiB first (a known-size reference for "
                         "hardware traffic counters)")
@@ -113,10 +119,12 @@ def algorithmic(shape, b, n_nano):
     }
 
 
-def cpu_baseline(shape, b, w, x, seed, n_dec, fetch_blocks):
+def cpu_baseline(shape, b, ws, x, seed, n_dec, fetch_blocks, n_layers_total=1):
     """The oracle as it stands, timed on a sample of the workload: n_dec decode requests
     (all of them when n_dec < 0) plus every prefill chunk, over a compact copy of the KV
-    blocks they use (fetch_blocks(ids) -> (k, v) bf16 bit arrays of those pool blocks)."""
+    blocks they use (fetch_blocks(layer, ids) -> (k, v) bf16 bit arrays of those pool
+    blocks), through the layers of ``ws`` (host weight dicts); the time is scaled to
+    n_layers_total layers."""
     from oracle import layer as ol
     from synth import workloads as sw
 
@@ -142,20 +150,23 @@ def cpu_baseline(shape, b, w, x, seed, n_dec, fetch_blocks):
     bt = np.full_like(sub.block_table, -1)
     bt[mask] = np.searchsorted(used, sub.block_table[mask])
     compact = sw.Batch(sub.decode_ctx, sub.prefill_len, sub.prefill_prefix, bt, len(used))
-    kp, vp = fetch_blocks(used)
+    pools = [fetch_blocks(l, used) for l in range(len(ws))]
     xs = x[rows]
     t0 = time.perf_counter()
-    ol.layer_forward(shape, w, xs, compact, kp, vp)
+    ol.stack_forward(shape, ws, xs, compact, [p[0] for p in pools], [p[1] for p in pools])
     dt = time.perf_counter() - t0
+    dt_all = dt * n_layers_total / len(ws)
     what = ("the whole dense batch" if n_dec == b.n_decode else
             f"{n_dec} of {b.n_decode} decode requests (sampled, seed {seed + 7}) + all prefill chunks")
+    layers = (f"one float64 layer pass in {dt:.2f} s" if n_layers_total == 1 else
+              f"{len(ws)} of {n_layers_total} float64 layer passes in {dt:.2f} s, scaled to all layers")
     return {
-        "value": round(len(rows) / dt, 2),
+        "value": round(len(rows) / dt_all, 2),
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"{what}: {len(rows)} tokens ({b.n_prefill} prefill chunk(s), {int(b.prefill_len.sum())} "
-                  f"tokens), {len(used)} KV blocks; one float64 layer pass in {dt:.2f} s "
+                  f"tokens), {len(used)} KV blocks; {layers} "
                   f"({os.cpu_count()} host CPUs, {threads} BLAS threads)",
     }
 
@@ -181,18 +192,37 @@ def main():
     T = b.n_tokens
     log(f"workload {wl.name}: T={T}, decode={b.n_decode}, prefill={b.prefill_len.tolist()}, blocks={b.num_blocks}")
     t0 = time.time()
-    w = sw.make_weights(shape, args.seed)
+    n_layers = shape.n_layers
+    stack = n_layers > 1
     x = sw.make_x(shape, T, args.seed)
-    wd = DeviceWeights(w, "cuda")
     xd = bf16_tensor(x, "cuda")
     yd = torch.empty_like(xd)
-    k16, v16 = make_kv_pool_torch(shape, b.num_blocks, args.seed, device="cuda")
-    pool = DevicePool.from_int16(k16, v16)
+    if stack:
+        # every layer's weights (counter-based generator, drawn on the device) and KV pool
+        w = None
+        wds = [DeviceWeights.from_int16(sw.make_weights_counter_torch(shape, args.seed, l, device="cuda"))
+               for l in range(n_layers)]
+        k16s, v16s = [], []
+        for l in range(n_layers):
+            k16, v16 = make_kv_pool_torch(shape, b.num_blocks, args.seed, layer=l, device="cuda")
+            k16s.append(k16)
+            v16s.append(v16)
+        pools = [DevicePool.from_int16(k, v) for k, v in zip(k16s, v16s)]
+    else:
+        w = sw.make_weights(shape, args.seed)
+        wds = [DeviceWeights(w, "cuda")]
+        k16, v16 = make_kv_pool_torch(shape, b.num_blocks, args.seed, device="cuda")
+        k16s, v16s = [k16], [v16]
+        pools = [DevicePool.from_int16(k16, v16)]
+    w_descs = [wd.desc for wd in wds]
+    p_descs = [p.desc for p in pools]
     bt_dev = torch.from_numpy(np.ascontiguousarray(b.block_table)).cuda()
     hb = abi.HostBatch.from_batch(b, block_table_dev_ptr=bt_dev.data_ptr())
     cfg = abi.make_cfg(shape)
     torch.cuda.synchronize()
-    log(f"inputs resident in {time.time() - t0:.1f} s")
+    free, total = torch.cuda.mem_get_info()
+    log(f"inputs resident in {time.time() - t0:.1f} s ({n_layers} layer(s); device memory used "
+        f"{(total - free) / 1e9:.1f} of {total / 1e9:.1f} GB)")
 
     if args.copy_probe_mib:
         nbytes = args.copy_probe_mib << 20
@@ -234,16 +264,25 @@ def main():
             f"{args.mem_cus}/32 CUs per XCD" if args.mem_cus else "unmasked")
         return plans.overlap(hb, bounds, *masks), desc
 
-    def run(plan, steps, warmup, timing_mask=0):
+    stack_flags = 0 if args.no_pipeline else abi.NF_STACK_PIPELINE
+
+    def step(plan, flags):
+        if stack:
+            abi.nf_stack_forward(ctx, cfg, w_descs, xd.data_ptr(), yd.data_ptr(), hb, p_descs, plan, flags, stream)
+        else:
+            abi.nf_layer_forward(ctx, cfg, w_descs[0], xd.data_ptr(), yd.data_ptr(), hb, p_descs[0], plan, stream)
+
+    def run(plan, steps, warmup, timing_mask=0, flags=None):
+        flags = stack_flags if flags is None else flags
         for _ in range(warmup):
-            abi.nf_layer_forward(ctx, cfg, wd.desc, xd.data_ptr(), yd.data_ptr(), hb, pool.desc, plan, stream)
+            step(plan, flags)
         torch.cuda.synchronize()
         abi.nf_ctx_set_timing(ctx, timing_mask)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(steps):
-            abi.nf_layer_forward(ctx, cfg, wd.desc, xd.data_ptr(), yd.data_ptr(), hb, pool.desc, plan, stream)
+            step(plan, flags)
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / steps
@@ -264,7 +303,7 @@ def main():
     dk = kern["decode_attn"]
     launches_per_step = dk["launches"] / args.steps
     dec_avg_ms = dk["total_ms"] / dk["launches"]
-    bytes_per_launch = alg["decode_bytes"] / launches_per_step
+    bytes_per_launch = alg["decode_bytes"] * n_layers / launches_per_step
     achieved = bytes_per_launch / (dec_avg_ms * 1e-3)
     log(f"plan: {plan_desc}: {ms:.3f} ms/step; decode attention {dec_avg_ms:.3f} ms/launch "
         f"x {launches_per_step:g} -> {achieved / 1e9:.0f} GB/s")
@@ -281,6 +320,7 @@ def main():
         "gemm_down": 2 * T * shape.ffn * shape.hidden,
     }
     for k, f in flops_by.items():
+        f *= n_layers
         if k in breakdown and breakdown[k]["launches"]:
             per_step_ms = breakdown[k]["total_ms"] / 5
             breakdown[k]["tflops"] = round(f / (per_step_ms * 1e-3) / 1e12, 1)
@@ -291,30 +331,42 @@ def main():
     schedules = {"timed": round(ms, 4)}
     seq_ms = None
     if not args.no_baseline:
-        seq_ms, _ = run(None, args.steps, args.warmup)
+        seq_ms, _ = run(None, args.steps, args.warmup, flags=0)
         schedules["sequential"] = round(seq_ms, 4)
         for n in (2, 4):
             bnd = plans.even_bounds(T, n)
-            schedules[f"nanobatch_only_{n}"] = round(run(plans.sequential(hb, bnd), args.steps, args.warmup)[0], 4)
-            schedules[f"overlap_{n}"] = round(run(plans.overlap(hb, bnd), args.steps, args.warmup)[0], 4)
+            schedules[f"nanobatch_only_{n}"] = round(run(plans.sequential(hb, bnd), args.steps, args.warmup,
+                                                         flags=0)[0], 4)
+            schedules[f"overlap_{n}"] = round(run(plans.overlap(hb, bnd), args.steps, args.warmup, flags=0)[0], 4)
+        if stack:
+            # cross-layer pipelining of the same plans
+            for n in (2, 4):
+                ov = plans.overlap(hb, plans.even_bounds(T, n))
+                schedules[f"overlap_{n}_pipelined"] = round(run(ov, args.steps, args.warmup,
+                                                                flags=abi.NF_STACK_PIPELINE)[0], 4)
         log("schedules (ms/step): " + ", ".join(f"{k} {v:.3f}" for k, v in schedules.items()))
 
     traffic = counted_traffic(wl.name, args.seed, launches_per_step)
     tokens_per_s = T / (ms * 1e-3)
-    layer_flops = alg["gemm_flops"] + alg["attn_flops"]
-    mfma_frac = alg["gemm_flops"] / (ms * 1e-3) / PEAK_BF16
-    t_lb = max(alg["gemm_flops"] / PEAK_BF16, alg["layer_bytes"] / PEAK_HBM)
+    step_gemm_flops = alg["gemm_flops"] * n_layers
+    mfma_frac = step_gemm_flops / (ms * 1e-3) / PEAK_BF16
+    t_lb = n_layers * max(alg["gemm_flops"] / PEAK_BF16, alg["layer_bytes"] / PEAK_HBM)
 
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
-        def fetch_blocks(ids):
+        def fetch_blocks(layer, ids):
             idx = torch.from_numpy(np.asarray(ids, dtype=np.int64)).cuda()
-            kp = k16.index_select(0, idx).cpu().numpy().view(np.uint16)
-            vp = v16.index_select(0, idx).cpu().numpy().view(np.uint16)
+            kp = k16s[layer].index_select(0, idx).cpu().numpy().view(np.uint16)
+            vp = v16s[layer].index_select(0, idx).cpu().numpy().view(np.uint16)
             return kp, vp
 
-        cpu = cpu_baseline(shape, b, w, x, args.seed, args.cpu_decode_sample, fetch_blocks)
+        if stack:
+            n_cpu = max(1, min(args.cpu_layers, n_layers))
+            ws_host = [wds[l].host_bits() for l in range(n_cpu)]
+        else:
+            ws_host = [w]
+        cpu = cpu_baseline(shape, b, ws_host, x, args.seed, args.cpu_decode_sample, fetch_blocks, n_layers)
         log(f"cpu oracle: {cpu['value']} tokens/s on {cpu['cores']} threads")
 
     out = {
@@ -332,6 +384,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": wl.name,
+            "n_layers": n_layers,
+            "stack_pipelined": (not args.no_pipeline) if stack else None,
             "dense_batch": T,
             "n_decode": b.n_decode,
             "prefill_len": b.prefill_len.tolist(),
@@ -344,7 +398,7 @@ def main():
             "gemm_variant": args.gemm_variant,
         },
         "mfma_frac_of_bf16_peak": round(mfma_frac, 4),
-        "layer_gemm_tflops": round(alg["gemm_flops"] / (ms * 1e-3) / 1e12, 1),
+        "layer_gemm_tflops": round(step_gemm_flops / (ms * 1e-3) / 1e12, 1),
         "layer_roofline_frac": round(t_lb / (ms * 1e-3), 4),
         "sequential_ms_per_step": None if seq_ms is None else round(seq_ms, 4),
         "speedup_vs_sequential": None if seq_ms is None else round(seq_ms / ms, 4),

@@ -179,6 +179,24 @@ nf_status nf_plan_dependencies(const nf_batch_desc *batch, const nf_plan *plan, 
                                int32_t cap, int32_t *n_edges, int32_t *order_out, char *err_msg,
                                size_t err_cap);
 
+/* Flags of the layer-stack entry points. */
+enum {
+  NF_STACK_PIPELINE = 1, /* cross-layer nano-batch pipelining (see nf_stack_forward)          */
+  NF_STACK_GRAPH = 2     /* replay a captured HIP graph of the stack (switched off: see below) */
+};
+
+/* Dependency edges and issue order of n_layers layers over one batch, each with `plan`
+ * (see nf_stack_forward). Stack op l * n_ops + i is the plan's op i (plan order; the NULL
+ * plan lists KQV, decode attention, prefill attention, O, UGD) in layer l. Edges (i, j):
+ * op j depends on op i. listing_out (host [n_layers * n_ops] or NULL) receives the order in
+ * which each stream takes its ops (every stream runs its ops in this order); order_out
+ * (same size or NULL) a global issue order consistent with both. Errors as
+ * nf_plan_dependencies; NF_E_ARG for n_layers < 1 or unknown flags.                         */
+nf_status nf_stack_dependencies(const nf_batch_desc *batch, const nf_plan *plan, int32_t n_layers,
+                                int32_t flags, int32_t *edges, int32_t cap, int32_t *n_edges,
+                                int32_t *listing_out, int32_t *order_out, char *err_msg,
+                                size_t err_cap);
+
 /* ---- the layer --------------------------------------------------------------------------- */
 
 /* One decoder-layer iteration. x_in, y_out: device [T][hidden] (may alias: every row is
@@ -190,6 +208,33 @@ nf_status nf_plan_dependencies(const nf_batch_desc *batch, const nf_plan *plan, 
 nf_status nf_layer_forward(nf_ctx *ctx, const nf_layer_cfg *cfg, const nf_layer_weights *w,
                            const void *x_in, void *y_out, const nf_batch_desc *batch,
                            nf_kv_pool *pool, const nf_plan *plan, void *stream);
+
+/* n_layers decoder-layer iterations over one dense batch, end to end: the layers of one
+ * model iteration (summary page, "The NanoFlow Runtime System"; slides "8B Pipeline
+ * Design": the next layer's KQV of a nano-batch follows this layer's Down of the same
+ * nano-batch). Layer l applies weights[l] to the output of layer l - 1 (layer 0 to x_in)
+ * and appends to pools[l]; y_out receives the last layer's output. weights, pools: host
+ * arrays [n_layers] of device tensors, laid out as for nf_layer_forward; every pool has
+ * the same num_blocks and is addressed through the one block table of `batch` (one paged
+ * KV cache per layer, one block allocation per request); pools must not overlap (distinct
+ * k and v buffers per layer). x_in and y_out may alias; layers after the first run in
+ * place on y_out. The batch is laid out and its metadata uploaded once for all layers.
+ * plan: as for nf_layer_forward, applied to every layer.
+ * flags: NF_STACK_PIPELINE — layer l + 1's KQV of a nano-batch is issued as soon as layer
+ *   l's UGD ops it depends on (intersecting rows) are, instead of after all of layer l, so
+ *   on a multi-stream plan the next layer's decode attention of nano-batch j can overlap
+ *   this layer's dense ops of nano-batch j + 1 (results are identical).
+ *   NF_STACK_GRAPH — capture the enqueued work once into a HIP graph owned by the context
+ *   and replay it while the batch (contents included), plan, flags, weights, pools and
+ *   x_in / y_out pointers are unchanged. Switched off in this build: a call with this flag
+ *   returns NF_E_UNSUPPORTED before enqueueing anything.
+ * Work is enqueued after all prior work on `stream` and `stream` waits for all of it.
+ * Errors: as nf_layer_forward; NF_E_ARG for n_layers < 1, null arrays, unknown flags,
+ * unequal num_blocks or overlapping pools; NF_E_UNSUPPORTED as above.                      */
+nf_status nf_stack_forward(nf_ctx *ctx, const nf_layer_cfg *cfg, int32_t n_layers,
+                           const nf_layer_weights *weights, const void *x_in, void *y_out,
+                           const nf_batch_desc *batch, nf_kv_pool *pools, const nf_plan *plan,
+                           int32_t flags, void *stream);
 
 /* Intermediate buffers of the last nf_layer_forward call, for inspection (device pointers
  * into the context's workspace, valid until the next call): which = 0 h, 1 qkv (q rotated),

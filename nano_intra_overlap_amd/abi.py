@@ -30,6 +30,7 @@ STATUS_NAMES = {v: k for k, v in dict(globals()).items() if k.startswith("NF_E_"
 
 NF_CU_MASK_WORDS = 8
 NF_OP_KQV, NF_OP_DECATTN, NF_OP_PFATTN, NF_OP_O, NF_OP_UGD, NF_OP_KINDS = range(6)
+NF_STACK_PIPELINE, NF_STACK_GRAPH = 1, 2
 OP_NAMES = ["KQV", "DECATTN", "PFATTN", "O", "UGD"]
 (NF_K_DECODE_ATTN, NF_K_DECODE_COMBINE, NF_K_PREFILL_ATTN, NF_K_GEMM_KQV, NF_K_GEMM_O, NF_K_GEMM_UG, NF_K_GEMM_DOWN,
  NF_K_RMSNORM, NF_K_ROPE_KV, NF_K_CLASSES) = range(10)
@@ -97,6 +98,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "nf_layer_forward": (I, [V, ctypes.POINTER(nf_layer_cfg), ctypes.POINTER(nf_layer_weights), V, V,
                                  ctypes.POINTER(nf_batch_desc), ctypes.POINTER(nf_kv_pool), ctypes.POINTER(nf_plan),
                                  V]),
+        "nf_stack_dependencies": (I, [ctypes.POINTER(nf_batch_desc), ctypes.POINTER(nf_plan), I, I, _i32p, I, _i32p,
+                                      _i32p, _i32p, ctypes.c_char_p, S]),
+        "nf_stack_forward": (I, [V, ctypes.POINTER(nf_layer_cfg), I, ctypes.POINTER(nf_layer_weights), V, V,
+                                 ctypes.POINTER(nf_batch_desc), ctypes.POINTER(nf_kv_pool), ctypes.POINTER(nf_plan),
+                                 I, V]),
         "nf_debug_buffer": (I, [V, I, ctypes.POINTER(V), ctypes.POINTER(S)]),
         "nf_op_gemm": (I, [V, V, V, V, V, I, I, I, I, I, V]),
         "nf_gemm_variants": (I, [_i32p, I, _i32p]),
@@ -118,6 +124,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "nf_ctx_set_gemm_variant": (I, [V, I, I, I]),
         "nf_ctx_set_decode_launch": (I, [V, I, I, I]),
         "nf_copy_reference": (I, [V, V, S, V]),
+        "nf_ctx_graph_stats": (I, [V, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
     }
     missing = []
     for name, (res, args) in sig.items():
@@ -286,6 +293,43 @@ def nf_layer_forward(ctx, cfg: nf_layer_cfg, weights: nf_layer_weights, x_ptr: i
     _check(st, ctx)
 
 
+def nf_stack_dependencies(batch: HostBatch, plan: HostPlan | None, n_layers: int, flags: int = 0):
+    """(edges [(i, j): stack op j depends on stack op i], listing, global issue order) of
+    n_layers layers with one plan; stack op l * n_ops + i is the plan's op i in layer l."""
+    n_ops = (len(plan.ops) if plan is not None else NF_OP_KINDS) * n_layers
+    cap = n_ops * 8 + 64
+    edges = np.zeros(2 * cap, np.int32)
+    n = ctypes.c_int32()
+    listing = np.zeros(n_ops, np.int32)
+    order = np.zeros(n_ops, np.int32)
+    err = ctypes.create_string_buffer(512)
+    lib = load()
+    st = lib.nf_stack_dependencies(ctypes.byref(batch.desc), ctypes.byref(plan.desc) if plan else None, n_layers,
+                                   flags, _ptr(edges), cap, ctypes.byref(n), _ptr(listing), _ptr(order), err, 512)
+    if st == NF_E_CAPACITY:
+        cap = n.value
+        edges = np.zeros(2 * cap, np.int32)
+        st = lib.nf_stack_dependencies(ctypes.byref(batch.desc), ctypes.byref(plan.desc) if plan else None, n_layers,
+                                       flags, _ptr(edges), cap, ctypes.byref(n), _ptr(listing), _ptr(order), err, 512)
+    _check(st, msg=err.value.decode())
+    e = edges[: 2 * n.value].reshape(-1, 2)
+    return [tuple(map(int, p)) for p in e], listing.tolist(), order.tolist()
+
+
+def nf_stack_forward(ctx, cfg: nf_layer_cfg, weights, x_ptr: int, y_ptr: int, batch: HostBatch, pools,
+                     plan: HostPlan | None, flags: int, stream: int) -> None:
+    """n_layers = len(weights) layers end to end; weights: nf_layer_weights per layer,
+    pools: nf_kv_pool per layer."""
+    n = len(weights)
+    if len(pools) != n:
+        raise ValueError("one pool per layer")
+    w_arr = (nf_layer_weights * n)(*weights)
+    p_arr = (nf_kv_pool * n)(*pools)
+    st = load().nf_stack_forward(ctx, ctypes.byref(cfg), n, w_arr, x_ptr, y_ptr, ctypes.byref(batch.desc), p_arr,
+                                 ctypes.byref(plan.desc) if plan is not None else None, flags, stream)
+    _check(st, ctx)
+
+
 def nf_debug_buffer(ctx, which: int):
     p = ctypes.c_void_p()
     n = ctypes.c_size_t()
@@ -375,6 +419,13 @@ def nf_ctx_set_decode_launch(ctx, max_workgroups: int, nbuf: int = 1, ring: int 
     """Decode attention launch: workgroup cap (0 = one wave per unit), KV blocks per softmax
     step, and ring depth (register buffers of nbuf blocks; ring - 1 groups in flight)."""
     _check(load().nf_ctx_set_decode_launch(ctx, max_workgroups, nbuf, ring), ctx)
+
+
+def nf_ctx_graph_stats(ctx):
+    """(captures, launches) of the context's layer-stack graph so far."""
+    c, n = ctypes.c_int64(), ctypes.c_int64()
+    _check(load().nf_ctx_graph_stats(ctx, ctypes.byref(c), ctypes.byref(n)), ctx)
+    return c.value, n.value
 
 
 def nf_ctx_set_gemm_variant(ctx, kind: int, which: int, variant: int) -> None:

@@ -33,7 +33,8 @@ def search_plan(workload: str, seed: int = 0, max_nano: int = 4, granularity: in
 
     from . import abi
 
-    d, r, _ = table_paths(workload)
+    # a layer stack uses the tables profiled for its layer shape
+    d, r, _ = table_paths(sw.WORKLOADS[workload].extra.get("layer_workload", workload))
     b = sw.make_batch(workload, seed)
     return abi.nf_plan_search(dbest or d, rp or r, abi.HostBatch.from_batch(b), max_nano=max_nano,
                               granularity=granularity)

@@ -301,6 +301,100 @@ nf_status build_plan_graph(const BatchLayout& L, const nf_plan* plan, PlanGraph&
   return NF_OK;
 }
 
+nf_status build_stack_graph(const PlanGraph& g, int32_t n_layers, bool pipelined, StackGraph& s, std::string& err) {
+  s = StackGraph();
+  if (n_layers < 1) {
+    err = "n_layers must be >= 1";
+    return NF_E_ARG;
+  }
+  const int32_t n = (int32_t)g.ops.size();
+  const int32_t N = n_layers * n;
+  s.n_layers = n_layers;
+  s.n_ops = n;
+  s.deps.assign(N, {});
+  for (int32_t l = 0; l < n_layers; ++l)
+    for (int32_t j = 0; j < n; ++j) {
+      auto& d = s.deps[l * n + j];
+      for (int32_t i : g.deps[j]) d.push_back(l * n + i);
+      if (l > 0 && g.ops[j].kind == NF_OP_KQV)
+        for (int32_t i = 0; i < n; ++i)
+          if (g.ops[i].kind == NF_OP_UGD && intersects(g.ops[i], g.ops[j])) d.push_back((l - 1) * n + i);
+    }
+  // listing: layer 0 as listed; every later layer as listed, its KQV ops moved up when
+  // pipelined (each right after its last producer in the listing, after any KQV moved
+  // there before it)
+  s.listing.clear();
+  s.listing.reserve(N);
+  for (int32_t l = 0; l < n_layers; ++l) {
+    for (int32_t j = 0; j < n; ++j)
+      if (!(pipelined && l > 0 && g.ops[j].kind == NF_OP_KQV)) s.listing.push_back(l * n + j);
+    if (!pipelined || l + 1 >= n_layers) continue;
+    // place layer l+1's KQV ops (listed order) inside what is listed so far
+    std::vector<int32_t> pos(N, -1);
+    for (int32_t k = 0; k < (int32_t)s.listing.size(); ++k) pos[s.listing[k]] = k;
+    std::vector<std::pair<int32_t, int32_t>> ins;  // (insert after listing index, op)
+    for (int32_t j = 0; j < n; ++j) {
+      if (g.ops[j].kind != NF_OP_KQV) continue;
+      const int32_t op = (l + 1) * n + j;
+      int32_t after = -1;
+      for (int32_t d : s.deps[op]) after = std::max(after, pos[d]);
+      if (after < 0) after = (int32_t)s.listing.size() - 1;  // no producer: end of layer l
+      ins.push_back({after, op});
+    }
+    std::stable_sort(ins.begin(), ins.end(),
+                     [](const std::pair<int32_t, int32_t>& a, const std::pair<int32_t, int32_t>& b) {
+                       return a.first < b.first;
+                     });
+    std::vector<int32_t> merged;
+    merged.reserve(s.listing.size() + ins.size());
+    size_t q = 0;
+    for (size_t k = 0; k < s.listing.size(); ++k) {
+      merged.push_back(s.listing[k]);
+      while (q < ins.size() && ins[q].first == (int32_t)k) merged.push_back(ins[q++].second);
+    }
+    s.listing.swap(merged);
+  }
+  // global order: Kahn's algorithm over dependencies plus per-stream listing order,
+  // preferring the earliest listing position
+  std::vector<std::vector<int32_t>> succ(N);
+  std::vector<int32_t> indeg(N, 0);
+  for (int32_t j = 0; j < N; ++j)
+    for (int32_t i : s.deps[j]) {
+      succ[i].push_back(j);
+      indeg[j]++;
+    }
+  std::vector<int32_t> last(g.n_streams, -1);
+  for (int32_t op : s.listing) {
+    const int32_t st = g.ops[op % n].stream;
+    if (last[st] >= 0) {
+      succ[last[st]].push_back(op);
+      indeg[op]++;
+    }
+    last[st] = op;
+  }
+  std::vector<char> done(N, 0);
+  s.order.clear();
+  s.order.reserve(N);
+  for (int32_t step = 0; step < N; ++step) {
+    int32_t pick = -1;
+    for (int32_t k = 0; k < N; ++k) {
+      const int32_t op = s.listing[k];
+      if (!done[op] && indeg[op] == 0) {
+        pick = op;
+        break;
+      }
+    }
+    if (pick < 0) {
+      err = "stack order deadlocks: a stream's order contradicts a dependency";
+      return NF_E_PLAN;
+    }
+    done[pick] = 1;
+    s.order.push_back(pick);
+    for (int32_t j : succ[pick]) indeg[j]--;
+  }
+  return NF_OK;
+}
+
 // Chunk size (blocks) for the decode requests [r0, r1): the longest of 128, 64, 32, 16
 // blocks that still yields at least kMinUnits (request chunk, KV head) work units, so that
 // the waves fill the GPU several times over; long chunks have fewer start-ups and combines.
@@ -414,22 +508,15 @@ extern "C" nf_status nf_batch_slots(const nf_layer_cfg* cfg, const nf_batch_desc
   return NF_OK;
 }
 
-extern "C" nf_status nf_plan_dependencies(const nf_batch_desc* batch, const nf_plan* plan, int32_t* edges, int32_t cap,
-                                          int32_t* n_edges, int32_t* order_out, char* err_msg, size_t err_cap) {
-  std::string err;
-  if (!batch || !n_edges) {
-    put_err(err_msg, err_cap, "null argument");
-    return NF_E_ARG;
-  }
-  // layout without a pool: token ranges only (blocks are not needed for the DAG)
-  nf::BatchLayout L;
+// Token ranges of a batch without a pool (blocks are not needed for the DAG).
+static nf_status token_layout(const nf_batch_desc* batch, nf::BatchLayout& L, std::string& err) {
   int64_t t = 0;
   for (int32_t r = 0; r < batch->n_decode + batch->n_prefill; ++r) {
     nf::ReqInfo ri;
     ri.decode = r < batch->n_decode;
     const int32_t q = ri.decode ? 1 : batch->prefill_len[r - batch->n_decode];
     if (q < 1) {
-      put_err(err_msg, err_cap, "prefill length < 1");
+      err = "prefill length < 1";
       return NF_E_ARG;
     }
     ri.t0 = (int32_t)t;
@@ -440,15 +527,14 @@ extern "C" nf_status nf_plan_dependencies(const nf_batch_desc* batch, const nf_p
     t += q;
   }
   L.T = (int32_t)t;
-  nf::PlanGraph g;
-  nf_status st = nf::build_plan_graph(L, plan, g, err);
-  if (st != NF_OK) {
-    put_err(err_msg, err_cap, err);
-    return st;
-  }
+  return NF_OK;
+}
+
+static nf_status put_edges(const std::vector<std::vector<int32_t>>& deps, int32_t* edges, int32_t cap,
+                           int32_t* n_edges, char* err_msg, size_t err_cap) {
   int32_t n = 0;
-  for (int32_t j = 0; j < (int32_t)g.deps.size(); ++j)
-    for (int32_t i : g.deps[j]) {
+  for (int32_t j = 0; j < (int32_t)deps.size(); ++j)
+    for (int32_t i : deps[j]) {
       if (n < cap && edges) {
         edges[2 * n] = i;
         edges[2 * n + 1] = j;
@@ -456,11 +542,57 @@ extern "C" nf_status nf_plan_dependencies(const nf_batch_desc* batch, const nf_p
       ++n;
     }
   *n_edges = n;
-  if (order_out) memcpy(order_out, g.order.data(), sizeof(int32_t) * g.order.size());
   if (n > cap) {
     put_err(err_msg, err_cap, "edge capacity too small");
     return NF_E_CAPACITY;
   }
-  put_err(err_msg, err_cap, "");
   return NF_OK;
+}
+
+extern "C" nf_status nf_plan_dependencies(const nf_batch_desc* batch, const nf_plan* plan, int32_t* edges, int32_t cap,
+                                          int32_t* n_edges, int32_t* order_out, char* err_msg, size_t err_cap) {
+  std::string err;
+  if (!batch || !n_edges) {
+    put_err(err_msg, err_cap, "null argument");
+    return NF_E_ARG;
+  }
+  nf::BatchLayout L;
+  nf_status st = token_layout(batch, L, err);
+  if (st == NF_OK) {
+    nf::PlanGraph g;
+    st = nf::build_plan_graph(L, plan, g, err);
+    if (st == NF_OK) {
+      if (order_out) memcpy(order_out, g.order.data(), sizeof(int32_t) * g.order.size());
+      st = put_edges(g.deps, edges, cap, n_edges, err_msg, err_cap);
+      if (st != NF_OK) return st;
+    }
+  }
+  put_err(err_msg, err_cap, err);
+  return st;
+}
+
+extern "C" nf_status nf_stack_dependencies(const nf_batch_desc* batch, const nf_plan* plan, int32_t n_layers,
+                                           int32_t flags, int32_t* edges, int32_t cap, int32_t* n_edges,
+                                           int32_t* listing_out, int32_t* order_out, char* err_msg, size_t err_cap) {
+  std::string err;
+  if (!batch || !n_edges || n_layers < 1 || (flags & ~(NF_STACK_PIPELINE | NF_STACK_GRAPH))) {
+    put_err(err_msg, err_cap, "bad argument");
+    return NF_E_ARG;
+  }
+  nf::BatchLayout L;
+  nf_status st = token_layout(batch, L, err);
+  if (st == NF_OK) {
+    nf::PlanGraph g;
+    st = nf::build_plan_graph(L, plan, g, err);
+    nf::StackGraph sg;
+    if (st == NF_OK) st = nf::build_stack_graph(g, n_layers, (flags & NF_STACK_PIPELINE) != 0, sg, err);
+    if (st == NF_OK) {
+      if (listing_out) memcpy(listing_out, sg.listing.data(), sizeof(int32_t) * sg.listing.size());
+      if (order_out) memcpy(order_out, sg.order.data(), sizeof(int32_t) * sg.order.size());
+      st = put_edges(sg.deps, edges, cap, n_edges, err_msg, err_cap);
+      if (st != NF_OK) return st;
+    }
+  }
+  put_err(err_msg, err_cap, err);
+  return st;
 }

@@ -85,6 +85,23 @@ struct PlanGraph {
 // one stream, kinds in layer order). Checks bounds, the op list and acyclicity.
 nf_status build_plan_graph(const BatchLayout& L, const nf_plan* plan, PlanGraph& g, std::string& err);
 
+// The nano-operations of n_layers consecutive layers over one batch, each layer with the
+// same plan. Stack op l * n_ops + i is op i of the plan in layer l. Besides every layer's own
+// dependencies, the first dense op of layer l + 1 (KQV: it reads the layer input rows)
+// depends on the UGD ops of layer l whose rows intersect its rows. `listing` is the order
+// the ops are taken in, streams included: layer by layer in the plan's listed order, or,
+// when pipelined, with each KQV of layer l + 1 moved up to just after the last layer-l op
+// it depends on, so that a stream can start the next layer's nano-batch j while nano-batch
+// j + 1 of this layer is still running elsewhere (cross-layer nano-batch pipelining). A
+// stream runs its ops in listing order; `order` is a global issue order consistent with
+// both that and the dependencies.
+struct StackGraph {
+  int32_t n_layers = 1, n_ops = 0;        // layers; ops per layer
+  std::vector<std::vector<int32_t>> deps;  // per stack op
+  std::vector<int32_t> listing, order;
+};
+nf_status build_stack_graph(const PlanGraph& g, int32_t n_layers, bool pipelined, StackGraph& s, std::string& err);
+
 // Parent-operation dependency of the layer (does kind b consume a product of kind a?).
 bool parent_depends(int32_t a, int32_t b);
 

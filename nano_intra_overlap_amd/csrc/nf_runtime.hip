@@ -23,6 +23,11 @@ namespace {
 constexpr int kMaxSplit = 4096;    // decode chunk limit (blocks per work item)
 constexpr int kDefaultSplit = 0;  // default decode chunk: 0 = chosen per nano-op from its work
 constexpr int kMaxStreams = 3;  // + the caller's stream: within the 4 HW queues of a process
+// Replay of a captured stack (NF_STACK_GRAPH) is switched off: its first run on the device
+// ended in a host segmentation fault inside the capture / instantiate / launch sequence
+// below, with no cause found in this library's code. Calls asking for it get
+// NF_E_UNSUPPORTED.
+constexpr bool kGraphReplayEnabled = false;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -47,6 +52,16 @@ struct nf_ctx {
   // split-KV partials
   DevBuf part_o, part_ml;
   DevBuf gemm_ws;  // split-K fp32 partials, one region per GEMM of a plan
+  uint64_t ws_gen = 0;  // bumped whenever a device buffer is reallocated
+  // captured layer stack: its own metadata buffer, the key it was captured for
+  hipStream_t cap_stream = nullptr;
+  DevBuf graph_meta;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t graph_exec = nullptr;
+  std::vector<uint64_t> graph_key;
+  std::vector<unsigned char> graph_meta_bytes;
+  hipEvent_t graph_in = nullptr, graph_out = nullptr;
+  int64_t graph_captures = 0, graph_launches = 0;
   // streams keyed by CU mask (all-ones key = unmasked)
   struct StreamEntry {
     std::vector<uint32_t> mask;
@@ -98,6 +113,7 @@ nf_status ensure(nf_ctx* ctx, DevBuf& b, size_t bytes) {
   const size_t cap = align_up(std::max<size_t>(bytes, 256), 1 << 20);
   NF_HIP(ctx, hipMalloc(&b.p, cap));
   b.cap = cap;
+  ++ctx->ws_gen;
   return NF_OK;
 }
 
@@ -187,57 +203,85 @@ nf_status ensure_events(nf_ctx* ctx, size_t n) {
 // metadata
 // ---------------------------------------------------------------------------------------
 
-// Pack and upload the metadata on `stream` (ordered before the work that reads it).
-nf_status upload_meta(nf_ctx* ctx, const nf_layer_cfg& cfg, const nf_batch_desc& b, const BatchLayout& L, Meta& M,
-                      hipStream_t stream) {
+// Byte offsets of the packed metadata (one upload per call).
+struct MetaPack {
+  size_t o_pos = 0, o_slot = 0, o_inv = 0, o_dec = 0, o_comb = 0, o_pf = 0, o_bt = 0, total = 0;
+  bool bt_up = false;
+};
+
+// Pack the metadata into the pinned staging buffer (after the previous upload from it).
+nf_status pack_meta(nf_ctx* ctx, const nf_layer_cfg& cfg, const nf_batch_desc& b, const BatchLayout& L, const Meta& M,
+                    MetaPack& P) {
   const int T = L.T;
   const int half = cfg.head_dim / 2;
   const size_t n_req = L.req.size();
-  const bool bt_up = b.block_table_dev == nullptr;
+  P = MetaPack();
+  P.bt_up = b.block_table_dev == nullptr;
   size_t off = 0;
   auto slot = [&](size_t bytes) {
     const size_t o = off;
     off = align_up(off + bytes, 256);
     return o;
   };
-  const size_t o_pos = slot(sizeof(int32_t) * T);
-  const size_t o_slot = slot(sizeof(int32_t) * T);
-  const size_t o_inv = slot(sizeof(float) * half);
-  const size_t o_dec = slot(sizeof(DecodeItem) * M.dec.size());
-  const size_t o_comb = slot(sizeof(CombineItem) * M.comb.size());
-  const size_t o_pf = slot(sizeof(PrefillItem) * M.pf.size());
-  const size_t o_bt = slot(bt_up ? sizeof(int32_t) * n_req * b.max_blocks : 0);
-  const size_t total = off;
-  nf_status st = ensure_host(ctx, total);
+  P.o_pos = slot(sizeof(int32_t) * T);
+  P.o_slot = slot(sizeof(int32_t) * T);
+  P.o_inv = slot(sizeof(float) * half);
+  P.o_dec = slot(sizeof(DecodeItem) * M.dec.size());
+  P.o_comb = slot(sizeof(CombineItem) * M.comb.size());
+  P.o_pf = slot(sizeof(PrefillItem) * M.pf.size());
+  P.o_bt = slot(P.bt_up ? sizeof(int32_t) * n_req * b.max_blocks : 0);
+  P.total = off;
+  nf_status st = ensure_host(ctx, P.total);
   if (st != NF_OK) return st;
-  if (ctx->meta_dev.cap < total) {
-    st = ensure(ctx, ctx->meta_dev, total);
-    if (st != NF_OK) return st;
-  }
   if (ctx->upload_pending) {
     NF_HIP(ctx, hipEventSynchronize(ctx->upload_done));  // staging buffer free again
     ctx->upload_pending = false;
   }
   unsigned char* h = static_cast<unsigned char*>(ctx->meta_host);
-  memcpy(h + o_pos, L.pos.data(), sizeof(int32_t) * T);
-  memcpy(h + o_slot, L.slot.data(), sizeof(int32_t) * T);
-  float* inv = reinterpret_cast<float*>(h + o_inv);
+  memset(h, 0, P.total);  // padding too: the bytes are compared when a graph is reused
+  memcpy(h + P.o_pos, L.pos.data(), sizeof(int32_t) * T);
+  memcpy(h + P.o_slot, L.slot.data(), sizeof(int32_t) * T);
+  float* inv = reinterpret_cast<float*>(h + P.o_inv);
   for (int i = 0; i < half; ++i) inv[i] = (float)std::pow((double)cfg.rope_base, -2.0 * i / cfg.head_dim);
-  if (!M.dec.empty()) memcpy(h + o_dec, M.dec.data(), sizeof(DecodeItem) * M.dec.size());
-  if (!M.comb.empty()) memcpy(h + o_comb, M.comb.data(), sizeof(CombineItem) * M.comb.size());
-  if (!M.pf.empty()) memcpy(h + o_pf, M.pf.data(), sizeof(PrefillItem) * M.pf.size());
-  if (bt_up && n_req) memcpy(h + o_bt, b.block_table, sizeof(int32_t) * n_req * b.max_blocks);
-  NF_HIP(ctx, hipMemcpyAsync(ctx->meta_dev.p, h, total, hipMemcpyHostToDevice, stream));
+  if (!M.dec.empty()) memcpy(h + P.o_dec, M.dec.data(), sizeof(DecodeItem) * M.dec.size());
+  if (!M.comb.empty()) memcpy(h + P.o_comb, M.comb.data(), sizeof(CombineItem) * M.comb.size());
+  if (!M.pf.empty()) memcpy(h + P.o_pf, M.pf.data(), sizeof(PrefillItem) * M.pf.size());
+  if (P.bt_up && n_req) memcpy(h + P.o_bt, b.block_table, sizeof(int32_t) * n_req * b.max_blocks);
+  return NF_OK;
+}
+
+// Copy the staged metadata to `dst` on `stream` (ordered before the work that reads it).
+nf_status copy_meta(nf_ctx* ctx, const MetaPack& P, DevBuf& dst, hipStream_t stream) {
+  if (dst.cap < P.total) {
+    nf_status st = ensure(ctx, dst, P.total);
+    if (st != NF_OK) return st;
+  }
+  NF_HIP(ctx, hipMemcpyAsync(dst.p, ctx->meta_host, P.total, hipMemcpyHostToDevice, stream));
   NF_HIP(ctx, hipEventRecord(ctx->upload_done, stream));
   ctx->upload_pending = true;
-  unsigned char* d = static_cast<unsigned char*>(ctx->meta_dev.p);
-  M.d_pos = reinterpret_cast<const int32_t*>(d + o_pos);
-  M.d_slot = reinterpret_cast<const int32_t*>(d + o_slot);
-  M.d_inv_freq = reinterpret_cast<const float*>(d + o_inv);
-  M.d_dec = reinterpret_cast<const DecodeItem*>(d + o_dec);
-  M.d_comb = reinterpret_cast<const CombineItem*>(d + o_comb);
-  M.d_pf = reinterpret_cast<const PrefillItem*>(d + o_pf);
-  M.d_bt = bt_up ? reinterpret_cast<const int32_t*>(d + o_bt) : b.block_table_dev;
+  return NF_OK;
+}
+
+// Device pointers of the metadata held at `base`.
+void point_meta(const MetaPack& P, const void* base, const nf_batch_desc& b, Meta& M) {
+  const unsigned char* d = static_cast<const unsigned char*>(base);
+  M.d_pos = reinterpret_cast<const int32_t*>(d + P.o_pos);
+  M.d_slot = reinterpret_cast<const int32_t*>(d + P.o_slot);
+  M.d_inv_freq = reinterpret_cast<const float*>(d + P.o_inv);
+  M.d_dec = reinterpret_cast<const DecodeItem*>(d + P.o_dec);
+  M.d_comb = reinterpret_cast<const CombineItem*>(d + P.o_comb);
+  M.d_pf = reinterpret_cast<const PrefillItem*>(d + P.o_pf);
+  M.d_bt = P.bt_up ? reinterpret_cast<const int32_t*>(d + P.o_bt) : b.block_table_dev;
+}
+
+// Pack and upload the metadata to the context's metadata buffer on `stream`.
+nf_status upload_meta(nf_ctx* ctx, const nf_layer_cfg& cfg, const nf_batch_desc& b, const BatchLayout& L, Meta& M,
+                      hipStream_t stream) {
+  MetaPack P;
+  nf_status st = pack_meta(ctx, cfg, b, L, M, P);
+  if (st != NF_OK) return st;
+  if ((st = copy_meta(ctx, P, ctx->meta_dev, stream)) != NF_OK) return st;
+  point_meta(P, ctx->meta_dev.p, b, M);
   return NF_OK;
 }
 
@@ -431,8 +475,10 @@ nf_status launch_op(nf_ctx* ctx, const LayerArgs& A, const PlanGraph& g, const N
   return NF_OK;
 }
 
-nf_status prepare_batch(nf_ctx* ctx, const nf_layer_cfg* cfg, const nf_batch_desc* batch, int32_t num_blocks,
-                        const nf_plan* plan, BatchLayout& L, PlanGraph& g, Meta& M, hipStream_t stream) {
+// Everything of a call before the metadata upload: validation, layout, DAG, work lists and
+// workspace sizes (may reallocate context buffers; enqueues nothing).
+nf_status prepare_host(nf_ctx* ctx, const nf_layer_cfg* cfg, const nf_batch_desc* batch, int32_t num_blocks,
+                       const nf_plan* plan, BatchLayout& L, PlanGraph& g, Meta& M) {
   nf_status st = check_cfg(*cfg, ctx->err);
   if (st != NF_OK) return st;
   st = build_layout(*cfg, *batch, num_blocks, L, ctx->err);
@@ -447,8 +493,91 @@ nf_status prepare_batch(nf_ctx* ctx, const nf_layer_cfg* cfg, const nf_batch_des
   build_work(L, g, ctx->decode_split, cfg->n_kv_heads, M);
   if ((st = ensure_workspace(ctx, *cfg, L.T)) != NF_OK) return st;
   if ((st = ensure_parts(ctx, *cfg, M.n_parts)) != NF_OK) return st;
-  if ((st = plan_gemm_ws(ctx, *cfg, g, M)) != NF_OK) return st;
+  return plan_gemm_ws(ctx, *cfg, g, M);
+}
+
+nf_status prepare_batch(nf_ctx* ctx, const nf_layer_cfg* cfg, const nf_batch_desc* batch, int32_t num_blocks,
+                        const nf_plan* plan, BatchLayout& L, PlanGraph& g, Meta& M, hipStream_t stream) {
+  nf_status st = prepare_host(ctx, cfg, batch, num_blocks, plan, L, g, M);
+  if (st != NF_OK) return st;
   return upload_meta(ctx, *cfg, *batch, L, M, stream);
+}
+
+// The layers of one call: layer l reads x (layer 0: x_in, later layers: y in place).
+struct StackArgs {
+  const nf_layer_cfg* cfg;
+  int32_t n_layers;
+  const nf_layer_weights* w;  // [n_layers]
+  const bf16* x_in;
+  bf16* y;
+  nf_kv_pool* pools;  // [n_layers]
+  int max_blocks;
+  int decode_grid;
+  LayerArgs layer(int l) const {
+    return LayerArgs{cfg, &w[l], l == 0 ? x_in : y, y, &pools[l], max_blocks, decode_grid};
+  }
+};
+
+// One nano-batch on one unmasked stream: nothing to order across streams, so the caller's
+// stream runs it directly (no fork/join).
+bool runs_direct(const nf_plan* plan, const PlanGraph& g) {
+  return !plan || (g.n_streams == 1 && !plan->cu_masks);
+}
+
+// The plan's streams and enough events, created before anything is enqueued (a capture
+// then sees no creation calls).
+nf_status plan_resources(nf_ctx* ctx, const nf_plan* plan, const PlanGraph& g, size_t n_stack_ops,
+                         std::vector<hipStream_t>& ss) {
+  ss.clear();
+  if (runs_direct(plan, g)) return NF_OK;
+  ss.resize(g.n_streams);
+  for (int s = 0; s < g.n_streams; ++s) {
+    nf_status st = get_stream(ctx, plan->cu_masks ? plan->cu_masks + s * NF_CU_MASK_WORDS : nullptr, s, &ss[s]);
+    if (st != NF_OK) return st;
+  }
+  return ensure_events(ctx, n_stack_ops);
+}
+
+// Enqueue every nano-op of the stack in the graph's global order: directly on `caller`
+// when `ss` is empty, else on the plan's streams, forked from and joined back into `caller`.
+nf_status enqueue_stack(nf_ctx* ctx, const StackArgs& S, const PlanGraph& g, const StackGraph& sg, const Meta& M,
+                        const std::vector<hipStream_t>& ss, hipStream_t caller) {
+  const int32_t n = sg.n_ops;
+  nf_status st;
+  if (ss.empty()) {
+    for (int32_t op : sg.order) {
+      const NanoOp& o = g.ops[op % n];
+      if (o.empty && o.kind != NF_OP_KQV) continue;
+      if ((st = launch_op(ctx, S.layer(op / n), g, o, M, caller)) != NF_OK) return st;
+    }
+    return NF_OK;
+  }
+  // an op's completion event is recorded only when an op on another stream waits for it
+  const size_t N = sg.order.size();
+  std::vector<char> waited(N, 0);
+  for (size_t j = 0; j < N; ++j)
+    for (int32_t dep : sg.deps[j])
+      if (g.ops[dep % n].stream != g.ops[j % n].stream) waited[dep] = 1;
+  NF_HIP(ctx, hipEventRecord(ctx->fork_ev, caller));
+  std::vector<char> used(g.n_streams, 0);
+  for (auto& op : g.ops) used[op.stream] = 1;
+  for (int s = 0; s < g.n_streams; ++s)
+    if (used[s]) NF_HIP(ctx, hipStreamWaitEvent(ss[s], ctx->fork_ev, 0));
+  for (int32_t i : sg.order) {
+    const NanoOp& op = g.ops[i % n];
+    hipStream_t s = ss[op.stream];
+    for (int32_t dep : sg.deps[i])
+      if (g.ops[dep % n].stream != op.stream) NF_HIP(ctx, hipStreamWaitEvent(s, ctx->events[dep], 0));
+    if (!op.empty || op.kind == NF_OP_KQV)
+      if ((st = launch_op(ctx, S.layer(i / n), g, op, M, s)) != NF_OK) return st;
+    if (waited[i]) NF_HIP(ctx, hipEventRecord(ctx->events[i], s));
+  }
+  for (int s = 0; s < g.n_streams; ++s)
+    if (used[s]) {
+      NF_HIP(ctx, hipEventRecord(ctx->join_ev[s], ss[s]));
+      NF_HIP(ctx, hipStreamWaitEvent(caller, ctx->join_ev[s], 0));
+    }
+  return NF_OK;
 }
 
 }  // namespace
@@ -483,9 +612,14 @@ extern "C" void nf_ctx_destroy(nf_ctx* ctx) {
   for (auto e : ctx->timing_pool) (void)hipEventDestroy(e);
   for (auto e : ctx->join_ev) (void)hipEventDestroy(e);
   if (ctx->fork_ev) (void)hipEventDestroy(ctx->fork_ev);
+  if (ctx->graph_exec) (void)hipGraphExecDestroy(ctx->graph_exec);
+  if (ctx->graph) (void)hipGraphDestroy(ctx->graph);
+  if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
+  if (ctx->graph_in) (void)hipEventDestroy(ctx->graph_in);
+  if (ctx->graph_out) (void)hipEventDestroy(ctx->graph_out);
   if (ctx->upload_done) (void)hipEventDestroy(ctx->upload_done);
   for (DevBuf* b : {&ctx->h, &ctx->qkv, &ctx->attn, &ctx->x1, &ctx->h2, &ctx->a, &ctx->meta_dev, &ctx->part_o,
-                    &ctx->part_ml, &ctx->gemm_ws})
+                    &ctx->part_ml, &ctx->gemm_ws, &ctx->graph_meta})
     if (b->p) (void)hipFree(b->p);
   if (ctx->meta_host) (void)hipHostFree(ctx->meta_host);
   delete ctx;
@@ -493,70 +627,206 @@ extern "C" void nf_ctx_destroy(nf_ctx* ctx) {
 
 extern "C" const char* nf_last_error(const nf_ctx* ctx) { return ctx ? ctx->err.c_str() : "null context"; }
 
+namespace {
+
+bool weights_ok(const nf_layer_weights& w) {
+  return w.g_attn && w.w_qkv && w.w_o && w.g_ffn && w.w_gate_up && w.w_down;
+}
+
+// Stack call: validate the layer arrays (host checks only).
+nf_status check_stack_args(nf_ctx* ctx, const nf_layer_cfg* cfg, int32_t n_layers, const nf_layer_weights* w,
+                           const nf_kv_pool* pools, int32_t flags) {
+  if (n_layers < 1 || !w || !pools || (flags & ~(NF_STACK_PIPELINE | NF_STACK_GRAPH))) {
+    ctx->err = "nf_stack_forward: n_layers >= 1, weight and pool arrays and known flags needed";
+    return NF_E_ARG;
+  }
+  const size_t pool_bytes =
+      (size_t)pools[0].num_blocks * cfg->n_kv_heads * cfg->block_size * cfg->head_dim * sizeof(uint16_t);
+  std::vector<std::pair<uintptr_t, uintptr_t>> spans;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    if (!weights_ok(w[l]) || !pools[l].k || !pools[l].v) {
+      ctx->err = "nf_stack_forward: null weight or pool pointer in layer " + std::to_string(l);
+      return NF_E_ARG;
+    }
+    if (pools[l].num_blocks != pools[0].num_blocks) {
+      ctx->err = "nf_stack_forward: every layer's pool needs the same num_blocks";
+      return NF_E_ARG;
+    }
+    for (const void* p : {pools[l].k, pools[l].v})
+      spans.push_back({reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + pool_bytes});
+  }
+  std::sort(spans.begin(), spans.end());
+  for (size_t i = 1; i < spans.size(); ++i)
+    if (spans[i].first < spans[i - 1].second) {
+      ctx->err = "nf_stack_forward: KV pools of different layers overlap";
+      return NF_E_ARG;
+    }
+  return NF_OK;
+}
+
+// Everything a captured stack bakes into its kernel arguments, besides the metadata bytes.
+std::vector<uint64_t> graph_key(const nf_ctx* ctx, const nf_layer_cfg& cfg, const StackArgs& S, const nf_plan* plan,
+                                int32_t flags, const nf_batch_desc& b) {
+  std::vector<uint64_t> k;
+  auto u = [&](uint64_t v) { k.push_back(v); };
+  auto p = [&](const void* v) { k.push_back(reinterpret_cast<uintptr_t>(v)); };
+  u(ctx->ws_gen);
+  u((uint64_t)flags);
+  u((uint64_t)S.n_layers);
+  u(((uint64_t)(uint32_t)cfg.hidden << 32) | (uint32_t)cfg.ffn);
+  u(((uint64_t)(uint32_t)cfg.n_q_heads << 32) | (uint32_t)cfg.n_kv_heads);
+  u(((uint64_t)(uint32_t)cfg.head_dim << 32) | (uint32_t)cfg.block_size);
+  uint32_t eps, base;
+  memcpy(&eps, &cfg.rms_eps, 4);
+  memcpy(&base, &cfg.rope_base, 4);
+  u(((uint64_t)eps << 32) | base);
+  p(S.x_in);
+  p(S.y);
+  u((uint64_t)S.max_blocks);
+  u((uint64_t)S.decode_grid);
+  p(b.block_table_dev);
+  u(((uint64_t)(uint32_t)b.n_decode << 32) | (uint32_t)b.n_prefill);
+  for (int32_t l = 0; l < S.n_layers; ++l) {
+    const nf_layer_weights& w = S.w[l];
+    for (const void* q : {w.g_attn, w.w_qkv, w.w_o, w.g_ffn, w.w_gate_up, w.w_down}) p(q);
+    p(S.pools[l].k);
+    p(S.pools[l].v);
+    u((uint64_t)S.pools[l].num_blocks);
+  }
+  u((uint64_t)ctx->decode_split);
+  u((uint64_t)ctx->decode_nbuf);
+  u((uint64_t)ctx->decode_ring);
+  for (auto& row : ctx->gemm_variant) u(((uint64_t)(uint32_t)row[0] << 32) | (uint32_t)row[1]);
+  if (plan) {
+    u((uint64_t)plan->n_nano);
+    for (int32_t j = 0; j <= plan->n_nano; ++j) u((uint64_t)(uint32_t)plan->bounds[j]);
+    u((uint64_t)plan->n_streams);
+    u((uint64_t)plan->n_ops);
+    for (int32_t i = 0; i < plan->n_ops; ++i)
+      u(((uint64_t)(uint32_t)plan->op_kind[i] << 40) | ((uint64_t)(uint32_t)plan->op_nano[i] << 20) |
+        (uint32_t)plan->op_stream[i]);
+    u((uint64_t)(uint32_t)plan->decode_max_workgroups);
+  } else {
+    u(~0ull);
+  }
+  return k;
+}
+
+}  // namespace
+
+// One call of the layer stack (nf_layer_forward is the one-layer, unpipelined case).
+static nf_status stack_forward(nf_ctx* ctx, const nf_layer_cfg* cfg, int32_t n_layers, const nf_layer_weights* w,
+                               const void* x_in, void* y_out, const nf_batch_desc* batch, nf_kv_pool* pools,
+                               const nf_plan* plan, int32_t flags, hipStream_t caller) {
+  BatchLayout L;
+  PlanGraph g;
+  Meta M;
+  nf_status st = prepare_host(ctx, cfg, batch, pools[0].num_blocks, plan, L, g, M);
+  if (st != NF_OK) return st;
+  const bool graph = (flags & NF_STACK_GRAPH) != 0;
+  if (graph && !kGraphReplayEnabled) {
+    ctx->err = "captured-graph replay of the layer stack is switched off in this build";
+    return NF_E_UNSUPPORTED;
+  }
+  if (graph && plan && plan->cu_masks) {
+    ctx->err = "a captured stack cannot keep the CU masks of the plan's streams";
+    return NF_E_UNSUPPORTED;
+  }
+  StackGraph sg;
+  if ((st = build_stack_graph(g, n_layers, (flags & NF_STACK_PIPELINE) != 0, sg, ctx->err)) != NF_OK) return st;
+  std::vector<hipStream_t> ss;
+  if ((st = plan_resources(ctx, plan, g, sg.order.size(), ss)) != NF_OK) return st;
+  StackArgs S{cfg,
+              n_layers,
+              w,
+              static_cast<const bf16*>(x_in),
+              static_cast<bf16*>(y_out),
+              pools,
+              batch->max_blocks,
+              (plan && plan->decode_max_workgroups > 0) ? plan->decode_max_workgroups : ctx->decode_grid};
+  if (!graph) {
+    if ((st = upload_meta(ctx, *cfg, *batch, L, M, caller)) != NF_OK) return st;
+    if (L.T == 0) return NF_OK;
+    return enqueue_stack(ctx, S, g, sg, M, ss, caller);
+  }
+  // captured stack: replayed while its key and metadata bytes are unchanged
+  MetaPack P;
+  if ((st = pack_meta(ctx, *cfg, *batch, L, M, P)) != NF_OK) return st;
+  if (L.T == 0) return NF_OK;
+  if (!ctx->cap_stream) NF_HIP(ctx, hipStreamCreateWithFlags(&ctx->cap_stream, hipStreamNonBlocking));
+  if (!ctx->graph_in) NF_HIP(ctx, hipEventCreateWithFlags(&ctx->graph_in, hipEventDisableTiming));
+  if (!ctx->graph_out) NF_HIP(ctx, hipEventCreateWithFlags(&ctx->graph_out, hipEventDisableTiming));
+  if (ctx->graph_meta.cap < P.total && (st = ensure(ctx, ctx->graph_meta, P.total)) != NF_OK) return st;
+  std::vector<uint64_t> key = graph_key(ctx, *cfg, S, plan, flags, *batch);
+  const unsigned char* staged = static_cast<const unsigned char*>(ctx->meta_host);
+  const bool reuse = ctx->graph_exec && key == ctx->graph_key && ctx->graph_meta_bytes.size() == P.total &&
+                     memcmp(ctx->graph_meta_bytes.data(), staged, P.total) == 0;
+  if (!reuse) {
+    if (ctx->graph_exec) {
+      NF_HIP(ctx, hipStreamSynchronize(ctx->cap_stream));  // the last replay is done with it
+      NF_HIP(ctx, hipGraphExecDestroy(ctx->graph_exec));
+      ctx->graph_exec = nullptr;
+    }
+    if (ctx->graph) {
+      NF_HIP(ctx, hipGraphDestroy(ctx->graph));
+      ctx->graph = nullptr;
+    }
+    ctx->graph_key.clear();
+    ctx->graph_meta_bytes.clear();
+    if ((st = copy_meta(ctx, P, ctx->graph_meta, caller)) != NF_OK) return st;
+    point_meta(P, ctx->graph_meta.p, *batch, M);
+    const uint32_t timing = ctx->timing_mask;
+    ctx->timing_mask = 0;
+    NF_HIP(ctx, hipStreamBeginCapture(ctx->cap_stream, hipStreamCaptureModeThreadLocal));
+    st = enqueue_stack(ctx, S, g, sg, M, ss, ctx->cap_stream);
+    hipGraph_t gr = nullptr;
+    const hipError_t e = hipStreamEndCapture(ctx->cap_stream, &gr);
+    ctx->timing_mask = timing;
+    if (st != NF_OK) {
+      if (gr) (void)hipGraphDestroy(gr);
+      return st;
+    }
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamEndCapture");
+    ctx->graph = gr;
+    NF_HIP(ctx, hipGraphInstantiate(&ctx->graph_exec, gr, nullptr, nullptr, 0));
+    ctx->graph_key = std::move(key);
+    ctx->graph_meta_bytes.assign(staged, staged + P.total);
+    ++ctx->graph_captures;
+  }
+  ++ctx->graph_launches;
+  NF_HIP(ctx, hipEventRecord(ctx->graph_in, caller));
+  NF_HIP(ctx, hipStreamWaitEvent(ctx->cap_stream, ctx->graph_in, 0));
+  NF_HIP(ctx, hipGraphLaunch(ctx->graph_exec, ctx->cap_stream));
+  NF_HIP(ctx, hipEventRecord(ctx->graph_out, ctx->cap_stream));
+  NF_HIP(ctx, hipStreamWaitEvent(caller, ctx->graph_out, 0));
+  return NF_OK;
+}
+
 extern "C" nf_status nf_layer_forward(nf_ctx* ctx, const nf_layer_cfg* cfg, const nf_layer_weights* w,
                                       const void* x_in, void* y_out, const nf_batch_desc* batch, nf_kv_pool* pool,
                                       const nf_plan* plan, void* stream_) {
   if (!ctx) return NF_E_ARG;
-  if (!cfg || !w || !x_in || !y_out || !batch || !pool || !pool->k || !pool->v || !w->g_attn || !w->w_qkv ||
-      !w->w_o || !w->g_ffn || !w->w_gate_up || !w->w_down) {
+  if (!cfg || !w || !x_in || !y_out || !batch || !pool || !pool->k || !pool->v || !weights_ok(*w)) {
     ctx->err = "null argument";
     return NF_E_ARG;
   }
-  hipStream_t caller = static_cast<hipStream_t>(stream_);
-  BatchLayout L;
-  PlanGraph g;
-  Meta M;
-  nf_status st = prepare_batch(ctx, cfg, batch, pool->num_blocks, plan, L, g, M, caller);
-  if (st != NF_OK) return st;
-  if (L.T == 0) return NF_OK;
-  LayerArgs A{cfg,  w, static_cast<const bf16*>(x_in), static_cast<bf16*>(y_out), pool, batch->max_blocks,
-              (plan && plan->decode_max_workgroups > 0) ? plan->decode_max_workgroups : ctx->decode_grid};
+  return stack_forward(ctx, cfg, 1, w, x_in, y_out, batch, pool, plan, 0, static_cast<hipStream_t>(stream_));
+}
 
-  // one nano-batch on one unmasked stream: nothing to order across streams, so the
-  // caller's stream runs it directly (no fork/join)
-  const bool single = plan && g.n_streams == 1 && !plan->cu_masks;
-  if (!plan || single) {
-    for (int32_t i : g.order)
-      if (!g.ops[i].empty || g.ops[i].kind == NF_OP_KQV) {
-        st = launch_op(ctx, A, g, g.ops[i], M, caller);
-        if (st != NF_OK) return st;
-      }
-    return NF_OK;
+extern "C" nf_status nf_stack_forward(nf_ctx* ctx, const nf_layer_cfg* cfg, int32_t n_layers,
+                                      const nf_layer_weights* weights, const void* x_in, void* y_out,
+                                      const nf_batch_desc* batch, nf_kv_pool* pools, const nf_plan* plan,
+                                      int32_t flags, void* stream_) {
+  if (!ctx) return NF_E_ARG;
+  if (!cfg || !x_in || !y_out || !batch) {
+    ctx->err = "null argument";
+    return NF_E_ARG;
   }
-  // streams of the plan
-  std::vector<hipStream_t> ss(g.n_streams);
-  for (int s = 0; s < g.n_streams; ++s) {
-    st = get_stream(ctx, plan->cu_masks ? plan->cu_masks + s * NF_CU_MASK_WORDS : nullptr, s, &ss[s]);
-    if (st != NF_OK) return st;
-  }
-  if ((st = ensure_events(ctx, g.ops.size())) != NF_OK) return st;
-  // an op's completion event is recorded only when an op on another stream waits for it
-  std::vector<char> waited(g.ops.size(), 0);
-  for (size_t i = 0; i < g.ops.size(); ++i)
-    for (int32_t dep : g.deps[i])
-      if (g.ops[dep].stream != g.ops[i].stream) waited[dep] = 1;
-  NF_HIP(ctx, hipEventRecord(ctx->fork_ev, caller));
-  std::vector<char> used(g.n_streams, 0);
-  for (auto& op : g.ops) used[op.stream] = 1;
-  for (int s = 0; s < g.n_streams; ++s)
-    if (used[s]) NF_HIP(ctx, hipStreamWaitEvent(ss[s], ctx->fork_ev, 0));
-  for (int32_t i : g.order) {
-    const NanoOp& op = g.ops[i];
-    hipStream_t s = ss[op.stream];
-    for (int32_t dep : g.deps[i])
-      if (g.ops[dep].stream != op.stream) NF_HIP(ctx, hipStreamWaitEvent(s, ctx->events[dep], 0));
-    if (!op.empty || op.kind == NF_OP_KQV) {
-      st = launch_op(ctx, A, g, op, M, s);
-      if (st != NF_OK) return st;
-    }
-    if (waited[i]) NF_HIP(ctx, hipEventRecord(ctx->events[i], s));
-  }
-  for (int s = 0; s < g.n_streams; ++s)
-    if (used[s]) {
-      NF_HIP(ctx, hipEventRecord(ctx->join_ev[s], ss[s]));
-      NF_HIP(ctx, hipStreamWaitEvent(caller, ctx->join_ev[s], 0));
-    }
-  return NF_OK;
+  nf_status st = check_cfg(*cfg, ctx->err);
+  if (st != NF_OK) return st;
+  if ((st = check_stack_args(ctx, cfg, n_layers, weights, pools, flags)) != NF_OK) return st;
+  return stack_forward(ctx, cfg, n_layers, weights, x_in, y_out, batch, pools, plan, flags,
+                       static_cast<hipStream_t>(stream_));
 }
 
 extern "C" nf_status nf_debug_buffer(nf_ctx* ctx, int32_t which, void** ptr, size_t* bytes) {
@@ -723,6 +993,12 @@ extern "C" nf_status nf_ctx_set_decode_launch(nf_ctx* ctx, int32_t max_workgroup
   ctx->decode_grid = max_workgroups;
   ctx->decode_nbuf = nbuf;
   ctx->decode_ring = ring;
+  return NF_OK;
+}
+extern "C" nf_status nf_ctx_graph_stats(nf_ctx* ctx, int64_t* captures, int64_t* launches) {
+  if (!ctx || !captures || !launches) return NF_E_ARG;
+  *captures = ctx->graph_captures;
+  *launches = ctx->graph_launches;
   return NF_OK;
 }
 extern "C" nf_status nf_ctx_set_gemm_variant(nf_ctx* ctx, int32_t kind, int32_t which, int32_t variant) {

@@ -28,9 +28,17 @@ class DeviceWeights:
 
     NAMES = ("g_attn", "w_qkv", "w_o", "g_ffn", "w_gate_up", "w_down")
 
-    def __init__(self, host: dict, device):
-        self.t = {k: bf16_tensor(host[k], device) for k in self.NAMES}
+    def __init__(self, host: dict | None, device, tensors: dict | None = None):
+        self.t = tensors if tensors is not None else {k: bf16_tensor(host[k], device) for k in self.NAMES}
         self.desc = abi.nf_layer_weights(*[self.t[k].data_ptr() for k in self.NAMES])
+
+    @classmethod
+    def from_int16(cls, t16: dict) -> "DeviceWeights":
+        """From device int16 tensors holding bf16 bit patterns (no copy)."""
+        return cls(None, None, {k: t16[k].view(torch.bfloat16) for k in cls.NAMES})
+
+    def host_bits(self) -> dict:
+        return {k: bf16_bits(v) for k, v in self.t.items()}
 
 
 class DevicePool:

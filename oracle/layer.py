@@ -284,11 +284,15 @@ def layer_forward(cfg, weights, x_bits, batch, k_pool, v_pool, storage: str = "b
     Returns a dict: y (float64 [T, H]), k_pool / v_pool (updated copies), the intermediates
     h, q, k, v (after rotary), attn [T, n_q d], x1, h2, a, and flops (int).
     """
+    return _layer(cfg, weights, bf16_to_f64(x_bits), batch, k_pool, v_pool, storage)
+
+
+def _layer(cfg, weights, x, batch, k_pool, v_pool, storage):
+    """layer_forward on a float64 input x [T, H]."""
     if storage not in ("bf16", "exact"):
         raise ValueError("storage must be 'bf16' or 'exact'")
     st = store_bf16 if storage == "bf16" else (lambda a: a)
     H, nq, nkv, d, F = cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.ffn
-    x = bf16_to_f64(x_bits)
     T = x.shape[0]
     W = {name: bf16_to_f64(val) for name, val in weights.items()}
     _, pos = token_positions(batch)
@@ -312,6 +316,38 @@ def layer_forward(cfg, weights, x_bits, batch, k_pool, v_pool, storage: str = "b
         "y": y, "k_pool": k_new, "v_pool": v_new, "h": h, "q": q, "k": k, "v": v,
         "attn": attn, "x1": x1, "h2": h2, "a": a, "flops": layer_flops(cfg, batch),
     }
+
+
+def stack_forward(cfg, layer_weights, x_bits, batch, k_pools, v_pools, storage: str = "bf16"):
+    """Several decoder layers end to end over one batch (one model iteration).
+
+    The layers of a decoder-only model run in sequence, each on the previous one's output,
+    and every layer keeps a KV cache of its own; the batch (positions, slots, block table)
+    is the same for all of them (summary page, "The NanoFlow Runtime System": one iteration
+    runs the whole model over the dense batch; slides "8B Pipeline Design": the next
+    layer's KQV follows this layer's Down).
+
+    layer_weights  list of weight dicts as for layer_forward, one per layer
+    k_pools, v_pools  lists of per-layer pools (bf16 bits), as for layer_forward
+    storage  as for layer_forward; with "bf16" the hidden state handed from one layer to the
+             next is stored in bfloat16, with "exact" it is not rounded.
+
+    Returns a dict: y (float64 [T, H]), k_pools / v_pools (updated copies, per layer),
+    ys and attns (every layer's output and attention output), flops.
+    """
+    if not (len(layer_weights) == len(k_pools) == len(v_pools)) or not layer_weights:
+        raise ValueError("one weight dict and one pool pair per layer, at least one layer")
+    x = bf16_to_f64(x_bits)
+    ys, attns, kps, vps, flops = [], [], [], [], 0
+    for w, kp, vp in zip(layer_weights, k_pools, v_pools):
+        out = _layer(cfg, w, x, batch, kp, vp, storage)
+        x = out["y"]
+        ys.append(x)
+        attns.append(out["attn"])
+        kps.append(out["k_pool"])
+        vps.append(out["v_pool"])
+        flops += out["flops"]
+    return {"y": x, "ys": ys, "attns": attns, "k_pools": kps, "v_pools": vps, "flops": flops}
 
 
 # --------------------------------------------------------------------------------------

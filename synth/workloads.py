@@ -142,6 +142,7 @@ WORKLOADS = {
         prefill_lognormal=(512, 0.5, 1024),
         decode_ctx_range=(256, 2048),
         nano_sweep=(1, 2, 4),
+        extra={"layer_workload": "llama3_8b_layer"},
     ),
     "llama2_70b_tp8_layer": Workload(
         name="llama2_70b_tp8_layer",
@@ -455,3 +456,73 @@ def make_kv_pool_torch(shape: Shape, num_blocks: int, seed: int, layer: int = 0,
                 dst[b0:b1].copy_(bits.transpose(2, 3))
             del idx, vals, bits
     return K, V
+
+
+# --------------------------------------------------------------------------------------
+# Counter-based weights (for many-layer stacks): bit-identical on host and device
+# --------------------------------------------------------------------------------------
+
+WEIGHT_NAMES = ("g_attn", "w_qkv", "w_o", "g_ffn", "w_gate_up", "w_down")
+
+
+def _weight_shapes(shape: Shape) -> dict:
+    H, F = shape.hidden, shape.ffn
+    return {"w_qkv": (shape.qkv_rows, H), "w_o": (H, shape.q_width), "w_gate_up": (2 * F, H), "w_down": (H, F)}
+
+
+def _weight_scale() -> np.float32:
+    return np.float32(WEIGHT_STD / _IH_SD)
+
+
+def make_weights_counter(shape: Shape, seed: int, layer: int, rows=None, matrices=None) -> dict:
+    """One layer's weights from the counter-based generator (host, numpy).
+
+    Every entry is a scaled sum of four uniform 16-bit integers drawn from a hash of
+    (seed, layer, matrix, element index): mean 0, std WEIGHT_STD (an approximately normal
+    draw bounded at +-3.46 std), rounded to bf16. Gains are 1.0. ``rows`` (optional dict
+    name -> row indices) draws only those rows; ``matrices`` limits the names drawn.
+    """
+    out = {}
+    H = shape.hidden
+    one = f32_to_bf16_bits(np.ones(H, np.float32))
+    scale = _weight_scale()
+    for name in matrices or WEIGHT_NAMES:
+        if name in ("g_attn", "g_ffn"):
+            out[name] = one.copy()
+            continue
+        n_rows, n_cols = _weight_shapes(shape)[name]
+        r = np.arange(n_rows, dtype=np.int64) if rows is None or name not in rows else np.asarray(rows[name], np.int64)
+        idx = (r[:, None] * n_cols + np.arange(n_cols, dtype=np.int64)[None, :]).astype(np.uint64)
+        k1, k2 = _keys(seed, 1000 + layer, 10 + WEIGHT_NAMES.index(name))
+        vals = _kv_f32_from_counter(idx, np.uint64(k1), np.uint64(k2), scale, np,
+                                    lambda s: s.astype(np.int64).astype(np.float32))
+        out[name] = f32_to_bf16_bits(vals).reshape(len(r), n_cols)
+    return out
+
+
+def make_weights_counter_torch(shape: Shape, seed: int, layer: int, device="cpu", chunk: int = 1 << 24) -> dict:
+    """make_weights_counter as torch int16 tensors (bf16 bits) on ``device`` (bit-identical)."""
+    import torch
+
+    out = {}
+    H = shape.hidden
+    scale = float(_weight_scale())
+    for name in WEIGHT_NAMES:
+        if name in ("g_attn", "g_ffn"):
+            out[name] = torch.full((H,), 0x3F80, dtype=torch.int16, device=device)  # bf16 1.0
+            continue
+        n_rows, n_cols = _weight_shapes(shape)[name]
+        n = n_rows * n_cols
+        if n > 2**32:
+            raise ValueError("matrix too large for the 32-bit element counter")
+        dst = torch.empty(n, dtype=torch.int16, device=device)
+        k1, k2 = _keys(seed, 1000 + layer, 10 + WEIGHT_NAMES.index(name))
+        for e0 in range(0, n, chunk):
+            e1 = min(n, e0 + chunk)
+            idx = torch.arange(e0, e1, dtype=torch.int64, device=device)
+            vals = _kv_f32_from_counter(idx, k1, k2, torch.tensor(scale, dtype=torch.float32, device=device),
+                                        torch, lambda s: s.to(torch.float32))
+            dst[e0:e1].copy_(vals.to(torch.bfloat16).view(torch.int16))
+            del idx, vals
+        out[name] = dst.view(n_rows, n_cols)
+    return out

@@ -19,6 +19,25 @@ def rel_inf(got, ref) -> float:
     return float(np.max(np.abs(got - ref))) / denom
 
 
+def rel_rms(got, ref) -> float:
+    """||gpu - ref||_2 / ||ref||_2 over the whole tensor."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    denom = float(np.sqrt(np.sum(ref * ref)))
+    diff = float(np.sqrt(np.sum((got - ref) ** 2)))
+    return diff / denom if denom else diff
+
+
+def deep_tol(ref_bf16, ref_exact, measure=None) -> float:
+    """Tolerance for a result that several layers feed: the larger of TOL and twice the
+    distance between the oracle's bf16-storage and exact-storage results for the same
+    inputs. Both are computed by the oracle alone. Any bf16-storage implementation differs
+    from the exact result by rounding noise that the layers amplify; two such
+    implementations may differ by the sum of their distances from it."""
+    measure = measure or rel_inf
+    return max(TOL, 2.0 * measure(ref_bf16, ref_exact))
+
+
 def rand_bf16(rng, shape, scale=1.0) -> np.ndarray:
     return sw.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * np.float32(scale))
 

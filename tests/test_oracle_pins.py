@@ -398,6 +398,81 @@ def test_bf16_storage_model_rounds_every_handoff():
     assert 0 < rel < 2e-2
 
 
+# ---- layer stack -----------------------------------------------------------------------
+
+
+def _stack_inputs(n_layers, seed=7):
+    wl = sw.WORKLOADS["tiny"]
+    b = sw.make_batch("tiny", seed)
+    ws = [sw.make_weights(wl.shape, seed, gain_jitter=0.1, layer=l) for l in range(n_layers)]
+    x = sw.make_x(wl.shape, b.n_tokens, seed)
+    pools = [sw.make_kv_pool(wl.shape, b.num_blocks, seed, layer=l) for l in range(n_layers)]
+    return wl.shape, b, ws, x, [p[0] for p in pools], [p[1] for p in pools]
+
+
+def _slot_major(k_tok):
+    """[num_blocks, n_kv, BS, d] -> [num_blocks, BS, n_kv, d] (indexable by (block, offset))."""
+    return k_tok.transpose(0, 2, 1, 3)
+
+
+def _zero_branches(w):
+    z = dict(w)
+    z["w_o"] = np.zeros_like(w["w_o"])
+    z["w_down"] = np.zeros_like(w["w_down"])
+    return z
+
+
+def test_stack_of_identity_layers_returns_its_input():
+    """With the O and Down projections zero every layer is the identity on the hidden
+    state; each layer still writes this iteration's K/V into its own pool only, and layers
+    with equal weights write equal K/V."""
+    shape, b, ws, x, kps, vps = _stack_inputs(3)
+    zs = [_zero_branches(ws[0])] * 2 + [_zero_branches(ws[2])]
+    for storage in ("exact", "bf16"):
+        out = ol.stack_forward(shape, zs, x, b, kps, vps, storage=storage)
+        for y in out["ys"]:
+            assert np.array_equal(y, ol.bf16_to_f64(x))
+    slots = ol.new_token_slots(b, 16)
+    new = np.zeros((b.num_blocks, 16), bool)
+    new[[s_[0] for s_ in slots], [s_[1] for s_ in slots]] = True
+    for l in range(3):
+        kt, kt0 = _slot_major(ol.k_tokens(out["k_pools"][l])), _slot_major(ol.k_tokens(kps[l]))
+        vt, vt0 = out["v_pools"][l], vps[l]
+        assert np.array_equal(kt[~new], kt0[~new])  # only the new slots of its own pool
+        assert np.array_equal(vt.transpose(0, 3, 1, 2)[~new], vt0.transpose(0, 3, 1, 2)[~new])
+        assert not np.array_equal(kt[new], kt0[new])
+    # layers 0 and 1 share weights: same new K/V though their pools differ elsewhere
+    k0, k1, k2 = (_slot_major(ol.k_tokens(out["k_pools"][l])) for l in range(3))
+    assert np.array_equal(k0[new], k1[new]) and not np.array_equal(k0[~new], k1[~new])
+    assert not np.array_equal(k0[new], k2[new])
+
+
+def test_stack_applies_each_layer_with_its_own_weights_and_pool():
+    """An identity layer placed first or last leaves exactly the other layer's result."""
+    shape, b, ws, x, kps, vps = _stack_inputs(2, seed=8)
+    z = _zero_branches(ws[0])
+    one = ol.layer_forward(shape, ws[1], x, b, kps[1], vps[1])
+    first = ol.stack_forward(shape, [z, ws[1]], x, b, kps, vps)
+    assert np.array_equal(first["y"], one["y"])
+    assert np.array_equal(first["k_pools"][1], one["k_pool"]) and np.array_equal(first["v_pools"][1], one["v_pool"])
+    last = ol.stack_forward(shape, [ws[1], z], x, b, kps[::-1], vps[::-1])
+    assert np.array_equal(last["y"], one["y"])
+    assert np.array_equal(last["k_pools"][0], one["k_pool"])
+    # a single-layer stack is the layer
+    single = ol.stack_forward(shape, [ws[1]], x, b, [kps[1]], [vps[1]])
+    assert np.array_equal(single["y"], one["y"])
+
+
+def test_stack_flops_are_layers_times_layer_flops():
+    shape, b, ws, x, kps, vps = _stack_inputs(3, seed=9)
+    out = ol.stack_forward(shape, ws, x, b, kps, vps)
+    H, F, d, nq, nkv = shape.hidden, shape.ffn, shape.head_dim, shape.n_q, shape.n_kv
+    params = H * (nq + 2 * nkv) * d + nq * d * H + 3 * H * F
+    attn = sum(4 * nq * d * (int(c) + 1) for c in b.decode_ctx) + sum(
+        4 * nq * d * int(L) * (int(L) + 1) // 2 for L in b.prefill_len)
+    assert out["flops"] == 3 * (2 * b.n_tokens * params + attn)
+
+
 # ---- analytical cost model -----------------------------------------------------------
 
 from oracle import costmodel as cm  # noqa: E402

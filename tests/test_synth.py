@@ -1,0 +1,41 @@
+"""The seeded input generators (no GPU): the counter-based generators give the same bits on
+the host (numpy) and through torch, so a device-resident input and the oracle's host copy
+of it agree without a device-to-host transfer."""
+
+import numpy as np
+
+from synth import workloads as sw
+
+
+def test_kv_pool_host_and_torch_agree():
+    shape = sw.WORKLOADS["tiny"].shape
+    for layer in (0, 3):
+        k, v = sw.make_kv_pool(shape, 9, 5, layer=layer)
+        kt, vt = sw.make_kv_pool_torch(shape, 9, 5, layer=layer, chunk_blocks=4)
+        assert np.array_equal(k, kt.numpy().view(np.uint16)) and np.array_equal(v, vt.numpy().view(np.uint16))
+    k0, _ = sw.make_kv_pool(shape, 9, 5, layer=0)
+    assert not np.array_equal(k0, sw.make_kv_pool(shape, 9, 5, layer=1)[0])
+
+
+def test_counter_weights_host_and_torch_agree():
+    shape = sw.WORKLOADS["tiny"].shape
+    a = sw.make_weights_counter(shape, 3, 2)
+    b = sw.make_weights_counter_torch(shape, 3, 2, chunk=1000)
+    for name in sw.WEIGHT_NAMES:
+        assert np.array_equal(a[name], b[name].numpy().view(np.uint16)), name
+    rows = sw.make_weights_counter(shape, 3, 2, rows={"w_o": [5, 7], "w_down": [0]}, matrices=("w_o", "w_down"))
+    assert np.array_equal(rows["w_o"], a["w_o"][[5, 7]]) and np.array_equal(rows["w_down"], a["w_down"][[0]])
+    assert set(rows) == {"w_o", "w_down"}
+
+
+def test_counter_weights_statistics_and_independence():
+    shape = sw.WORKLOADS["tiny"].shape
+    w = sw.make_weights_counter(shape, 0, 0)
+    assert np.array_equal(w["g_attn"], sw.f32_to_bf16_bits(np.ones(shape.hidden, np.float32)))
+    f = sw.bf16_bits_to_f32(w["w_gate_up"]).astype(np.float64)
+    assert abs(f.mean()) < 2e-4 and abs(f.std() / sw.WEIGHT_STD - 1) < 0.01
+    assert np.abs(f).max() <= 3.47 * sw.WEIGHT_STD
+    other = sw.bf16_bits_to_f32(sw.make_weights_counter(shape, 0, 1)["w_gate_up"]).astype(np.float64)
+    assert abs(np.corrcoef(f.ravel(), other.ravel())[0, 1]) < 0.01  # layers draw independently
+    q = sw.bf16_bits_to_f32(w["w_qkv"]).astype(np.float64).ravel()
+    assert abs(np.corrcoef(q[:-1], q[1:])[0, 1]) < 0.02  # neighbouring entries independent
