@@ -346,7 +346,8 @@ def main():
                                                                 flags=abi.NF_STACK_PIPELINE)[0], 4)
         log("schedules (ms/step): " + ", ".join(f"{k} {v:.3f}" for k, v in schedules.items()))
 
-    traffic = counted_traffic(wl.name, args.seed, launches_per_step)
+    # a stack's decode-attention launch is its layer's launch on the same batch
+    traffic = counted_traffic(wl.extra.get("layer_workload", wl.name), args.seed, launches_per_step / n_layers)
     tokens_per_s = T / (ms * 1e-3)
     step_gemm_flops = alg["gemm_flops"] * n_layers
     mfma_frac = step_gemm_flops / (ms * 1e-3) / PEAK_BF16
