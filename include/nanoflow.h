@@ -69,10 +69,18 @@ typedef struct nf_ctx nf_ctx;  /* owns streams, events, metadata workspace, spli
 
 /* Layer shape. Supported: head_dim in {64, 128}; n_q_heads a multiple of n_kv_heads with
  * n_q_heads / n_kv_heads <= 16; block_size 16; hidden, ffn and n_q_heads*head_dim multiples
- * of 8. rms_eps and rope_base as in the model (1e-5 and 10000 for the LLaMA shapes). */
+ * of 8. rms_eps and rope_base as in the model (1e-5 and 10000 for the LLaMA shapes).
+ * n_experts = 0: dense SwiGLU FFN. n_experts > 0: mixture-of-experts FFN (summary page,
+ * "MoE models": a gate-routing operation, then the experts as a grouped GEMM): router
+ * logits h2 W_router^T, the top_k largest per token (ties: lower expert index), weights =
+ * softmax over the chosen logits, FFN output = sum over the chosen experts of weight x
+ * expert SwiGLU FFN of h2. Supported: n_experts in {4, 8, 16}, top_k = 2, hidden and ffn
+ * multiples of 32. */
 typedef struct {
   int32_t hidden, n_q_heads, n_kv_heads, head_dim, ffn, block_size;
   float rms_eps, rope_base;
+  int32_t n_experts; /* 0 = dense FFN                                                   */
+  int32_t top_k;     /* experts per token (MoE only)                                     */
 } nf_layer_cfg;
 
 /* Weights, device, Linear layout [out, in]:
@@ -80,9 +88,12 @@ typedef struct {
  *   w_qkv  [(n_q + 2 n_kv) head_dim, hidden]            rows = q heads | k heads | v heads
  *   w_o    [hidden, n_q head_dim]
  *   w_gate_up [2 ffn, hidden]                           rows = gate (ffn) | up (ffn)
- *   w_down [hidden, ffn]                                                                   */
+ *   w_down [hidden, ffn]
+ * MoE layers (n_experts = E > 0): w_gate_up [E][2 ffn, hidden] and w_down [E][hidden, ffn]
+ * (expert-major, each expert as above), w_router [E, hidden]; NULL for dense layers.      */
 typedef struct {
   const void *g_attn, *w_qkv, *w_o, *g_ffn, *w_gate_up, *w_down;
+  const void *w_router;
 } nf_layer_weights;
 
 /* Dense batch (slides, "Batch Formation": decode requests first, then prefill chunks).
@@ -272,6 +283,16 @@ nf_status nf_op_attention(nf_ctx *ctx, const nf_layer_cfg *cfg, const void *qkv,
                           const nf_batch_desc *batch, const nf_kv_pool *pool, void *out,
                           int32_t decode, int32_t kv_split_blocks, void *stream);
 
+/* The mixture-of-experts FFN alone (see nf_layer_cfg), for tests and profiling:
+ * y = x1 + sum over the top_k chosen experts of weight x expert(h2), for n_tokens rows.
+ * h2, x1, y: device [n_tokens][hidden] (y may alias x1); w: the layer's weights (g_* and
+ * attention weights unused). sel_out (int32) and wts_out (float), device [n_tokens][top_k]
+ * or NULL: the chosen experts (largest logit first) and their weights. Errors: NF_E_ARG,
+ * NF_E_UNSUPPORTED (dense cfg or unsupported MoE shape), NF_E_HIP.                         */
+nf_status nf_op_moe_ffn(nf_ctx *ctx, const nf_layer_cfg *cfg, const nf_layer_weights *w, const void *h2,
+                        const void *x1, void *y, int32_t n_tokens, int32_t *sel_out, float *wts_out,
+                        void *stream);
+
 /* ---- kernel timing ------------------------------------------------------------------------ */
 
 /* Kernel classes that can be timed. */
@@ -285,7 +306,9 @@ enum {
   NF_K_GEMM_DOWN = 6,
   NF_K_RMSNORM = 7,
   NF_K_ROPE_KV = 8,
-  NF_K_CLASSES = 9
+  NF_K_MOE_ROUTE = 9,      /* MoE router + dispatch (grouped GEMMs count as UG / Down) */
+  NF_K_MOE_COMBINE = 10,   /* MoE weighted combine + residual                */
+  NF_K_CLASSES = 11
 };
 
 /* Start collecting kernel timings for the classes whose bit is set in class_mask (0 stops):

@@ -33,9 +33,9 @@ NF_OP_KQV, NF_OP_DECATTN, NF_OP_PFATTN, NF_OP_O, NF_OP_UGD, NF_OP_KINDS = range(
 NF_STACK_PIPELINE, NF_STACK_GRAPH = 1, 2
 OP_NAMES = ["KQV", "DECATTN", "PFATTN", "O", "UGD"]
 (NF_K_DECODE_ATTN, NF_K_DECODE_COMBINE, NF_K_PREFILL_ATTN, NF_K_GEMM_KQV, NF_K_GEMM_O, NF_K_GEMM_UG, NF_K_GEMM_DOWN,
- NF_K_RMSNORM, NF_K_ROPE_KV, NF_K_CLASSES) = range(10)
+ NF_K_RMSNORM, NF_K_ROPE_KV, NF_K_MOE_ROUTE, NF_K_MOE_COMBINE, NF_K_CLASSES) = range(12)
 KERNEL_CLASS_NAMES = ["decode_attn", "decode_combine", "prefill_attn", "gemm_kqv", "gemm_o", "gemm_ug_swiglu",
-                      "gemm_down", "rmsnorm", "rope_kv_append"]
+                      "gemm_down", "rmsnorm", "rope_kv_append", "moe_route", "moe_combine"]
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _u32p = ctypes.POINTER(ctypes.c_uint32)
@@ -44,11 +44,12 @@ _u32p = ctypes.POINTER(ctypes.c_uint32)
 class nf_layer_cfg(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32), ("block_size", ctypes.c_int32),
-                ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float)]
+                ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32)]
 
 
 class nf_layer_weights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("g_attn", "w_qkv", "w_o", "g_ffn", "w_gate_up", "w_down")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("g_attn", "w_qkv", "w_o", "g_ffn", "w_gate_up", "w_down", "w_router")]
 
 
 class nf_batch_desc(ctypes.Structure):
@@ -104,6 +105,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                  ctypes.POINTER(nf_batch_desc), ctypes.POINTER(nf_kv_pool), ctypes.POINTER(nf_plan),
                                  I, V]),
         "nf_debug_buffer": (I, [V, I, ctypes.POINTER(V), ctypes.POINTER(S)]),
+        "nf_op_moe_ffn": (I, [V, ctypes.POINTER(nf_layer_cfg), ctypes.POINTER(nf_layer_weights), V, V, V, I, V, V, V]),
         "nf_op_gemm": (I, [V, V, V, V, V, I, I, I, I, I, V]),
         "nf_gemm_variants": (I, [_i32p, I, _i32p]),
         "nf_op_rmsnorm": (I, [V, V, V, V, I, I, ctypes.c_float, V]),
@@ -165,9 +167,10 @@ def _ptr(a: np.ndarray | None):
 
 
 def make_cfg(shape) -> nf_layer_cfg:
-    """nf_layer_cfg from any object with hidden, n_q, n_kv, head_dim, ffn, block_size, rms_eps, rope_base."""
+    """nf_layer_cfg from any object with hidden, n_q, n_kv, head_dim, ffn, block_size, rms_eps, rope_base
+    (and n_experts, top_k for MoE shapes)."""
     return nf_layer_cfg(shape.hidden, shape.n_q, shape.n_kv, shape.head_dim, shape.ffn, shape.block_size,
-                        shape.rms_eps, shape.rope_base)
+                        shape.rms_eps, shape.rope_base, getattr(shape, "n_experts", 0), getattr(shape, "top_k", 0))
 
 
 class HostBatch:
@@ -340,6 +343,12 @@ def nf_debug_buffer(ctx, which: int):
 def nf_op_gemm(ctx, A: int, B: int, C: int, R: int | None, m: int, n: int, k: int, epilogue: int = 0,
                variant: int = -1, stream: int = 0) -> None:
     _check(load().nf_op_gemm(ctx, A, B, C, R, m, n, k, epilogue, variant, stream), ctx)
+
+
+def nf_op_moe_ffn(ctx, cfg: nf_layer_cfg, weights: nf_layer_weights, h2: int, x1: int, y: int, n_tokens: int,
+                  sel_out: int | None = None, wts_out: int | None = None, stream: int = 0) -> None:
+    _check(load().nf_op_moe_ffn(ctx, ctypes.byref(cfg), ctypes.byref(weights), h2, x1, y, n_tokens, sel_out, wts_out,
+                                stream), ctx)
 
 
 def nf_gemm_variants():

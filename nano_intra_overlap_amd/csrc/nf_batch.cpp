@@ -50,6 +50,20 @@ nf_status check_cfg(const nf_layer_cfg& c, std::string& err) {
     err = "rms_eps must be >= 0 and rope_base > 0";
     return NF_E_ARG;
   }
+  if (c.n_experts < 0) {
+    err = "n_experts must be >= 0";
+    return NF_E_ARG;
+  }
+  if (c.n_experts > 0) {
+    if (!moe_experts_supported(c.n_experts) || c.top_k != 2) {
+      err = fmt("MoE with %ld experts, top %ld unsupported (4, 8 or 16 experts, top 2)", c.n_experts, c.top_k);
+      return NF_E_UNSUPPORTED;
+    }
+    if (c.hidden % 32 || c.ffn % 32) {
+      err = "MoE layers need hidden and ffn multiples of 32";
+      return NF_E_UNSUPPORTED;
+    }
+  }
   return NF_OK;
 }
 

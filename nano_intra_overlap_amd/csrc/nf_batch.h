@@ -60,6 +60,8 @@ nf_status build_layout(const nf_layer_cfg& cfg, const nf_batch_desc& b, int32_t 
 
 // Validate the layer shape against what the kernels implement.
 nf_status check_cfg(const nf_layer_cfg& cfg, std::string& err);
+// Expert counts the MoE kernels are built for (defined with them).
+bool moe_experts_supported(int n_experts);
 
 // A nano-operation of a plan with the token rows it reads/writes (its "range").
 struct NanoOp {

@@ -261,10 +261,11 @@ __device__ __forceinline__ void interleave_loads_reads() {
   if constexpr (NR > PR) __builtin_amdgcn_sched_group_barrier(0x100, NR - PR, 0);
 }
 
-template <int BM, int BN, int STAGES, int EPI>
-__global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B, bf16* C,
-                                                        const bf16* R, int M, int N, int K, int tiles_m, int tiles_n,
-                                                        int per_xcd, float* __restrict__ part) {
+template <int BM, int BN, int STAGES, int EPI, bool GRP = false>
+__global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__ A0, const bf16* __restrict__ B0,
+                                                        bf16* C0, const bf16* R, int M0, int N, int K, int tiles_m0,
+                                                        int tiles_n, int per_xcd, float* __restrict__ part,
+                                                        GroupArgs ga) {
   constexpr int BK = 32;
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -274,12 +275,40 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__
   constexpr int NL = A_LOADS + B_LOADS;
   static_assert(EPI != EPI_SWIGLU || (WTN % 64) == 0, "SwiGLU needs gate/up pairs of 32 columns");
 
+  static_assert(!GRP || EPI == EPI_STORE || EPI == EPI_SWIGLU, "grouped products store or apply SwiGLU");
   extern __shared__ __align__(16) unsigned char smem_raw[];
 
   const int w = blockIdx.x;
-  const int t = (w % kNumXcd) * per_xcd + (w / kNumXcd);
-  const int ntiles = tiles_m * tiles_n;
-  if (t >= ntiles) return;
+  int t = (w % kNumXcd) * per_xcd + (w / kNumXcd);
+  // the product of this workgroup: the whole problem, or (grouped) the group whose tiles
+  // cover t, its rows counted from the group's first row in the grouped order
+  int M = M0, tiles_m = tiles_m0;
+  const bf16* A = A0;
+  const bf16* B = B0;
+  bf16* C = C0;
+  const int32_t* a_rows = nullptr;
+  if constexpr (GRP) {
+    int g = 0, first = 0, tm = 0;
+    for (; g < ga.n_groups; ++g) {
+      tm = (ga.grp[g] + BM - 1) / BM;
+      if (t < first + tm * tiles_n) break;
+      first += tm * tiles_n;
+    }
+    if (g == ga.n_groups) return;
+    t -= first;
+    M = ga.grp[g];
+    tiles_m = tm;
+    const int rb = ga.grp[ga.n_groups + g];
+    if (ga.a_rows)
+      a_rows = ga.a_rows + rb;
+    else
+      A = A0 + (size_t)rb * K;
+    B = B0 + (size_t)g * ga.b_stride;
+    C = C0 + (size_t)rb * N;
+  } else {
+    (void)ga;
+    if (t >= tiles_m * tiles_n) return;
+  }
   constexpr int GM = 8;
   const int group = t / (GM * tiles_n);
   const int first_m = group * GM;
@@ -305,7 +334,10 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const bf16* __restrict__
   for (int i = 0; i < A_LOADS; ++i) {
     const int c = (i * 4 + wave) * 64 + lane;
     const int row = c >> 2, kc = (c & 3) ^ swz(row);
-    const int gr = min(m0 + row, M - 1);
+    int gr = min(m0 + row, M - 1);
+    if constexpr (GRP) {
+      if (a_rows) gr = a_rows[gr];  // gathered rows of A
+    }
     a_src[i] = A + (size_t)gr * K + k_begin + kc * 8;
   }
 #pragma unroll
@@ -652,7 +684,32 @@ static hipError_t launch_pipe_t(const bf16* A, const bf16* B, bf16* C, const bf1
     attr_set = true;
   }
   hipLaunchKernelGGL(kern, dim3(per_xcd * kNumXcd, ks), dim3(256), lds, s, A, B, C, R, M, N, K, tiles_m, tiles_n,
-                     per_xcd, part);
+                     per_xcd, part, GroupArgs{});
+  return hipGetLastError();
+}
+
+// Grouped product (the experts of an MoE FFN): group g multiplies its grp[g] rows (from
+// row grp[n_groups + g] of the grouped order; A's rows gathered through a_rows when given)
+// by B + g * b_stride. The grid covers the most tiles any split of n_rows rows can need;
+// workgroups past the actual tiles exit at once.
+template <int BM, int BN, int STAGES, int EPI>
+static hipError_t launch_grouped_t(const bf16* A, const int32_t* a_rows, const bf16* B, long long b_stride, bf16* C,
+                                   const int32_t* grp, int n_groups, int n_rows, int N, int K, hipStream_t s) {
+  const int tiles_n = (EPI == EPI_SWIGLU) ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
+  const long long max_tiles = ((long long)(n_rows + BM - 1) / BM + n_groups) * tiles_n;
+  const int per_xcd = (int)((max_tiles + kNumXcd - 1) / kNumXcd);
+  const size_t lds = (size_t)STAGES * (BM + BN) * 64;
+  auto kern = gemm_pipe_kernel<BM, BN, STAGES, EPI, true>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  GroupArgs ga{grp, a_rows, n_groups, b_stride};
+  hipLaunchKernelGGL(kern, dim3(per_xcd * kNumXcd), dim3(256), lds, s, A, B, C, nullptr, n_rows, N, K, 0, tiles_n,
+                     per_xcd, nullptr, ga);
   return hipGetLastError();
 }
 
@@ -709,6 +766,37 @@ hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int
     case 10: return launch_pipe<128, 128, 4>(A, B, C, R, m, n, k, epilogue, 2, ws, s);
     case 11: return launch_pipe<128, 128, 4>(A, B, C, R, m, n, k, epilogue, 4, ws, s);
 
+  }
+  return hipErrorInvalidValue;
+}
+
+bool gemm_grouped_variant_ok(int variant, int n, int k, int epilogue) {
+  return variant >= 6 && variant <= 9 && k % 32 == 0 && n % 8 == 0 && (epilogue == EPI_STORE || epilogue == EPI_SWIGLU);
+}
+
+int gemm_grouped_default_variant(int n_rows, int n_groups, int epilogue) {
+  // 256-row tiles once the average group fills them (measured: fewer, larger tiles win when
+  // the rows per group allow); 128 rows otherwise
+  const bool tall = n_rows >= 256 * n_groups;
+  if (epilogue == EPI_SWIGLU) return tall ? 6 : 8;
+  return tall ? 7 : 9;
+}
+
+hipError_t launch_gemm_grouped(const bf16* A, const int32_t* a_rows, const bf16* B, long long b_stride, bf16* C,
+                               const int32_t* grp, int n_groups, int n_rows, int n, int k, int epilogue, int variant,
+                               hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  if (!gemm_grouped_variant_ok(variant, n, k, epilogue)) return hipErrorInvalidValue;
+  const bool sw = epilogue == EPI_SWIGLU;
+  switch (variant) {
+    case 6: return sw ? launch_grouped_t<256, 256, 4, EPI_SWIGLU>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s)
+                      : launch_grouped_t<256, 256, 4, EPI_STORE>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s);
+    case 7: return sw ? launch_grouped_t<256, 128, 4, EPI_SWIGLU>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s)
+                      : launch_grouped_t<256, 128, 4, EPI_STORE>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s);
+    case 8: return sw ? launch_grouped_t<128, 256, 4, EPI_SWIGLU>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s)
+                      : launch_grouped_t<128, 256, 4, EPI_STORE>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s);
+    case 9: return sw ? launch_grouped_t<128, 128, 4, EPI_SWIGLU>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s)
+                      : launch_grouped_t<128, 128, 4, EPI_STORE>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s);
   }
   return hipErrorInvalidValue;
 }

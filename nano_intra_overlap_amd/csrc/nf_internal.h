@@ -29,6 +29,15 @@ constexpr int kNumXcd = 8;       // XCDs of an MI355X
 // kernel launchers (defined in the .hip files)
 // ---------------------------------------------------------------------------------------
 
+// Grouped products (one per expert): see launch_gemm_grouped. Passed by value to the
+// pipelined GEMM kernel; unused by its plain instantiations.
+struct GroupArgs {
+  const int32_t* grp;     // device [2 n_groups]: rows of each group, first grouped row of each group
+  const int32_t* a_rows;  // device, optional: A row of each grouped row (gather); null = contiguous
+  int n_groups;
+  long long b_stride;     // elements between consecutive groups' B matrices
+};
+
 struct GemmVariant {
   int bm, bn, bk, ks;  // tile, k step, K slices (split-K; 1 = none)
   int stages = 4;      // LDS slabs of the pipelined kernels
@@ -43,6 +52,23 @@ size_t gemm_workspace_bytes(int variant, int m, int n);
 // gemm_workspace_bytes(variant, m, n) bytes (may be null when that is 0).
 hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int m, int n, int k,
                        int epilogue, int variant, hipStream_t s, float* ws = nullptr, size_t ws_bytes = 0);
+
+// C = A B_g^T per group g (epilogue 0 store or 2 SwiGLU), pipelined tiles (variants 6-9),
+// k a multiple of 32, n of 8. grp: device [2 n_groups] (rows, first row in the grouped
+// order); n_rows: total grouped rows (an upper bound on the sum of grp rows is enough).
+// C rows follow the grouped order; A rows too unless a_rows gathers them.
+hipError_t launch_gemm_grouped(const bf16* A, const int32_t* a_rows, const bf16* B, long long b_stride, bf16* C,
+                               const int32_t* grp, int n_groups, int n_rows, int n, int k, int epilogue, int variant,
+                               hipStream_t s);
+bool gemm_grouped_variant_ok(int variant, int n, int k, int epilogue);
+int gemm_grouped_default_variant(int n_rows, int n_groups, int epilogue);
+
+// MoE: router + dispatch of tokens [t_begin, t_end) (sel/wts/pos/src indexed by token
+// entry 2 t + k; grp: this nano-batch's [2 n_experts] group table), and the combine.
+hipError_t launch_moe_route(const bf16* h2, const bf16* wr, int t_begin, int t_end, int H, int n_experts, int32_t* sel,
+                            float* wts, int32_t* pos, int32_t* src, int32_t* grp, hipStream_t s);
+hipError_t launch_moe_combine(const bf16* x1, const bf16* out, const int32_t* pos, const float* wts, bf16* y,
+                              int t_begin, int t_end, int H, hipStream_t s);
 
 hipError_t launch_rmsnorm(const bf16* x, const bf16* g, bf16* out, int m, int n, float eps,
                           hipStream_t s);

@@ -52,6 +52,10 @@ struct nf_ctx {
   // split-KV partials
   DevBuf part_o, part_ml;
   DevBuf gemm_ws;  // split-K fp32 partials, one region per GEMM of a plan
+  // MoE FFN: per token entry (2 T) the chosen expert, weight, grouped row; per grouped row
+  // its token; per nano-batch the expert group table; the grouped expert outputs
+  DevBuf moe_idx, moe_out;
+  size_t moe_rows = 0;  // 2 T the MoE index arrays were laid out for
   uint64_t ws_gen = 0;  // bumped whenever a device buffer is reallocated
   // captured layer stack: its own metadata buffer, the key it was captured for
   hipStream_t cap_stream = nullptr;
@@ -293,16 +297,45 @@ nf_status ensure_parts(nf_ctx* ctx, const nf_layer_cfg& cfg, int32_t n_parts) {
   return ensure(ctx, ctx->part_ml, n * 2 * sizeof(float));
 }
 
+// MoE index arrays in ctx->moe_idx for 2T token entries: sel | wts | pos | src | group
+// tables (2 n_experts per nano-batch, room for T nano-batches).
+struct MoeIdx {
+  int32_t* sel;
+  float* wts;
+  int32_t* pos;
+  int32_t* src;
+  int32_t* grp;
+};
+MoeIdx moe_idx(nf_ctx* ctx) {
+  const size_t n = ctx->moe_rows;
+  char* b = static_cast<char*>(ctx->moe_idx.p);
+  return MoeIdx{reinterpret_cast<int32_t*>(b), reinterpret_cast<float*>(b + 4 * n),
+                reinterpret_cast<int32_t*>(b + 8 * n), reinterpret_cast<int32_t*>(b + 12 * n),
+                reinterpret_cast<int32_t*>(b + 16 * n)};
+}
+
 nf_status ensure_workspace(nf_ctx* ctx, const nf_layer_cfg& c, int T) {
   const size_t t = std::max(T, 1);
   const size_t qkvw = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const size_t fan = c.n_experts > 0 ? (size_t)c.top_k : 1;  // rows of a per token
   nf_status st;
   if ((st = ensure(ctx, ctx->h, t * c.hidden * 2)) != NF_OK) return st;
   if ((st = ensure(ctx, ctx->qkv, t * qkvw * 2)) != NF_OK) return st;
   if ((st = ensure(ctx, ctx->attn, t * c.n_q_heads * c.head_dim * 2)) != NF_OK) return st;
   if ((st = ensure(ctx, ctx->x1, t * c.hidden * 2)) != NF_OK) return st;
   if ((st = ensure(ctx, ctx->h2, t * c.hidden * 2)) != NF_OK) return st;
-  if ((st = ensure(ctx, ctx->a, t * c.ffn * 2)) != NF_OK) return st;
+  if ((st = ensure(ctx, ctx->a, fan * t * c.ffn * 2)) != NF_OK) return st;
+  if (c.n_experts > 0) {
+    const size_t rows = 2 * t;
+    if ((st = ensure(ctx, ctx->moe_out, rows * c.hidden * 2)) != NF_OK) return st;
+    // laid out for the most rows seen so far; group tables for up to rows / 2 nano-batches
+    const size_t r = std::max(rows, ctx->moe_rows);
+    const size_t need = 16 * r + 4 * (size_t)(2 * c.n_experts) * (r / 2);
+    if (ctx->moe_rows < r || ctx->moe_idx.cap < need) {
+      if ((st = ensure(ctx, ctx->moe_idx, need)) != NF_OK) return st;
+      ctx->moe_rows = r;
+    }
+  }
   return NF_OK;
 }
 
@@ -344,7 +377,7 @@ nf_status plan_gemm_ws(nf_ctx* ctx, const nf_layer_cfg& c, const PlanGraph& g, M
     if (m <= 0) continue;
     if (op.kind == NF_OP_KQV) take(2 * i, gemm_workspace_bytes(pick_variant(ctx, NF_OP_KQV, 0, m, W, H, 0), m, W));
     if (op.kind == NF_OP_O) take(2 * i, gemm_workspace_bytes(pick_variant(ctx, NF_OP_O, 0, m, H, Q, 1), m, H));
-    if (op.kind == NF_OP_UGD) {
+    if (op.kind == NF_OP_UGD && c.n_experts == 0) {
       take(2 * i, gemm_workspace_bytes(pick_variant(ctx, NF_OP_UGD, 0, m, F, H, 2), m, F));
       take(2 * i + 1, gemm_workspace_bytes(pick_variant(ctx, NF_OP_UGD, 1, m, H, F, 1), m, H));
     }
@@ -379,6 +412,40 @@ nf_status timed(nf_ctx* ctx, int cls, hipStream_t s, F fn) {
     ctx->timed.push_back({cls, a, b});
   }
   return NF_OK;
+}
+
+int pick_grouped(nf_ctx* ctx, int which, int rows, int n_experts, int n, int k, int epi) {
+  const int v = ctx->gemm_variant[NF_OP_UGD][which];
+  if (gemm_grouped_variant_ok(v, n, k, epi)) return v;
+  return gemm_grouped_default_variant(rows, n_experts, epi);
+}
+
+// MoE FFN over token rows [lo, hi): y = x1 + sum_k w_k expert_k(h2); grp is this
+// nano-batch's group table. The token entries of [lo, hi) own grouped rows [2 lo, 2 hi).
+nf_status moe_ffn_rows(nf_ctx* ctx, const nf_layer_cfg& c, const nf_layer_weights& w, const bf16* h2, const bf16* x1,
+                       bf16* y, int lo, int hi, int32_t* grp, hipStream_t s) {
+  const int H = c.hidden, F = c.ffn, E = c.n_experts, rows = 2 * (hi - lo);
+  const MoeIdx ix = moe_idx(ctx);
+  bf16* a = static_cast<bf16*>(ctx->a.p) + (size_t)2 * lo * F;
+  bf16* out = static_cast<bf16*>(ctx->moe_out.p) + (size_t)2 * lo * H;
+  nf_status st;
+  if ((st = timed(ctx, NF_K_MOE_ROUTE, s, [&] {
+         return launch_moe_route(h2, static_cast<const bf16*>(w.w_router), lo, hi, H, E, ix.sel, ix.wts, ix.pos,
+                                 ix.src, grp, s);
+       })) != NF_OK)
+    return st;
+  if ((st = timed(ctx, NF_K_GEMM_UG, s, [&] {
+         return launch_gemm_grouped(h2, ix.src + 2 * lo, static_cast<const bf16*>(w.w_gate_up), (long long)2 * F * H, a,
+                                    grp, E, rows, F, H, 2, pick_grouped(ctx, 0, rows, E, F, H, 2), s);
+       })) != NF_OK)
+    return st;
+  if ((st = timed(ctx, NF_K_GEMM_DOWN, s, [&] {
+         return launch_gemm_grouped(a, nullptr, static_cast<const bf16*>(w.w_down), (long long)H * F, out, grp, E, rows,
+                                    H, F, 0, pick_grouped(ctx, 1, rows, E, H, F, 0), s);
+       })) != NF_OK)
+    return st;
+  return timed(ctx, NF_K_MOE_COMBINE, s,
+               [&] { return launch_moe_combine(x1, out - (size_t)2 * lo * H, ix.pos, ix.wts, y, lo, hi, H, s); });
 }
 
 nf_status launch_op(nf_ctx* ctx, const LayerArgs& A, const PlanGraph& g, const NanoOp& op, const Meta& M,
@@ -458,6 +525,11 @@ nf_status launch_op(nf_ctx* ctx, const LayerArgs& A, const PlanGraph& g, const N
         return launch_rmsnorm(x1 + (size_t)lo * H, static_cast<const bf16*>(A.w->g_ffn), h2 + (size_t)lo * H, m, H,
                               c.rms_eps, s);
       }));
+      if (c.n_experts > 0) {
+        NF_TRY(moe_ffn_rows(ctx, c, *A.w, h2, x1, A.y, lo, hi, moe_idx(ctx).grp + (size_t)op.nano * 2 * c.n_experts,
+                            s));
+        break;
+      }
       NF_TRY(timed(ctx, NF_K_GEMM_UG, s, [&] {
         return launch_gemm(h2 + (size_t)lo * H, static_cast<const bf16*>(A.w->w_gate_up), a + (size_t)lo * F, nullptr,
                            m, F, H, 2, pick_variant(ctx, NF_OP_UGD, 0, m, F, H, 2), s, ws(0),
@@ -619,7 +691,7 @@ extern "C" void nf_ctx_destroy(nf_ctx* ctx) {
   if (ctx->graph_out) (void)hipEventDestroy(ctx->graph_out);
   if (ctx->upload_done) (void)hipEventDestroy(ctx->upload_done);
   for (DevBuf* b : {&ctx->h, &ctx->qkv, &ctx->attn, &ctx->x1, &ctx->h2, &ctx->a, &ctx->meta_dev, &ctx->part_o,
-                    &ctx->part_ml, &ctx->gemm_ws, &ctx->graph_meta})
+                    &ctx->part_ml, &ctx->gemm_ws, &ctx->graph_meta, &ctx->moe_idx, &ctx->moe_out})
     if (b->p) (void)hipFree(b->p);
   if (ctx->meta_host) (void)hipHostFree(ctx->meta_host);
   delete ctx;
@@ -629,8 +701,8 @@ extern "C" const char* nf_last_error(const nf_ctx* ctx) { return ctx ? ctx->err.
 
 namespace {
 
-bool weights_ok(const nf_layer_weights& w) {
-  return w.g_attn && w.w_qkv && w.w_o && w.g_ffn && w.w_gate_up && w.w_down;
+bool weights_ok(const nf_layer_cfg& c, const nf_layer_weights& w) {
+  return w.g_attn && w.w_qkv && w.w_o && w.g_ffn && w.w_gate_up && w.w_down && (c.n_experts == 0 || w.w_router);
 }
 
 // Stack call: validate the layer arrays (host checks only).
@@ -644,7 +716,7 @@ nf_status check_stack_args(nf_ctx* ctx, const nf_layer_cfg* cfg, int32_t n_layer
       (size_t)pools[0].num_blocks * cfg->n_kv_heads * cfg->block_size * cfg->head_dim * sizeof(uint16_t);
   std::vector<std::pair<uintptr_t, uintptr_t>> spans;
   for (int32_t l = 0; l < n_layers; ++l) {
-    if (!weights_ok(w[l]) || !pools[l].k || !pools[l].v) {
+    if (!weights_ok(*cfg, w[l]) || !pools[l].k || !pools[l].v) {
       ctx->err = "nf_stack_forward: null weight or pool pointer in layer " + std::to_string(l);
       return NF_E_ARG;
     }
@@ -806,7 +878,7 @@ extern "C" nf_status nf_layer_forward(nf_ctx* ctx, const nf_layer_cfg* cfg, cons
                                       const void* x_in, void* y_out, const nf_batch_desc* batch, nf_kv_pool* pool,
                                       const nf_plan* plan, void* stream_) {
   if (!ctx) return NF_E_ARG;
-  if (!cfg || !w || !x_in || !y_out || !batch || !pool || !pool->k || !pool->v || !weights_ok(*w)) {
+  if (!cfg || !w || !x_in || !y_out || !batch || !pool || !pool->k || !pool->v || !weights_ok(*cfg, *w)) {
     ctx->err = "null argument";
     return NF_E_ARG;
   }
@@ -949,6 +1021,33 @@ extern "C" nf_status nf_op_attention(nf_ctx* ctx, const nf_layer_cfg* cfg, const
                                     static_cast<const bf16*>(pool->v), M.d_bt, batch->max_blocks, M.d_pf,
                                     (int)M.pf.size(), static_cast<bf16*>(out), nq, nkv, d, s));
   }
+  return NF_OK;
+}
+
+extern "C" nf_status nf_op_moe_ffn(nf_ctx* ctx, const nf_layer_cfg* cfg, const nf_layer_weights* w, const void* h2,
+                                   const void* x1, void* y, int32_t n_tokens, int32_t* sel_out, float* wts_out,
+                                   void* stream) {
+  if (!ctx) return NF_E_ARG;
+  if (!cfg || !w || !h2 || !x1 || !y || n_tokens < 0 || !w->w_gate_up || !w->w_down || !w->w_router) {
+    ctx->err = "nf_op_moe_ffn: bad argument";
+    return NF_E_ARG;
+  }
+  nf_status st = check_cfg(*cfg, ctx->err);
+  if (st != NF_OK) return st;
+  if (cfg->n_experts == 0) {
+    ctx->err = "nf_op_moe_ffn: the layer shape has a dense FFN";
+    return NF_E_UNSUPPORTED;
+  }
+  if (n_tokens == 0) return NF_OK;
+  if ((st = ensure_workspace(ctx, *cfg, n_tokens)) != NF_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const MoeIdx ix = moe_idx(ctx);
+  if ((st = moe_ffn_rows(ctx, *cfg, *w, static_cast<const bf16*>(h2), static_cast<const bf16*>(x1),
+                         static_cast<bf16*>(y), 0, n_tokens, ix.grp, s)) != NF_OK)
+    return st;
+  const size_t n = (size_t)2 * n_tokens;
+  if (sel_out) NF_HIP(ctx, hipMemcpyAsync(sel_out, ix.sel, n * 4, hipMemcpyDeviceToDevice, s));
+  if (wts_out) NF_HIP(ctx, hipMemcpyAsync(wts_out, ix.wts, n * 4, hipMemcpyDeviceToDevice, s));
   return NF_OK;
 }
 

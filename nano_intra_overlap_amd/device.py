@@ -26,16 +26,17 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
 class DeviceWeights:
     """A layer's weights resident on the device, plus the nf_layer_weights view of them."""
 
-    NAMES = ("g_attn", "w_qkv", "w_o", "g_ffn", "w_gate_up", "w_down")
+    NAMES = ("g_attn", "w_qkv", "w_o", "g_ffn", "w_gate_up", "w_down", "w_router")  # w_router: MoE only
 
     def __init__(self, host: dict | None, device, tensors: dict | None = None):
-        self.t = tensors if tensors is not None else {k: bf16_tensor(host[k], device) for k in self.NAMES}
-        self.desc = abi.nf_layer_weights(*[self.t[k].data_ptr() for k in self.NAMES])
+        self.t = tensors if tensors is not None else {
+            k: bf16_tensor(host[k], device) for k in self.NAMES if k in host}
+        self.desc = abi.nf_layer_weights(*[self.t[k].data_ptr() if k in self.t else None for k in self.NAMES])
 
     @classmethod
     def from_int16(cls, t16: dict) -> "DeviceWeights":
         """From device int16 tensors holding bf16 bit patterns (no copy)."""
-        return cls(None, None, {k: t16[k].view(torch.bfloat16) for k in cls.NAMES})
+        return cls(None, None, {k: t16[k].view(torch.bfloat16) for k in cls.NAMES if k in t16})
 
     def host_bits(self) -> dict:
         return {k: bf16_bits(v) for k, v in self.t.items()}

@@ -271,7 +271,8 @@ def layer_forward(cfg, weights, x_bits, batch, k_pool, v_pool, storage: str = "b
 
     cfg     object with hidden, n_q, n_kv, head_dim, ffn, block_size, rms_eps, rope_base
     weights dict of bf16 bit arrays: g_attn [H], w_qkv [(n_q+2n_kv)d, H], w_o [H, n_q d],
-            g_ffn [H], w_gate_up [2F, H], w_down [H, F]
+            g_ffn [H], w_gate_up [2F, H], w_down [H, F]; for an MoE shape (cfg.n_experts = E
+            > 0) w_gate_up [E, 2F, H], w_down [E, H, F], w_router [E, H] (see moe_ffn)
     x_bits  bf16 bits [T, H]
     batch   object with decode_ctx, prefill_len, prefill_prefix, block_table, num_blocks
     k_pool  bf16 bits [num_blocks, n_kv, d/32, BS, 32]; v_pool bf16 bits [num_blocks, n_kv, d, BS]
@@ -282,7 +283,8 @@ def layer_forward(cfg, weights, x_bits, batch, k_pool, v_pool, storage: str = "b
             bfloat16 storage by definition.
 
     Returns a dict: y (float64 [T, H]), k_pool / v_pool (updated copies), the intermediates
-    h, q, k, v (after rotary), attn [T, n_q d], x1, h2, a, and flops (int).
+    h, q, k, v (after rotary), attn [T, n_q d], x1, h2, a (None for MoE), and flops (int);
+    MoE layers add moe_sel, moe_wts, moe_logits (see moe_ffn).
     """
     return _layer(cfg, weights, bf16_to_f64(x_bits), batch, k_pool, v_pool, storage)
 
@@ -310,12 +312,61 @@ def _layer(cfg, weights, x, batch, k_pool, v_pool, storage):
     attn = st(attention_all(cfg, batch, q, k_new, v_new).reshape(T, nq * d))
     x1 = st(x + linear(attn, W["w_o"]))
     h2 = st(rmsnorm(x1, W["g_ffn"], cfg.rms_eps))
-    a = st(swiglu(linear(h2, W["w_gate_up"]), F))
-    y = st(x1 + linear(a, W["w_down"]))
-    return {
+    out = {}
+    if getattr(cfg, "n_experts", 0):
+        ffn, out["moe_sel"], out["moe_wts"], out["moe_logits"] = moe_ffn(h2, W, cfg, st)
+        y = st(x1 + ffn)
+        a = None
+    else:
+        a = st(swiglu(linear(h2, W["w_gate_up"]), F))
+        y = st(x1 + linear(a, W["w_down"]))
+    out.update({
         "y": y, "k_pool": k_new, "v_pool": v_new, "h": h, "q": q, "k": k, "v": v,
         "attn": attn, "x1": x1, "h2": h2, "a": a, "flops": layer_flops(cfg, batch),
-    }
+    })
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# Mixture-of-experts FFN
+# --------------------------------------------------------------------------------------
+
+
+def moe_route(logits, top_k: int):
+    """The top_k experts of every token by router logit, largest first (equal logits: the
+    lower expert index first), and the softmax of the chosen logits.
+
+    The summary page ("MoE models") adds a gate-routing operation in front of an FFN whose
+    experts each compute on their own tokens; the routing rule itself (top-2 of the router
+    logits, softmax over the chosen two) is the Mixtral-style reading of that operation.
+    """
+    order = np.argsort(-logits, axis=1, kind="stable")[:, :top_k]
+    chosen = np.take_along_axis(logits, order, axis=1)
+    w = np.exp(chosen - chosen[:, :1])
+    return order, w / w.sum(axis=1, keepdims=True)
+
+
+def moe_ffn(h2, W, cfg, st):
+    """FFN of a mixture-of-experts layer on float64 h2 [T, H] with float64 weights W:
+    w_router [E, H], w_gate_up [E, 2F, H], w_down [E, H, F]. Every expert is a SwiGLU FFN
+    applied to the tokens routed to it (its rows of the grouped GEMM); the output of a token
+    is the routing-weighted sum of its experts' outputs. ``st`` stores the tensors handed
+    between operations (each expert's a and output) as for the dense FFN.
+
+    Returns (ffn [T, H], chosen experts [T, top_k], weights [T, top_k], logits [T, E]).
+    """
+    F = cfg.ffn
+    logits = linear(h2, W["w_router"])
+    sel, wts = moe_route(logits, cfg.top_k)
+    ffn = np.zeros_like(h2)
+    for e in range(cfg.n_experts):
+        tok, slot = np.nonzero(sel == e)
+        if tok.size == 0:
+            continue
+        a = st(swiglu(linear(h2[tok], W["w_gate_up"][e]), F))
+        o = st(linear(a, W["w_down"][e]))
+        np.add.at(ffn, tok, wts[tok, slot][:, None] * o)
+    return ffn, sel, wts, logits
 
 
 def stack_forward(cfg, layer_weights, x_bits, batch, k_pools, v_pools, storage: str = "bf16"):
@@ -361,14 +412,20 @@ def matmul_flops(m: int, n: int, k: int) -> int:
 
 
 def op_flops(cfg, n_tokens: int) -> dict:
-    """FLOPs of each projection of one layer at a dense batch of ``n_tokens`` rows."""
+    """FLOPs of each projection of one layer at a dense batch of ``n_tokens`` rows (an MoE
+    layer: the router, and Up/Gate/Down once per chosen expert of every token)."""
     H, nq, nkv, d, F = cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.ffn
-    return {
+    E = getattr(cfg, "n_experts", 0)
+    rows = n_tokens * (cfg.top_k if E else 1)
+    out = {
         "kqv": matmul_flops(n_tokens, (nq + 2 * nkv) * d, H),
         "o": matmul_flops(n_tokens, H, nq * d),
-        "ug": matmul_flops(n_tokens, 2 * F, H),
-        "down": matmul_flops(n_tokens, H, F),
+        "ug": matmul_flops(rows, 2 * F, H),
+        "down": matmul_flops(rows, H, F),
     }
+    if E:
+        out["router"] = matmul_flops(n_tokens, E, H)
+    return out
 
 
 def attention_flops(cfg, batch) -> int:

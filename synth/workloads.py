@@ -107,6 +107,7 @@ class Workload:
 
 
 TINY = Shape(hidden=256, n_q=4, n_kv=2, head_dim=64, ffn=688)
+TINY_MOE = Shape(hidden=256, n_q=4, n_kv=2, head_dim=64, ffn=256, n_experts=8, top_k=2)
 LLAMA3_8B = Shape(hidden=4096, n_q=32, n_kv=8, head_dim=128, ffn=14336)
 LLAMA3_8B_X32 = Shape(hidden=4096, n_q=32, n_kv=8, head_dim=128, ffn=14336, n_layers=32)
 LLAMA2_70B_TP8 = Shape(hidden=8192, n_q=8, n_kv=1, head_dim=128, ffn=3584)
@@ -118,6 +119,17 @@ WORKLOADS = {
         shape=TINY,
         n_tokens=78,
         description="tiny layer: 2 prefill x 32 + 14 decode, ctx U[16,128]",
+        prefill_fixed=(32, 32),
+        n_decode_fixed=14,
+        decode_ctx_range=(16, 128),
+        nano_sweep=(2,),
+        default_bounds=(0, 39, 78),
+    ),
+    "tiny_moe": Workload(
+        name="tiny_moe",
+        shape=TINY_MOE,
+        n_tokens=78,
+        description="tiny MoE layer (8 experts, top 2): 2 prefill x 32 + 14 decode, ctx U[16,128]",
         prefill_fixed=(32, 32),
         n_decode_fixed=14,
         decode_ctx_range=(16, 128),
@@ -319,6 +331,8 @@ def make_weights(shape: Shape, seed: int, *, gain_jitter: float = 0.0, layer: in
 
     ``w_qkv`` rows are [q (n_q*d) | k (n_kv*d) | v (n_kv*d)]; ``w_gate_up`` rows are
     [gate (F) | up (F)]. Norm gains are 1.0, or 1 + N(0, gain_jitter) when jittered.
+    MoE shapes: ``w_gate_up`` [E, 2F, H] and ``w_down`` [E, H, F] (one FFN per expert) and
+    ``w_router`` [E, H] ~ N(0, 1/H).
     """
     rng = _rng(seed * 1000 + layer, STREAM_WEIGHTS)
     H, F = shape.hidden, shape.ffn
@@ -338,8 +352,16 @@ def make_weights(shape: Shape, seed: int, *, gain_jitter: float = 0.0, layer: in
     out["w_qkv"] = w(shape.qkv_rows, H)
     out["w_o"] = w(H, shape.q_width)
     out["g_ffn"] = gain()
-    out["w_gate_up"] = w(2 * F, H)
-    out["w_down"] = w(H, F)
+    if shape.n_experts:
+        # per expert a SwiGLU FFN; router rows N(0, 1/H), so logits of a unit-RMS h2 are ~N(0, 1)
+        E = shape.n_experts
+        out["w_gate_up"] = np.stack([w(2 * F, H) for _ in range(E)])
+        out["w_down"] = np.stack([w(H, F) for _ in range(E)])
+        buf = rng.standard_normal((E, H), dtype=np.float32) * np.float32(1.0 / math.sqrt(H))
+        out["w_router"] = f32_to_bf16_bits(buf)
+    else:
+        out["w_gate_up"] = w(2 * F, H)
+        out["w_down"] = w(H, F)
     return out
 
 
@@ -462,16 +484,32 @@ def make_kv_pool_torch(shape: Shape, num_blocks: int, seed: int, layer: int = 0,
 # Counter-based weights (for many-layer stacks): bit-identical on host and device
 # --------------------------------------------------------------------------------------
 
-WEIGHT_NAMES = ("g_attn", "w_qkv", "w_o", "g_ffn", "w_gate_up", "w_down")
+WEIGHT_NAMES = ("g_attn", "w_qkv", "w_o", "g_ffn", "w_gate_up", "w_down", "w_router")
 
 
 def _weight_shapes(shape: Shape) -> dict:
-    H, F = shape.hidden, shape.ffn
-    return {"w_qkv": (shape.qkv_rows, H), "w_o": (H, shape.q_width), "w_gate_up": (2 * F, H), "w_down": (H, F)}
+    """(rows, cols) of each matrix; an MoE shape's expert matrices stack E of them."""
+    H, F, E = shape.hidden, shape.ffn, shape.n_experts
+    out = {"w_qkv": (shape.qkv_rows, H), "w_o": (H, shape.q_width)}
+    if E:
+        out.update({"w_gate_up": (E * 2 * F, H), "w_down": (E * H, F), "w_router": (E, H)})
+    else:
+        out.update({"w_gate_up": (2 * F, H), "w_down": (H, F)})
+    return out
 
 
-def _weight_scale() -> np.float32:
-    return np.float32(WEIGHT_STD / _IH_SD)
+def _weight_scale(shape: Shape = None, name: str = "") -> np.float32:
+    std = 1.0 / math.sqrt(shape.hidden) if name == "w_router" else WEIGHT_STD
+    return np.float32(std / _IH_SD)
+
+
+def _weight_dims(shape: Shape, name: str, n_rows: int, n_cols: int):
+    E = shape.n_experts
+    if E and name == "w_gate_up":
+        return (E, 2 * shape.ffn, n_cols)
+    if E and name == "w_down":
+        return (E, shape.hidden, n_cols)
+    return (n_rows, n_cols)
 
 
 def make_weights_counter(shape: Shape, seed: int, layer: int, rows=None, matrices=None) -> dict:
@@ -479,24 +517,30 @@ def make_weights_counter(shape: Shape, seed: int, layer: int, rows=None, matrice
 
     Every entry is a scaled sum of four uniform 16-bit integers drawn from a hash of
     (seed, layer, matrix, element index): mean 0, std WEIGHT_STD (an approximately normal
-    draw bounded at +-3.46 std), rounded to bf16. Gains are 1.0. ``rows`` (optional dict
-    name -> row indices) draws only those rows; ``matrices`` limits the names drawn.
+    draw bounded at +-3.46 std; the MoE router: std 1/sqrt(H)), rounded to bf16. Gains are
+    1.0. ``rows`` (optional dict name -> row indices of the flattened [rows, cols] matrix)
+    draws only those rows; ``matrices`` limits the names drawn.
     """
     out = {}
     H = shape.hidden
     one = f32_to_bf16_bits(np.ones(H, np.float32))
-    scale = _weight_scale()
+    shapes = _weight_shapes(shape)
     for name in matrices or WEIGHT_NAMES:
         if name in ("g_attn", "g_ffn"):
             out[name] = one.copy()
             continue
-        n_rows, n_cols = _weight_shapes(shape)[name]
+        if name not in shapes:
+            continue
+        scale = _weight_scale(shape, name)
+        n_rows, n_cols = shapes[name]
         r = np.arange(n_rows, dtype=np.int64) if rows is None or name not in rows else np.asarray(rows[name], np.int64)
         idx = (r[:, None] * n_cols + np.arange(n_cols, dtype=np.int64)[None, :]).astype(np.uint64)
         k1, k2 = _keys(seed, 1000 + layer, 10 + WEIGHT_NAMES.index(name))
         vals = _kv_f32_from_counter(idx, np.uint64(k1), np.uint64(k2), scale, np,
                                     lambda s: s.astype(np.int64).astype(np.float32))
         out[name] = f32_to_bf16_bits(vals).reshape(len(r), n_cols)
+        if rows is None or name not in rows:
+            out[name] = out[name].reshape(_weight_dims(shape, name, n_rows, n_cols))
     return out
 
 
@@ -506,12 +550,15 @@ def make_weights_counter_torch(shape: Shape, seed: int, layer: int, device="cpu"
 
     out = {}
     H = shape.hidden
-    scale = float(_weight_scale())
+    shapes = _weight_shapes(shape)
     for name in WEIGHT_NAMES:
         if name in ("g_attn", "g_ffn"):
             out[name] = torch.full((H,), 0x3F80, dtype=torch.int16, device=device)  # bf16 1.0
             continue
-        n_rows, n_cols = _weight_shapes(shape)[name]
+        if name not in shapes:
+            continue
+        scale = float(_weight_scale(shape, name))
+        n_rows, n_cols = shapes[name]
         n = n_rows * n_cols
         if n > 2**32:
             raise ValueError("matrix too large for the 32-bit element counter")
@@ -524,5 +571,5 @@ def make_weights_counter_torch(shape: Shape, seed: int, layer: int, device="cpu"
                                         torch, lambda s: s.to(torch.float32))
             dst[e0:e1].copy_(vals.to(torch.bfloat16).view(torch.int16))
             del idx, vals
-        out[name] = dst.view(n_rows, n_cols)
+        out[name] = dst.view(_weight_dims(shape, name, n_rows, n_cols))
     return out

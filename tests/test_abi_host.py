@@ -102,6 +102,19 @@ def test_batch_validation_error_codes(abi):
     assert _status(abi, b, b.num_blocks, cfg=bad) == abi.NF_E_UNSUPPORTED
 
 
+def test_moe_shape_validation(abi):
+    import dataclasses
+
+    b = sw.batch_from_lengths([20, 33], [17], [0], seed=1)
+    moe = sw.WORKLOADS["tiny_moe"].shape
+    assert _status(abi, b, b.num_blocks, cfg=abi.make_cfg(moe)) == abi.NF_OK
+    assert _status(abi, b, b.num_blocks, cfg=abi.make_cfg(sw.WORKLOADS["mixtral_8x7b_layer"].shape)) == abi.NF_OK
+    for bad in (dataclasses.replace(moe, n_experts=6), dataclasses.replace(moe, top_k=1),
+                dataclasses.replace(moe, ffn=264), dataclasses.replace(moe, n_experts=32)):
+        assert _status(abi, b, b.num_blocks, cfg=abi.make_cfg(bad)) == abi.NF_E_UNSUPPORTED, bad
+    assert _status(abi, b, b.num_blocks, cfg=abi.make_cfg(dataclasses.replace(moe, n_experts=-1))) == abi.NF_E_ARG
+
+
 def test_dependency_rule_pages_example(abi):
     """O1 on tokens 0-767 depends on Attn1 (0-767) but not on Attn2 (768-2048)."""
     ex = GOLDEN["intersection_dependency_example"]

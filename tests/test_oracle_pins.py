@@ -473,6 +473,100 @@ def test_stack_flops_are_layers_times_layer_flops():
     assert out["flops"] == 3 * (2 * b.n_tokens * params + attn)
 
 
+# ---- mixture-of-experts FFN --------------------------------------------------------------
+
+
+def test_moe_route_matches_brute_force_and_breaks_ties_low():
+    rng = np.random.default_rng(21)
+    logits = rng.standard_normal((60, 8))
+    logits[0] = [0.5, 2.0, 2.0, -1, 0, 2.0, 0, 0]  # three-way tie: experts 1 and 2 win, in that order
+    logits[1] = [1.0] * 8                           # all equal: experts 0 and 1, weights 1/2
+    sel, w = ol.moe_route(logits, 2)
+    for t in range(60):
+        ranked = sorted(range(8), key=lambda e: (-logits[t, e], e))[:2]
+        assert sel[t].tolist() == ranked
+        l0, l1 = logits[t, ranked[0]], logits[t, ranked[1]]
+        assert np.isclose(w[t, 0], 1.0 / (1.0 + np.exp(l1 - l0)), rtol=1e-14)
+        assert np.isclose(w[t].sum(), 1.0, rtol=1e-15)
+    assert sel[0].tolist() == [1, 2] and np.allclose(w[0], 0.5)
+    assert sel[1].tolist() == [0, 1] and np.allclose(w[1], 0.5)
+
+
+def _moe_inputs(seed=0):
+    wl = sw.WORKLOADS["tiny_moe"]
+    b = sw.make_batch("tiny_moe", seed)
+    w = sw.make_weights(wl.shape, seed, gain_jitter=0.1)
+    x = sw.make_x(wl.shape, b.n_tokens, seed)
+    kp, vp = sw.make_kv_pool(wl.shape, b.num_blocks, seed)
+    return wl.shape, b, w, x, kp, vp
+
+
+def test_moe_with_identical_experts_is_the_dense_ffn():
+    """Every expert the same FFN: the routing weights sum to one, so the layer is the dense
+    layer with that FFN."""
+    import dataclasses
+
+    shape, b, w, x, kp, vp = _moe_inputs(1)
+    same = dict(w)
+    same["w_gate_up"] = np.stack([w["w_gate_up"][3]] * shape.n_experts)
+    same["w_down"] = np.stack([w["w_down"][3]] * shape.n_experts)
+    dense_shape = dataclasses.replace(shape, n_experts=0, top_k=0)
+    dense_w = {k: v for k, v in w.items() if k != "w_router"}
+    dense_w["w_gate_up"], dense_w["w_down"] = w["w_gate_up"][3], w["w_down"][3]
+    moe = ol.layer_forward(shape, same, x, b, kp, vp, storage="exact")
+    dense = ol.layer_forward(dense_shape, dense_w, x, b, kp, vp, storage="exact")
+    assert np.allclose(moe["y"], dense["y"], rtol=1e-12, atol=1e-12)
+
+
+def test_moe_is_invariant_to_renumbering_experts():
+    shape, b, w, x, kp, vp = _moe_inputs(2)
+    perm = np.array([5, 2, 7, 0, 3, 6, 1, 4])
+    wp = dict(w)
+    for k in ("w_gate_up", "w_down", "w_router"):
+        wp[k] = w[k][perm]
+    for storage in ("exact", "bf16"):
+        a = ol.layer_forward(shape, w, x, b, kp, vp, storage=storage)
+        c = ol.layer_forward(shape, wp, x, b, kp, vp, storage=storage)
+        assert np.array_equal(a["y"], c["y"])
+        assert np.array_equal(perm[c["moe_sel"]], a["moe_sel"])
+
+
+def test_moe_token_output_depends_only_on_its_chosen_experts():
+    shape, b, w, x, kp, vp = _moe_inputs(3)
+    base = ol.layer_forward(shape, w, x, b, kp, vp)
+    e = 4
+    w2 = dict(w)
+    w2["w_down"] = w["w_down"].copy()
+    w2["w_down"][e] = sw.make_weights(shape, 99)["w_down"][e]
+    out = ol.layer_forward(shape, w2, x, b, kp, vp)
+    routed = (base["moe_sel"] == e).any(axis=1)
+    assert routed.any() and (~routed).any()
+    assert np.array_equal(out["y"][~routed], base["y"][~routed])
+    assert (out["y"][routed] != base["y"][routed]).any(axis=1).all()
+    # doubling expert e's down projection (exact in bf16) adds, to each token routed to e,
+    # its routing weight for e times that expert's output
+    w3 = dict(w)
+    w3["w_down"] = w["w_down"].copy()
+    w3["w_down"][e] = sw.f32_to_bf16_bits(2.0 * sw.bf16_bits_to_f32(w["w_down"][e]))
+    ex = ol.layer_forward(shape, w, x, b, kp, vp, storage="exact")
+    ex3 = ol.layer_forward(shape, w3, x, b, kp, vp, storage="exact")
+    tok, slot = np.nonzero(ex["moe_sel"] == e)
+    gu, down = ol.bf16_to_f64(w["w_gate_up"][e]), ol.bf16_to_f64(w["w_down"][e])
+    o = ol.linear(ol.swiglu(ol.linear(ex["h2"][tok], gu), shape.ffn), down)
+    assert np.allclose(ex3["y"][tok] - ex["y"][tok], ex["moe_wts"][tok, slot][:, None] * o, rtol=1e-9, atol=1e-12)
+
+
+def test_moe_flops_closed_form():
+    shape, b, w, x, kp, vp = _moe_inputs(4)
+    out = ol.layer_forward(shape, w, x, b, kp, vp)
+    H, F, d, nq, nkv, E = shape.hidden, shape.ffn, shape.head_dim, shape.n_q, shape.n_kv, shape.n_experts
+    T = b.n_tokens
+    attn = sum(4 * nq * d * (int(c) + 1) for c in b.decode_ctx) + sum(
+        4 * nq * d * int(L) * (int(L) + 1) // 2 for L in b.prefill_len)
+    want = 2 * T * (H * (nq + 2 * nkv) * d + nq * d * H) + 2 * T * 2 * 3 * H * F + 2 * T * E * H + attn
+    assert out["flops"] == want
+
+
 # ---- analytical cost model -----------------------------------------------------------
 
 from oracle import costmodel as cm  # noqa: E402

@@ -21,8 +21,18 @@ def test_counter_weights_host_and_torch_agree():
     shape = sw.WORKLOADS["tiny"].shape
     a = sw.make_weights_counter(shape, 3, 2)
     b = sw.make_weights_counter_torch(shape, 3, 2, chunk=1000)
-    for name in sw.WEIGHT_NAMES:
+    assert set(a) == set(b) == {"g_attn", "w_qkv", "w_o", "g_ffn", "w_gate_up", "w_down"}
+    for name in a:
         assert np.array_equal(a[name], b[name].numpy().view(np.uint16)), name
+    # an MoE shape: experts stacked, router rows with std 1/sqrt(H)
+    moe = sw.WORKLOADS["tiny_moe"].shape
+    am, bm = sw.make_weights_counter(moe, 3, 1), sw.make_weights_counter_torch(moe, 3, 1, chunk=5000)
+    assert am["w_gate_up"].shape == (8, 2 * moe.ffn, moe.hidden) and am["w_down"].shape == (8, moe.hidden, moe.ffn)
+    for name in am:
+        assert np.array_equal(am[name], bm[name].numpy().view(np.uint16)), name
+    r = sw.bf16_bits_to_f32(sw.make_weights_counter(sw.WORKLOADS["mixtral_8x7b_layer"].shape, 0, 0,
+                                                    matrices=("w_router",))["w_router"]).astype(np.float64)
+    assert abs(r.std() * np.sqrt(4096) - 1) < 0.02
     rows = sw.make_weights_counter(shape, 3, 2, rows={"w_o": [5, 7], "w_down": [0]}, matrices=("w_o", "w_down"))
     assert np.array_equal(rows["w_o"], a["w_o"][[5, 7]]) and np.array_equal(rows["w_down"], a["w_down"][[0]])
     assert set(rows) == {"w_o", "w_down"}
