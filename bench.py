@@ -98,7 +98,10 @@ def algorithmic(shape, b, n_nano):
     """Algorithmic FLOPs and bytes of one layer iteration (per-unit figures x units)."""
     H, nq, nkv, d, F = shape.hidden, shape.n_q, shape.n_kv, shape.head_dim, shape.ffn
     T = b.n_tokens
-    p_layer = H * (nq + 2 * nkv) * d + nq * d * H + 3 * H * F  # weight elements of the GEMMs
+    E, k = shape.n_experts, (shape.top_k if shape.n_experts else 1)
+    p_attn = H * (nq + 2 * nkv) * d + nq * d * H
+    # weight elements a token multiplies (MoE: its top_k experts and the router)
+    p_layer = p_attn + k * 3 * H * F + E * H
     gemm_flops = 2 * T * p_layer
     ctx = b.decode_ctx.astype(np.int64)
     kv_unit = 2 * nkv * d * 2  # bytes of K and V per key (all KV heads)
@@ -106,7 +109,7 @@ def algorithmic(shape, b, n_nano):
     decode_bytes = decode_keys * kv_unit + b.n_decode * (nq * d * 2) * 2  # KV stream + q in + o out
     pre = b.prefill_len.astype(np.int64)
     attn_flops = 4 * d * nq * (decode_keys + int((pre * (pre + 1) // 2).sum()))
-    weight_bytes = 2 * p_layer
+    weight_bytes = 2 * (p_attn + max(E, 1) * 3 * H * F + E * H)  # every weight read once
     act_bytes = T * H * 2 * 2 + T * 2 * nkv * d * 2  # x in, y out, new K/V written
     return {
         "gemm_flops": gemm_flops,
@@ -197,7 +200,7 @@ def main():
     x = sw.make_x(shape, T, args.seed)
     xd = bf16_tensor(x, "cuda")
     yd = torch.empty_like(xd)
-    if stack:
+    if stack or shape.n_experts:
         # every layer's weights (counter-based generator, drawn on the device) and KV pool
         w = None
         wds = [DeviceWeights.from_int16(sw.make_weights_counter_torch(shape, args.seed, l, device="cuda"))
@@ -313,11 +316,12 @@ def main():
     _, breakdown = run(plan, 5, 1, all_mask)
     for k, v in breakdown.items():
         v["avg_ms"] = v["total_ms"] / max(v["launches"], 1)
+    fan = shape.top_k if shape.n_experts else 1  # rows per token of the FFN products
     flops_by = {
         "gemm_kqv": 2 * T * shape.hidden * shape.qkv_rows,
         "gemm_o": 2 * T * shape.q_width * shape.hidden,
-        "gemm_ug_swiglu": 2 * T * shape.hidden * 2 * shape.ffn,
-        "gemm_down": 2 * T * shape.ffn * shape.hidden,
+        "gemm_ug_swiglu": 2 * fan * T * shape.hidden * 2 * shape.ffn,
+        "gemm_down": 2 * fan * T * shape.ffn * shape.hidden,
     }
     for k, f in flops_by.items():
         f *= n_layers
@@ -362,7 +366,7 @@ def main():
             vp = v16s[layer].index_select(0, idx).cpu().numpy().view(np.uint16)
             return kp, vp
 
-        if stack:
+        if w is None:  # device-drawn weights: the oracle reads host copies of the layers it runs
             n_cpu = max(1, min(args.cpu_layers, n_layers))
             ws_host = [wds[l].host_bits() for l in range(n_cpu)]
         else:

@@ -775,11 +775,12 @@ bool gemm_grouped_variant_ok(int variant, int n, int k, int epilogue) {
 }
 
 int gemm_grouped_default_variant(int n_rows, int n_groups, int epilogue) {
-  // 256-row tiles once the average group fills them (measured: fewer, larger tiles win when
-  // the rows per group allow); 128 rows otherwise
-  const bool tall = n_rows >= 256 * n_groups;
-  if (epilogue == EPI_SWIGLU) return tall ? 6 : 8;
-  return tall ? 7 : 9;
+  // measured on MI355X with 8 experts of the Mixtral shape: Up/Gate takes 256x256 tiles
+  // once the groups average 512 rows (2048 tokens, top 2), 128x256 below; Down always takes
+  // 128x128 (its long k loop wants the most tiles; each group's last, partly filled tile
+  // wastes less)
+  if (epilogue == EPI_SWIGLU) return n_rows >= 512 * n_groups ? 6 : 8;
+  return 9;
 }
 
 hipError_t launch_gemm_grouped(const bf16* A, const int32_t* a_rows, const bf16* B, long long b_stride, bf16* C,

@@ -173,23 +173,31 @@ bool build_decode_set(Err& E, const nf_layer_cfg& c, const nf_batch_desc& tmpl, 
 
 struct Scratch {
   Buf x, g, wqkv, wo, wgu, wd, h, qkv, attn, x1, h2, a, y, kpool, vpool, pos, slot, inv;
+  Buf wr, moe_out, moe_idx;  // MoE: router, grouped expert outputs, index arrays
 };
 
 bool alloc_dense(Err& E, const nf_layer_cfg& c, int max_t, Scratch& S, hipStream_t s) {
   const size_t H = c.hidden, F = c.ffn, W = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim,
                Q = (size_t)c.n_q_heads * c.head_dim, T = max_t;
+  const size_t E_ = c.n_experts > 0 ? (size_t)c.n_experts : 1, fan = c.n_experts > 0 ? 2 : 1;
   struct A {
     Buf* b;
     size_t n;
     float scale;
   } list[] = {{&S.x, T * H, 2.0f},      {&S.g, H, 1.0f},       {&S.wqkv, W * H, 0.03f}, {&S.wo, H * Q, 0.03f},
-              {&S.wgu, 2 * F * H, 0.03f}, {&S.wd, H * F, 0.03f}, {&S.h, T * H, 1.0f},     {&S.qkv, T * W, 1.0f},
-              {&S.attn, T * Q, 1.0f},    {&S.x1, T * H, 1.0f},  {&S.h2, T * H, 1.0f},    {&S.a, T * F, 1.0f},
+              {&S.wgu, E_ * 2 * F * H, 0.03f}, {&S.wd, E_ * H * F, 0.03f}, {&S.h, T * H, 1.0f}, {&S.qkv, T * W, 1.0f},
+              {&S.attn, T * Q, 1.0f},    {&S.x1, T * H, 1.0f},  {&S.h2, T * H, 1.0f},    {&S.a, fan * T * F, 1.0f},
               {&S.y, T * H, 1.0f}};
   uint32_t seed = 1;
   for (auto& e : list) {
     PF_HIP(e.b->alloc(e.n * 2));
     if (!fill(E, *e.b, e.n, seed++, e.scale, s)) return false;
+  }
+  if (c.n_experts > 0) {
+    PF_HIP(S.wr.alloc(E_ * H * 2));
+    if (!fill(E, S.wr, E_ * H, seed++, 0.05f, s)) return false;
+    PF_HIP(S.moe_out.alloc(2 * T * H * 2));
+    PF_HIP(S.moe_idx.alloc(16 * 2 * T + 8 * E_));
   }
   // a small pool and positions / slots for the rotary + KV append kernel
   const size_t blocks = T / kBlock + 1;
@@ -209,6 +217,29 @@ bool alloc_dense(Err& E, const nf_layer_cfg& c, int max_t, Scratch& S, hipStream
   PF_HIP(hipMemcpy(S.slot.p, slot.data(), T * 4, hipMemcpyHostToDevice));
   PF_HIP(hipMemcpy(S.inv.p, inv.data(), inv.size() * 4, hipMemcpyHostToDevice));
   return true;
+}
+
+// The MoE FFN of m tokens (router + dispatch, grouped Up/Gate, grouped Down, combine) on
+// the scratch buffers, default grouped tiles.
+hipError_t moe_ffn_op(const nf_layer_cfg& c, Scratch& S, int m, hipStream_t s) {
+  const int H = c.hidden, F = c.ffn, Ex = c.n_experts, rows = 2 * m;
+  char* b = static_cast<char*>(S.moe_idx.p);
+  const size_t n = (size_t)2 * m;
+  int32_t* sel = reinterpret_cast<int32_t*>(b);
+  float* wts = reinterpret_cast<float*>(b + 4 * n);
+  int32_t* pos = reinterpret_cast<int32_t*>(b + 8 * n);
+  int32_t* src = reinterpret_cast<int32_t*>(b + 12 * n);
+  int32_t* grp = reinterpret_cast<int32_t*>(b + 16 * n);
+  hipError_t e = launch_moe_route(S.h2.as<bf16>(), S.wr.as<bf16>(), 0, m, H, Ex, sel, wts, pos, src, grp, s);
+  if (e == hipSuccess)
+    e = launch_gemm_grouped(S.h2.as<bf16>(), src, S.wgu.as<bf16>(), (long long)2 * F * H, S.a.as<bf16>(), grp, Ex,
+                            rows, F, H, 2, gemm_grouped_default_variant(rows, Ex, 2), s);
+  if (e == hipSuccess)
+    e = launch_gemm_grouped(S.a.as<bf16>(), nullptr, S.wd.as<bf16>(), (long long)H * F, S.moe_out.as<bf16>(), grp, Ex,
+                            rows, H, F, 0, gemm_grouped_default_variant(rows, Ex, 0), s);
+  if (e == hipSuccess)
+    e = launch_moe_combine(S.x1.as<bf16>(), S.moe_out.as<bf16>(), pos, wts, S.y.as<bf16>(), 0, m, H, s);
+  return e;
 }
 
 // Best GEMM variant for (m, n, k, epi): returns ms and variant.
@@ -237,7 +268,7 @@ bool best_gemm(Err& E, hipStream_t s, const bf16* A, const bf16* B, bf16* C, con
 std::string cfg_json(const nf_layer_cfg& c) {
   std::ostringstream o;
   o << "{\"hidden\": " << c.hidden << ", \"n_q_heads\": " << c.n_q_heads << ", \"n_kv_heads\": " << c.n_kv_heads
-    << ", \"head_dim\": " << c.head_dim << ", \"ffn\": " << c.ffn << "}";
+    << ", \"head_dim\": " << c.head_dim << ", \"ffn\": " << c.ffn << ", \"n_experts\": " << c.n_experts << "}";
   return o.str();
 }
 
@@ -311,13 +342,19 @@ extern "C" nf_status nf_profile_ops(nf_ctx* ctx, const nf_layer_cfg* cfg, const 
       if (!best_gemm(E, s, S.attn.as<bf16>(), S.wo.as<bf16>(), S.x1.as<bf16>(), S.x.as<bf16>(), m, H, Q, 1, reps, to,
                      v2))
         return false;
-      double tug, tdown;
-      if (!best_gemm(E, s, S.h2.as<bf16>(), S.wgu.as<bf16>(), S.a.as<bf16>(), nullptr, m, F, H, 2, reps, tug, v3))
-        return false;
+      double tug, tdown = 0.0;
       int v4;
-      if (!best_gemm(E, s, S.a.as<bf16>(), S.wd.as<bf16>(), S.y.as<bf16>(), S.x1.as<bf16>(), m, H, F, 1, reps, tdown,
-                     v4))
-        return false;
+      if (c.n_experts > 0) {  // the MoE FFN as one nano-op (its tiles are chosen per call)
+        if (!time_ms(E, s, reps, [&] { return moe_ffn_op(c, S, m, s); }, tug)) return false;
+        v3 = gemm_grouped_default_variant(2 * m, c.n_experts, 2);
+        v4 = gemm_grouped_default_variant(2 * m, c.n_experts, 0);
+      } else {
+        if (!best_gemm(E, s, S.h2.as<bf16>(), S.wgu.as<bf16>(), S.a.as<bf16>(), nullptr, m, F, H, 2, reps, tug, v3))
+          return false;
+        if (!best_gemm(E, s, S.a.as<bf16>(), S.wd.as<bf16>(), S.y.as<bf16>(), S.x1.as<bf16>(), m, H, F, 1, reps, tdown,
+                       v4))
+          return false;
+      }
       tu = tn + tug + tdown;
       td = tn + tg + tr;
       const char* sep = m == step ? "" : ", ";
@@ -464,6 +501,7 @@ extern "C" nf_status nf_profile_interference(nf_ctx* ctx, const nf_layer_cfg* cf
     if (wsb) PF_HIP(gws.alloc(wsb));
     // compute op: one Up/Gate/Down nano-op; memory op: one decode attention nano-op
     auto gemm_op = [&](hipStream_t s) -> hipError_t {
+      if (c.n_experts > 0) return moe_ffn_op(c, S, m, s);
       hipError_t e = launch_gemm(S.h2.as<bf16>(), S.wgu.as<bf16>(), S.a.as<bf16>(), nullptr, m, F, H, 2, vug, s,
                                  gws.as<float>(), wsb);
       if (e != hipSuccess) return e;
@@ -497,7 +535,7 @@ extern "C" nf_status nf_profile_interference(nf_ctx* ctx, const nf_layer_cfg* cf
       snprintf(nm, sizeof nm, "mask_r%.3g", r_grid[i]);
       cfgs.push_back({nm, (double)r_grid[i], true, 0});
     }
-    o << "{\"device_cus\": 256, \"cfg\": " << cfg_json(c) << ", \"gemm_op\": \"Up/Gate+SwiGLU+Down, " << m
+    o << "{\"device_cus\": 256, \"cfg\": " << cfg_json(c) << ", \"gemm_op\": \"" << (c.n_experts > 0 ? "MoE FFN (router, grouped Up/Gate+SwiGLU, grouped Down, combine), " : "Up/Gate+SwiGLU+Down, ") << m
       << " rows\", \"mem_op\": \"decode attention, " << n_dec << " requests\", \"t_gemm_best_ms\": "
       << json::num(tg_best) << ", \"t_mem_best_ms\": " << json::num(tm_best) << ",\n \"configs\": [";
     bool first = true;
