@@ -208,6 +208,39 @@ nf_status nf_stack_dependencies(const nf_batch_desc *batch, const nf_plan *plan,
                                 int32_t *listing_out, int32_t *order_out, char *err_msg,
                                 size_t err_cap);
 
+/* ---- KV-cache offload and multi-round reload ---------------------------------------------- */
+
+/* Token ranges of requests in a pool, for moving their K/V between the pool and host memory
+ * (summary page, "KV-cache management and offloading"): request r's tokens at positions
+ * first[r] .. first[r] + n_tokens[r] - 1, addressed through row r of block_table as in
+ * nf_batch_desc. Host data is token-major: the ranges in request order, each token's K then
+ * V, each [n_kv][head_dim] bf16 (2 n_kv head_dim values, 4 KB for the 8B shape).          */
+typedef struct {
+  int32_t n_req;
+  const int32_t *first;       /* host [n_req], >= 0                                        */
+  const int32_t *n_tokens;    /* host [n_req], >= 0                                        */
+  const int32_t *block_table; /* host [n_req][max_blocks]                                  */
+  int32_t max_blocks;
+} nf_kv_ranges;
+
+/* Offload: copy the ranges' K/V from `pool` to host_dst (host, sum(n_tokens) x 2 n_kv
+ * head_dim bf16; pinned memory keeps the copy asynchronous): a gather kernel packs them
+ * token-major into a context buffer, then one device-to-host copy (copy engine) — the
+ * pages copy each token's KV out as it is produced, by the copy engine. host_dst is
+ * complete when `stream` passes the copy. The pool is not modified.
+ * Errors: NF_E_ARG, NF_E_BLOCK_RANGE, NF_E_BLOCK_TABLE_SHORT, NF_E_HIP.                   */
+nf_status nf_kv_offload(nf_ctx *ctx, const nf_layer_cfg *cfg, const nf_kv_pool *pool,
+                        const nf_kv_ranges *ranges, void *host_dst, void *stream);
+
+/* Reload (multi-round conversations): write host_src (the layout above) into the ranges'
+ * slots of `pool`, in two stages as the pages describe for paged KV: one contiguous
+ * host-to-device copy into a context buffer, then a scatter kernel that fills each (block,
+ * KV head) of the ranges. Only the ranges' slots change. host_src must stay valid until
+ * `stream` passes the copy. Errors: as nf_kv_offload, plus NF_E_SLOT_ALIAS when two tokens
+ * of the ranges map to one slot.                                                            */
+nf_status nf_kv_reload(nf_ctx *ctx, const nf_layer_cfg *cfg, nf_kv_pool *pool,
+                       const nf_kv_ranges *ranges, const void *host_src, void *stream);
+
 /* ---- the layer --------------------------------------------------------------------------- */
 
 /* One decoder-layer iteration. x_in, y_out: device [T][hidden] (may alias: every row is

@@ -68,6 +68,11 @@ class nf_plan(ctypes.Structure):
                 ("decode_max_workgroups", ctypes.c_int32)]
 
 
+class nf_kv_ranges(ctypes.Structure):
+    _fields_ = [("n_req", ctypes.c_int32), ("first", _i32p), ("n_tokens", _i32p), ("block_table", _i32p),
+                ("max_blocks", ctypes.c_int32)]
+
+
 class NanoflowError(RuntimeError):
     def __init__(self, status: int, message: str = ""):
         self.status = status
@@ -105,6 +110,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                  ctypes.POINTER(nf_batch_desc), ctypes.POINTER(nf_kv_pool), ctypes.POINTER(nf_plan),
                                  I, V]),
         "nf_debug_buffer": (I, [V, I, ctypes.POINTER(V), ctypes.POINTER(S)]),
+        "nf_kv_offload": (I, [V, ctypes.POINTER(nf_layer_cfg), ctypes.POINTER(nf_kv_pool),
+                              ctypes.POINTER(nf_kv_ranges), V, V]),
+        "nf_kv_reload": (I, [V, ctypes.POINTER(nf_layer_cfg), ctypes.POINTER(nf_kv_pool), ctypes.POINTER(nf_kv_ranges),
+                             V, V]),
         "nf_op_moe_ffn": (I, [V, ctypes.POINTER(nf_layer_cfg), ctypes.POINTER(nf_layer_weights), V, V, V, I, V, V, V]),
         "nf_op_gemm": (I, [V, V, V, V, V, I, I, I, I, I, V]),
         "nf_gemm_variants": (I, [_i32p, I, _i32p]),
@@ -343,6 +352,31 @@ def nf_debug_buffer(ctx, which: int):
 def nf_op_gemm(ctx, A: int, B: int, C: int, R: int | None, m: int, n: int, k: int, epilogue: int = 0,
                variant: int = -1, stream: int = 0) -> None:
     _check(load().nf_op_gemm(ctx, A, B, C, R, m, n, k, epilogue, variant, stream), ctx)
+
+
+class HostKvRanges:
+    """Host arrays behind an nf_kv_ranges (kept alive with it)."""
+
+    def __init__(self, first, n_tokens, block_table):
+        self.first = _i32(first)
+        self.n_tokens = _i32(n_tokens)
+        self.block_table = _i32(np.asarray(block_table).reshape(len(self.first), -1))
+        self.desc = nf_kv_ranges(len(self.first), _ptr(self.first), _ptr(self.n_tokens), _ptr(self.block_table),
+                                 self.block_table.shape[1])
+
+    @property
+    def n_rows(self) -> int:
+        return int(self.n_tokens.sum())
+
+
+def nf_kv_offload(ctx, cfg: nf_layer_cfg, pool: nf_kv_pool, ranges: HostKvRanges, host_dst: int, stream: int = 0):
+    _check(load().nf_kv_offload(ctx, ctypes.byref(cfg), ctypes.byref(pool), ctypes.byref(ranges.desc), host_dst,
+                                stream), ctx)
+
+
+def nf_kv_reload(ctx, cfg: nf_layer_cfg, pool: nf_kv_pool, ranges: HostKvRanges, host_src: int, stream: int = 0):
+    _check(load().nf_kv_reload(ctx, ctypes.byref(cfg), ctypes.byref(pool), ctypes.byref(ranges.desc), host_src,
+                               stream), ctx)
 
 
 def nf_op_moe_ffn(ctx, cfg: nf_layer_cfg, weights: nf_layer_weights, h2: int, x1: int, y: int, n_tokens: int,

@@ -409,6 +409,58 @@ nf_status build_stack_graph(const PlanGraph& g, int32_t n_layers, bool pipelined
   return NF_OK;
 }
 
+nf_status build_kv_moves(const nf_layer_cfg& cfg, const nf_kv_ranges& r, int32_t num_blocks, bool check_alias,
+                         std::vector<KvMoveItem>& items, int64_t& n_rows, std::string& err) {
+  const int32_t BS = cfg.block_size;
+  items.clear();
+  n_rows = 0;
+  if (r.n_req < 0 || (r.n_req > 0 && (!r.first || !r.n_tokens || !r.block_table || r.max_blocks <= 0))) {
+    err = "KV ranges: bad request count or null array";
+    return NF_E_ARG;
+  }
+  std::vector<uint8_t> used;
+  if (check_alias) used.assign((size_t)num_blocks * BS, 0);
+  for (int32_t q = 0; q < r.n_req; ++q) {
+    const int64_t p0 = r.first[q], n = r.n_tokens[q];
+    if (p0 < 0 || n < 0) {
+      err = fmt("KV range %ld: negative first or length", q);
+      return NF_E_ARG;
+    }
+    if (n == 0) continue;
+    if ((p0 + n + BS - 1) / BS > r.max_blocks) {
+      err = fmt("KV range %ld needs %ld blocks, table row holds %ld", q, (p0 + n + BS - 1) / BS, r.max_blocks);
+      return NF_E_BLOCK_TABLE_SHORT;
+    }
+    for (int64_t p = p0; p < p0 + n;) {
+      const int64_t lb = p / BS;
+      const int32_t blk = r.block_table[(size_t)q * r.max_blocks + lb];
+      if (blk < 0 || blk >= num_blocks) {
+        err = fmt("KV range %ld: block id %ld outside [0, %ld)", q, (int64_t)blk, (int64_t)num_blocks);
+        return NF_E_BLOCK_RANGE;
+      }
+      const int64_t end = std::min(p0 + n, (lb + 1) * BS);
+      KvMoveItem it{blk, (int32_t)(p % BS), (int32_t)(end - lb * BS), (int32_t)n_rows};
+      if (check_alias)
+        for (int32_t o = it.tok0; o < it.tok1; ++o) {
+          uint8_t& u = used[(size_t)blk * BS + o];
+          if (u) {
+            err = fmt("KV range %ld: slot %ld written twice", q, (int64_t)blk * BS + o);
+            return NF_E_SLOT_ALIAS;
+          }
+          u = 1;
+        }
+      items.push_back(it);
+      n_rows += end - p;
+      p = end;
+    }
+  }
+  if (n_rows > INT32_MAX) {
+    err = "KV ranges: too many tokens";
+    return NF_E_ARG;
+  }
+  return NF_OK;
+}
+
 // Chunk size (blocks) for the decode requests [r0, r1): the longest of 128, 64, 32, 16
 // blocks that still yields at least kMinUnits (request chunk, KV head) work units, so that
 // the waves fill the GPU several times over; long chunks have fewer start-ups and combines.

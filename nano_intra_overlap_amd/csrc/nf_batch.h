@@ -104,6 +104,16 @@ struct StackGraph {
 };
 nf_status build_stack_graph(const PlanGraph& g, int32_t n_layers, bool pipelined, StackGraph& s, std::string& err);
 
+// One (block, token run) of a KV move between a pool and token-major staging rows: slots
+// blk * 16 + [tok0, tok1) <-> staging rows row .. row + tok1 - tok0 - 1.
+struct KvMoveItem {
+  int32_t blk, tok0, tok1, row;
+};
+// Validate ranges against a pool of num_blocks blocks and list their moves; check_alias:
+// reject two tokens on one slot (NF_E_SLOT_ALIAS). n_rows: total tokens.
+nf_status build_kv_moves(const nf_layer_cfg& cfg, const nf_kv_ranges& r, int32_t num_blocks, bool check_alias,
+                         std::vector<KvMoveItem>& items, int64_t& n_rows, std::string& err);
+
 // Parent-operation dependency of the layer (does kind b consume a product of kind a?).
 bool parent_depends(int32_t a, int32_t b);
 

@@ -70,6 +70,11 @@ hipError_t launch_moe_route(const bf16* h2, const bf16* wr, int t_begin, int t_e
 hipError_t launch_moe_combine(const bf16* x1, const bf16* out, const int32_t* pos, const float* wts, bf16* y,
                               int t_begin, int t_end, int H, hipStream_t s);
 
+// Move the K/V of the listed (block, token run) items between a pool and token-major
+// staging rows (to_pool: staging -> pool). d in {64, 128}.
+hipError_t launch_kv_move(bool to_pool, bf16* kpool, bf16* vpool, bf16* stage, const KvMoveItem* items, int n_items,
+                          int n_kv, int d, hipStream_t s);
+
 hipError_t launch_rmsnorm(const bf16* x, const bf16* g, bf16* out, int m, int n, float eps,
                           hipStream_t s);
 

@@ -55,6 +55,7 @@ struct nf_ctx {
   // MoE FFN: per token entry (2 T) the chosen expert, weight, grouped row; per grouped row
   // its token; per nano-batch the expert group table; the grouped expert outputs
   DevBuf moe_idx, moe_out;
+  DevBuf kv_stage, kv_items;  // KV offload / reload: token-major staging rows, move items
   size_t moe_rows = 0;  // 2 T the MoE index arrays were laid out for
   uint64_t ws_gen = 0;  // bumped whenever a device buffer is reallocated
   // captured layer stack: its own metadata buffer, the key it was captured for
@@ -691,7 +692,8 @@ extern "C" void nf_ctx_destroy(nf_ctx* ctx) {
   if (ctx->graph_out) (void)hipEventDestroy(ctx->graph_out);
   if (ctx->upload_done) (void)hipEventDestroy(ctx->upload_done);
   for (DevBuf* b : {&ctx->h, &ctx->qkv, &ctx->attn, &ctx->x1, &ctx->h2, &ctx->a, &ctx->meta_dev, &ctx->part_o,
-                    &ctx->part_ml, &ctx->gemm_ws, &ctx->graph_meta, &ctx->moe_idx, &ctx->moe_out})
+                    &ctx->part_ml, &ctx->gemm_ws, &ctx->graph_meta, &ctx->moe_idx, &ctx->moe_out, &ctx->kv_stage,
+                    &ctx->kv_items})
     if (b->p) (void)hipFree(b->p);
   if (ctx->meta_host) (void)hipHostFree(ctx->meta_host);
   delete ctx;
@@ -1049,6 +1051,58 @@ extern "C" nf_status nf_op_moe_ffn(nf_ctx* ctx, const nf_layer_cfg* cfg, const n
   if (sel_out) NF_HIP(ctx, hipMemcpyAsync(sel_out, ix.sel, n * 4, hipMemcpyDeviceToDevice, s));
   if (wts_out) NF_HIP(ctx, hipMemcpyAsync(wts_out, ix.wts, n * 4, hipMemcpyDeviceToDevice, s));
   return NF_OK;
+}
+
+// KV offload / reload: validate on the host, upload the move items, then gather + copy out
+// or copy in + scatter, all on `stream`.
+static nf_status kv_move(nf_ctx* ctx, const nf_layer_cfg* cfg, const nf_kv_pool* pool, const nf_kv_ranges* ranges,
+                         bool reload, void* host, hipStream_t s) {
+  if (!ctx) return NF_E_ARG;
+  if (!cfg || !pool || !pool->k || !pool->v || !ranges || !host) {
+    ctx->err = "null argument";
+    return NF_E_ARG;
+  }
+  nf_status st = check_cfg(*cfg, ctx->err);
+  if (st != NF_OK) return st;
+  std::vector<KvMoveItem> items;
+  int64_t n_rows = 0;
+  if ((st = build_kv_moves(*cfg, *ranges, pool->num_blocks, reload, items, n_rows, ctx->err)) != NF_OK) return st;
+  if (items.empty()) return NF_OK;
+  const size_t row_bytes = (size_t)2 * cfg->n_kv_heads * cfg->head_dim * sizeof(uint16_t);
+  const size_t bytes = (size_t)n_rows * row_bytes, item_bytes = items.size() * sizeof(KvMoveItem);
+  if ((st = ensure(ctx, ctx->kv_stage, bytes)) != NF_OK) return st;
+  if ((st = ensure(ctx, ctx->kv_items, item_bytes)) != NF_OK) return st;
+  if ((st = ensure_host(ctx, item_bytes)) != NF_OK) return st;
+  if (ctx->upload_pending) {
+    NF_HIP(ctx, hipEventSynchronize(ctx->upload_done));  // staging buffer free again
+    ctx->upload_pending = false;
+  }
+  memcpy(ctx->meta_host, items.data(), item_bytes);
+  NF_HIP(ctx, hipMemcpyAsync(ctx->kv_items.p, ctx->meta_host, item_bytes, hipMemcpyHostToDevice, s));
+  NF_HIP(ctx, hipEventRecord(ctx->upload_done, s));
+  ctx->upload_pending = true;
+  bf16* stage = static_cast<bf16*>(ctx->kv_stage.p);
+  const KvMoveItem* d_items = static_cast<const KvMoveItem*>(ctx->kv_items.p);
+  bf16* kp = static_cast<bf16*>(pool->k);
+  bf16* vp = static_cast<bf16*>(pool->v);
+  if (reload) {
+    NF_HIP(ctx, hipMemcpyAsync(stage, host, bytes, hipMemcpyHostToDevice, s));
+    NF_HIP(ctx, launch_kv_move(true, kp, vp, stage, d_items, (int)items.size(), cfg->n_kv_heads, cfg->head_dim, s));
+  } else {
+    NF_HIP(ctx, launch_kv_move(false, kp, vp, stage, d_items, (int)items.size(), cfg->n_kv_heads, cfg->head_dim, s));
+    NF_HIP(ctx, hipMemcpyAsync(host, stage, bytes, hipMemcpyDeviceToHost, s));
+  }
+  return NF_OK;
+}
+
+extern "C" nf_status nf_kv_offload(nf_ctx* ctx, const nf_layer_cfg* cfg, const nf_kv_pool* pool,
+                                   const nf_kv_ranges* ranges, void* host_dst, void* stream) {
+  return kv_move(ctx, cfg, pool, ranges, false, host_dst, static_cast<hipStream_t>(stream));
+}
+
+extern "C" nf_status nf_kv_reload(nf_ctx* ctx, const nf_layer_cfg* cfg, nf_kv_pool* pool, const nf_kv_ranges* ranges,
+                                  const void* host_src, void* stream) {
+  return kv_move(ctx, cfg, pool, ranges, true, const_cast<void*>(host_src), static_cast<hipStream_t>(stream));
 }
 
 extern "C" nf_status nf_ctx_set_timing(nf_ctx* ctx, uint32_t class_mask) {

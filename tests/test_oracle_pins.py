@@ -567,6 +567,47 @@ def test_moe_flops_closed_form():
     assert out["flops"] == want
 
 
+# ---- KV offload / reload ------------------------------------------------------------------
+
+
+def test_kv_offload_is_the_attention_history_of_the_request():
+    """Offloading a request's positions 0..n-1 yields, in order, exactly the keys and values
+    attention gathers for it."""
+    from oracle import kvio
+
+    shape, b, w, x, kp, vp = _tiny_inputs(7)
+    for r in (0, 3, b.n_requests - 1):
+        n = int(b.cached_lens()[r])
+        rows = kvio.offload(kp, vp, [0], [n], b.block_table[r:r + 1])
+        keys, vals = ol.gather_kv(kp, vp, b, 16, r, n)
+        assert np.array_equal(ol.bf16_to_f64(rows[:, 0]), keys)
+        assert np.array_equal(ol.bf16_to_f64(rows[:, 1]), vals)
+
+
+def test_kv_reload_round_trip_into_other_blocks():
+    """A request's KV offloaded from one set of pages and reloaded into another (as for a
+    follow-up round) reads back identically; every other slot of the new pool is untouched."""
+    from oracle import kvio
+
+    shape = sw.WORKLOADS["tiny"].shape
+    kp, vp = sw.make_kv_pool(shape, 12, 1)
+    kq, vq = sw.make_kv_pool(shape, 12, 2)
+    t_a = np.array([[3, 7, 1, 9]])
+    t_b = np.array([[10, 0, 5, 2]])
+    rows = kvio.offload(kp, vp, [5], [50], t_a)
+    k2, v2 = kvio.reload(kq, vq, [5], [50], t_b, rows)
+    assert np.array_equal(kvio.offload(k2, v2, [5], [50], t_b), rows)
+    moved = set(kvio.range_slots([5], [50], t_b))
+    kt2, ktq = ol.k_tokens(k2), ol.k_tokens(kq)
+    for blk in range(12):
+        for off in range(16):
+            if (blk, off) not in moved:
+                assert np.array_equal(kt2[blk, :, off], ktq[blk, :, off])
+                assert np.array_equal(v2[blk, :, :, off], vq[blk, :, :, off])
+    with pytest.raises(ValueError):
+        kvio.reload(kq, vq, [0, 0], [4, 4], np.array([[1], [1]]), np.zeros((8, 2, 2, 64), np.uint16))
+
+
 # ---- analytical cost model -----------------------------------------------------------
 
 from oracle import costmodel as cm  # noqa: E402
