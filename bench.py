@@ -62,6 +62,8 @@ def parse():
                    help="layer stacks: issue layer by layer instead of cross-layer pipelining")
     p.add_argument("--cpu-layers", type=int, default=2,
                    help="layer stacks: layers the CPU oracle runs on its sample (its time is scaled to all layers)")
+    p.add_argument("--kv-io", action="store_true",
+                   help="also measure KV offload / multi-round reload (adds a kv_io object to the JSON line)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="run one plain device copy of this many MiB first (a known-size reference for "
                         "hardware traffic counters)")
@@ -171,6 +173,96 @@ def cpu_baseline(shape, b, ws, x, seed, n_dec, fetch_blocks, n_layers_total=1):
         "sample": f"{what}: {len(rows)} tokens ({b.n_prefill} prefill chunk(s), {int(b.prefill_len.sum())} "
                   f"tokens), {len(used)} KV blocks; {layers} "
                   f"({os.cpu_count()} host CPUs, {threads} BLAS threads)",
+    }
+
+
+def kv_io_probe(abi, torch, ctx, cfg, shape, b, step, stream, n_conv=16, conv_len=2048, steps=10):
+    """KV movement measured on its own and beside the layer (summary page, "KV-cache
+    management and offloading").
+
+    reload: n_conv conversations of conv_len tokens each, from pinned host rows into a pool
+    of their own (shuffled pages): the library's two-stage path (one contiguous copy in +
+    the scatter kernel), a plain contiguous host-to-device copy of the same bytes, and
+    per-page copies (one 4-KB copy per (block, KV head) of K and of V, issued from Python,
+    first 2048 pieces) as the naive path the pages compare against.
+    offload: the batch's new tokens (one row each) copied out after every layer step, on a
+    second stream beside the next step, against steps without it."""
+    from nano_intra_overlap_amd.device import DevicePool
+
+    row_bytes = 2 * shape.n_kv * shape.head_dim * 2
+    n_tok = n_conv * conv_len
+    nb = n_tok // 16
+    rng = np.random.default_rng(5)
+    table = rng.permutation(nb).astype(np.int32).reshape(n_conv, conv_len // 16)
+    ranges = abi.HostKvRanges([0] * n_conv, [conv_len] * n_conv, table)
+    k = torch.empty((nb, shape.n_kv, shape.head_dim // 32, 16, 32), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty((nb, shape.n_kv, shape.head_dim, 16), dtype=torch.bfloat16, device="cuda")
+    pool = DevicePool(k, v)
+    host = torch.empty(n_tok * row_bytes // 2, dtype=torch.int16, pin_memory=True)
+    host.numpy()[:] = rng.integers(-2000, 2000, host.shape[0], dtype=np.int16)
+    dev = torch.empty(n_tok * row_bytes // 2, dtype=torch.int16, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    nbytes = n_tok * row_bytes
+    t_reload = timed(lambda: abi.nf_kv_reload(ctx, cfg, pool.desc, ranges, host.data_ptr(), stream))
+    t_h2d = timed(lambda: dev.copy_(host, non_blocking=True))
+    t_off = timed(lambda: abi.nf_kv_offload(ctx, cfg, pool.desc, ranges, host.data_ptr(), stream))
+    # naive: one copy per (block, KV head) piece of K and of V, straight into the pages
+    import ctypes
+
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpyAsync.restype = ctypes.c_int
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    piece = 16 * shape.head_dim * 2
+    n_pieces = 2048
+
+    def naive():
+        base_k, base_v, src = k.data_ptr(), v.data_ptr(), host.data_ptr()
+        for i in range(n_pieces // 2):
+            blk, g = divmod(i, shape.n_kv)
+            off = (blk * shape.n_kv + g) * piece
+            hip.hipMemcpyAsync(base_k + off, src + 2 * i * piece, piece, 1, ctypes.c_void_p(stream))
+            hip.hipMemcpyAsync(base_v + off, src + (2 * i + 1) * piece, piece, 1, ctypes.c_void_p(stream))
+
+    t_naive = timed(naive, reps=3)
+    # offload of every new token beside the layer
+    new = abi.HostKvRanges(np.concatenate([b.decode_ctx, b.prefill_prefix]),
+                           np.concatenate([np.ones(b.n_decode, np.int32), b.prefill_len]), b.block_table)
+    out = torch.empty(new.n_rows * row_bytes // 2, dtype=torch.int16, pin_memory=True)
+    side = torch.cuda.Stream()
+    done = torch.cuda.Event()
+
+    def step_with_offload():
+        step()
+        done.record()
+        side.wait_event(done)
+        abi.nf_kv_offload(ctx, cfg, step.pool_desc, new, out.data_ptr(), side.cuda_stream)
+
+    t_plain = timed(step, reps=steps)
+    t_with = timed(step_with_offload, reps=steps)
+    torch.cuda.synchronize()
+    return {
+        "reload": {"conversations": n_conv, "tokens": n_tok, "bytes": nbytes, "ms": round(t_reload, 4),
+                   "GB_per_s": round(nbytes / t_reload / 1e6, 1)},
+        "contiguous_h2d": {"ms": round(t_h2d, 4), "GB_per_s": round(nbytes / t_h2d / 1e6, 1)},
+        "scatter_share_ms": round(t_reload - t_h2d, 4),
+        "naive_page_copies": {"pieces": n_pieces, "bytes_each": piece, "ms": round(t_naive, 4),
+                              "GB_per_s": round(n_pieces * piece / t_naive / 1e6, 2),
+                              "note": "one hipMemcpyAsync per (block, KV head) piece, issued from Python"},
+        "offload_all": {"ms": round(t_off, 4), "GB_per_s": round(nbytes / t_off / 1e6, 1)},
+        "layer_step_ms": round(t_plain, 4),
+        "layer_step_with_offload_ms": round(t_with, 4),
+        "offload_rows_per_step": new.n_rows,
     }
 
 
@@ -357,6 +449,14 @@ def main():
     mfma_frac = step_gemm_flops / (ms * 1e-3) / PEAK_BF16
     t_lb = n_layers * max(alg["gemm_flops"] / PEAK_BF16, alg["layer_bytes"] / PEAK_HBM)
 
+    kv_io = None
+    if args.kv_io and not stack:
+        def one_step():
+            abi.nf_layer_forward(ctx, cfg, w_descs[0], xd.data_ptr(), yd.data_ptr(), hb, p_descs[0], plan, stream)
+        one_step.pool_desc = p_descs[0]
+        kv_io = kv_io_probe(abi, torch, ctx, cfg, shape, b, one_step, stream, steps=args.steps)
+        log(f"kv io: {kv_io}")
+
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
@@ -425,6 +525,7 @@ def main():
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in breakdown.items()},
         "cpu_baseline": cpu,
+        "kv_io": kv_io,
     }
     abi.nf_ctx_destroy(ctx)
     print(json.dumps(out))

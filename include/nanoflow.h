@@ -227,7 +227,10 @@ typedef struct {
  * head_dim bf16; pinned memory keeps the copy asynchronous): a gather kernel packs them
  * token-major into a context buffer, then one device-to-host copy (copy engine) — the
  * pages copy each token's KV out as it is produced, by the copy engine. host_dst is
- * complete when `stream` passes the copy. The pool is not modified.
+ * complete when `stream` passes the copy. The pool is not modified. KV moves use buffers of
+ * their own in the context: they may run on another stream than the context's layer calls
+ * (e.g. beside the next layer, as the pages schedule their copies), but KV moves of one
+ * context must be ordered among themselves.
  * Errors: NF_E_ARG, NF_E_BLOCK_RANGE, NF_E_BLOCK_TABLE_SHORT, NF_E_HIP.                   */
 nf_status nf_kv_offload(nf_ctx *ctx, const nf_layer_cfg *cfg, const nf_kv_pool *pool,
                         const nf_kv_ranges *ranges, void *host_dst, void *stream);

@@ -56,6 +56,10 @@ struct nf_ctx {
   // its token; per nano-batch the expert group table; the grouped expert outputs
   DevBuf moe_idx, moe_out;
   DevBuf kv_stage, kv_items;  // KV offload / reload: token-major staging rows, move items
+  void* kv_host = nullptr;     // pinned staging of the move items (their own, so that KV
+  size_t kv_host_cap = 0;      // moves on another stream never wait for a layer's upload)
+  hipEvent_t kv_upload_done = nullptr;
+  bool kv_upload_pending = false;
   size_t moe_rows = 0;  // 2 T the MoE index arrays were laid out for
   uint64_t ws_gen = 0;  // bumped whenever a device buffer is reallocated
   // captured layer stack: its own metadata buffer, the key it was captured for
@@ -696,6 +700,8 @@ extern "C" void nf_ctx_destroy(nf_ctx* ctx) {
                     &ctx->kv_items})
     if (b->p) (void)hipFree(b->p);
   if (ctx->meta_host) (void)hipHostFree(ctx->meta_host);
+  if (ctx->kv_host) (void)hipHostFree(ctx->kv_host);
+  if (ctx->kv_upload_done) (void)hipEventDestroy(ctx->kv_upload_done);
   delete ctx;
 }
 
@@ -1072,15 +1078,22 @@ static nf_status kv_move(nf_ctx* ctx, const nf_layer_cfg* cfg, const nf_kv_pool*
   const size_t bytes = (size_t)n_rows * row_bytes, item_bytes = items.size() * sizeof(KvMoveItem);
   if ((st = ensure(ctx, ctx->kv_stage, bytes)) != NF_OK) return st;
   if ((st = ensure(ctx, ctx->kv_items, item_bytes)) != NF_OK) return st;
-  if ((st = ensure_host(ctx, item_bytes)) != NF_OK) return st;
-  if (ctx->upload_pending) {
-    NF_HIP(ctx, hipEventSynchronize(ctx->upload_done));  // staging buffer free again
-    ctx->upload_pending = false;
+  if (!ctx->kv_upload_done) NF_HIP(ctx, hipEventCreateWithFlags(&ctx->kv_upload_done, hipEventDisableTiming));
+  if (ctx->kv_upload_pending) {
+    NF_HIP(ctx, hipEventSynchronize(ctx->kv_upload_done));  // item staging free again
+    ctx->kv_upload_pending = false;
   }
-  memcpy(ctx->meta_host, items.data(), item_bytes);
-  NF_HIP(ctx, hipMemcpyAsync(ctx->kv_items.p, ctx->meta_host, item_bytes, hipMemcpyHostToDevice, s));
-  NF_HIP(ctx, hipEventRecord(ctx->upload_done, s));
-  ctx->upload_pending = true;
+  if (ctx->kv_host_cap < item_bytes) {
+    if (ctx->kv_host) NF_HIP(ctx, hipHostFree(ctx->kv_host));
+    ctx->kv_host = nullptr;
+    const size_t cap = align_up(item_bytes, 1 << 16);
+    NF_HIP(ctx, hipHostMalloc(&ctx->kv_host, cap, hipHostMallocDefault));
+    ctx->kv_host_cap = cap;
+  }
+  memcpy(ctx->kv_host, items.data(), item_bytes);
+  NF_HIP(ctx, hipMemcpyAsync(ctx->kv_items.p, ctx->kv_host, item_bytes, hipMemcpyHostToDevice, s));
+  NF_HIP(ctx, hipEventRecord(ctx->kv_upload_done, s));
+  ctx->kv_upload_pending = true;
   bf16* stage = static_cast<bf16*>(ctx->kv_stage.p);
   const KvMoveItem* d_items = static_cast<const KvMoveItem*>(ctx->kv_items.p);
   bf16* kp = static_cast<bf16*>(pool->k);
