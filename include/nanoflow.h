@@ -297,9 +297,11 @@ nf_status nf_debug_buffer(nf_ctx *ctx, int32_t which, void **ptr, size_t *bytes)
  * NF_E_UNSUPPORTED, NF_E_HIP.                                                               */
 nf_status nf_op_gemm(nf_ctx *ctx, const void *A, const void *B, void *C, const void *R, int32_t m,
                      int32_t n, int32_t k, int32_t epilogue, int32_t variant, void *stream);
-/* Number of GEMM tile configurations and, for index i, its tile (bm, bn), k step and number
- * of K slices (split-K, 1 = none; not available with the SwiGLU epilogue) into out4. */
-nf_status nf_gemm_variants(int32_t *count, int32_t index, int32_t *out4);
+/* Number of GEMM tile configurations and, for index i, into out5: its tile (bm, bn), k
+ * step, number of K slices (split-K, 1 = none; not with the SwiGLU epilogue) and waves per
+ * workgroup (the SwiGLU epilogue needs each wave's bn / (waves / 2) columns to be a
+ * multiple of 64). */
+nf_status nf_gemm_variants(int32_t *count, int32_t index, int32_t *out5);
 
 /* out[r][:] = x[r] / sqrt(mean(x[r]^2) + eps) * g, rows r in [0, m), width n (mult. of 8). */
 nf_status nf_op_rmsnorm(nf_ctx *ctx, const void *x, const void *g, void *out, int32_t m, int32_t n,

@@ -391,7 +391,7 @@ def nf_gemm_variants():
     _check(lib.nf_gemm_variants(ctypes.byref(cnt), 0, None))
     out = []
     for i in range(cnt.value):
-        t = (ctypes.c_int32 * 4)()
+        t = (ctypes.c_int32 * 5)()
         _check(lib.nf_gemm_variants(None, i, t))
         out.append(tuple(t))
     return out

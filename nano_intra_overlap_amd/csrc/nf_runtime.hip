@@ -926,15 +926,16 @@ extern "C" nf_status nf_debug_buffer(nf_ctx* ctx, int32_t which, void** ptr, siz
   return NF_OK;
 }
 
-extern "C" nf_status nf_gemm_variants(int32_t* count, int32_t index, int32_t* out4) {
+extern "C" nf_status nf_gemm_variants(int32_t* count, int32_t index, int32_t* out5) {
   if (count) *count = gemm_variant_count();
-  if (out4) {
+  if (out5) {
     if (index < 0 || index >= gemm_variant_count()) return NF_E_ARG;
     const GemmVariant v = gemm_variant(index);
-    out4[0] = v.bm;
-    out4[1] = v.bn;
-    out4[2] = v.bk;
-    out4[3] = v.ks;
+    out5[0] = v.bm;
+    out5[1] = v.bn;
+    out5[2] = v.bk;
+    out5[3] = v.ks;
+    out5[4] = v.waves;
   }
   return NF_OK;
 }

@@ -45,8 +45,8 @@ LAYER_GEMMS = [(1024, 6144, 4096, 0), (2048, 4096, 4096, 1), (1536, 14336, 4096,
                (1024, 8192, 1024, 1)]
 
 
-def _supported(v, k, epi, bn, ks=1):
-    return (not (epi == 2 and bn < 128) and not (v >= 6 and k % 32)
+def _supported(v, k, epi, bn, ks=1, waves=4):
+    return (not (epi == 2 and (bn < 128 or (bn // (waves // 2)) % 64)) and not (v >= 6 and k % 32)
             and not (ks > 1 and (epi == 2 or k % (32 * ks))))
 
 
@@ -65,8 +65,8 @@ def test_gemm_all_variants(ctx, m, n, k, epi):
     if epi == 2:
         ref = ol.swiglu(ref, n)
     dA, dB, dR = _dev(A), _dev(B), _dev(R)
-    for v, (bm, bn, bk, ks) in enumerate(abi.nf_gemm_variants()):
-        if not _supported(v, k, epi, bn, ks):
+    for v, (bm, bn, bk, ks, waves) in enumerate(abi.nf_gemm_variants()):
+        if not _supported(v, k, epi, bn, ks, waves):
             continue
         dC = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
         log_case(f"gemm m={m} n={n} k={k} epi={epi} variant={v}")
@@ -94,8 +94,8 @@ def test_gemm_layer_shapes_sampled_rows(ctx, m, n, k, epi):
     if epi == 2:
         ref = ol.swiglu(ref, n)
     dA, dB, dR = _dev(A), _dev(B), _dev(R)
-    for v, (bm, bn, bk, ks) in [(-1, (0, 0, 0, 1))] + list(enumerate(abi.nf_gemm_variants())):
-        if v >= 0 and (not _supported(v, k, epi, bn, ks) or v < 6):
+    for v, (bm, bn, bk, ks, waves) in [(-1, (0, 0, 0, 1, 4))] + list(enumerate(abi.nf_gemm_variants())):
+        if v >= 0 and (not _supported(v, k, epi, bn, ks, waves) or v < 6):
             continue
         dC = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
         log_case(f"gemm layer shape m={m} n={n} k={k} epi={epi} variant={v}")
@@ -108,7 +108,7 @@ def test_gemm_layer_shapes_sampled_rows(ctx, m, n, k, epi):
         assert err <= TOL, f"variant {v}: rel err {err}"
 
 
-@pytest.mark.parametrize("variant", [-1, 6, 7, 9, 10, 11])
+@pytest.mark.parametrize("variant", [-1, 6, 7, 9, 10, 11, 12, 13])
 def test_gemm_residual_in_place(ctx, variant):
     from nano_intra_overlap_amd import abi
 
