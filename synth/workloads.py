@@ -156,6 +156,16 @@ WORKLOADS = {
         nano_sweep=(1, 2, 4),
         extra={"layer_workload": "llama3_8b_layer"},
     ),
+    "llama3_8b_longctx_layer": Workload(
+        name="llama3_8b_longctx_layer",
+        shape=LLAMA3_8B,
+        n_tokens=2048,
+        description="LLaMA-3-8B-shaped layer, 2048-token batch with long decode contexts: 1 lognormal "
+        "prefill chunk (median 512, cap 1024) + decode ctx U[4096,16384] (attention-dominated)",
+        prefill_lognormal=(512, 0.5, 1024),
+        decode_ctx_range=(4096, 16384),
+        nano_sweep=(1, 2, 4),
+    ),
     "llama2_70b_tp8_layer": Workload(
         name="llama2_70b_tp8_layer",
         shape=LLAMA2_70B_TP8,
@@ -406,8 +416,13 @@ def _mix32(x, xp):
 
 
 def _kv_f32_from_counter(counter, k1: int, k2: int, scale: float, xp, to_f32):
-    h1 = _mix32(counter ^ k1, xp)
-    h2 = _mix32(counter ^ k2, xp)
+    # counters past 2^32: the high word is mixed into the keys (a high word of 0 leaves
+    # them as they are, so smaller pools keep their values)
+    hi = counter >> 32
+    lo = counter & _M32
+    mh = _mix32(hi, xp)
+    h1 = _mix32(lo ^ (k1 ^ mh), xp)
+    h2 = _mix32(lo ^ (k2 ^ mh), xp)
     s = (h1 & 0xFFFF) + (h1 >> 16) + (h2 & 0xFFFF) + (h2 >> 16)  # in [0, 262140]
     return (to_f32(s) - 131070.0) * scale  # both steps exact or single-rounded in fp32
 
@@ -426,8 +441,6 @@ def make_kv_pool_blocks(shape: Shape, blocks, seed: int, layer: int = 0):
     blocks = np.asarray(blocks, dtype=np.int64).reshape(-1)
     G, BS, D = shape.n_kv, shape.block_size, shape.head_dim
     per_block = G * BS * D
-    if (blocks.max(initial=0) + 1) * per_block > 2**32:
-        raise ValueError("KV pool too large for the 32-bit element counter")
     idx = (blocks[:, None] * per_block + np.arange(per_block, dtype=np.int64)[None, :]).astype(np.uint64)
     scale = _kv_scale(shape)
     out = []
@@ -458,8 +471,6 @@ def make_kv_pool_torch(shape: Shape, num_blocks: int, seed: int, layer: int = 0,
 
     G, BS, D = shape.n_kv, shape.block_size, shape.head_dim
     per_block = G * BS * D
-    if num_blocks * per_block > 2**32:
-        raise ValueError("KV pool too large for the 32-bit element counter")
     ch = _k_chunk(D)
     K = torch.empty((num_blocks, G, D // ch, BS, ch), dtype=torch.int16, device=device)
     V = torch.empty((num_blocks, G, D, BS), dtype=torch.int16, device=device)

@@ -49,3 +49,23 @@ def test_counter_weights_statistics_and_independence():
     assert abs(np.corrcoef(f.ravel(), other.ravel())[0, 1]) < 0.01  # layers draw independently
     q = sw.bf16_bits_to_f32(w["w_qkv"]).astype(np.float64).ravel()
     assert abs(np.corrcoef(q[:-1], q[1:])[0, 1]) < 0.02  # neighbouring entries independent
+
+
+def test_counter_generator_past_2_pow_32_matches_between_host_and_torch():
+    """Pools of more than 2^32 elements (the long-context workload) keep one value per
+    element, the same through numpy and torch; below 2^32 nothing changes."""
+    import torch
+
+    k1, k2 = sw._keys(3, 1, 0)
+    scale = float(sw._kv_scale(sw.WORKLOADS["llama3_8b_layer"].shape))
+    idx = np.concatenate([np.arange(0, 64), np.arange(2**32 - 64, 2**32 + 64), np.arange(2**33 + 5, 2**33 + 69)])
+    host = sw._kv_f32_from_counter(idx.astype(np.uint64), np.uint64(k1), np.uint64(k2), np.float32(scale), np,
+                                   lambda s: s.astype(np.int64).astype(np.float32))
+    dev = sw._kv_f32_from_counter(torch.from_numpy(idx.astype(np.int64)), k1, k2,
+                                  torch.tensor(scale, dtype=torch.float32), torch, lambda s: s.to(torch.float32))
+    assert np.array_equal(host, dev.numpy())
+    # elements 2^32 apart differ (the high word reaches the hash)
+    lo = host[:64]
+    wrapped = sw._kv_f32_from_counter((idx[:64] + 2**32).astype(np.uint64), np.uint64(k1), np.uint64(k2),
+                                      np.float32(scale), np, lambda s: s.astype(np.int64).astype(np.float32))
+    assert (lo != wrapped).mean() > 0.9
