@@ -516,6 +516,13 @@ void build_work(const BatchLayout& L, const PlanGraph& g, int split, int n_kv, M
           M.n_parts += nch;
         }
       }
+      // Longest runs first: workgroups are dispatched in item order as slots free up, so
+      // the last ones to start are the shortest and the grid drains evenly (a request of
+      // 2048 keys started last would stream alone for a tenth of the kernel). Each item
+      // writes its own output row or partial slot, so the order changes no result.
+      std::stable_sort(M.dec.begin() + M.dec_begin[j], M.dec.end(), [](const DecodeItem& a, const DecodeItem& b) {
+        return a.blk_end - a.blk_begin > b.blk_end - b.blk_begin;
+      });
     }
     M.pf_begin[j] = (int32_t)M.pf.size();
     if (pf_op[j]) {
