@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--decode-ring", type=int, default=2, choices=[2, 3, 4],
                    help="decode attention register ring depth (ring - 1 groups of KV blocks in flight)")
     p.add_argument("--gemm-variant", type=int, default=-1, help="force one GEMM tile variant for every GEMM")
+    p.add_argument("--gemm-variants", default="",
+                   help="tile variants of the KQV, O, Up/Gate and Down GEMMs, comma-separated (-1 = library choice)")
     p.add_argument("--no-pipeline", action="store_true",
                    help="layer stacks: issue layer by layer instead of cross-layer pipelining")
     p.add_argument("--cpu-layers", type=int, default=2,
@@ -337,6 +339,12 @@ def main():
         for kind in (abi.NF_OP_KQV, abi.NF_OP_O, abi.NF_OP_UGD):
             for which in (0, 1):
                 abi.nf_ctx_set_gemm_variant(ctx, kind, which, args.gemm_variant)
+    if args.gemm_variants:
+        vs = [int(v) for v in args.gemm_variants.split(",")]
+        if len(vs) != 4:
+            raise SystemExit("--gemm-variants takes four variants: KQV,O,UG,Down")
+        for (kind, which), v in zip(((abi.NF_OP_KQV, 0), (abi.NF_OP_O, 0), (abi.NF_OP_UGD, 0), (abi.NF_OP_UGD, 1)), vs):
+            abi.nf_ctx_set_gemm_variant(ctx, kind, which, v)
 
     def make_plan(kind):
         if kind == "null":
@@ -501,6 +509,7 @@ def main():
             "decode_nbuf": args.decode_nbuf,
             "decode_ring": args.decode_ring,
             "gemm_variant": args.gemm_variant,
+            "gemm_variants": args.gemm_variants or None,
         },
         "mfma_frac_of_bf16_peak": round(mfma_frac, 4),
         "layer_gemm_tflops": round(step_gemm_flops / (ms * 1e-3) / 1e12, 1),

@@ -302,6 +302,12 @@ nf_status nf_op_gemm(nf_ctx *ctx, const void *A, const void *B, void *C, const v
  * workgroup (the SwiGLU epilogue needs each wave's bn / (waves / 2) columns to be a
  * multiple of 64). */
 nf_status nf_gemm_variants(int32_t *count, int32_t index, int32_t *out5);
+/* Host query, no device needed: the tile configuration nf_op_gemm (and the layer) takes
+ * for variant -1 at this shape, and whether it is available there (*supported = 1). Same
+ * argument rules as nf_op_gemm. Errors: NF_E_ARG (bad sizes or epilogue, NULL outputs),
+ * NF_E_UNSUPPORTED (n or k not a multiple of 8).                                            */
+nf_status nf_gemm_choice(int32_t m, int32_t n, int32_t k, int32_t epilogue, int32_t *variant,
+                         int32_t *supported);
 
 /* out[r][:] = x[r] / sqrt(mean(x[r]^2) + eps) * g, rows r in [0, m), width n (mult. of 8). */
 nf_status nf_op_rmsnorm(nf_ctx *ctx, const void *x, const void *g, void *out, int32_t m, int32_t n,

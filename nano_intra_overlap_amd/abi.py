@@ -117,6 +117,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "nf_op_moe_ffn": (I, [V, ctypes.POINTER(nf_layer_cfg), ctypes.POINTER(nf_layer_weights), V, V, V, I, V, V, V]),
         "nf_op_gemm": (I, [V, V, V, V, V, I, I, I, I, I, V]),
         "nf_gemm_variants": (I, [_i32p, I, _i32p]),
+        "nf_gemm_choice": (I, [I, I, I, I, _i32p, _i32p]),
         "nf_op_rmsnorm": (I, [V, V, V, V, I, I, ctypes.c_float, V]),
         "nf_op_rope_kv_append": (I, [V, ctypes.POINTER(nf_layer_cfg), V, ctypes.POINTER(nf_batch_desc),
                                      ctypes.POINTER(nf_kv_pool), V]),
@@ -395,6 +396,13 @@ def nf_gemm_variants():
         _check(lib.nf_gemm_variants(None, i, t))
         out.append(tuple(t))
     return out
+
+
+def nf_gemm_choice(m: int, n: int, k: int, epilogue: int):
+    """(variant, supported): the library's tile choice for nf_op_gemm at this shape (host)."""
+    v, ok = ctypes.c_int32(), ctypes.c_int32()
+    _check(load().nf_gemm_choice(m, n, k, epilogue, ctypes.byref(v), ctypes.byref(ok)))
+    return v.value, bool(ok.value)
 
 
 def nf_op_rmsnorm(ctx, x: int, g: int, out: int, m: int, n: int, eps: float, stream: int = 0) -> None:

@@ -431,13 +431,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
       for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
   // wait until at most `newer` slabs issued after the awaited one are still in flight
+  static_assert(STAGES >= 3 && STAGES <= 6, "wait_slab covers up to five newer slabs");
+  static_assert(NL * (STAGES - 1) < 64, "the in-flight loads fit the wait counter");
   auto wait_slab = [&](int newer) {
+    if constexpr (STAGES > 5) {
+      if (newer >= 5) return wait_vmcnt<NL * 5>();
+    }
+    if constexpr (STAGES > 4) {
+      if (newer >= 4) return wait_vmcnt<NL * 4>();
+    }
     if (newer >= 3) wait_vmcnt<NL * 3>();
     else if (newer == 2) wait_vmcnt<NL * 2>();
     else if (newer == 1) wait_vmcnt<NL>();
     else wait_vmcnt<0>();
   };
-  static_assert(STAGES >= 3 && STAGES <= 4, "wait_slab covers up to three newer slabs");
 
   wait_slab(min(STAGES - 1, nk - 1));
   lds_barrier();
@@ -574,6 +581,16 @@ static const GemmVariant kVariants[] = {
     // layer's 256x256 shapes)
     {256, 256, 32, 1, 4, 8},  // 12
     {256, 128, 32, 1, 4, 8},  // 13 (not SwiGLU: a wave's 32 columns hold no gate/up pair)
+    // 4 waves, 96 columns each: a product of n = 6144 (the 8B KQV) in exactly 256 tiles of
+    // 2048 rows, one per CU (256x256 leaves a quarter of the CUs idle); not SwiGLU
+    {256, 192, 32, 1, 4, 4},  // 14
+    // deeper rings for operands that stream from HBM (a layer's weights do not stay in the
+    // last-level cache between its products): 6 slabs of 256x128 (144 KB), 5 of 256x256
+    // (160 KB)
+    {256, 128, 32, 1, 6, 4},  // 15
+    {256, 256, 32, 1, 5, 8},  // 16
+    {256, 256, 32, 1, 5, 4},  // 17
+    {256, 128, 32, 1, 6, 8},  // 18
 };
 static constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -602,8 +619,16 @@ int gemm_default_variant(int m, int n, int k, int epilogue) {
     // still gives at least 192 tiles (three quarters of the 256 CUs in one round)
     const int nn = epilogue == EPI_SWIGLU ? 2 * n : n;
     auto tiles = [&](int bm, int bn) { return ((m + bm - 1) / bm) * ((nn + bn - 1) / bn); };
-    if (tiles(256, 256) >= 192) return 12;
-    if (tiles(256, 128) >= 192) return 7;
+    if (tiles(256, 256) >= 192) {
+      // 256x192 when it fills whole rounds of the 256 CUs and 256x256 does not (8B KQV at
+      // 2048 rows: 256 tiles instead of 192; 100.7 against 106.7 us in the layer)
+      if (epilogue != EPI_SWIGLU && nn % 192 == 0 && tiles(256, 192) % 256 == 0 && tiles(256, 256) % 256 != 0)
+        return 14;
+      return 12;
+    }
+    // 256x128 with 8 waves and 6 slabs (8B O and Down in the layer: 83 and 268 us against 87
+    // and 278 with 4 waves and 4 slabs); SwiGLU needs 64 columns per wave: 4 waves
+    if (tiles(256, 128) >= 192) return epilogue == EPI_SWIGLU ? 7 : 18;
     const int t = tiles(128, 128);
     if (t < 128 && epilogue != EPI_SWIGLU) {
       // half the CUs or fewer busy: K slices of at least 1024 (measured: 2 slices pay off
@@ -781,6 +806,11 @@ hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int
     case 11: return launch_pipe<128, 128, 4>(A, B, C, R, m, n, k, epilogue, 4, ws, s);
     case 12: return launch_pipe<256, 256, 4, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
     case 13: return launch_pipe<256, 128, 4, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 14: return launch_pipe<256, 192, 4>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 15: return launch_pipe<256, 128, 6>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 16: return launch_pipe<256, 256, 5, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 17: return launch_pipe<256, 256, 5>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 18: return launch_pipe<256, 128, 6, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
   }
   return hipErrorInvalidValue;
 }

@@ -940,6 +940,15 @@ extern "C" nf_status nf_gemm_variants(int32_t* count, int32_t index, int32_t* ou
   return NF_OK;
 }
 
+extern "C" nf_status nf_gemm_choice(int32_t m, int32_t n, int32_t k, int32_t epilogue, int32_t* variant,
+                                    int32_t* supported) {
+  if (!variant || !supported || m < 0 || n <= 0 || k <= 0 || epilogue < 0 || epilogue > 2) return NF_E_ARG;
+  if (n % 8 || k % 8) return NF_E_UNSUPPORTED;
+  *variant = gemm_default_variant(m, n, k, epilogue);
+  *supported = gemm_variant_supported(*variant, m, n, k, epilogue) ? 1 : 0;
+  return NF_OK;
+}
+
 extern "C" nf_status nf_op_gemm(nf_ctx* ctx, const void* A, const void* B, void* C, const void* R, int32_t m, int32_t n,
                                 int32_t k, int32_t epilogue, int32_t variant, void* stream) {
   if (!ctx) return NF_E_ARG;

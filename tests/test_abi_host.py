@@ -115,6 +115,28 @@ def test_moe_shape_validation(abi):
     assert _status(abi, b, b.num_blocks, cfg=abi.make_cfg(dataclasses.replace(moe, n_experts=-1))) == abi.NF_E_ARG
 
 
+def test_gemm_choice_is_always_an_available_variant(abi):
+    """The library's own tile choice must be a configuration the launcher accepts for the
+    shape and epilogue: every nano-batch row count of the workloads' projections (1..2048
+    rows, each GEMM of the 8B, 70B-share, tiny and MoE shapes) and a sweep of other sizes."""
+    variants = abi.nf_gemm_variants()
+    shapes = set()
+    for name in ("tiny", "llama3_8b_layer", "llama2_70b_tp8_layer", "tiny_moe", "mixtral_8x7b_layer"):
+        sh = sw.WORKLOADS[name].shape
+        q = sh.n_q * sh.head_dim
+        shapes |= {(sh.qkv_rows, sh.hidden, 0), (sh.hidden, q, 1), (sh.ffn, sh.hidden, 2), (sh.hidden, sh.ffn, 1),
+                   (sh.ffn, sh.hidden, 0)}
+    shapes |= {(n, k, e) for n in (8, 64, 520, 1280, 4096, 6144, 8192) for k in (8, 96, 256, 4096) for e in (0, 1, 2)}
+    for n, k, epi in sorted(shapes):
+        for m in sorted({1, 7, 63, 64, 65, 127, 128, 200, 255, 256, 511, 512, 768, 1000, 1024, 1536, 2048, 4096}):
+            v, ok = abi.nf_gemm_choice(m, n, k, epi)
+            assert ok, (m, n, k, epi, v, variants[v])
+    with pytest.raises(abi.NanoflowError):
+        abi.nf_gemm_choice(16, 12, 64, 0)
+    with pytest.raises(abi.NanoflowError):
+        abi.nf_gemm_choice(16, 64, 64, 3)
+
+
 def test_dependency_rule_pages_example(abi):
     """O1 on tokens 0-767 depends on Attn1 (0-767) but not on Attn2 (768-2048)."""
     ex = GOLDEN["intersection_dependency_example"]

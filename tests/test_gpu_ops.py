@@ -108,7 +108,7 @@ def test_gemm_layer_shapes_sampled_rows(ctx, m, n, k, epi):
         assert err <= TOL, f"variant {v}: rel err {err}"
 
 
-@pytest.mark.parametrize("variant", [-1, 6, 7, 9, 10, 11, 12, 13])
+@pytest.mark.parametrize("variant", [-1, 6, 7, 9, 10, 11, 12, 13, 14])
 def test_gemm_residual_in_place(ctx, variant):
     from nano_intra_overlap_amd import abi
 
