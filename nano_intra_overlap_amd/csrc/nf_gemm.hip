@@ -215,6 +215,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// C and R rows are ldc elements apart and, with SwiGLU, the up weights of output column c
+// sit in row b_up + c of B: a launch may cover a column range of a wider product.
+
 // Workgroup barrier ordering LDS only. __syncthreads() (a workgroup fence) also waits for
 // every outstanding global load, vmcnt(0), which would drain the slabs still in flight.
 // Here: this wave's LDS reads complete (lgkmcnt(0)), then s_barrier; the empty asm
@@ -265,7 +268,8 @@ __device__ __forceinline__ void interleave_loads_reads() {
 
 template <int BM, int BN, int STAGES, int EPI, bool GRP = false, int NW = 4>
 __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restrict__ A0, const bf16* __restrict__ B0,
-                                                        bf16* C0, const bf16* R, int M0, int N, int K, int tiles_m0,
+                                                        bf16* C0, const bf16* R, int M0, int N, int K, int ldc,
+                                                        int b_up, int tiles_m0,
                                                         int tiles_n, int per_xcd, float* __restrict__ part,
                                                         GroupArgs ga) {
   constexpr int BK = 32;
@@ -310,7 +314,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
     else
       A = A0 + (size_t)rb * K;
     B = B0 + (size_t)g * ga.b_stride;
-    C = C0 + (size_t)rb * N;
+    C = C0 + (size_t)rb * ldc;
   } else {
     (void)ga;
     if (t >= tiles_m * tiles_n) return;
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
     if constexpr (EPI == EPI_SWIGLU) {
       const int sl = row / WTN, tt = row % WTN, p = tt / 64, u = tt % 64;
       const int col = min(n0 + sl * (WTN / 2) + p * 32 + (u & 31), N - 1);
-      gr = (u < 32) ? col : N + col;
+      gr = (u < 32) ? col : b_up + col;
     } else {
       gr = min(n0 + row, N - 1);
     }
@@ -543,7 +547,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
       if constexpr (EPI == EPI_RESID) {
         const f32x4 v0 = *reinterpret_cast<const f32x4*>(park + lr * OC + lc);
         const f32x4 v1 = *reinterpret_cast<const f32x4*>(park + lr * OC + lc + 4);
-        const bf16x8 rr = *reinterpret_cast<const bf16x8*>(R + (size_t)grow * N + gcol);
+        const bf16x8 rr = *reinterpret_cast<const bf16x8*>(R + (size_t)grow * ldc + gcol);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           o[e] = (bf16)(v0[e] + (float)rr[e]);
@@ -552,7 +556,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
       } else {
         o = *reinterpret_cast<const bf16x8*>(park + lr * OC + lc);
       }
-      *reinterpret_cast<bf16x8*>(C + (size_t)grow * N + gcol) = o;
+      *reinterpret_cast<bf16x8*>(C + (size_t)grow * ldc + gcol) = o;
     }
     if (PASSES > 1 && pass + 1 < PASSES) lds_barrier();
   }
@@ -591,7 +595,12 @@ static const GemmVariant kVariants[] = {
     {256, 256, 32, 1, 5, 8},  // 16
     {256, 256, 32, 1, 5, 4},  // 17
     {256, 128, 32, 1, 6, 8},  // 18
+    // variant 12 with the columns that would leave its last round of the 256 CUs at most half
+    // full moved to a second launch of 256x128 tiles, one round of half tiles (8B Up/Gate at
+    // 2048 rows: 896 tiles = 3.5 rounds become 768 + 256 half tiles)
+    {256, 256, 32, 1, 4, 8},  // 19
 };
+constexpr int kBalancedVariant = 19;
 static constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 int gemm_variant_count() { return kNumVariants; }
@@ -624,7 +633,9 @@ int gemm_default_variant(int m, int n, int k, int epilogue) {
       // 2048 rows: 256 tiles instead of 192; 100.7 against 106.7 us in the layer)
       if (epilogue != EPI_SWIGLU && nn % 192 == 0 && tiles(256, 192) % 256 == 0 && tiles(256, 256) % 256 != 0)
         return 14;
-      return 12;
+      // SwiGLU (8B Up/Gate): the balanced launch (plain variant 12 when no round is left
+      // half empty)
+      return epilogue == EPI_SWIGLU ? kBalancedVariant : 12;
     }
     // 256x128 with 8 waves and 6 slabs (8B O and Down in the layer: 83 and 268 us against 87
     // and 278 with 4 waves and 4 slabs); SwiGLU needs 64 columns per wave: 4 waves
@@ -703,9 +714,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
+// ldc: row stride of C and R (N for a whole product); b_up: SwiGLU's row of B holding the
+// up weights of output column 0 (N for a whole product, gate rows [0, N) then up rows).
 template <int BM, int BN, int STAGES, int EPI, int NW = 4>
 static hipError_t launch_pipe_t(const bf16* A, const bf16* B, bf16* C, const bf16* R, int M, int N, int K, int ks,
-                                float* part, hipStream_t s) {
+                                float* part, hipStream_t s, int ldc = -1, int b_up = -1) {
+  if (ldc < 0) ldc = N;
+  if (b_up < 0) b_up = N;
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (EPI == EPI_SWIGLU) ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
   const int ntiles = tiles_m * tiles_n;
@@ -719,8 +734,8 @@ static hipError_t launch_pipe_t(const bf16* A, const bf16* B, bf16* C, const bf1
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(per_xcd * kNumXcd, ks), dim3(64 * NW), lds, s, A, B, C, R, M, N, K, tiles_m, tiles_n,
-                     per_xcd, part, GroupArgs{});
+  hipLaunchKernelGGL(kern, dim3(per_xcd * kNumXcd, ks), dim3(64 * NW), lds, s, A, B, C, R, M, N, K, ldc, b_up, tiles_m,
+                     tiles_n, per_xcd, part, GroupArgs{});
   return hipGetLastError();
 }
 
@@ -744,8 +759,8 @@ static hipError_t launch_grouped_t(const bf16* A, const int32_t* a_rows, const b
     attr_set = true;
   }
   GroupArgs ga{grp, a_rows, n_groups, b_stride};
-  hipLaunchKernelGGL(kern, dim3(per_xcd * kNumXcd), dim3(256), lds, s, A, B, C, nullptr, n_rows, N, K, 0, tiles_n,
-                     per_xcd, nullptr, ga);
+  hipLaunchKernelGGL(kern, dim3(per_xcd * kNumXcd), dim3(256), lds, s, A, B, C, nullptr, n_rows, N, K, N, N, 0,
+                     tiles_n, per_xcd, nullptr, ga);
   return hipGetLastError();
 }
 
@@ -786,6 +801,50 @@ static hipError_t launch_epi(const bf16* A, const bf16* B, bf16* C, const bf16* 
   return hipErrorInvalidValue;
 }
 
+static int device_cus() {
+  static int cached = 0;
+  if (cached > 0) return cached;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;
+  cached = cus;
+  return cached;
+}
+
+// Variant 19: output columns [0, n1) in 256x256 tiles filling whole rounds of the CUs, the
+// rest in one round of 256x128 tiles (4 waves with SwiGLU, else 8 waves and 6 slabs); the
+// plain 256x256 launch when the last round is more than half full or the product has fewer
+// tiles than one round.
+template <int EPI>
+static hipError_t launch_balanced_t(const bf16* A, const bf16* B, bf16* C, const bf16* R, int m, int n, int k,
+                                    hipStream_t s) {
+  const int cus = device_cus();
+  const int cw = EPI == EPI_SWIGLU ? 128 : 256;  // output columns of one 256x256 tile
+  const int rt = (m + 255) / 256, ct = (n + cw - 1) / cw, T = rt * ct, r = T % cus;
+  const int ct1 = (T - r) / rt;
+  if (r == 0 || ct1 <= 0 || ct1 >= ct || 2 * rt * (ct - ct1) > cus)
+    return launch_pipe_t<256, 256, 4, EPI, 8>(A, B, C, R, m, n, k, 1, nullptr, s);
+  const int n1 = ct1 * cw;
+  hipError_t e = launch_pipe_t<256, 256, 4, EPI, 8>(A, B, C, R, m, n1, k, 1, nullptr, s, n, n);
+  if (e != hipSuccess) return e;
+  const bf16* R2 = R ? R + n1 : nullptr;
+  if constexpr (EPI == EPI_SWIGLU)
+    return launch_pipe_t<256, 128, 4, EPI, 4>(A, B + (size_t)n1 * k, C + n1, R2, m, n - n1, k, 1, nullptr, s, n, n);
+  else
+    return launch_pipe_t<256, 128, 6, EPI, 8>(A, B + (size_t)n1 * k, C + n1, R2, m, n - n1, k, 1, nullptr, s, n, n);
+}
+
+static hipError_t launch_balanced(const bf16* A, const bf16* B, bf16* C, const bf16* R, int m, int n, int k, int epi,
+                                  hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE: return launch_balanced_t<EPI_STORE>(A, B, C, R, m, n, k, s);
+    case EPI_RESID: return launch_balanced_t<EPI_RESID>(A, B, C, R, m, n, k, s);
+    case EPI_SWIGLU: return launch_balanced_t<EPI_SWIGLU>(A, B, C, R, m, n, k, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int m, int n, int k,
                        int epilogue, int variant, hipStream_t s, float* ws, size_t ws_bytes) {
   if (m <= 0 || n <= 0 || k <= 0) return hipSuccess;
@@ -811,6 +870,7 @@ hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int
     case 16: return launch_pipe<256, 256, 5, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
     case 17: return launch_pipe<256, 256, 5>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
     case 18: return launch_pipe<256, 128, 6, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case kBalancedVariant: return launch_balanced(A, B, C, R, m, n, k, epilogue, s);
   }
   return hipErrorInvalidValue;
 }
