@@ -52,13 +52,18 @@ hipError_t launch_rmsnorm(const bf16* x, const bf16* g, bf16* out, int m, int n,
   return hipGetLastError();
 }
 
-// One workgroup per token. Threads walk the (head, pair) space of q and k heads, then the
-// v elements. q is rotated in place in qkv; k and v go to the pool.
+// One workgroup per token. The token's angles pos * inv_freq[i] are evaluated once (d/2
+// sincos, shared through LDS by its n_q + n_kv heads); then each thread rotates 8
+// consecutive pairs (i0..i0+7, i0+d/2..i0+d/2+7) of one head with two 16-byte loads and two
+// 16-byte stores: q in place in qkv, k into the token's slot of the pool (8 consecutive dims
+// lie in one 32-dim column chunk). v is read 16 bytes at a time and stored dim-major, one
+// 2-byte element per dimension row of the block.
 __global__ __launch_bounds__(256) void rope_kv_kernel(bf16* __restrict__ qkv, const int32_t* __restrict__ tok_pos,
                                                       const int32_t* __restrict__ tok_slot,
                                                       const float* __restrict__ inv_freq, bf16* __restrict__ kpool,
                                                       bf16* __restrict__ vpool, int t_begin, int n_q, int n_kv,
                                                       int d) {
+  __shared__ float cs_l[128], sn_l[128];  // d / 2 <= 128
   const int t = t_begin + blockIdx.x;
   const int pos = tok_pos[t];
   const int slot = tok_slot[t];
@@ -66,31 +71,46 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(bf16* __restrict__ qkv, co
   const int half = d / 2;
   const int width = (n_q + 2 * n_kv) * d;
   bf16* row = qkv + (size_t)t * width;
-  const float fpos = (float)pos;
-  const int n_pairs = (n_q + n_kv) * half;
-  for (int i = threadIdx.x; i < n_pairs; i += 256) {
-    const int head = i / half, j = i % half;
+  for (int i = threadIdx.x; i < half; i += 256) {
     float sn, cs;
-    sincosf(fpos * inv_freq[j], &sn, &cs);  // full-range reduction (angles reach ~4096 rad)
+    sincosf((float)pos * inv_freq[i], &sn, &cs);  // full-range reduction (angles reach ~4096 rad)
+    cs_l[i] = cs;
+    sn_l[i] = sn;
+  }
+  __syncthreads();
+  const int per_head = half / 8;
+  const int n_chunks = (n_q + n_kv) * per_head;
+  for (int c = threadIdx.x; c < n_chunks; c += 256) {
+    const int head = c / per_head, i0 = (c % per_head) * 8;
     bf16* hp = row + head * d;
-    const float x1 = (float)hp[j], x2 = (float)hp[j + half];
-    const bf16 o1 = (bf16)(x1 * cs - x2 * sn);
-    const bf16 o2 = (bf16)(x2 * cs + x1 * sn);
+    const bf16x8 x1 = *reinterpret_cast<const bf16x8*>(hp + i0);
+    const bf16x8 x2 = *reinterpret_cast<const bf16x8*>(hp + i0 + half);
+    bf16x8 o1, o2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float cs = cs_l[i0 + e], sn = sn_l[i0 + e];
+      const float a = (float)x1[e], b = (float)x2[e];
+      o1[e] = (bf16)(a * cs - b * sn);
+      o2[e] = (bf16)(b * cs + a * sn);
+    }
     if (head < n_q) {
-      hp[j] = o1;
-      hp[j + half] = o2;
+      *reinterpret_cast<bf16x8*>(hp + i0) = o1;
+      *reinterpret_cast<bf16x8*>(hp + i0 + half) = o2;
     } else {
       // key block layout [d/32][16][32]: dim i of this token at (i / 32, off, i % 32)
       const int g = head - n_q;
       bf16* kb = kpool + ((size_t)blk * n_kv + g) * (kBlock * d) + off * 32;
-      kb[(j >> 5) * (kBlock * 32) + (j & 31)] = o1;
-      kb[((j + half) >> 5) * (kBlock * 32) + ((j + half) & 31)] = o2;
+      *reinterpret_cast<bf16x8*>(kb + (i0 >> 5) * (kBlock * 32) + (i0 & 31)) = o1;
+      *reinterpret_cast<bf16x8*>(kb + ((i0 + half) >> 5) * (kBlock * 32) + ((i0 + half) & 31)) = o2;
     }
   }
   const bf16* vrow = row + (n_q + n_kv) * d;
-  for (int i = threadIdx.x; i < n_kv * d; i += 256) {
-    const int g = i / d, j = i % d;
-    vpool[(((size_t)blk * n_kv + g) * d + j) * kBlock + off] = vrow[i];
+  for (int c = threadIdx.x; c < n_kv * d / 8; c += 256) {
+    const int g = (c * 8) / d, j0 = (c * 8) % d;
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(vrow + c * 8);
+    bf16* vb = vpool + (((size_t)blk * n_kv + g) * d + j0) * kBlock + off;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vb[e * kBlock] = v[e];
   }
 }
 
