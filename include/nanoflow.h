@@ -384,9 +384,12 @@ nf_status nf_profile_ops(nf_ctx *ctx, const nf_layer_cfg *cfg, const nf_batch_de
                          int32_t num_blocks, int32_t step, int32_t max_tokens, const char *out_json);
 
 /* Pairwise interference: for each CU share R of the non-GEMM kernel in r_grid (n_r values in
- * (0,1)), run a GEMM nano-op on a mask of (1-R) of the CUs and a decode-attention nano-op
- * on a mask of R concurrently, and record each one's speed relative to its own best
- * (P values). Writes JSON to out_json. Errors: NF_E_ARG, NF_E_IO, NF_E_HIP, NF_E_CU_MASK.   */
+ * (0,1)), and for the shared GPU without masks (plain and with bounded attention grids),
+ * run a GEMM nano-op on a mask of (1-R) of the CUs and a decode-attention nano-op on a mask
+ * of R concurrently, and record each one's speed relative to its own best (P values). The
+ * plain fields of an entry come from the Up/Gate/Down nano-op; the KQV and O nano-ops are
+ * measured the same way (p_gemm_both_kind, p_mem_both_kind, p_gemm_alone_kind, keyed by
+ * kind). Writes JSON to out_json. Errors: NF_E_ARG, NF_E_IO, NF_E_HIP, NF_E_CU_MASK.        */
 nf_status nf_profile_interference(nf_ctx *ctx, const nf_layer_cfg *cfg,
                                   const nf_batch_desc *batch_template, int32_t num_blocks,
                                   const float *r_grid, int32_t n_r, const char *out_json);

@@ -495,12 +495,17 @@ extern "C" nf_status nf_profile_interference(nf_ctx* ctx, const nf_layer_cfg* cf
     if (!fill(E, kp, (size_t)D.num_blocks * per_block, 91, 1.3f, s0)) return false;
     if (!fill(E, vp, (size_t)D.num_blocks * per_block, 92, 1.3f, s0)) return false;
     PF_HIP(hipStreamSynchronize(s0));
+    const int W = (c.n_q_heads + 2 * nkv) * d;
     const int vug = gemm_default_variant(m, F, H, 2), vdn = gemm_default_variant(m, H, F, 1);
-    const size_t wsb = std::max(gemm_workspace_bytes(vug, m, F), gemm_workspace_bytes(vdn, m, H));
+    const int vqkv = gemm_default_variant(m, W, H, 0), vo = gemm_default_variant(m, H, Q, 1);
+    const size_t wsb = std::max(std::max(gemm_workspace_bytes(vug, m, F), gemm_workspace_bytes(vdn, m, H)),
+                                std::max(gemm_workspace_bytes(vqkv, m, W), gemm_workspace_bytes(vo, m, H)));
     Buf gws;
     if (wsb) PF_HIP(gws.alloc(wsb));
-    // compute op: one Up/Gate/Down nano-op; memory op: one decode attention nano-op
-    auto gemm_op = [&](hipStream_t s) -> hipError_t {
+    // compute ops: one nano-op of each compute kind (the main entry is Up/Gate/Down); memory
+    // op: one decode attention nano-op. The KQV product writes into the FFN activation
+    // buffer, not into the qkv rows the attention reads.
+    auto ugd_op = [&](hipStream_t s) -> hipError_t {
       if (c.n_experts > 0) return moe_ffn_op(c, S, m, s);
       hipError_t e = launch_gemm(S.h2.as<bf16>(), S.wgu.as<bf16>(), S.a.as<bf16>(), nullptr, m, F, H, 2, vug, s,
                                  gws.as<float>(), wsb);
@@ -508,6 +513,20 @@ extern "C" nf_status nf_profile_interference(nf_ctx* ctx, const nf_layer_cfg* cf
       return launch_gemm(S.a.as<bf16>(), S.wd.as<bf16>(), S.y.as<bf16>(), S.x1.as<bf16>(), m, H, F, 1, vdn, s,
                          gws.as<float>(), wsb);
     };
+    auto kqv_op = [&](hipStream_t s) -> hipError_t {
+      return launch_gemm(S.h.as<bf16>(), S.wqkv.as<bf16>(), S.a.as<bf16>(), nullptr, m, W, H, 0, vqkv, s,
+                         gws.as<float>(), wsb);
+    };
+    auto o_op = [&](hipStream_t s) -> hipError_t {
+      return launch_gemm(S.attn.as<bf16>(), S.wo.as<bf16>(), S.y.as<bf16>(), S.x.as<bf16>(), m, H, Q, 1, vo, s,
+                         gws.as<float>(), wsb);
+    };
+    struct Kind {
+      const char* name;
+      std::function<hipError_t(hipStream_t)> op;
+      double best = 0.0;
+    };
+    std::vector<Kind> kinds = {{"UGD", ugd_op}, {"KQV", kqv_op}, {"O", o_op}};
     int grid = 0;
     auto mem_op = [&](hipStream_t s) -> hipError_t {
       hipError_t e = launch_decode_attn(S.qkv.as<bf16>(), kp.as<bf16>(), vp.as<bf16>(), D.d_bt.as<int32_t>(),
@@ -518,9 +537,23 @@ extern "C" nf_status nf_profile_interference(nf_ctx* ctx, const nf_layer_cfg* cf
       return launch_decode_combine(D.d_comb.as<CombineItem>(), (int)D.M.comb.size(), D.d_part_o.as<float>(),
                                    D.d_part_ml.as<float>(), out.as<bf16>(), c.n_q_heads, c.n_kv_heads, d, s);
     };
+    // best times: after a warm-up (code loaded, clocks and caches settled), the fastest of
+    // three rounds; every P value below is a speed relative to these
+    auto best_ms = [&](const std::function<hipError_t(hipStream_t)>& op, double& best) -> bool {
+      for (int i = 0; i < 10; ++i) PF_HIP(op(s0));
+      best = 1e30;
+      for (int r = 0; r < 3; ++r) {
+        double t;
+        if (!time_ms(E, s0, 5, [&] { return op(s0); }, t)) return false;
+        best = std::min(best, t);
+      }
+      return true;
+    };
     double tg_best, tm_best;
-    if (!time_ms(E, s0, 5, [&] { return gemm_op(s0); }, tg_best)) return false;
-    if (!time_ms(E, s0, 5, [&] { return mem_op(s0); }, tm_best)) return false;
+    for (Kind& k : kinds)
+      if (!best_ms(k.op, k.best)) return false;
+    tg_best = kinds[0].best;
+    if (!best_ms(mem_op, tm_best)) return false;
 
     struct Cfg {
       std::string name;
@@ -536,7 +569,7 @@ extern "C" nf_status nf_profile_interference(nf_ctx* ctx, const nf_layer_cfg* cf
       cfgs.push_back({nm, (double)r_grid[i], true, 0});
     }
     o << "{\"device_cus\": 256, \"cfg\": " << cfg_json(c) << ", \"gemm_op\": \"" << (c.n_experts > 0 ? "MoE FFN (router, grouped Up/Gate+SwiGLU, grouped Down, combine), " : "Up/Gate+SwiGLU+Down, ") << m
-      << " rows\", \"mem_op\": \"decode attention, " << n_dec << " requests\", \"t_gemm_best_ms\": "
+      << " rows (KQV and O of as many rows in the *_kind fields)\", \"mem_op\": \"decode attention, " << n_dec << " requests\", \"t_gemm_best_ms\": "
       << json::num(tg_best) << ", \"t_mem_best_ms\": " << json::num(tm_best) << ",\n \"configs\": [";
     bool first = true;
     for (const Cfg& cf : cfgs) {
@@ -559,49 +592,77 @@ extern "C" nf_status nf_profile_interference(nf_ctx* ctx, const nf_layer_cfg* cf
         sm = own[1];
       }
       grid = cf.grid;
-      double tg_alone, tm_alone;
-      if (!time_ms(E, sg, 3, [&] { return gemm_op(sg); }, tg_alone)) return false;
-      if (!time_ms(E, sm, 3, [&] { return mem_op(sm); }, tm_alone)) return false;
-      // concurrent: loops sized to about the same length, started together
-      const int lm = 2;
-      const int lg = std::max(1, (int)std::lround(lm * tm_alone / tg_alone));
-      hipEvent_t e0, eg, em;
-      PF_HIP(hipEventCreate(&e0));
-      PF_HIP(hipEventCreate(&eg));
-      PF_HIP(hipEventCreate(&em));
-      PF_HIP(hipStreamSynchronize(sg));
-      PF_HIP(hipStreamSynchronize(sm));
-      PF_HIP(hipEventRecord(e0, sg));
-      PF_HIP(hipStreamWaitEvent(sm, e0, 0));
-      for (int i = 0; i < lg; ++i) PF_HIP(gemm_op(sg));
-      for (int i = 0; i < lm; ++i) PF_HIP(mem_op(sm));
-      PF_HIP(hipEventRecord(eg, sg));
-      PF_HIP(hipEventRecord(em, sm));
-      PF_HIP(hipEventSynchronize(eg));
-      PF_HIP(hipEventSynchronize(em));
-      float fg = 0, fm = 0;
-      PF_HIP(hipEventElapsedTime(&fg, e0, eg));
-      PF_HIP(hipEventElapsedTime(&fm, e0, em));
-      (void)hipEventDestroy(e0);
-      (void)hipEventDestroy(eg);
-      (void)hipEventDestroy(em);
-      // work in units of best time; the longer loop's tail ran alone at its alone speed
-      const double wg = lg * tg_best, wm = lm * tm_best;
-      const double pg_alone = tg_best / tg_alone, pm_alone = tm_best / tm_alone;
-      const double t1 = std::min((double)fg, (double)fm);
-      double pg_both, pm_both;
-      if (fg <= fm) {
-        pg_both = wg / t1;
-        pm_both = std::max(1e-3, (wm - (fm - t1) * pm_alone) / t1);
-      } else {
-        pm_both = wm / t1;
-        pg_both = std::max(1e-3, (wg - (fg - t1) * pg_alone) / t1);
+      // alone on a masked stream: slower than on the whole GPU; on the shared GPU an op
+      // alone runs at its best by definition (a bounded attention grid is timed)
+      double tm_alone = tm_best;
+      if (cf.masked || cf.grid > 0)
+        if (!time_ms(E, sm, 3, [&] { return mem_op(sm); }, tm_alone)) return false;
+      const double pm_alone = std::min(1.0, tm_best / tm_alone);
+      // each compute kind against the memory op: loops sized to about the same length,
+      // started together; work in units of best time, the longer loop's tail ran alone
+      struct Pair {
+        double pg_both, pm_both, pg_alone, fg, fm;
+        int lg;
+      };
+      std::vector<Pair> pairs;
+      for (Kind& k : kinds) {
+        double tg_alone = k.best;
+        if (cf.masked)
+          if (!time_ms(E, sg, 3, [&] { return k.op(sg); }, tg_alone)) return false;
+        const int lm = 2;
+        const int lg = std::max(1, (int)std::lround(lm * tm_alone / tg_alone));
+        hipEvent_t e0, eg, em;
+        PF_HIP(hipEventCreate(&e0));
+        PF_HIP(hipEventCreate(&eg));
+        PF_HIP(hipEventCreate(&em));
+        PF_HIP(hipStreamSynchronize(sg));
+        PF_HIP(hipStreamSynchronize(sm));
+        PF_HIP(hipEventRecord(e0, sg));
+        PF_HIP(hipStreamWaitEvent(sm, e0, 0));
+        for (int i = 0; i < lg; ++i) PF_HIP(k.op(sg));
+        for (int i = 0; i < lm; ++i) PF_HIP(mem_op(sm));
+        PF_HIP(hipEventRecord(eg, sg));
+        PF_HIP(hipEventRecord(em, sm));
+        PF_HIP(hipEventSynchronize(eg));
+        PF_HIP(hipEventSynchronize(em));
+        float fg = 0, fm = 0;
+        PF_HIP(hipEventElapsedTime(&fg, e0, eg));
+        PF_HIP(hipEventElapsedTime(&fm, e0, em));
+        (void)hipEventDestroy(e0);
+        (void)hipEventDestroy(eg);
+        (void)hipEventDestroy(em);
+        const double wg = lg * k.best, wm = lm * tm_best;
+        const double pg_alone = std::min(1.0, k.best / tg_alone);
+        const double t1 = std::min((double)fg, (double)fm);
+        double pg_both, pm_both;
+        if (fg <= fm) {
+          pg_both = wg / t1;
+          pm_both = std::max(1e-3, (wm - (fm - t1) * pm_alone) / t1);
+        } else {
+          pm_both = wm / t1;
+          pg_both = std::max(1e-3, (wg - (fg - t1) * pg_alone) / t1);
+        }
+        pairs.push_back({pg_both, pm_both, pg_alone, fg, fm, lg});
       }
+      const Pair& u = pairs[0];  // Up/Gate/Down: the entry's plain fields
+      const double pg_both = u.pg_both, pm_both = u.pm_both, pg_alone = u.pg_alone;
+      const float fg = (float)u.fg, fm = (float)u.fm;
+      const int lg = u.lg, lm = 2;
+      auto kind_obj = [&](double Pair::*f) {
+        std::ostringstream k;
+        k << "{";
+        for (size_t i = 0; i < kinds.size(); ++i)
+          k << (i ? ", " : "") << json::quote(kinds[i].name) << ": " << json::num(pairs[i].*f);
+        k << "}";
+        return k.str();
+      };
       o << (first ? "" : ",") << "\n  {\"name\": " << json::quote(cf.name) << ", \"r_mem\": " << json::num(cf.r)
         << ", \"decode_grid\": " << cf.grid << ", \"p_gemm_both\": " << json::num(pg_both)
         << ", \"p_mem_both\": " << json::num(pm_both) << ", \"p_gemm_alone\": " << json::num(pg_alone)
         << ", \"p_mem_alone\": " << json::num(pm_alone) << ", \"concurrent_ms\": [" << json::num(fg) << ", "
-        << json::num(fm) << "], \"loops\": [" << lg << ", " << lm << "]";
+        << json::num(fm) << "], \"loops\": [" << lg << ", " << lm << "]"
+        << ", \"p_gemm_both_kind\": " << kind_obj(&Pair::pg_both) << ", \"p_mem_both_kind\": " << kind_obj(&Pair::pm_both)
+        << ", \"p_gemm_alone_kind\": " << kind_obj(&Pair::pg_alone);
       if (cf.masked) {
         o << ", \"cu_masks\": [";
         for (int s = 0; s < 2; ++s) {

@@ -17,8 +17,13 @@
 // best speed while an op of the other class runs and at P_alone(c) otherwise (a masked
 // stream is slower even alone). The schedule is re-simulated with these rates (time advances
 // from one completion to the next) and the configuration with the shortest makespan wins.
+// The compute rate, and the memory op's rate beside it, may be given per compute kind (KQV,
+// O, UGD measured each against the memory op): on a shared GPU a short product beside
+// decode attention waits for CU slots far longer than the long FFN product does.
 // Extension: the K best Stage-I structures and the single-stream sequential plan are all
-// re-ranked under interference, since on this GPU interference can reverse Stage I's order.
+// re-ranked under interference, since on this GPU interference can reverse Stage I's order;
+// an overlapped plan is taken only when predicted faster than the sequential one by more
+// than the table's "min_gain" fraction (0 when absent).
 #include <algorithm>
 #include <cmath>
 #include <cstring>
@@ -56,6 +61,10 @@ struct InterfCfg {
   std::string name;
   double r = -1.0;  // memory stream CU share (-1: shared GPU, no masks)
   double pg_both = 1, pm_both = 1, pg_alone = 1, pm_alone = 1;
+  // per compute kind (KQV, O, UGD) when the table measured each against the memory op;
+  // otherwise pg_both / pg_alone. pm_both_k: the memory op's speed beside each compute kind.
+  double pg_both_k[NF_OP_KINDS] = {1, 1, 1, 1, 1}, pg_alone_k[NF_OP_KINDS] = {1, 1, 1, 1, 1};
+  double pm_both_k[NF_OP_KINDS] = {1, 1, 1, 1, 1};
   bool has_masks = false;
   uint32_t masks[2][NF_CU_MASK_WORDS];
   int decode_grid = 0;
@@ -90,8 +99,9 @@ bool load_profile(const char* path, Profile& P, std::string& err) {
   return true;
 }
 
-bool load_interference(const char* path, std::vector<InterfCfg>& out, std::string& err) {
+bool load_interference(const char* path, std::vector<InterfCfg>& out, double& min_gain, std::string& err) {
   out.clear();
+  min_gain = 0.0;
   if (!path || !*path) {
     InterfCfg c;
     c.name = "ideal";
@@ -100,6 +110,11 @@ bool load_interference(const char* path, std::vector<InterfCfg>& out, std::strin
   }
   json::Value v;
   if (!json::parse_file(path, v, err)) return false;
+  min_gain = v.number("min_gain", 0.0);
+  if (!(min_gain >= 0.0 && min_gain < 1.0)) {
+    err = "interference table: min_gain must lie in [0, 1)";
+    return false;
+  }
   const json::Value& cs = v.at("configs");
   if (!cs.is_arr() || cs.arr.empty()) {
     err = "interference table lacks a non-empty 'configs' array";
@@ -113,6 +128,20 @@ bool load_interference(const char* path, std::vector<InterfCfg>& out, std::strin
     c.pm_both = e.number("p_mem_both", 1.0);
     c.pg_alone = e.number("p_gemm_alone", 1.0);
     c.pm_alone = e.number("p_mem_alone", 1.0);
+    for (int k = 0; k < NF_OP_KINDS; ++k) {
+      c.pg_both_k[k] = c.pg_both;
+      c.pg_alone_k[k] = c.pg_alone;
+      c.pm_both_k[k] = c.pm_both;
+    }
+    for (int k : {(int)NF_OP_KQV, (int)NF_OP_O, (int)NF_OP_UGD}) {
+      c.pg_both_k[k] = e.at("p_gemm_both_kind").number(kKindNames[k], c.pg_both);
+      c.pg_alone_k[k] = e.at("p_gemm_alone_kind").number(kKindNames[k], c.pg_alone);
+      c.pm_both_k[k] = e.at("p_mem_both_kind").number(kKindNames[k], c.pm_both);
+      if (!(c.pg_both_k[k] > 0 && c.pg_alone_k[k] > 0 && c.pm_both_k[k] > 0)) {
+        err = "interference entry '" + c.name + "' has a non-positive speed";
+        return false;
+      }
+    }
     c.decode_grid = (int)e.number("decode_grid", 0.0);
     const json::Value& m = e.at("cu_masks");
     if (m.is_arr() && m.arr.size() == 2) {
@@ -231,9 +260,9 @@ SimResult simulate(const Structure& S, const PlanGraph& g, const std::vector<dou
       if (ns == 1)
         rate[s] = 1.0;
       else if (is_compute)
-        rate[s] = other ? c.pg_both : c.pg_alone;
+        rate[s] = other ? c.pg_both_k[cur[s] / n] : c.pg_alone_k[cur[s] / n];
       else
-        rate[s] = other ? c.pm_both : c.pm_alone;
+        rate[s] = other ? c.pm_both_k[cur[compute_is_stream0 ? 0 : 1] / n] : c.pm_alone;
     }
     // next completion
     double dt = 1e300;
@@ -341,7 +370,8 @@ extern "C" nf_status nf_plan_search(const char* dbest_json, const char* rp_json,
     return NF_E_IO;
   }
   std::vector<InterfCfg> cfgs;
-  if (!load_interference(rp_json, cfgs, err)) {
+  double min_gain = 0.0;
+  if (!load_interference(rp_json, cfgs, min_gain, err)) {
     put(plan_json_out, cap, err);
     return NF_E_IO;
   }
@@ -441,6 +471,20 @@ extern "C" nf_status nf_plan_search(const char* dbest_json, const char* rp_json,
         best_k = pool[ci].S.sequential ? -1 : (int)k;
         best_start = r.start;
       }
+    }
+  }
+  // an overlapped plan has to beat the sequential one by more than the table's min_gain
+  // (the interference model's observed error on this device); otherwise sequential
+  {
+    const int seq_c = (int)pool.size() - 1;
+    if (best_c != seq_c && best_ms > seq.stage1 * (1.0 - min_gain)) {
+      PlanGraph g;
+      graph_for(seq.S.bounds, g);
+      SimResult r = simulate(seq.S, g, op_durations(L, g, P), ideal);
+      best_ms = r.makespan;
+      best_c = seq_c;
+      best_k = -1;
+      best_start = r.start;
     }
   }
   const Candidate& win = pool[best_c];

@@ -20,6 +20,7 @@ Pins: the page's O1/Attn example and hand-built cases in the not-gpu tests.
 from __future__ import annotations
 
 KQV, DECATTN, PFATTN, O, UGD = range(5)
+KIND_NAMES = ("KQV", "DECATTN", "PFATTN", "O", "UGD")
 PARENTS = {DECATTN: {KQV}, PFATTN: {KQV}, O: {DECATTN, PFATTN}, UGD: {O}}
 
 
@@ -114,8 +115,13 @@ def simulate(streams, deps, dur, speeds=None):
     """Makespan of in-order streams (lists of (kind, nano)) with dependency waits.
 
     speeds: None (every op at full speed) or a dict with p_gemm_both, p_mem_both,
-    p_gemm_alone, p_mem_alone; stream 0 is the compute stream. Returns None on deadlock.
-    Time advances from one completion to the next; a running op progresses at its speed.
+    p_gemm_alone, p_mem_alone, and optionally p_gemm_both_kind / p_gemm_alone_kind /
+    p_mem_both_kind: the compute speeds of the KQV, O and UGD ops, and the memory op's speed
+    beside each of them, measured one compute kind at a time against the memory op (the
+    pages' pairwise interference profile, taken per compute kind; a kind without an entry
+    uses the plain speed). Stream 0 is the compute stream. Returns None on
+    deadlock. Time advances from one completion to the next; a running op progresses at its
+    speed.
     """
     pos = [0] * len(streams)
     cur = [None] * len(streams)
@@ -151,6 +157,12 @@ def simulate(streams, deps, dur, speeds=None):
                 both = len(running) > 1
                 key = ("p_gemm_" if s == 0 else "p_mem_") + ("both" if both else "alone")
                 rate[s] = speeds[key]
+                per_kind = speeds.get(key + "_kind") or {}
+                # the compute stream's own kind; the memory stream's speed beside it is keyed
+                # by the kind of the compute op running next to it
+                name = KIND_NAMES[cur[s][0]] if s == 0 else (KIND_NAMES[cur[0][0]] if both else None)
+                if name in per_kind:
+                    rate[s] = per_kind[name]
         dt = min(left[s] / rate[s] for s in running)
         t += dt
         for s in running:
@@ -187,10 +199,12 @@ def all_bounds(T, n, gran):
         yield [0, *c, T]
 
 
-def search(batch, table, configs=None, max_nano=4, gran=128, top_k=8):
+def search(batch, table, configs=None, max_nano=4, gran=128, top_k=8, min_gain=0.0):
     """Brute force over the same space as the library: Stage I by exhaustive enumeration,
     Stage II over the interference configurations for the K best structures and the
-    sequential single-stream plan. Returns (best makespan, stage-I best makespan)."""
+    sequential single-stream plan; an overlapped plan wins only when it beats the
+    sequential one by more than the fraction min_gain. Returns (best makespan, stage-I best
+    makespan)."""
     T = sum(e - s for s, e, _ in _requests(batch))
     cands = []
     for n in range(1, max_nano + 1):
@@ -212,10 +226,13 @@ def search(batch, table, configs=None, max_nano=4, gran=128, top_k=8):
     for a, b in dependencies(batch, seq_bounds):
         seq_deps.setdefault(b, set()).add(a)
     seq_dur = durations(batch, seq_bounds, table)
-    best = simulate([[(k, 0) for k in range(5)]], seq_deps, seq_dur)
+    seq = simulate([[(k, 0) for k in range(5)]], seq_deps, seq_dur)
+    best = seq
     for ms, n, bounds, st, deps, dur in cands[:top_k]:
         for c in (configs or [None]):
             r = simulate(st, deps, dur, c)
             if r is not None and r < best:
                 best = r
+    if best > seq * (1.0 - min_gain):
+        best = seq
     return best, stage1

@@ -102,12 +102,18 @@ def test_search_matches_brute_force(abi, tmp_path, seed):
         {"name": "shared", "p_gemm_both": 0.7, "p_mem_both": 0.8},
         {"name": "mem25", "r_mem": 0.25, "p_gemm_both": 0.85, "p_mem_both": 0.5, "p_gemm_alone": 0.75,
          "p_mem_alone": 0.55},
+        # per compute kind: short products starve beside the memory op (as measured on a shared
+        # GPU), the FFN product does not
+        {"name": "shared_kinds", "p_gemm_both": 0.9, "p_mem_both": 0.85,
+         "p_gemm_both_kind": {"KQV": 0.12, "O": 0.2, "UGD": 0.9}, "p_gemm_alone_kind": {"KQV": 0.95},
+         "p_mem_both_kind": {"KQV": 0.95, "UGD": 0.7}},
     ]
     dpath = _write(tmp_path, "dbest.json", {"ops": table})
     rpath = _write(tmp_path, "rp.json", {"configs": configs})
     hb = abi.HostBatch.from_batch(b)
     plan = json.loads(abi.nf_plan_search(dpath, rpath, hb, max_nano=4, granularity=128))
-    speeds = [{k: c.get(k, 1.0) for k in ("p_gemm_both", "p_mem_both", "p_gemm_alone", "p_mem_alone")}
+    speeds = [{**{k: c.get(k, 1.0) for k in ("p_gemm_both", "p_mem_both", "p_gemm_alone", "p_mem_alone")},
+               **{k: c[k] for k in ("p_gemm_both_kind", "p_gemm_alone_kind", "p_mem_both_kind") if k in c}}
               for c in configs]
     best, stage1 = osch.search(b, table, speeds, max_nano=4, gran=128, top_k=8)
     assert plan["stage1"]["best_ms"] == pytest.approx(stage1, rel=1e-9)
@@ -117,6 +123,57 @@ def test_search_matches_brute_force(abi, tmp_path, seed):
 
     hp, rec = plans.from_json(json.dumps(plan))
     abi.nf_plan_dependencies(hb, hp)
+
+
+def test_search_per_kind_compute_interference(abi, tmp_path):
+    """A table that gives the compute speed beside the memory op per compute kind: the
+    library and the brute-force search agree, and the per-kind speeds change the outcome
+    against the same table without them (so the kinds are actually read)."""
+    rng = np.random.default_rng(21)
+    b = _batch(rng)
+    table = _table(rng)
+    plain = {"name": "shared", "p_gemm_both": 0.9, "p_mem_both": 0.9}
+    kinds = dict(plain, p_gemm_both_kind={"KQV": 0.3, "O": 0.45, "UGD": 0.95}, p_gemm_alone_kind={"O": 0.98},
+                 p_mem_both_kind={"KQV": 0.97, "O": 0.93, "UGD": 0.6})
+    dpath = _write(tmp_path, "dbest.json", {"ops": table})
+    hb = abi.HostBatch.from_batch(b)
+    got = {}
+    for name, cfg in (("plain", plain), ("kinds", kinds)):
+        rpath = _write(tmp_path, f"rp_{name}.json", {"configs": [cfg]})
+        plan = json.loads(abi.nf_plan_search(dpath, rpath, hb, max_nano=4, granularity=128))
+        speeds = {k: cfg.get(k, 1.0) for k in ("p_gemm_both", "p_mem_both", "p_gemm_alone", "p_mem_alone")}
+        speeds.update({k: cfg[k] for k in ("p_gemm_both_kind", "p_gemm_alone_kind", "p_mem_both_kind") if k in cfg})
+        best, _ = osch.search(b, table, [speeds], max_nano=4, gran=128, top_k=8)
+        assert plan["predicted_ms"] == pytest.approx(best, rel=1e-6), name
+        got[name] = plan["predicted_ms"]
+    assert got["kinds"] > got["plain"]
+
+
+@pytest.mark.parametrize("min_gain", [0.0, 0.05, 0.3])
+def test_search_min_gain(abi, tmp_path, min_gain):
+    """The table's min_gain: an overlapped plan is taken only when predicted faster than the
+    sequential one by more than that fraction (brute force applies the same rule)."""
+    rng = np.random.default_rng(33)
+    b = _batch(rng)
+    table = _table(rng)
+    cfg = {"name": "shared", "p_gemm_both": 0.8, "p_mem_both": 0.85}
+    dpath = _write(tmp_path, "dbest.json", {"ops": table})
+    rpath = _write(tmp_path, "rp.json", {"configs": [cfg], "min_gain": min_gain})
+    plan = json.loads(abi.nf_plan_search(dpath, rpath, abi.HostBatch.from_batch(b), max_nano=4, granularity=128))
+    speeds = {k: cfg.get(k, 1.0) for k in ("p_gemm_both", "p_mem_both", "p_gemm_alone", "p_mem_alone")}
+    best, _ = osch.search(b, table, [speeds], max_nano=4, gran=128, top_k=8, min_gain=min_gain)
+    assert plan["predicted_ms"] == pytest.approx(best, rel=1e-6)
+    overlapped = plan["n_streams"] == 2
+    assert overlapped == (best < plan["sequential_ms"] * (1 - min_gain))
+    if overlapped:
+        assert plan["predicted_ms"] < plan["sequential_ms"] * (1 - min_gain)
+    else:
+        assert plan["predicted_ms"] == pytest.approx(plan["sequential_ms"])
+    if min_gain == 0.3:
+        assert not overlapped
+    rpath = _write(tmp_path, "rp_bad.json", {"configs": [cfg], "min_gain": 1.5})
+    with pytest.raises(abi.NanoflowError):
+        abi.nf_plan_search(dpath, rpath, abi.HostBatch.from_batch(b), max_nano=4, granularity=128)
 
 
 def test_search_prefers_sequential_when_interference_is_ruinous(abi, tmp_path):
