@@ -599,6 +599,9 @@ static const GemmVariant kVariants[] = {
     // full moved to a second launch of 256x128 tiles, one round of half tiles (8B Up/Gate at
     // 2048 rows: 896 tiles = 3.5 rounds become 768 + 256 half tiles)
     {256, 256, 32, 1, 4, 8},  // 19
+    // 256x256, 8 waves, K split in 2 (fp32 partials + reduce): a product of n = 4096 at 2048
+    // rows (8B O and Down) in 256 workgroups of the larger tile; not SwiGLU
+    {256, 256, 32, 2, 4, 8},  // 20
 };
 constexpr int kBalancedVariant = 19;
 static constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
@@ -637,6 +640,11 @@ int gemm_default_variant(int m, int n, int k, int epilogue) {
       // half empty)
       return epilogue == EPI_SWIGLU ? kBalancedVariant : 12;
     }
+    // long K (>= 8192): 256x256 with K split in 2 when that gives >= 192 workgroups; the fp32
+    // partials' round trip is small beside the k loop (8B Down in the layer: 234 against 264
+    // us; the O product, k = 4096, loses: 90 against 82)
+    if (epilogue != EPI_SWIGLU && k >= 8192 && k % 64 == 0 && 2 * tiles(256, 256) >= 192 && tiles(256, 128) >= 192)
+      return 20;
     // 256x128 with 8 waves and 6 slabs (8B O and Down in the layer: 83 and 268 us against 87
     // and 278 with 4 waves and 4 slabs); SwiGLU needs 64 columns per wave: 4 waves
     if (tiles(256, 128) >= 192) return epilogue == EPI_SWIGLU ? 7 : 18;
@@ -769,7 +777,7 @@ static hipError_t launch_pipe(const bf16* A, const bf16* B, bf16* C, const bf16*
                               int ks, float* ws, hipStream_t s) {
   if (ks > 1) {
     // fp32 partials of the ks K-slices, then one pass that sums them with the epilogue
-    hipError_t e = launch_pipe_t<BM, BN, STAGES, EPI_PARTIAL>(A, B, C, R, M, N, K, ks, ws, s);
+    hipError_t e = launch_pipe_t<BM, BN, STAGES, EPI_PARTIAL, NW>(A, B, C, R, M, N, K, ks, ws, s);
     if (e != hipSuccess) return e;
     const size_t n8 = (size_t)M * N / 8;
     const int grid = (int)std::min<size_t>((n8 + 255) / 256, 4096);
@@ -871,6 +879,7 @@ hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int
     case 17: return launch_pipe<256, 256, 5>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
     case 18: return launch_pipe<256, 128, 6, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
     case kBalancedVariant: return launch_balanced(A, B, C, R, m, n, k, epilogue, s);
+    case 20: return launch_pipe<256, 256, 4, 8>(A, B, C, R, m, n, k, epilogue, 2, ws, s);
   }
   return hipErrorInvalidValue;
 }

@@ -143,7 +143,7 @@ def test_gemm_balanced_last_round(ctx, m, n, k, epi):
     assert rel_inf(got[rows], ref) <= TOL
 
 
-@pytest.mark.parametrize("variant", [-1, 6, 7, 9, 10, 11, 12, 13, 14, 15, 18, 19])
+@pytest.mark.parametrize("variant", [-1, 6, 7, 9, 10, 11, 12, 13, 14, 15, 18, 19, 20])
 def test_gemm_residual_in_place(ctx, variant):
     from nano_intra_overlap_amd import abi
 
