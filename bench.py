@@ -411,6 +411,34 @@ def main():
     log(f"plan: {plan_desc}: {ms:.3f} ms/step; decode attention {dec_avg_ms:.3f} ms/launch "
         f"x {launches_per_step:g} -> {achieved / 1e9:.0f} GB/s")
 
+    # step-time distribution (separate pass, one event pair per step; informational)
+    for _ in range(2):
+        step(plan, stack_flags)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, z in evs:
+        a.record()
+        step(plan, stack_flags)
+        z.record()
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(z) for a, z in evs])
+    dist = {q: round(float(np.percentile(per_step, p)), 4) for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
+
+    # measured copy bandwidth on this GPU: nf_copy_reference reading and writing 1 GiB
+    cbytes = 1 << 30
+    csrc = torch.ones(cbytes // 2, dtype=torch.bfloat16, device="cuda")
+    cdst = torch.empty_like(csrc)
+    abi.nf_copy_reference(cdst.data_ptr(), csrc.data_ptr(), cbytes, stream)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(3):
+        abi.nf_copy_reference(cdst.data_ptr(), csrc.data_ptr(), cbytes, stream)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * cbytes * 3 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del csrc, cdst
+
     # per-kernel breakdown (separate instrumented pass; informational)
     all_mask = (1 << abi.NF_K_CLASSES) - 1
     _, breakdown = run(plan, 5, 1, all_mask)
@@ -429,6 +457,8 @@ def main():
             per_step_ms = breakdown[k]["total_ms"] / 5
             breakdown[k]["tflops"] = round(f / (per_step_ms * 1e-3) / 1e12, 1)
             breakdown[k]["mfma_frac"] = round(f / (per_step_ms * 1e-3) / PEAK_BF16, 4)
+
+    own_peak = max((v.get("tflops", 0.0) for v in breakdown.values()), default=0.0) or None
 
     # comparison schedules on the same batch: the plain sequential layer (one nano-batch,
     # caller stream), nano-batching without overlap, and the two-stream overlap template
@@ -511,7 +541,13 @@ def main():
             "gemm_variant": args.gemm_variant,
             "gemm_variants": args.gemm_variants or None,
         },
+        "step_ms_distribution": dict(dist, steps=args.steps),
         "mfma_frac_of_bf16_peak": round(mfma_frac, 4),
+        # against the fastest of this run's own GEMM kernels (the profiled-peak convention)
+        "own_gemm_peak_tflops": own_peak,
+        "mfma_frac_of_own_gemm_peak": None if not own_peak else round(step_gemm_flops / (ms * 1e-3) / 1e12 / own_peak, 4),
+        "hbm_copy_gbps": round(copy_gbps, 1),
+        "decode_attn_vs_copy": round(achieved / 1e9 / copy_gbps, 4),
         "layer_gemm_tflops": round(step_gemm_flops / (ms * 1e-3) / 1e12, 1),
         "layer_roofline_frac": round(t_lb / (ms * 1e-3), 4),
         "sequential_ms_per_step": None if seq_ms is None else round(seq_ms, 4),
