@@ -9,9 +9,10 @@
 // Structure: a workgroup of 4 waves computes a BM x BN tile; waves form a 2 x 2 grid, each
 // owning a (BM/2) x (BN/2) sub-tile built from 32x32x16 bf16 MFMAs. Two pipelines:
 //  - gemm_pipe_kernel (K a multiple of 32, the layer's shapes): the load unit writes a ring
-//    of 4 LDS slabs directly (no register staging), 3 slabs ahead of the MFMAs; it also
-//    runs with 8 waves in a 2 x 4 grid (two waves per SIMD for the large tiles), and in a
-//    grouped mode for the experts of an MoE FFN;
+//    of 3-6 LDS slabs directly (no register staging), all but one ahead of the MFMAs; it
+//    also runs with 8 waves in a 2 x 4 grid (two waves per SIMD), with the K range split
+//    over workgroups (fp32 partials, then a reduce), over a column range of a wider product
+//    (a last round of half tiles), and in a grouped mode for the experts of an MoE FFN;
 //  - gemm_kernel (any K multiple of 8): register-staged, padded LDS, double buffered.
 // Tiles are ordered so that consecutive tiles share rows of A and columns of B, and that
 // consecutive tiles land on the same XCD (workgroups are dealt round-robin to the 8 XCDs,
