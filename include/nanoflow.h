@@ -170,6 +170,28 @@ const char *nf_last_error(const nf_ctx *ctx);
 /* Library version string, e.g. "nanoflow-mi355x 0.1". Never NULL. */
 const char *nf_version(void);
 
+/* Context tuning knobs (profiling, sweeps and tests; the defaults are the library's choice).
+ * Each applies to later calls of the context only; results do not depend on them beyond
+ * floating-point summation order. */
+
+/* Decode split-KV chunk, in KV blocks per work item: 0 (default) = chosen per nano-op from
+ * its work, else 1..4096. Errors: NF_E_ARG.                                                 */
+nf_status nf_ctx_set_decode_split(nf_ctx *ctx, int32_t blocks);
+/* Decode-attention launch: max_workgroups caps its grid (0 = one workgroup per four work
+ * units; a smaller grid makes the kernel persistent, each wave looping over units), nbuf KV
+ * blocks per online-softmax step and ring register buffers of nbuf blocks (ring - 1 steps in
+ * flight). Supported (nbuf, ring): (1, 2..4), (2, 2..3); default (1, 2).
+ * Errors: NF_E_ARG.                                                                          */
+nf_status nf_ctx_set_decode_launch(nf_ctx *ctx, int32_t max_workgroups, int32_t nbuf, int32_t ring);
+/* GEMM tile configuration of a dense op kind (NF_OP_KQV, NF_OP_O, NF_OP_UGD): which = 0 its
+ * GEMM (Up/Gate for UGD), 1 the Down GEMM of UGD; variant -1 restores the library choice,
+ * else an index of nf_gemm_variants. A variant not available at a call's shape or epilogue
+ * falls back to the library choice there. Errors: NF_E_ARG.                                 */
+nf_status nf_ctx_set_gemm_variant(nf_ctx *ctx, int32_t kind, int32_t which, int32_t variant);
+/* Counters of the stack's graph path: captures made and replays launched since the context
+ * was created (both stay 0 while graph replay is switched off). Errors: NF_E_ARG.          */
+nf_status nf_ctx_graph_stats(nf_ctx *ctx, int64_t *captures, int64_t *launches);
+
 /* ---- host-only helpers (no GPU needed) ------------------------------------------------------ */
 
 /* Validate a batch against a shape and a pool size, and derive each token's position and

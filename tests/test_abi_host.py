@@ -34,6 +34,11 @@ def test_library_exports_every_declared_function(abi):
     lib = ctypes.CDLL(abi.LIB_PATH)
     missing = [n for n in sorted(declared) if not hasattr(lib, n)]
     assert not missing, missing
+    # and the binding calls nothing the header leaves undeclared
+    bound = set(re.findall(r'^\s*"(nf_\w+)": \(', open(abi.__file__).read(), re.M))
+    assert "nf_layer_forward" in bound
+    undeclared = [n for n in sorted(bound) if n not in declared]
+    assert not undeclared, undeclared
     assert abi.nf_version().startswith("nanoflow-mi355x")
 
 
