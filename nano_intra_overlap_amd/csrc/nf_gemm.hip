@@ -200,14 +200,27 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16* __restrict__ A, c
 // ---------------------------------------------------------------------------------------
 // Pipelined variant: global -> LDS with the load unit writing LDS directly
 // (global_load_lds_dwordx4: lane l lands at LDS base + 16 l), a ring of STAGES slabs of
-// BK = 32, loads issued STAGES-1 slabs ahead of the MFMAs. Rows of a slab hold 4 chunks
-// of 16 bytes; chunk slot s of row r holds k-chunk s ^ f(r), f(r) = ((r >> 2) & 3) ^ (r & 2),
-// which makes the fragment reads (32 rows, one k-chunk) hit distinct banks for both 8- and
-// 16-lane LDS read phases. Rows past M / N are clamped to the last valid row (their results
-// are never stored); K must be a multiple of 32.
+// BK = 32 or 64 k values, loads issued STAGES-1 slabs ahead of the MFMAs. Rows of a 32-deep
+// slab hold 4 chunks of 16 bytes; chunk slot s of row r holds k-chunk s ^ f(r),
+// f(r) = ((r >> 2) & 3) ^ (r & 2), which makes the fragment reads (32 rows, one k-chunk) hit
+// distinct banks for both 8- and 16-lane LDS read phases (64-deep slabs: swz_k below). Rows
+// past M / N are clamped to the last valid row (their results are never stored); K must be
+// a multiple of BK.
 // ---------------------------------------------------------------------------------------
 
 __device__ __forceinline__ int swz(int row) { return ((row >> 2) & 3) ^ (row & 2); }
+
+// Slot swizzle for a slab row of KC 16-byte chunks: KC = 4 as above; KC = 8 (BK = 64,
+// 128-byte rows) f(r) = (r & 7) ^ ((r >> 3) & 1): 16 consecutive rows land on 16 distinct
+// (row parity, slot) pairs, i.e. distinct banks of a 256-byte read phase, and 8 consecutive
+// rows on 8 distinct slots of a 128-byte phase.
+template <int KC>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (KC == 4)
+    return swz(row);
+  else
+    return (row & 7) ^ ((row >> 3) & 1);
+}
 
 // s_waitcnt vmcnt(n) with expcnt / lgkmcnt left free (gfx9 encoding).
 template <int N>
@@ -245,6 +258,21 @@ __device__ __forceinline__ void interleave_reads() {
   if constexpr (NR > P) __builtin_amdgcn_sched_group_barrier(0x100, NR - P, 0);
 }
 
+// One MFMA, then an LDS read while any are left, then a global (direct-to-LDS) load while
+// any are left, repeated; leftover loads at the end. Used by the 64-deep slabs, whose refill
+// step also carries the next step's reads.
+template <int NL, int NR, int NM>
+__device__ __forceinline__ void interleave_mixed() {
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+    if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
+    if (i < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // VMEM read
+  }
+  if constexpr (NR > NM) __builtin_amdgcn_sched_group_barrier(0x100, NR - NM, 0);
+  if constexpr (NL > NM) __builtin_amdgcn_sched_group_barrier(0x020, NL - NM, 0);
+}
+
 // As interleave_reads, with NL global (direct-to-LDS) loads first: MFMA, load, ..., then
 // MFMA, LDS read, ..., then whatever is left (MFMAs, or reads when the tile has fewer MFMAs
 // than memory instructions).
@@ -267,19 +295,21 @@ __device__ __forceinline__ void interleave_loads_reads() {
   if constexpr (NR > PR) __builtin_amdgcn_sched_group_barrier(0x100, NR - PR, 0);
 }
 
-template <int BM, int BN, int STAGES, int EPI, bool GRP = false, int NW = 4>
+template <int BM, int BN, int STAGES, int EPI, bool GRP = false, int NW = 4, int KC = 4>
 __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restrict__ A0, const bf16* __restrict__ B0,
                                                         bf16* C0, const bf16* R, int M0, int N, int K, int ldc,
                                                         int b_up, int tiles_m0,
                                                         int tiles_n, int per_xcd, float* __restrict__ part,
                                                         GroupArgs ga) {
-  constexpr int BK = 32;
+  // KC 16-byte k-chunks per slab row: slabs of BK = 32 (KC = 4) or 64 (KC = 8) k values
+  static_assert(KC == 4 || KC == 8, "slabs of 32 or 64 k values");
+  constexpr int BK = 8 * KC, Q = KC / 2;  // Q: k16 MFMA steps per slab
   // NW waves in a 2 x (NW / 2) grid; each wave a WTM x WTN sub-tile
   constexpr int NT = 64 * NW, WAVES_N = NW / 2;
   constexpr int WTM = BM / 2, WTN = BN / WAVES_N;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int A_CH = BM * 4, B_CH = BN * 4;       // 16-byte chunks per slab
+  constexpr int A_CH = BM * KC, B_CH = BN * KC;     // 16-byte chunks per slab
   constexpr int STAGE_BYTES = (A_CH + B_CH) * 16;
   constexpr int A_LOADS = A_CH / NT, B_LOADS = B_CH / NT;  // per thread (= per wave instruction count)
   static_assert(A_LOADS * NT == A_CH && B_LOADS * NT == B_CH, "slab chunks split evenly over the threads");
@@ -344,7 +374,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
 #pragma unroll
   for (int i = 0; i < A_LOADS; ++i) {
     const int c = (i * NW + wave) * 64 + lane;
-    const int row = c >> 2, kc = (c & 3) ^ swz(row);
+    const int row = c / KC, kc = (c % KC) ^ swz_k<KC>(row);
     int gr = min(m0 + row, M - 1);
     if constexpr (GRP) {
       if (a_rows) gr = a_rows[gr];  // gathered rows of A
@@ -354,7 +384,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
     const int c = (i * NW + wave) * 64 + lane;
-    const int row = c >> 2, kc = (c & 3) ^ swz(row);
+    const int row = c / KC, kc = (c % KC) ^ swz_k<KC>(row);
     int gr;
     if constexpr (EPI == EPI_SWIGLU) {
       const int sl = row / WTN, tt = row % WTN, p = tt / 64, u = tt % 64;
@@ -400,20 +430,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
 
   // fragment read offsets (bytes within a slab): row (l % 32) of each 32-row tile, k-chunk 2 kk + l / 32
   const int fr = lane & 31, fk = lane >> 5;
-  int a_off[TM][2], b_off[TN][2];
+  int a_off[TM][Q], b_off[TN][Q];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < Q; ++kk) {
       const int row = wm * WTM + i * 32 + fr;
-      a_off[i][kk] = row * 64 + (((2 * kk + fk) ^ swz(row)) * 16);
+      a_off[i][kk] = row * (16 * KC) + (((2 * kk + fk) ^ swz_k<KC>(row)) * 16);
     }
 #pragma unroll
   for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < Q; ++kk) {
       const int row = wn * WTN + j * 32 + fr;
-      b_off[j][kk] = A_CH * 16 + row * 64 + (((2 * kk + fk) ^ swz(row)) * 16);
+      b_off[j][kk] = A_CH * 16 + row * (16 * KC) + (((2 * kk + fk) ^ swz_k<KC>(row)) * 16);
     }
 
   // Fragments of the two 16-wide k halves of a slab live in separate registers, so the LDS
@@ -436,7 +466,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
       for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
   // wait until at most `newer` slabs issued after the awaited one are still in flight
-  static_assert(STAGES >= 3 && STAGES <= 6, "wait_slab covers up to five newer slabs");
+  static_assert(STAGES >= 2 && STAGES <= 6, "wait_slab covers up to five newer slabs");
   static_assert(NL * (STAGES - 1) < 64, "the in-flight loads fit the wait counter");
   auto wait_slab = [&](int newer) {
     if constexpr (STAGES > 5) {
@@ -459,11 +489,24 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
   // MFMAs of the second half with the reads of slab kt+1's first half slotted between them.
   // Each MFMA phase starts with no newer LDS read in flight, so its wait covers only reads
   // issued a whole phase earlier.
+  // k16 steps 0 .. Q-2 of slab kt: the reads of step q + 1 between the MFMAs of step q
+  // (fragment sets alternate; Q is even, so step Q - 1 always uses the second set)
+  auto steps_but_last = [&](int kt) {
+#pragma unroll
+    for (int q = 0; q + 1 < Q; ++q) {
+      if (q % 2 == 0) {
+        read_frags(kt, q + 1, fa1, fb1);
+        mfmas(fa0, fb0);
+      } else {
+        read_frags(kt, q + 1, fa0, fb0);
+        mfmas(fa1, fb1);
+      }
+      interleave_reads<TM + TN, TM * TN>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   auto trip = [&](int kt, auto wait_next, bool refill) {
-    read_frags(kt, 1, fa1, fb1);
-    mfmas(fa0, fb0);
-    interleave_reads<TM + TN, TM * TN>();
-    __builtin_amdgcn_sched_barrier(0);
+    steps_but_last(kt);
     wait_next();
     lds_barrier();  // every wave has read slab kt
     __builtin_amdgcn_sched_barrier(0);
@@ -472,10 +515,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
     if (refill) issue(kt + STAGES);
     read_frags(kt + 1, 0, fa0, fb0);
     mfmas(fa1, fb1);
-    if (refill)
+    if (!refill)
+      interleave_reads<TM + TN, TM * TN>();
+    else if constexpr (KC == 4)
       interleave_loads_reads<NL, TM + TN, TM * TN>();
     else
-      interleave_reads<TM + TN, TM * TN>();
+      interleave_mixed<NL, TM + TN, TM * TN>();
     __builtin_amdgcn_sched_barrier(0);
   };
   // steady state: slabs kt+1 .. kt+STAGES-1 in flight, slab kt+1 is awaited with the two
@@ -485,10 +530,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
   for (; kt + STAGES < nk; ++kt) trip(kt, [] { wait_vmcnt<NL * (STAGES - 2)>(); }, true);
   // drain: no refills; at most min(2, nk - 2 - kt) newer slabs remain
   for (; kt + 1 < nk; ++kt) trip(kt, [&] { wait_slab(min(STAGES - 2, nk - 2 - kt)); }, false);
-  read_frags(nk - 1, 1, fa1, fb1);
-  mfmas(fa0, fb0);
-  interleave_reads<TM + TN, TM * TN>();
-  __builtin_amdgcn_sched_barrier(0);
+  steps_but_last(nk - 1);
   mfmas(fa1, fb1);
 
   // Epilogue through LDS: waves park their results row-major in the (now idle) slab ring,
@@ -603,8 +645,17 @@ static const GemmVariant kVariants[] = {
     // 256x256, 8 waves, K split in 2 (fp32 partials + reduce): a product of n = 4096 at 2048
     // rows (8B O and Down) in 256 workgroups of the larger tile; not SwiGLU
     {256, 256, 32, 2, 4, 8},  // 20
+    // slabs of 64 k values (K % 64 == 0): half the barriers per k, whole 128-byte lines per
+    // row load; 2 slabs of 256x256 (128 KB) or 3 of 256x128 (144 KB)
+    {256, 256, 64, 1, 2, 4},  // 21
+    {256, 256, 64, 1, 2, 8},  // 22
+    {256, 128, 64, 1, 3, 8},  // 23 (not SwiGLU)
+    {256, 128, 64, 1, 3, 4},  // 24
+    {256, 256, 64, 2, 2, 8},  // 25: variant 22 with K split in 2 (not SwiGLU)
+    {256, 256, 64, 1, 2, 8},  // 26: variant 19's column split with 64-deep slabs
+    {256, 192, 64, 1, 2, 4},  // 27: variant 14 with 64-deep slabs (not SwiGLU)
 };
-constexpr int kBalancedVariant = 19;
+constexpr int kBalancedVariant = 19, kBalancedDeepVariant = 26;
 static constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 int gemm_variant_count() { return kNumVariants; }
@@ -614,8 +665,8 @@ bool gemm_variant_supported(int v, int m, int n, int k, int epilogue) {
   if (v < 0 || v >= kNumVariants) return false;
   const GemmVariant& g = kVariants[v];
   if (epilogue == EPI_SWIGLU && (g.bn < 128 || (g.bn / (g.waves / 2)) % 64 != 0)) return false;
-  if (v >= 6 && (k % 32 != 0)) return false;
-  if (g.ks > 1 && (epilogue == EPI_SWIGLU || k % (32 * g.ks) != 0)) return false;
+  if (v >= 6 && (k % g.bk != 0)) return false;
+  if (g.ks > 1 && (epilogue == EPI_SWIGLU || k % (g.bk * g.ks) != 0)) return false;
   (void)m;
   (void)n;
   return true;
@@ -629,26 +680,31 @@ size_t gemm_workspace_bytes(int v, int m, int n) {
 int gemm_default_variant(int m, int n, int k, int epilogue) {
   if (k % 32 == 0 && m >= 64) {
     // pipelined tiles (measured on MI355X at the layer's shapes): the largest tile that
-    // still gives at least 192 tiles (three quarters of the 256 CUs in one round)
+    // still gives at least 192 tiles (three quarters of the 256 CUs in one round); slabs of
+    // 64 k values wherever K allows (in the 8B layer at 2048 rows: O 88 -> 78 us, Up/Gate
+    // 435 -> 411, Down 232 -> 225, the layer 2.17 -> 2.12 ms)
+    const bool deep = k % 64 == 0;
     const int nn = epilogue == EPI_SWIGLU ? 2 * n : n;
     auto tiles = [&](int bm, int bn) { return ((m + bm - 1) / bm) * ((nn + bn - 1) / bn); };
     if (tiles(256, 256) >= 192) {
       // 256x192 when it fills whole rounds of the 256 CUs and 256x256 does not (8B KQV at
       // 2048 rows: 256 tiles instead of 192; 100.7 against 106.7 us in the layer)
       if (epilogue != EPI_SWIGLU && nn % 192 == 0 && tiles(256, 192) % 256 == 0 && tiles(256, 256) % 256 != 0)
-        return 14;
-      // SwiGLU (8B Up/Gate): the balanced launch (plain variant 12 when no round is left
-      // half empty)
-      return epilogue == EPI_SWIGLU ? kBalancedVariant : 12;
+        return deep ? 27 : 14;
+      // SwiGLU (8B Up/Gate): the balanced launch (plain 256x256 when no round is left half
+      // empty)
+      if (epilogue == EPI_SWIGLU) return deep ? kBalancedDeepVariant : kBalancedVariant;
+      return deep ? 22 : 12;
     }
     // long K (>= 8192): 256x256 with K split in 2 when that gives >= 192 workgroups; the fp32
     // partials' round trip is small beside the k loop (8B Down in the layer: 234 against 264
     // us; the O product, k = 4096, loses: 90 against 82)
     if (epilogue != EPI_SWIGLU && k >= 8192 && k % 64 == 0 && 2 * tiles(256, 256) >= 192 && tiles(256, 128) >= 192)
-      return 20;
-    // 256x128 with 8 waves and 6 slabs (8B O and Down in the layer: 83 and 268 us against 87
-    // and 278 with 4 waves and 4 slabs); SwiGLU needs 64 columns per wave: 4 waves
-    if (tiles(256, 128) >= 192) return epilogue == EPI_SWIGLU ? 7 : 18;
+      return k % 128 == 0 ? 25 : 20;
+    // 256x128 with 8 waves and 6 slabs of 32 or 3 of 64 (8B O and Down in the layer: 83 and
+    // 268 us against 87 and 278 with 4 waves and 4 slabs of 32); SwiGLU needs 64 columns per
+    // wave: 4 waves
+    if (tiles(256, 128) >= 192) return epilogue == EPI_SWIGLU ? 7 : (deep ? 23 : 18);
     const int t = tiles(128, 128);
     if (t < 128 && epilogue != EPI_SWIGLU) {
       // half the CUs or fewer busy: K slices of at least 1024 (measured: 2 slices pay off
@@ -725,7 +781,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 // ldc: row stride of C and R (N for a whole product); b_up: SwiGLU's row of B holding the
 // up weights of output column 0 (N for a whole product, gate rows [0, N) then up rows).
-template <int BM, int BN, int STAGES, int EPI, int NW = 4>
+template <int BM, int BN, int STAGES, int EPI, int NW = 4, int KC = 4>
 static hipError_t launch_pipe_t(const bf16* A, const bf16* B, bf16* C, const bf16* R, int M, int N, int K, int ks,
                                 float* part, hipStream_t s, int ldc = -1, int b_up = -1) {
   if (ldc < 0) ldc = N;
@@ -734,8 +790,8 @@ static hipError_t launch_pipe_t(const bf16* A, const bf16* B, bf16* C, const bf1
   const int tiles_n = (EPI == EPI_SWIGLU) ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
   const int ntiles = tiles_m * tiles_n;
   const int per_xcd = (ntiles + kNumXcd - 1) / kNumXcd;
-  const size_t lds = (size_t)STAGES * (BM + BN) * 64;
-  auto kern = gemm_pipe_kernel<BM, BN, STAGES, EPI, false, NW>;
+  const size_t lds = (size_t)STAGES * (BM + BN) * 16 * KC;
+  auto kern = gemm_pipe_kernel<BM, BN, STAGES, EPI, false, NW, KC>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -773,12 +829,12 @@ static hipError_t launch_grouped_t(const bf16* A, const int32_t* a_rows, const b
   return hipGetLastError();
 }
 
-template <int BM, int BN, int STAGES, int NW = 4>
+template <int BM, int BN, int STAGES, int NW = 4, int KC = 4>
 static hipError_t launch_pipe(const bf16* A, const bf16* B, bf16* C, const bf16* R, int M, int N, int K, int epi,
                               int ks, float* ws, hipStream_t s) {
   if (ks > 1) {
     // fp32 partials of the ks K-slices, then one pass that sums them with the epilogue
-    hipError_t e = launch_pipe_t<BM, BN, STAGES, EPI_PARTIAL, NW>(A, B, C, R, M, N, K, ks, ws, s);
+    hipError_t e = launch_pipe_t<BM, BN, STAGES, EPI_PARTIAL, NW, KC>(A, B, C, R, M, N, K, ks, ws, s);
     if (e != hipSuccess) return e;
     const size_t n8 = (size_t)M * N / 8;
     const int grid = (int)std::min<size_t>((n8 + 255) / 256, 4096);
@@ -787,11 +843,11 @@ static hipError_t launch_pipe(const bf16* A, const bf16* B, bf16* C, const bf16*
     return hipGetLastError();
   }
   switch (epi) {
-    case EPI_STORE: return launch_pipe_t<BM, BN, STAGES, EPI_STORE, NW>(A, B, C, R, M, N, K, 1, nullptr, s);
-    case EPI_RESID: return launch_pipe_t<BM, BN, STAGES, EPI_RESID, NW>(A, B, C, R, M, N, K, 1, nullptr, s);
+    case EPI_STORE: return launch_pipe_t<BM, BN, STAGES, EPI_STORE, NW, KC>(A, B, C, R, M, N, K, 1, nullptr, s);
+    case EPI_RESID: return launch_pipe_t<BM, BN, STAGES, EPI_RESID, NW, KC>(A, B, C, R, M, N, K, 1, nullptr, s);
     case EPI_SWIGLU:
       if constexpr ((BN / (NW / 2)) % 64 == 0)
-        return launch_pipe_t<BM, BN, STAGES, EPI_SWIGLU, NW>(A, B, C, R, M, N, K, 1, nullptr, s);
+        return launch_pipe_t<BM, BN, STAGES, EPI_SWIGLU, NW, KC>(A, B, C, R, M, N, K, 1, nullptr, s);
       return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
@@ -825,31 +881,36 @@ static int device_cus() {
 // rest in one round of 256x128 tiles (4 waves with SwiGLU, else 8 waves and 6 slabs); the
 // plain 256x256 launch when the last round is more than half full or the product has fewer
 // tiles than one round.
-template <int EPI>
+template <int EPI, int KC = 4>
 static hipError_t launch_balanced_t(const bf16* A, const bf16* B, bf16* C, const bf16* R, int m, int n, int k,
                                     hipStream_t s) {
+  constexpr int S_FULL = KC == 4 ? 4 : 2;  // slabs of the 256x256 tiles (128 KB either way)
   const int cus = device_cus();
   const int cw = EPI == EPI_SWIGLU ? 128 : 256;  // output columns of one 256x256 tile
   const int rt = (m + 255) / 256, ct = (n + cw - 1) / cw, T = rt * ct, r = T % cus;
   const int ct1 = (T - r) / rt;
   if (r == 0 || ct1 <= 0 || ct1 >= ct || 2 * rt * (ct - ct1) > cus)
-    return launch_pipe_t<256, 256, 4, EPI, 8>(A, B, C, R, m, n, k, 1, nullptr, s);
+    return launch_pipe_t<256, 256, S_FULL, EPI, 8, KC>(A, B, C, R, m, n, k, 1, nullptr, s);
   const int n1 = ct1 * cw;
-  hipError_t e = launch_pipe_t<256, 256, 4, EPI, 8>(A, B, C, R, m, n1, k, 1, nullptr, s, n, n);
+  hipError_t e = launch_pipe_t<256, 256, S_FULL, EPI, 8, KC>(A, B, C, R, m, n1, k, 1, nullptr, s, n, n);
   if (e != hipSuccess) return e;
   const bf16* R2 = R ? R + n1 : nullptr;
+  constexpr int S_HALF4 = KC == 4 ? 4 : 3, S_HALF8 = KC == 4 ? 6 : 3;  // slabs of the 256x128 tiles
   if constexpr (EPI == EPI_SWIGLU)
-    return launch_pipe_t<256, 128, 4, EPI, 4>(A, B + (size_t)n1 * k, C + n1, R2, m, n - n1, k, 1, nullptr, s, n, n);
+    return launch_pipe_t<256, 128, S_HALF4, EPI, 4, KC>(A, B + (size_t)n1 * k, C + n1, R2, m, n - n1, k, 1, nullptr, s,
+                                                        n, n);
   else
-    return launch_pipe_t<256, 128, 6, EPI, 8>(A, B + (size_t)n1 * k, C + n1, R2, m, n - n1, k, 1, nullptr, s, n, n);
+    return launch_pipe_t<256, 128, S_HALF8, EPI, 8, KC>(A, B + (size_t)n1 * k, C + n1, R2, m, n - n1, k, 1, nullptr, s,
+                                                        n, n);
 }
 
+template <int KC>
 static hipError_t launch_balanced(const bf16* A, const bf16* B, bf16* C, const bf16* R, int m, int n, int k, int epi,
                                   hipStream_t s) {
   switch (epi) {
-    case EPI_STORE: return launch_balanced_t<EPI_STORE>(A, B, C, R, m, n, k, s);
-    case EPI_RESID: return launch_balanced_t<EPI_RESID>(A, B, C, R, m, n, k, s);
-    case EPI_SWIGLU: return launch_balanced_t<EPI_SWIGLU>(A, B, C, R, m, n, k, s);
+    case EPI_STORE: return launch_balanced_t<EPI_STORE, KC>(A, B, C, R, m, n, k, s);
+    case EPI_RESID: return launch_balanced_t<EPI_RESID, KC>(A, B, C, R, m, n, k, s);
+    case EPI_SWIGLU: return launch_balanced_t<EPI_SWIGLU, KC>(A, B, C, R, m, n, k, s);
   }
   return hipErrorInvalidValue;
 }
@@ -879,8 +940,15 @@ hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int
     case 16: return launch_pipe<256, 256, 5, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
     case 17: return launch_pipe<256, 256, 5>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
     case 18: return launch_pipe<256, 128, 6, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
-    case kBalancedVariant: return launch_balanced(A, B, C, R, m, n, k, epilogue, s);
+    case kBalancedVariant: return launch_balanced<4>(A, B, C, R, m, n, k, epilogue, s);
     case 20: return launch_pipe<256, 256, 4, 8>(A, B, C, R, m, n, k, epilogue, 2, ws, s);
+    case 21: return launch_pipe<256, 256, 2, 4, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 22: return launch_pipe<256, 256, 2, 8, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 23: return launch_pipe<256, 128, 3, 8, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 24: return launch_pipe<256, 128, 3, 4, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 25: return launch_pipe<256, 256, 2, 8, 8>(A, B, C, R, m, n, k, epilogue, 2, ws, s);
+    case kBalancedDeepVariant: return launch_balanced<8>(A, B, C, R, m, n, k, epilogue, s);
+    case 27: return launch_pipe<256, 192, 2, 4, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
   }
   return hipErrorInvalidValue;
 }

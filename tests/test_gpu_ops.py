@@ -45,9 +45,9 @@ LAYER_GEMMS = [(1024, 6144, 4096, 0), (2048, 4096, 4096, 1), (1536, 14336, 4096,
                (1024, 8192, 1024, 1)]
 
 
-def _supported(v, k, epi, bn, ks=1, waves=4):
-    return (not (epi == 2 and (bn < 128 or (bn // (waves // 2)) % 64)) and not (v >= 6 and k % 32)
-            and not (ks > 1 and (epi == 2 or k % (32 * ks))))
+def _supported(v, k, epi, bn, ks=1, waves=4, bk=32):
+    return (not (epi == 2 and (bn < 128 or (bn // (waves // 2)) % 64)) and not (v >= 6 and k % bk)
+            and not (ks > 1 and (epi == 2 or k % (bk * ks))))
 
 
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
@@ -66,7 +66,7 @@ def test_gemm_all_variants(ctx, m, n, k, epi):
         ref = ol.swiglu(ref, n)
     dA, dB, dR = _dev(A), _dev(B), _dev(R)
     for v, (bm, bn, bk, ks, waves) in enumerate(abi.nf_gemm_variants()):
-        if not _supported(v, k, epi, bn, ks, waves):
+        if not _supported(v, k, epi, bn, ks, waves, bk):
             continue
         dC = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
         log_case(f"gemm m={m} n={n} k={k} epi={epi} variant={v}")
@@ -95,7 +95,7 @@ def test_gemm_layer_shapes_sampled_rows(ctx, m, n, k, epi):
         ref = ol.swiglu(ref, n)
     dA, dB, dR = _dev(A), _dev(B), _dev(R)
     for v, (bm, bn, bk, ks, waves) in [(-1, (0, 0, 0, 1, 4))] + list(enumerate(abi.nf_gemm_variants())):
-        if v >= 0 and (not _supported(v, k, epi, bn, ks, waves) or v < 6):
+        if v >= 0 and (not _supported(v, k, epi, bn, ks, waves, bk) or v < 6):
             continue
         dC = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
         log_case(f"gemm layer shape m={m} n={n} k={k} epi={epi} variant={v}")
@@ -143,7 +143,38 @@ def test_gemm_balanced_last_round(ctx, m, n, k, epi):
     assert rel_inf(got[rows], ref) <= TOL
 
 
-@pytest.mark.parametrize("variant", [-1, 6, 7, 9, 10, 11, 12, 13, 14, 15, 18, 19, 20])
+@pytest.mark.parametrize("m,n,k,epi", [(600, 1000, 1024, 0), (600, 1000, 1024, 1), (513, 768, 640, 2), (64, 256, 64, 1)])
+def test_gemm_deep_slabs_bit_identical(ctx, m, n, k, epi):
+    """The 64-deep slab variants (21-24, 26, 27) sum k in the same order as the 32-deep ones: every
+    output bit-identical to variant 12 (ragged m and n, a single slab at k = 64)."""
+    from nano_intra_overlap_amd import abi
+
+    rng = np.random.default_rng(m + 3 * n + k + epi)
+    A = rand_bf16(rng, (m, k))
+    B = rand_bf16(rng, (2 * n if epi == 2 else n, k), 0.05)
+    R = rand_bf16(rng, (m, n))
+    dA, dB, dR = _dev(A), _dev(B), _dev(R)
+    outs = {}
+    for v in (12, 21, 22, 23, 24, 26, 27):
+        if v in (23, 27) and epi == 2:
+            continue
+        dC = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+        log_case(f"gemm deep slabs m={m} n={n} k={k} epi={epi} variant={v}")
+        abi.nf_op_gemm(ctx, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), dR.data_ptr(), m, n, k, epi, v,
+                       torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        outs[v] = _host(dC)
+    for v, o in outs.items():
+        assert np.array_equal(o, outs[12]), f"variant {v} differs from variant 12"
+    ref = ol.linear(f64(A), f64(B))
+    if epi == 1:
+        ref = f64(R) + ref
+    if epi == 2:
+        ref = ol.swiglu(ref, n)
+    assert rel_inf(f64(outs[12]), ref) <= TOL
+
+
+@pytest.mark.parametrize("variant", [-1, 6, 7, 9, 10, 11, 12, 13, 14, 15, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27])
 def test_gemm_residual_in_place(ctx, variant):
     from nano_intra_overlap_amd import abi
 
