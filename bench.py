@@ -66,10 +66,62 @@ def parse():
                    help="layer stacks: layers the CPU oracle runs on its sample (its time is scaled to all layers)")
     p.add_argument("--kv-io", action="store_true",
                    help="also measure KV offload / multi-round reload (adds a kv_io object to the JSON line)")
+    p.add_argument("--vendor-gemm", action="store_true",
+                   help="also time the layer's four dense products alone, this library's GEMM against the "
+                        "vendor library's (torch.nn.functional.linear, hipBLASLt), into gemm_vs_vendor")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="run one plain device copy of this many MiB first (a known-size reference for "
                         "hardware traffic counters)")
     return p.parse_args()
+
+
+def gemm_vs_vendor(ctx, shape, T: int, seed: int) -> dict:
+    """The layer's dense products at T rows, each alone and back to back: nf_op_gemm (library
+    tile choice, fused epilogue) against torch.nn.functional.linear (the vendor library's
+    plain product). Best of 3 x 30 launches timed with events on torch's current stream; a
+    comparison only, nothing of the layer runs through the vendor library."""
+    import torch
+
+    from nano_intra_overlap_amd import abi
+
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    prods = {"kqv": (shape.qkv_rows, shape.hidden, 0), "o": (shape.hidden, shape.q_width, 1),
+             "ug_swiglu": (shape.ffn, shape.hidden, 2), "down": (shape.hidden, shape.ffn, 1)}
+    stream = torch.cuda.current_stream()
+
+    def best_us(fn):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(30):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / 30 * 1e3)
+        return best
+
+    res = {}
+    for name, (n, k, epi) in prods.items():
+        nb = 2 * n if epi == 2 else n
+        A = (torch.randn(T, k, device="cuda", generator=g) * 0.05).to(torch.bfloat16)
+        B = (torch.randn(nb, k, device="cuda", generator=g) * 0.05).to(torch.bfloat16)
+        R = torch.randn(T, n, device="cuda", generator=g).to(torch.bfloat16)
+        C = torch.empty(T, n, device="cuda", dtype=torch.bfloat16)
+        ours = best_us(lambda: abi.nf_op_gemm(ctx, A.data_ptr(), B.data_ptr(), C.data_ptr(), R.data_ptr(), T, n, k,
+                                              epi, -1, stream.cuda_stream))
+        vendor = best_us(lambda: torch.nn.functional.linear(A, B))
+        flops = 2.0 * T * nb * k
+        res[name] = {"m": T, "n": nb, "k": k, "variant": abi.nf_gemm_choice(T, n, k, epi)[0],
+                     "ours_us": round(ours, 1), "vendor_us": round(vendor, 1),
+                     "ours_tflops": round(flops / ours / 1e6, 1), "vendor_tflops": round(flops / vendor / 1e6, 1)}
+        print(f"[bench] {name}: ours {ours:.1f} us, vendor {vendor:.1f} us (plain product)", file=sys.stderr,
+              flush=True)
+        del A, B, R, C
+    return res
 
 
 def kernel_source_hash(files) -> str:
@@ -572,6 +624,8 @@ def main():
         "cpu_baseline": cpu,
         "kv_io": kv_io,
     }
+    if args.vendor_gemm and not shape.n_experts:
+        out["gemm_vs_vendor"] = gemm_vs_vendor(ctx, shape, T, args.seed)
     abi.nf_ctx_destroy(ctx)
     print(json.dumps(out))
 
