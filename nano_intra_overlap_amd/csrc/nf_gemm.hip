@@ -654,6 +654,9 @@ static const GemmVariant kVariants[] = {
     {256, 256, 64, 2, 2, 8},  // 25: variant 22 with K split in 2 (not SwiGLU)
     {256, 256, 64, 1, 2, 8},  // 26: variant 19's column split with 64-deep slabs
     {256, 192, 64, 1, 2, 4},  // 27: variant 14 with 64-deep slabs (not SwiGLU)
+    {128, 128, 64, 1, 4, 4},  // 28: 4 slabs of 128x128 (128 KB)
+    {128, 256, 64, 1, 3, 4},  // 29: 3 slabs of 128x256 (144 KB)
+    {128, 256, 64, 1, 3, 8},  // 30
 };
 constexpr int kBalancedVariant = 19, kBalancedDeepVariant = 26;
 static constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
@@ -701,10 +704,11 @@ int gemm_default_variant(int m, int n, int k, int epilogue) {
     // us; the O product, k = 4096, loses: 90 against 82)
     if (epilogue != EPI_SWIGLU && k >= 8192 && k % 64 == 0 && 2 * tiles(256, 256) >= 192 && tiles(256, 128) >= 192)
       return k % 128 == 0 ? 25 : 20;
-    // 256x128 with 8 waves and 6 slabs of 32 or 3 of 64 (8B O and Down in the layer: 83 and
-    // 268 us against 87 and 278 with 4 waves and 4 slabs of 32); SwiGLU needs 64 columns per
-    // wave: 4 waves
-    if (tiles(256, 128) >= 192) return epilogue == EPI_SWIGLU ? 7 : (deep ? 23 : 18);
+    // 256x128 with 8 waves and 6 slabs of 32 (8B O and Down in the layer: 83 and 268 us
+    // against 87 and 278 with 4 waves and 4 slabs of 32), or with 64-deep slabs 128x256 with
+    // 8 waves and 3 slabs (8B O alone: 68 against 75 us for 256x128); SwiGLU needs 64
+    // columns per wave: 4 waves
+    if (tiles(256, 128) >= 192) return epilogue == EPI_SWIGLU ? 7 : (deep ? 30 : 18);
     const int t = tiles(128, 128);
     if (t < 128 && epilogue != EPI_SWIGLU) {
       // half the CUs or fewer busy: K slices of at least 1024 (measured: 2 slices pay off
@@ -713,7 +717,9 @@ int gemm_default_variant(int m, int n, int k, int epilogue) {
       if (k % 128 == 0 && k / 4 >= 1024) return 11;
       if (k % 64 == 0 && k / 2 >= 1024) return 10;
     }
-    return 9;
+    // 128x128, 4 slabs of 64 where K allows (8B O and Down at 1024 rows, alone: 42 and 128
+    // against 43 and 139 us with slabs of 32)
+    return deep ? 28 : 9;
   }
   // enough tiles to cover the 256 CUs at least once; otherwise smaller tiles
   auto tiles = [&](int v) {
@@ -949,6 +955,9 @@ hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int
     case 25: return launch_pipe<256, 256, 2, 8, 8>(A, B, C, R, m, n, k, epilogue, 2, ws, s);
     case kBalancedDeepVariant: return launch_balanced<8>(A, B, C, R, m, n, k, epilogue, s);
     case 27: return launch_pipe<256, 192, 2, 4, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 28: return launch_pipe<128, 128, 4, 4, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 29: return launch_pipe<128, 256, 3, 4, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 30: return launch_pipe<128, 256, 3, 8, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
   }
   return hipErrorInvalidValue;
 }
