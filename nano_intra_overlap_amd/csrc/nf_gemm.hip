@@ -814,14 +814,14 @@ static hipError_t launch_pipe_t(const bf16* A, const bf16* B, bf16* C, const bf1
 // row grp[n_groups + g] of the grouped order; A's rows gathered through a_rows when given)
 // by B + g * b_stride. The grid covers the most tiles any split of n_rows rows can need;
 // workgroups past the actual tiles exit at once.
-template <int BM, int BN, int STAGES, int EPI, int NW = 4>
+template <int BM, int BN, int STAGES, int EPI, int NW = 4, int KC = 4>
 static hipError_t launch_grouped_t(const bf16* A, const int32_t* a_rows, const bf16* B, long long b_stride, bf16* C,
                                    const int32_t* grp, int n_groups, int n_rows, int N, int K, hipStream_t s) {
   const int tiles_n = (EPI == EPI_SWIGLU) ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
   const long long max_tiles = ((long long)(n_rows + BM - 1) / BM + n_groups) * tiles_n;
   const int per_xcd = (int)((max_tiles + kNumXcd - 1) / kNumXcd);
-  const size_t lds = (size_t)STAGES * (BM + BN) * 64;
-  auto kern = gemm_pipe_kernel<BM, BN, STAGES, EPI, true, NW>;
+  const size_t lds = (size_t)STAGES * (BM + BN) * 16 * KC;
+  auto kern = gemm_pipe_kernel<BM, BN, STAGES, EPI, true, NW, KC>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -965,15 +965,19 @@ hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int
 bool gemm_grouped_variant_ok(int variant, int n, int k, int epilogue) {
   const bool tile = (variant >= 6 && variant <= 9) || variant == 12 ||
                     ((variant == 13 || variant == 18) && epilogue != EPI_SWIGLU);  // 32 columns per wave: no SwiGLU
-  return tile && k % 32 == 0 && n % 8 == 0 && (epilogue == EPI_STORE || epilogue == EPI_SWIGLU);
+  const bool deep = variant == 22 || (variant >= 28 && variant <= 30);          // slabs of 64 k values
+  return (tile ? k % 32 == 0 : deep && k % 64 == 0) && n % 8 == 0 &&
+         (epilogue == EPI_STORE || epilogue == EPI_SWIGLU);
 }
 
-int gemm_grouped_default_variant(int n_rows, int n_groups, int epilogue) {
-  // measured on MI355X with 8 experts of the Mixtral shape: Up/Gate takes 256x256 tiles
-  // (8 waves: 1242 against 1282 us with 4 at 2048 tokens) once the groups average 512 rows
-  // (2048 tokens, top 2), 128x256 below; Down always takes 128x128 with 4 waves (its long k
-  // loop wants the most tiles; each group's last, partly filled tile wastes less; 8-wave
-  // 256x128 measured 833 against 771 us)
+int gemm_grouped_default_variant(int n_rows, int n_groups, int k, int epilogue) {
+  // measured on MI355X with 8 experts of the Mixtral shape at 2048 tokens (top 2): with
+  // slabs of 64 k values (K % 64 == 0) 128x256 tiles with 8 waves for both products (the
+  // layer 3.54 -> 3.35 ms; Up/Gate 1246 -> 1155 us, Down 751 -> 644 us against 256x256 /
+  // 128x128 with slabs of 32; 256x256 deep: 1177-1189 us). Slabs of 32: Up/Gate takes
+  // 256x256 tiles (8 waves: 1242 against 1282 us with 4) once the groups average 512 rows,
+  // 128x256 below; Down 128x128 with 4 waves (8-wave 256x128: 833 against 771 us).
+  if (k % 64 == 0) return 30;
   if (epilogue == EPI_SWIGLU) return n_rows >= 512 * n_groups ? 12 : 8;
   return 9;
 }
@@ -997,6 +1001,19 @@ hipError_t launch_gemm_grouped(const bf16* A, const int32_t* a_rows, const bf16*
                        : launch_grouped_t<256, 256, 4, EPI_STORE, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s);
     case 13: return launch_grouped_t<256, 128, 4, EPI_STORE, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s);
     case 18: return launch_grouped_t<256, 128, 6, EPI_STORE, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s);
+    // 64-deep slabs
+    case 22:
+      return sw ? launch_grouped_t<256, 256, 2, EPI_SWIGLU, 8, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s)
+                : launch_grouped_t<256, 256, 2, EPI_STORE, 8, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s);
+    case 28:
+      return sw ? launch_grouped_t<128, 128, 4, EPI_SWIGLU, 4, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s)
+                : launch_grouped_t<128, 128, 4, EPI_STORE, 4, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s);
+    case 29:
+      return sw ? launch_grouped_t<128, 256, 3, EPI_SWIGLU, 4, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s)
+                : launch_grouped_t<128, 256, 3, EPI_STORE, 4, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s);
+    case 30:
+      return sw ? launch_grouped_t<128, 256, 3, EPI_SWIGLU, 8, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s)
+                : launch_grouped_t<128, 256, 3, EPI_STORE, 8, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s);
   }
   return hipErrorInvalidValue;
 }

@@ -62,7 +62,7 @@ hipError_t launch_gemm_grouped(const bf16* A, const int32_t* a_rows, const bf16*
                                const int32_t* grp, int n_groups, int n_rows, int n, int k, int epilogue, int variant,
                                hipStream_t s);
 bool gemm_grouped_variant_ok(int variant, int n, int k, int epilogue);
-int gemm_grouped_default_variant(int n_rows, int n_groups, int epilogue);
+int gemm_grouped_default_variant(int n_rows, int n_groups, int k, int epilogue);
 
 // MoE: router + dispatch of tokens [t_begin, t_end) (sel/wts/pos/src indexed by token
 // entry 2 t + k; grp: this nano-batch's [2 n_experts] group table), and the combine.

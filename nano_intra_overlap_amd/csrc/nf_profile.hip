@@ -233,10 +233,10 @@ hipError_t moe_ffn_op(const nf_layer_cfg& c, Scratch& S, int m, hipStream_t s) {
   hipError_t e = launch_moe_route(S.h2.as<bf16>(), S.wr.as<bf16>(), 0, m, H, Ex, sel, wts, pos, src, grp, s);
   if (e == hipSuccess)
     e = launch_gemm_grouped(S.h2.as<bf16>(), src, S.wgu.as<bf16>(), (long long)2 * F * H, S.a.as<bf16>(), grp, Ex,
-                            rows, F, H, 2, gemm_grouped_default_variant(rows, Ex, 2), s);
+                            rows, F, H, 2, gemm_grouped_default_variant(rows, Ex, H, 2), s);
   if (e == hipSuccess)
     e = launch_gemm_grouped(S.a.as<bf16>(), nullptr, S.wd.as<bf16>(), (long long)H * F, S.moe_out.as<bf16>(), grp, Ex,
-                            rows, H, F, 0, gemm_grouped_default_variant(rows, Ex, 0), s);
+                            rows, H, F, 0, gemm_grouped_default_variant(rows, Ex, F, 0), s);
   if (e == hipSuccess)
     e = launch_moe_combine(S.x1.as<bf16>(), S.moe_out.as<bf16>(), pos, wts, S.y.as<bf16>(), 0, m, H, s);
   return e;
@@ -346,8 +346,8 @@ extern "C" nf_status nf_profile_ops(nf_ctx* ctx, const nf_layer_cfg* cfg, const 
       int v4;
       if (c.n_experts > 0) {  // the MoE FFN as one nano-op (its tiles are chosen per call)
         if (!time_ms(E, s, reps, [&] { return moe_ffn_op(c, S, m, s); }, tug)) return false;
-        v3 = gemm_grouped_default_variant(2 * m, c.n_experts, 2);
-        v4 = gemm_grouped_default_variant(2 * m, c.n_experts, 0);
+        v3 = gemm_grouped_default_variant(2 * m, c.n_experts, c.hidden, 2);
+        v4 = gemm_grouped_default_variant(2 * m, c.n_experts, c.ffn, 0);
       } else {
         if (!best_gemm(E, s, S.h2.as<bf16>(), S.wgu.as<bf16>(), S.a.as<bf16>(), nullptr, m, F, H, 2, reps, tug, v3))
           return false;

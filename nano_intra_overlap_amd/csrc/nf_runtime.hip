@@ -422,7 +422,7 @@ nf_status timed(nf_ctx* ctx, int cls, hipStream_t s, F fn) {
 int pick_grouped(nf_ctx* ctx, int which, int rows, int n_experts, int n, int k, int epi) {
   const int v = ctx->gemm_variant[NF_OP_UGD][which];
   if (gemm_grouped_variant_ok(v, n, k, epi)) return v;
-  return gemm_grouped_default_variant(rows, n_experts, epi);
+  return gemm_grouped_default_variant(rows, n_experts, k, epi);
 }
 
 // MoE FFN over token rows [lo, hi): y = x1 + sum_k w_k expert_k(h2); grp is this
