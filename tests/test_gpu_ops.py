@@ -111,8 +111,8 @@ def test_gemm_layer_shapes_sampled_rows(ctx, m, n, k, epi):
 @pytest.mark.parametrize("m,n,k,epi", [(2048, 14336, 4096, 2), (300, 16640, 96, 2), (512, 33280, 64, 0),
                                         (512, 33280, 64, 1), (256, 2048, 64, 2)])
 def test_gemm_balanced_last_round(ctx, m, n, k, epi):
-    """Variant 19 splits the columns between a 256x256 launch and a last round of 256x128
-    tiles (at these shapes the last round of 256x256 tiles would be at most half full; the
+    """Variants 19 and 26 (64-deep) split the columns between a 256x256 launch and a last
+    round of half tiles (at these shapes the last round of 256x256 tiles would be at most half full; the
     last shape has fewer tiles than CUs and takes the plain launch). Each output element
     sums k in the same order in every tile shape: bit-identical to variant 12, and the
     oracle's values on sampled rows."""
@@ -124,14 +124,15 @@ def test_gemm_balanced_last_round(ctx, m, n, k, epi):
     R = rand_bf16(rng, (m, n))
     dA, dB, dR = _dev(A), _dev(B), _dev(R)
     outs = {}
-    for v in (12, 19):
+    for v in (12, 19) + ((26,) if k % 64 == 0 else ()):
         dC = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
         log_case(f"gemm balanced m={m} n={n} k={k} epi={epi} variant={v}")
         abi.nf_op_gemm(ctx, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), dR.data_ptr(), m, n, k, epi, v,
                        torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
         outs[v] = _host(dC)
-    assert np.array_equal(outs[19], outs[12])
+    for v in outs:
+        assert np.array_equal(outs[v], outs[12]), f"variant {v} differs from variant 12"
     rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, 24, replace=False)]))
     ref = ol.linear(f64(A[rows]), f64(B))
     if epi == 1:
