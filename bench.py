@@ -54,6 +54,8 @@ def parse():
     p.add_argument("--cpu-decode-sample", type=int, default=-1,
                    help="decode requests in the CPU oracle's sample (-1 = all: the whole dense batch)")
     p.add_argument("--decode-grid", type=int, default=0, help="max decode-attention workgroups (0 = one wave per unit)")
+    p.add_argument("--decode-split", type=int, default=0,
+                   help="decode split-KV chunk in KV blocks (0 = the library's choice per nano-op)")
     p.add_argument("--decode-nbuf", type=int, default=1, choices=[1, 2], help="KV blocks per softmax step")
     p.add_argument("--decode-ring", type=int, default=2, choices=[2, 3, 4],
                    help="decode attention register ring depth (ring - 1 groups of KV blocks in flight)")
@@ -387,6 +389,8 @@ def main():
     ctx = abi.nf_ctx_create(0)
     stream = torch.cuda.current_stream().cuda_stream
     abi.nf_ctx_set_decode_launch(ctx, args.decode_grid, args.decode_nbuf, args.decode_ring)
+    if args.decode_split:
+        abi.nf_ctx_set_decode_split(ctx, args.decode_split)
     if args.gemm_variant >= 0:
         for kind in (abi.NF_OP_KQV, abi.NF_OP_O, abi.NF_OP_UGD):
             for which in (0, 1):
@@ -588,6 +592,7 @@ def main():
             "seed": args.seed,
             "plan": plan_desc,
             "decode_grid": args.decode_grid,
+            "decode_split": args.decode_split,
             "decode_nbuf": args.decode_nbuf,
             "decode_ring": args.decode_ring,
             "gemm_variant": args.gemm_variant,
