@@ -6,9 +6,9 @@
 * nf_kv_reload: the pool after a reload bit-exact against the oracle's (every slot of the
   ranges set, every other byte unchanged); aliasing ranges and bad block ids rejected on the
   host with the pool untouched;
-* a follow-up round: a prefill chunk is processed, its K/V offloaded, reloaded into other
+* a follow-up turn: a prefill chunk is processed, its K/V offloaded, reloaded into other
   pages of a fresh pool, and the request's next chunk runs as a prefill with that cached
-  prefix. The GPU's round-2 output against the oracle doing the same on its own round-1
+  prefix. The GPU's second-turn output against the oracle doing the same on its own first-turn
   K/V.
 """
 
@@ -119,7 +119,7 @@ def test_kv_reload_rejects_bad_ranges_without_touching_the_pool(ctx):
 
 
 @pytest.mark.parametrize("name,l1,l2", [("tiny", 40, 12), ("tiny", 37, 29), ("llama3_8b_layer", 300, 77)])
-def test_follow_up_round_prefill_over_reloaded_prefix(ctx, name, l1, l2):
+def test_follow_up_turn_prefill_over_reloaded_prefix(ctx, name, l1, l2):
     from nano_intra_overlap_amd import abi
     from nano_intra_overlap_amd.device import DevicePool, DeviceWeights, bf16_bits, bf16_tensor
 
@@ -129,14 +129,14 @@ def test_follow_up_round_prefill_over_reloaded_prefix(ctx, name, l1, l2):
     dw = DeviceWeights(w, "cuda")
     rng = np.random.default_rng(9)
     dec1 = rng.integers(16, 200, 6)
-    # round 1: decodes + the first chunk of a conversation (no prefix)
+    # turn 1: decodes + the first chunk of a conversation (no prefix)
     b1 = sw.batch_from_lengths(dec1, [l1], [0], seed=21)
     x1 = sw.make_x(shape, b1.n_tokens, 21)
     kp1, vp1 = sw.make_kv_pool(shape, b1.num_blocks, 21)
     pool1 = DevicePool.from_host(kp1, vp1, "cuda")
     x1d = bf16_tensor(x1, "cuda")
     y1 = torch.empty_like(x1d)
-    log_case(f"round 1 {name}: prefill {l1}")
+    log_case(f"turn 1 {name}: prefill {l1}")
     abi.nf_layer_forward(ctx, cfg, dw.desc, x1d.data_ptr(), y1.data_ptr(), abi.HostBatch.from_batch(b1), pool1.desc,
                          None, _stream())
     r1 = ol.layer_forward(shape, w, x1, b1, kp1, vp1)
@@ -150,7 +150,7 @@ def test_follow_up_round_prefill_over_reloaded_prefix(ctx, name, l1, l2):
     rows_ref = kvio.offload(r1["k_pool"], r1["v_pool"], [0], [l1], b1.block_table[conv:conv + 1])
     assert rel_inf(f64(rows_gpu), f64(rows_ref)) <= TOL
 
-    # round 2: other decodes, the conversation's next chunk with its l1-token prefix, in a
+    # turn 2: other decodes, the conversation's next chunk with its l1-token prefix, in a
     # fresh pool with other pages; the prefix comes back by reload
     dec2 = rng.integers(16, 200, 5)
     b2 = sw.batch_from_lengths(dec2, [l2], [l1], seed=22)
@@ -162,7 +162,7 @@ def test_follow_up_round_prefill_over_reloaded_prefix(ctx, name, l1, l2):
     hr2 = abi.HostKvRanges([0], [l1], t2)
     src = _pinned_u16((l1, 2, shape.n_kv, shape.head_dim))
     src.numpy()[:] = rows_gpu.view(np.int16)
-    log_case(f"round 2 {name}: reload {l1}, prefill {l2} over the prefix")
+    log_case(f"turn 2 {name}: reload {l1}, prefill {l2} over the prefix")
     abi.nf_kv_reload(ctx, cfg, pool2.desc, hr2, src.data_ptr(), _stream())
     x2d = bf16_tensor(x2, "cuda")
     y2 = torch.full_like(x2d, float("nan"))
