@@ -180,12 +180,23 @@ def algorithmic(shape, b, n_nano):
     }
 
 
-def cpu_baseline(shape, b, ws, x, seed, n_dec, fetch_blocks, n_layers_total=1):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def cpu_baseline(shape, b, ws, x, seed, n_dec, fetch_blocks, n_layers_total=1, repeats=3):
     """The oracle as it stands, timed on a sample of the workload: n_dec decode requests
     (all of them when n_dec < 0) plus every prefill chunk, over a compact copy of the KV
     blocks they use (fetch_blocks(layer, ids) -> (k, v) bf16 bit arrays of those pool
-    blocks), through the layers of ``ws`` (host weight dicts); the time is scaled to
-    n_layers_total layers."""
+    blocks), through the layers of ``ws`` (host weight dicts): one warm-up pass, then the
+    median of ``repeats`` timed passes; the time is scaled to n_layers_total layers."""
     from oracle import layer as ol
     from synth import workloads as sw
 
@@ -213,14 +224,19 @@ def cpu_baseline(shape, b, ws, x, seed, n_dec, fetch_blocks, n_layers_total=1):
     compact = sw.Batch(sub.decode_ctx, sub.prefill_len, sub.prefill_prefix, bt, len(used))
     pools = [fetch_blocks(l, used) for l in range(len(ws))]
     xs = x[rows]
-    t0 = time.perf_counter()
-    ol.stack_forward(shape, ws, xs, compact, [p[0] for p in pools], [p[1] for p in pools])
-    dt = time.perf_counter() - t0
+    times = []
+    for rep in range(1 + repeats):  # one warm-up pass, then the timed ones
+        t0 = time.perf_counter()
+        ol.stack_forward(shape, ws, xs, compact, [p[0] for p in pools], [p[1] for p in pools])
+        if rep:
+            times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
     dt_all = dt * n_layers_total / len(ws)
     what = ("the whole dense batch" if n_dec == b.n_decode else
             f"{n_dec} of {b.n_decode} decode requests (sampled, seed {seed + 7}) + all prefill chunks")
-    layers = (f"one float64 layer pass in {dt:.2f} s" if n_layers_total == 1 else
-              f"{len(ws)} of {n_layers_total} float64 layer passes in {dt:.2f} s, scaled to all layers")
+    spread = f"median of {repeats} after a warm-up pass; passes {min(times):.2f}-{max(times):.2f} s"
+    layers = (f"one float64 layer pass in {dt:.2f} s ({spread})" if n_layers_total == 1 else
+              f"{len(ws)} of {n_layers_total} float64 layer passes in {dt:.2f} s ({spread}), scaled to all layers")
     return {
         "value": round(len(rows) / dt_all, 2),
         "unit": "tokens/s",
@@ -228,7 +244,7 @@ def cpu_baseline(shape, b, ws, x, seed, n_dec, fetch_blocks, n_layers_total=1):
         "kind": "oracle",
         "sample": f"{what}: {len(rows)} tokens ({b.n_prefill} prefill chunk(s), {int(b.prefill_len.sum())} "
                   f"tokens), {len(used)} KV blocks; {layers} "
-                  f"({os.cpu_count()} host CPUs, {threads} BLAS threads)",
+                  f"({cpu_model()}, {os.cpu_count()} host CPUs, {threads} BLAS threads)",
     }
 
 

@@ -34,6 +34,12 @@
  *  - Calls are asynchronous with respect to the host and ordered with respect to the
  *    stream argument; calls that share one nf_ctx must be ordered (same stream, or
  *    externally synchronized). One nf_ctx per host thread.
+ *  - Departures from a plain reading of the problem statement, by design: the KV pool keeps
+ *    keys in 32-dim column chunks and values dim-major inside a block (see nf_kv_pool), not
+ *    token-major [block][kv head][16][d], because the attention kernels then read whole
+ *    128-byte lines straight into matrix-core operands; and a plan lists its
+ *    nano-operations as (kind, nano-batch, stream) triples in issue order (see nf_plan)
+ *    instead of a separate op order and op-to-stream map, so one array fixes both.
  */
 #ifndef NANOFLOW_H
 #define NANOFLOW_H
@@ -310,13 +316,25 @@ nf_status nf_stack_forward(nf_ctx *ctx, const nf_layer_cfg *cfg, int32_t n_layer
  * 2 attention output [T][n_q head_dim], 3 x1, 4 h2, 5 a [T][ffn]. Errors: NF_E_ARG.         */
 nf_status nf_debug_buffer(nf_ctx *ctx, int32_t which, void **ptr, size_t *bytes);
 
-/* ---- per-operation entry points (tests and profiler); one stream each -------------------- */
+/* ---- per-operation entry points (tests and profiler); one stream each --------------------
+ *
+ * Each operation of the layer runs alone on one stream, as the profiler needs it: the pages
+ * time every operation type in isolation, for every batch size and kernel configuration,
+ * to find its best interference-free time D_best (summary page, "Kernel Profiling and
+ * Interference Modeling", interference-free kernel profiling). The layer call runs the
+ * same kernels. Errors of every call: NF_E_ARG for null pointers or bad sizes (nothing is
+ * enqueued), NF_E_UNSUPPORTED for a shape the kernels do not implement, NF_E_HIP when a
+ * launch fails. */
 
-/* C[m][n] = A[m][k] B[n][k]^T (+ epilogue). epilogue 0: store; 1: C = R + A B^T with R
- * device [m][n] (may alias C); 2: SwiGLU — B holds 2n rows (gate | up) and
+/* The dense projections of the layer (summary page, "Operation classification": KQV, O,
+ * Up/Gate and Down are the compute-bound GEMMs of a decoder layer; slides "8B Pipeline
+ * Design"). C[m][n] = A[m][k] B[n][k]^T (+ epilogue), all device bf16, row-major:
+ * A [m][k] activations, B [n][k] a Linear-layout weight. epilogue 0: store; 1: C = R + A B^T
+ * (the residual add after O and Down) with R device [m][n] (may alias C); 2: SwiGLU
+ * (silu(gate) * up of the FFN) — B holds 2n rows (gate | up) and
  * C[m][n] = silu(A Bg^T) * (A Bu^T). variant: -1 = library choice, else a tile
- * configuration index (see nf_gemm_variants). k and n multiples of 8. Errors: NF_E_ARG,
- * NF_E_UNSUPPORTED, NF_E_HIP.                                                               */
+ * configuration index (see nf_gemm_variants). k and n multiples of 8. Split-K variants keep
+ * their fp32 partials in a workspace the context owns (grown on demand).                   */
 nf_status nf_op_gemm(nf_ctx *ctx, const void *A, const void *B, void *C, const void *R, int32_t m,
                      int32_t n, int32_t k, int32_t epilogue, int32_t variant, void *stream);
 /* Number of GEMM tile configurations and, for index i, into out5: its tile (bm, bn), k
@@ -331,23 +349,41 @@ nf_status nf_gemm_variants(int32_t *count, int32_t index, int32_t *out5);
 nf_status nf_gemm_choice(int32_t m, int32_t n, int32_t k, int32_t epilogue, int32_t *variant,
                          int32_t *supported);
 
-/* out[r][:] = x[r] / sqrt(mean(x[r]^2) + eps) * g, rows r in [0, m), width n (mult. of 8). */
+/* The norm before attention and before the FFN (the pages name no norm: a pre-norm LLaMA
+ * layer's RMSNorm, eps from the model): out[r][:] = x[r] / sqrt(mean(x[r]^2) + eps) * g for
+ * rows r in [0, m), width n (a multiple of 8). x, out device [m][n]; g device [n].          */
 nf_status nf_op_rmsnorm(nf_ctx *ctx, const void *x, const void *g, void *out, int32_t m, int32_t n,
                         float eps, void *stream);
 
-/* Rotary embedding of q and k in qkv (device [T][(n_q+2n_kv) d], q rotated in place) at
- * the batch's token positions, and append of k, v to the pool slots of the batch.           */
+/* Rotary embedding of q and k and the paged KV append (slides, "Batch Formation": new
+ * tokens' K/V go to their pages; "Inside nano-vLLM", the slot mapping locates each new KV
+ * store): q and k of qkv (device [T][(n_q+2n_kv) d], q rotated in place) rotated at the
+ * batch's token positions, then k and v written to each token's slot of the pool
+ * (slot = table[r][pos / 16] * 16 + pos % 16). Only those slots change. Errors as the
+ * layer call for the batch (NF_E_BLOCK_*, NF_E_SLOT_ALIAS).                                  */
 nf_status nf_op_rope_kv_append(nf_ctx *ctx, const nf_layer_cfg *cfg, void *qkv,
                                const nf_batch_desc *batch, nf_kv_pool *pool, void *stream);
 
-/* Attention of the batch's decode requests (decode = 1) or prefill chunks (decode = 0),
- * reading q from qkv (device [T][(n_q+2n_kv) d], already rotated) and K/V from the pool
- * (already holding this iteration's tokens); writes rows of out (device [T][n_q d]) that
- * belong to those requests. kv_split_blocks: decode split-KV chunk in blocks, 0..4096
- * (0 = the context's default). */
-nf_status nf_op_attention(nf_ctx *ctx, const nf_layer_cfg *cfg, const void *qkv,
-                          const nf_batch_desc *batch, const nf_kv_pool *pool, void *out,
-                          int32_t decode, int32_t kv_split_blocks, void *stream);
+/* Decode attention, the memory-bound operation of the layer (summary page, "Operation
+ * classification": decode attention loads each request's KV-cache): for every decode
+ * request r and query head h, softmax(q k^T / sqrt(d)) v over the request's decode_ctx_len[r]
+ * + 1 keys of KV head h / (n_q / n_kv), read through its block-table row. q is read from qkv
+ * (device [T][(n_q+2n_kv) d], already rotated), K/V from the pool (already holding this
+ * iteration's tokens); writes the decode rows of out (device [T][n_q d]) and nothing else.
+ * kv_split_blocks: split-KV chunk in blocks, 0..4096 (0 = the context's default). The
+ * split-KV partials live in the context's workspace. Errors as the layer call for the
+ * batch.                                                                                     */
+nf_status nf_op_decode_attn(nf_ctx *ctx, const nf_layer_cfg *cfg, const void *qkv,
+                            const nf_batch_desc *batch, const nf_kv_pool *pool, void *out,
+                            int32_t kv_split_blocks, void *stream);
+
+/* Prefill attention, compute-bound, causal within each prefill chunk ("Inside nano-vLLM",
+ * prefill batching keeps request boundaries; slides "Batch Formation"): query i of chunk j
+ * attends to keys 0 .. prefill_prefix_len[j] + i of its request. Same buffers as
+ * nf_op_decode_attn; writes the prefill rows of out only.                                   */
+nf_status nf_op_prefill_attn(nf_ctx *ctx, const nf_layer_cfg *cfg, const void *qkv,
+                             const nf_batch_desc *batch, const nf_kv_pool *pool, void *out,
+                             void *stream);
 
 /* The mixture-of-experts FFN alone (see nf_layer_cfg), for tests and profiling:
  * y = x1 + sum over the top_k chosen experts of weight x expert(h2), for n_tokens rows.

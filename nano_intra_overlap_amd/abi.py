@@ -121,8 +121,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "nf_op_rmsnorm": (I, [V, V, V, V, I, I, ctypes.c_float, V]),
         "nf_op_rope_kv_append": (I, [V, ctypes.POINTER(nf_layer_cfg), V, ctypes.POINTER(nf_batch_desc),
                                      ctypes.POINTER(nf_kv_pool), V]),
-        "nf_op_attention": (I, [V, ctypes.POINTER(nf_layer_cfg), V, ctypes.POINTER(nf_batch_desc),
-                                ctypes.POINTER(nf_kv_pool), V, I, I, V]),
+        "nf_op_decode_attn": (I, [V, ctypes.POINTER(nf_layer_cfg), V, ctypes.POINTER(nf_batch_desc),
+                                  ctypes.POINTER(nf_kv_pool), V, I, V]),
+        "nf_op_prefill_attn": (I, [V, ctypes.POINTER(nf_layer_cfg), V, ctypes.POINTER(nf_batch_desc),
+                                   ctypes.POINTER(nf_kv_pool), V, V]),
         "nf_profile_ops": (I, [V, ctypes.POINTER(nf_layer_cfg), ctypes.POINTER(nf_batch_desc), I, I, I,
                                ctypes.c_char_p]),
         "nf_profile_interference": (I, [V, ctypes.POINTER(nf_layer_cfg), ctypes.POINTER(nf_batch_desc), I,
@@ -414,10 +416,16 @@ def nf_op_rope_kv_append(ctx, cfg: nf_layer_cfg, qkv: int, batch: HostBatch, poo
                                        stream), ctx)
 
 
-def nf_op_attention(ctx, cfg: nf_layer_cfg, qkv: int, batch: HostBatch, pool: nf_kv_pool, out: int, decode: bool,
-                    kv_split_blocks: int = 0, stream: int = 0) -> None:
-    _check(load().nf_op_attention(ctx, ctypes.byref(cfg), qkv, ctypes.byref(batch.desc), ctypes.byref(pool), out,
-                                  int(decode), kv_split_blocks, stream), ctx)
+def nf_op_decode_attn(ctx, cfg: nf_layer_cfg, qkv: int, batch: HostBatch, pool: nf_kv_pool, out: int,
+                      kv_split_blocks: int = 0, stream: int = 0) -> None:
+    _check(load().nf_op_decode_attn(ctx, ctypes.byref(cfg), qkv, ctypes.byref(batch.desc), ctypes.byref(pool), out,
+                                    kv_split_blocks, stream), ctx)
+
+
+def nf_op_prefill_attn(ctx, cfg: nf_layer_cfg, qkv: int, batch: HostBatch, pool: nf_kv_pool, out: int,
+                       stream: int = 0) -> None:
+    _check(load().nf_op_prefill_attn(ctx, ctypes.byref(cfg), qkv, ctypes.byref(batch.desc), ctypes.byref(pool), out,
+                                     stream), ctx)
 
 
 def nf_profile_ops(ctx, cfg: nf_layer_cfg, batch: HostBatch, num_blocks: int, step: int, max_tokens: int,

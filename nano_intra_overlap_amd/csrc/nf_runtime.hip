@@ -1006,13 +1006,14 @@ extern "C" nf_status nf_op_rope_kv_append(nf_ctx* ctx, const nf_layer_cfg* cfg, 
   return NF_OK;
 }
 
-extern "C" nf_status nf_op_attention(nf_ctx* ctx, const nf_layer_cfg* cfg, const void* qkv, const nf_batch_desc* batch,
-                                     const nf_kv_pool* pool, void* out, int32_t decode, int32_t kv_split_blocks,
-                                     void* stream) {
+// Attention of the batch's decode requests (decode) or prefill chunks, alone on `stream`.
+static nf_status op_attention(nf_ctx* ctx, const char* name, const nf_layer_cfg* cfg, const void* qkv,
+                              const nf_batch_desc* batch, const nf_kv_pool* pool, void* out, bool decode,
+                              int32_t kv_split_blocks, void* stream) {
   if (!ctx) return NF_E_ARG;
   if (!cfg || !qkv || !batch || !pool || !pool->k || !pool->v || !out || kv_split_blocks < 0 ||
       kv_split_blocks > kMaxSplit) {
-    ctx->err = "nf_op_attention: bad argument (kv_split_blocks in 0..4096)";
+    ctx->err = std::string(name) + ": bad argument (null pointer, or kv_split_blocks outside 0..4096)";
     return NF_E_ARG;
   }
   const int saved = ctx->decode_split;
@@ -1040,6 +1041,17 @@ extern "C" nf_status nf_op_attention(nf_ctx* ctx, const nf_layer_cfg* cfg, const
                                     (int)M.pf.size(), static_cast<bf16*>(out), nq, nkv, d, s));
   }
   return NF_OK;
+}
+
+extern "C" nf_status nf_op_decode_attn(nf_ctx* ctx, const nf_layer_cfg* cfg, const void* qkv,
+                                       const nf_batch_desc* batch, const nf_kv_pool* pool, void* out,
+                                       int32_t kv_split_blocks, void* stream) {
+  return op_attention(ctx, "nf_op_decode_attn", cfg, qkv, batch, pool, out, true, kv_split_blocks, stream);
+}
+
+extern "C" nf_status nf_op_prefill_attn(nf_ctx* ctx, const nf_layer_cfg* cfg, const void* qkv,
+                                        const nf_batch_desc* batch, const nf_kv_pool* pool, void* out, void* stream) {
+  return op_attention(ctx, "nf_op_prefill_attn", cfg, qkv, batch, pool, out, false, 0, stream);
 }
 
 extern "C" nf_status nf_op_moe_ffn(nf_ctx* ctx, const nf_layer_cfg* cfg, const nf_layer_weights* w, const void* h2,

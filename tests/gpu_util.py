@@ -49,3 +49,24 @@ def f64(bits) -> np.ndarray:
 def log_case(name: str):
     """Name the case on stdout before a GPU step (a fault then still identifies it)."""
     print(f"[gpu case] {name}", flush=True)
+
+
+def oracle_subbatch(shape, b, w, x, sample, seed):
+    """Run the oracle on the sampled requests with a compact pool of only their blocks
+    (rows of different requests are independent, so a sub-batch reproduces their rows)."""
+    sub = b.select(sample)
+    ranges = ol.request_ranges(b)
+    rows = np.concatenate([np.arange(ranges[r][0], ranges[r][1]) for r in sample])
+    need = (sub.cached_lens() + sub.q_lens() + 15) // 16
+    used = sorted({int(sub.block_table[i, j]) for i in range(sub.n_requests) for j in range(int(need[i]))})
+    remap = {blk: i for i, blk in enumerate(used)}
+    bt = np.full_like(sub.block_table, -1)
+    for i in range(sub.n_requests):
+        for j in range(int(need[i])):
+            bt[i, j] = remap[int(sub.block_table[i, j])]
+    compact = sw.Batch(sub.decode_ctx, sub.prefill_len, sub.prefill_prefix, bt, len(used))
+    kp, vp = sw.make_kv_pool_blocks(shape, used, seed)
+    ref = ol.layer_forward(shape, w, x[rows], compact, kp, vp)
+    exact = ol.layer_forward(shape, w, x[rows], compact, kp, vp, storage="exact")
+    ref["y_exact"] = exact["y"]
+    return rows, used, compact, ref

@@ -2,9 +2,10 @@
 
 * tiny layer (2 prefill x 32 + 14 decode): every output, for the sequential layer, the
   given 2-nano-batch split, two-stream overlap with CU masks and random plans;
-* 8B-shaped layer and the 70B TP-8 share at full size, in the bench's launch
-  configuration: sampled requests recomputed by the oracle one sub-batch at a time, plus
-  the property that every pool slot other than this iteration's is bitwise unchanged.
+* 8B-shaped layer (prefill chunks of 445, 952 and 1024 tokens) and the 70B TP-8 share at
+  full size, in the bench's launch configuration: every row and every written K/V slot
+  against the oracle run on the whole batch, plus the property that every pool slot other
+  than this iteration's is bitwise unchanged.
 """
 
 import numpy as np
@@ -197,90 +198,86 @@ def test_layer_rejects_bad_batch_without_touching_memory(ctx):
 
 # ------------------------------------------------------------------------------ full size
 
+# The GPU layer against the exact-storage oracle (no bf16 rounding between operations):
+# the bf16-storage model itself sits up to ~0.9% from it on these shapes (the 70B share's
+# 8192-wide rows, oracle-computed), and the GPU sits within TOL of that model.
+EXACT_TOL = 2e-2
 
-def _full_size_case(name, seed, n_sample):
-    """GPU-resident full-size inputs and a sampled sub-batch for the oracle."""
+
+def _full_size_inputs(name, seed, prefill_len=None):
+    """GPU-resident full-size inputs, plus a host copy of the pool as it was before the layer."""
     from nano_intra_overlap_amd.device import DevicePool, DeviceWeights, bf16_tensor
     from synth.workloads import make_kv_pool_torch
 
     wl = sw.WORKLOADS[name]
     shape = wl.shape
-    b = sw.make_batch(name, seed)
+    b = sw.make_batch(name, seed, prefill_len=prefill_len)
     w = sw.make_weights(shape, seed)
     x = sw.make_x(shape, b.n_tokens, seed)
     k16, v16 = make_kv_pool_torch(shape, b.num_blocks, seed, device="cuda")
+    kp = k16.cpu().numpy().view(np.uint16)
+    vp = v16.cpu().numpy().view(np.uint16)
     pool = DevicePool.from_int16(k16, v16)
-    rng = np.random.default_rng(seed + 99)
-    sample = sorted(rng.choice(b.n_decode, size=n_sample, replace=False).tolist()) + list(
-        range(b.n_decode, b.n_requests))
-    return wl, shape, b, w, x, DeviceWeights(w, "cuda"), bf16_tensor(x, "cuda"), pool, sample
-
-
-def _oracle_subbatch(shape, b, w, x, sample, seed):
-    """Run the oracle on the sampled requests with a compact pool of only their blocks."""
-    sub = b.select(sample)
-    ranges = ol.request_ranges(b)
-    rows = np.concatenate([np.arange(ranges[r][0], ranges[r][1]) for r in sample])
-    need = (sub.cached_lens() + sub.q_lens() + 15) // 16
-    used = sorted({int(sub.block_table[i, j]) for i in range(sub.n_requests) for j in range(int(need[i]))})
-    remap = {blk: i for i, blk in enumerate(used)}
-    bt = np.full_like(sub.block_table, -1)
-    for i in range(sub.n_requests):
-        for j in range(int(need[i])):
-            bt[i, j] = remap[int(sub.block_table[i, j])]
-    compact = sw.Batch(sub.decode_ctx, sub.prefill_len, sub.prefill_prefix, bt, len(used))
-    kp, vp = sw.make_kv_pool_blocks(shape, used, seed)
-    ref = ol.layer_forward(shape, w, x[rows], compact, kp, vp)
-    exact = ol.layer_forward(shape, w, x[rows], compact, kp, vp, storage="exact")
-    ref["y_exact"] = exact["y"]
-    return rows, used, compact, ref
+    return wl, shape, b, w, x, DeviceWeights(w, "cuda"), bf16_tensor(x, "cuda"), pool, kp, vp
 
 
 @pytest.mark.parametrize("name,seed,plan_kind", [
     ("llama3_8b_layer", 0, "overlap2"),
     ("llama3_8b_layer", 1, "null"),
+    ("llama3_8b_layer", 2, "null"),  # prefill chunk of 952 tokens
+    ("llama3_8b_layer", 0, "cap1024"),  # the prefill draw's cap: one chunk of 1024 tokens
     ("llama2_70b_tp8_layer", 0, "overlap2"),
 ])
-def test_full_size_layer_sampled(ctx, name, seed, plan_kind):
+def test_full_size_layer(ctx, name, seed, plan_kind):
+    """Every row of y and of the attention output, and every written K/V slot, of a
+    full-size layer against the oracle run on the whole batch, in the bench's launch
+    configuration; every other pool slot bitwise unchanged."""
     from nano_intra_overlap_amd import plans
     from nano_intra_overlap_amd.device import bf16_bits
-    from synth.workloads import make_kv_pool_torch
 
-    wl, shape, b, w, x, w_dev, x_dev, pool, sample = _full_size_case(name, seed, n_sample=24)
+    wl, shape, b, w, x, w_dev, x_dev, pool, kp, vp = _full_size_inputs(
+        name, seed, prefill_len=[1024] if plan_kind == "cap1024" else None)
     T = b.n_tokens
-    plan = None if plan_kind == "null" else plans.overlap(_host_batch(b), plans.even_bounds(T, 2))
+    print(f"[{name} seed={seed}] {b.n_decode} decode requests, prefill {b.prefill_len.tolist()}", flush=True)
+    plan = plans.overlap(_host_batch(b), plans.even_bounds(T, 2)) if plan_kind == "overlap2" else None
     y_dev = torch.full_like(x_dev, float("nan"))
     log_case(f"full-size layer {name} seed={seed} plan={plan_kind}")
     _run_layer(ctx, shape, w_dev, x_dev, y_dev, _host_batch(b), pool, plan)
     y = f64(bf16_bits(y_dev))
     assert np.isfinite(y).all()
+    attn = f64(_attn_buffer(ctx, T, shape.n_q * shape.head_dim))
 
     # untouched slots, over the whole pool, on the device
-    k0, v0 = make_kv_pool_torch(shape, b.num_blocks, seed, device="cuda")
+    k0 = torch.from_numpy(kp.view(np.int16)).cuda()
     changed_k = (pool.k.view(torch.int16) != k0).any(dim=4).any(dim=2).any(dim=1)  # [nb, 16]
+    del k0
+    v0 = torch.from_numpy(vp.view(np.int16)).cuda()
     changed_v = (pool.v.view(torch.int16) != v0).any(dim=2).any(dim=1)
-    del k0, v0
-    new = torch.zeros((b.num_blocks, 16), dtype=torch.bool)
+    del v0
     slots = ol.new_token_slots(b, 16)
+    new = torch.zeros((b.num_blocks, 16), dtype=torch.bool)
     new[[s[0] for s in slots], [s[1] for s in slots]] = True
     new = new.cuda()
     assert not (changed_k & ~new).any() and not (changed_v & ~new).any()
     assert int(changed_k.sum()) == T and int(changed_v.sum()) == T
+    blk = torch.as_tensor([s[0] for s in slots], device="cuda")
+    off = torch.as_tensor([s[1] for s in slots], device="cuda")
+    kgot = pool.k.view(torch.int16)[blk, :, :, off, :].cpu().numpy().view(np.uint16)  # [T, n_kv, d/32, 32]
+    vgot = pool.v.view(torch.int16)[blk, :, :, off].cpu().numpy().view(np.uint16)  # [T, n_kv, d]
 
-    # sampled rows against the oracle
-    rows, used, compact, ref = _oracle_subbatch(shape, b, w, x, sample, seed)
-    print(f"[{name}] y rel err vs bf16-storage oracle {rel_inf(y[rows], ref['y']):.3e}, "
-          f"vs exact oracle {rel_inf(y[rows], ref['y_exact']):.3e}", flush=True)
-    assert rel_inf(y[rows], ref["y"]) <= TOL, rel_inf(y[rows], ref["y"])
-    attn = f64(_attn_buffer(ctx, T, shape.n_q * shape.head_dim))[rows]
-    assert rel_inf(attn, ref["attn"]) <= TOL, rel_inf(attn, ref["attn"])
-    idx = torch.as_tensor(used, device="cuda")
-    kg = pool.k[idx].view(torch.int16).cpu().numpy().view(np.uint16)
-    vg = pool.v[idx].view(torch.int16).cpu().numpy().view(np.uint16)
-    sl = ol.new_token_slots(compact, 16)
-    kgot = np.stack([kg[blk, :, :, off, :] for blk, off in sl])
-    kref = np.stack([ref["k_pool"][blk, :, :, off, :] for blk, off in sl])
-    vgot = np.stack([vg[blk, :, :, off] for blk, off in sl])
-    vref = np.stack([ref["v_pool"][blk, :, :, off] for blk, off in sl])
-    assert rel_inf(f64(kgot), f64(kref)) <= TOL
-    assert rel_inf(f64(vgot), f64(vref)) <= TOL
+    # the oracle over the whole batch (bf16-storage model), then the exact-storage one
+    ref = ol.layer_forward(shape, w, x, b, kp, vp)
+    sb, so = np.array([s[0] for s in slots]), np.array([s[1] for s in slots])
+    kref = ref["k_pool"][sb, :, :, so, :]
+    vref = ref["v_pool"][sb, :, :, so]
+    e_y, e_a = rel_inf(y, ref["y"]), rel_inf(attn, ref["attn"])
+    e_k, e_v = rel_inf(f64(kgot), f64(kref)), rel_inf(f64(vgot), f64(vref))
+    y_bf16 = ref["y"]
+    del ref
+    exact = ol.layer_forward(shape, w, x, b, kp, vp, storage="exact")
+    e_x, e_model = rel_inf(y, exact["y"]), rel_inf(y_bf16, exact["y"])
+    print(f"[{name} seed={seed} {plan_kind}] all {T} rows: y {e_y:.3e}, attention {e_a:.3e}, written K {e_k:.3e}, "
+          f"V {e_v:.3e} (bf16-storage oracle); y vs exact oracle {e_x:.3e} (the model itself: {e_model:.3e})",
+          flush=True)
+    assert e_y <= TOL and e_a <= TOL and e_k <= TOL and e_v <= TOL, (e_y, e_a, e_k, e_v)
+    assert e_x <= EXACT_TOL, e_x

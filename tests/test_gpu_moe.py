@@ -210,9 +210,9 @@ def test_full_size_moe_layer_sampled(ctx):
     abi.nf_layer_forward(ctx, abi.make_cfg(shape), dw.desc, xd.data_ptr(), y.data_ptr(), hb, pool.desc, plan,
                          _stream())
     torch.cuda.synchronize()
-    from tests.test_gpu_layer import _oracle_subbatch
+    from tests.gpu_util import oracle_subbatch
 
     rng = np.random.default_rng(seed + 99)
     sample = sorted(rng.choice(b.n_decode, size=24, replace=False).tolist()) + list(range(b.n_decode, b.n_requests))
-    rows, used, compact, ref = _oracle_subbatch(shape, b, w, x, sample, seed)
+    rows, used, compact, ref = oracle_subbatch(shape, b, w, x, sample, seed)
     _check_moe_layer(ctx, shape, b, None, None, ref, y, None, ROUTE_MARGIN_LAYER, rows=rows)

@@ -287,8 +287,8 @@ def test_decode_attention(ctx, n_q, n_kv, d, split):
     pool = DevicePool.from_host(kp, vp, "cuda")
     dqkv = _dev(qkv)
     log_case(f"decode attention n_q={n_q} n_kv={n_kv} d={d} split={split}")
-    abi.nf_op_attention(ctx, abi.make_cfg(shape), dqkv.data_ptr(), abi.HostBatch.from_batch(b), pool.desc,
-                        out.data_ptr(), True, split, torch.cuda.current_stream().cuda_stream)
+    abi.nf_op_decode_attn(ctx, abi.make_cfg(shape), dqkv.data_ptr(), abi.HostBatch.from_batch(b), pool.desc,
+                          out.data_ptr(), split, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     got = f64(_host(out))
     assert np.isfinite(got).all()
@@ -316,8 +316,8 @@ def test_decode_attention_launch_configs(ctx, n_q, n_kv, d, nb, ring, grid):
         for split in (0, 48, 300):
             out = torch.full((T, n_q * d), float("nan"), dtype=torch.bfloat16, device="cuda")
             log_case(f"decode attention nb={nb} ring={ring} grid={grid} split={split} n_q={n_q} d={d}")
-            abi.nf_op_attention(ctx, abi.make_cfg(shape), dqkv.data_ptr(), abi.HostBatch.from_batch(b), pool.desc,
-                                out.data_ptr(), True, split, torch.cuda.current_stream().cuda_stream)
+            abi.nf_op_decode_attn(ctx, abi.make_cfg(shape), dqkv.data_ptr(), abi.HostBatch.from_batch(b), pool.desc,
+                                  out.data_ptr(), split, torch.cuda.current_stream().cuda_stream)
             torch.cuda.synchronize()
             got = f64(_host(out))
             assert np.isfinite(got).all()
@@ -333,8 +333,8 @@ def test_decode_attention_launch_configs(ctx, n_q, n_kv, d, nb, ring, grid):
         for split in (0, 48, 300):
             out = torch.full((T, n_q * d), float("nan"), dtype=torch.bfloat16, device="cuda")
             log_case(f"uniform decode attention nb={nb} ring={ring} grid={grid} split={split} n_q={n_q} d={d}")
-            abi.nf_op_attention(ctx, abi.make_cfg(shape), dq0.data_ptr(), abi.HostBatch.from_batch(b), pool.desc,
-                                out.data_ptr(), True, split, torch.cuda.current_stream().cuda_stream)
+            abi.nf_op_decode_attn(ctx, abi.make_cfg(shape), dq0.data_ptr(), abi.HostBatch.from_batch(b), pool.desc,
+                                  out.data_ptr(), split, torch.cuda.current_stream().cuda_stream)
             torch.cuda.synchronize()
             got = f64(_host(out))
             bound = 2.0**-8 * np.abs(ref0) + 4e-4 * vmax
@@ -352,14 +352,23 @@ def test_decode_launch_rejects_unsupported_configs(ctx):
             abi.nf_ctx_set_decode_launch(ctx, 0, nb, ring)
 
 
+# prefill chunk lengths and cached prefixes: ragged tiles, a prefix that is not block
+# aligned, and the lengths the 8B workload's draw reaches (445, 952 and its cap of 1024)
+PREFILL_CASES = {
+    "ragged": ([1, 15, 16, 17, 100, 300], [0, 0, 7, 0, 33, 0]),
+    "cap1024": ([1024], [0]),
+    "long_prefix": ([952, 445, 63], [0, 37, 200]),
+}
+
+
+@pytest.mark.parametrize("case", list(PREFILL_CASES))
 @pytest.mark.parametrize("n_q,n_kv,d", [(4, 2, 64), (32, 8, 128), (8, 1, 128)])
-def test_prefill_attention(ctx, n_q, n_kv, d):
+def test_prefill_attention(ctx, n_q, n_kv, d, case):
     from nano_intra_overlap_amd import abi
     from nano_intra_overlap_amd.device import DevicePool
 
-    rng = np.random.default_rng(7 * n_q + d)
-    pre_len = [1, 15, 16, 17, 100, 300]
-    pre_prefix = [0, 0, 7, 0, 33, 0]
+    rng = np.random.default_rng(7 * n_q + d + len(case))
+    pre_len, pre_prefix = PREFILL_CASES[case]
     b, shape, qkv, kp, vp = _attention_case(rng, n_q, n_kv, d, [5, 9], pre_len, pre_prefix, seed=11)
     T = b.n_tokens
     q = f64(qkv[:, : n_q * d]).reshape(T, n_q, d)
@@ -367,9 +376,9 @@ def test_prefill_attention(ctx, n_q, n_kv, d):
     out = torch.full((T, n_q * d), float("nan"), dtype=torch.bfloat16, device="cuda")
     pool = DevicePool.from_host(kp, vp, "cuda")
     dqkv = _dev(qkv)
-    log_case(f"prefill attention n_q={n_q} n_kv={n_kv} d={d}")
-    abi.nf_op_attention(ctx, abi.make_cfg(shape), dqkv.data_ptr(), abi.HostBatch.from_batch(b), pool.desc,
-                        out.data_ptr(), False, 0, torch.cuda.current_stream().cuda_stream)
+    log_case(f"prefill attention n_q={n_q} n_kv={n_kv} d={d} case={case}")
+    abi.nf_op_prefill_attn(ctx, abi.make_cfg(shape), dqkv.data_ptr(), abi.HostBatch.from_batch(b), pool.desc,
+                           out.data_ptr(), torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     got = f64(_host(out))
     rows = np.arange(b.n_decode, T)
