@@ -337,6 +337,17 @@ nf_status nf_debug_buffer(nf_ctx *ctx, int32_t which, void **ptr, size_t *bytes)
  * their fp32 partials in a workspace the context owns (grown on demand).                   */
 nf_status nf_op_gemm(nf_ctx *ctx, const void *A, const void *B, void *C, const void *R, int32_t m,
                      int32_t n, int32_t k, int32_t epilogue, int32_t variant, void *stream);
+/* nf_op_gemm for callers that cannot allocate device memory: code under HIP-graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments, result and errors
+ * as nf_op_gemm, but the call allocates nothing: the fp32 partials of a split-K
+ * configuration go to a static scratch array of 64 MiB per GPU (held until the process
+ * ends) instead of the context's workspace. Every partial is written before it is read,
+ * so nothing needs clearing. Calls on one GPU share that array: calls that overlap in time
+ * on one GPU (different streams or contexts, not ordered) race. NF_E_CAPACITY when the
+ * product's partials (K slices x m x n x 4 bytes) exceed 64 MiB; nothing is enqueued then. */
+nf_status nf_op_gemm_noalloc(nf_ctx *ctx, const void *A, const void *B, void *C, const void *R,
+                             int32_t m, int32_t n, int32_t k, int32_t epilogue, int32_t variant,
+                             void *stream);
 /* Number of GEMM tile configurations and, for index i, into out5: its tile (bm, bn), k
  * step, number of K slices (split-K, 1 = none; not with the SwiGLU epilogue) and waves per
  * workgroup (the SwiGLU epilogue needs each wave's bn / (waves / 2) columns to be a

@@ -116,6 +116,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
                              V, V]),
         "nf_op_moe_ffn": (I, [V, ctypes.POINTER(nf_layer_cfg), ctypes.POINTER(nf_layer_weights), V, V, V, I, V, V, V]),
         "nf_op_gemm": (I, [V, V, V, V, V, I, I, I, I, I, V]),
+        "nf_op_gemm_noalloc": (I, [V, V, V, V, V, I, I, I, I, I, V]),
         "nf_gemm_variants": (I, [_i32p, I, _i32p]),
         "nf_gemm_choice": (I, [I, I, I, I, _i32p, _i32p]),
         "nf_op_rmsnorm": (I, [V, V, V, V, I, I, ctypes.c_float, V]),
@@ -355,6 +356,12 @@ def nf_debug_buffer(ctx, which: int):
 def nf_op_gemm(ctx, A: int, B: int, C: int, R: int | None, m: int, n: int, k: int, epilogue: int = 0,
                variant: int = -1, stream: int = 0) -> None:
     _check(load().nf_op_gemm(ctx, A, B, C, R, m, n, k, epilogue, variant, stream), ctx)
+
+
+def nf_op_gemm_noalloc(ctx, A: int, B: int, C: int, R: int | None, m: int, n: int, k: int, epilogue: int = 0,
+                       variant: int = -1, stream: int = 0) -> None:
+    """nf_op_gemm without any allocation (split-K partials in the library's static scratch)."""
+    _check(load().nf_op_gemm_noalloc(ctx, A, B, C, R, m, n, k, epilogue, variant, stream), ctx)
 
 
 class HostKvRanges:

@@ -732,6 +732,19 @@ int gemm_default_variant(int m, int n, int k, int epilogue) {
   return 0;
 }
 
+// Kernel attributes (the dynamic LDS limit) are set once per kernel. A context sets them for
+// every configuration when it is created (gemm_prepare_kernels: the launchers run with
+// t_prepare_only set, which stops each one after its attribute), so that a later launch
+// makes no runtime call other than the launch itself, e.g. while a stream is captured.
+static thread_local bool t_prepare_only = false;
+
+static hipError_t set_lds_attr(const void* kern, size_t lds, bool& done) {
+  if (done) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) done = true;
+  return e;
+}
+
 template <int BM, int BN, int BK, int EPI>
 static hipError_t launch_t(const bf16* A, const bf16* B, bf16* C, const bf16* R, int M, int N, int K,
                            hipStream_t s) {
@@ -743,12 +756,8 @@ static hipError_t launch_t(const bf16* A, const bf16* B, bf16* C, const bf16* R,
   const size_t lds = (size_t)2 * (BM + BN) * (BK + 8) * sizeof(bf16);
   auto kern = gemm_kernel<BM, BN, BK, EPI>;
   static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  if (hipError_t e = set_lds_attr(reinterpret_cast<const void*>(kern), lds, attr_set); e != hipSuccess || t_prepare_only)
+    return e;
   hipLaunchKernelGGL(kern, dim3(per_xcd * kNumXcd), dim3(256), lds, s, A, B, C, R, M, N, K, tiles_m,
                      tiles_n, per_xcd);
   return hipGetLastError();
@@ -799,12 +808,8 @@ static hipError_t launch_pipe_t(const bf16* A, const bf16* B, bf16* C, const bf1
   const size_t lds = (size_t)STAGES * (BM + BN) * 16 * KC;
   auto kern = gemm_pipe_kernel<BM, BN, STAGES, EPI, false, NW, KC>;
   static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  if (hipError_t e = set_lds_attr(reinterpret_cast<const void*>(kern), lds, attr_set); e != hipSuccess || t_prepare_only)
+    return e;
   hipLaunchKernelGGL(kern, dim3(per_xcd * kNumXcd, ks), dim3(64 * NW), lds, s, A, B, C, R, M, N, K, ldc, b_up, tiles_m,
                      tiles_n, per_xcd, part, GroupArgs{});
   return hipGetLastError();
@@ -823,12 +828,8 @@ static hipError_t launch_grouped_t(const bf16* A, const int32_t* a_rows, const b
   const size_t lds = (size_t)STAGES * (BM + BN) * 16 * KC;
   auto kern = gemm_pipe_kernel<BM, BN, STAGES, EPI, true, NW, KC>;
   static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  if (hipError_t e = set_lds_attr(reinterpret_cast<const void*>(kern), lds, attr_set); e != hipSuccess || t_prepare_only)
+    return e;
   GroupArgs ga{grp, a_rows, n_groups, b_stride};
   hipLaunchKernelGGL(kern, dim3(per_xcd * kNumXcd), dim3(64 * NW), lds, s, A, B, C, nullptr, n_rows, N, K, N, N, 0,
                      tiles_n, per_xcd, nullptr, ga);
@@ -841,7 +842,7 @@ static hipError_t launch_pipe(const bf16* A, const bf16* B, bf16* C, const bf16*
   if (ks > 1) {
     // fp32 partials of the ks K-slices, then one pass that sums them with the epilogue
     hipError_t e = launch_pipe_t<BM, BN, STAGES, EPI_PARTIAL, NW, KC>(A, B, C, R, M, N, K, ks, ws, s);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || t_prepare_only) return e;
     const size_t n8 = (size_t)M * N / 8;
     const int grid = (int)std::min<size_t>((n8 + 255) / 256, 4096);
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, s, ws, ks, C, epi == EPI_RESID ? R : nullptr,
@@ -1016,6 +1017,31 @@ hipError_t launch_gemm_grouped(const bf16* A, const int32_t* a_rows, const bf16*
                 : launch_grouped_t<128, 256, 3, EPI_STORE, 8, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t gemm_prepare_kernels() {
+  // sizes at which every configuration launches all of its kernels (the balanced variants
+  // both of theirs): n = 5120 with SwiGLU, 10240 without, 2048 rows, k = 4096
+  static int dummy;
+  t_prepare_only = true;
+  hipError_t err = hipSuccess;
+  for (int v = 0; v < gemm_variant_count() && err == hipSuccess; ++v)
+    for (int epi = EPI_STORE; epi <= EPI_SWIGLU && err == hipSuccess; ++epi) {
+      if (!gemm_variant_supported(v, 2048, epi == EPI_SWIGLU ? 5120 : 10240, 4096, epi)) continue;
+      const bf16* p = reinterpret_cast<const bf16*>(&dummy);  // never dereferenced: nothing is launched
+      err = launch_gemm(p, p, const_cast<bf16*>(p), p, 2048, epi == EPI_SWIGLU ? 5120 : 10240, 4096, epi, v, nullptr,
+                        reinterpret_cast<float*>(&dummy), ~size_t(0));
+    }
+  for (int v = 0; v < gemm_variant_count() && err == hipSuccess; ++v)
+    for (int epi : {EPI_STORE, EPI_SWIGLU}) {
+      if (!gemm_grouped_variant_ok(v, 4096, 4096, epi)) continue;
+      const bf16* p = reinterpret_cast<const bf16*>(&dummy);
+      err = launch_gemm_grouped(p, nullptr, p, 0, const_cast<bf16*>(p), reinterpret_cast<const int32_t*>(&dummy), 8,
+                                4096, 4096, 4096, epi, v, nullptr);
+      if (err != hipSuccess) break;
+    }
+  t_prepare_only = false;
+  return err;
 }
 
 }  // namespace nf

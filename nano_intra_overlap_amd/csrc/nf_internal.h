@@ -53,6 +53,9 @@ size_t gemm_workspace_bytes(int variant, int m, int n);
 // gemm_workspace_bytes(variant, m, n) bytes (may be null when that is 0).
 hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int m, int n, int k,
                        int epilogue, int variant, hipStream_t s, float* ws = nullptr, size_t ws_bytes = 0);
+// Set the kernel attributes of every GEMM configuration (plain and grouped) up front, so
+// that launches make no other runtime call. Launches nothing.
+hipError_t gemm_prepare_kernels();
 
 // C = A B_g^T per group g (epilogue 0 store or 2 SwiGLU), pipelined tiles (variants 6-9),
 // k a multiple of 32, n of 8. grp: device [2 n_groups] (rows, first row in the grouped

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <map>
 #include <memory>
+#include <mutex>
 
 #include "nf_batch.h"
 #include "nf_internal.h"
@@ -38,6 +39,33 @@ struct DevBuf {
 
 }  // namespace
 
+// Device scratch of the allocation-free entry point (nf_op_gemm_noalloc): fp32 split-K
+// partials live here instead of in a workspace the context allocates. One copy per GPU the
+// library runs on, held until the process ends. Host code never uses the symbol itself as
+// an address: each device's address is taken once with hipGetSymbolAddress (scratch_setup)
+// and kept in g_scratch.
+static constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// With `device` current: its address of the scratch array (taken on the first call).
+hipError_t scratch_setup(int device, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[device] = p;
+  }
+  *out = g_scratch[device];
+  return hipSuccess;
+}
+}  // namespace
+
 struct nf_ctx {
   int device = 0;
   std::string err;
@@ -52,6 +80,7 @@ struct nf_ctx {
   // split-KV partials
   DevBuf part_o, part_ml;
   DevBuf gemm_ws;  // split-K fp32 partials, one region per GEMM of a plan
+  void* scratch = nullptr;  // this device's address of the static scratch array
   // MoE FFN: per token entry (2 T) the chosen expert, weight, grouped row; per grouped row
   // its token; per nano-batch the expert group table; the grouped expert outputs
   DevBuf moe_idx, moe_out;
@@ -676,6 +705,8 @@ extern "C" nf_status nf_ctx_create(int device, nf_ctx** out) {
   for (auto& row : ctx->gemm_variant) row[0] = row[1] = -1;
   if (hipEventCreateWithFlags(&ctx->upload_done, hipEventDisableTiming) != hipSuccess) return NF_E_HIP;
   if (hipEventCreateWithFlags(&ctx->fork_ev, hipEventDisableTiming) != hipSuccess) return NF_E_HIP;
+  if (device >= kMaxDevices || scratch_setup(device, &ctx->scratch) != hipSuccess) return NF_E_HIP;
+  if (gemm_prepare_kernels() != hipSuccess) return NF_E_HIP;
   *out = ctx.release();
   return NF_OK;
 }
@@ -973,6 +1004,32 @@ extern "C" nf_status nf_op_gemm(nf_ctx* ctx, const void* A, const void* B, void*
   NF_HIP(ctx, launch_gemm(static_cast<const bf16*>(A), static_cast<const bf16*>(B), static_cast<bf16*>(C),
                           static_cast<const bf16*>(R), m, n, k, epilogue, v, static_cast<hipStream_t>(stream),
                           static_cast<float*>(ctx->gemm_ws.p), ctx->gemm_ws.cap));
+  return NF_OK;
+}
+
+extern "C" nf_status nf_op_gemm_noalloc(nf_ctx* ctx, const void* A, const void* B, void* C, const void* R, int32_t m,
+                                        int32_t n, int32_t k, int32_t epilogue, int32_t variant, void* stream) {
+  if (!ctx) return NF_E_ARG;
+  if (!A || !B || !C || m < 0 || n <= 0 || k <= 0 || epilogue < 0 || epilogue > 2 || (epilogue == 1 && !R)) {
+    ctx->err = "nf_op_gemm_noalloc: bad argument";
+    return NF_E_ARG;
+  }
+  if (n % 8 || k % 8) {
+    ctx->err = "nf_op_gemm_noalloc: n and k must be multiples of 8";
+    return NF_E_UNSUPPORTED;
+  }
+  if (variant >= 0 && !gemm_variant_supported(variant, m, n, k, epilogue)) {
+    ctx->err = "nf_op_gemm_noalloc: variant not available for this epilogue / k";
+    return NF_E_ARG;
+  }
+  const int v = variant < 0 ? gemm_default_variant(m, n, k, epilogue) : variant;
+  if (gemm_workspace_bytes(v, m, n) > kNoAllocScratchBytes) {
+    ctx->err = "nf_op_gemm_noalloc: the split-K partials of this product exceed the 64 MiB static scratch";
+    return NF_E_CAPACITY;
+  }
+  NF_HIP(ctx, launch_gemm(static_cast<const bf16*>(A), static_cast<const bf16*>(B), static_cast<bf16*>(C),
+                          static_cast<const bf16*>(R), m, n, k, epilogue, v, static_cast<hipStream_t>(stream),
+                          static_cast<float*>(ctx->scratch), kNoAllocScratchBytes));
   return NF_OK;
 }
 
