@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="llama3_8b_layer")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--prefill-len", type=int, default=0,
+                   help="one prefill chunk of this many tokens instead of the workload's draw (the rest decode)")
     p.add_argument("--plan", default="searched", choices=["overlap", "sequential", "null", "searched"],
                    help="searched: the two-stage search's plan for this batch (from the profiled tables)")
     p.add_argument("--n-nano", type=int, default=2)
@@ -56,6 +58,8 @@ def parse():
     p.add_argument("--decode-grid", type=int, default=0, help="max decode-attention workgroups (0 = one wave per unit)")
     p.add_argument("--decode-split", type=int, default=0,
                    help="decode split-KV chunk in KV blocks (0 = the library's choice per nano-op)")
+    p.add_argument("--prefill-chunk", type=int, default=0,
+                   help="prefill attention keys per work item (0 = the library's choice)")
     p.add_argument("--decode-nbuf", type=int, default=1, choices=[1, 2], help="KV blocks per softmax step")
     p.add_argument("--decode-ring", type=int, default=2, choices=[2, 3, 4],
                    help="decode attention register ring depth (ring - 1 groups of KV blocks in flight)")
@@ -355,7 +359,7 @@ def main():
     assert torch.cuda.is_available(), "bench needs a GPU"
     wl = sw.WORKLOADS[args.workload]
     shape = wl.shape
-    b = sw.make_batch(args.workload, args.seed)
+    b = sw.make_batch(args.workload, args.seed, prefill_len=[args.prefill_len] if args.prefill_len else None)
     T = b.n_tokens
     log(f"workload {wl.name}: T={T}, decode={b.n_decode}, prefill={b.prefill_len.tolist()}, blocks={b.num_blocks}")
     t0 = time.time()
@@ -407,6 +411,8 @@ def main():
     abi.nf_ctx_set_decode_launch(ctx, args.decode_grid, args.decode_nbuf, args.decode_ring)
     if args.decode_split:
         abi.nf_ctx_set_decode_split(ctx, args.decode_split)
+    if args.prefill_chunk:
+        abi.nf_ctx_set_prefill_chunk(ctx, args.prefill_chunk)
     if args.gemm_variant >= 0:
         for kind in (abi.NF_OP_KQV, abi.NF_OP_O, abi.NF_OP_UGD):
             for which in (0, 1):
@@ -530,7 +536,14 @@ def main():
             breakdown[k]["tflops"] = round(f / (per_step_ms * 1e-3) / 1e12, 1)
             breakdown[k]["mfma_frac"] = round(f / (per_step_ms * 1e-3) / PEAK_BF16, 4)
 
-    own_peak = max((v.get("tflops", 0.0) for v in breakdown.values()), default=0.0) or None
+    own_peak = max((v.get("tflops", 0.0) for k, v in breakdown.items() if k.startswith("gemm")), default=0.0) or None
+    # prefill attention: 4 d per (query head, causally visible key), as the oracle counts it
+    pre, pfx = b.prefill_len.astype(np.int64), b.prefill_prefix.astype(np.int64)
+    pf_flops = 4 * shape.head_dim * shape.n_q * int((pre * pfx + pre * (pre + 1) // 2).sum()) * n_layers
+    if breakdown.get("prefill_attn", {}).get("launches"):
+        per_step_ms = breakdown["prefill_attn"]["total_ms"] / 5
+        breakdown["prefill_attn"]["tflops"] = round(pf_flops / (per_step_ms * 1e-3) / 1e12, 1)
+        breakdown["prefill_attn"]["mfma_frac"] = round(pf_flops / (per_step_ms * 1e-3) / PEAK_BF16, 4)
 
     # comparison schedules on the same batch: the plain sequential layer (one nano-batch,
     # caller stream), nano-batching without overlap, and the two-stream overlap template
@@ -609,6 +622,7 @@ def main():
             "plan": plan_desc,
             "decode_grid": args.decode_grid,
             "decode_split": args.decode_split,
+            "prefill_chunk": args.prefill_chunk,
             "decode_nbuf": args.decode_nbuf,
             "decode_ring": args.decode_ring,
             "gemm_variant": args.gemm_variant,

@@ -183,6 +183,11 @@ const char *nf_version(void);
 /* Decode split-KV chunk, in KV blocks per work item: 0 (default) = chosen per nano-op from
  * its work, else 1..4096. Errors: NF_E_ARG.                                                 */
 nf_status nf_ctx_set_decode_split(nf_ctx *ctx, int32_t blocks);
+/* Prefill attention work item: keys of a query tile per item, 0 (default) = chosen per
+ * nano-op (the longest of 1024, 512, 256, 128 that still gives a few workgroups per CU),
+ * else a multiple of 32 up to 1024; a tile with more keys is split into items whose fp32
+ * partials are merged after. Errors: NF_E_ARG.                                              */
+nf_status nf_ctx_set_prefill_chunk(nf_ctx *ctx, int32_t keys);
 /* Decode-attention launch: max_workgroups caps its grid (0 = one workgroup per four work
  * units; a smaller grid makes the kernel persistent, each wave looping over units), nbuf KV
  * blocks per online-softmax step and ring register buffers of nbuf blocks (ring - 1 steps in

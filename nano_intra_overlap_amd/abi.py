@@ -136,6 +136,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "nf_timing_summary": (I, [V, I, _i32p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                   ctypes.POINTER(ctypes.c_double)]),
         "nf_ctx_set_decode_split": (I, [V, I]),
+        "nf_ctx_set_prefill_chunk": (I, [V, I]),
         "nf_ctx_set_gemm_variant": (I, [V, I, I, I]),
         "nf_ctx_set_decode_launch": (I, [V, I, I, I]),
         "nf_copy_reference": (I, [V, V, S, V]),
@@ -479,6 +480,11 @@ def nf_timing_summary(ctx, cls: int):
 
 def nf_ctx_set_decode_split(ctx, blocks: int) -> None:
     _check(load().nf_ctx_set_decode_split(ctx, blocks), ctx)
+
+
+def nf_ctx_set_prefill_chunk(ctx, keys: int) -> None:
+    """Prefill attention keys per work item (0 = the library's choice per nano-op)."""
+    _check(load().nf_ctx_set_prefill_chunk(ctx, keys), ctx)
 
 
 def nf_ctx_set_decode_launch(ctx, max_workgroups: int, nbuf: int = 1, ring: int = 2) -> None:

@@ -477,16 +477,72 @@ static int32_t auto_split(const BatchLayout& L, int32_t r0, int32_t r1, int32_t 
   return sp;
 }
 
+// Keys a tile of queries [q0, q1) of a prefill chunk can see: its cached prefix and the
+// chunk's queries up to the last one (causal).
+static int32_t tile_keys(const PrefillReq& r, int32_t q1) { return r.prefix + q1; }
+
+int prefill_chunk_keys(const std::vector<PrefillReq>& reqs, int n_q, int n_kv) {
+  const int G = n_q / n_kv, TQ = prefill_tile_queries(G);
+  const int64_t wg_per_item = n_q / prefill_heads_per_wg(G);
+  for (int chunk = kPrefillMaxChunkKeys; chunk > 128; chunk /= 2) {
+    int64_t items = 0;
+    for (const PrefillReq& r : reqs)
+      for (int32_t q0 = 0; q0 < r.q_len; q0 += TQ) items += (tile_keys(r, std::min(q0 + TQ, r.q_len)) + chunk - 1) / chunk;
+    if (items * wg_per_item >= kPrefillTargetWgs) return chunk;
+  }
+  return 128;
+}
+
+void build_prefill_work(const std::vector<PrefillReq>& reqs, int n_q, int n_kv, int chunk_keys,
+                        std::vector<PrefillItem>& items, std::vector<CombineItem>& comb, int32_t& n_parts) {
+  const int G = n_q / n_kv, TQ = prefill_tile_queries(G);
+  chunk_keys = std::max(32, std::min(chunk_keys, kPrefillMaxChunkKeys)) / 32 * 32;
+  const size_t first = items.size();
+  for (const PrefillReq& r : reqs)
+    for (int32_t q0 = 0; q0 < r.q_len; q0 += TQ) {
+      const int32_t q1 = std::min(q0 + TQ, r.q_len);
+      const int32_t keys = tile_keys(r, q1);
+      // chunks of about equal length in 32-key steps, none empty
+      const int32_t steps = (keys + 31) / 32;
+      const int32_t per_steps = (steps + (keys + chunk_keys - 1) / chunk_keys - 1) / ((keys + chunk_keys - 1) / chunk_keys);
+      const int32_t nch = (steps + per_steps - 1) / per_steps, per = per_steps * 32;
+      const int32_t base = nch > 1 ? n_parts : -1;
+      for (int32_t c = 0; c < nch; ++c) {
+        PrefillItem it{};
+        it.req = r.req;
+        it.token0 = r.token0;
+        it.q_begin = q0;
+        it.q_len = r.q_len;
+        it.prefix = r.prefix;
+        it.key_begin = c * per;
+        it.key_end = std::min(keys, (c + 1) * per);
+        it.part = nch > 1 ? base + c : -1;
+        it.n_chunks = nch;
+        items.push_back(it);
+      }
+      if (nch > 1) {
+        for (int32_t i = 0; i < q1 - q0; ++i) comb.push_back(CombineItem{r.token0 + q0 + i, base + i * nch, nch, 0});
+        n_parts += (q1 - q0) * nch;
+      }
+    }
+  // longest key ranges first: workgroups start in item order, the shortest last
+  std::stable_sort(items.begin() + first, items.end(), [](const PrefillItem& a, const PrefillItem& b) {
+    return a.key_end - a.key_begin > b.key_end - b.key_begin;
+  });
+}
+
 // Work lists of the decode attention and prefill attention nano-ops of each nano-batch.
 // split: decode chunk in blocks, 0 = auto_split per nano-op.
-void build_work(const BatchLayout& L, const PlanGraph& g, int split, int n_kv, Meta& M) {
+void build_work(const BatchLayout& L, const PlanGraph& g, int split, int pf_chunk, int n_q, int n_kv, Meta& M) {
   const int n_nano = g.n_nano;
   M.dec.clear();
   M.comb.clear();
   M.pf.clear();
+  M.pcomb.clear();
   M.dec_begin.assign(n_nano + 1, 0);
   M.comb_begin.assign(n_nano + 1, 0);
   M.pf_begin.assign(n_nano + 1, 0);
+  M.pcomb_begin.assign(n_nano + 1, 0);
   M.n_parts = 0;
   std::vector<const NanoOp*> dec_op(n_nano, nullptr), pf_op(n_nano, nullptr);
   for (auto& op : g.ops) {
@@ -527,26 +583,21 @@ void build_work(const BatchLayout& L, const PlanGraph& g, int split, int n_kv, M
       });
     }
     M.pf_begin[j] = (int32_t)M.pf.size();
+    M.pcomb_begin[j] = (int32_t)M.pcomb.size();
     if (pf_op[j]) {
+      std::vector<PrefillReq> reqs;
       for (int32_t r : pf_op[j]->prefill_reqs) {
         const ReqInfo& ri = L.req[r];
-        const int32_t qlen = ri.t1 - ri.t0;
-        // longest tiles (latest queries, most keys) first
-        for (int32_t q0 = ((qlen - 1) / 16) * 16; q0 >= 0; q0 -= 16) {
-          PrefillItem it{};
-          it.req = r;
-          it.token0 = ri.t0;
-          it.q_begin = q0;
-          it.q_len = qlen;
-          it.prefix = ri.cached;
-          M.pf.push_back(it);
-        }
+        reqs.push_back(PrefillReq{r, ri.t0, ri.t1 - ri.t0, ri.cached});
       }
+      build_prefill_work(reqs, n_q, n_kv, pf_chunk > 0 ? pf_chunk : prefill_chunk_keys(reqs, n_q, n_kv), M.pf, M.pcomb,
+                         M.n_parts);
     }
   }
   M.dec_begin[n_nano] = (int32_t)M.dec.size();
   M.comb_begin[n_nano] = (int32_t)M.comb.size();
   M.pf_begin[n_nano] = (int32_t)M.pf.size();
+  M.pcomb_begin[n_nano] = (int32_t)M.pcomb.size();
 }
 
 

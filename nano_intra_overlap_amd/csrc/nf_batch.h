@@ -29,15 +29,44 @@ struct CombineItem {
   int32_t pad;
 };
 
-// One prefill attention work item: 16 consecutive queries of one prefill request.
+// One prefill attention work item: a tile of consecutive queries of one prefill chunk
+// (prefill_tile_queries of them) against a range of the request's keys. A tile whose keys
+// are split over several items writes fp32 partials, merged by the decode combine kernel.
 struct PrefillItem {
   int32_t req;        // request index (row of the block table)
   int32_t token0;     // dense-batch row of the first query of the request
-  int32_t q_begin;    // first query (within the request) of this 16-query tile
+  int32_t q_begin;    // first query (within the request) of this tile
   int32_t q_len;      // queries of the request
   int32_t prefix;     // cached prefix length
+  int32_t key_begin;  // keys [key_begin, key_end) of the request: key_begin a multiple of
+  int32_t key_end;    // 32, at most kPrefillMaxChunkKeys keys
+  int32_t part;       // -1: the tile's only chunk (final output); else the partial slot of the
+                      // tile's first query for this chunk (query i of the tile: part + i * n_chunks)
+  int32_t n_chunks;   // chunks of the tile
   int32_t pad[3];
 };
+
+// Prefill attention workgroups: 4 waves of 32 queries each, covering heads_per_wg query
+// heads of one KV group times 4 / heads_per_wg consecutive 32-query tiles (they share the
+// KV tiles staged in LDS). A group of G query heads per KV head takes 4, 2 or 1 heads per
+// workgroup, the largest that divides G.
+inline int prefill_heads_per_wg(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
+inline int prefill_tile_queries(int G) { return 32 * (4 / prefill_heads_per_wg(G)); }
+constexpr int kPrefillMaxChunkKeys = 1024;  // keys of one item: its <= 64 block ids fit one wave
+
+// Prefill work of chunks (request r: q_len queries after prefix cached keys, rows from
+// token0): tiles longest first, each tile's keys split into chunks of at most chunk_keys
+// (a multiple of 32, <= kPrefillMaxChunkKeys). Items go to `items`; a split tile gets
+// q_len-of-tile x n_chunks partial slots from n_parts on and one combine entry per query.
+struct PrefillReq {
+  int32_t req, token0, q_len, prefix;
+};
+void build_prefill_work(const std::vector<PrefillReq>& reqs, int n_q, int n_kv, int chunk_keys,
+                        std::vector<PrefillItem>& items, std::vector<CombineItem>& comb, int32_t& n_parts);
+// The chunk size build_work takes: the longest of 1024, 512, 256, 128 keys that gives at
+// least kPrefillTargetWgs workgroups (128 when none does).
+int prefill_chunk_keys(const std::vector<PrefillReq>& reqs, int n_q, int n_kv);
+constexpr int kPrefillTargetWgs = 512;
 
 // One request of the dense batch, in dense-batch order (decodes, then prefill chunks).
 struct ReqInfo {
@@ -120,15 +149,16 @@ bool parent_depends(int32_t a, int32_t b);
 // Attention work lists of every nano-batch (host side) and, after upload, device pointers.
 struct Meta {
   std::vector<DecodeItem> dec;
-  std::vector<CombineItem> comb;
+  std::vector<CombineItem> comb, pcomb;  // combines of split decode / prefill work
   std::vector<PrefillItem> pf;
-  std::vector<int32_t> dec_begin, comb_begin, pf_begin;  // size n_nano + 1
+  std::vector<int32_t> dec_begin, comb_begin, pf_begin, pcomb_begin;  // size n_nano + 1
   int32_t n_parts = 0;
   const int32_t* d_pos = nullptr;
   const int32_t* d_slot = nullptr;
   const float* d_inv_freq = nullptr;
   const DecodeItem* d_dec = nullptr;
   const CombineItem* d_comb = nullptr;
+  const CombineItem* d_pcomb = nullptr;
   const PrefillItem* d_pf = nullptr;
   const int32_t* d_bt = nullptr;
   // dense ops: byte offset of each GEMM's split-K workspace (2 per op: first, second GEMM)
@@ -137,7 +167,9 @@ struct Meta {
 
 // Decode split-KV chunks of at most `split` blocks (0 = chosen per nano-op so that its
 // (chunk, KV head) units fill the GPU several times; multi-chunk requests get partial slots
-// and a combine entry) and 16-query prefill tiles (longest first), per nano-batch.
-void build_work(const BatchLayout& L, const PlanGraph& g, int split, int n_kv, Meta& M);
+// and a combine entry) and prefill tiles with their key chunks (build_prefill_work, chunk
+// size pf_chunk keys, 0 = prefill_chunk_keys per nano-op), per nano-batch. Partial slots of all of them are
+// distinct (ops of one layer may run concurrently).
+void build_work(const BatchLayout& L, const PlanGraph& g, int split, int pf_chunk, int n_q, int n_kv, Meta& M);
 
 }  // namespace nf

@@ -222,27 +222,8 @@ __device__ __forceinline__ int swz_k(int row) {
     return (row & 7) ^ ((row >> 3) & 1);
 }
 
-// s_waitcnt vmcnt(n) with expcnt / lgkmcnt left free (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // C and R rows are ldc elements apart and, with SwiGLU, the up weights of output column c
 // sit in row b_up + c of B: a launch may cover a column range of a wider product.
-
-// Workgroup barrier ordering LDS only. __syncthreads() (a workgroup fence) also waits for
-// every outstanding global load, vmcnt(0), which would drain the slabs still in flight.
-// Here: this wave's LDS reads complete (lgkmcnt(0)), then s_barrier; the empty asm
-// statements keep the compiler from moving memory accesses across the barrier. Slab data
-// written by the load unit is covered by the explicit vmcnt wait before the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0) only
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // Scheduling request for the region before the next sched_barrier: one MFMA, one LDS read,
 // repeated, then the remaining MFMAs (or reads).

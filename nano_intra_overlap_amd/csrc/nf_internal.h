@@ -25,6 +25,27 @@ constexpr int kBlock = 16;       // KV block size (tokens)
 constexpr int kMaxGroup = 16;    // max query heads per KV head (MFMA column count)
 constexpr int kNumXcd = 8;       // XCDs of an MI355X
 
+// Device helpers shared by the kernels that stream tiles into LDS with direct-to-LDS loads.
+
+// s_waitcnt vmcnt(n) with expcnt / lgkmcnt left free (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier ordering LDS only. __syncthreads() (a workgroup fence) also waits for
+// every outstanding global load, vmcnt(0), which would drain the slabs still in flight.
+// Here: this wave's LDS reads complete (lgkmcnt(0)), then s_barrier; the empty asm
+// statements keep the compiler from moving memory accesses across the barrier. Slab data
+// written by the load unit is covered by the explicit vmcnt wait before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------------------
 // kernel launchers (defined in the .hip files)
 // ---------------------------------------------------------------------------------------
@@ -95,8 +116,11 @@ hipError_t launch_decode_combine(const CombineItem* combines, int n_combines, co
                                  const float* part_ml, bf16* out, int n_q, int n_kv, int d,
                                  hipStream_t s);
 
+// Prefill attention of the listed items, then the merge of the split tiles' partials
+// (combines: one per query of a split tile; partial slots as in PrefillItem).
 hipError_t launch_prefill_attn(const bf16* qkv, const bf16* kpool, const bf16* vpool,
                                const int32_t* block_table, int max_blocks, const PrefillItem* items,
-                               int n_items, bf16* out, int n_q, int n_kv, int d, hipStream_t s);
+                               int n_items, const CombineItem* combines, int n_combines, float* part_o,
+                               float* part_ml, bf16* out, int n_q, int n_kv, int d, hipStream_t s);
 
 }  // namespace nf

@@ -48,6 +48,11 @@ struct Buf {
     bytes = b;
     return hipMalloc(&p, std::max<size_t>(b, 256));
   }
+  void free() {
+    if (p) (void)hipFree(p);
+    p = nullptr;
+    bytes = 0;
+  }
   template <class T>
   T* as() const {
     return static_cast<T*>(p);
@@ -153,7 +158,7 @@ bool build_decode_set(Err& E, const nf_layer_cfg& c, const nf_batch_desc& tmpl, 
     E.msg = err;
     return false;
   }
-  build_work(D.L, D.g, split, c.n_kv_heads, D.M);
+  build_work(D.L, D.g, split, 0, c.n_q_heads, c.n_kv_heads, D.M);
   const int G = c.n_q_heads / c.n_kv_heads;
   if (upload_table) {
     PF_HIP(D.d_bt.alloc(D.bt.size() * 4));
@@ -402,34 +407,41 @@ extern "C" nf_status nf_profile_ops(nf_ctx* ctx, const nf_layer_cfg* cfg, const 
         first = false;
       }
     }
-    // prefill attention: one chunk of length len, no cached prefix
+    // prefill attention: one chunk of length len, no cached prefix (work list and key
+    // chunks as the layer builds them, partials merged by the combine kernel)
     {
       const int lmax = std::min(max_tokens, 2048);
       std::vector<int32_t> bt((lmax + kBlock - 1) / kBlock);
       for (size_t i = 0; i < bt.size(); ++i) bt[i] = (int32_t)i;
-      Buf d_bt, items, out;
+      Buf d_bt, items, combs, part_o, part_ml, out;
       PF_HIP(d_bt.alloc(bt.size() * 4));
       PF_HIP(hipMemcpy(d_bt.p, bt.data(), bt.size() * 4, hipMemcpyHostToDevice));
       PF_HIP(out.alloc((size_t)lmax * Q * 2));
       bool first = true;
       for (int len = step; len <= lmax; len += step) {
+        std::vector<PrefillReq> reqs{PrefillReq{0, 0, len, 0}};
         std::vector<PrefillItem> its;
-        for (int q0 = ((len - 1) / 16) * 16; q0 >= 0; q0 -= 16) {
-          PrefillItem it{};
-          it.req = 0;
-          it.token0 = 0;
-          it.q_begin = q0;
-          it.q_len = len;
-          it.prefix = 0;
-          its.push_back(it);
-        }
-        PF_HIP(items.p ? hipSuccess : items.alloc(((lmax + 15) / 16) * sizeof(PrefillItem)));
+        std::vector<CombineItem> cmb;
+        int32_t n_parts = 0;
+        build_prefill_work(reqs, nq, nkv, prefill_chunk_keys(reqs, nq, nkv), its, cmb, n_parts);
+        items.free();
+        combs.free();
+        part_o.free();
+        part_ml.free();
+        PF_HIP(items.alloc(its.size() * sizeof(PrefillItem)));
         PF_HIP(hipMemcpy(items.p, its.data(), its.size() * sizeof(PrefillItem), hipMemcpyHostToDevice));
+        PF_HIP(combs.alloc(std::max<size_t>(1, cmb.size()) * sizeof(CombineItem)));
+        if (!cmb.empty())
+          PF_HIP(hipMemcpy(combs.p, cmb.data(), cmb.size() * sizeof(CombineItem), hipMemcpyHostToDevice));
+        PF_HIP(part_o.alloc((size_t)std::max(n_parts, 1) * nq * d * 4));
+        PF_HIP(part_ml.alloc((size_t)std::max(n_parts, 1) * nq * 2 * 4));
         double ms;
         if (!time_ms(E, s, 3, [&] { return launch_prefill_attn(S.qkv.as<bf16>(), S.kpool.as<bf16>(),
                                                                 S.vpool.as<bf16>(), d_bt.as<int32_t>(),
                                                                 (int)bt.size(), items.as<PrefillItem>(),
-                                                                (int)its.size(), out.as<bf16>(), nq, nkv, d, s); },
+                                                                (int)its.size(), combs.as<CombineItem>(),
+                                                                (int)cmb.size(), part_o.as<float>(),
+                                                                part_ml.as<float>(), out.as<bf16>(), nq, nkv, d, s); },
                      ms))
           return false;
         pf << (first ? "" : ", ") << "[" << len << ", " << json::num(ms) << "]";

@@ -112,6 +112,7 @@ struct nf_ctx {
   hipEvent_t fork_ev = nullptr;
   std::vector<hipEvent_t> join_ev;
   int decode_split = kDefaultSplit;
+  int prefill_chunk = 0;  // prefill keys per work item (0 = chosen per nano-op)
   int decode_grid = 0;  // max workgroups of the decode attention kernel (0 = one wave per work unit)
   int decode_nbuf = 1;  // KV blocks per online-softmax step
   int decode_ring = 2;  // register buffers of decode_nbuf blocks; decode_ring - 1 groups in flight
@@ -243,7 +244,7 @@ nf_status ensure_events(nf_ctx* ctx, size_t n) {
 
 // Byte offsets of the packed metadata (one upload per call).
 struct MetaPack {
-  size_t o_pos = 0, o_slot = 0, o_inv = 0, o_dec = 0, o_comb = 0, o_pf = 0, o_bt = 0, total = 0;
+  size_t o_pos = 0, o_slot = 0, o_inv = 0, o_dec = 0, o_comb = 0, o_pcomb = 0, o_pf = 0, o_bt = 0, total = 0;
   bool bt_up = false;
 };
 
@@ -266,6 +267,7 @@ nf_status pack_meta(nf_ctx* ctx, const nf_layer_cfg& cfg, const nf_batch_desc& b
   P.o_inv = slot(sizeof(float) * half);
   P.o_dec = slot(sizeof(DecodeItem) * M.dec.size());
   P.o_comb = slot(sizeof(CombineItem) * M.comb.size());
+  P.o_pcomb = slot(sizeof(CombineItem) * M.pcomb.size());
   P.o_pf = slot(sizeof(PrefillItem) * M.pf.size());
   P.o_bt = slot(P.bt_up ? sizeof(int32_t) * n_req * b.max_blocks : 0);
   P.total = off;
@@ -283,6 +285,7 @@ nf_status pack_meta(nf_ctx* ctx, const nf_layer_cfg& cfg, const nf_batch_desc& b
   for (int i = 0; i < half; ++i) inv[i] = (float)std::pow((double)cfg.rope_base, -2.0 * i / cfg.head_dim);
   if (!M.dec.empty()) memcpy(h + P.o_dec, M.dec.data(), sizeof(DecodeItem) * M.dec.size());
   if (!M.comb.empty()) memcpy(h + P.o_comb, M.comb.data(), sizeof(CombineItem) * M.comb.size());
+  if (!M.pcomb.empty()) memcpy(h + P.o_pcomb, M.pcomb.data(), sizeof(CombineItem) * M.pcomb.size());
   if (!M.pf.empty()) memcpy(h + P.o_pf, M.pf.data(), sizeof(PrefillItem) * M.pf.size());
   if (P.bt_up && n_req) memcpy(h + P.o_bt, b.block_table, sizeof(int32_t) * n_req * b.max_blocks);
   return NF_OK;
@@ -308,6 +311,7 @@ void point_meta(const MetaPack& P, const void* base, const nf_batch_desc& b, Met
   M.d_inv_freq = reinterpret_cast<const float*>(d + P.o_inv);
   M.d_dec = reinterpret_cast<const DecodeItem*>(d + P.o_dec);
   M.d_comb = reinterpret_cast<const CombineItem*>(d + P.o_comb);
+  M.d_pcomb = reinterpret_cast<const CombineItem*>(d + P.o_pcomb);
   M.d_pf = reinterpret_cast<const PrefillItem*>(d + P.o_pf);
   M.d_bt = P.bt_up ? reinterpret_cast<const int32_t*>(d + P.o_bt) : b.block_table_dev;
 }
@@ -540,9 +544,12 @@ nf_status launch_op(nf_ctx* ctx, const LayerArgs& A, const PlanGraph& g, const N
     }
     case NF_OP_PFATTN: {
       const int i0 = M.pf_begin[op.nano], i1 = M.pf_begin[op.nano + 1];
+      const int c0 = M.pcomb_begin[op.nano], c1 = M.pcomb_begin[op.nano + 1];
       NF_TRY(timed(ctx, NF_K_PREFILL_ATTN, s, [&] {
         return launch_prefill_attn(qkv, static_cast<const bf16*>(A.pool->k), static_cast<const bf16*>(A.pool->v),
-                                   M.d_bt, A.max_blocks, M.d_pf + i0, i1 - i0, attn, nq, nkv, d, s);
+                                   M.d_bt, A.max_blocks, M.d_pf + i0, i1 - i0, M.d_pcomb + c0, c1 - c0,
+                                   static_cast<float*>(ctx->part_o.p), static_cast<float*>(ctx->part_ml.p), attn, nq,
+                                   nkv, d, s);
       }));
       break;
     }
@@ -596,7 +603,7 @@ nf_status prepare_host(nf_ctx* ctx, const nf_layer_cfg* cfg, const nf_batch_desc
       st = mask_ok(ctx, plan->cu_masks + s * NF_CU_MASK_WORDS);
       if (st != NF_OK) return st;
     }
-  build_work(L, g, ctx->decode_split, cfg->n_kv_heads, M);
+  build_work(L, g, ctx->decode_split, ctx->prefill_chunk, cfg->n_q_heads, cfg->n_kv_heads, M);
   if ((st = ensure_workspace(ctx, *cfg, L.T)) != NF_OK) return st;
   if ((st = ensure_parts(ctx, *cfg, M.n_parts)) != NF_OK) return st;
   return plan_gemm_ws(ctx, *cfg, g, M);
@@ -1095,7 +1102,9 @@ static nf_status op_attention(nf_ctx* ctx, const char* name, const nf_layer_cfg*
   } else {
     NF_HIP(ctx, launch_prefill_attn(static_cast<const bf16*>(qkv), static_cast<const bf16*>(pool->k),
                                     static_cast<const bf16*>(pool->v), M.d_bt, batch->max_blocks, M.d_pf,
-                                    (int)M.pf.size(), static_cast<bf16*>(out), nq, nkv, d, s));
+                                    (int)M.pf.size(), M.d_pcomb, (int)M.pcomb.size(),
+                                    static_cast<float*>(ctx->part_o.p), static_cast<float*>(ctx->part_ml.p),
+                                    static_cast<bf16*>(out), nq, nkv, d, s));
   }
   return NF_OK;
 }
@@ -1231,6 +1240,11 @@ extern "C" nf_status nf_timing_summary(nf_ctx* ctx, int32_t cls, int32_t* count,
 extern "C" nf_status nf_ctx_set_decode_split(nf_ctx* ctx, int32_t blocks) {
   if (!ctx || blocks < 0 || blocks > kMaxSplit) return NF_E_ARG;
   ctx->decode_split = blocks;
+  return NF_OK;
+}
+extern "C" nf_status nf_ctx_set_prefill_chunk(nf_ctx* ctx, int32_t keys) {
+  if (!ctx || keys < 0 || keys > kPrefillMaxChunkKeys || keys % 32) return NF_E_ARG;
+  ctx->prefill_chunk = keys;
   return NF_OK;
 }
 extern "C" nf_status nf_ctx_set_decode_launch(nf_ctx* ctx, int32_t max_workgroups, int32_t nbuf, int32_t ring) {

@@ -62,7 +62,9 @@ def test_profilers_on_the_tiny_layer(tmp_path):
     finally:
         abi.nf_ctx_destroy(ctx)
     with open(d_path) as f:
-        check_dbest(json.load(f), 256, n_variants=len(abi.nf_gemm_variants()))
+        # the tiny shape's products take a few microseconds, launch latency included: their
+        # times need not grow with the batch
+        check_dbest(json.load(f), 256, n_variants=len(abi.nf_gemm_variants()), monotone=False)
     with open(r_path) as f:
         r = json.load(f)
     r["min_gain"] = 0.0
