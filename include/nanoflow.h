@@ -184,7 +184,7 @@ const char *nf_version(void);
  * its work, else 1..4096. Errors: NF_E_ARG.                                                 */
 nf_status nf_ctx_set_decode_split(nf_ctx *ctx, int32_t blocks);
 /* Prefill attention work item: keys of a query tile per item, 0 (default) = chosen per
- * nano-op (the longest of 1024, 512, 256, 128 that still gives a few workgroups per CU),
+ * nano-op (the longest of 1024, 512, 256, 128 that still gives a workgroup per CU),
  * else a multiple of 32 up to 1024; a tile with more keys is split into items whose fp32
  * partials are merged after. Errors: NF_E_ARG.                                              */
 nf_status nf_ctx_set_prefill_chunk(nf_ctx *ctx, int32_t keys);

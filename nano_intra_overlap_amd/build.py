@@ -27,7 +27,8 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", 
              "-munsafe-fp-atomics"]
 # attention: MFMA accumulators in ordinary VGPRs (fewer registers, no AGPR copies around the
 # online-softmax rescale), which leaves room for GEMM waves on the same SIMD
-PER_FILE_FLAGS = {"nf_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+PER_FILE_FLAGS = {"nf_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                  "nf_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():

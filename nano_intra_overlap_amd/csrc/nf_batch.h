@@ -66,7 +66,7 @@ void build_prefill_work(const std::vector<PrefillReq>& reqs, int n_q, int n_kv, 
 // The chunk size build_work takes: the longest of 1024, 512, 256, 128 keys that gives at
 // least kPrefillTargetWgs workgroups (128 when none does).
 int prefill_chunk_keys(const std::vector<PrefillReq>& reqs, int n_q, int n_kv);
-constexpr int kPrefillTargetWgs = 512;
+constexpr int kPrefillTargetWgs = 256;
 
 // One request of the dense batch, in dense-batch order (decodes, then prefill chunks).
 struct ReqInfo {

@@ -12,20 +12,34 @@
 
 namespace nf {
 
-// One workgroup of 256 threads per row; each thread owns chunks of 8 contiguous elements.
+// One workgroup of 256 threads per row; each thread owns CPT chunks of 8 contiguous
+// elements (n <= 2048 CPT), loaded once and kept in registers for the scaling pass (0: any n,
+// the row read twice).
+template <int CPT>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const bf16* __restrict__ x, const bf16* __restrict__ g,
                                                       bf16* __restrict__ out, int n, float eps) {
   const int row = blockIdx.x;
   const bf16* xr = x + (size_t)row * n;
   bf16* orow = out + (size_t)row * n;
   const int chunks = n / 8;
+  constexpr int R = CPT > 0 ? CPT : 1;
+  bf16x8 keep[R];
   float ss = 0.0f;
-  for (int c = threadIdx.x; c < chunks; c += 256) {
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(xr + c * 8);
+  if constexpr (CPT > 0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float f = (float)v[j];
-      ss += f * f;
+    for (int i = 0; i < CPT; ++i) {
+      const int c = threadIdx.x + i * 256;
+      if (c < chunks) {
+        keep[i] = *reinterpret_cast<const bf16x8*>(xr + c * 8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss += (float)keep[i][j] * (float)keep[i][j];
+      }
+    }
+  } else {
+    for (int c = threadIdx.x; c < chunks; c += 256) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(xr + c * 8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += (float)v[j] * (float)v[j];
     }
   }
   // wave reduction then across the 4 waves
@@ -36,19 +50,35 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const bf16* __restrict__ x
   __syncthreads();
   const float total = red[0] + red[1] + red[2] + red[3];
   const float inv = rsqrtf(total / (float)n + eps);
-  for (int c = threadIdx.x; c < chunks; c += 256) {
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(xr + c * 8);
+  auto scale = [&](int c, const bf16x8& v) {
     const bf16x8 gv = *reinterpret_cast<const bf16x8*>(g + c * 8);
     bf16x8 o;
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = (bf16)(((float)v[j] * inv) * (float)gv[j]);
     *reinterpret_cast<bf16x8*>(orow + c * 8) = o;
+  };
+  if constexpr (CPT > 0) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = threadIdx.x + i * 256;
+      if (c < chunks) scale(c, keep[i]);
+    }
+  } else {
+    for (int c = threadIdx.x; c < chunks; c += 256) scale(c, *reinterpret_cast<const bf16x8*>(xr + c * 8));
   }
 }
 
 hipError_t launch_rmsnorm(const bf16* x, const bf16* g, bf16* out, int m, int n, float eps, hipStream_t s) {
   if (m <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(m), dim3(256), 0, s, x, g, out, n, eps);
+  const int cpt = (n / 8 + 255) / 256;
+  if (cpt <= 1)
+    hipLaunchKernelGGL(rmsnorm_kernel<1>, dim3(m), dim3(256), 0, s, x, g, out, n, eps);
+  else if (cpt == 2)
+    hipLaunchKernelGGL(rmsnorm_kernel<2>, dim3(m), dim3(256), 0, s, x, g, out, n, eps);
+  else if (cpt <= 4)
+    hipLaunchKernelGGL(rmsnorm_kernel<4>, dim3(m), dim3(256), 0, s, x, g, out, n, eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<0>, dim3(m), dim3(256), 0, s, x, g, out, n, eps);
   return hipGetLastError();
 }
 
