@@ -155,7 +155,13 @@ enum {
  * the range-intersection dependencies. A NULL plan runs one nano-batch sequentially on
  * the caller's stream (the non-overlapped baseline). decode_max_workgroups bounds the
  * decode-attention grid (its waves then stride over the work), i.e. the memory nano-op's
- * share of the CUs' wave slots when it shares them with the GEMMs.                        */
+ * share of the CUs' wave slots when it shares them with the GEMMs.
+ * op_lane (optional, NULL = each op's lane is its stream; else n_ops entries in 0..2)
+ * groups nano-operations into lanes that run one op at a time in the listed order even
+ * when their ops sit on different streams: a compute lane can then put some dense ops on a
+ * CU-masked stream beside the memory stream and others on an unmasked stream, i.e. give
+ * each nano-operation its own resource share (NanoFlow summary page, "Auto-Search Stage
+ * II: Refining the Pipeline"), without two of its ops running at once.                     */
 typedef struct {
   int32_t n_nano;
   const int32_t *bounds;
@@ -164,6 +170,7 @@ typedef struct {
   int32_t n_ops;
   const int32_t *op_kind, *op_nano, *op_stream;
   int32_t decode_max_workgroups; /* cap on decode-attention workgroups, 0 = context default */
+  const int32_t *op_lane;        /* NULL, or the lane (0..2) of each listed op              */
 } nf_plan;
 
 /* ---- context ---------------------------------------------------------------------------- */
@@ -431,7 +438,9 @@ enum {
 
 /* Start collecting kernel timings for the classes whose bit is set in class_mask (0 stops):
  * every later launch of such a kernel by nf_layer_forward is bracketed by HIP timing events
- * recorded on the stream the kernel runs on. Clears earlier records. Errors: NF_E_ARG.      */
+ * recorded on the stream the kernel runs on (decode attention: by the kernel's dispatch
+ * itself, so its timing adds no marker between it and its neighbours). Clears earlier
+ * records. Errors: NF_E_ARG.                                                                */
 nf_status nf_ctx_set_timing(nf_ctx *ctx, uint32_t class_mask);
 
 /* Launch count and total / min / max duration (ms) of the recorded launches of class `cls`

@@ -65,7 +65,7 @@ class nf_kv_pool(ctypes.Structure):
 class nf_plan(ctypes.Structure):
     _fields_ = [("n_nano", ctypes.c_int32), ("bounds", _i32p), ("n_streams", ctypes.c_int32), ("cu_masks", _u32p),
                 ("n_ops", ctypes.c_int32), ("op_kind", _i32p), ("op_nano", _i32p), ("op_stream", _i32p),
-                ("decode_max_workgroups", ctypes.c_int32)]
+                ("decode_max_workgroups", ctypes.c_int32), ("op_lane", _i32p)]
 
 
 class nf_kv_ranges(ctypes.Structure):
@@ -215,26 +215,35 @@ class HostPlan:
     """nf_plan over numpy arrays kept alive by this object.
 
     ops: list of (kind, nano, stream) in issue order; cu_masks: list of n_streams lists of
-    NF_CU_MASK_WORDS words, or None for unmasked streams.
+    NF_CU_MASK_WORDS words, or None for unmasked streams; lanes: None (lane = stream) or
+    one lane (0..2) per listed op.
     """
 
-    def __init__(self, bounds, ops, n_streams: int, cu_masks=None, decode_max_workgroups: int = 0):
+    def __init__(self, bounds, ops, n_streams: int, cu_masks=None, decode_max_workgroups: int = 0, lanes=None):
         self.bounds = _i32(bounds)
         ops = np.asarray(ops, dtype=np.int32).reshape(-1, 3)
         self.kind = np.ascontiguousarray(ops[:, 0])
         self.nano = np.ascontiguousarray(ops[:, 1])
         self.stream = np.ascontiguousarray(ops[:, 2])
+        self.lane = None if lanes is None else _i32(lanes)
+        if self.lane is not None and self.lane.shape[0] != ops.shape[0]:
+            raise ValueError("lanes needs one entry per op")
         self.masks = None
         if cu_masks is not None:
             self.masks = np.ascontiguousarray(np.asarray(cu_masks, dtype=np.uint32).reshape(n_streams, NF_CU_MASK_WORDS))
         self.n_streams = n_streams
         self.desc = nf_plan(self.bounds.shape[0] - 1, _ptr(self.bounds), n_streams,
                             None if self.masks is None else self.masks.ctypes.data_as(_u32p), ops.shape[0],
-                            _ptr(self.kind), _ptr(self.nano), _ptr(self.stream), int(decode_max_workgroups))
+                            _ptr(self.kind), _ptr(self.nano), _ptr(self.stream), int(decode_max_workgroups),
+                            None if self.lane is None else _ptr(self.lane))
 
     @property
     def ops(self):
         return list(zip(self.kind.tolist(), self.nano.tolist(), self.stream.tolist()))
+
+    @property
+    def lanes(self):
+        return self.stream.tolist() if self.lane is None else self.lane.tolist()
 
 
 def cu_mask(fraction: float | None = None, per_xcd: int | None = None, offset: int = 0, n_cu: int = 256):

@@ -48,8 +48,11 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--step", type=int, default=128)
     ap.add_argument("--max-nano", type=int, default=4)
-    ap.add_argument("--r-grid", default="0.25,0.375,0.5,0.625,0.75")
+    ap.add_argument("--r-grid", default="0.125,0.25,0.375,0.5,0.625,0.75,0.875",
+                    help="memory-stream CU shares to profile (each with the compute op on the complement mask "
+                         "and on the whole GPU)")
     ap.add_argument("--skip-profile", action="store_true")
+    ap.add_argument("--skip-ops", action="store_true", help="keep the D_best table, profile interference only")
     ap.add_argument("--min-gain", type=float, default=0.06,
                     help="an overlapped plan must be predicted this fraction faster than the sequential one "
                          "(written into the interference table; measured on MI355X: overlapped plans run 6-10%% "
@@ -70,8 +73,9 @@ def main():
     if not args.skip_profile:
         ctx = abi.nf_ctx_create(0)
         t0 = time.time()
-        abi.nf_profile_ops(ctx, cfg, hb, b.num_blocks, args.step, wl.n_tokens, d)
-        print(f"[autosearch] D_best table -> {d} ({time.time() - t0:.1f} s)", flush=True)
+        if not args.skip_ops:
+            abi.nf_profile_ops(ctx, cfg, hb, b.num_blocks, args.step, wl.n_tokens, d)
+            print(f"[autosearch] D_best table -> {d} ({time.time() - t0:.1f} s)", flush=True)
         t0 = time.time()
         grid = [float(x) for x in args.r_grid.split(",") if x]
         abi.nf_profile_interference(ctx, cfg, hb, b.num_blocks, grid, r)

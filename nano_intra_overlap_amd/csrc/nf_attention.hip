@@ -293,12 +293,20 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const CombineItem* 
 
 // ---------------------------------------------------------------------------------------
 
+// ev_start / ev_stop (both or neither): timing events recorded by the dispatch itself
+// (no marker packets between this kernel and its neighbours on the stream).
 template <int D, int NB, int R>
 static void launch_decode_t(int grid, hipStream_t s, const bf16* qkv, const bf16* kpool, const bf16* vpool,
                             const int32_t* block_table, int max_blocks, const DecodeItem* items, int n_items,
-                            float* part_o, float* part_ml, bf16* out, int n_q, int n_kv, float scale_log2) {
-  hipLaunchKernelGGL((decode_attn_kernel<D, NB, R>), dim3(grid), dim3(256), 0, s, qkv, kpool, vpool, block_table,
-                     max_blocks, items, n_items, part_o, part_ml, out, n_q, n_kv, scale_log2);
+                            float* part_o, float* part_ml, bf16* out, int n_q, int n_kv, float scale_log2,
+                            hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (ev_start)
+    hipExtLaunchKernelGGL((decode_attn_kernel<D, NB, R>), dim3(grid), dim3(256), 0, s, ev_start, ev_stop, 0, qkv,
+                          kpool, vpool, block_table, max_blocks, items, n_items, part_o, part_ml, out, n_q, n_kv,
+                          scale_log2);
+  else
+    hipLaunchKernelGGL((decode_attn_kernel<D, NB, R>), dim3(grid), dim3(256), 0, s, qkv, kpool, vpool, block_table,
+                       max_blocks, items, n_items, part_o, part_ml, out, n_q, n_kv, scale_log2);
 }
 
 // Supported (blocks per softmax step, ring depth) pairs.
@@ -306,11 +314,11 @@ template <int D>
 static hipError_t launch_decode_d(int nb, int ring, int grid, hipStream_t s, const bf16* qkv, const bf16* kpool,
                                   const bf16* vpool, const int32_t* block_table, int max_blocks,
                                   const DecodeItem* items, int n_items, float* part_o, float* part_ml, bf16* out,
-                                  int n_q, int n_kv, float scale_log2) {
+                                  int n_q, int n_kv, float scale_log2, hipEvent_t ev_start, hipEvent_t ev_stop) {
 #define NF_DECODE_CASE(NB_, R_)                                                                                 \
   if (nb == NB_ && ring == R_) {                                                                                \
     launch_decode_t<D, NB_, R_>(grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o,    \
-                                part_ml, out, n_q, n_kv, scale_log2);                                           \
+                                part_ml, out, n_q, n_kv, scale_log2, ev_start, ev_stop);                        \
     return hipGetLastError();                                                                                   \
   }
   NF_DECODE_CASE(1, 2)
@@ -330,7 +338,8 @@ bool decode_config_supported(int nb, int ring) {
 // flight); max_grid: workgroup cap (0 = one wave per unit)
 hipError_t launch_decode_attn(const bf16* qkv, const bf16* kpool, const bf16* vpool, const int32_t* block_table,
                               int max_blocks, const DecodeItem* items, int n_items, float* part_o, float* part_ml,
-                              bf16* out, int n_q, int n_kv, int d, int max_grid, int nb, int ring, hipStream_t s) {
+                              bf16* out, int n_q, int n_kv, int d, int max_grid, int nb, int ring, hipStream_t s,
+                              hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (n_items <= 0) return hipSuccess;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)d);
   const int waves = n_items * n_kv;
@@ -338,10 +347,10 @@ hipError_t launch_decode_attn(const bf16* qkv, const bf16* kpool, const bf16* vp
   if (max_grid > 0 && grid > max_grid) grid = max_grid;
   if (d == 128)
     return launch_decode_d<128>(nb, ring, grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o,
-                                part_ml, out, n_q, n_kv, scale_log2);
+                                part_ml, out, n_q, n_kv, scale_log2, ev_start, ev_stop);
   if (d == 64)
     return launch_decode_d<64>(nb, ring, grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o,
-                               part_ml, out, n_q, n_kv, scale_log2);
+                               part_ml, out, n_q, n_kv, scale_log2, ev_start, ev_stop);
   return hipErrorInvalidValue;
 }
 

@@ -178,7 +178,7 @@ static bool intersects(const NanoOp& a, const NanoOp& b) {
 nf_status build_plan_graph(const BatchLayout& L, const nf_plan* plan, PlanGraph& g, std::string& err) {
   g = PlanGraph();
   const int32_t T = L.T;
-  std::vector<int32_t> kinds, nanos, streams;
+  std::vector<int32_t> kinds, nanos, streams, lanes;
   if (!plan) {
     g.n_nano = 1;
     g.n_streams = 1;
@@ -224,9 +224,15 @@ nf_status build_plan_graph(const BatchLayout& L, const nf_plan* plan, PlanGraph&
         err = fmt("plan lists op kind %ld of nano-batch %ld twice", k, j);
         return NF_E_PLAN;
       }
+      const int32_t lane = plan->op_lane ? plan->op_lane[i] : s;
+      if (lane < 0 || lane > 2) {
+        err = fmt("plan op %ld: lane out of range 0..2", i);
+        return NF_E_PLAN;
+      }
       kinds.push_back(k);
       nanos.push_back(j);
       streams.push_back(s);
+      lanes.push_back(lane);
     }
   }
   // nano-batch of a token row
@@ -277,6 +283,18 @@ nf_status build_plan_graph(const BatchLayout& L, const nf_plan* plan, PlanGraph&
     for (int32_t i = 0; i < n_ops; ++i)
       if (i != j && parent_depends(g.ops[i].kind, g.ops[j].kind) && intersects(g.ops[i], g.ops[j]))
         g.deps[j].push_back(i);
+  // lane order: an op waits for the lane's previous listed op when that one ran on another
+  // stream (on the same stream, stream order already serialises them)
+  if (!lanes.empty()) {
+    int32_t prev[3] = {-1, -1, -1};
+    for (int32_t j = 0; j < n_ops; ++j) {
+      const int32_t i = prev[lanes[j]];
+      if (i >= 0 && g.ops[i].stream != g.ops[j].stream &&
+          std::find(g.deps[j].begin(), g.deps[j].end(), i) == g.deps[j].end())
+        g.deps[j].push_back(i);
+      prev[lanes[j]] = j;
+    }
+  }
   // global order: Kahn's algorithm over dependency edges plus per-stream order edges,
   // preferring the plan's listed position
   std::vector<std::vector<int32_t>> succ(n_ops);

@@ -107,10 +107,12 @@ hipError_t launch_rope_kv(bf16* qkv, const int32_t* tok_pos, const int32_t* tok_
                           const float* inv_freq, bf16* kpool, bf16* vpool, int t_begin, int t_end,
                           int n_q, int n_kv, int d, hipStream_t s);
 
+// ev_start / ev_stop: optional timing events recorded by the dispatch itself (both or none).
 hipError_t launch_decode_attn(const bf16* qkv, const bf16* kpool, const bf16* vpool,
                               const int32_t* block_table, int max_blocks, const DecodeItem* items,
                               int n_items, float* part_o, float* part_ml, bf16* out, int n_q,
-                              int n_kv, int d, int max_grid, int nb, int ring, hipStream_t s);
+                              int n_kv, int d, int max_grid, int nb, int ring, hipStream_t s,
+                              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 bool decode_config_supported(int nb, int ring);
 hipError_t launch_decode_combine(const CombineItem* combines, int n_combines, const float* part_o,
                                  const float* part_ml, bf16* out, int n_q, int n_kv, int d,

@@ -533,6 +533,7 @@ extern "C" nf_status nf_profile_interference(nf_ctx* ctx, const nf_layer_cfg* cf
       return launch_gemm(S.attn.as<bf16>(), S.wo.as<bf16>(), S.y.as<bf16>(), S.x.as<bf16>(), m, H, Q, 1, vo, s,
                          gws.as<float>(), wsb);
     };
+    constexpr int kMemLoops = 4;  // memory nano-ops per concurrent run
     struct Kind {
       const char* name;
       std::function<hipError_t(hipStream_t)> op;
@@ -567,18 +568,24 @@ extern "C" nf_status nf_profile_interference(nf_ctx* ctx, const nf_layer_cfg* cf
     tg_best = kinds[0].best;
     if (!best_ms(mem_op, tm_best)) return false;
 
+    // masked entries come in pairs: the compute op on the complement of the memory mask,
+    // and ("gemm_full") on the whole GPU beside the same memory mask, so a plan can give
+    // each compute kind either share
     struct Cfg {
       std::string name;
       double r;
       bool masked;
       int grid;
+      bool gemm_full;
     };
-    std::vector<Cfg> cfgs = {{"shared", -1.0, false, 0}, {"shared_grid256", -1.0, false, 256},
-                             {"shared_grid512", -1.0, false, 512}};
+    std::vector<Cfg> cfgs = {{"shared", -1.0, false, 0, false}, {"shared_grid256", -1.0, false, 256, false},
+                             {"shared_grid512", -1.0, false, 512, false}};
     for (int i = 0; i < n_r; ++i) {
-      char nm[32];
+      char nm[48];
       snprintf(nm, sizeof nm, "mask_r%.3g", r_grid[i]);
-      cfgs.push_back({nm, (double)r_grid[i], true, 0});
+      cfgs.push_back({nm, (double)r_grid[i], true, 0, false});
+      snprintf(nm, sizeof nm, "mask_r%.3g_gemm_full", r_grid[i]);
+      cfgs.push_back({nm, (double)r_grid[i], true, 0, true});
     }
     o << "{\"device_cus\": 256, \"cfg\": " << cfg_json(c) << ", \"gemm_op\": \"" << (c.n_experts > 0 ? "MoE FFN (router, grouped Up/Gate+SwiGLU, grouped Down, combine), " : "Up/Gate+SwiGLU+Down, ") << m
       << " rows (KQV and O of as many rows in the *_kind fields)\", \"mem_op\": \"decode attention, " << n_dec << " requests\", \"t_gemm_best_ms\": "
@@ -596,11 +603,15 @@ extern "C" nf_status nf_profile_interference(nf_ctx* ctx, const nf_layer_cfg* cf
           const int slot = i / 8;  // bit i -> XCD i % 8; the slot-th CU of that XCD
           masks[slot < 32 - per ? 0 : 1][i / 32] |= 1u << (i % 32);
         }
-        PF_HIP(hipExtStreamCreateWithCUMask(&own[0], NF_CU_MASK_WORDS, masks[0]));
-        made.push_back(own[0]);
+        if (cf.gemm_full) {
+          for (int w = 0; w < NF_CU_MASK_WORDS; ++w) masks[0][w] = 0xFFFFFFFFu;
+        } else {
+          PF_HIP(hipExtStreamCreateWithCUMask(&own[0], NF_CU_MASK_WORDS, masks[0]));
+          made.push_back(own[0]);
+          sg = own[0];
+        }
         PF_HIP(hipExtStreamCreateWithCUMask(&own[1], NF_CU_MASK_WORDS, masks[1]));
         made.push_back(own[1]);
-        sg = own[0];
         sm = own[1];
       }
       grid = cf.grid;
@@ -619,47 +630,57 @@ extern "C" nf_status nf_profile_interference(nf_ctx* ctx, const nf_layer_cfg* cf
       std::vector<Pair> pairs;
       for (Kind& k : kinds) {
         double tg_alone = k.best;
-        if (cf.masked)
+        if (cf.masked && !cf.gemm_full)
           if (!time_ms(E, sg, 3, [&] { return k.op(sg); }, tg_alone)) return false;
-        const int lm = 2;
+        const int lm = kMemLoops;
         const int lg = std::max(1, (int)std::lround(lm * tm_alone / tg_alone));
-        hipEvent_t e0, eg, em;
-        PF_HIP(hipEventCreate(&e0));
-        PF_HIP(hipEventCreate(&eg));
-        PF_HIP(hipEventCreate(&em));
-        PF_HIP(hipStreamSynchronize(sg));
-        PF_HIP(hipStreamSynchronize(sm));
-        PF_HIP(hipEventRecord(e0, sg));
-        PF_HIP(hipStreamWaitEvent(sm, e0, 0));
-        for (int i = 0; i < lg; ++i) PF_HIP(k.op(sg));
-        for (int i = 0; i < lm; ++i) PF_HIP(mem_op(sm));
-        PF_HIP(hipEventRecord(eg, sg));
-        PF_HIP(hipEventRecord(em, sm));
-        PF_HIP(hipEventSynchronize(eg));
-        PF_HIP(hipEventSynchronize(em));
-        float fg = 0, fm = 0;
-        PF_HIP(hipEventElapsedTime(&fg, e0, eg));
-        PF_HIP(hipEventElapsedTime(&fm, e0, em));
-        (void)hipEventDestroy(e0);
-        (void)hipEventDestroy(eg);
-        (void)hipEventDestroy(em);
         const double wg = lg * k.best, wm = lm * tm_best;
         const double pg_alone = std::min(1.0, k.best / tg_alone);
-        const double t1 = std::min((double)fg, (double)fm);
-        double pg_both, pm_both;
-        if (fg <= fm) {
-          pg_both = wg / t1;
-          pm_both = std::max(1e-3, (wm - (fm - t1) * pm_alone) / t1);
-        } else {
-          pm_both = wm / t1;
-          pg_both = std::max(1e-3, (wg - (fg - t1) * pg_alone) / t1);
+        // three concurrent runs; each speed is the median of its three values
+        double v_pg[3], v_pm[3], v_fg[3], v_fm[3];
+        for (int rep = 0; rep < 3; ++rep) {
+          hipEvent_t e0, eg, em;
+          PF_HIP(hipEventCreate(&e0));
+          PF_HIP(hipEventCreate(&eg));
+          PF_HIP(hipEventCreate(&em));
+          PF_HIP(hipStreamSynchronize(sg));
+          PF_HIP(hipStreamSynchronize(sm));
+          PF_HIP(hipEventRecord(e0, sg));
+          PF_HIP(hipStreamWaitEvent(sm, e0, 0));
+          for (int i = 0; i < lg; ++i) PF_HIP(k.op(sg));
+          for (int i = 0; i < lm; ++i) PF_HIP(mem_op(sm));
+          PF_HIP(hipEventRecord(eg, sg));
+          PF_HIP(hipEventRecord(em, sm));
+          PF_HIP(hipEventSynchronize(eg));
+          PF_HIP(hipEventSynchronize(em));
+          float fg = 0, fm = 0;
+          PF_HIP(hipEventElapsedTime(&fg, e0, eg));
+          PF_HIP(hipEventElapsedTime(&fm, e0, em));
+          (void)hipEventDestroy(e0);
+          (void)hipEventDestroy(eg);
+          (void)hipEventDestroy(em);
+          const double t1 = std::min((double)fg, (double)fm);
+          if (fg <= fm) {
+            v_pg[rep] = wg / t1;
+            v_pm[rep] = std::max(1e-3, (wm - (fm - t1) * pm_alone) / t1);
+          } else {
+            v_pm[rep] = wm / t1;
+            v_pg[rep] = std::max(1e-3, (wg - (fg - t1) * pg_alone) / t1);
+          }
+          v_fg[rep] = fg;
+          v_fm[rep] = fm;
         }
+        auto median3 = [](double* v) {
+          std::sort(v, v + 3);
+          return v[1];
+        };
+        const double pg_both = median3(v_pg), pm_both = median3(v_pm), fg = median3(v_fg), fm = median3(v_fm);
         pairs.push_back({pg_both, pm_both, pg_alone, fg, fm, lg});
       }
       const Pair& u = pairs[0];  // Up/Gate/Down: the entry's plain fields
       const double pg_both = u.pg_both, pm_both = u.pm_both, pg_alone = u.pg_alone;
       const float fg = (float)u.fg, fm = (float)u.fm;
-      const int lg = u.lg, lm = 2;
+      const int lg = u.lg, lm = kMemLoops;
       auto kind_obj = [&](double Pair::*f) {
         std::ostringstream k;
         k << "{";
@@ -669,6 +690,7 @@ extern "C" nf_status nf_profile_interference(nf_ctx* ctx, const nf_layer_cfg* cf
         return k.str();
       };
       o << (first ? "" : ",") << "\n  {\"name\": " << json::quote(cf.name) << ", \"r_mem\": " << json::num(cf.r)
+        << ", \"gemm_full\": " << (cf.gemm_full ? "true" : "false")
         << ", \"decode_grid\": " << cf.grid << ", \"p_gemm_both\": " << json::num(pg_both)
         << ", \"p_mem_both\": " << json::num(pm_both) << ", \"p_gemm_alone\": " << json::num(pg_alone)
         << ", \"p_mem_alone\": " << json::num(pm_alone) << ", \"concurrent_ms\": [" << json::num(fg) << ", "

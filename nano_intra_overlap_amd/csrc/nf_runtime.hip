@@ -224,15 +224,20 @@ nf_status get_stream(nf_ctx* ctx, const uint32_t* mask, int idx, hipStream_t* ou
   return NF_OK;
 }
 
+// Events that order work between streams of this one device: agent-scope fences suffice
+// (every stream's kernels run on this device), so the system-scope fence that would make
+// memory visible to the host at each record is left out.
+constexpr unsigned kDeviceEventFlags = hipEventDisableTiming | hipEventDisableSystemFence;
+
 nf_status ensure_events(nf_ctx* ctx, size_t n) {
   while (ctx->events.size() < n) {
     hipEvent_t e;
-    NF_HIP(ctx, hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    NF_HIP(ctx, hipEventCreateWithFlags(&e, kDeviceEventFlags));
     ctx->events.push_back(e);
   }
   while (ctx->join_ev.size() < (size_t)kMaxStreams) {
     hipEvent_t e;
-    NF_HIP(ctx, hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    NF_HIP(ctx, hipEventCreateWithFlags(&e, kDeviceEventFlags));
     ctx->join_ev.push_back(e);
   }
   return NF_OK;
@@ -425,8 +430,8 @@ nf_status plan_gemm_ws(nf_ctx* ctx, const nf_layer_cfg& c, const PlanGraph& g, M
 
 nf_status timing_event(nf_ctx* ctx, hipEvent_t* e) {
   if (ctx->timing_pool_used == ctx->timing_pool.size()) {
-    hipEvent_t ev;
-    NF_HIP(ctx, hipEventCreate(&ev));
+    hipEvent_t ev;  // timing only: no memory is handed to the host through it
+    NF_HIP(ctx, hipEventCreateWithFlags(&ev, hipEventDisableSystemFence));
     ctx->timing_pool.push_back(ev);
   }
   *e = ctx->timing_pool[ctx->timing_pool_used++];
@@ -449,6 +454,23 @@ nf_status timed(nf_ctx* ctx, int cls, hipStream_t s, F fn) {
     NF_HIP(ctx, hipEventRecord(b, s));
     ctx->timed.push_back({cls, a, b});
   }
+  return NF_OK;
+}
+
+// As timed, for a launcher that records the events in its kernel's dispatch (fn(start,
+// stop), both null when the class is not timed): no marker packets on the stream, so timing
+// does not delay the kernels around it.
+template <class F>
+nf_status timed_dispatch(nf_ctx* ctx, int cls, F fn) {
+  const bool on = (ctx->timing_mask >> cls) & 1u;
+  hipEvent_t a = nullptr, b = nullptr;
+  if (on) {
+    nf_status st = timing_event(ctx, &a);
+    if (st == NF_OK) st = timing_event(ctx, &b);
+    if (st != NF_OK) return st;
+  }
+  NF_HIP(ctx, fn(a, b));
+  if (on) ctx->timed.push_back({cls, a, b});
   return NF_OK;
 }
 
@@ -529,11 +551,11 @@ nf_status launch_op(nf_ctx* ctx, const LayerArgs& A, const PlanGraph& g, const N
     case NF_OP_DECATTN: {
       const int i0 = M.dec_begin[op.nano], i1 = M.dec_begin[op.nano + 1];
       const int c0 = M.comb_begin[op.nano], c1 = M.comb_begin[op.nano + 1];
-      NF_TRY(timed(ctx, NF_K_DECODE_ATTN, s, [&] {
+      NF_TRY(timed_dispatch(ctx, NF_K_DECODE_ATTN, [&](hipEvent_t e0, hipEvent_t e1) {
         return launch_decode_attn(qkv, static_cast<const bf16*>(A.pool->k), static_cast<const bf16*>(A.pool->v),
                                   M.d_bt, A.max_blocks, M.d_dec + i0, i1 - i0, static_cast<float*>(ctx->part_o.p),
                                   static_cast<float*>(ctx->part_ml.p), attn, nq, nkv, d, A.decode_grid,
-                                  ctx->decode_nbuf, ctx->decode_ring, s);
+                                  ctx->decode_nbuf, ctx->decode_ring, s, e0, e1);
       }));
       if (c1 > c0)
         NF_TRY(timed(ctx, NF_K_DECODE_COMBINE, s, [&] {
@@ -711,7 +733,7 @@ extern "C" nf_status nf_ctx_create(int device, nf_ctx** out) {
   ctx->device = device;
   for (auto& row : ctx->gemm_variant) row[0] = row[1] = -1;
   if (hipEventCreateWithFlags(&ctx->upload_done, hipEventDisableTiming) != hipSuccess) return NF_E_HIP;
-  if (hipEventCreateWithFlags(&ctx->fork_ev, hipEventDisableTiming) != hipSuccess) return NF_E_HIP;
+  if (hipEventCreateWithFlags(&ctx->fork_ev, kDeviceEventFlags) != hipSuccess) return NF_E_HIP;
   if (device >= kMaxDevices || scratch_setup(device, &ctx->scratch) != hipSuccess) return NF_E_HIP;
   if (gemm_prepare_kernels() != hipSuccess) return NF_E_HIP;
   *out = ctx.release();
@@ -824,6 +846,7 @@ std::vector<uint64_t> graph_key(const nf_ctx* ctx, const nf_layer_cfg& cfg, cons
       u(((uint64_t)(uint32_t)plan->op_kind[i] << 40) | ((uint64_t)(uint32_t)plan->op_nano[i] << 20) |
         (uint32_t)plan->op_stream[i]);
     u((uint64_t)(uint32_t)plan->decode_max_workgroups);
+    for (int32_t i = 0; plan->op_lane && i < plan->n_ops; ++i) u((uint64_t)(uint32_t)plan->op_lane[i]);
   } else {
     u(~0ull);
   }

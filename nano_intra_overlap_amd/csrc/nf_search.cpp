@@ -20,6 +20,12 @@
 // The compute rate, and the memory op's rate beside it, may be given per compute kind (KQV,
 // O, UGD measured each against the memory op): on a shared GPU a short product beside
 // decode attention waits for CU slots far longer than the long FFN product does.
+// Resource share per compute kind: the memory class keeps one CU mask (share R, over the
+// table's grid), and each compute kind (KQV, O, UGD) takes either the complement of that
+// mask or the whole GPU beside it (the table's "gemm_full" entry of the same R), so the
+// kinds can hold different shares (the pages' per-operation R). Mixed choices need three
+// streams (masked compute, memory, unmasked compute); the compute ops stay one lane that
+// runs one op at a time in the listed order.
 // Extension: the K best Stage-I structures and the single-stream sequential plan are all
 // re-ranked under interference, since on this GPU interference can reverse Stage I's order;
 // an overlapped plan is taken only when predicted faster than the sequential one by more
@@ -66,9 +72,26 @@ struct InterfCfg {
   double pg_both_k[NF_OP_KINDS] = {1, 1, 1, 1, 1}, pg_alone_k[NF_OP_KINDS] = {1, 1, 1, 1, 1};
   double pm_both_k[NF_OP_KINDS] = {1, 1, 1, 1, 1};
   bool has_masks = false;
+  bool gemm_full = false;  // compute op unmasked beside a masked memory op
   uint32_t masks[2][NF_CU_MASK_WORDS];
   int decode_grid = 0;
 };
+
+// Stage II's placement of compute kinds: kinds in full_kinds run as in `full` (unmasked
+// beside the memory mask), the others on the complement mask of the configuration.
+struct Placement {
+  const InterfCfg* full = nullptr;
+  unsigned full_kinds = 0;  // bit k: kind k on the unmasked stream
+};
+
+const int kComputeKinds[3] = {NF_OP_KQV, NF_OP_O, NF_OP_UGD};
+
+unsigned placement_kinds(unsigned choice) {  // bit i of choice: kComputeKinds[i] unmasked
+  unsigned m = 0;
+  for (int i = 0; i < 3; ++i)
+    if (choice >> i & 1u) m |= 1u << kComputeKinds[i];
+  return m;
+}
 
 const char* kKindNames[NF_OP_KINDS] = {"KQV", "DECATTN", "PFATTN", "O", "UGD"};
 
@@ -143,6 +166,7 @@ bool load_interference(const char* path, std::vector<InterfCfg>& out, double& mi
       }
     }
     c.decode_grid = (int)e.number("decode_grid", 0.0);
+    c.gemm_full = e.at("gemm_full").kind == json::Value::Bool && e.at("gemm_full").b;
     const json::Value& m = e.at("cu_masks");
     if (m.is_arr() && m.arr.size() == 2) {
       c.has_masks = true;
@@ -197,7 +221,8 @@ std::vector<double> op_durations(const BatchLayout& L, const PlanGraph& g, const
 
 // Event-driven simulation of two (or one) in-order streams with dependency waits. The rate
 // of a running op depends on whether an op of the other stream runs at the same time.
-SimResult simulate(const Structure& S, const PlanGraph& g, const std::vector<double>& dur, const InterfCfg& c) {
+SimResult simulate(const Structure& S, const PlanGraph& g, const std::vector<double>& dur, const InterfCfg& c,
+                   const Placement* pl = nullptr) {
   const int n = g.n_nano;
   const int n_ops = NF_OP_KINDS * n;
   SimResult R;
@@ -251,18 +276,25 @@ SimResult simulate(const Structure& S, const PlanGraph& g, const std::vector<dou
       if (all) break;
       return R;  // deadlock: a head op waits for an op that can never run
     }
-    // rates
+    // rates; a compute op placed on the unmasked stream takes the "full" entry's speeds, and
+    // so does the memory op beside it
+    auto cfg_of = [&](int id) -> const InterfCfg& {
+      return (pl && pl->full && (pl->full_kinds >> (id / n) & 1u)) ? *pl->full : c;
+    };
     std::vector<double> rate(ns, 1.0);
     for (int s = 0; s < ns; ++s) {
       if (cur[s] < 0) continue;
       const bool is_compute = (s == 0) == compute_is_stream0;
       const bool other = active > 1;
-      if (ns == 1)
+      if (ns == 1) {
         rate[s] = 1.0;
-      else if (is_compute)
-        rate[s] = other ? c.pg_both_k[cur[s] / n] : c.pg_alone_k[cur[s] / n];
-      else
-        rate[s] = other ? c.pm_both_k[cur[compute_is_stream0 ? 0 : 1] / n] : c.pm_alone;
+      } else if (is_compute) {
+        const InterfCfg& cc = cfg_of(cur[s]);
+        rate[s] = other ? cc.pg_both_k[cur[s] / n] : cc.pg_alone_k[cur[s] / n];
+      } else {
+        const int g_op = cur[compute_is_stream0 ? 0 : 1];
+        rate[s] = other ? cfg_of(g_op).pm_both_k[g_op / n] : c.pm_alone;
+      }
     }
     // next completion
     double dt = 1e300;
@@ -454,8 +486,16 @@ extern "C" nf_status nf_plan_search(const char* dbest_json, const char* rp_json,
     seq.stage1 = simulate(seq.S, g, op_durations(L, g, P), ideal).makespan;
   }
   pool.push_back(seq);
+  // the unmasked-compute partner of a masked entry: the "gemm_full" entry of the same R
+  auto partner = [&](size_t k) -> const InterfCfg* {
+    if (!cfgs[k].has_masks || cfgs[k].gemm_full) return nullptr;
+    for (auto& f : cfgs)
+      if (f.gemm_full && f.has_masks && std::fabs(f.r - cfgs[k].r) < 1e-6) return &f;
+    return nullptr;
+  };
   double best_ms = 1e300;
   int best_c = -1, best_k = -1;
+  unsigned best_choice = 0;  // bit i: kComputeKinds[i] on the unmasked stream
   std::vector<double> best_start;
   for (size_t ci = 0; ci < pool.size(); ++ci) {
     PlanGraph g;
@@ -463,13 +503,20 @@ extern "C" nf_status nf_plan_search(const char* dbest_json, const char* rp_json,
     const std::vector<double> dur = op_durations(L, g, P);
     for (size_t k = 0; k < cfgs.size(); ++k) {
       if (pool[ci].S.sequential && k > 0) break;  // one stream: no interference, full GPU
-      SimResult r = simulate(pool[ci].S, g, dur, pool[ci].S.sequential ? ideal : cfgs[k]);
-      if (!r.ok) continue;
-      if (r.makespan < best_ms - 1e-12) {
-        best_ms = r.makespan;
-        best_c = (int)ci;
-        best_k = pool[ci].S.sequential ? -1 : (int)k;
-        best_start = r.start;
+      // every kind on the complement mask (choice 0); with a partner entry also the mixed
+      // choices (all kinds unmasked is the partner entry itself)
+      const InterfCfg* full = pool[ci].S.sequential ? nullptr : partner(k);
+      for (unsigned choice = 0; choice < (full ? 7u : 1u); ++choice) {
+        const Placement pl{full, placement_kinds(choice)};
+        SimResult r = simulate(pool[ci].S, g, dur, pool[ci].S.sequential ? ideal : cfgs[k], &pl);
+        if (!r.ok) continue;
+        if (r.makespan < best_ms - 1e-12) {
+          best_ms = r.makespan;
+          best_c = (int)ci;
+          best_k = pool[ci].S.sequential ? -1 : (int)k;
+          best_choice = choice;
+          best_start = r.start;
+        }
       }
     }
   }
@@ -484,6 +531,7 @@ extern "C" nf_status nf_plan_search(const char* dbest_json, const char* rp_json,
       best_ms = r.makespan;
       best_c = seq_c;
       best_k = -1;
+      best_choice = 0;
       best_start = r.start;
     }
   }
@@ -505,13 +553,20 @@ extern "C" nf_status nf_plan_search(const char* dbest_json, const char* rp_json,
     if (a.s != b.s) return a.s < b.s;
     return a.p < b.p;
   });
+  // streams: lane 0 (compute) and lane 1 (memory) as in the structure; a mixed placement
+  // adds stream 2, unmasked, for the compute kinds placed there (still lane 0)
+  const unsigned full_kinds = placement_kinds(best_choice);
+  const bool mixed = best_choice != 0;
+  auto stream_of = [&](const Item& it) {
+    return (mixed && it.s == 0 && (full_kinds >> it.kind & 1u)) ? 2 : it.s;
+  };
   std::ostringstream o;
   o << "{\"bounds\": [";
   for (size_t i = 0; i < win.S.bounds.size(); ++i) o << (i ? ", " : "") << win.S.bounds[i];
-  o << "], \"n_streams\": " << win.S.streams.size() << ", \"ops\": [";
+  o << "], \"n_streams\": " << win.S.streams.size() + (mixed ? 1 : 0) << ", \"ops\": [";
   for (size_t i = 0; i < items.size(); ++i)
     o << (i ? ", " : "") << "{\"kind\": " << items[i].kind << ", \"nano\": " << items[i].nano
-      << ", \"stream\": " << items[i].s << "}";
+      << ", \"stream\": " << stream_of(items[i]) << ", \"lane\": " << items[i].s << "}";
   o << "], \"cu_masks\": ";
   if (best_k >= 0 && cfgs[best_k].has_masks) {
     o << "[";
@@ -520,12 +575,31 @@ extern "C" nf_status nf_plan_search(const char* dbest_json, const char* rp_json,
       for (int w = 0; w < NF_CU_MASK_WORDS; ++w) o << (w ? ", " : "") << cfgs[best_k].masks[s][w];
       o << "]";
     }
+    if (mixed) {
+      o << ", [";
+      for (int w = 0; w < NF_CU_MASK_WORDS; ++w) o << (w ? ", " : "") << 0xFFFFFFFFu;
+      o << "]";
+    }
     o << "]";
   } else {
     o << "null";
   }
+  std::string cfg_name = best_k >= 0 ? cfgs[best_k].name : "sequential";
+  if (mixed) {
+    cfg_name += " + unmasked";
+    for (int i = 0; i < 3; ++i)
+      if (best_choice >> i & 1u) cfg_name += std::string(" ") + kKindNames[kComputeKinds[i]];
+  }
   o << ", \"decode_grid\": " << (best_k >= 0 ? cfgs[best_k].decode_grid : 0);
-  o << ", \"interference_config\": " << json::quote(best_k >= 0 ? cfgs[best_k].name : "sequential");
+  o << ", \"interference_config\": " << json::quote(cfg_name);
+  o << ", \"r_mem\": " << json::num(best_k >= 0 ? cfgs[best_k].r : -1.0);
+  o << ", \"unmasked_kinds\": [";
+  for (int i = 0, first = 1; i < 3; ++i)
+    if (best_choice >> i & 1u) {
+      o << (first ? "" : ", ") << json::quote(kKindNames[kComputeKinds[i]]);
+      first = 0;
+    }
+  o << "]";
   o << ", \"predicted_ms\": " << json::num(best_ms);
   o << ", \"sequential_ms\": " << json::num(seq.stage1);
   o << ", \"lookahead\": " << win.S.lookahead << ", \"prefill_on_memory_stream\": "
@@ -536,7 +610,7 @@ extern "C" nf_status nf_plan_search(const char* dbest_json, const char* rp_json,
   o << "], \"best_lookahead\": " << best1.S.lookahead << "}";
   std::ostringstream sm;
   sm << (win.S.sequential ? "sequential" : "overlap") << ", " << n << " nano-batch(es), predicted "
-     << json::num(best_ms) << " ms (" << (best_k >= 0 ? cfgs[best_k].name : "one stream") << ")";
+     << json::num(best_ms) << " ms (" << (best_k >= 0 ? cfg_name : std::string("one stream")) << ")";
   o << ", \"summary\": " << json::quote(sm.str()) << "}";
   const std::string out = o.str();
   if (out.size() + 1 > cap) {

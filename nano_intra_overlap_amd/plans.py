@@ -67,15 +67,20 @@ def sequential(batch: abi.HostBatch, bounds) -> HostPlan:
 
 
 def overlap(batch: abi.HostBatch, bounds, compute_mask=None, memory_mask=None,
-            prefill_on_memory: bool = True) -> HostPlan:
+            prefill_on_memory: bool = True, unmasked_kinds=()) -> HostPlan:
     """Two streams (0 compute, 1 memory): KQV of every nano-batch first on the compute
     stream, then O and Up/Gate/Down per nano-batch; decode attention per nano-batch on
-    the memory stream (prefill attention there too unless prefill_on_memory is False)."""
+    the memory stream (prefill attention there too unless prefill_on_memory is False).
+
+    unmasked_kinds: dense kinds (NF_OP_KQV, NF_OP_O, NF_OP_UGD) that run on a third,
+    unmasked stream beside the memory stream's mask instead of on the compute mask; the
+    dense ops stay one lane (one at a time, in order) across the two compute streams."""
+    third = bool(unmasked_kinds)
 
     def stream_of(k, j):
         if k == NF_OP_DECATTN or (k == NF_OP_PFATTN and prefill_on_memory):
             return 1
-        return 0
+        return 2 if k in unmasked_kinds else 0
 
     def rank(k, j):
         if k == NF_OP_KQV:
@@ -85,15 +90,20 @@ def overlap(batch: abi.HostBatch, bounds, compute_mask=None, memory_mask=None,
         return (2, j, k)
 
     masks = None
+    full = [0xFFFFFFFF] * abi.NF_CU_MASK_WORDS
     if compute_mask is not None or memory_mask is not None:
-        full = [0xFFFFFFFF] * abi.NF_CU_MASK_WORDS
-        masks = [compute_mask or full, memory_mask or full]
-    return schedule(batch, bounds, stream_of, rank, 2, masks)
+        masks = [compute_mask or full, memory_mask or full] + ([full] if third else [])
+    plan = schedule(batch, bounds, stream_of, rank, 3 if third else 2, masks)
+    if not third:
+        return plan
+    lanes = [1 if s == 1 else 0 for s in plan.stream.tolist()]
+    return HostPlan(bounds, plan.ops, 3, masks, 0, lanes)
 
 
 def from_json(text: str) -> tuple[HostPlan, dict]:
     """Parse a plan written by nf_plan_search (returns the plan and the whole record)."""
     rec = json.loads(text)
     ops = [(o["kind"], o["nano"], o["stream"]) for o in rec["ops"]]
+    lanes = [o["lane"] for o in rec["ops"]] if all("lane" in o for o in rec["ops"]) else None
     masks = rec.get("cu_masks")
-    return HostPlan(rec["bounds"], ops, rec["n_streams"], masks, rec.get("decode_grid", 0)), rec
+    return HostPlan(rec["bounds"], ops, rec["n_streams"], masks, rec.get("decode_grid", 0), lanes), rec

@@ -111,7 +111,7 @@ def durations(batch, bounds, table):
     return out
 
 
-def simulate(streams, deps, dur, speeds=None):
+def simulate(streams, deps, dur, speeds=None, full=None, full_kinds=()):
     """Makespan of in-order streams (lists of (kind, nano)) with dependency waits.
 
     speeds: None (every op at full speed) or a dict with p_gemm_both, p_mem_both,
@@ -122,6 +122,11 @@ def simulate(streams, deps, dur, speeds=None):
     uses the plain speed). Stream 0 is the compute stream. Returns None on
     deadlock. Time advances from one completion to the next; a running op progresses at its
     speed.
+
+    full, full_kinds: a second speed dict and the compute kinds that take it (the pages'
+    per-operation resource share: those kinds run with their own share, here the whole
+    GPU beside the memory op's mask); while such a kind runs, the memory op's speed beside
+    it comes from `full` too. The memory op alone keeps `speeds`.
     """
     pos = [0] * len(streams)
     cur = [None] * len(streams)
@@ -156,8 +161,13 @@ def simulate(streams, deps, dur, speeds=None):
             else:
                 both = len(running) > 1
                 key = ("p_gemm_" if s == 0 else "p_mem_") + ("both" if both else "alone")
-                rate[s] = speeds[key]
-                per_kind = speeds.get(key + "_kind") or {}
+                # the compute op's own placement decides its speeds, and the memory op's
+                # beside it; the memory op alone runs at the plain entry's speed
+                sp = speeds
+                if full is not None and cur[0] is not None and cur[0][0] in full_kinds and (s == 0 or both):
+                    sp = full
+                rate[s] = sp[key]
+                per_kind = sp.get(key + "_kind") or {}
                 # the compute stream's own kind; the memory stream's speed beside it is keyed
                 # by the kind of the compute op running next to it
                 name = KIND_NAMES[cur[s][0]] if s == 0 else (KIND_NAMES[cur[0][0]] if both else None)
@@ -199,12 +209,39 @@ def all_bounds(T, n, gran):
         yield [0, *c, T]
 
 
+def _partner(c, configs):
+    """The entry measured with the compute op unmasked beside the same memory mask as the
+    masked entry c (same r_mem, "gemm_full" true), or None."""
+    if c is None or c.get("gemm_full") or c.get("cu_masks") is None:
+        return None
+    for f in configs:
+        if f.get("gemm_full") and f.get("cu_masks") is not None and abs(f.get("r_mem", -1) - c.get("r_mem", -1)) < 1e-6:
+            return f
+    return None
+
+
+def placements(c, configs):
+    """Stage II's per-kind choices for entry c: (full entry, kinds placed unmasked). Every
+    compute kind on the complement mask, and with a partner entry each mixed subset of
+    {KQV, O, UGD} (all three unmasked is the partner entry itself, searched on its own)."""
+    out = [(None, ())]
+    f = _partner(c, configs)
+    if f is not None:
+        import itertools
+
+        for n in (1, 2):
+            for kinds in itertools.combinations((KQV, O, UGD), n):
+                out.append((f, kinds))
+    return out
+
+
 def search(batch, table, configs=None, max_nano=4, gran=128, top_k=8, min_gain=0.0):
     """Brute force over the same space as the library: Stage I by exhaustive enumeration,
-    Stage II over the interference configurations for the K best structures and the
-    sequential single-stream plan; an overlapped plan wins only when it beats the
-    sequential one by more than the fraction min_gain. Returns (best makespan, stage-I best
-    makespan)."""
+    Stage II over the interference configurations (and, per masked configuration, every
+    placement of the compute kinds on its complement mask or the whole GPU) for the K best
+    structures and the sequential single-stream plan; an overlapped plan wins only when it
+    beats the sequential one by more than the fraction min_gain. Returns (best makespan,
+    stage-I best makespan)."""
     T = sum(e - s for s, e, _ in _requests(batch))
     cands = []
     for n in range(1, max_nano + 1):
@@ -230,9 +267,10 @@ def search(batch, table, configs=None, max_nano=4, gran=128, top_k=8, min_gain=0
     best = seq
     for ms, n, bounds, st, deps, dur in cands[:top_k]:
         for c in (configs or [None]):
-            r = simulate(st, deps, dur, c)
-            if r is not None and r < best:
-                best = r
+            for f, kinds in placements(c, configs or []):
+                r = simulate(st, deps, dur, c, f, kinds)
+                if r is not None and r < best:
+                    best = r
     if best > seq * (1.0 - min_gain):
         best = seq
     return best, stage1

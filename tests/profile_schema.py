@@ -45,9 +45,17 @@ def check_interference(r: dict, r_grid=None):
     assert r["t_gemm_best_ms"] > 0 and r["t_mem_best_ms"] > 0
     names = [c["name"] for c in r["configs"]]
     assert "shared" in names, names
-    masked = [c for c in r["configs"] if c["name"].startswith("mask_r")]
+    masked = [c for c in r["configs"] if c["name"].startswith("mask_r") and not c.get("gemm_full")]
+    full = [c for c in r["configs"] if c.get("gemm_full")]
     if r_grid is not None:
         assert sorted(round(c["r_mem"], 6) for c in masked) == sorted(round(x, 6) for x in r_grid)
+    # a table with unmasked-compute entries has one per masked entry, same memory mask
+    if full:
+        assert sorted(round(c["r_mem"], 6) for c in full) == sorted(round(c["r_mem"], 6) for c in masked)
+        by_r = {round(c["r_mem"], 6): c for c in masked}
+        for c in full:
+            assert c["cu_masks"][1] == by_r[round(c["r_mem"], 6)]["cu_masks"][1], c["name"]
+            assert all(w == 0xFFFFFFFF for w in c["cu_masks"][0]), c["name"]
     for c in r["configs"]:
         ps = [c["p_gemm_both"], c["p_mem_both"], c["p_gemm_alone"], c["p_mem_alone"]]
         for key in ("p_gemm_both_kind", "p_mem_both_kind", "p_gemm_alone_kind"):
@@ -57,9 +65,11 @@ def check_interference(r: dict, r_grid=None):
         if c["name"].startswith("mask_r"):
             assert 0 < c["r_mem"] < 1
             assert c["cu_masks"] is not None and len(c["cu_masks"]) == 2
-            # the two streams' CU masks are disjoint and leave no XCD without CUs
+            # the two streams' CU masks are disjoint (the compute one is the whole GPU in a
+            # "gemm_full" entry) and leave no XCD without CUs
             g, m = c["cu_masks"]
-            assert all((a & b) == 0 for a, b in zip(g, m)), c["name"]
+            if not c.get("gemm_full"):
+                assert all((a & b) == 0 for a, b in zip(g, m)), c["name"]
             for mask in (g, m):
                 per = [0] * 8
                 for i in range(32 * len(mask)):

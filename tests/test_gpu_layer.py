@@ -102,6 +102,10 @@ def _plans(hb, T):
     yield "overlap2_masked", plans.overlap(hb, [0, 39, T], abi.cu_mask(per_xcd=24, offset=0),
                                            abi.cu_mask(per_xcd=8, offset=24))
     yield "overlap4_pf_compute", plans.overlap(hb, [0, 10, 20, 50, T], prefill_on_memory=False)
+    # per-kind shares: Up/Gate/Down on an unmasked third stream, KQV and O on the compute
+    # mask, one compute lane across the two
+    yield "overlap3_lanes", plans.overlap(hb, [0, 20, 39, T], abi.cu_mask(per_xcd=20, offset=0),
+                                          abi.cu_mask(per_xcd=12, offset=20), unmasked_kinds=(abi.NF_OP_UGD,))
 
 
 @pytest.mark.parametrize("seed", [0, 1])

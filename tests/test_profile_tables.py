@@ -35,7 +35,7 @@ def test_committed_interference_tables(path):
     with open(path) as f:
         r = json.load(f)
     assert r["cfg"]["hidden"] == wl.shape.hidden
-    check_interference(r, r_grid=[0.25, 0.375, 0.5, 0.625, 0.75])
+    check_interference(r, r_grid=[0.125, 0.25, 0.375, 0.5, 0.625, 0.75, 0.875])
     assert 0 <= r["min_gain"] < 1
 
 

@@ -149,6 +149,104 @@ def test_search_per_kind_compute_interference(abi, tmp_path):
     assert got["kinds"] > got["plain"]
 
 
+def _masks(r):
+    per = round(32 * r)
+    mem = [0] * 8
+    gem = [0] * 8
+    for i in range(256):
+        (mem if i // 8 >= 32 - per else gem)[i // 32] |= 1 << (i % 32)
+    return gem, mem
+
+
+def _per_kind_table(r, kqv_full, o_full, ugd_full, masked_kqv=0.95, masked_ugd=0.6):
+    """A masked entry and its unmasked-compute partner at memory share r."""
+    gem, mem = _masks(r)
+    masked = {"name": f"mask_r{r}", "r_mem": r, "p_gemm_both": masked_ugd, "p_mem_both": 0.55,
+              "p_gemm_alone": 0.7, "p_mem_alone": 0.85,
+              "p_gemm_both_kind": {"KQV": masked_kqv, "O": 0.6, "UGD": masked_ugd},
+              "p_gemm_alone_kind": {"KQV": 1.0, "O": 0.65, "UGD": 0.7},
+              "p_mem_both_kind": {"KQV": 0.75, "O": 0.6, "UGD": 0.45}, "cu_masks": [gem, mem]}
+    full = {"name": f"mask_r{r}_gemm_full", "r_mem": r, "gemm_full": True, "p_gemm_both": ugd_full,
+            "p_mem_both": 0.35, "p_gemm_alone": 1.0, "p_mem_alone": 0.85,
+            "p_gemm_both_kind": {"KQV": kqv_full, "O": o_full, "UGD": ugd_full},
+            "p_gemm_alone_kind": {"KQV": 1.0, "O": 1.0, "UGD": 1.0},
+            "p_mem_both_kind": {"KQV": 0.3, "O": 0.33, "UGD": 0.6}, "cu_masks": [[0xFFFFFFFF] * 8, mem]}
+    return [masked, full]
+
+
+def _speeds(c):
+    out = {k: c.get(k, 1.0) for k in ("p_gemm_both", "p_mem_both", "p_gemm_alone", "p_mem_alone")}
+    out.update({k: c[k] for k in ("p_gemm_both_kind", "p_gemm_alone_kind", "p_mem_both_kind", "r_mem",
+                                   "gemm_full", "cu_masks") if k in c})
+    return out
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_search_per_kind_resource_share(abi, tmp_path, seed):
+    """Stage II gives each compute kind its own share: the complement of the memory mask or
+    the whole GPU beside it. The library and the brute-force search agree on the best
+    makespan; a table where KQV keeps its speed on the complement mask but the FFN product
+    needs the whole GPU yields a three-stream plan with the compute ops on one lane."""
+    rng = np.random.default_rng(40 + seed)
+    b = _batch(rng)
+    table = _table(rng)
+    configs = _per_kind_table(0.375, kqv_full=0.3, o_full=0.5, ugd_full=0.95, masked_kqv=1.0, masked_ugd=0.5) + \
+        _per_kind_table(0.25, kqv_full=0.35, o_full=0.4, ugd_full=0.9, masked_kqv=0.95, masked_ugd=0.55)
+    dpath = _write(tmp_path, "dbest.json", {"ops": table})
+    rpath = _write(tmp_path, "rp.json", {"configs": configs})
+    hb = abi.HostBatch.from_batch(b)
+    plan = json.loads(abi.nf_plan_search(dpath, rpath, hb, max_nano=4, granularity=128))
+    best, _ = osch.search(b, table, [_speeds(c) for c in configs], max_nano=4, gran=128, top_k=8)
+    assert plan["predicted_ms"] == pytest.approx(best, rel=1e-6)
+    # the same tables without the partner entries: never better
+    only_masked = [c for c in configs if not c.get("gemm_full")]
+    best_masked, _ = osch.search(b, table, [_speeds(c) for c in only_masked], max_nano=4, gran=128, top_k=8)
+    assert best <= best_masked + 1e-12
+    assert plan["n_streams"] == 3 and plan["unmasked_kinds"] and len(plan["cu_masks"]) == 3
+    lanes = {(o["kind"], o["nano"]): (o["stream"], o["lane"]) for o in plan["ops"]}
+    compute = [v for (k, _), v in lanes.items() if k in (osch.KQV, osch.O, osch.UGD)]
+    assert {ln for _, ln in compute} == {0} and {st for st, _ in compute} == {0, 2}
+    for (k, _), (st, ln) in lanes.items():
+        full = osch.KIND_NAMES[k] in plan["unmasked_kinds"]
+        if k in (osch.KQV, osch.O, osch.UGD):
+            assert st == (2 if full else 0)
+    from nano_intra_overlap_amd import plans
+
+    hp, _ = plans.from_json(json.dumps(plan))
+    edges, order = abi.nf_plan_dependencies(hb, hp)
+    # the compute lane runs one op at a time: consecutive lane ops on different streams
+    # are joined by an edge
+    listed = [(o["kind"], o["nano"], o["stream"], o["lane"]) for o in plan["ops"]]
+    lane0 = [i for i, o in enumerate(listed) if o[3] == 0]
+    for a, c in zip(lane0, lane0[1:]):
+        if listed[a][2] != listed[c][2]:
+            assert (a, c) in edges
+
+
+def test_lane_edges_in_plan_graph(abi):
+    """op_lane: consecutive ops of one lane on different streams get an ordering edge; on
+    the same stream they need none; without lanes nothing is added; a lane out of range is
+    refused."""
+    b = sw.batch_from_lengths(np.full(256, 300), [], seed=0)
+    hb = abi.HostBatch.from_batch(b)
+    K, D, P, O, U = osch.KQV, osch.DECATTN, osch.PFATTN, osch.O, osch.UGD
+    bounds = [0, 128, 256]
+    ops = [(K, 0, 0), (D, 0, 1), (P, 0, 1), (K, 1, 2), (D, 1, 1), (P, 1, 1), (O, 0, 0), (U, 0, 2),
+           (O, 1, 0), (U, 1, 0)]
+    lanes = [0, 1, 1, 0, 1, 1, 0, 0, 0, 0]
+    plain, _ = abi.nf_plan_dependencies(hb, abi.HostPlan(bounds, ops, 3))
+    laned, order = abi.nf_plan_dependencies(hb, abi.HostPlan(bounds, ops, 3, lanes=lanes))
+    added = set(laned) - set(plain)
+    # lane 0 in listed order: 0(s0) 3(s2) 6(s0) 7(s2) 8(s0) 9(s0)
+    assert added == {(0, 3), (3, 6), (6, 7), (7, 8)} - set(plain)
+    assert set(plain) <= set(laned)
+    pos = {op: i for i, op in enumerate(order)}
+    for i, j in laned:
+        assert pos[i] < pos[j]
+    with pytest.raises(abi.NanoflowError):
+        abi.nf_plan_dependencies(hb, abi.HostPlan(bounds, ops, 3, lanes=[0] * 9 + [3]))
+
+
 @pytest.mark.parametrize("min_gain", [0.0, 0.05, 0.3])
 def test_search_min_gain(abi, tmp_path, min_gain):
     """The table's min_gain: an overlapped plan is taken only when predicted faster than the
@@ -163,7 +261,7 @@ def test_search_min_gain(abi, tmp_path, min_gain):
     speeds = {k: cfg.get(k, 1.0) for k in ("p_gemm_both", "p_mem_both", "p_gemm_alone", "p_mem_alone")}
     best, _ = osch.search(b, table, [speeds], max_nano=4, gran=128, top_k=8, min_gain=min_gain)
     assert plan["predicted_ms"] == pytest.approx(best, rel=1e-6)
-    overlapped = plan["n_streams"] == 2
+    overlapped = plan["n_streams"] >= 2
     assert overlapped == (best < plan["sequential_ms"] * (1 - min_gain))
     if overlapped:
         assert plan["predicted_ms"] < plan["sequential_ms"] * (1 - min_gain)
