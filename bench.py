@@ -60,8 +60,9 @@ def parse():
                    help="decode split-KV chunk in KV blocks (0 = the library's choice per nano-op)")
     p.add_argument("--prefill-chunk", type=int, default=0,
                    help="prefill attention keys per work item (0 = the library's choice)")
-    p.add_argument("--decode-nbuf", type=int, default=1, choices=[1, 2], help="KV blocks per softmax step")
-    p.add_argument("--decode-ring", type=int, default=2, choices=[2, 3, 4],
+    p.add_argument("--decode-nbuf", type=int, default=0, choices=[0, 1, 2],
+                   help="KV blocks per softmax step (0 with --decode-ring 0: chosen per launch)")
+    p.add_argument("--decode-ring", type=int, default=0, choices=[0, 2, 3, 4],
                    help="decode attention register ring depth (ring - 1 groups of KV blocks in flight)")
     p.add_argument("--gemm-variant", type=int, default=-1, help="force one GEMM tile variant for every GEMM")
     p.add_argument("--gemm-variants", default="",

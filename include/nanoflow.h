@@ -198,8 +198,9 @@ nf_status nf_ctx_set_prefill_chunk(nf_ctx *ctx, int32_t keys);
 /* Decode-attention launch: max_workgroups caps its grid (0 = one workgroup per four work
  * units; a smaller grid makes the kernel persistent, each wave looping over units), nbuf KV
  * blocks per online-softmax step and ring register buffers of nbuf blocks (ring - 1 steps in
- * flight). Supported (nbuf, ring): (1, 2..4), (2, 2..3); default (1, 2).
- * Errors: NF_E_ARG.                                                                          */
+ * flight). Supported (nbuf, ring): (0, 0) = chosen per launch (the default: (1, 2), or (2, 2)
+ * when the launch has fewer waves than one round of (1, 2)'s wave slots), (1, 2..4),
+ * (2, 2..3). Errors: NF_E_ARG.                                                               */
 nf_status nf_ctx_set_decode_launch(nf_ctx *ctx, int32_t max_workgroups, int32_t nbuf, int32_t ring);
 /* GEMM tile configuration of a dense op kind (NF_OP_KQV, NF_OP_O, NF_OP_UGD): which = 0 its
  * GEMM (Up/Gate for UGD), 1 the Down GEMM of UGD; variant -1 restores the library choice,

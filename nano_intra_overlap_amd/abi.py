@@ -496,9 +496,10 @@ def nf_ctx_set_prefill_chunk(ctx, keys: int) -> None:
     _check(load().nf_ctx_set_prefill_chunk(ctx, keys), ctx)
 
 
-def nf_ctx_set_decode_launch(ctx, max_workgroups: int, nbuf: int = 1, ring: int = 2) -> None:
+def nf_ctx_set_decode_launch(ctx, max_workgroups: int, nbuf: int = 0, ring: int = 0) -> None:
     """Decode attention launch: workgroup cap (0 = one wave per unit), KV blocks per softmax
-    step, and ring depth (register buffers of nbuf blocks; ring - 1 groups in flight)."""
+    step, and ring depth (register buffers of nbuf blocks; ring - 1 groups in flight);
+    nbuf = ring = 0 lets each launch choose from its work (the default)."""
     _check(load().nf_ctx_set_decode_launch(ctx, max_workgroups, nbuf, ring), ctx)
 
 

@@ -331,11 +331,25 @@ static hipError_t launch_decode_d(int nb, int ring, int grid, hipStream_t s, con
 }
 
 bool decode_config_supported(int nb, int ring) {
-  return (nb == 1 && ring >= 2 && ring <= 4) || (nb == 2 && (ring == 2 || ring == 3));
+  return (nb == 0 && ring == 0) || (nb == 1 && ring >= 2 && ring <= 4) || (nb == 2 && (ring == 2 || ring == 3));
 }
 
-// nb: KV blocks per softmax step; ring: register buffers of nb blocks (ring - 1 groups in
-// flight); max_grid: workgroup cap (0 = one wave per unit)
+// The automatic launch shape (nb = 0): the default kernel (1 block per step, ring of 2) holds
+// 3 waves per SIMD. Work of fewer waves than one round of those slots (a KV head per GPU
+// with long contexts: a few thousand units) leaves most slots empty, so each wave then
+// streams 2 blocks per step instead (2 waves per SIMD, twice the bytes in flight per wave);
+// measured in the 70B tensor-parallel share's layer: 316 -> 303 us, while the 8B layer's
+// 12.8k units keep the default (1229 against 1240 us).
+static void decode_auto_config(int waves, int& nb, int& ring) {
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  nb = waves < n_cu * 4 * 3 ? 2 : 1;
+  ring = 2;
+}
+
+// nb: KV blocks per softmax step (0 = chosen from the work, with ring 0); ring: register
+// buffers of nb blocks (ring - 1 groups in flight); max_grid: workgroup cap (0 = one wave
+// per unit)
 hipError_t launch_decode_attn(const bf16* qkv, const bf16* kpool, const bf16* vpool, const int32_t* block_table,
                               int max_blocks, const DecodeItem* items, int n_items, float* part_o, float* part_ml,
                               bf16* out, int n_q, int n_kv, int d, int max_grid, int nb, int ring, hipStream_t s,
@@ -343,6 +357,7 @@ hipError_t launch_decode_attn(const bf16* qkv, const bf16* kpool, const bf16* vp
   if (n_items <= 0) return hipSuccess;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)d);
   const int waves = n_items * n_kv;
+  if (nb == 0) decode_auto_config(waves, nb, ring);
   int grid = (waves + 3) / 4;
   if (max_grid > 0 && grid > max_grid) grid = max_grid;
   if (d == 128)

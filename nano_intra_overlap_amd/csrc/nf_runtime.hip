@@ -114,8 +114,8 @@ struct nf_ctx {
   int decode_split = kDefaultSplit;
   int prefill_chunk = 0;  // prefill keys per work item (0 = chosen per nano-op)
   int decode_grid = 0;  // max workgroups of the decode attention kernel (0 = one wave per work unit)
-  int decode_nbuf = 1;  // KV blocks per online-softmax step
-  int decode_ring = 2;  // register buffers of decode_nbuf blocks; decode_ring - 1 groups in flight
+  int decode_nbuf = 0;  // KV blocks per online-softmax step (0: chosen per launch from its work)
+  int decode_ring = 0;  // register buffers of decode_nbuf blocks; decode_ring - 1 groups in flight
   int gemm_variant[NF_OP_KINDS][2];  // per dense op kind: [0] first GEMM, [1] second (UGD down); -1 = default
   // kernel timing: events recorded around instrumented kernel classes on their own stream
   uint32_t timing_mask = 0;

@@ -46,8 +46,9 @@ LAYER_GEMMS = [(1024, 6144, 4096, 0), (2048, 4096, 4096, 1), (1536, 14336, 4096,
 
 
 def _supported(v, k, epi, bn, ks=1, waves=4, bk=32):
+    # split-K slices are whole slabs (sizes differing by at most one): at least one per slice
     return (not (epi == 2 and (bn < 128 or (bn // (waves // 2)) % 64)) and not (v >= 6 and k % bk)
-            and not (ks > 1 and (epi == 2 or k % (bk * ks))))
+            and not (ks > 1 and (epi == 2 or k // bk < ks)))
 
 
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
@@ -175,7 +176,8 @@ def test_gemm_deep_slabs_bit_identical(ctx, m, n, k, epi):
     assert rel_inf(f64(outs[12]), ref) <= TOL
 
 
-@pytest.mark.parametrize("variant", [-1, 6, 7, 9, 10, 11, 12, 13, 14, 15, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30])
+@pytest.mark.parametrize("variant", [-1, 6, 7, 9, 10, 11, 12, 13, 14, 15, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30,
+                                     31])
 def test_gemm_residual_in_place(ctx, variant):
     from nano_intra_overlap_amd import abi
 
@@ -295,7 +297,8 @@ def test_decode_attention(ctx, n_q, n_kv, d, split):
     assert rel_inf(got, ref) <= TOL
 
 
-@pytest.mark.parametrize("nb,ring,grid", [(1, 2, 0), (1, 3, 0), (1, 4, 0), (2, 2, 0), (2, 3, 0), (1, 2, 64), (2, 2, 37)])
+@pytest.mark.parametrize("nb,ring,grid", [(0, 0, 0), (1, 2, 0), (1, 3, 0), (1, 4, 0), (2, 2, 0), (2, 3, 0), (1, 2, 64),
+                                          (2, 2, 37), (0, 0, 37)])
 @pytest.mark.parametrize("n_q,n_kv,d", [(32, 8, 128), (16, 1, 64)])
 def test_decode_attention_launch_configs(ctx, n_q, n_kv, d, nb, ring, grid):
     """Every supported (blocks per softmax step, ring depth) pair and bounded persistent
@@ -347,7 +350,7 @@ def test_decode_attention_launch_configs(ctx, n_q, n_kv, d, nb, ring, grid):
 def test_decode_launch_rejects_unsupported_configs(ctx):
     from nano_intra_overlap_amd import abi
 
-    for nb, ring in ((1, 1), (1, 5), (2, 4), (3, 2), (4, 2)):
+    for nb, ring in ((1, 1), (1, 5), (2, 4), (3, 2), (4, 2), (0, 2), (1, 0)):
         with pytest.raises(abi.NanoflowError):
             abi.nf_ctx_set_decode_launch(ctx, 0, nb, ring)
 
