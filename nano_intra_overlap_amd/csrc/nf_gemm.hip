@@ -346,9 +346,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
   const int wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-  // split-K: slice blockIdx.y of gridDim.y equal slices of K (EPI_PARTIAL only)
-  const int Ks = K / (int)gridDim.y;
-  const int k_begin = (int)blockIdx.y * Ks;
+  // split-K (EPI_PARTIAL only): slice blockIdx.y of gridDim.y slices of whole BK slabs, their
+  // sizes differing by at most one slab (equal when gridDim.y divides the slab count)
+  const int n_slabs = K / BK;
+  const int s_begin = (int)(((long long)blockIdx.y * n_slabs) / gridDim.y);
+  const int s_end = (int)(((long long)(blockIdx.y + 1) * n_slabs) / gridDim.y);
+  const int k_begin = s_begin * BK;
   // per-thread source rows of the direct loads (fixed across k): chunk c = (i*4 + wave)*64 + lane
   const bf16* a_src[A_LOADS];
   const bf16* b_src[B_LOADS];
@@ -402,7 +405,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = Ks / BK;
+  const int nk = s_end - s_begin;
   // all STAGES slabs in flight from the start; slab kt + STAGES is issued into slab kt's
   // buffer once every wave has read slab kt
 #pragma unroll
@@ -638,6 +641,10 @@ static const GemmVariant kVariants[] = {
     {128, 128, 64, 1, 4, 4},  // 28: 4 slabs of 128x128 (128 KB)
     {128, 256, 64, 1, 3, 4},  // 29: 3 slabs of 128x256 (144 KB)
     {128, 256, 64, 1, 3, 8},  // 30
+    // 256x128, 8 waves, 3 slabs of 64, K split in 3 slices of whole slabs (fp32 partials +
+    // reduce; not SwiGLU): a narrow product with a long k loop (the 70B share's KQV, n = 1280,
+    // k = 8192, at 2048 rows: 80 tiles x 3 = 240 workgroups where 128x128 tiles give 160)
+    {256, 128, 64, 3, 3, 8},  // 31
 };
 constexpr int kBalancedVariant = 19, kBalancedDeepVariant = 26;
 static constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
@@ -650,7 +657,7 @@ bool gemm_variant_supported(int v, int m, int n, int k, int epilogue) {
   const GemmVariant& g = kVariants[v];
   if (epilogue == EPI_SWIGLU && (g.bn < 128 || (g.bn / (g.waves / 2)) % 64 != 0)) return false;
   if (v >= 6 && (k % g.bk != 0)) return false;
-  if (g.ks > 1 && (epilogue == EPI_SWIGLU || k % (g.bk * g.ks) != 0)) return false;
+  if (g.ks > 1 && (epilogue == EPI_SWIGLU || k / g.bk < g.ks)) return false;
   (void)m;
   (void)n;
   return true;
@@ -690,6 +697,12 @@ int gemm_default_variant(int m, int n, int k, int epilogue) {
     // 8 waves and 3 slabs (8B O alone: 68 against 75 us for 256x128); SwiGLU needs 64
     // columns per wave: 4 waves
     if (tiles(256, 128) >= 192) return epilogue == EPI_SWIGLU ? 7 : (deep ? 30 : 18);
+    // a narrow product with a long k loop: 256x128 tiles with K cut into 3 slices of at least
+    // 8 slabs when that gives 192-256 workgroups (the 70B share's KQV, 2048 x 1280 x 8192, in
+    // the layer: 59.6 against 72.3 us with 160 128x128 tiles)
+    if (epilogue != EPI_SWIGLU && deep && 3 * tiles(256, 128) >= 192 && 3 * tiles(256, 128) <= 256 &&
+        k / 64 >= 3 * 8)
+      return 31;
     const int t = tiles(128, 128);
     if (t < 128 && epilogue != EPI_SWIGLU) {
       // half the CUs or fewer busy: K slices of at least 1024 (measured: 2 slices pay off
@@ -940,6 +953,7 @@ hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int
     case 28: return launch_pipe<128, 128, 4, 4, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
     case 29: return launch_pipe<128, 256, 3, 4, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
     case 30: return launch_pipe<128, 256, 3, 8, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 31: return launch_pipe<256, 128, 3, 8, 8>(A, B, C, R, m, n, k, epilogue, 3, ws, s);
   }
   return hipErrorInvalidValue;
 }
