@@ -381,7 +381,7 @@ nf_status nf_op_rmsnorm(nf_ctx *ctx, const void *x, const void *g, void *out, in
 
 /* Rotary embedding of q and k and the paged KV append (slides, "Batch Formation": new
  * tokens' K/V go to their pages; "Inside nano-vLLM", the slot mapping locates each new KV
- * store): q and k of qkv (device [T][(n_q+2n_kv) d], q rotated in place) rotated at the
+ * store): q and k of qkv (device [T][(n_q+2n_kv) d], both rotated in place) rotated at the
  * batch's token positions, then k and v written to each token's slot of the pool
  * (slot = table[r][pos / 16] * 16 + pos % 16). Only those slots change. Errors as the
  * layer call for the batch (NF_E_BLOCK_*, NF_E_SLOT_ALIAS).                                  */

@@ -175,20 +175,50 @@ __device__ __forceinline__ void init_state(AttnState<D>& st) {
   for (int dc = 0; dc < D / 16; ++dc) st.o[dc] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// The request's newest key (sequence position pos) taken from its row of qkv instead of the
+// pool: a virtual block whose key row 0 holds the rotated k and whose value column 0 holds v,
+// every other key masked (and its value zero).
+template <int D>
+__device__ __forceinline__ void attend_new_key(AttnState<D>& st, const bf16x8* qf, const bf16* __restrict__ krow,
+                                               const bf16* __restrict__ vrow, int pos, float scale_log2, int lane) {
+  const int i16 = lane & 15, grp = lane >> 4;
+  KvFrag<D> f[1];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    if (i16 == 0) {
+      f[0].k[c] = *reinterpret_cast<const bf16x8*>(krow + c * 32 + grp * 8);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[0].k[c][j] = (bf16)0.0f;
+    }
+  }
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f[0].v[dc][r] = (bf16)0.0f;
+    if (grp == 0) f[0].v[dc][0] = vrow[dc * 16 + i16];
+  }
+  attend_group<D, 1>(st, f, qf, pos, pos, scale_log2, grp);
+}
+
 // ---------------------------------------------------------------------------------------
 // decode
 // ---------------------------------------------------------------------------------------
 
 // Waves take work units (item, KV head) in strides of the grid's wave count, so a grid
 // smaller than the work keeps a bounded footprint (the memory nano-op's resource share)
-// while each wave streams many blocks.
+// while each wave streams many blocks. With new_from_qkv the newest key of each request
+// (position n_keys - 1) is read from the request's qkv row (rotated k, v), not from the
+// pool: the layer appends the decode tokens' K/V to the pool after this kernel, since a
+// launch that reads pool lines just partially written by the append runs 3-6% slower.
 template <int D, int NB, int R>
 __global__ __launch_bounds__(256) void decode_attn_kernel(const bf16* __restrict__ qkv, const bf16* __restrict__ kpool,
                                                           const bf16* __restrict__ vpool,
                                                           const int32_t* __restrict__ block_table, int max_blocks,
                                                           const DecodeItem* __restrict__ items, int n_items,
                                                           float* __restrict__ part_o, float* __restrict__ part_ml,
-                                                          bf16* __restrict__ out, int n_q, int n_kv, float scale_log2) {
+                                                          bf16* __restrict__ out, int n_q, int n_kv, float scale_log2,
+                                                          int new_from_qkv) {
   const int lane = threadIdx.x & 63;
   const int n_waves = gridDim.x * 4;
   const int G = n_q / n_kv;
@@ -213,8 +243,20 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const bf16* __restrict
     }
     AttnState<D> st;
     init_state<D>(st);
-    attend_range<D, NB, R>(st, qf, block_table + (size_t)it.req * max_blocks, it.blk_begin, it.blk_end, kpool, vpool,
-                          n_kv, g, it.n_keys - 1, it.n_keys, scale_log2, lane);
+    if (new_from_qkv) {
+      const int n_pool = it.n_keys - 1;  // keys already in the pool
+      const int b1 = min(it.blk_end, (n_pool + kBlock - 1) / kBlock);
+      attend_range<D, NB, R>(st, qf, block_table + (size_t)it.req * max_blocks, it.blk_begin, b1, kpool, vpool, n_kv,
+                            g, n_pool - 1, n_pool, scale_log2, lane);
+      if (it.blk_end * kBlock >= it.n_keys) {  // this item holds the request's last block
+        const bf16* row = qkv + (size_t)it.token * width;
+        attend_new_key<D>(st, qf, row + (size_t)(n_q + g) * D, row + (size_t)(n_q + n_kv + g) * D, n_pool, scale_log2,
+                          lane);
+      }
+    } else {
+      attend_range<D, NB, R>(st, qf, block_table + (size_t)it.req * max_blocks, it.blk_begin, it.blk_end, kpool,
+                            vpool, n_kv, g, it.n_keys - 1, it.n_keys, scale_log2, lane);
+    }
     const float l = wave_sum16(st.l);
     if (i16 < G) {
       if (it.part < 0) {
@@ -299,14 +341,14 @@ template <int D, int NB, int R>
 static void launch_decode_t(int grid, hipStream_t s, const bf16* qkv, const bf16* kpool, const bf16* vpool,
                             const int32_t* block_table, int max_blocks, const DecodeItem* items, int n_items,
                             float* part_o, float* part_ml, bf16* out, int n_q, int n_kv, float scale_log2,
-                            hipEvent_t ev_start, hipEvent_t ev_stop) {
+                            int new_from_qkv, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (ev_start)
     hipExtLaunchKernelGGL((decode_attn_kernel<D, NB, R>), dim3(grid), dim3(256), 0, s, ev_start, ev_stop, 0, qkv,
                           kpool, vpool, block_table, max_blocks, items, n_items, part_o, part_ml, out, n_q, n_kv,
-                          scale_log2);
+                          scale_log2, new_from_qkv);
   else
     hipLaunchKernelGGL((decode_attn_kernel<D, NB, R>), dim3(grid), dim3(256), 0, s, qkv, kpool, vpool, block_table,
-                       max_blocks, items, n_items, part_o, part_ml, out, n_q, n_kv, scale_log2);
+                       max_blocks, items, n_items, part_o, part_ml, out, n_q, n_kv, scale_log2, new_from_qkv);
 }
 
 // Supported (blocks per softmax step, ring depth) pairs.
@@ -314,11 +356,12 @@ template <int D>
 static hipError_t launch_decode_d(int nb, int ring, int grid, hipStream_t s, const bf16* qkv, const bf16* kpool,
                                   const bf16* vpool, const int32_t* block_table, int max_blocks,
                                   const DecodeItem* items, int n_items, float* part_o, float* part_ml, bf16* out,
-                                  int n_q, int n_kv, float scale_log2, hipEvent_t ev_start, hipEvent_t ev_stop) {
+                                  int n_q, int n_kv, float scale_log2, int new_from_qkv, hipEvent_t ev_start,
+                                  hipEvent_t ev_stop) {
 #define NF_DECODE_CASE(NB_, R_)                                                                                 \
   if (nb == NB_ && ring == R_) {                                                                                \
     launch_decode_t<D, NB_, R_>(grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o,    \
-                                part_ml, out, n_q, n_kv, scale_log2, ev_start, ev_stop);                        \
+                                part_ml, out, n_q, n_kv, scale_log2, new_from_qkv, ev_start, ev_stop);          \
     return hipGetLastError();                                                                                   \
   }
   NF_DECODE_CASE(1, 2)
@@ -353,7 +396,7 @@ static void decode_auto_config(int waves, int& nb, int& ring) {
 hipError_t launch_decode_attn(const bf16* qkv, const bf16* kpool, const bf16* vpool, const int32_t* block_table,
                               int max_blocks, const DecodeItem* items, int n_items, float* part_o, float* part_ml,
                               bf16* out, int n_q, int n_kv, int d, int max_grid, int nb, int ring, hipStream_t s,
-                              hipEvent_t ev_start, hipEvent_t ev_stop) {
+                              hipEvent_t ev_start, hipEvent_t ev_stop, int new_from_qkv) {
   if (n_items <= 0) return hipSuccess;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)d);
   const int waves = n_items * n_kv;
@@ -362,10 +405,10 @@ hipError_t launch_decode_attn(const bf16* qkv, const bf16* kpool, const bf16* vp
   if (max_grid > 0 && grid > max_grid) grid = max_grid;
   if (d == 128)
     return launch_decode_d<128>(nb, ring, grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o,
-                                part_ml, out, n_q, n_kv, scale_log2, ev_start, ev_stop);
+                                part_ml, out, n_q, n_kv, scale_log2, new_from_qkv, ev_start, ev_stop);
   if (d == 64)
     return launch_decode_d<64>(nb, ring, grid, s, qkv, kpool, vpool, block_table, max_blocks, items, n_items, part_o,
-                               part_ml, out, n_q, n_kv, scale_log2, ev_start, ev_stop);
+                               part_ml, out, n_q, n_kv, scale_log2, new_from_qkv, ev_start, ev_stop);
   return hipErrorInvalidValue;
 }
 

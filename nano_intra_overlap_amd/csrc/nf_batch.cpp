@@ -235,6 +235,7 @@ nf_status build_plan_graph(const BatchLayout& L, const nf_plan* plan, PlanGraph&
       lanes.push_back(lane);
     }
   }
+  while (g.n_dec < (int32_t)L.req.size() && L.req[g.n_dec].decode) ++g.n_dec;
   // nano-batch of a token row
   auto nano_of = [&](int32_t t) {
     return (int32_t)(std::upper_bound(g.bounds.begin(), g.bounds.end(), t) - g.bounds.begin()) - 1;

@@ -106,6 +106,7 @@ struct NanoOp {
 
 struct PlanGraph {
   int32_t n_nano = 1, n_streams = 1;
+  int32_t n_dec = 0;  // decode tokens (= decode requests), rows [0, n_dec) of the batch
   std::vector<int32_t> bounds;
   std::vector<NanoOp> ops;                 // in the plan's listed order
   std::vector<std::vector<int32_t>> deps;  // deps[j] = ops j depends on (range intersection)

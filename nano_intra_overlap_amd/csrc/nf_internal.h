@@ -103,16 +103,23 @@ hipError_t launch_kv_move(bool to_pool, bf16* kpool, bf16* vpool, bf16* stage, c
 hipError_t launch_rmsnorm(const bf16* x, const bf16* g, bf16* out, int m, int n, float eps,
                           hipStream_t s);
 
+// Rotary embedding of q and k (both in place in qkv) and the paged KV append of tokens
+// [max(t_begin, t_defer), t_end); tokens below t_defer are appended later by launch_kv_append.
 hipError_t launch_rope_kv(bf16* qkv, const int32_t* tok_pos, const int32_t* tok_slot,
                           const float* inv_freq, bf16* kpool, bf16* vpool, int t_begin, int t_end,
-                          int n_q, int n_kv, int d, hipStream_t s);
+                          int n_q, int n_kv, int d, hipStream_t s, int t_defer = 0);
+hipError_t launch_kv_append(const bf16* qkv, const int32_t* tok_slot, bf16* kpool, bf16* vpool, int t_begin,
+                            int t_end, int n_q, int n_kv, int d, hipStream_t s);
 
 // ev_start / ev_stop: optional timing events recorded by the dispatch itself (both or none).
+// new_from_qkv: each request's newest key (position n_keys - 1) comes from its qkv row (rotated
+// k, v) instead of the pool, which then need not hold it yet.
 hipError_t launch_decode_attn(const bf16* qkv, const bf16* kpool, const bf16* vpool,
                               const int32_t* block_table, int max_blocks, const DecodeItem* items,
                               int n_items, float* part_o, float* part_ml, bf16* out, int n_q,
                               int n_kv, int d, int max_grid, int nb, int ring, hipStream_t s,
-                              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
+                              int new_from_qkv = 0);
 bool decode_config_supported(int nb, int ring);
 hipError_t launch_decode_combine(const CombineItem* combines, int n_combines, const float* part_o,
                                  const float* part_ml, bf16* out, int n_q, int n_kv, int d,

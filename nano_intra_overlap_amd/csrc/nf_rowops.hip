@@ -85,16 +85,18 @@ hipError_t launch_rmsnorm(const bf16* x, const bf16* g, bf16* out, int m, int n,
 // One workgroup per token. The token's angles pos * inv_freq[i] are evaluated once (d/2
 // sincos, shared through LDS by its n_q + n_kv heads); then each thread rotates 8
 // consecutive pairs (i0..i0+7, i0+d/2..i0+d/2+7) of one head with two 16-byte loads and two
-// 16-byte stores: q in place in qkv, k into the token's slot of the pool (8 consecutive dims
-// lie in one 32-dim column chunk). v is read 16 bytes at a time and stored dim-major, one
-// 2-byte element per dimension row of the block.
+// 16-byte stores: q and k in place in qkv, k also into the token's slot of the pool (8
+// consecutive dims lie in one 32-dim column chunk). v is read 16 bytes at a time and stored
+// dim-major, one 2-byte element per dimension row of the block. Tokens below t_defer keep
+// their K/V out of the pool here (kv_append_kernel stores them later, from qkv).
 __global__ __launch_bounds__(256) void rope_kv_kernel(bf16* __restrict__ qkv, const int32_t* __restrict__ tok_pos,
                                                       const int32_t* __restrict__ tok_slot,
                                                       const float* __restrict__ inv_freq, bf16* __restrict__ kpool,
-                                                      bf16* __restrict__ vpool, int t_begin, int n_q, int n_kv,
-                                                      int d) {
+                                                      bf16* __restrict__ vpool, int t_begin, int t_defer, int n_q,
+                                                      int n_kv, int d) {
   __shared__ float cs_l[128], sn_l[128];  // d / 2 <= 128
   const int t = t_begin + blockIdx.x;
+  const bool append = t >= t_defer;
   const int pos = tok_pos[t];
   const int slot = tok_slot[t];
   const int blk = slot / kBlock, off = slot % kBlock;
@@ -123,10 +125,9 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(bf16* __restrict__ qkv, co
       o1[e] = (bf16)(a * cs - b * sn);
       o2[e] = (bf16)(b * cs + a * sn);
     }
-    if (head < n_q) {
-      *reinterpret_cast<bf16x8*>(hp + i0) = o1;
-      *reinterpret_cast<bf16x8*>(hp + i0 + half) = o2;
-    } else {
+    *reinterpret_cast<bf16x8*>(hp + i0) = o1;
+    *reinterpret_cast<bf16x8*>(hp + i0 + half) = o2;
+    if (head >= n_q && append) {
       // key block layout [d/32][16][32]: dim i of this token at (i / 32, off, i % 32)
       const int g = head - n_q;
       bf16* kb = kpool + ((size_t)blk * n_kv + g) * (kBlock * d) + off * 32;
@@ -134,6 +135,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(bf16* __restrict__ qkv, co
       *reinterpret_cast<bf16x8*>(kb + ((i0 + half) >> 5) * (kBlock * 32) + ((i0 + half) & 31)) = o2;
     }
   }
+  if (!append) return;
   const bf16* vrow = row + (n_q + n_kv) * d;
   for (int c = threadIdx.x; c < n_kv * d / 8; c += 256) {
     const int g = (c * 8) / d, j0 = (c * 8) % d;
@@ -146,10 +148,46 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(bf16* __restrict__ qkv, co
 
 hipError_t launch_rope_kv(bf16* qkv, const int32_t* tok_pos, const int32_t* tok_slot, const float* inv_freq,
                           bf16* kpool, bf16* vpool, int t_begin, int t_end, int n_q, int n_kv, int d,
-                          hipStream_t s) {
+                          hipStream_t s, int t_defer) {
   if (t_end <= t_begin) return hipSuccess;
   hipLaunchKernelGGL(rope_kv_kernel, dim3(t_end - t_begin), dim3(256), 0, s, qkv, tok_pos, tok_slot, inv_freq,
-                     kpool, vpool, t_begin, n_q, n_kv, d);
+                     kpool, vpool, t_begin, t_defer, n_q, n_kv, d);
+  return hipGetLastError();
+}
+
+// The paged KV append of tokens whose rotated k and v are already in qkv: one wave per
+// token, k rows in 16-byte pieces into the 32-dim column chunks, v dim-major (2-byte
+// stores, one per dimension row of the block).
+__global__ __launch_bounds__(256) void kv_append_kernel(const bf16* __restrict__ qkv,
+                                                        const int32_t* __restrict__ tok_slot, bf16* __restrict__ kpool,
+                                                        bf16* __restrict__ vpool, int t_begin, int t_end, int n_q,
+                                                        int n_kv, int d) {
+  const int t = t_begin + blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= t_end) return;
+  const int lane = threadIdx.x & 63;
+  const int slot = tok_slot[t];
+  const int blk = slot / kBlock, off = slot % kBlock;
+  const bf16* row = qkv + (size_t)t * (n_q + 2 * n_kv) * d;
+  const bf16* krow = row + n_q * d;
+  const bf16* vrow = row + (n_q + n_kv) * d;
+  const int pieces = n_kv * d / 8;  // 16-byte pieces of the token's k (and of its v)
+  for (int c = lane; c < pieces; c += 64) {
+    const int g = (c * 8) / d, j0 = (c * 8) % d;
+    const bf16x8 k = *reinterpret_cast<const bf16x8*>(krow + c * 8);
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(vrow + c * 8);
+    bf16* kb = kpool + ((size_t)blk * n_kv + g) * (kBlock * d) + off * 32;
+    *reinterpret_cast<bf16x8*>(kb + (j0 >> 5) * (kBlock * 32) + (j0 & 31)) = k;
+    bf16* vb = vpool + (((size_t)blk * n_kv + g) * d + j0) * kBlock + off;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vb[e * kBlock] = v[e];
+  }
+}
+
+hipError_t launch_kv_append(const bf16* qkv, const int32_t* tok_slot, bf16* kpool, bf16* vpool, int t_begin,
+                            int t_end, int n_q, int n_kv, int d, hipStream_t s) {
+  if (t_end <= t_begin) return hipSuccess;
+  hipLaunchKernelGGL(kv_append_kernel, dim3((t_end - t_begin + 3) / 4), dim3(256), 0, s, qkv, tok_slot, kpool, vpool,
+                     t_begin, t_end, n_q, n_kv, d);
   return hipGetLastError();
 }
 

@@ -542,9 +542,11 @@ nf_status launch_op(nf_ctx* ctx, const LayerArgs& A, const PlanGraph& g, const N
         return launch_gemm(h + (size_t)lo * H, static_cast<const bf16*>(A.w->w_qkv), qkv + (size_t)lo * W, nullptr, m,
                            W, H, 0, pick_variant(ctx, NF_OP_KQV, 0, m, W, H, 0), s, ws(0), ws_cap - M.gemm_ws_off[2 * op_i]);
       }));
+      // decode tokens' K/V go to the pool after their attention (DECATTN below): an attention
+      // launch right after the partial-line stores of their append ran 3-6% slower
       NF_TRY(timed(ctx, NF_K_ROPE_KV, s, [&] {
         return launch_rope_kv(qkv, M.d_pos, M.d_slot, M.d_inv_freq, static_cast<bf16*>(A.pool->k),
-                              static_cast<bf16*>(A.pool->v), lo, hi, nq, nkv, d, s);
+                              static_cast<bf16*>(A.pool->v), lo, hi, nq, nkv, d, s, g.n_dec);
       }));
       break;
     }
@@ -555,13 +557,18 @@ nf_status launch_op(nf_ctx* ctx, const LayerArgs& A, const PlanGraph& g, const N
         return launch_decode_attn(qkv, static_cast<const bf16*>(A.pool->k), static_cast<const bf16*>(A.pool->v),
                                   M.d_bt, A.max_blocks, M.d_dec + i0, i1 - i0, static_cast<float*>(ctx->part_o.p),
                                   static_cast<float*>(ctx->part_ml.p), attn, nq, nkv, d, A.decode_grid,
-                                  ctx->decode_nbuf, ctx->decode_ring, s, e0, e1);
+                                  ctx->decode_nbuf, ctx->decode_ring, s, e0, e1, /*new_from_qkv=*/1);
       }));
       if (c1 > c0)
         NF_TRY(timed(ctx, NF_K_DECODE_COMBINE, s, [&] {
           return launch_decode_combine(M.d_comb + c0, c1 - c0, static_cast<const float*>(ctx->part_o.p),
                                        static_cast<const float*>(ctx->part_ml.p), attn, nq, nkv, d, s);
         }));
+      // the decode tokens' K/V (rotated k and v in qkv) into their pool slots
+      NF_TRY(timed(ctx, NF_K_ROPE_KV, s, [&] {
+        return launch_kv_append(qkv, M.d_slot, static_cast<bf16*>(A.pool->k), static_cast<bf16*>(A.pool->v), op.r0,
+                                op.r1, nq, nkv, d, s);
+      }));
       break;
     }
     case NF_OP_PFATTN: {

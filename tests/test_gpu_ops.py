@@ -253,8 +253,14 @@ def test_rope_kv_append_slots_bit_exact(ctx, n_q, n_kv, d):
     assert rel_inf(f64(kg[wk]), f64(k_ref[wk])) <= TOL
     qg = f64(_host(dqkv)[:, : n_q * d]).reshape(T, n_q, d)
     assert rel_inf(qg, q) <= TOL
-    # k, v columns of qkv are left as they were
-    assert np.array_equal(_host(dqkv)[:, n_q * d :], qkv[:, n_q * d :])
+    # k is rotated in place too (the same bf16 values the pool received); v columns are left
+    # as they were
+    kq = _host(dqkv)[:, n_q * d : (n_q + n_kv) * d]
+    assert rel_inf(f64(kq).reshape(T, n_kv, d), k) <= TOL
+    kq_pool = ol.write_kv(np.full_like(kp, CANARY), np.full_like(vp, CANARY), b, 16,
+                          f64(kq).reshape(T, n_kv, d), v)[0]
+    assert np.array_equal(kg[wk], kq_pool[wk])
+    assert np.array_equal(_host(dqkv)[:, (n_q + n_kv) * d :], qkv[:, (n_q + n_kv) * d :])
 
 
 def _attention_case(rng, n_q, n_kv, d, dec_ctx, pre_len, pre_prefix, seed):

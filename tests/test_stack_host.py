@@ -53,8 +53,9 @@ def _accesses(b, bounds, op_index, kind, j, layer, alias_x):
     ws = f"ws{op_index}"  # split-K workspace region of this op (shared by every layer)
     if kind == 0:
         return [(x, R, 0), ("h", R, 1), ("h", R, 0), ("qkv", R, 1), (pool, R, 1), (ws, None, 1)]
-    if kind == 1:  # an op without rows launches nothing
-        return [("qkv", R, 0), (pool, R, 0), ("attn", R, 1), (f"part{j}", None, 1), (f"part{j}", None, 0)] if R else []
+    if kind == 1:  # an op without rows launches nothing; it also appends its decode tokens' K/V
+        return [("qkv", R, 0), (pool, R, 0), ("attn", R, 1), (f"part{j}", None, 1), (f"part{j}", None, 0),
+                (pool, R, 1)] if R else []
     if kind == 2:
         return [("qkv", R, 0), (pool, R, 0), ("attn", R, 1)] if R else []
     if kind == 3:
