@@ -86,9 +86,9 @@ hipError_t launch_rmsnorm(const bf16* x, const bf16* g, bf16* out, int m, int n,
 // sincos, shared through LDS by its n_q + n_kv heads); then each thread rotates 8
 // consecutive pairs (i0..i0+7, i0+d/2..i0+d/2+7) of one head with two 16-byte loads and two
 // 16-byte stores: q and k in place in qkv, k also into the token's slot of the pool (8
-// consecutive dims lie in one 32-dim column chunk). v is read 16 bytes at a time and stored
-// dim-major, one 2-byte element per dimension row of the block. Tokens below t_defer keep
-// their K/V out of the pool here (kv_append_kernel stores them later, from qkv).
+// consecutive dims lie in one 32-dim column chunk). v is stored dim-major, one 2-byte
+// element per dimension row of the block. Tokens below t_defer keep their K/V out of the
+// pool here (kv_append_kernel stores them later, from qkv).
 __global__ __launch_bounds__(256) void rope_kv_kernel(bf16* __restrict__ qkv, const int32_t* __restrict__ tok_pos,
                                                       const int32_t* __restrict__ tok_slot,
                                                       const float* __restrict__ inv_freq, bf16* __restrict__ kpool,
@@ -136,14 +136,11 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(bf16* __restrict__ qkv, co
     }
   }
   if (!append) return;
+  // v element i = (head g, dim j) to row (g, j) of the block; consecutive threads take
+  // consecutive i, so one store instruction touches 16 lines (rows are 32 bytes apart)
   const bf16* vrow = row + (n_q + n_kv) * d;
-  for (int c = threadIdx.x; c < n_kv * d / 8; c += 256) {
-    const int g = (c * 8) / d, j0 = (c * 8) % d;
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(vrow + c * 8);
-    bf16* vb = vpool + (((size_t)blk * n_kv + g) * d + j0) * kBlock + off;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vb[e * kBlock] = v[e];
-  }
+  bf16* vb = vpool + (size_t)blk * n_kv * d * kBlock + off;
+  for (int i = threadIdx.x; i < n_kv * d; i += 256) vb[(size_t)i * kBlock] = vrow[i];
 }
 
 hipError_t launch_rope_kv(bf16* qkv, const int32_t* tok_pos, const int32_t* tok_slot, const float* inv_freq,
@@ -156,8 +153,10 @@ hipError_t launch_rope_kv(bf16* qkv, const int32_t* tok_pos, const int32_t* tok_
 }
 
 // The paged KV append of tokens whose rotated k and v are already in qkv: one wave per
-// token, k rows in 16-byte pieces into the 32-dim column chunks, v dim-major (2-byte
-// stores, one per dimension row of the block).
+// token, k rows in 16-byte pieces into the 32-dim column chunks; v dim-major, one 2-byte
+// store per dimension row of the block, consecutive lanes on consecutive dimensions so
+// that one store instruction touches 16 lines (dimension rows are 32 bytes apart) rather
+// than one line per lane.
 __global__ __launch_bounds__(256) void kv_append_kernel(const bf16* __restrict__ qkv,
                                                         const int32_t* __restrict__ tok_slot, bf16* __restrict__ kpool,
                                                         bf16* __restrict__ vpool, int t_begin, int t_end, int n_q,
@@ -170,17 +169,16 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const bf16* __restrict__
   const bf16* row = qkv + (size_t)t * (n_q + 2 * n_kv) * d;
   const bf16* krow = row + n_q * d;
   const bf16* vrow = row + (n_q + n_kv) * d;
-  const int pieces = n_kv * d / 8;  // 16-byte pieces of the token's k (and of its v)
+  const int pieces = n_kv * d / 8;  // 16-byte pieces of the token's k
   for (int c = lane; c < pieces; c += 64) {
     const int g = (c * 8) / d, j0 = (c * 8) % d;
     const bf16x8 k = *reinterpret_cast<const bf16x8*>(krow + c * 8);
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(vrow + c * 8);
     bf16* kb = kpool + ((size_t)blk * n_kv + g) * (kBlock * d) + off * 32;
     *reinterpret_cast<bf16x8*>(kb + (j0 >> 5) * (kBlock * 32) + (j0 & 31)) = k;
-    bf16* vb = vpool + (((size_t)blk * n_kv + g) * d + j0) * kBlock + off;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vb[e * kBlock] = v[e];
   }
+  // v element i = (head g, dim j) goes to row (g, j) of the block: lanes take consecutive i
+  bf16* vb = vpool + (size_t)blk * n_kv * d * kBlock + off;
+  for (int i = lane; i < n_kv * d; i += 64) vb[(size_t)i * kBlock] = vrow[i];
 }
 
 hipError_t launch_kv_append(const bf16* qkv, const int32_t* tok_slot, bf16* kpool, bf16* vpool, int t_begin,
