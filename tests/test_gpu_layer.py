@@ -121,6 +121,33 @@ def test_tiny_layer_plans(ctx, seed):
         _check_layer(ctx, wl, b, kp, vp, ref, dev, y_dev)
 
 
+@pytest.mark.parametrize("split", [0, 1, 2])
+def test_tiny_layer_decode_block_edges(ctx, split):
+    """The layer takes each decode request's newest key from its qkv row and appends the
+    decode tokens' K/V after their attention: contexts at block edges (an empty context, a
+    new token opening a fresh block, one closing a block), with split-KV chunks of 1 and 2
+    blocks so that an item holding only the newest key occurs, against the oracle."""
+    from nano_intra_overlap_amd import abi
+    from nano_intra_overlap_amd.device import DevicePool, DeviceWeights, bf16_tensor
+
+    wl = sw.WORKLOADS["tiny"]
+    dec = [0, 1, 15, 16, 17, 31, 32, 33, 47, 48, 63, 64, 100]
+    b = sw.batch_from_lengths(dec, [20], [16], seed=11, spare_blocks=3)
+    w = sw.make_weights(wl.shape, 4, gain_jitter=0.1)
+    x = sw.make_x(wl.shape, b.n_tokens, 4)
+    kp, vp = sw.make_kv_pool(wl.shape, b.num_blocks, 4)
+    ref = ol.layer_forward(wl.shape, w, x, b, kp, vp)
+    dev = dict(w=DeviceWeights(w, "cuda"), x=bf16_tensor(x, "cuda"), pool=DevicePool.from_host(kp, vp, "cuda"))
+    y_dev = torch.full_like(dev["x"], float("nan"))
+    log_case(f"tiny layer decode block edges split={split}")
+    abi.nf_ctx_set_decode_split(ctx, split)
+    try:
+        _run_layer(ctx, wl.shape, dev["w"], dev["x"], y_dev, _host_batch(b), dev["pool"], None)
+    finally:
+        abi.nf_ctx_set_decode_split(ctx, 0)
+    _check_layer(ctx, wl, b, kp, vp, ref, dev, y_dev)
+
+
 def _host_batch(b):
     from nano_intra_overlap_amd import abi
 
