@@ -276,7 +276,11 @@ __device__ __forceinline__ void interleave_loads_reads() {
   if constexpr (NR > PR) __builtin_amdgcn_sched_group_barrier(0x100, NR - PR, 0);
 }
 
-template <int BM, int BN, int STAGES, int EPI, bool GRP = false, int NW = 4, int KC = 4>
+// SB: slabs of the B ring (the weights). SB = STAGES: A and B share one ring of STAGES slabs.
+// SB = STAGES + 1 (with STAGES = 2): B, streamed from HBM, gets its own ring with one slab
+// more of lookahead than A (A's rows are recent activations, mostly cache hits): slab kt + 3
+// of B is requested while slab kt is multiplied.
+template <int BM, int BN, int STAGES, int EPI, bool GRP = false, int NW = 4, int KC = 4, int SB = STAGES>
 __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restrict__ A0, const bf16* __restrict__ B0,
                                                         bf16* C0, const bf16* R, int M0, int N, int K, int ldc,
                                                         int b_up, int tiles_m0,
@@ -292,6 +296,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int A_CH = BM * KC, B_CH = BN * KC;     // 16-byte chunks per slab
   constexpr int STAGE_BYTES = (A_CH + B_CH) * 16;
+  static_assert(SB == STAGES || (SB == STAGES + 1 && STAGES == 2), "B ring: STAGES slabs, or 3 with an A ring of 2");
+  constexpr bool SPLIT = SB != STAGES;
+  // slab kt of A and of B: one ring of A+B stages, or (SPLIT) an A ring then a B ring
+  auto a_slab = [](int kt) { return SPLIT ? (kt % STAGES) * (A_CH * 16) : (kt % STAGES) * STAGE_BYTES; };
+  auto b_slab = [](int kt) {
+    return SPLIT ? STAGES * (A_CH * 16) + (kt % SB) * (B_CH * 16) : (kt % STAGES) * STAGE_BYTES + A_CH * 16;
+  };
   constexpr int A_LOADS = A_CH / NT, B_LOADS = B_CH / NT;  // per thread (= per wave instruction count)
   static_assert(A_LOADS * NT == A_CH && B_LOADS * NT == B_CH, "slab chunks split evenly over the threads");
   constexpr int NL = A_LOADS + B_LOADS;
@@ -380,8 +391,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
     b_src[i] = B + (size_t)gr * K + k_begin + kc * 8;
   }
   typedef __attribute__((address_space(3))) void lds_void;
-  auto issue = [&](int kt) {
-    lds_void* base = (lds_void*)(smem_raw + (kt % STAGES) * STAGE_BYTES);
+  auto issue_a = [&](int kt) {
+    lds_void* base = (lds_void*)(smem_raw + a_slab(kt));
     const int k0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i)
@@ -389,12 +400,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
                                        (lds_void*)((unsigned char __attribute__((address_space(3)))*)base +
                                                    ((i * NW + wave) * 64) * 16),
                                        16, 0, 0);
+  };
+  auto issue_b = [&](int kt) {
+    lds_void* base = (lds_void*)(smem_raw + b_slab(kt));
+    const int k0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + k0),
-                                       (lds_void*)((unsigned char __attribute__((address_space(3)))*)base + A_CH * 16 +
+                                       (lds_void*)((unsigned char __attribute__((address_space(3)))*)base +
                                                    ((i * NW + wave) * 64) * 16),
                                        16, 0, 0);
+  };
+  auto issue = [&](int kt) {
+    issue_a(kt);
+    issue_b(kt);
   };
 
   f32x16 acc[TM][TN];
@@ -407,10 +426,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
 
   const int nk = s_end - s_begin;
   // all STAGES slabs in flight from the start; slab kt + STAGES is issued into slab kt's
-  // buffer once every wave has read slab kt
+  // buffer once every wave has read slab kt (SPLIT: B's slab 2 as well)
 #pragma unroll
   for (int s = 0; s < STAGES; ++s)
     if (s < nk) issue(s);
+  if constexpr (SPLIT)
+    if (STAGES < nk) issue_b(STAGES);
 
   // fragment read offsets (bytes within a slab): row (l % 32) of each 32-row tile, k-chunk 2 kk + l / 32
   const int fr = lane & 31, fk = lane >> 5;
@@ -427,7 +448,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
 #pragma unroll
     for (int kk = 0; kk < Q; ++kk) {
       const int row = wn * WTN + j * 32 + fr;
-      b_off[j][kk] = A_CH * 16 + row * (16 * KC) + (((2 * kk + fk) ^ swz_k<KC>(row)) * 16);
+      b_off[j][kk] = row * (16 * KC) + (((2 * kk + fk) ^ swz_k<KC>(row)) * 16);  // within B's slab
     }
 
   // Fragments of the two 16-wide k halves of a slab live in separate registers, so the LDS
@@ -437,11 +458,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
   // The scheduling barriers keep the compiler from regrouping reads next to their MFMAs.
   bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
   auto read_frags = [&](int kt, int kk, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
-    const unsigned char* slab = smem_raw + (kt % STAGES) * STAGE_BYTES;
+    const unsigned char* sa = smem_raw + a_slab(kt);
+    const unsigned char* sb = smem_raw + b_slab(kt);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(slab + a_off[i][kk]);
+    for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(sa + a_off[i][kk]);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(slab + b_off[j][kk]);
+    for (int j = 0; j < TN; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(sb + b_off[j][kk]);
   };
   auto mfmas = [&](const bf16x8 (&fa)[TM], const bf16x8 (&fb)[TN]) {
 #pragma unroll
@@ -465,7 +487,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
     else wait_vmcnt<0>();
   };
 
-  wait_slab(min(STAGES - 1, nk - 1));
+  if constexpr (SPLIT) {
+    // issued: A0 B0 [A1 B1] [B2]; slab 0 needed
+    if (nk > 2) wait_vmcnt<A_LOADS + 2 * B_LOADS>();
+    else if (nk > 1) wait_vmcnt<A_LOADS + B_LOADS>();
+    else wait_vmcnt<0>();
+  } else {
+    wait_slab(min(STAGES - 1, nk - 1));
+  }
   lds_barrier();
   read_frags(0, 0, fa0, fb0);
   // one trip: MFMAs of slab kt's first half with the reads of its second half slotted
@@ -511,9 +540,47 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
   // newest still outstanding; the body is straight-line so the compiler's LDS wait counts
   // stay exact
   int kt = 0;
-  for (; kt + STAGES < nk; ++kt) trip(kt, [] { wait_vmcnt<NL * (STAGES - 2)>(); }, true);
-  // drain: no refills; at most min(2, nk - 2 - kt) newer slabs remain
-  for (; kt + 1 < nk; ++kt) trip(kt, [&] { wait_slab(min(STAGES - 2, nk - 2 - kt)); }, false);
+  if constexpr (SPLIT) {
+    // slab kt+1 is awaited with B's slab kt+2 still in flight (issued after A's slab kt+1);
+    // after the barrier, A's slab kt+2 and B's slab kt+3 are issued
+    auto trip_split = [&](int kt, auto wait_next, auto refill, auto sched) {
+      steps_but_last(kt);
+      wait_next();
+      lds_barrier();  // every wave has read slab kt
+      __builtin_amdgcn_sched_barrier(0);
+      refill();
+      read_frags(kt + 1, 0, fa0, fb0);
+      mfmas(fa1, fb1);
+      sched();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (; kt + 3 < nk; ++kt)
+      trip_split(kt, [] { wait_vmcnt<B_LOADS>(); },
+                 [&] {
+                   issue_a(kt + 2);
+                   issue_b(kt + 3);
+                 },
+                 [] {
+                   if constexpr (KC == 4)
+                     interleave_loads_reads<NL, TM + TN, TM * TN>();
+                   else
+                     interleave_mixed<NL, TM + TN, TM * TN>();
+                 });
+    for (; kt + 2 < nk; ++kt)
+      trip_split(kt, [] { wait_vmcnt<B_LOADS>(); }, [&] { issue_a(kt + 2); },
+                 [] {
+                   if constexpr (KC == 4)
+                     interleave_loads_reads<A_LOADS, TM + TN, TM * TN>();
+                   else
+                     interleave_mixed<A_LOADS, TM + TN, TM * TN>();
+                 });
+    for (; kt + 1 < nk; ++kt)
+      trip_split(kt, [] { wait_vmcnt<0>(); }, [] {}, [] { interleave_reads<TM + TN, TM * TN>(); });
+  } else {
+    for (; kt + STAGES < nk; ++kt) trip(kt, [] { wait_vmcnt<NL * (STAGES - 2)>(); }, true);
+    // drain: no refills; at most min(2, nk - 2 - kt) newer slabs remain
+    for (; kt + 1 < nk; ++kt) trip(kt, [&] { wait_slab(min(STAGES - 2, nk - 2 - kt)); }, false);
+  }
   steps_but_last(nk - 1);
   mfmas(fa1, fb1);
 
@@ -524,7 +591,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
   // when the tile does not fit.
   using T = typename std::conditional<EPI == EPI_RESID || EPI == EPI_PARTIAL, float, bf16>::type;
   constexpr int OC = (EPI == EPI_SWIGLU) ? BN / 2 : BN;  // output columns of the tile
-  constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  constexpr int LDS_BYTES = SPLIT ? STAGES * A_CH * 16 + SB * B_CH * 16 : STAGES * STAGE_BYTES;
   constexpr int PASSES = (BM * OC * (int)sizeof(T) <= LDS_BYTES) ? 1 : 2;
   static_assert(PASSES == 1 || WTM * OC * (int)sizeof(T) <= LDS_BYTES, "epilogue tile half must fit");
   constexpr int RP = PASSES == 1 ? BM : WTM;  // rows per pass
@@ -645,6 +712,11 @@ static const GemmVariant kVariants[] = {
     // reduce; not SwiGLU): a narrow product with a long k loop (the 70B share's KQV, n = 1280,
     // k = 8192, at 2048 rows: 80 tiles x 3 = 240 workgroups where 128x128 tiles give 160)
     {256, 128, 64, 3, 3, 8},  // 31
+    // variant 22 (and 26, the column-split launch) with the B operand in its own ring of 3
+    // slabs beside A's 2 (160 KB): the weights, which stream from HBM, are requested a slab
+    // further ahead
+    {256, 256, 64, 1, 2, 8, 3},  // 32
+    {256, 256, 64, 1, 2, 8, 3},  // 33
 };
 constexpr int kBalancedVariant = 19, kBalancedDeepVariant = 26;
 static constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
@@ -790,7 +862,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 // ldc: row stride of C and R (N for a whole product); b_up: SwiGLU's row of B holding the
 // up weights of output column 0 (N for a whole product, gate rows [0, N) then up rows).
-template <int BM, int BN, int STAGES, int EPI, int NW = 4, int KC = 4>
+template <int BM, int BN, int STAGES, int EPI, int NW = 4, int KC = 4, int SB = STAGES>
 static hipError_t launch_pipe_t(const bf16* A, const bf16* B, bf16* C, const bf16* R, int M, int N, int K, int ks,
                                 float* part, hipStream_t s, int ldc = -1, int b_up = -1) {
   if (ldc < 0) ldc = N;
@@ -799,8 +871,8 @@ static hipError_t launch_pipe_t(const bf16* A, const bf16* B, bf16* C, const bf1
   const int tiles_n = (EPI == EPI_SWIGLU) ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
   const int ntiles = tiles_m * tiles_n;
   const int per_xcd = (ntiles + kNumXcd - 1) / kNumXcd;
-  const size_t lds = (size_t)STAGES * (BM + BN) * 16 * KC;
-  auto kern = gemm_pipe_kernel<BM, BN, STAGES, EPI, false, NW, KC>;
+  const size_t lds = (size_t)(STAGES * BM + SB * BN) * 16 * KC;
+  auto kern = gemm_pipe_kernel<BM, BN, STAGES, EPI, false, NW, KC, SB>;
   static bool attr_set = false;
   if (hipError_t e = set_lds_attr(reinterpret_cast<const void*>(kern), lds, attr_set); e != hipSuccess || t_prepare_only)
     return e;
@@ -830,12 +902,12 @@ static hipError_t launch_grouped_t(const bf16* A, const int32_t* a_rows, const b
   return hipGetLastError();
 }
 
-template <int BM, int BN, int STAGES, int NW = 4, int KC = 4>
+template <int BM, int BN, int STAGES, int NW = 4, int KC = 4, int SB = STAGES>
 static hipError_t launch_pipe(const bf16* A, const bf16* B, bf16* C, const bf16* R, int M, int N, int K, int epi,
                               int ks, float* ws, hipStream_t s) {
   if (ks > 1) {
     // fp32 partials of the ks K-slices, then one pass that sums them with the epilogue
-    hipError_t e = launch_pipe_t<BM, BN, STAGES, EPI_PARTIAL, NW, KC>(A, B, C, R, M, N, K, ks, ws, s);
+    hipError_t e = launch_pipe_t<BM, BN, STAGES, EPI_PARTIAL, NW, KC, SB>(A, B, C, R, M, N, K, ks, ws, s);
     if (e != hipSuccess || t_prepare_only) return e;
     const size_t n8 = (size_t)M * N / 8;
     const int grid = (int)std::min<size_t>((n8 + 255) / 256, 4096);
@@ -844,11 +916,11 @@ static hipError_t launch_pipe(const bf16* A, const bf16* B, bf16* C, const bf16*
     return hipGetLastError();
   }
   switch (epi) {
-    case EPI_STORE: return launch_pipe_t<BM, BN, STAGES, EPI_STORE, NW, KC>(A, B, C, R, M, N, K, 1, nullptr, s);
-    case EPI_RESID: return launch_pipe_t<BM, BN, STAGES, EPI_RESID, NW, KC>(A, B, C, R, M, N, K, 1, nullptr, s);
+    case EPI_STORE: return launch_pipe_t<BM, BN, STAGES, EPI_STORE, NW, KC, SB>(A, B, C, R, M, N, K, 1, nullptr, s);
+    case EPI_RESID: return launch_pipe_t<BM, BN, STAGES, EPI_RESID, NW, KC, SB>(A, B, C, R, M, N, K, 1, nullptr, s);
     case EPI_SWIGLU:
       if constexpr ((BN / (NW / 2)) % 64 == 0)
-        return launch_pipe_t<BM, BN, STAGES, EPI_SWIGLU, NW, KC>(A, B, C, R, M, N, K, 1, nullptr, s);
+        return launch_pipe_t<BM, BN, STAGES, EPI_SWIGLU, NW, KC, SB>(A, B, C, R, M, N, K, 1, nullptr, s);
       return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
@@ -882,7 +954,7 @@ static int device_cus() {
 // rest in one round of 256x128 tiles (4 waves with SwiGLU, else 8 waves and 6 slabs); the
 // plain 256x256 launch when the last round is more than half full or the product has fewer
 // tiles than one round.
-template <int EPI, int KC = 4>
+template <int EPI, int KC = 4, int SB_FULL = (KC == 4 ? 4 : 2)>
 static hipError_t launch_balanced_t(const bf16* A, const bf16* B, bf16* C, const bf16* R, int m, int n, int k,
                                     hipStream_t s) {
   constexpr int S_FULL = KC == 4 ? 4 : 2;  // slabs of the 256x256 tiles (128 KB either way)
@@ -891,9 +963,9 @@ static hipError_t launch_balanced_t(const bf16* A, const bf16* B, bf16* C, const
   const int rt = (m + 255) / 256, ct = (n + cw - 1) / cw, T = rt * ct, r = T % cus;
   const int ct1 = (T - r) / rt;
   if (r == 0 || ct1 <= 0 || ct1 >= ct || 2 * rt * (ct - ct1) > cus)
-    return launch_pipe_t<256, 256, S_FULL, EPI, 8, KC>(A, B, C, R, m, n, k, 1, nullptr, s);
+    return launch_pipe_t<256, 256, S_FULL, EPI, 8, KC, SB_FULL>(A, B, C, R, m, n, k, 1, nullptr, s);
   const int n1 = ct1 * cw;
-  hipError_t e = launch_pipe_t<256, 256, S_FULL, EPI, 8, KC>(A, B, C, R, m, n1, k, 1, nullptr, s, n, n);
+  hipError_t e = launch_pipe_t<256, 256, S_FULL, EPI, 8, KC, SB_FULL>(A, B, C, R, m, n1, k, 1, nullptr, s, n, n);
   if (e != hipSuccess) return e;
   const bf16* R2 = R ? R + n1 : nullptr;
   constexpr int S_HALF4 = KC == 4 ? 4 : 3, S_HALF8 = KC == 4 ? 6 : 3;  // slabs of the 256x128 tiles
@@ -905,13 +977,13 @@ static hipError_t launch_balanced_t(const bf16* A, const bf16* B, bf16* C, const
                                                         n, n);
 }
 
-template <int KC>
+template <int KC, int SB_FULL = (KC == 4 ? 4 : 2)>
 static hipError_t launch_balanced(const bf16* A, const bf16* B, bf16* C, const bf16* R, int m, int n, int k, int epi,
                                   hipStream_t s) {
   switch (epi) {
-    case EPI_STORE: return launch_balanced_t<EPI_STORE, KC>(A, B, C, R, m, n, k, s);
-    case EPI_RESID: return launch_balanced_t<EPI_RESID, KC>(A, B, C, R, m, n, k, s);
-    case EPI_SWIGLU: return launch_balanced_t<EPI_SWIGLU, KC>(A, B, C, R, m, n, k, s);
+    case EPI_STORE: return launch_balanced_t<EPI_STORE, KC, SB_FULL>(A, B, C, R, m, n, k, s);
+    case EPI_RESID: return launch_balanced_t<EPI_RESID, KC, SB_FULL>(A, B, C, R, m, n, k, s);
+    case EPI_SWIGLU: return launch_balanced_t<EPI_SWIGLU, KC, SB_FULL>(A, B, C, R, m, n, k, s);
   }
   return hipErrorInvalidValue;
 }
@@ -954,6 +1026,8 @@ hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int
     case 29: return launch_pipe<128, 256, 3, 4, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
     case 30: return launch_pipe<128, 256, 3, 8, 8>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
     case 31: return launch_pipe<256, 128, 3, 8, 8>(A, B, C, R, m, n, k, epilogue, 3, ws, s);
+    case 32: return launch_pipe<256, 256, 2, 8, 8, 3>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 33: return launch_balanced<8, 3>(A, B, C, R, m, n, k, epilogue, s);
   }
   return hipErrorInvalidValue;
 }

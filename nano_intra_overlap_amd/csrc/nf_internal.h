@@ -63,6 +63,7 @@ struct GemmVariant {
   int bm, bn, bk, ks;  // tile, k step, K slices (split-K; 1 = none)
   int stages = 4;      // LDS slabs of the pipelined kernels
   int waves = 4;       // waves per workgroup (pipelined kernels: 4 or 8)
+  int b_stages = 0;    // slabs of a separate B ring (0: A and B share the STAGES ring)
 };
 int gemm_variant_count();
 GemmVariant gemm_variant(int i);

@@ -145,10 +145,13 @@ def test_gemm_balanced_last_round(ctx, m, n, k, epi):
     assert rel_inf(got[rows], ref) <= TOL
 
 
-@pytest.mark.parametrize("m,n,k,epi", [(600, 1000, 1024, 0), (600, 1000, 1024, 1), (513, 768, 640, 2), (64, 256, 64, 1)])
+@pytest.mark.parametrize("m,n,k,epi", [(600, 1000, 1024, 0), (600, 1000, 1024, 1), (513, 768, 640, 2), (64, 256, 64, 1),
+                                       (300, 512, 128, 0), (300, 512, 192, 1), (257, 1024, 256, 2)])
 def test_gemm_deep_slabs_bit_identical(ctx, m, n, k, epi):
-    """The 64-deep slab variants (21-24, 26-30) sum k in the same order as the 32-deep ones: every
-    output bit-identical to variant 12 (ragged m and n, a single slab at k = 64)."""
+    """The 64-deep slab variants (21-24, 26-30, and 32-33 with the B operand in its own ring
+    of 3 slabs) sum k in the same order as the 32-deep ones: every output bit-identical to
+    variant 12 (ragged m and n; 1, 2, 3 and 4 slabs of 64, which take every branch of the
+    split ring's prologue and drain)."""
     from nano_intra_overlap_amd import abi
 
     rng = np.random.default_rng(m + 3 * n + k + epi)
@@ -157,7 +160,7 @@ def test_gemm_deep_slabs_bit_identical(ctx, m, n, k, epi):
     R = rand_bf16(rng, (m, n))
     dA, dB, dR = _dev(A), _dev(B), _dev(R)
     outs = {}
-    for v in (12, 21, 22, 23, 24, 26, 27, 28, 29, 30):
+    for v in (12, 21, 22, 23, 24, 26, 27, 28, 29, 30, 32, 33):
         if v in (23, 27) and epi == 2:
             continue
         dC = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
@@ -177,7 +180,7 @@ def test_gemm_deep_slabs_bit_identical(ctx, m, n, k, epi):
 
 
 @pytest.mark.parametrize("variant", [-1, 6, 7, 9, 10, 11, 12, 13, 14, 15, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30,
-                                     31])
+                                     31, 32, 33])
 def test_gemm_residual_in_place(ctx, variant):
     from nano_intra_overlap_amd import abi
 
