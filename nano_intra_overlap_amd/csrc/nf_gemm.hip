@@ -276,6 +276,15 @@ __device__ __forceinline__ void interleave_loads_reads() {
   if constexpr (NR > PR) __builtin_amdgcn_sched_group_barrier(0x100, NR - PR, 0);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
+
+// 16 bytes per lane from buffer r at byte offset voff + soff into LDS (lane l at dst + 16 l).
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff,
+                                                  uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+}
+
 // SB: slabs of the B ring (the weights). SB = STAGES: A and B share one ring of STAGES slabs.
 // SB = STAGES + 1 (with STAGES = 2): B, streamed from HBM, gets its own ring with one slab
 // more of lookahead than A (A's rows are recent activations, mostly cache hits): slab kt + 3
@@ -298,6 +307,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
   constexpr int STAGE_BYTES = (A_CH + B_CH) * 16;
   static_assert(SB == STAGES || (SB == STAGES + 1 && STAGES == 2), "B ring: STAGES slabs, or 3 with an A ring of 2");
   constexpr bool SPLIT = SB != STAGES;
+  // one wave per SIMD: the last k16 step of a trip runs in a fixed MFMA / load / read order
+  // (with the split ring the compiler's LDS-DMA wait tracking then serialises the loads)
+  constexpr bool PIN = NW == 4 && !SPLIT;
   // slab kt of A and of B: one ring of A+B stages, or (SPLIT) an A ring then a B ring
   auto a_slab = [](int kt) { return SPLIT ? (kt % STAGES) * (A_CH * 16) : (kt % STAGES) * STAGE_BYTES; };
   auto b_slab = [](int kt) {
@@ -363,18 +375,29 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
   const int s_begin = (int)(((long long)blockIdx.y * n_slabs) / gridDim.y);
   const int s_end = (int)(((long long)(blockIdx.y + 1) * n_slabs) / gridDim.y);
   const int k_begin = s_begin * BK;
-  // per-thread source rows of the direct loads (fixed across k): chunk c = (i*4 + wave)*64 + lane
-  const bf16* a_src[A_LOADS];
-  const bf16* b_src[B_LOADS];
+  // Direct loads through buffer resources: a lane's source is a fixed 32-bit byte offset
+  // from the tile's first row of A or B (chunk c = (i * NW + wave) * 64 + lane of the slab),
+  // the k position a scalar offset and the LDS destination M0 (scalar too), so a refill is
+  // one scalar add and one load instruction per chunk row, with no per-load vector
+  // address arithmetic. The launcher checks that every offset fits in 31 bits.
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  bool a_gather = false;
+  if constexpr (GRP) a_gather = a_rows != nullptr;
+  const bf16* a_base = a_gather ? A : A + (size_t)m0 * K;
+  const bf16* b_base = B + (size_t)n0 * K;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, -1, 0x00020000);
+  uint32_t a_off_g[A_LOADS], b_off_g[B_LOADS];
 #pragma unroll
   for (int i = 0; i < A_LOADS; ++i) {
     const int c = (i * NW + wave) * 64 + lane;
     const int row = c / KC, kc = (c % KC) ^ swz_k<KC>(row);
     int gr = min(m0 + row, M - 1);
     if constexpr (GRP) {
-      if (a_rows) gr = a_rows[gr];  // gathered rows of A
+      if (a_rows) gr = a_rows[gr];  // gathered rows of A (offsets from A itself)
     }
-    a_src[i] = A + (size_t)gr * K + k_begin + kc * 8;
+    const int rel = a_gather ? gr : gr - m0;
+    a_off_g[i] = (uint32_t)(((size_t)rel * K + k_begin + kc * 8) * sizeof(bf16));
   }
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
@@ -388,28 +411,21 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
     } else {
       gr = min(n0 + row, N - 1);
     }
-    b_src[i] = B + (size_t)gr * K + k_begin + kc * 8;
+    b_off_g[i] = (uint32_t)(((size_t)(gr - n0) * K + k_begin + kc * 8) * sizeof(bf16));
   }
-  typedef __attribute__((address_space(3))) void lds_void;
   auto issue_a = [&](int kt) {
-    lds_void* base = (lds_void*)(smem_raw + a_slab(kt));
-    const int k0 = kt * BK;
+    lds_byte* dst = (lds_byte*)smem_raw + a_slab(kt) + wave_s * 64 * 16;
+    const uint32_t ks = (uint32_t)(kt * BK * (int)sizeof(bf16));
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + k0),
-                                       (lds_void*)((unsigned char __attribute__((address_space(3)))*)base +
-                                                   ((i * NW + wave) * 64) * 16),
-                                       16, 0, 0);
+      buffer_load_lds16(a_rsrc, (lds_void*)(dst + i * NW * 64 * 16), a_off_g[i], ks);
   };
   auto issue_b = [&](int kt) {
-    lds_void* base = (lds_void*)(smem_raw + b_slab(kt));
-    const int k0 = kt * BK;
+    lds_byte* dst = (lds_byte*)smem_raw + b_slab(kt) + wave_s * 64 * 16;
+    const uint32_t ks = (uint32_t)(kt * BK * (int)sizeof(bf16));
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + k0),
-                                       (lds_void*)((unsigned char __attribute__((address_space(3)))*)base +
-                                                   ((i * NW + wave) * 64) * 16),
-                                       16, 0, 0);
+      buffer_load_lds16(b_rsrc, (lds_void*)(dst + i * NW * 64 * 16), b_off_g[i], ks);
   };
   auto issue = [&](int kt) {
     issue_a(kt);
@@ -518,11 +534,49 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // The trip's last k16 step in a fixed order: MFMA x, refill load x (A's chunk rows, then
+  // B's), fragment read x of slab kt + 1's first step, for x = 0, 1, ..., with a scheduling
+  // barrier after each. Left to itself the compiler bunches the loads, and a wave that is
+  // alone on its SIMD then leaves the matrix core idle while they issue.
+  auto last_step_pinned = [&](int kt, int a_kt, int b_kt, auto n_a, auto n_b) {
+    constexpr int NA = decltype(n_a)::value, NB = decltype(n_b)::value;
+    constexpr int NM = TM * TN, NR = TM + TN, NLX = NA + NB;
+    constexpr int NX = NM > NLX ? (NM > NR ? NM : NR) : (NLX > NR ? NLX : NR);
+    const unsigned char* sa = smem_raw + a_slab(kt + 1);
+    const unsigned char* sb = smem_raw + b_slab(kt + 1);
+    lds_byte* da = (lds_byte*)smem_raw + a_slab(a_kt) + wave_s * 64 * 16;
+    lds_byte* db = (lds_byte*)smem_raw + b_slab(b_kt) + wave_s * 64 * 16;
+    const uint32_t ka = (uint32_t)(a_kt * BK * (int)sizeof(bf16)), kb = (uint32_t)(b_kt * BK * (int)sizeof(bf16));
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+      if (x < NM)
+        acc[x / TN][x % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[x / TN], fb1[x % TN], acc[x / TN][x % TN], 0, 0, 0);
+      if (x < NA)
+        buffer_load_lds16(a_rsrc, (lds_void*)(da + x * NW * 64 * 16), a_off_g[x], ka);
+      else if (x < NLX)
+        buffer_load_lds16(b_rsrc, (lds_void*)(db + (x - NA) * NW * 64 * 16), b_off_g[x - NA], kb);
+      if (x < TM)
+        fa0[x] = *reinterpret_cast<const bf16x8*>(sa + a_off[x][0]);
+      else if (x < NR)
+        fb0[x - TM] = *reinterpret_cast<const bf16x8*>(sb + b_off[x - TM][0]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using IA = std::integral_constant<int, A_LOADS>;
+  using IB = std::integral_constant<int, B_LOADS>;
   auto trip = [&](int kt, auto wait_next, bool refill) {
     steps_but_last(kt);
     wait_next();
     lds_barrier();  // every wave has read slab kt
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (PIN) {
+      if (refill)
+        last_step_pinned(kt, kt + STAGES, kt + STAGES, IA{}, IB{});
+      else
+        last_step_pinned(kt, kt, kt, I0{}, I0{});
+      return;
+    }
     // the refill's loads go between this phase's MFMAs too: a load held back by the memory
     // pipeline then delays one MFMA issue, not the whole phase
     if (refill) issue(kt + STAGES);
@@ -717,8 +771,16 @@ static const GemmVariant kVariants[] = {
     // further ahead
     {256, 256, 64, 1, 2, 8, 3},  // 32
     {256, 256, 64, 1, 2, 8, 3},  // 33
+    // variant 21 (4 waves, 128 x 128 per wave, one wave per SIMD) with that split ring
+    {256, 256, 64, 1, 2, 4, 3},  // 34
+    // one wave per SIMD (4 waves, 128 x 128 per wave: two thirds of the 8-wave kernels' LDS
+    // reads per MFMA): variant 26's column split, variant 25's two K slices, variant 31's
+    // three
+    {256, 256, 64, 1, 2, 4},  // 35
+    {256, 256, 64, 2, 2, 4},  // 36 (not SwiGLU)
+    {256, 128, 64, 3, 3, 4},  // 37 (not SwiGLU)
 };
-constexpr int kBalancedVariant = 19, kBalancedDeepVariant = 26;
+constexpr int kBalancedVariant = 19, kBalancedDeepVariant = 26, kBalancedDeep4Variant = 35;
 static constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 int gemm_variant_count() { return kNumVariants; }
@@ -755,8 +817,9 @@ int gemm_default_variant(int m, int n, int k, int epilogue) {
       if (epilogue != EPI_SWIGLU && nn % 192 == 0 && tiles(256, 192) % 256 == 0 && tiles(256, 256) % 256 != 0)
         return deep ? 27 : 14;
       // SwiGLU (8B Up/Gate): the balanced launch (plain 256x256 when no round is left half
-      // empty)
-      if (epilogue == EPI_SWIGLU) return deep ? kBalancedDeepVariant : kBalancedVariant;
+      // empty); with 64-deep slabs its 256x256 part runs one wave per SIMD (alone, 8B Up/Gate
+      // 400.6 against 403.8 us with 8 waves, the 70B share's 198.2 against 200.9)
+      if (epilogue == EPI_SWIGLU) return deep ? kBalancedDeep4Variant : kBalancedVariant;
       return deep ? 22 : 12;
     }
     // long K (>= 8192): 256x256 with K split in 2 when that gives >= 192 workgroups; the fp32
@@ -860,6 +923,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
+// gemm_pipe_kernel addresses A and B with 32-bit byte offsets from a tile's first row (or,
+// for gathered rows, from A itself): each must stay below 2^31.
+static bool pipe_offsets_fit(int BM, int BN, int K, bool swiglu, int b_up, long long gathered_rows) {
+  const long long lim = 1LL << 31, row = 2LL * K;
+  const long long a_rows = gathered_rows > 0 ? gathered_rows : BM;
+  const long long b_rows = swiglu ? (long long)b_up + BN / 2 : BN;
+  return a_rows * row < lim && b_rows * row < lim;
+}
+
 // ldc: row stride of C and R (N for a whole product); b_up: SwiGLU's row of B holding the
 // up weights of output column 0 (N for a whole product, gate rows [0, N) then up rows).
 template <int BM, int BN, int STAGES, int EPI, int NW = 4, int KC = 4, int SB = STAGES>
@@ -872,6 +944,7 @@ static hipError_t launch_pipe_t(const bf16* A, const bf16* B, bf16* C, const bf1
   const int ntiles = tiles_m * tiles_n;
   const int per_xcd = (ntiles + kNumXcd - 1) / kNumXcd;
   const size_t lds = (size_t)(STAGES * BM + SB * BN) * 16 * KC;
+  if (!pipe_offsets_fit(BM, BN, K, EPI == EPI_SWIGLU, b_up, 0)) return hipErrorInvalidValue;
   auto kern = gemm_pipe_kernel<BM, BN, STAGES, EPI, false, NW, KC, SB>;
   static bool attr_set = false;
   if (hipError_t e = set_lds_attr(reinterpret_cast<const void*>(kern), lds, attr_set); e != hipSuccess || t_prepare_only)
@@ -892,6 +965,7 @@ static hipError_t launch_grouped_t(const bf16* A, const int32_t* a_rows, const b
   const long long max_tiles = ((long long)(n_rows + BM - 1) / BM + n_groups) * tiles_n;
   const int per_xcd = (int)((max_tiles + kNumXcd - 1) / kNumXcd);
   const size_t lds = (size_t)STAGES * (BM + BN) * 16 * KC;
+  if (!pipe_offsets_fit(BM, BN, K, EPI == EPI_SWIGLU, N, a_rows ? n_rows : 0)) return hipErrorInvalidValue;
   auto kern = gemm_pipe_kernel<BM, BN, STAGES, EPI, true, NW, KC>;
   static bool attr_set = false;
   if (hipError_t e = set_lds_attr(reinterpret_cast<const void*>(kern), lds, attr_set); e != hipSuccess || t_prepare_only)
@@ -954,7 +1028,7 @@ static int device_cus() {
 // rest in one round of 256x128 tiles (4 waves with SwiGLU, else 8 waves and 6 slabs); the
 // plain 256x256 launch when the last round is more than half full or the product has fewer
 // tiles than one round.
-template <int EPI, int KC = 4, int SB_FULL = (KC == 4 ? 4 : 2)>
+template <int EPI, int KC = 4, int SB_FULL = (KC == 4 ? 4 : 2), int NW_FULL = 8>
 static hipError_t launch_balanced_t(const bf16* A, const bf16* B, bf16* C, const bf16* R, int m, int n, int k,
                                     hipStream_t s) {
   constexpr int S_FULL = KC == 4 ? 4 : 2;  // slabs of the 256x256 tiles (128 KB either way)
@@ -963,9 +1037,9 @@ static hipError_t launch_balanced_t(const bf16* A, const bf16* B, bf16* C, const
   const int rt = (m + 255) / 256, ct = (n + cw - 1) / cw, T = rt * ct, r = T % cus;
   const int ct1 = (T - r) / rt;
   if (r == 0 || ct1 <= 0 || ct1 >= ct || 2 * rt * (ct - ct1) > cus)
-    return launch_pipe_t<256, 256, S_FULL, EPI, 8, KC, SB_FULL>(A, B, C, R, m, n, k, 1, nullptr, s);
+    return launch_pipe_t<256, 256, S_FULL, EPI, NW_FULL, KC, SB_FULL>(A, B, C, R, m, n, k, 1, nullptr, s);
   const int n1 = ct1 * cw;
-  hipError_t e = launch_pipe_t<256, 256, S_FULL, EPI, 8, KC, SB_FULL>(A, B, C, R, m, n1, k, 1, nullptr, s, n, n);
+  hipError_t e = launch_pipe_t<256, 256, S_FULL, EPI, NW_FULL, KC, SB_FULL>(A, B, C, R, m, n1, k, 1, nullptr, s, n, n);
   if (e != hipSuccess) return e;
   const bf16* R2 = R ? R + n1 : nullptr;
   constexpr int S_HALF4 = KC == 4 ? 4 : 3, S_HALF8 = KC == 4 ? 6 : 3;  // slabs of the 256x128 tiles
@@ -977,13 +1051,13 @@ static hipError_t launch_balanced_t(const bf16* A, const bf16* B, bf16* C, const
                                                         n, n);
 }
 
-template <int KC, int SB_FULL = (KC == 4 ? 4 : 2)>
+template <int KC, int SB_FULL = (KC == 4 ? 4 : 2), int NW_FULL = 8>
 static hipError_t launch_balanced(const bf16* A, const bf16* B, bf16* C, const bf16* R, int m, int n, int k, int epi,
                                   hipStream_t s) {
   switch (epi) {
-    case EPI_STORE: return launch_balanced_t<EPI_STORE, KC, SB_FULL>(A, B, C, R, m, n, k, s);
-    case EPI_RESID: return launch_balanced_t<EPI_RESID, KC, SB_FULL>(A, B, C, R, m, n, k, s);
-    case EPI_SWIGLU: return launch_balanced_t<EPI_SWIGLU, KC, SB_FULL>(A, B, C, R, m, n, k, s);
+    case EPI_STORE: return launch_balanced_t<EPI_STORE, KC, SB_FULL, NW_FULL>(A, B, C, R, m, n, k, s);
+    case EPI_RESID: return launch_balanced_t<EPI_RESID, KC, SB_FULL, NW_FULL>(A, B, C, R, m, n, k, s);
+    case EPI_SWIGLU: return launch_balanced_t<EPI_SWIGLU, KC, SB_FULL, NW_FULL>(A, B, C, R, m, n, k, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1028,6 +1102,10 @@ hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int
     case 31: return launch_pipe<256, 128, 3, 8, 8>(A, B, C, R, m, n, k, epilogue, 3, ws, s);
     case 32: return launch_pipe<256, 256, 2, 8, 8, 3>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
     case 33: return launch_balanced<8, 3>(A, B, C, R, m, n, k, epilogue, s);
+    case 34: return launch_pipe<256, 256, 2, 4, 8, 3>(A, B, C, R, m, n, k, epilogue, 1, nullptr, s);
+    case 35: return launch_balanced<8, 2, 4>(A, B, C, R, m, n, k, epilogue, s);
+    case 36: return launch_pipe<256, 256, 2, 4, 8>(A, B, C, R, m, n, k, epilogue, 2, ws, s);
+    case 37: return launch_pipe<256, 128, 3, 4, 8>(A, B, C, R, m, n, k, epilogue, 3, ws, s);
   }
   return hipErrorInvalidValue;
 }

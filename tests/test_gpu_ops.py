@@ -112,7 +112,7 @@ def test_gemm_layer_shapes_sampled_rows(ctx, m, n, k, epi):
 @pytest.mark.parametrize("m,n,k,epi", [(2048, 14336, 4096, 2), (300, 16640, 96, 2), (512, 33280, 64, 0),
                                         (512, 33280, 64, 1), (256, 2048, 64, 2)])
 def test_gemm_balanced_last_round(ctx, m, n, k, epi):
-    """Variants 19 and 26 (64-deep) split the columns between a 256x256 launch and a last
+    """Variants 19, 26 and 35 (64-deep; 35 with 4 waves) split the columns between a 256x256 launch and a last
     round of half tiles (at these shapes the last round of 256x256 tiles would be at most half full; the
     last shape has fewer tiles than CUs and takes the plain launch). Each output element
     sums k in the same order in every tile shape: bit-identical to variant 12, and the
@@ -125,7 +125,7 @@ def test_gemm_balanced_last_round(ctx, m, n, k, epi):
     R = rand_bf16(rng, (m, n))
     dA, dB, dR = _dev(A), _dev(B), _dev(R)
     outs = {}
-    for v in (12, 19) + ((26,) if k % 64 == 0 else ()):
+    for v in (12, 19) + ((26, 35) if k % 64 == 0 else ()):
         dC = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
         log_case(f"gemm balanced m={m} n={n} k={k} epi={epi} variant={v}")
         abi.nf_op_gemm(ctx, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), dR.data_ptr(), m, n, k, epi, v,
@@ -148,8 +148,8 @@ def test_gemm_balanced_last_round(ctx, m, n, k, epi):
 @pytest.mark.parametrize("m,n,k,epi", [(600, 1000, 1024, 0), (600, 1000, 1024, 1), (513, 768, 640, 2), (64, 256, 64, 1),
                                        (300, 512, 128, 0), (300, 512, 192, 1), (257, 1024, 256, 2)])
 def test_gemm_deep_slabs_bit_identical(ctx, m, n, k, epi):
-    """The 64-deep slab variants (21-24, 26-30, and 32-33 with the B operand in its own ring
-    of 3 slabs) sum k in the same order as the 32-deep ones: every output bit-identical to
+    """The 64-deep slab variants (21-24, 26-30, 35, and 32-34 with the B operand in its own
+    ring of 3 slabs) sum k in the same order as the 32-deep ones: every output bit-identical to
     variant 12 (ragged m and n; 1, 2, 3 and 4 slabs of 64, which take every branch of the
     split ring's prologue and drain)."""
     from nano_intra_overlap_amd import abi
@@ -160,7 +160,7 @@ def test_gemm_deep_slabs_bit_identical(ctx, m, n, k, epi):
     R = rand_bf16(rng, (m, n))
     dA, dB, dR = _dev(A), _dev(B), _dev(R)
     outs = {}
-    for v in (12, 21, 22, 23, 24, 26, 27, 28, 29, 30, 32, 33):
+    for v in (12, 21, 22, 23, 24, 26, 27, 28, 29, 30, 32, 33, 34, 35):
         if v in (23, 27) and epi == 2:
             continue
         dC = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
@@ -180,7 +180,7 @@ def test_gemm_deep_slabs_bit_identical(ctx, m, n, k, epi):
 
 
 @pytest.mark.parametrize("variant", [-1, 6, 7, 9, 10, 11, 12, 13, 14, 15, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30,
-                                     31, 32, 33])
+                                     31, 32, 33, 34, 35, 36, 37])
 def test_gemm_residual_in_place(ctx, variant):
     from nano_intra_overlap_amd import abi
 
