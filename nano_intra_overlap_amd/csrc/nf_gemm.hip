@@ -26,7 +26,12 @@ namespace nf {
 
 enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_PARTIAL = 3 };
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU z * sigmoid(z) from the hardware exp2 and reciprocal (about 1 ulp each, far below the
+// bf16 rounding of the result): a third of the instructions of an IEEE division, which made
+// the SwiGLU epilogue of a 256 x 256 tile take a tenth of the tile's time.
+__device__ __forceinline__ float silu_f(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
 
 template <int BM, int BN, int BK, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B,
@@ -279,6 +284,13 @@ __device__ __forceinline__ void interleave_loads_reads() {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) unsigned char lds_byte;
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes from buffer r at byte offset voff + soff.
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
 // 16 bytes per lane from buffer r at byte offset voff + soff into LDS (lane l at dst + 16 l).
 __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff,
                                                   uint32_t soff) {
@@ -307,9 +319,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
   constexpr int STAGE_BYTES = (A_CH + B_CH) * 16;
   static_assert(SB == STAGES || (SB == STAGES + 1 && STAGES == 2), "B ring: STAGES slabs, or 3 with an A ring of 2");
   constexpr bool SPLIT = SB != STAGES;
-  // one wave per SIMD: the last k16 step of a trip runs in a fixed MFMA / load / read order
-  // (with the split ring the compiler's LDS-DMA wait tracking then serialises the loads)
-  constexpr bool PIN = NW == 4 && !SPLIT;
   // slab kt of A and of B: one ring of A+B stages, or (SPLIT) an A ring then a B ring
   auto a_slab = [](int kt) { return SPLIT ? (kt % STAGES) * (A_CH * 16) : (kt % STAGES) * STAGE_BYTES; };
   auto b_slab = [](int kt) {
@@ -318,6 +327,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
   constexpr int A_LOADS = A_CH / NT, B_LOADS = B_CH / NT;  // per thread (= per wave instruction count)
   static_assert(A_LOADS * NT == A_CH && B_LOADS * NT == B_CH, "slab chunks split evenly over the threads");
   constexpr int NL = A_LOADS + B_LOADS;
+  // One wave per SIMD, two slabs of 64 (RS): the refill of a slab is staged through
+  // registers and spread over the whole k loop (below). Other one-wave-per-SIMD rings (PIN):
+  // the last k16 step of a trip runs in a fixed MFMA / load / read order (with the split ring
+  // the compiler's LDS-DMA wait tracking would serialise the loads).
+  constexpr bool RS = NW == 4 && !SPLIT && KC == 8 && STAGES == 2 && TM * TN >= 8 + 2 * ((NL + 3) / 4);
+  constexpr bool PIN = NW == 4 && !SPLIT && !RS;
   static_assert(EPI != EPI_SWIGLU || (WTN % 64) == 0, "SwiGLU needs gate/up pairs of 32 columns");
 
   static_assert(!GRP || EPI == EPI_STORE || EPI == EPI_SWIGLU, "grouped products store or apply SwiGLU");
@@ -503,7 +518,36 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
     else wait_vmcnt<0>();
   };
 
-  if constexpr (SPLIT) {
+  // RS: the chunk rows of a slab, staged in registers between their global load and their
+  // LDS write; NCH per thread, written and reloaded in 4 groups, one group per k16 step
+  constexpr int NCH = A_LOADS + B_LOADS, GSZ = (NCH + 3) / 4;
+  static_assert(!RS || (Q == 4 && GSZ <= 4), "RS: four k16 steps per slab, at most 4 chunks per group");
+  u32x4 stg[RS ? NCH : 1];
+  auto load_chunk = [&](int sl, int i) {
+    const uint32_t ks = (uint32_t)(sl * BK * (int)sizeof(bf16));
+    if (i < A_LOADS)
+      stg[i] = buffer_load16(a_rsrc, a_off_g[i], ks);
+    else
+      stg[i] = buffer_load16(b_rsrc, b_off_g[i - A_LOADS], ks);
+  };
+  auto write_chunk = [&](int sl, int i) {
+    const int off = i < A_LOADS ? a_slab(sl) + (i * NW + wave_s) * 64 * 16
+                                : b_slab(sl) + ((i - A_LOADS) * NW + wave_s) * 64 * 16;
+    *reinterpret_cast<u32x4*>(smem_raw + off + lane * 16) = stg[i];
+  };
+  if constexpr (RS) {
+    // group 0 of slab 2 follows the two slabs' direct loads
+    if (2 < nk) {
+#pragma unroll
+      for (int i = 0; i < GSZ; ++i) load_chunk(2, i);
+    }
+  }
+  if constexpr (RS) {
+    // issued: slab 0, [slab 1], [group 0 of slab 2]; slab 0 needed
+    if (nk > 2) wait_vmcnt<NCH + GSZ>();
+    else if (nk > 1) wait_vmcnt<NCH>();
+    else wait_vmcnt<0>();
+  } else if constexpr (SPLIT) {
     // issued: A0 B0 [A1 B1] [B2]; slab 0 needed
     if (nk > 2) wait_vmcnt<A_LOADS + 2 * B_LOADS>();
     else if (nk > 1) wait_vmcnt<A_LOADS + B_LOADS>();
@@ -594,7 +638,80 @@ __global__ __launch_bounds__(64 * NW) void gemm_pipe_kernel(const bf16* __restri
   // newest still outstanding; the body is straight-line so the compiler's LDS wait counts
   // stay exact
   int kt = 0;
-  if constexpr (SPLIT) {
+  if constexpr (RS) {
+    // Slab buffers alternate; slabs 0 and 1 come by direct loads, slab s >= 2 through the
+    // staging registers: group g of slab s is loaded in one k16 step and written to LDS in
+    // the same step one trip (four steps) later, then the group of slab s + 1 is loaded
+    // into the same registers. Per step: 16 MFMAs, the 8 fragment reads of the next step, a
+    // group's 4 writes and 4 loads, in that fixed order, so the load unit sees an even
+    // stream (a whole slab's loads at once kept it busy for half a trip while the wave
+    // could not issue its MFMAs) and a load has a whole trip to arrive. Groups 1-3 of slab
+    // kt + 1 go to LDS in steps 0-2 of trip kt; after the barrier, step 3 writes group 0 of
+    // slab kt + 2 into slab kt's buffer, which no wave reads any more.
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using BF = std::integral_constant<bool, false>;
+    using BT = std::integral_constant<bool, true>;
+    // (write / load flags are compile-time, so the load stream has one fixed shape per kind
+    // of trip and the compiler's wait counts before the writes stay exact)
+    auto rs_step = [&](const bf16x8 (&ca)[TM], const bf16x8 (&cb)[TN], bf16x8 (&na)[TM], bf16x8 (&nb)[TN], int rs,
+                       int rq, auto gc, int ws, auto wrc, int ls, auto ldc) {
+      constexpr int g = decltype(gc)::value, c0 = g * GSZ;
+      constexpr bool wr = decltype(wrc)::value, ld = decltype(ldc)::value;
+      constexpr int cn = NCH - c0 < GSZ ? (NCH - c0 > 0 ? NCH - c0 : 0) : GSZ;
+      constexpr int NM = TM * TN, NR = TM + TN;
+      static_assert(NM >= NR && NM >= 8 + 2 * GSZ, "slots for the reads, writes and loads");
+      const unsigned char* sa = smem_raw + a_slab(rs);
+      const unsigned char* sb = smem_raw + b_slab(rs);
+      // reads in the order the next step's MFMAs use them (A row 0 with every B column
+      // first), so its first MFMA waits for two reads, not five
+#pragma unroll
+      for (int x = 0; x < NM; ++x) {
+        acc[x / TN][x % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[x / TN], cb[x % TN], acc[x / TN][x % TN], 0, 0, 0);
+        if (x == 0)
+          na[0] = *reinterpret_cast<const bf16x8*>(sa + a_off[0][rq]);
+        else if (x <= TN)
+          nb[x - 1] = *reinterpret_cast<const bf16x8*>(sb + b_off[x - 1][rq]);
+        else if (x < NR)
+          na[x - TN] = *reinterpret_cast<const bf16x8*>(sa + a_off[x - TN][rq]);
+        if (x >= 8 && x < 8 + cn && wr) write_chunk(ws, c0 + x - 8);
+        if (x >= 8 + GSZ && x < 8 + GSZ + cn && ld) load_chunk(ls, c0 + x - 8 - GSZ);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // trip kt (kt <= nk - 2): W1 = groups 1-3 of slab kt + 1 come from the registers
+    // (kt >= 1), L2 = slab kt + 2 exists, L3 = slab kt + 3 exists
+    auto rs_trip = [&](int kt, auto w1, auto l2, auto l3) {
+      rs_step(fa0, fb0, fa1, fb1, kt, 1, I1{}, kt + 1, w1, kt + 2, l2);
+      rs_step(fa1, fb1, fa0, fb0, kt, 2, I2{}, kt + 1, w1, kt + 2, l2);
+      rs_step(fa0, fb0, fa1, fb1, kt, 3, I3{}, kt + 1, w1, kt + 2, l2);
+      // slab kt + 1 complete (trip 0: its direct loads, followed by group 0 of slab 2 and,
+      // in this trip, groups 1-3 of slab 2), and every wave done reading slab kt
+      if constexpr (!decltype(w1)::value) {
+        if constexpr (decltype(l2)::value)
+          wait_vmcnt<NCH>();
+        else
+          wait_vmcnt<0>();
+      }
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      rs_step(fa1, fb1, fa0, fb0, kt + 1, 0, I0{}, kt + 2, l2, kt + 3, l3);
+    };
+    if (nk >= 2) {
+      if (nk >= 4)
+        rs_trip(0, BF{}, BT{}, BT{});
+      else if (nk == 3)
+        rs_trip(0, BF{}, BT{}, BF{});
+      else
+        rs_trip(0, BF{}, BF{}, BF{});
+      kt = 1;
+      for (; kt + 3 < nk; ++kt) rs_trip(kt, BT{}, BT{}, BT{});
+      if (kt + 2 < nk) rs_trip(kt++, BT{}, BT{}, BF{});
+      if (kt + 1 < nk) rs_trip(kt++, BT{}, BF{}, BF{});
+    }
+  } else if constexpr (SPLIT) {
     // slab kt+1 is awaited with B's slab kt+2 still in flight (issued after A's slab kt+1);
     // after the barrier, A's slab kt+2 and B's slab kt+3 are issued
     auto trip_split = [&](int kt, auto wait_next, auto refill, auto sched) {
