@@ -896,6 +896,12 @@ static const GemmVariant kVariants[] = {
     {256, 256, 64, 1, 2, 4},  // 35
     {256, 256, 64, 2, 2, 4},  // 36 (not SwiGLU)
     {256, 128, 64, 3, 3, 4},  // 37 (not SwiGLU)
+    // one wave per SIMD, 256x256, K in 4 or 3 slices: a product of n = 4096 at 1024 rows
+    // (a nano-batch's O and Down in the 8B layer) in one round of 256 (or 192) workgroups of
+    // the large tile instead of 256 128x128 tiles; not SwiGLU
+    {256, 256, 64, 4, 2, 4},  // 38
+    {256, 256, 64, 3, 2, 4},  // 39
+    {256, 256, 64, 4, 2, 8},  // 40
 };
 constexpr int kBalancedVariant = 19, kBalancedDeepVariant = 26, kBalancedDeep4Variant = 35;
 static constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
@@ -944,6 +950,11 @@ int gemm_default_variant(int m, int n, int k, int epilogue) {
     // us; the O product, k = 4096, loses: 90 against 82)
     if (epilogue != EPI_SWIGLU && k >= 8192 && k % 64 == 0 && 2 * tiles(256, 256) >= 192 && tiles(256, 128) >= 192)
       return k % 128 == 0 ? 25 : 20;
+    // long K at half those rows: 256x256 with K in 4 slices, one round of the CUs (8B Down at
+    // 1024 rows, a nano-batch of two: 128 against 143 us in the layer with 128x128 tiles)
+    if (epilogue != EPI_SWIGLU && k >= 8192 && k % 64 == 0 && k / 64 >= 4 * 8 && 4 * tiles(256, 256) >= 192 &&
+        4 * tiles(256, 256) <= 256)
+      return 38;
     // 256x128 with 8 waves and 6 slabs of 32 (8B O and Down in the layer: 83 and 268 us
     // against 87 and 278 with 4 waves and 4 slabs of 32), or with 64-deep slabs 128x256 with
     // 8 waves and 3 slabs (8B O alone: 68 against 75 us for 256x128); SwiGLU needs 64
@@ -1223,6 +1234,9 @@ hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int
     case 35: return launch_balanced<8, 2, 4>(A, B, C, R, m, n, k, epilogue, s);
     case 36: return launch_pipe<256, 256, 2, 4, 8>(A, B, C, R, m, n, k, epilogue, 2, ws, s);
     case 37: return launch_pipe<256, 128, 3, 4, 8>(A, B, C, R, m, n, k, epilogue, 3, ws, s);
+    case 38: return launch_pipe<256, 256, 2, 4, 8>(A, B, C, R, m, n, k, epilogue, 4, ws, s);
+    case 39: return launch_pipe<256, 256, 2, 4, 8>(A, B, C, R, m, n, k, epilogue, 3, ws, s);
+    case 40: return launch_pipe<256, 256, 2, 8, 8>(A, B, C, R, m, n, k, epilogue, 4, ws, s);
   }
   return hipErrorInvalidValue;
 }

@@ -67,25 +67,31 @@ def sequential(batch: abi.HostBatch, bounds) -> HostPlan:
 
 
 def overlap(batch: abi.HostBatch, bounds, compute_mask=None, memory_mask=None,
-            prefill_on_memory: bool = True, unmasked_kinds=()) -> HostPlan:
+            prefill_on_memory: bool = True, unmasked_kinds=(), memory_kinds=()) -> HostPlan:
     """Two streams (0 compute, 1 memory): KQV of every nano-batch first on the compute
     stream, then O and Up/Gate/Down per nano-batch; decode attention per nano-batch on
     the memory stream (prefill attention there too unless prefill_on_memory is False).
 
     unmasked_kinds: dense kinds (NF_OP_KQV, NF_OP_O, NF_OP_UGD) that run on a third,
     unmasked stream beside the memory stream's mask instead of on the compute mask; the
-    dense ops stay one lane (one at a time, in order) across the two compute streams."""
+    dense ops stay one lane (one at a time, in order) across the two compute streams.
+
+    memory_kinds: dense kinds issued on the memory stream right after their nano-batch's
+    attention instead of on the compute stream (a product that runs poorly beside decode
+    attention then never runs beside it)."""
     third = bool(unmasked_kinds)
+    if third and memory_kinds:
+        raise ValueError("unmasked_kinds and memory_kinds do not combine")
 
     def stream_of(k, j):
-        if k == NF_OP_DECATTN or (k == NF_OP_PFATTN and prefill_on_memory):
+        if k == NF_OP_DECATTN or (k == NF_OP_PFATTN and prefill_on_memory) or k in memory_kinds:
             return 1
         return 2 if k in unmasked_kinds else 0
 
     def rank(k, j):
         if k == NF_OP_KQV:
             return (0, j, 0)
-        if k in (NF_OP_DECATTN, NF_OP_PFATTN):
+        if k in (NF_OP_DECATTN, NF_OP_PFATTN) or k in memory_kinds:
             return (1, j, k)
         return (2, j, k)
 

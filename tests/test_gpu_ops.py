@@ -180,7 +180,7 @@ def test_gemm_deep_slabs_bit_identical(ctx, m, n, k, epi):
 
 
 @pytest.mark.parametrize("variant", [-1, 6, 7, 9, 10, 11, 12, 13, 14, 15, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30,
-                                     31, 32, 33, 34, 35, 36, 37])
+                                     31, 32, 33, 34, 35, 36, 37, 38, 39, 40])
 def test_gemm_residual_in_place(ctx, variant):
     from nano_intra_overlap_amd import abi
 
