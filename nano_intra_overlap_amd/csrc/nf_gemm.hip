@@ -945,9 +945,13 @@ int gemm_default_variant(int m, int n, int k, int epilogue) {
       if (epilogue == EPI_SWIGLU) return deep ? kBalancedDeep4Variant : kBalancedVariant;
       return deep ? 22 : 12;
     }
-    // long K (>= 8192): 256x256 with K split in 2 when that gives >= 192 workgroups; the fp32
-    // partials' round trip is small beside the k loop (8B Down in the layer: 234 against 264
-    // us; the O product, k = 4096, loses: 90 against 82)
+    // long K (>= 8192) with a whole round of 128x256 tiles: those, 8 waves, 3 slabs of 64, the
+    // whole k loop in one workgroup (8B Down in the layer: 207 against 211 us for 256x256 tiles
+    // with K in 2 slices and their reduce)
+    if (epilogue != EPI_SWIGLU && k >= 8192 && k % 64 == 0 && tiles(128, 256) >= 256) return 30;
+    // else 256x256 with K split in 2 when that gives >= 192 workgroups; the fp32 partials'
+    // round trip is small beside the k loop (8B Down in the layer: 234 against 264 us with
+    // 32-deep slabs; the O product, k = 4096, loses: 90 against 82)
     if (epilogue != EPI_SWIGLU && k >= 8192 && k % 64 == 0 && 2 * tiles(256, 256) >= 192 && tiles(256, 128) >= 192)
       return k % 128 == 0 ? 25 : 20;
     // long K at half those rows: 256x256 with K in 4 slices, one round of the CUs (8B Down at
