@@ -211,8 +211,29 @@ def test_plan_templates_never_deadlock(abi):
         n = int(rng.integers(1, min(5, T) + 1))
         bounds = [0] + sorted(rng.choice(np.arange(1, T), size=n - 1, replace=False).tolist()) + [T]
         for plan in (plans.sequential(hb, bounds), plans.overlap(hb, bounds),
-                     plans.overlap(hb, bounds, prefill_on_memory=False)):
+                     plans.overlap(hb, bounds, prefill_on_memory=False),
+                     plans.overlap(hb, bounds, memory_kinds=(abi.NF_OP_O,))):
             abi.nf_plan_dependencies(hb, plan)  # raises NF_E_PLAN on a deadlocking order
+
+
+def test_overlap_memory_kinds_places_o_after_its_attention(abi):
+    """memory_kinds=(O,): every O runs on the memory stream, after its nano-batch's
+    attention there; the compute stream keeps KQV and Up/Gate/Down."""
+    from nano_intra_overlap_amd import plans
+
+    b = sw.make_batch("tiny", 0)
+    hb = abi.HostBatch.from_batch(b)
+    bounds = [0, 39, b.n_tokens]
+    plan = plans.overlap(hb, bounds, memory_kinds=(abi.NF_OP_O,))
+    ops = plan.ops
+    on_memory = [(k, j) for k, j, s in ops if s == 1]
+    assert {k for k, _ in on_memory} <= {abi.NF_OP_DECATTN, abi.NF_OP_PFATTN, abi.NF_OP_O}
+    assert all(s == 0 for k, _, s in ops if k in (abi.NF_OP_KQV, abi.NF_OP_UGD))
+    for j in range(len(bounds) - 1):
+        assert on_memory.index((abi.NF_OP_O, j)) > on_memory.index((abi.NF_OP_DECATTN, j))
+    abi.nf_plan_dependencies(hb, plan)
+    with pytest.raises(ValueError):
+        plans.overlap(hb, bounds, unmasked_kinds=(abi.NF_OP_UGD,), memory_kinds=(abi.NF_OP_O,))
 
 
 def test_cu_mask_helper_balances_xcds(abi):

@@ -106,6 +106,10 @@ def _plans(hb, T):
     # mask, one compute lane across the two
     yield "overlap3_lanes", plans.overlap(hb, [0, 20, 39, T], abi.cu_mask(per_xcd=20, offset=0),
                                           abi.cu_mask(per_xcd=12, offset=20), unmasked_kinds=(abi.NF_OP_UGD,))
+    # O issued on the memory stream right after its nano-batch's attention, with a bounded
+    # attention grid
+    p = plans.overlap(hb, [0, 39, T], memory_kinds=(abi.NF_OP_O,))
+    yield "overlap2_o_on_memory", abi.HostPlan([0, 39, T], p.ops, p.n_streams, None, 4)
 
 
 @pytest.mark.parametrize("seed", [0, 1])
