@@ -1248,7 +1248,7 @@ hipError_t launch_gemm(const bf16* A, const bf16* B, bf16* C, const bf16* R, int
 bool gemm_grouped_variant_ok(int variant, int n, int k, int epilogue) {
   const bool tile = (variant >= 6 && variant <= 9) || variant == 12 ||
                     ((variant == 13 || variant == 18) && epilogue != EPI_SWIGLU);  // 32 columns per wave: no SwiGLU
-  const bool deep = variant == 22 || (variant >= 28 && variant <= 30);          // slabs of 64 k values
+  const bool deep = variant == 21 || variant == 22 || variant == 24 || (variant >= 28 && variant <= 30);  // slabs of 64
   return (tile ? k % 32 == 0 : deep && k % 64 == 0) && n % 8 == 0 &&
          (epilogue == EPI_STORE || epilogue == EPI_SWIGLU);
 }
@@ -1260,7 +1260,10 @@ int gemm_grouped_default_variant(int n_rows, int n_groups, int k, int epilogue) 
   // 128x128 with slabs of 32; 256x256 deep: 1177-1189 us). Slabs of 32: Up/Gate takes
   // 256x256 tiles (8 waves: 1242 against 1282 us with 4) once the groups average 512 rows,
   // 128x256 below; Down 128x128 with 4 waves (8-wave 256x128: 833 against 771 us).
-  if (k % 64 == 0) return 30;
+  // With the groups averaging 512 rows or more (Mixtral at 2048 tokens) Up/Gate takes the
+  // same tile with 4 waves (in the layer, two boxes: 1043-1066 against 1058-1076 us); 256x256
+  // tiles with 4 waves for Down measured -2% on one box and +1% on another, not taken.
+  if (k % 64 == 0) return epilogue == EPI_SWIGLU && n_rows >= 512 * n_groups ? 29 : 30;
   if (epilogue == EPI_SWIGLU) return n_rows >= 512 * n_groups ? 12 : 8;
   return 9;
 }
@@ -1288,6 +1291,12 @@ hipError_t launch_gemm_grouped(const bf16* A, const int32_t* a_rows, const bf16*
     case 22:
       return sw ? launch_grouped_t<256, 256, 2, EPI_SWIGLU, 8, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s)
                 : launch_grouped_t<256, 256, 2, EPI_STORE, 8, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s);
+    case 21:
+      return sw ? launch_grouped_t<256, 256, 2, EPI_SWIGLU, 4, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s)
+                : launch_grouped_t<256, 256, 2, EPI_STORE, 4, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s);
+    case 24:
+      return sw ? launch_grouped_t<256, 128, 3, EPI_SWIGLU, 4, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s)
+                : launch_grouped_t<256, 128, 3, EPI_STORE, 4, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s);
     case 28:
       return sw ? launch_grouped_t<128, 128, 4, EPI_SWIGLU, 4, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s)
                 : launch_grouped_t<128, 128, 4, EPI_STORE, 4, 8>(A, a_rows, B, b_stride, C, grp, n_groups, n_rows, n, k, s);

@@ -114,7 +114,8 @@ def test_moe_ffn_op_every_grouped_variant(ctx):
     shape = sw.WORKLOADS["tiny_moe"].shape
     w = sw.make_weights(shape, 4)
     dw = DeviceWeights(w, "cuda")
-    for ug, down in ((6, 7), (7, 6), (8, 9), (9, 8), (12, 13), (12, 18), (22, 28), (28, 22), (29, 30), (30, 29)):
+    for ug, down in ((6, 7), (7, 6), (8, 9), (9, 8), (12, 13), (12, 18), (22, 28), (28, 22), (29, 30), (30, 29),
+                     (21, 24), (24, 21)):
         _moe_op_case(ctx, shape, w, dw, 300, seed=ug, variants=(ug, down))
 
 
