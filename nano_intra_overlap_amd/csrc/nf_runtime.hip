@@ -71,21 +71,12 @@ struct nf_ctx {
   std::string err;
   // activation workspace
   DevBuf h, qkv, attn, x1, h2, a;
-  // metadata: two slots (pinned staging + device copy) used by alternate calls. A call's
-  // copy runs on meta_stream, so it overlaps the previous call's kernels instead of
-  // standing between them and this call's first kernel on the caller's stream (an
-  // in-stream host-to-device copy left ~25 us idle at every call boundary).
-  DevBuf meta_dev[2];
-  void* meta_host[2] = {nullptr, nullptr};
-  size_t meta_host_cap[2] = {0, 0};
-  hipEvent_t meta_ready[2] = {nullptr, nullptr};  // the copy into slot k is done (meta_stream)
-  bool ready_pending[2] = {false, false};         // meta_ready[k] recorded, not yet waited on by the host
-  hipEvent_t meta_free[2] = {nullptr, nullptr};   // the last call that read slot k is done
-  bool free_recorded[2] = {false, false};
-  hipStream_t meta_stream = nullptr;
-  int meta_slot = 1;          // slot of the latest call (the next call takes the other one)
-  bool meta_used = false;     // a call has used meta_slot; last_stream holds its caller stream
-  hipStream_t meta_last_stream = nullptr;
+  // metadata: pinned staging + device copy
+  DevBuf meta_dev;
+  void* meta_host = nullptr;
+  size_t meta_host_cap = 0;
+  hipEvent_t upload_done = nullptr;
+  bool upload_pending = false;
   // split-KV partials
   DevBuf part_o, part_ml;
   DevBuf gemm_ws;  // split-K fp32 partials, one region per GEMM of a plan
@@ -165,20 +156,17 @@ nf_status ensure(nf_ctx* ctx, DevBuf& b, size_t bytes) {
   return NF_OK;
 }
 
-// Pinned staging of metadata slot k with room for `bytes`; waits until the slot's last
-// copy has left it.
-nf_status ensure_host(nf_ctx* ctx, int k, size_t bytes) {
-  if (ctx->ready_pending[k]) {
-    NF_HIP(ctx, hipEventSynchronize(ctx->meta_ready[k]));  // staging slot free again
-    ctx->ready_pending[k] = false;
+nf_status ensure_host(nf_ctx* ctx, size_t bytes) {
+  if (ctx->meta_host_cap >= bytes) return NF_OK;
+  if (ctx->upload_pending) {
+    NF_HIP(ctx, hipEventSynchronize(ctx->upload_done));
+    ctx->upload_pending = false;
   }
-  if (ctx->meta_host_cap[k] >= bytes) return NF_OK;
-  if (ctx->meta_host[k]) NF_HIP(ctx, hipHostFree(ctx->meta_host[k]));
-  ctx->meta_host[k] = nullptr;
-  ctx->meta_host_cap[k] = 0;
+  if (ctx->meta_host) NF_HIP(ctx, hipHostFree(ctx->meta_host));
+  ctx->meta_host = nullptr;
   const size_t cap = align_up(bytes, 1 << 20);
-  NF_HIP(ctx, hipHostMalloc(&ctx->meta_host[k], cap, hipHostMallocDefault));
-  ctx->meta_host_cap[k] = cap;
+  NF_HIP(ctx, hipHostMalloc(&ctx->meta_host, cap, hipHostMallocDefault));
+  ctx->meta_host_cap = cap;
   return NF_OK;
 }
 
@@ -265,9 +253,9 @@ struct MetaPack {
   bool bt_up = false;
 };
 
-// Pack the metadata into the pinned staging of slot k (after the slot's last copy from it).
+// Pack the metadata into the pinned staging buffer (after the previous upload from it).
 nf_status pack_meta(nf_ctx* ctx, const nf_layer_cfg& cfg, const nf_batch_desc& b, const BatchLayout& L, const Meta& M,
-                    MetaPack& P, int k) {
+                    MetaPack& P) {
   const int T = L.T;
   const int half = cfg.head_dim / 2;
   const size_t n_req = L.req.size();
@@ -288,9 +276,13 @@ nf_status pack_meta(nf_ctx* ctx, const nf_layer_cfg& cfg, const nf_batch_desc& b
   P.o_pf = slot(sizeof(PrefillItem) * M.pf.size());
   P.o_bt = slot(P.bt_up ? sizeof(int32_t) * n_req * b.max_blocks : 0);
   P.total = off;
-  nf_status st = ensure_host(ctx, k, P.total);
+  nf_status st = ensure_host(ctx, P.total);
   if (st != NF_OK) return st;
-  unsigned char* h = static_cast<unsigned char*>(ctx->meta_host[k]);
+  if (ctx->upload_pending) {
+    NF_HIP(ctx, hipEventSynchronize(ctx->upload_done));  // staging buffer free again
+    ctx->upload_pending = false;
+  }
+  unsigned char* h = static_cast<unsigned char*>(ctx->meta_host);
   memset(h, 0, P.total);  // padding too: the bytes are compared when a graph is reused
   memcpy(h + P.o_pos, L.pos.data(), sizeof(int32_t) * T);
   memcpy(h + P.o_slot, L.slot.data(), sizeof(int32_t) * T);
@@ -304,38 +296,16 @@ nf_status pack_meta(nf_ctx* ctx, const nf_layer_cfg& cfg, const nf_batch_desc& b
   return NF_OK;
 }
 
-// Copy slot k's staged metadata to `dst` on `stream`; meta_ready[k] marks its end.
-nf_status copy_meta(nf_ctx* ctx, const MetaPack& P, int k, DevBuf& dst, hipStream_t stream) {
+// Copy the staged metadata to `dst` on `stream` (ordered before the work that reads it).
+nf_status copy_meta(nf_ctx* ctx, const MetaPack& P, DevBuf& dst, hipStream_t stream) {
   if (dst.cap < P.total) {
     nf_status st = ensure(ctx, dst, P.total);
     if (st != NF_OK) return st;
   }
-  NF_HIP(ctx, hipMemcpyAsync(dst.p, ctx->meta_host[k], P.total, hipMemcpyHostToDevice, stream));
-  NF_HIP(ctx, hipEventRecord(ctx->meta_ready[k], stream));
-  ctx->ready_pending[k] = true;
+  NF_HIP(ctx, hipMemcpyAsync(dst.p, ctx->meta_host, P.total, hipMemcpyHostToDevice, stream));
+  NF_HIP(ctx, hipEventRecord(ctx->upload_done, stream));
+  ctx->upload_pending = true;
   return NF_OK;
-}
-
-// The metadata slot of the next call. The latest call's slot is marked free at the end of
-// what that call enqueued on its caller stream (a call returns with all of its work joined
-// into that stream, so this covers its kernels on every plan stream); the slot taken now
-// was last read by the call before it.
-int next_meta_slot(nf_ctx* ctx) {
-  if (ctx->meta_used) {
-    const int last = ctx->meta_slot;
-    if (hipEventRecord(ctx->meta_free[last], ctx->meta_last_stream) == hipSuccess) {
-      ctx->free_recorded[last] = true;
-    } else {
-      // that stream is gone: wait for the whole device instead, after which nothing reads
-      // the slot
-      (void)hipGetLastError();
-      (void)hipDeviceSynchronize();
-      ctx->free_recorded[last] = false;
-    }
-    ctx->meta_used = false;
-  }
-  ctx->meta_slot ^= 1;
-  return ctx->meta_slot;
 }
 
 // Device pointers of the metadata held at `base`.
@@ -351,23 +321,14 @@ void point_meta(const MetaPack& P, const void* base, const nf_batch_desc& b, Met
   M.d_bt = P.bt_up ? reinterpret_cast<const int32_t*>(d + P.o_bt) : b.block_table_dev;
 }
 
-// Pack and upload the metadata of a call that runs on `stream`: into the next slot, on the
-// metadata stream once the slot's previous reader is done, with `stream` waiting for the
-// copy. Issued while the previous call's kernels still run, the copy is over before they
-// end.
+// Pack and upload the metadata to the context's metadata buffer on `stream`.
 nf_status upload_meta(nf_ctx* ctx, const nf_layer_cfg& cfg, const nf_batch_desc& b, const BatchLayout& L, Meta& M,
                       hipStream_t stream) {
-  const int k = next_meta_slot(ctx);
   MetaPack P;
-  nf_status st = pack_meta(ctx, cfg, b, L, M, P, k);
+  nf_status st = pack_meta(ctx, cfg, b, L, M, P);
   if (st != NF_OK) return st;
-  if (ctx->meta_dev[k].cap < P.total && (st = ensure(ctx, ctx->meta_dev[k], P.total)) != NF_OK) return st;
-  if (ctx->free_recorded[k]) NF_HIP(ctx, hipStreamWaitEvent(ctx->meta_stream, ctx->meta_free[k], 0));
-  if ((st = copy_meta(ctx, P, k, ctx->meta_dev[k], ctx->meta_stream)) != NF_OK) return st;
-  NF_HIP(ctx, hipStreamWaitEvent(stream, ctx->meta_ready[k], 0));
-  ctx->meta_used = true;
-  ctx->meta_last_stream = stream;
-  point_meta(P, ctx->meta_dev[k].p, b, M);
+  if ((st = copy_meta(ctx, P, ctx->meta_dev, stream)) != NF_OK) return st;
+  point_meta(P, ctx->meta_dev.p, b, M);
   return NF_OK;
 }
 
@@ -778,11 +739,7 @@ extern "C" nf_status nf_ctx_create(int device, nf_ctx** out) {
   std::unique_ptr<nf_ctx> ctx(new nf_ctx());
   ctx->device = device;
   for (auto& row : ctx->gemm_variant) row[0] = row[1] = -1;
-  for (int k = 0; k < 2; ++k)
-    if (hipEventCreateWithFlags(&ctx->meta_ready[k], hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ctx->meta_free[k], hipEventDisableTiming) != hipSuccess)
-      return NF_E_HIP;
-  if (hipStreamCreateWithFlags(&ctx->meta_stream, hipStreamNonBlocking) != hipSuccess) return NF_E_HIP;
+  if (hipEventCreateWithFlags(&ctx->upload_done, hipEventDisableTiming) != hipSuccess) return NF_E_HIP;
   if (hipEventCreateWithFlags(&ctx->fork_ev, kDeviceEventFlags) != hipSuccess) return NF_E_HIP;
   if (device >= kMaxDevices || scratch_setup(device, &ctx->scratch) != hipSuccess) return NF_E_HIP;
   if (gemm_prepare_kernels() != hipSuccess) return NF_E_HIP;
@@ -804,17 +761,12 @@ extern "C" void nf_ctx_destroy(nf_ctx* ctx) {
   if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
   if (ctx->graph_in) (void)hipEventDestroy(ctx->graph_in);
   if (ctx->graph_out) (void)hipEventDestroy(ctx->graph_out);
-  for (int k = 0; k < 2; ++k) {
-    if (ctx->meta_ready[k]) (void)hipEventDestroy(ctx->meta_ready[k]);
-    if (ctx->meta_free[k]) (void)hipEventDestroy(ctx->meta_free[k]);
-    if (ctx->meta_dev[k].p) (void)hipFree(ctx->meta_dev[k].p);
-    if (ctx->meta_host[k]) (void)hipHostFree(ctx->meta_host[k]);
-  }
-  if (ctx->meta_stream) (void)hipStreamDestroy(ctx->meta_stream);
-  for (DevBuf* b : {&ctx->h, &ctx->qkv, &ctx->attn, &ctx->x1, &ctx->h2, &ctx->a, &ctx->part_o,
+  if (ctx->upload_done) (void)hipEventDestroy(ctx->upload_done);
+  for (DevBuf* b : {&ctx->h, &ctx->qkv, &ctx->attn, &ctx->x1, &ctx->h2, &ctx->a, &ctx->meta_dev, &ctx->part_o,
                     &ctx->part_ml, &ctx->gemm_ws, &ctx->graph_meta, &ctx->moe_idx, &ctx->moe_out, &ctx->kv_stage,
                     &ctx->kv_items})
     if (b->p) (void)hipFree(b->p);
+  if (ctx->meta_host) (void)hipHostFree(ctx->meta_host);
   if (ctx->kv_host) (void)hipHostFree(ctx->kv_host);
   if (ctx->kv_upload_done) (void)hipEventDestroy(ctx->kv_upload_done);
   delete ctx;
@@ -947,15 +899,14 @@ static nf_status stack_forward(nf_ctx* ctx, const nf_layer_cfg* cfg, int32_t n_l
   }
   // captured stack: replayed while its key and metadata bytes are unchanged
   MetaPack P;
-  const int k = next_meta_slot(ctx);  // staging only: a captured stack has its own device copy
-  if ((st = pack_meta(ctx, *cfg, *batch, L, M, P, k)) != NF_OK) return st;
+  if ((st = pack_meta(ctx, *cfg, *batch, L, M, P)) != NF_OK) return st;
   if (L.T == 0) return NF_OK;
   if (!ctx->cap_stream) NF_HIP(ctx, hipStreamCreateWithFlags(&ctx->cap_stream, hipStreamNonBlocking));
   if (!ctx->graph_in) NF_HIP(ctx, hipEventCreateWithFlags(&ctx->graph_in, hipEventDisableTiming));
   if (!ctx->graph_out) NF_HIP(ctx, hipEventCreateWithFlags(&ctx->graph_out, hipEventDisableTiming));
   if (ctx->graph_meta.cap < P.total && (st = ensure(ctx, ctx->graph_meta, P.total)) != NF_OK) return st;
   std::vector<uint64_t> key = graph_key(ctx, *cfg, S, plan, flags, *batch);
-  const unsigned char* staged = static_cast<const unsigned char*>(ctx->meta_host[k]);
+  const unsigned char* staged = static_cast<const unsigned char*>(ctx->meta_host);
   const bool reuse = ctx->graph_exec && key == ctx->graph_key && ctx->graph_meta_bytes.size() == P.total &&
                      memcmp(ctx->graph_meta_bytes.data(), staged, P.total) == 0;
   if (!reuse) {
@@ -970,7 +921,7 @@ static nf_status stack_forward(nf_ctx* ctx, const nf_layer_cfg* cfg, int32_t n_l
     }
     ctx->graph_key.clear();
     ctx->graph_meta_bytes.clear();
-    if ((st = copy_meta(ctx, P, k, ctx->graph_meta, caller)) != NF_OK) return st;
+    if ((st = copy_meta(ctx, P, ctx->graph_meta, caller)) != NF_OK) return st;
     point_meta(P, ctx->graph_meta.p, *batch, M);
     const uint32_t timing = ctx->timing_mask;
     ctx->timing_mask = 0;

@@ -1,11 +1,11 @@
 """Layer calls issued back to back on one context, with no host synchronisation between them.
 
-A call's batch metadata (positions, slots, work lists, block table) is copied to the device
-on the context's own copy stream, into one of two slots used by alternate calls, while the
-previous call's kernels still run; the call's kernels wait for that copy, and a slot is
-refilled only after the call that last read it has finished. These tests alternate two
-different batches call after call (and plans with one stream and with two) and check every
-call's output against the oracle.
+Every call packs its batch metadata (positions, slots, work lists, block table) into the
+context's pinned staging and copies it to the device ahead of its kernels; the staging is
+reused only after the previous copy from it is done, and the device copy is rewritten in
+stream order after the previous call's kernels. These tests alternate two different batches
+call after call (and plans with one stream and with two, and stand-alone attention calls)
+and check every call's output against the oracle.
 
 The two batches have the same request counts and prefill lengths, different decode context
 lengths, and share one block table whose rows are filled with distinct valid block ids to
