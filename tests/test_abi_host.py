@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function(abi):
         if name.endswith(".h"):
             text = open(os.path.join(ROOT, "include", name)).read()
             declared |= set(re.findall(r"^\s*(?:nf_status|void|const char \*)\s*\*?\s*(nf_\w+)\s*\(", text, re.M))
-    # the calls of the boundary as the hot-path survey lists them, by name
+    # the calls the layer boundary is specified with, by name
     assert {"nf_ctx_create", "nf_ctx_destroy", "nf_last_error", "nf_layer_forward", "nf_op_gemm", "nf_op_rmsnorm",
             "nf_op_rope_kv_append", "nf_op_decode_attn", "nf_op_prefill_attn", "nf_profile_ops",
             "nf_profile_interference", "nf_plan_search"} <= declared
